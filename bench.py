@@ -1,0 +1,274 @@
+"""Benchmark of the SLoPe 2:4 sparse linear layer on one MI355X.
+
+One step is one pass of the whole hot path over the four linears of an OPT-66B
+transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
+36864->9216; T = 8192 tokens, adapter rank 72, bf16 with fp32 accumulation):
+
+    prune24 -> compress24 -> double_prune -> spmm_fwd (+ fused adapter)
+            -> spmm_bwd_dx -> masked_wgrad
+
+prune24 and compress24 run once per layer in training (the forward mask is
+static); they are kept inside the timed step so the step covers every kernel of
+the path.  Inputs are synthetic (seeded Gaussian, see workloads/) and resident in
+HBM before the timed region starts.
+
+Prints one JSON line.  `value` is dense-equivalent TFLOP/s of the step's GEMMs
+(3 x 2*T*N*K per linear plus the adapter's 2*T*r*(K+N)); `useful_tflops` counts
+only products with a kept weight (T*N*K per GEMM).  `roofline` reports the
+kernel with the largest share of the step against the dense bf16 MFMA peak
+(2.5 PFLOP/s) using useful flops.  `cpu_baseline` times the CPU oracle on a
+bounded slice of the same layer on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_DENSE_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E (published)
+METRIC = "2:4 sparse-GEMM TFLOP/s fwd+bwd(dX,dW) +LoRA, % MFMA peak, OPT-66B layer"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt_66b")
+    ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Linear:
+    """Device buffers of one linear of the layer."""
+
+    def __init__(self, name, K, N, T, r, seed, index):
+        import numpy as np
+        import torch
+        from workloads import layer_inputs
+
+        self.name, self.K, self.N, self.T, self.r = name, K, N, T, r
+        d = layer_inputs(K, N, T, r, "bf16", seed=seed, index=index)
+        dev = "cuda"
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.W, self.X, self.dY, self.L, self.R = (up(d[k]) for k in ("W", "X", "dY", "L", "R"))
+        del d
+        bf = torch.bfloat16
+        self.mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        self.vs = torch.empty((N, K // 2), dtype=bf, device=dev)
+        self.ms = torch.empty((N, (K // 4 + 7) // 8), dtype=torch.int32, device=dev)
+        self.vdp = torch.empty((K, N // 2), dtype=bf, device=dev)
+        self.mdp = torch.empty((K, (N // 4 + 7) // 8), dtype=torch.int32, device=dev)
+        self.Y = torch.empty((T, N), dtype=bf, device=dev)
+        self.dX = torch.empty((T, K), dtype=bf, device=dev)
+        self.dW = torch.empty((N, K // 2), dtype=bf, device=dev)
+        import sparse_gemm_02_amd as S
+        self.ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, K, r)), dtype=torch.uint8, device=dev)
+
+    def flops(self):
+        T, N, K, r = self.T, self.N, self.K, self.r
+        return {"spmm_fwd": 2 * T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": 2 * T * N * K,
+                "masked_wgrad": 2 * T * N * K}
+
+    def useful(self):
+        T, N, K, r = self.T, self.N, self.K, self.r
+        return {"spmm_fwd": T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": T * N * K, "masked_wgrad": T * N * K}
+
+
+OPS = ("prune24", "compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad")
+
+
+def step(lins, S, ev=None):
+    """One pass of the hot path over every linear; optional per-op events."""
+    for li in lins:
+        calls = (
+            ("prune24", lambda: S.slope_prune24(li.W, li.mask)),
+            ("compress24", lambda: S.slope_compress24(li.W, li.mask, li.vs, li.ms)),
+            ("double_prune", lambda: S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)),
+            ("spmm_fwd", lambda: S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
+            ("spmm_bwd_dx", lambda: S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)),
+            ("masked_wgrad", lambda: S.slope_masked_wgrad(li.dY, li.X, li.ms, li.dW)),
+        )
+        for op, fn in calls:
+            if ev is not None:
+                a, b = ev.pair()
+                a.record()
+                fn()
+                b.record()
+                ev.add(li.name, op, a, b)
+            else:
+                fn()
+
+
+class Events:
+    def __init__(self, torch):
+        self.torch = torch
+        self.rec = []
+
+    def pair(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    def add(self, lin, op, a, b):
+        self.rec.append((lin, op, a, b))
+
+    def totals(self):
+        out = {}
+        for lin, op, a, b in self.rec:
+            out.setdefault((lin, op), []).append(a.elapsed_time(b))
+        return out
+
+
+def cpu_baseline(workload, budget_s):
+    """The CPU oracle on a bounded slice of the layer: for each linear in turn, the
+    first 256 output rows (N' = 256) and 256 tokens (T' = 256), running prune24,
+    compress24, double_prune (of the slice), forward with adapter, dX and dW.
+    Repeats over the linears until the budget is spent; rate in dense-equivalent
+    TFLOP/s of the slice's GEMMs (the same count as the GPU `value`)."""
+    import numpy as np
+
+    import oracle
+    from workloads import layer_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    Tn, Nn = 256, 256
+    samples = []
+    for i, lin in enumerate(workload.linears):
+        d = layer_inputs(lin.K, Nn, Tn, workload.r, "bf16", seed=0, index=100 + i)
+        samples.append((lin, d))
+    flops, spent, runs = 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    while spent < budget_s:
+        for lin, d in samples:
+            K = lin.K
+            t0 = time.perf_counter()
+            mask, _ = oracle.prune24(d["W"])
+            vs, ms, _ = oracle.compress24(d["W"], mask)
+            vdp, mdp, _ = oracle.double_prune(vs, ms, Nn, K)
+            oracle.spmm_fwd(d["X"], vs, ms, K, d["L"], d["R"])
+            oracle.spmm_bwd_dx(d["dY"], vdp, mdp, Nn)
+            oracle.masked_wgrad(d["dY"], d["X"], ms, K)
+            spent += time.perf_counter() - t0
+            flops += 3 * 2 * Tn * Nn * K + 2 * Tn * workload.r * (K + Nn)
+            runs += 1
+            if spent >= budget_s:
+                break
+        if time.perf_counter() - t_start > 4 * budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} linear slices of N'={Nn} output rows x T'={Tn} tokens (full K) of the "
+                      f"{workload.name} layer, whole path (prune, compress, double prune, fwd+adapter, dX, dW), "
+                      f"{spent:.1f} s of CPU work, numpy fp64 with {threads} BLAS threads on {os.cpu_count()} host cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the 2:4 layer kernels are "
+              "measured on a single MI355X; multi-GPU sharding is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_gemm_02_amd as S
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    T = args.tokens or wl.T
+    torch.cuda.set_device(0)
+    S.library()
+    t_in = time.perf_counter()
+    lins = [Linear(l.name, l.K, l.N, T, wl.r, seed=0, index=i) for i, l in enumerate(wl.linears)]
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_in:.1f}s: {args.workload} T={T} r={wl.r}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step(lins, S)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, no per-op events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(lins, S)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # the same steps again with an event pair around every call (per-op durations)
+    ev = Events(torch)
+    for _ in range(args.steps):
+        step(lins, S, ev)
+    torch.cuda.synchronize()
+    per = ev.totals()
+
+    dense_flops = sum(sum(l.flops().values()) for l in lins)
+    useful_flops = sum(sum(l.useful().values()) for l in lins)
+    value = dense_flops / (ms_step * 1e-3) / 1e12
+    useful = useful_flops / (ms_step * 1e-3) / 1e12
+
+    # per-op summary over the linears
+    ops = {}
+    for op in OPS:
+        t = sum(sum(per[(l.name, op)]) / len(per[(l.name, op)]) for l in lins)
+        ops[op] = {"ms_per_step": t}
+    for op in ("spmm_fwd", "spmm_bwd_dx", "masked_wgrad"):
+        uf = sum(l.useful()[op] for l in lins)
+        df = sum(l.flops()[op] for l in lins)
+        t = ops[op]["ms_per_step"] * 1e-3
+        ops[op].update(useful_tflops=uf / t / 1e12, dense_equiv_tflops=df / t / 1e12,
+                       frac_dense_peak_useful=uf / t / 1e12 / PEAK_BF16_DENSE_TFLOPS)
+    hbm = {"prune24": 3.0, "compress24": 4.125, "double_prune": 2.25}  # algorithmic bytes per weight
+    for op, bpe in hbm.items():
+        by = sum(l.N * l.K * bpe for l in lins)
+        ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9
+        ops[op]["frac_hbm_peak"] = ops[op]["gbs"] / PEAK_HBM_GBS
+
+    # dominant single-kernel call (spmm_fwd also launches the adapter down-projection)
+    dom = max(("spmm_bwd_dx", "masked_wgrad"), key=lambda o: ops[o]["ms_per_step"])
+    launches = [(l, sum(per[(l.name, dom)]) / len(per[(l.name, dom)])) for l in lins]
+    achieved = sum(l.useful()[dom] for l, _ in launches) / (sum(t for _, t in launches) * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_DENSE_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                "flops_counted": "useful (T*N*K per launch: products with a kept weight / kept output)",
+                "avg_launch_ms": {l.name: round(t, 4) for l, t in launches}}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{wl.name} layer: " + ", ".join(f"{l.name} {l.K}->{l.N}" for l in wl.linears)
+                      + f"; T={T} tokens; adapter rank {wl.r}; whole path per step",
+                      "tokens": T, "adapter_rank": wl.r},
+           "value_kind": "dense-equivalent TFLOP/s (2*T*N*K per GEMM)",
+           "useful_tflops": round(useful, 2),
+           "frac_dense_peak_useful": round(useful / PEAK_BF16_DENSE_TFLOPS, 4),
+           "ideal_step_ms": round(useful_flops / (PEAK_BF16_DENSE_TFLOPS * 1e12) * 1e3, 3),
+           "ops": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
+           "roofline": roofline}
+    # free the layer before the CPU leg
+    del lins
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * slope.h - C ABI of the SLoPe 2:4 sparse linear layer for AMD MI355X (gfx950).
+ *
+ * The operations are those of "SLoPe: Double-Pruned Sparse Plus Lazy Low-Rank
+ * Adapter Pretraining of LLMs" as described on its summary page (atlas.scime.ai,
+ * sections Problem and Approach), its technical explainer (gist.science,
+ * Technical Summary sections 2.A Double-Pruned Backward Pass, 2.B Lazy Low-Rank
+ * Adapters, 2.C Optimized CUDA Kernels) and its OpenReview discussion
+ * (paperhub.cn, sections "Memory Footprint Reduction During Pretraining and
+ * Inference" and "Clarification on Inference Speedup and Sparse Pre-Training").
+ *
+ * Notation.  A linear layer has weight W [N, K] = [out, in] (row-major, as in
+ * nn.Linear), input X [T, K], output Y [T, N] and output gradient dY [T, N].
+ *   W_s   = W pruned 2:4 along K (two of every four consecutive inputs kept)
+ *   W_dp  = the transpose of W_dpT = prune24(W_s^T): pruned 2:4 along N
+ *   Y     = X . W_s^T (+ (X . L) . R),  L [K, r], R [r, N]
+ *   dX    = dY . W_dp
+ *   dW    = (dY^T . X) kept at W_s's mask
+ *
+ * Data types.  SLOPE_BF16 tensors hold raw bfloat16 values, SLOPE_F32 raw
+ * float32 values.  Products accumulate in float32; bf16 outputs are rounded
+ * to nearest even once, at the end.  An F32-input call must use F32 outputs.
+ *
+ * Selection rule (prune24, double_prune): within a group of four, the two
+ * largest magnitudes are kept; equal magnitudes (including +0/-0 and x/-x) go
+ * to the lower position; NaN ranks above every number and NaNs tie.  Pruned
+ * entries become +0.  The pages fix 2:4 but not the score; magnitude and this
+ * tie rule are the library's reading.
+ *
+ * Compressed 2:4 format of a [rows, cols] matrix (cols % 4 == 0):
+ *   values [rows, cols/2]       the two kept values of every group, in
+ *                               ascending position order, same dtype as input
+ *   meta   [rows, ceil(cols/32)] uint32; group g of a row has nibble
+ *                               i0 | i1 << 2 (its kept positions, i0 < i1) at
+ *                               bits 4*(g%8) of word g/8; unused high nibbles
+ *                               of a row's last word are 0
+ * (two 16-bit values plus index bits per four weights: the discussion page's
+ * memory accounting; the page counts 3 index bits, this format stores 4.)
+ *
+ * Memory and execution.  Every pointer argument is device memory owned by the
+ * caller, contiguous row-major, 16-byte aligned; nothing is retained after a
+ * call returns.  `stream` is a hipStream_t (NULL = the null stream).  Calls
+ * only enqueue work and return without synchronising.  Arguments are checked
+ * before anything is enqueued; on an error nothing is written and no kernel is
+ * launched.  SLOPE_ERR_HIP reports a failed launch (hipGetLastError).  Calls
+ * that overlap on one stream are ordered; the library keeps no state between
+ * calls and is safe to call from several host threads.
+ */
+#ifndef SLOPE_H_
+#define SLOPE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SLOPE_F32 = 0, SLOPE_BF16 = 1 } slope_dtype;
+
+typedef enum {
+  SLOPE_OK = 0,
+  SLOPE_ERR_INVALID_ARG = -1, /* null pointer, unknown dtype, negative size */
+  SLOPE_ERR_SHAPE = -2,       /* a 2:4 dimension not a multiple of 4 */
+  SLOPE_ERR_ALIGN = -3,       /* a pointer not 16-byte aligned */
+  SLOPE_ERR_WORKSPACE = -4,   /* adapter workspace missing or too small */
+  SLOPE_ERR_HIP = -5,         /* the HIP runtime reported an error */
+  SLOPE_ERR_UNSUPPORTED = -6  /* dtype combination or size beyond the limits */
+} slope_status;
+
+/* Largest accepted size of any single dimension (rows, cols, T, N, K, r). */
+#define SLOPE_MAX_DIM (1 << 22)
+
+/* Library ABI version (major * 100 + minor). */
+int slope_version(void);
+
+/* Static text naming a status code (never NULL). */
+const char* slope_status_string(int status);
+
+/* Element counts of the compressed form of a [rows, cols] matrix: *n_values =
+ * rows*cols/2 values, *n_meta_words = rows*ceil(cols/32) uint32 words.
+ * Host-only; SLOPE_ERR_SHAPE if cols % 4 != 0. */
+slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_values, int64_t* n_meta_words);
+
+/* Bytes of device workspace the low-rank adapter needs for T tokens, input
+ * width K and rank r (partial sums X . L in float32).  Host-only. */
+slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t* bytes);
+
+/* Magnitude 2:4 pruning of W [rows, cols] along its rows: the forward weight
+ * W^R, pruned along rows (explainer 2.A; N:M = 2:4, summary page Approach).
+ * The mask is chosen once, at initialisation, and then kept static (explainer
+ * 2.A; summary page Approach).
+ *   W         [rows, cols] dt, input
+ *   mask      [rows, cols] uint8 output, 1 at kept positions, 0 elsewhere
+ *             (one byte per weight, as in the discussion page's accounting)
+ *   W_s       [rows, cols] dt output (kept values, +0 elsewhere) or NULL
+ * Errors: SLOPE_ERR_SHAPE if cols % 4 != 0. */
+slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask,
+                           void* W_s_or_null, void* stream);
+
+/* Compressed form of W under a mask (discussion page, "Memory Footprint":
+ * two 16-bit non-zeros plus their indices per four weights).
+ *   W, mask   [rows, cols] inputs (mask byte != 0 = kept)
+ *   values    [rows, cols/2] dt output, meta [rows, ceil(cols/32)] uint32 output
+ *   invalid   NULL, or a device int32 to which the number of groups whose mask
+ *             keeps more than two positions is added (atomically).  Such a
+ *             group keeps its two lowest kept positions; a group keeping fewer
+ *             than two is filled with its lowest unkept positions and +0.
+ * Errors: SLOPE_ERR_SHAPE if cols % 4 != 0. */
+slope_status slope_compress24(slope_dtype dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols,
+                              void* values, uint32_t* meta, int32_t* invalid_groups_or_null, void* stream);
+
+/* Double pruning for the backward pass: W_dpT = prune24(W_s^T), the weight
+ * W^{R,C} of explainer 2.A (the already 2:4-sparse weight is transposed and
+ * pruned 2:4 once more), kept as the compressed transposed copy that the
+ * discussion page counts next to the weight.
+ * Deterministic; meant to run on every step so the column mask follows W_s.
+ *   values_s, meta_s   compressed W_s of [N, K]
+ *   values_dpT [K, N/2], meta_dpT [K, ceil(N/32)]  compressed W_dpT [K, N]
+ *   mask_dpT   [K, N] uint8 output (1 = kept) or NULL
+ * Errors: SLOPE_ERR_SHAPE unless N % 4 == 0 and K % 4 == 0. */
+slope_status slope_double_prune(slope_dtype dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
+                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT_or_null, void* stream);
+
+/* Sparse forward with the fused unmerged adapter (explainer 2.A and 2.B; 2.C
+ * fuses the sparse product with the low-rank term; discussion page: adapters
+ * are not merged into the weights at inference):
+ *   Y [T, N] = X [T, K] . W_s^T  (+ (X . L) . R  when L, R != NULL and r > 0)
+ *   values_s [N, K/2], meta_s [N, ceil(K/32)]  compressed W_s
+ *   L [K, r], R [r, N] in_dt; workspace: device memory of at least
+ *   slope_lowrank_workspace_bytes(T, K, r) bytes (only used with an adapter)
+ *   out_dt: dtype of Y (BF16 or F32 for BF16 inputs; F32 for F32 inputs)
+ * Y is overwritten.  Errors: SLOPE_ERR_SHAPE if K % 4 != 0;
+ * SLOPE_ERR_WORKSPACE if the adapter is on and the workspace is short. */
+slope_status slope_spmm_fwd(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                            const void* values_s, const uint32_t* meta_s, int64_t N, const void* L_or_null,
+                            const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
+                            void* Y, void* stream);
+
+/* Double-pruned backward data product (explainer 2.A: the backward pass runs
+ * on the double-pruned weight):
+ *   dX [T, K] = dY [T, N] . W_dp,  W_dp = transpose of W_dpT [K, N]
+ *   values_dpT [K, N/2], meta_dpT [K, ceil(N/32)] from slope_double_prune
+ * dX is overwritten.  Errors: SLOPE_ERR_SHAPE if N % 4 != 0. */
+slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                               const void* values_dpT, const uint32_t* meta_dpT, int64_t K, void* dX,
+                               void* stream);
+
+/* Weight gradient at the static mask (the discussion page counts two 16-bit
+ * gradient values per four weights, and fine-tuning updates only the weights
+ * that are not pruned):
+ *   dW = (dY [T, N])^T . X [T, K], kept at the positions named by meta_s
+ *   dW_values [N, K/2] out_dt: values in W_s's slot order (same layout as
+ *             values_s)
+ *   dW_dense  [N, K] out_dt masked dense copy, or NULL
+ *   accumulate != 0: add to the existing contents instead of overwriting
+ * Errors: SLOPE_ERR_SHAPE if K % 4 != 0. */
+slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const void* dY, const void* X, int64_t T,
+                                int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                void* dW_dense_or_null, int accumulate, void* stream);
+
+/* Low-rank adapter term on its own (explainer 2.B: W_dense = W_sparse + L R):
+ *   Y [T, N] += (X [T, K] . L [K, r]) . R [r, N]
+ * The partial sums of X . L (float32) go to the workspace, which must hold
+ * slope_lowrank_workspace_bytes(T, K, r) bytes.  Y (out_dt) is read and
+ * written.  Errors: SLOPE_ERR_WORKSPACE if the workspace is short. */
+slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,
+                               int64_t T, int64_t K, int64_t r, int64_t N, void* workspace,
+                               int64_t workspace_bytes, void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLOPE_H_ */

@@ -1,0 +1,185 @@
+"""Python binding of libslope.so, the SLoPe 2:4 sparse linear layer for MI355X.
+
+Argument marshalling only: every function below checks that its tensors are
+contiguous device tensors, reads their shapes and dtypes, and calls the C ABI
+function of the same name (declared in include/slope.h) on the current HIP
+stream.  All computation happens in the library's HIP kernels; there is no
+fallback.  If the shared library has not been built, every call raises.
+
+Tensor conventions (see include/slope.h):
+  dense matrices      torch.bfloat16 or torch.float32, row-major
+  masks               torch.uint8, 1 = kept
+  compressed values   [rows, cols/2], same dtype as the dense matrix
+  compressed metadata [rows, ceil(cols/32)] torch.int32 holding the uint32 words
+  adapter workspace   torch.uint8 (or any dtype) of slope_lowrank_workspace_bytes()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SlopeError", "library", "library_path", "STATUS",
+    "slope_version", "slope_compressed_sizes", "slope_lowrank_workspace_bytes",
+    "slope_prune24", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
+    "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libslope.so")
+
+STATUS = {0: "SLOPE_OK", -1: "SLOPE_ERR_INVALID_ARG", -2: "SLOPE_ERR_SHAPE", -3: "SLOPE_ERR_ALIGN",
+          -4: "SLOPE_ERR_WORKSPACE", -5: "SLOPE_ERR_HIP", -6: "SLOPE_ERR_UNSUPPORTED"}
+
+_F32, _BF16 = 0, 1
+_i64, _vp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_P_I64 = ctypes.POINTER(ctypes.c_int64)
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "slope_version": (ctypes.c_int, []),
+    "slope_status_string": (ctypes.c_char_p, [_i32]),
+    "slope_compressed_sizes": (_i32, [_i64, _i64, _P_I64, _P_I64]),
+    "slope_lowrank_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
+    "slope_prune24": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "slope_compress24": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "slope_double_prune": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "slope_spmm_fwd": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "slope_spmm_bwd_dx": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]),
+    "slope_masked_wgrad": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+_lib = None
+
+
+class SlopeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({_status_text(status)})")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libslope.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it first "
+                               "(python -m sparse_gemm_02_amd.build); there is no fallback path")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return library().slope_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SlopeError(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.numel() and not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory")
+    return t.data_ptr() if t.numel() else None
+
+
+def _nn(t):
+    """Pointer of a required tensor (a dummy non-null address for empty ones)."""
+    p = _p(t)
+    return p if p is not None else 256  # never dereferenced: the size is zero
+
+
+def _s(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def slope_version() -> int:
+    return library().slope_version()
+
+
+def slope_compressed_sizes(rows: int, cols: int):
+    nv, nm = ctypes.c_int64(), ctypes.c_int64()
+    _check("slope_compressed_sizes", library().slope_compressed_sizes(rows, cols, ctypes.byref(nv), ctypes.byref(nm)))
+    return nv.value, nm.value
+
+
+def slope_lowrank_workspace_bytes(T: int, K: int, r: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_lowrank_workspace_bytes", library().slope_lowrank_workspace_bytes(T, K, r, ctypes.byref(b)))
+    return b.value
+
+
+def slope_prune24(W, mask, W_s=None, stream=None) -> None:
+    rows, cols = W.shape
+    _check("slope_prune24", library().slope_prune24(_dt(W), _nn(W), rows, cols, _nn(mask), _p(W_s), _s(stream)))
+
+
+def slope_compress24(W, mask, values, meta, invalid=None, stream=None) -> None:
+    rows, cols = W.shape
+    _check("slope_compress24", library().slope_compress24(_dt(W), _nn(W), _nn(mask), rows, cols, _nn(values),
+                                                          _nn(meta), _p(invalid), _s(stream)))
+
+
+def slope_double_prune(values_s, meta_s, N, K, values_dpT, meta_dpT, mask_dpT=None, stream=None) -> None:
+    _check("slope_double_prune", library().slope_double_prune(_dt(values_s), _nn(values_s), _nn(meta_s), N, K,
+                                                              _nn(values_dpT), _nn(meta_dpT), _p(mask_dpT),
+                                                              _s(stream)))
+
+
+def slope_spmm_fwd(X, values_s, meta_s, N, Y, L=None, R=None, workspace=None, stream=None) -> None:
+    T, K = X.shape
+    r = int(L.shape[1]) if L is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_spmm_fwd", library().slope_spmm_fwd(_dt(X), _dt(Y), _nn(X), T, K, _nn(values_s), _nn(meta_s), N,
+                                                      _p(L), _p(R), r, _p(workspace), wb, _nn(Y), _s(stream)))
+
+
+def slope_spmm_bwd_dx(dY, values_dpT, meta_dpT, K, dX, stream=None) -> None:
+    T, N = dY.shape
+    _check("slope_spmm_bwd_dx", library().slope_spmm_bwd_dx(_dt(dY), _dt(dX), _nn(dY), T, N, _nn(values_dpT),
+                                                            _nn(meta_dpT), K, _nn(dX), _s(stream)))
+
+
+def slope_masked_wgrad(dY, X, meta_s, dW_values, dW_dense=None, accumulate=False, stream=None) -> None:
+    T, N = dY.shape
+    K = X.shape[1]
+    _check("slope_masked_wgrad", library().slope_masked_wgrad(_dt(dY), _dt(dW_values), _nn(dY), _nn(X), T, N, K,
+                                                              _nn(meta_s), _nn(dW_values), _p(dW_dense),
+                                                              int(bool(accumulate)), _s(stream)))
+
+
+def slope_lowrank_add(X, L, R, workspace, Y, stream=None) -> None:
+    T, K = X.shape
+    r, N = R.shape
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_lowrank_add", library().slope_lowrank_add(_dt(X), _dt(Y), _nn(X), _nn(L), _nn(R), T, K, r, N,
+                                                            _p(workspace), wb, _nn(Y), _s(stream)))

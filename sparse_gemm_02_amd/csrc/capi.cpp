@@ -1,0 +1,209 @@
+// C ABI of the SLoPe 2:4 library: argument checks, then kernel launches.
+// Every check happens before the first launch, so an error leaves all outputs
+// untouched.  Declarations and the meaning of every argument: include/slope.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/slope.h"
+#include "launch.h"
+
+using slope::Dt;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dt_ok(int d) { return d == SLOPE_F32 || d == SLOPE_BF16; }
+
+bool in_range(int64_t v) { return v >= 0 && v <= SLOPE_MAX_DIM; }
+
+slope_status from_hip(hipError_t e) { return e == hipSuccess ? SLOPE_OK : SLOPE_ERR_HIP; }
+
+slope_status check_io(slope_dtype in, slope_dtype out) {
+  if (!dt_ok(in) || !dt_ok(out)) return SLOPE_ERR_INVALID_ARG;
+  if (in == SLOPE_F32 && out != SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
+  return SLOPE_OK;
+}
+
+// Pointer check: required pointers must be non-null; all non-null pointers aligned.
+slope_status ptr(const void* p, bool required) {
+  if (!p) return required ? SLOPE_ERR_INVALID_ARG : SLOPE_OK;
+  return aligned16(p) ? SLOPE_OK : SLOPE_ERR_ALIGN;
+}
+
+#define SLOPE_TRY(x)                       \
+  do {                                     \
+    slope_status _st = (x);                \
+    if (_st != SLOPE_OK) return _st;       \
+  } while (0)
+
+int64_t workspace_need(int64_t T, int64_t K, int64_t r) {
+  if (T == 0 || r == 0) return 0;
+  return (int64_t)slope::lowrank_splits(T, K) * T * r * (int64_t)sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int slope_version(void) { return 100; }
+
+const char* slope_status_string(int status) {
+  switch (status) {
+    case SLOPE_OK: return "ok";
+    case SLOPE_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown dtype or negative size)";
+    case SLOPE_ERR_SHAPE: return "a 2:4 dimension is not a multiple of 4";
+    case SLOPE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SLOPE_ERR_WORKSPACE: return "adapter workspace missing or too small";
+    case SLOPE_ERR_HIP: return "HIP runtime error";
+    case SLOPE_ERR_UNSUPPORTED: return "unsupported dtype combination or size";
+    default: return "unknown status";
+  }
+}
+
+slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_values, int64_t* n_meta_words) {
+  if (!n_values || !n_meta_words || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  if (cols % 4) return SLOPE_ERR_SHAPE;
+  *n_values = rows * (cols / 2);
+  *n_meta_words = rows * ((cols / 4 + 7) / 8);
+  return SLOPE_OK;
+}
+
+slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(K) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = workspace_need(T, K, r);
+  return SLOPE_OK;
+}
+
+slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask,
+                           void* W_s_or_null, void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(W, true));
+  SLOPE_TRY(ptr(mask, true));
+  SLOPE_TRY(ptr(W_s_or_null, false));
+  if (cols % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || !in_range(cols)) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_prune24((Dt)dt, W, rows, cols, mask, W_s_or_null, (hipStream_t)stream));
+}
+
+slope_status slope_compress24(slope_dtype dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols,
+                              void* values, uint32_t* meta, int32_t* invalid_groups_or_null, void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(W, true));
+  SLOPE_TRY(ptr(mask, true));
+  SLOPE_TRY(ptr(values, true));
+  SLOPE_TRY(ptr(meta, true));
+  if (invalid_groups_or_null && (reinterpret_cast<uintptr_t>(invalid_groups_or_null) & 3u)) return SLOPE_ERR_ALIGN;
+  if (cols % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || !in_range(cols)) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_compress24((Dt)dt, W, mask, rows, cols, values, meta, invalid_groups_or_null,
+                                           (hipStream_t)stream));
+}
+
+slope_status slope_double_prune(slope_dtype dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
+                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT_or_null, void* stream) {
+  if (!dt_ok(dt) || N < 0 || K < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values_s, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(values_dpT, true));
+  SLOPE_TRY(ptr(meta_dpT, true));
+  SLOPE_TRY(ptr(mask_dpT_or_null, false));
+  if (N % 4 || K % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(N) || !in_range(K)) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_double_prune((Dt)dt, values_s, meta_s, N, K, values_dpT, meta_dpT,
+                                             mask_dpT_or_null, (hipStream_t)stream));
+}
+
+slope_status slope_spmm_fwd(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                            const void* values_s, const uint32_t* meta_s, int64_t N, const void* L_or_null,
+                            const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
+                            void* Y, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(values_s, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(Y, true));
+  const bool adapter = L_or_null && R_or_null && r > 0;
+  if (adapter) {
+    SLOPE_TRY(ptr(L_or_null, true));
+    SLOPE_TRY(ptr(R_or_null, true));
+  }
+  if (K % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || !in_range(N) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
+  if (adapter) {
+    const int64_t need = workspace_need(T, K, r);
+    if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
+    if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
+  }
+  if (T == 0 || N == 0) return SLOPE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  float* xl = nullptr;
+  int splits = 1;
+  if (adapter) {
+    xl = static_cast<float*>(workspace_or_null);
+    splits = slope::lowrank_splits(T, K);
+    hipError_t e = slope::launch_lowrank_down((Dt)in_dt, X, L_or_null, T, K, r, splits, xl, s);
+    if (e != hipSuccess) return SLOPE_ERR_HIP;
+  }
+  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, X, T, K, values_s, meta_s, N, xl, splits,
+                                     adapter ? r : 0, R_or_null, Y, s));
+}
+
+slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                               const void* values_dpT, const uint32_t* meta_dpT, int64_t K, void* dX,
+                               void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(dY, true));
+  SLOPE_TRY(ptr(values_dpT, true));
+  SLOPE_TRY(ptr(meta_dpT, true));
+  SLOPE_TRY(ptr(dX, true));
+  if (N % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  if (T == 0 || K == 0) return SLOPE_OK;
+  // dX^T = W_dpT . dY^T: the forward kernel with reduction N and output rows K
+  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, dY, T, N, values_dpT, meta_dpT, K, nullptr, 1, 0,
+                                     nullptr, dX, (hipStream_t)stream));
+}
+
+slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const void* dY, const void* X, int64_t T,
+                                int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                void* dW_dense_or_null, int accumulate, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(dY, true));
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(dW_values, true));
+  SLOPE_TRY(ptr(dW_dense_or_null, false));
+  if (K % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return SLOPE_OK;
+  return from_hip(slope::launch_masked_wgrad((Dt)in_dt, (Dt)out_dt, dY, X, T, N, K, meta_s, dW_values,
+                                             dW_dense_or_null, accumulate, (hipStream_t)stream));
+}
+
+slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,
+                               int64_t T, int64_t K, int64_t r, int64_t N, void* workspace,
+                               int64_t workspace_bytes, void* Y, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(L, true));
+  SLOPE_TRY(ptr(R, true));
+  SLOPE_TRY(ptr(Y, true));
+  if (!in_range(T) || !in_range(K) || !in_range(N) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
+  const int64_t need = workspace_need(T, K, r);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return SLOPE_ERR_ALIGN;
+  if (T == 0 || N == 0 || r == 0) return SLOPE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  float* xl = static_cast<float*>(workspace);
+  const int splits = slope::lowrank_splits(T, K);
+  hipError_t e = slope::launch_lowrank_down((Dt)in_dt, X, L, T, K, r, splits, xl, s);
+  if (e != hipSuccess) return SLOPE_ERR_HIP;
+  return from_hip(slope::launch_lowrank_up_add((Dt)in_dt, (Dt)out_dt, xl, splits, R, T, r, N, Y, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Shared device helpers of the SLoPe 2:4 library (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slope {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ----------------------------------------------------------------- magnitudes
+// Magnitude order key of a raw value: the absolute-value bits, with every NaN
+// collapsed to one key just above +Inf (NaNs rank above numbers and tie).
+__device__ __forceinline__ uint32_t mag_key(uint16_t b) {
+  uint32_t m = b & 0x7FFFu;
+  return m > 0x7F80u ? 0x7F81u : m;
+}
+__device__ __forceinline__ uint32_t mag_key(uint32_t b) {
+  uint32_t m = b & 0x7FFFFFFFu;
+  return m > 0x7F800000u ? 0x7F800001u : m;
+}
+
+// 4-bit keep mask of the two largest of four keys; equal keys go to the lower
+// position.  rank(j) counts the positions that outrank j: a lower position i
+// outranks j when k_i >= k_j, a higher one when k_i > k_j.
+__device__ __forceinline__ uint32_t top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
+  uint32_t c01 = k0 >= k1, c02 = k0 >= k2, c03 = k0 >= k3;
+  uint32_t c12 = k1 >= k2, c13 = k1 >= k3, c23 = k2 >= k3;
+  uint32_t r0 = 3u - c01 - c02 - c03;
+  uint32_t r1 = c01 + 2u - c12 - c13;
+  uint32_t r2 = c02 + c12 + 1u - c23;
+  uint32_t r3 = c03 + c13 + c23;
+  return (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) | ((uint32_t)(r3 < 2) << 3);
+}
+
+// Nibble i0 | i1 << 2 of a 4-bit mask holding exactly two positions i0 < i1.
+__device__ __forceinline__ uint32_t pair_nibble(uint32_t m) {
+  uint32_t i0 = __builtin_ctz(m);
+  uint32_t i1 = 31u - __builtin_clz(m);
+  return i0 | (i1 << 2);
+}
+
+// ----------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ float to_f32(uint32_t b) { return __uint_as_float(b); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Output element stores (bf16 bits or fp32).
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ float load_out(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ float load_out(const float* p) { return *p; }
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace slope

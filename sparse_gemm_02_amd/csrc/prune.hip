@@ -1,0 +1,253 @@
+// Magnitude 2:4 pruning, compression and double pruning (HBM-bound kernels).
+//
+// SLoPe explainer (gist.science), Technical Summary 2.A: the forward weight is
+// pruned N:M (2:4) along its rows; the backward weight is the already sparse
+// weight, transposed and pruned 2:4 again.  The discussion page's "Memory
+// Footprint" section keeps each as two 16-bit values plus indices per group of
+// four.  Selection rule: the two largest magnitudes, equal magnitudes to the
+// lower position, NaN above every number.
+#include "common.h"
+#include "launch.h"
+
+namespace slope {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename E> struct Vec4;                       // one group of four raw values
+template <> struct Vec4<uint16_t> { typedef u32x2 T; };  // 8 bytes
+template <> struct Vec4<uint32_t> { typedef u32x4 T; };  // 16 bytes
+
+__device__ __forceinline__ void unpack(u32x2 v, uint16_t e[4]) {
+  e[0] = (uint16_t)(v[0] & 0xFFFF); e[1] = (uint16_t)(v[0] >> 16);
+  e[2] = (uint16_t)(v[1] & 0xFFFF); e[3] = (uint16_t)(v[1] >> 16);
+}
+__device__ __forceinline__ void unpack(u32x4 v, uint32_t e[4]) { e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3]; }
+__device__ __forceinline__ u32x2 pack(const uint16_t e[4]) {
+  u32x2 v; v[0] = e[0] | ((uint32_t)e[1] << 16); v[1] = e[2] | ((uint32_t)e[3] << 16); return v;
+}
+__device__ __forceinline__ u32x4 pack(const uint32_t e[4]) { u32x4 v; v[0] = e[0]; v[1] = e[1]; v[2] = e[2]; v[3] = e[3]; return v; }
+
+// ------------------------------------------------------------------ prune24
+// One group of four per thread and iteration; groups never straddle rows
+// because cols % 4 == 0, so the matrix is a flat array of groups.
+template <typename E, int UNROLL>
+__global__ __launch_bounds__(kThreads) void prune24_kernel(const E* __restrict__ W, int64_t groups,
+                                                           uint32_t* __restrict__ mask4, E* __restrict__ W_s) {
+  typedef typename Vec4<E>::T V;
+  const V* in = reinterpret_cast<const V*>(W);
+  V* out = reinterpret_cast<V*>(W_s);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; g0 < groups; g0 += stride * UNROLL) {
+    V v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      int64_t g = g0 + u * stride;
+      if (g < groups) v[u] = __builtin_nontemporal_load(in + g);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      int64_t g = g0 + u * stride;
+      if (g >= groups) break;
+      E e[4];
+      unpack(v[u], e);
+      uint32_t keep = top2_of_4(mag_key(e[0]), mag_key(e[1]), mag_key(e[2]), mag_key(e[3]));
+      // mask bytes 0/1 for the four positions, little-endian in one word
+      uint32_t mb = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
+      mask4[g] = mb;
+      if (W_s) {
+        E o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (keep >> i) & 1u ? e[i] : (E)0;
+        out[g] = pack(o);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ compress24
+// Thread slot f -> (row, word, j): eight consecutive lanes build one metadata
+// word (groups 8*word .. 8*word+7 of a row) and OR their nibbles together.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void compress24_kernel(const E* __restrict__ W, const uint8_t* __restrict__ mask,
+                                                              int64_t rows, int64_t cols, E* __restrict__ values,
+                                                              uint32_t* __restrict__ meta, int32_t* invalid) {
+  typedef typename Vec4<E>::T V;
+  const int64_t gpr = cols / 4;             // groups per row
+  const int64_t wpr = cdiv(gpr, 8);         // metadata words per row
+  const int64_t slots = rows * wpr * 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform loop bound so that every lane of a wave joins the shuffles
+  const int64_t wave_base0 = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63);
+  for (int64_t base = wave_base0; base < slots; base += stride) {
+    const int64_t f = base + lane;
+    const bool in_range = f < slots;
+    const int64_t w = f >> 3;
+    const int j = (int)(f & 7);
+    const int64_t row = in_range ? w / wpr : 0;
+    const int64_t gw = in_range ? w - row * wpr : 0;
+    const int64_t g = gw * 8 + j;
+    const bool valid = in_range && g < gpr;
+    uint32_t nib = 0;
+    bool bad = false;
+    if (valid) {
+      const int64_t gidx = row * gpr + g;   // flat group index
+      E e[4];
+      unpack(reinterpret_cast<const V*>(W)[gidx], e);
+      uint32_t mw = reinterpret_cast<const uint32_t*>(mask)[gidx];
+      uint32_t kept = ((mw & 0xFFu) != 0) | (((mw >> 8) & 0xFFu) != 0) << 1 |
+                      (((mw >> 16) & 0xFFu) != 0) << 2 | (((mw >> 24) & 0xFFu) != 0) << 3;
+      uint32_t sel = kept;
+      bad = __builtin_popcount(kept) > 2;
+      if (bad) {  // keep the two lowest kept positions
+        uint32_t lo = sel & (0u - sel);
+        uint32_t rest = sel & ~lo;
+        sel = lo | (rest & (0u - rest));
+      }
+      while (__builtin_popcount(sel) < 2) {  // fill with the lowest unkept positions
+        uint32_t un = ~sel & 0xFu;
+        sel |= un & (0u - un);
+      }
+      nib = pair_nibble(sel);
+      const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+      E v0 = (kept >> i0) & 1u ? e[i0] : (E)0;
+      E v1 = (kept >> i1) & 1u ? e[i1] : (E)0;
+      values[2 * gidx] = v0;
+      values[2 * gidx + 1] = v1;
+    }
+    uint32_t word = nib << (4 * j);
+    word |= __shfl_xor(word, 1, 8);
+    word |= __shfl_xor(word, 2, 8);
+    word |= __shfl_xor(word, 4, 8);
+    if (in_range && j == 0) meta[row * wpr + gw] = word;
+    if (invalid) {
+      uint64_t b = __ballot(bad);
+      if (b && lane == 0) atomicAdd(invalid, (int32_t)__builtin_popcountll(b));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ double prune
+// Block tile: 64 rows n of W_s x 128 columns k.  Phase 1 decompresses the tile
+// into LDS (one full metadata word, 32 columns, per thread).  Phase 2 gives each
+// thread one row k of W_s^T and 32 consecutive n (one output metadata word),
+// reads them down an LDS column, prunes 2:4 again and writes compressed rows.
+constexpr int DP_TN = 64, DP_TK = 128;
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restrict__ vals, const uint32_t* __restrict__ meta,
+                                                                int64_t N, int64_t K, E* __restrict__ out_vals,
+                                                                uint32_t* __restrict__ out_meta, uint8_t* __restrict__ out_mask) {
+  constexpr int PITCH = DP_TK + (sizeof(E) == 2 ? 2 : 1);  // odd word pitch: column reads spread over banks
+  __shared__ E tile[DP_TN * PITCH];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.y * DP_TN;
+  const int64_t k0 = (int64_t)blockIdx.x * DP_TK;
+  const int64_t in_wpr = cdiv(K / 4, 8), out_wpr = cdiv(N / 4, 8);
+  const int64_t in_gpr = K / 4;
+
+  {  // phase 1: decompress W_s[n0 + n][k0 + 32q .. +31]
+    const int n = tid >> 2, q = tid & 3;
+    const int64_t row = n0 + n;
+    E dense[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dense[i] = (E)0;
+    const int64_t gbase = (k0 >> 2) + 8 * q;  // first group of this thread
+    if (row < N && gbase < in_gpr) {
+      const uint32_t word = meta[row * in_wpr + (gbase >> 3)];
+      const E* v = vals + row * (K / 2) + 2 * gbase;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (gbase + i < in_gpr) {
+          const uint32_t nib = (word >> (4 * i)) & 0xFu;
+          dense[4 * i + (nib & 3u)] = v[2 * i];
+          dense[4 * i + (nib >> 2)] = v[2 * i + 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tile[n * PITCH + 32 * q + i] = dense[i];
+  }
+  __syncthreads();
+  {  // phase 2: row k of W_s^T, columns n0 + 32h .. +31
+    const int kk = tid & (DP_TK - 1), h = tid >> 7;
+    const int64_t krow = k0 + kk;
+    const int64_t g0 = (n0 >> 2) + 8 * h;  // first output group of this thread
+    if (krow < K && g0 < N / 4) {
+      uint32_t word = 0;
+      E ov[16];
+      uint32_t mbytes[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        E e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = tile[(32 * h + 4 * i + j) * PITCH + kk];
+        const uint32_t keep = top2_of_4(mag_key(e[0]), mag_key(e[1]), mag_key(e[2]), mag_key(e[3]));
+        const uint32_t nib = pair_nibble(keep);
+        word |= nib << (4 * i);
+        ov[2 * i] = e[nib & 3u];
+        ov[2 * i + 1] = e[nib >> 2];
+        mbytes[i] = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
+      }
+      const int64_t ngroups = N / 4 - g0 < 8 ? N / 4 - g0 : 8;
+      if (ngroups < 8) word &= (1u << (4 * ngroups)) - 1u;
+      out_meta[krow * out_wpr + (g0 >> 3)] = word;
+      E* ovp = out_vals + krow * (N / 2) + 2 * g0;
+      for (int i = 0; i < 2 * ngroups; ++i) ovp[i] = ov[i];
+      if (out_mask) {
+        uint32_t* mp = reinterpret_cast<uint32_t*>(out_mask + krow * N + 4 * g0);
+        for (int i = 0; i < ngroups; ++i) mp[i] = mbytes[i];
+      }
+    }
+  }
+}
+
+int grid_for(int64_t work, int per_block) {
+  int64_t b = cdiv(work, per_block);
+  const int64_t cap = 256 * 32;  // enough waves in flight on 256 CUs
+  return (int)(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+}  // namespace
+
+hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* W_s,
+                          hipStream_t s) {
+  const int64_t groups = rows * cols / 4;
+  if (groups == 0) return hipSuccess;
+  constexpr int U = 4;
+  const int grid = grid_for(groups, kThreads * U);
+  if (dt == Dt::BF16)
+    prune24_kernel<uint16_t, U><<<grid, kThreads, 0, s>>>((const uint16_t*)W, groups, (uint32_t*)mask, (uint16_t*)W_s);
+  else
+    prune24_kernel<uint32_t, U><<<grid, kThreads, 0, s>>>((const uint32_t*)W, groups, (uint32_t*)mask, (uint32_t*)W_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols, void* values,
+                             uint32_t* meta, int32_t* invalid, hipStream_t s) {
+  const int64_t slots = rows * cdiv(cols / 4, 8) * 8;
+  if (slots == 0) return hipSuccess;
+  const int grid = grid_for(slots, kThreads);
+  if (dt == Dt::BF16)
+    compress24_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)W, mask, rows, cols, (uint16_t*)values, meta, invalid);
+  else
+    compress24_kernel<uint32_t><<<grid, kThreads, 0, s>>>((const uint32_t*)W, mask, rows, cols, (uint32_t*)values, meta, invalid);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
+                               void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
+  if (N == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(K, DP_TK), (unsigned)cdiv(N, DP_TN));
+  if (dt == Dt::BF16)
+    double_prune_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,
+                                                            meta_dpT, mask_dpT);
+  else
+    double_prune_kernel<uint32_t><<<grid, kThreads, 0, s>>>((const uint32_t*)values_s, meta_s, N, K, (uint32_t*)values_dpT,
+                                                            meta_dpT, mask_dpT);
+  return hipGetLastError();
+}
+
+}  // namespace slope

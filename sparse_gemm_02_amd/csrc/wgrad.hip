@@ -1,0 +1,231 @@
+// Masked weight gradient dW = (dY^T . X) kept at the static 2:4 mask.
+//
+// The discussion page ("Memory Footprint Reduction During Pretraining and
+// Inference") stores the gradient as two 16-bit values per four weights, and
+// ("SLoPe downstream finetuning") only the non-zero weights are updated.  The
+// sparsity sits in the output, not in the reduction, so this is a dense MFMA
+// contraction over tokens whose epilogue keeps two of every four results.
+//
+// The kernel computes the transposed tile dW^T[k][n] = sum_t X[t][k] dY[t][n]:
+// in the 32x32 MFMA output layout lane l holds four consecutive rows
+// 8*(v/4) + 4*(l/32) + v%4, i.e. one whole 2:4 group of k, so the epilogue picks
+// its two kept values in registers and writes them in W_s's slot order.
+//
+// Both operands are stored with tokens (the reduction) as rows, so tiles go to
+// LDS as they are in memory and the MFMA fragments are read with the gfx950
+// transposing LDS load ds_read_b64_tr_b16.  Measured semantics: in each group of
+// 16 lanes, lane j supplies the address of four consecutive 16-bit values; lane
+// i receives value i%4 of the rows supplied by lanes i/4, i/4+4, i/4+8, i/4+12.
+// With lane j pointing at row (t + j/4), columns (c + 4*(j%4)) .. +3, lane i
+// receives column c + i of rows t .. t+3.
+#include "common.h"
+#include "launch.h"
+#include "tile_map.h"
+
+namespace slope {
+
+hipError_t launch_wgrad_generic(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+                                const uint32_t* meta_s, void* dWv, void* dWd, int accumulate, hipStream_t s);
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int BK_, int BN_>
+struct WGeo {
+  static constexpr int BK = BK_, BN = BN_;         // tile rows (k) x columns (n) of dW^T
+  static constexpr int WK = BK / 2, WN = BN / 2;   // 2 x 2 waves
+  static constexpr int FK = WK / 32, FN = WN / 32;
+  static constexpr int TS = 32;                    // tokens per LDS stage (two 16-deep MFMA steps)
+  static constexpr int XP = BK + 16, DP = BN + 16; // row pitches (bf16); 8 banks of skew per row
+  static constexpr int X_ELEMS = TS * XP, D_ELEMS = TS * DP;
+  static constexpr int STAGE_BYTES = (X_ELEMS + D_ELEMS) * 2;
+  static constexpr int NX = TS * BK / 8 / kThreads, ND = TS * BN / 8 / kThreads;  // 16-byte chunks per thread
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+};
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Two adjacent outputs as one store (4-byte aligned for bf16, 8-byte for fp32).
+__device__ __forceinline__ void store_pair(uint16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+__device__ __forceinline__ void store_pair(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+// Four adjacent outputs (8-byte aligned for bf16, 16-byte for fp32), optionally accumulated.
+__device__ __forceinline__ void store_quad(uint16_t* p, const float (&x)[4], int accumulate) {
+  float y[4] = {x[0], x[1], x[2], x[3]};
+  if (accumulate) {
+    const u32x2 o = *reinterpret_cast<const u32x2*>(p);
+    y[0] += bf16_bits_to_f32(o[0] & 0xFFFF); y[1] += bf16_bits_to_f32(o[0] >> 16);
+    y[2] += bf16_bits_to_f32(o[1] & 0xFFFF); y[3] += bf16_bits_to_f32(o[1] >> 16);
+  }
+  u32x2 w;
+  w[0] = f32_to_bf16_bits(y[0]) | ((uint32_t)f32_to_bf16_bits(y[1]) << 16);
+  w[1] = f32_to_bf16_bits(y[2]) | ((uint32_t)f32_to_bf16_bits(y[3]) << 16);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+__device__ __forceinline__ void store_quad(float* p, const float (&x)[4], int accumulate) {
+  f32x4 y = {x[0], x[1], x[2], x[3]};
+  if (accumulate) y += *reinterpret_cast<const f32x4*>(p);
+  *reinterpret_cast<f32x4*>(p) = y;
+}
+
+// Eight consecutive tokens (rows tb .. tb+7) of column c0 + (lane % 32) of a
+// row-major LDS tile, as an MFMA operand fragment (two transposing loads).
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* tile, int pitch, int tb, int c0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int c = c0 + 16 * (g & 1) + 4 * (j & 3);
+  const int t = tb + 8 * (g >> 1) + (j >> 2);
+  const uint16_t* p0 = tile + t * pitch + c;
+  const uint16_t* p1 = p0 + 4 * pitch;
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  s16x4 lo = a, hi = b;
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Requirements (host-checked): K % 8 == 0, N % 8 == 0, 16-byte aligned bases.
+template <class G, typename O>
+__global__ __launch_bounds__(kThreads, 1) void wgrad_mfma_kernel(const uint16_t* __restrict__ dY,
+                                                                 const uint16_t* __restrict__ X, int T, int N, int K,
+                                                                 const uint32_t* __restrict__ meta,
+                                                                 O* __restrict__ dWv, O* __restrict__ dWd,
+                                                                 int accumulate) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wk = wave & 1, wn = wave >> 1;
+  const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
+  int tk, tn;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_k, tiles_n, 8, tk, tn);
+  const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
+  const int stages = (T + G::TS - 1) / G::TS;
+
+  u32x4 px[G::NX], pd[G::ND];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < G::NX; ++i) {
+      const int c = tid + kThreads * i, row = c / (G::BK / 8), p = c % (G::BK / 8);
+      const int64_t t = (int64_t)s * G::TS + row, k = k0 + 8 * p;
+      px[i] = (t < T && k + 8 <= K) ? *reinterpret_cast<const u32x4*>(X + t * K + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < G::ND; ++i) {
+      const int c = tid + kThreads * i, row = c / (G::BN / 8), p = c % (G::BN / 8);
+      const int64_t t = (int64_t)s * G::TS + row, n = n0 + 8 * p;
+      pd[i] = (t < T && n + 8 <= N) ? *reinterpret_cast<const u32x4*>(dY + t * N + n) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int buf) {
+    uint16_t* Xs = reinterpret_cast<uint16_t*>(lds + buf * G::STAGE_BYTES);
+    uint16_t* Ds = Xs + G::X_ELEMS;
+#pragma unroll
+    for (int i = 0; i < G::NX; ++i) {
+      const int c = tid + kThreads * i, row = c / (G::BK / 8), p = c % (G::BK / 8);
+      *reinterpret_cast<u32x4*>(Xs + row * G::XP + 8 * p) = px[i];
+    }
+#pragma unroll
+    for (int i = 0; i < G::ND; ++i) {
+      const int c = tid + kThreads * i, row = c / (G::BN / 8), p = c % (G::BN / 8);
+      *reinterpret_cast<u32x4*>(Ds + row * G::DP + 8 * p) = pd[i];
+    }
+  };
+
+  f32x16 acc[G::FK][G::FN];
+#pragma unroll
+  for (int a = 0; a < G::FK; ++a)
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b) acc[a][b] = f32x16{};
+
+  if (stages > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int s = 0; s < stages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < stages) load(s + 1);
+    const uint16_t* Xs = reinterpret_cast<const uint16_t*>(lds + buf * G::STAGE_BYTES);
+    const uint16_t* Ds = Xs + G::X_ELEMS;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 xa[G::FK];
+#pragma unroll
+      for (int a = 0; a < G::FK; ++a) xa[a] = frag_tr(Xs, G::XP, 16 * sub, wk * G::WK + a * 32, lane);
+#pragma unroll
+      for (int b = 0; b < G::FN; ++b) {
+        const bf16x8 db = frag_tr(Ds, G::DP, 16 * sub, wn * G::WN + b * 32, lane);
+#pragma unroll
+        for (int a = 0; a < G::FK; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], db, acc[a][b], 0, 0, 0);
+      }
+    }
+    if (s + 1 < stages) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: rows k (4 consecutive = one group) x column n of this lane
+  const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
+#pragma unroll
+  for (int b = 0; b < G::FN; ++b) {
+    const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
+    if (n >= N) continue;
+#pragma unroll
+    for (int a = 0; a < G::FK; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
+        if (k >= K) continue;
+        const int64_t g = k >> 2;
+        const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
+        const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+        const float r0 = acc[a][b][4 * q], r1 = acc[a][b][4 * q + 1];
+        const float r2 = acc[a][b][4 * q + 2], r3 = acc[a][b][4 * q + 3];
+        // i0 < i1: i0 in {0,1,2}, i1 in {1,2,3}; selects without indexing registers
+        float v0 = i0 == 0 ? r0 : (i0 == 1 ? r1 : r2);
+        float v1 = i1 == 3 ? r3 : (i1 == 2 ? r2 : r1);
+        O* vp = dWv + n * (K / 2) + 2 * g;
+        if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
+        store_pair(vp, v0, v1);
+        if (dWd) {
+          O* dp = dWd + n * K + k;
+          const float x[4] = {(i0 == 0) ? r0 : 0.f, (i0 == 1 || i1 == 1) ? r1 : 0.f,
+                              (i0 == 2 || i1 == 2) ? r2 : 0.f, (i1 == 3) ? r3 : 0.f};
+          store_quad(dp, x, accumulate);
+        }
+      }
+    }
+  }
+}
+
+typedef WGeo<256, 256> WGeoBig;
+
+}  // namespace
+
+hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+                               const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
+                               hipStream_t s) {
+  const bool fast = in == Dt::BF16 && K % 8 == 0 && N % 8 == 0;
+  if (!fast) return launch_wgrad_generic(in, out, dY, X, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
+  typedef WGeoBig G;
+  const int64_t nb = cdiv(K, G::BK) * cdiv(N, G::BN);
+  if (out == Dt::BF16) {
+    auto kern = wgrad_mfma_kernel<G, uint16_t>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    kern<<<(unsigned)nb, kThreads, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
+                                                      meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense, accumulate);
+  } else {
+    auto kern = wgrad_mfma_kernel<G, float>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    kern<<<(unsigned)nb, kThreads, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
+                                                      meta_s, (float*)dW_values, (float*)dW_dense, accumulate);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace slope

@@ -1,0 +1,86 @@
+"""The C ABI library: it loads, exports what include/slope.h declares, and
+rejects bad arguments on the host before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_gemm_02_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slope.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.library_path):
+        from sparse_gemm_02_amd.build import build
+        build()
+    return S.library()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(slope_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(S.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings(lib):
+    assert S.slope_version() == 100
+    for code in S.STATUS:
+        assert lib.slope_status_string(code)
+    assert lib.slope_status_string(12345) == b"unknown status"
+
+
+def test_size_queries(lib):
+    assert S.slope_compressed_sizes(36864, 9216) == (36864 * 4608, 36864 * 288)
+    assert S.slope_compressed_sizes(3, 36) == (54, 6)        # ragged: ceil(36/32) = 2 words
+    with pytest.raises(S.SlopeError):
+        S.slope_compressed_sizes(3, 6)
+    assert S.slope_lowrank_workspace_bytes(64, 256, 8) % (64 * 8 * 4) == 0
+    assert S.slope_lowrank_workspace_bytes(64, 256, 0) == 0
+    assert S.slope_lowrank_workspace_bytes(0, 256, 8) == 0
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails its checks first
+
+
+def test_argument_errors(lib):
+    bf, f32 = 1, 0
+    assert lib.slope_prune24(7, FAKE, 4, 4, FAKE, None, None) == -1            # bad dtype
+    assert lib.slope_prune24(bf, None, 4, 4, FAKE, None, None) == -1           # null input
+    assert lib.slope_prune24(bf, FAKE, -1, 4, FAKE, None, None) == -1          # negative size
+    assert lib.slope_prune24(bf, FAKE, 4, 6, FAKE, None, None) == -2           # cols % 4
+    assert lib.slope_prune24(bf, FAKE + 2, 4, 4, FAKE, None, None) == -3       # misaligned
+    assert lib.slope_prune24(bf, FAKE, 4, (1 << 22) + 4, FAKE, None, None) == -6
+    assert lib.slope_compress24(bf, FAKE, FAKE, 4, 4, FAKE, None, None, None) == -1
+    assert lib.slope_compress24(bf, FAKE, FAKE, 4, 4, FAKE, FAKE, FAKE + 2, None) == -3
+    assert lib.slope_double_prune(bf, FAKE, FAKE, 6, 8, FAKE, FAKE, None, None) == -2
+    assert lib.slope_double_prune(bf, FAKE, FAKE, 8, 6, FAKE, FAKE, None, None) == -2
+    # fp32 inputs with bf16 output are not offered
+    assert lib.slope_spmm_fwd(f32, bf, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_spmm_fwd(bf, bf, FAKE, 4, 6, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -2
+    # adapter on without a workspace, or with a short one
+    assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, FAKE, 16, FAKE, None) == -4
+    assert lib.slope_spmm_bwd_dx(bf, bf, FAKE, 4, 6, FAKE, FAKE, 8, FAKE, None) == -2
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 4, 8, 6, FAKE, FAKE, None, 0, None) == -2
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, None, 4, 8, 8, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
+    assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    W = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.slope_prune24(W, torch.zeros(4, 8, dtype=torch.uint8))

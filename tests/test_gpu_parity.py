@@ -1,0 +1,344 @@
+"""GPU parity at oracle-friendly sizes: every entry point against the CPU oracle.
+
+Masks, metadata, compressed values and the pruned weights must match bit for
+bit; products must stay within the normwise tolerance (bf16 outputs 1e-2, fp32
+path 1e-5, max |gpu - oracle| / max |oracle|), and integer-valued inputs whose
+sums are exact must match bit for bit.  Sizes span several tiles of the fast
+kernels (256 x 256 output tiles, 64-wide reduction stages) and ragged tails;
+shapes whose rows are not 16-byte aligned exercise the generic kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_02_amd as S
+from workloads import f32_to_bf16_bits, layer_inputs
+
+from gpu_util import TOL, Compressed, dev, dev_meta, empty, host, host_f64, normwise, say, torch_dtype, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.library()  # raises if the library was not built
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(vals, dt):
+    v = np.asarray(vals, dtype=np.float32)
+    return f32_to_bf16_bits(v) if dt == "bf16" else v.view(np.uint32).copy()
+
+
+def _special_matrix(rows, cols, dt, seed):
+    """Ties, signed zeros, denormals, infinities and NaN mixed into Gaussian values."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, cols)).astype(np.float32) * 0.02
+    pick = rng.integers(0, 10, size=(rows, cols))
+    v[pick == 0] = 0.0
+    v[pick == 1] = -0.0
+    v[pick == 2] = np.round(v[pick == 2] * 100) / 100          # many ties after rounding
+    v[pick == 3] = -v[pick == 3]
+    bits = _bits(v, dt)
+    flat = bits.reshape(-1)
+    n = flat.size
+    idx = rng.choice(n, size=max(1, n // 50), replace=False)
+    if dt == "bf16":
+        specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0x0001, 0x8003, 0x7F7F], dtype=np.uint16)
+    else:
+        specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0x00000001, 0x80000005, 0x7F7FFFFF], dtype=np.uint32)
+    flat[idx] = specials[rng.integers(0, len(specials), size=idx.size)]
+    return bits
+
+
+# ------------------------------------------------------------------ prune / compress / double prune
+
+PRUNE_SHAPES = [(64, 256), (100, 68), (256, 1024), (7, 4), (33, 36)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", PRUNE_SHAPES)
+def test_prune24_bit_exact(dt, rows, cols):
+    say(f"prune24 {dt} {rows}x{cols}")
+    W = _special_matrix(rows, cols, dt, rows * cols)
+    mask_ref, Ws_ref = oracle.prune24(W)
+    Wd = dev(W)
+    mask = empty((rows, cols), torch.uint8)
+    Ws = empty((rows, cols), torch_dtype(dt))
+    S.slope_prune24(Wd, mask, Ws)
+    torch.cuda.synchronize()
+    assert (host(mask) == mask_ref).all()
+    assert (host(Ws) == Ws_ref).all()
+    # W_s is optional
+    mask2 = empty((rows, cols), torch.uint8)
+    S.slope_prune24(Wd, mask2)
+    assert (host(mask2) == mask_ref).all()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", PRUNE_SHAPES)
+def test_compress24_bit_exact(dt, rows, cols):
+    say(f"compress24 {dt} {rows}x{cols}")
+    W = _special_matrix(rows, cols, dt, 7 + rows)
+    mask_ref, _ = oracle.prune24(W)
+    vals_ref, meta_ref, inv_ref = oracle.compress24(W, mask_ref)
+    c = Compressed(rows, cols, torch_dtype(dt))
+    inv = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S.slope_compress24(dev(W), dev(mask_ref), c.values, c.meta, inv)
+    torch.cuda.synchronize()
+    assert (host(c.values) == vals_ref).all()
+    assert (host(c.meta) == meta_ref).all()
+    assert int(inv.item()) == inv_ref == 0
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_compress24_user_masks(dt):
+    say(f"compress24 user masks {dt}")
+    rng = np.random.default_rng(11)
+    rows, cols = 40, 100
+    W = _bits(rng.standard_normal((rows, cols)), dt)
+    mask = (rng.integers(0, 4, size=(rows, cols)) == 0).astype(np.uint8) * rng.integers(1, 255, size=(rows, cols)).astype(np.uint8)
+    mask[0, :8] = [1, 1, 1, 1, 0, 0, 0, 0]   # four kept, then none
+    vals_ref, meta_ref, inv_ref = oracle.compress24(W, mask)
+    assert inv_ref > 0
+    c = Compressed(rows, cols, torch_dtype(dt))
+    inv = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S.slope_compress24(dev(W), dev(mask), c.values, c.meta, inv)
+    torch.cuda.synchronize()
+    assert (host(c.values) == vals_ref).all()
+    assert (host(c.meta) == meta_ref).all()
+    assert int(inv.item()) == inv_ref
+
+
+DP_SHAPES = [(64, 128), (100, 68), (256, 384), (36, 260), (4, 4), (520, 132)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("N,K", DP_SHAPES)
+def test_double_prune_bit_exact(dt, N, K):
+    say(f"double_prune {dt} N={N} K={K}")
+    W = _special_matrix(N, K, dt, N + K)
+    mask_s, _ = oracle.prune24(W)
+    vs, ms, _ = oracle.compress24(W, mask_s)
+    v_ref, m_ref, mask_ref = oracle.double_prune(vs, ms, N, K)
+    out = Compressed(K, N, torch_dtype(dt))
+    mask = empty((K, N), torch.uint8)
+    S.slope_double_prune(dev(vs), dev_meta(ms), N, K, out.values, out.meta, mask)
+    torch.cuda.synchronize()
+    assert (host(out.values) == v_ref).all()
+    assert (host(out.meta) == m_ref).all()
+    assert (host(mask) == mask_ref).all()
+    out2 = Compressed(K, N, torch_dtype(dt))
+    S.slope_double_prune(dev(vs), dev_meta(ms), N, K, out2.values, out2.meta)
+    assert (host(out2.meta) == m_ref).all()
+
+
+def test_chain_prune_compress_double_prune_on_device():
+    say("chain prune -> compress -> double prune")
+    N, K = 300, 520
+    W = _special_matrix(N, K, "bf16", 99)
+    mask_s, _ = oracle.prune24(W)
+    vs, ms, _ = oracle.compress24(W, mask_s)
+    v_ref, m_ref, _ = oracle.double_prune(vs, ms, N, K)
+    Wd = dev(W)
+    mask = empty((N, K), torch.uint8)
+    S.slope_prune24(Wd, mask)
+    c = Compressed(N, K, torch.bfloat16)
+    S.slope_compress24(Wd, mask, c.values, c.meta)
+    out = Compressed(K, N, torch.bfloat16)
+    S.slope_double_prune(c.values, c.meta, N, K, out.values, out.meta)
+    torch.cuda.synchronize()
+    assert (host(out.values) == v_ref).all() and (host(out.meta) == m_ref).all()
+
+
+# ------------------------------------------------------------------ products
+
+def _layer(T, N, K, r, dt, seed, ints=False):
+    if ints:
+        rng = np.random.default_rng(seed)
+        mk = lambda *s: _bits(rng.integers(-3, 4, size=s), dt)
+        d = {"W": mk(N, K), "X": mk(T, K), "dY": mk(T, N), "L": mk(K, r), "R": mk(r, N)}
+    else:
+        d = layer_inputs(K, N, T, r, dt, seed=seed)
+    mask_s, W_s = oracle.prune24(d["W"])
+    vs, ms, _ = oracle.compress24(d["W"], mask_s)
+    vdp = mdp = None
+    if N % 4 == 0:  # double pruning groups along N
+        vdp, mdp, _ = oracle.double_prune(vs, ms, N, K)
+    d.update(mask_s=mask_s, vs=vs, ms=ms, vdp=vdp, mdp=mdp)
+    return d
+
+
+# (T, N, K): several 256-wide output tiles, 64-wide stages, ragged tails;
+# K % 16 != 0 or N % 4 != 0 route to the generic kernels.
+GEMM_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
+               (257, 260, 528), (50, 102, 64)]
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("adapter", [False, True])
+@pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
+def test_spmm_fwd(T, N, K, adapter, out_dt):
+    say(f"spmm_fwd T={T} N={N} K={K} adapter={adapter} out={out_dt}")
+    r = 8 if adapter else 0
+    d = _layer(T, N, K, max(r, 1), "bf16", seed=T + N + K)
+    L, R = (d["L"][:, :r], d["R"][:r]) if adapter else (None, None)
+    ref = oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, L, R)
+    Y = empty((T, N), torch_dtype(out_dt))
+    S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y,
+                     L=dev(np.ascontiguousarray(L)) if adapter else None,
+                     R=dev(np.ascontiguousarray(R)) if adapter else None,
+                     workspace=workspace(T, K, r) if adapter else None)
+    torch.cuda.synchronize()
+    err = normwise(host_f64(Y), ref)
+    assert err <= TOL["bf16"], err
+    if out_dt == "f32":  # fp32 output keeps the fp32 accumulation: much tighter
+        assert err <= 2e-5 * max(1.0, np.sqrt(K / 256)), err
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
+def test_spmm_bwd_dx(T, N, K, out_dt):
+    if N % 4:
+        pytest.skip("double pruning needs N % 4 == 0")
+    say(f"spmm_bwd_dx T={T} N={N} K={K} out={out_dt}")
+    d = _layer(T, N, K, 1, "bf16", seed=3 * T + N + K)
+    ref = oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N)
+    dX = empty((T, K), torch_dtype(out_dt))
+    S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
+    torch.cuda.synchronize()
+    err = normwise(host_f64(dX), ref)
+    assert err <= TOL["bf16"], err
+
+
+WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
+                (0, 64, 64), (257, 264, 520)]
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,N,K", WGRAD_SHAPES)
+def test_masked_wgrad(T, N, K, out_dt):
+    say(f"masked_wgrad T={T} N={N} K={K} out={out_dt}")
+    d = _layer(T, N, K, 1, "bf16", seed=5 * T + N + K)
+    v_ref, d_ref = oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)
+    dWv = empty((N, K // 2), torch_dtype(out_dt))
+    dWd = empty((N, K), torch_dtype(out_dt))
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv, dWd)
+    torch.cuda.synchronize()
+    assert normwise(host_f64(dWv), v_ref) <= TOL["bf16"]
+    assert normwise(host_f64(dWd), d_ref) <= TOL["bf16"]
+    assert (host_f64(dWd)[d["mask_s"] == 0] == 0).all()
+    # accumulation adds to what is there
+    base = torch.randn((N, K // 2), device="cuda").to(torch_dtype(out_dt))
+    acc = base.clone()
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert normwise(host_f64(acc), v_ref + host_f64(base)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,N,K,r", [(64, 256, 256, 8), (300, 520, 272, 72), (37, 100, 68, 5), (513, 260, 1024, 40),
+                                     (8, 64, 64, 130)])
+def test_lowrank_add(T, N, K, r, out_dt):
+    say(f"lowrank_add T={T} N={N} K={K} r={r} out={out_dt}")
+    d = layer_inputs(K, N, T, r, "bf16", seed=T + r)
+    Y0 = torch.randn((T, N), device="cuda").to(torch_dtype(out_dt))
+    y0_bits = host(Y0)
+    _, ref = oracle.lowrank_add(d["X"], d["L"], d["R"], Y_in=y0_bits)
+    Y = Y0.clone()
+    S.slope_lowrank_add(dev(d["X"]), dev(d["L"]), dev(d["R"]), workspace(T, K, r), Y)
+    torch.cuda.synchronize()
+    assert normwise(host_f64(Y), ref) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ fp32 path (toy workload precision)
+
+@pytest.mark.parametrize("T,N,K", [(64, 256, 256), (37, 100, 68)])
+def test_fp32_path(T, N, K):
+    say(f"fp32 path T={T} N={N} K={K}")
+    r = 8
+    d = _layer(T, N, K, r, "f32", seed=T * N)
+    Y = empty((T, N), torch.float32)
+    S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y, L=dev(d["L"]), R=dev(d["R"]),
+                     workspace=workspace(T, K, r))
+    dX = empty((T, K), torch.float32)
+    S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
+    dWv = empty((N, K // 2), torch.float32)
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv)
+    torch.cuda.synchronize()
+    assert normwise(host_f64(Y), oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"])) <= TOL["f32"]
+    assert normwise(host_f64(dX), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N)) <= TOL["f32"]
+    assert normwise(host_f64(dWv), oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)[0]) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------ exact integer probes
+
+@pytest.mark.parametrize("T,N,K", [(300, 520, 512), (64, 256, 256), (37, 100, 68)])
+def test_integer_inputs_bit_exact(T, N, K):
+    """Integers in [-3, 3]: every product and partial sum is exact in fp32, so
+    fp32 outputs must equal the oracle exactly (pins orientation and slots)."""
+    say(f"integer probe T={T} N={N} K={K}")
+    r = 4
+    d = _layer(T, N, K, r, "bf16", seed=17, ints=True)
+    Y = empty((T, N), torch.float32)
+    S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y, L=dev(d["L"]), R=dev(d["R"]),
+                     workspace=workspace(T, K, r))
+    dX = empty((T, K), torch.float32)
+    S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
+    dWv = empty((N, K // 2), torch.float32)
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(Y), oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"]))
+    assert np.array_equal(host_f64(dX), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N))
+    assert np.array_equal(host_f64(dWv), oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)[0])
+
+
+def test_empty_and_degenerate():
+    say("empty and degenerate sizes")
+    # T = 0: nothing written, no error
+    X = empty((0, 64), torch.bfloat16)
+    c = Compressed(32, 64, torch.bfloat16)
+    Y = empty((0, 32), torch.bfloat16)
+    S.slope_spmm_fwd(X, c.values, c.meta, 32, Y)
+    # K = 0: Y is the empty sum, 0
+    Y = torch.full((5, 8), 7.0, device="cuda", dtype=torch.bfloat16)
+    S.slope_spmm_fwd(empty((5, 0), torch.bfloat16), empty((8, 0), torch.bfloat16),
+                     torch.empty((8, 0), dtype=torch.int32, device="cuda"), 8, Y)
+    torch.cuda.synchronize()
+    assert (Y.float() == 0).all()
+    # rows = 0 prune / compress
+    S.slope_prune24(empty((0, 8), torch.bfloat16), empty((0, 8), torch.uint8))
+    # an all-zero weight keeps positions 0 and 1 of every group (ties to the lower index)
+    W = torch.zeros((8, 16), device="cuda", dtype=torch.bfloat16)
+    mask = empty((8, 16), torch.uint8)
+    S.slope_prune24(W, mask)
+    torch.cuda.synchronize()
+    assert (mask.view(8, 4, 4).cpu() == torch.tensor([1, 1, 0, 0], dtype=torch.uint8)).all()
+
+
+def test_deterministic_repeat():
+    say("bitwise determinism")
+    T, N, K, r = 300, 520, 528, 16
+    d = _layer(T, N, K, r, "bf16", seed=1)
+    args = (dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N)
+    outs = []
+    for _ in range(2):
+        Y = empty((T, N), torch.bfloat16)
+        S.slope_spmm_fwd(*args, Y, L=dev(d["L"]), R=dev(d["R"]), workspace=workspace(T, K, r))
+        dW = empty((N, K // 2), torch.bfloat16)
+        S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dW)
+        torch.cuda.synchronize()
+        outs.append((host(Y), host(dW)))
+    assert all((a == b).all() for a, b in zip(outs[0], outs[1]))
+
+
+def test_single_hip_runtime_loaded():
+    """torch's HIP runtime and the library's must be the same mapped object."""
+    import re
+    maps = open("/proc/self/maps").read()
+    libs = set(re.findall(r"\S*libamdhip64\S*", maps))
+    assert len(libs) == 1, libs
