@@ -87,8 +87,8 @@ def _ranks_above(mag, nan, i, j):
 def prune24(A: np.ndarray):
     """Magnitude 2:4 pruning along the rows of A (groups of 4 consecutive columns).
 
-    Forward weight W^R: "row-wise pruned" in the explainer's section 2.A; N:M with
-    2:4 in the summary page's Approach.  Within each group the element j is kept
+    Forward weight W^R: pruned along its rows (the explainer's section 2.A); N:M
+    with 2:4 in the summary page's Approach.  Within each group the element j is kept
     iff fewer than two elements rank above it (magnitude, ties to lower index).
 
     Returns (mask uint8 [rows, cols] with 1 at kept positions,
@@ -193,7 +193,7 @@ def double_prune(values_s: np.ndarray, meta_s: np.ndarray, N: int, K: int):
     Explainer section 2.A and Key Contributions: the already 2:4-sparse W_s is
     transposed and pruned 2:4 a second time, so the backward operand is N:M
     sparse along its new rows (the output dimension N).  The discussion page
-    keeps the result as a second compressed copy ("Weight-Transpose").
+    keeps the result as a second compressed copy next to the weight.
 
     Returns (values_dpT [K, N/2], meta_dpT [K, ceil(N/32)], mask_dpT [K, N]).
     """
@@ -232,9 +232,9 @@ def spmm_bwd_dx(dY, values_dpT, meta_dpT, N) -> np.ndarray:
 def masked_wgrad(dY, X, meta_s, K, dW_values_in=None, dW_dense_in=None):
     """Weight gradient kept at the static mask: dW = (dY^T . X) (.) M_s.
 
-    The discussion page stores the gradient as "2 * 16 bits" per four weights
-    and, for fine-tuning, updates "only the non-zero weights"; the values are
-    laid out in W_s's compressed slot order.  With ``dW_*_in`` given the result
+    The discussion page counts two 16-bit gradient values per four weights
+    and, for fine-tuning, updates only the weights that are not pruned; the
+    values are laid out in W_s's compressed slot order.  With ``dW_*_in`` given the result
     is added to them (gradient accumulation).
 
     Returns (dW_values [N, K/2] float64, dW_dense [N, K] float64).
