@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--profile-op", choices=OPS + ("copy",), default=None,
+                    help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
+    ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
+    ap.add_argument("--repeat", type=int, default=10)
+    ap.add_argument("--copy-mib", type=int, default=1024, help="profiling mode 'copy': bytes of a plain device copy")
     return ap.parse_args()
 
 
@@ -74,7 +79,7 @@ class Linear:
         self.dX = torch.empty((T, K), dtype=bf, device=dev)
         self.dW = torch.empty((N, K // 2), dtype=bf, device=dev)
         import sparse_gemm_02_amd as S
-        self.ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, K, r)), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, K, r, N)), dtype=torch.uint8, device=dev)
 
     def flops(self):
         T, N, K, r = self.T, self.N, self.K, self.r
@@ -176,6 +181,48 @@ def cpu_baseline(workload, budget_s):
                       f"{spent:.1f} s of CPU work, numpy fp64 with {threads} BLAS threads on {os.cpu_count()} host cores"}
 
 
+def profile_mode(args, wl, T):
+    """Run one op alone (for rocprofv3 counters), or a plain device copy of known size."""
+    import torch
+
+    import sparse_gemm_02_amd as S
+    if args.profile_op == "copy":
+        n = args.copy_mib * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(args.repeat):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[profile] copy {n} bytes x {args.repeat}", flush=True)
+        return
+    sel = [(i, l) for i, l in enumerate(wl.linears) if args.linear in (None, l.name)]
+    lins = [Linear(l.name, l.K, l.N, T, wl.r, seed=0, index=i) for i, l in sel]
+    for li in lins:  # prerequisites of every op
+        S.slope_prune24(li.W, li.mask)
+        S.slope_compress24(li.W, li.mask, li.vs, li.ms)
+        S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+    torch.cuda.synchronize()
+    op = args.profile_op
+    for _ in range(args.repeat):
+        for li in lins:
+            if op == "prune24":
+                S.slope_prune24(li.W, li.mask)
+            elif op == "compress24":
+                S.slope_compress24(li.W, li.mask, li.vs, li.ms)
+            elif op == "double_prune":
+                S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+            elif op == "spmm_fwd":
+                S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
+            elif op == "spmm_bwd_dx":
+                S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)
+            elif op == "masked_wgrad":
+                S.slope_masked_wgrad(li.dY, li.X, li.ms, li.dW)
+    torch.cuda.synchronize()
+    print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -191,6 +238,9 @@ def main():
     T = args.tokens or wl.T
     torch.cuda.set_device(0)
     S.library()
+    if args.profile_op:
+        profile_mode(args, wl, T)
+        return
     t_in = time.perf_counter()
     lins = [Linear(l.name, l.K, l.N, T, wl.r, seed=0, index=i) for i, l in enumerate(wl.linears)]
     torch.cuda.synchronize()

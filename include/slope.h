@@ -83,8 +83,10 @@ const char* slope_status_string(int status);
 slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_values, int64_t* n_meta_words);
 
 /* Bytes of device workspace the low-rank adapter needs for T tokens, input
- * width K and rank r (partial sums X . L in float32).  Host-only. */
-slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t* bytes);
+ * width K, rank r and output width N: the split partial sums of X . L
+ * (float32), X . L as bf16 hi + lo parts, and transposed copies of L and R.
+ * Host-only; 0 when T == 0 or r == 0. */
+slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
 
 /* Magnitude 2:4 pruning of W [rows, cols] along its rows: the forward weight
  * W^R, pruned along rows (explainer 2.A; N:M = 2:4, summary page Approach).
@@ -128,7 +130,8 @@ slope_status slope_double_prune(slope_dtype dt, const void* values_s, const uint
  *   Y [T, N] = X [T, K] . W_s^T  (+ (X . L) . R  when L, R != NULL and r > 0)
  *   values_s [N, K/2], meta_s [N, ceil(K/32)]  compressed W_s
  *   L [K, r], R [r, N] in_dt; workspace: device memory of at least
- *   slope_lowrank_workspace_bytes(T, K, r) bytes (only used with an adapter)
+ *   slope_lowrank_workspace_bytes(T, K, r, N) bytes (only used with an adapter;
+ *   its contents are scratch, overwritten by every call)
  *   out_dt: dtype of Y (BF16 or F32 for BF16 inputs; F32 for F32 inputs)
  * Y is overwritten.  Errors: SLOPE_ERR_SHAPE if K % 4 != 0;
  * SLOPE_ERR_WORKSPACE if the adapter is on and the workspace is short. */
@@ -161,8 +164,8 @@ slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const voi
 
 /* Low-rank adapter term on its own (explainer 2.B: W_dense = W_sparse + L R):
  *   Y [T, N] += (X [T, K] . L [K, r]) . R [r, N]
- * The partial sums of X . L (float32) go to the workspace, which must hold
- * slope_lowrank_workspace_bytes(T, K, r) bytes.  Y (out_dt) is read and
+ * X . L and transposed copies of L and R go to the workspace, which must hold
+ * slope_lowrank_workspace_bytes(T, K, r, N) bytes.  Y (out_dt) is read and
  * written.  Errors: SLOPE_ERR_WORKSPACE if the workspace is short. */
 slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,
                                int64_t T, int64_t K, int64_t r, int64_t N, void* workspace,

@@ -43,7 +43,7 @@ _SIGS = {
     "slope_version": (ctypes.c_int, []),
     "slope_status_string": (ctypes.c_char_p, [_i32]),
     "slope_compressed_sizes": (_i32, [_i64, _i64, _P_I64, _P_I64]),
-    "slope_lowrank_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
+    "slope_lowrank_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
     "slope_prune24": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp]),
     "slope_compress24": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "slope_double_prune": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -132,9 +132,9 @@ def slope_compressed_sizes(rows: int, cols: int):
     return nv.value, nm.value
 
 
-def slope_lowrank_workspace_bytes(T: int, K: int, r: int) -> int:
+def slope_lowrank_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
     b = ctypes.c_int64()
-    _check("slope_lowrank_workspace_bytes", library().slope_lowrank_workspace_bytes(T, K, r, ctypes.byref(b)))
+    _check("slope_lowrank_workspace_bytes", library().slope_lowrank_workspace_bytes(T, K, r, N, ctypes.byref(b)))
     return b.value
 
 

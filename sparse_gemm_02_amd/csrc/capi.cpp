@@ -36,10 +36,7 @@ slope_status ptr(const void* p, bool required) {
     if (_st != SLOPE_OK) return _st;       \
   } while (0)
 
-int64_t workspace_need(int64_t T, int64_t K, int64_t r) {
-  if (T == 0 || r == 0) return 0;
-  return (int64_t)slope::lowrank_splits(T, K) * T * r * (int64_t)sizeof(float);
-}
+int64_t workspace_need(int64_t T, int64_t K, int64_t r, int64_t N) { return slope::lowrank_workspace_bytes(T, K, r, N); }
 
 }  // namespace
 
@@ -68,10 +65,10 @@ slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_value
   return SLOPE_OK;
 }
 
-slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t* bytes) {
-  if (!bytes || T < 0 || K < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
-  if (!in_range(T) || !in_range(K) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
-  *bytes = workspace_need(T, K, r);
+slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || r < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(K) || !in_range(r) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = workspace_need(T, K, r, N);
   return SLOPE_OK;
 }
 
@@ -132,21 +129,19 @@ slope_status slope_spmm_fwd(slope_dtype in_dt, slope_dtype out_dt, const void* X
   if (K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
   if (adapter) {
-    const int64_t need = workspace_need(T, K, r);
+    const int64_t need = workspace_need(T, K, r, N);
     if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
     if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
   }
   if (T == 0 || N == 0) return SLOPE_OK;
   hipStream_t s = (hipStream_t)stream;
-  float* xl = nullptr;
-  int splits = 1;
+  slope::LowrankWs w;
   if (adapter) {
-    xl = static_cast<float*>(workspace_or_null);
-    splits = slope::lowrank_splits(T, K);
-    hipError_t e = slope::launch_lowrank_down((Dt)in_dt, X, L_or_null, T, K, r, splits, xl, s);
+    w = slope::lowrank_layout((Dt)in_dt, workspace_or_null, T, K, r, N);
+    hipError_t e = slope::launch_lowrank_prepare((Dt)in_dt, X, L_or_null, R_or_null, T, K, r, N, w, s);
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
-  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, X, T, K, values_s, meta_s, N, xl, splits,
+  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, X, T, K, values_s, meta_s, N, adapter ? &w : nullptr,
                                      adapter ? r : 0, R_or_null, Y, s));
 }
 
@@ -163,8 +158,8 @@ slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void
   if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
   if (T == 0 || K == 0) return SLOPE_OK;
   // dX^T = W_dpT . dY^T: the forward kernel with reduction N and output rows K
-  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, dY, T, N, values_dpT, meta_dpT, K, nullptr, 1, 0,
-                                     nullptr, dX, (hipStream_t)stream));
+  return from_hip(slope::launch_spmm((Dt)in_dt, (Dt)out_dt, dY, T, N, values_dpT, meta_dpT, K, nullptr, 0, nullptr,
+                                     dX, (hipStream_t)stream));
 }
 
 slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const void* dY, const void* X, int64_t T,
@@ -194,16 +189,15 @@ slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void
   SLOPE_TRY(ptr(R, true));
   SLOPE_TRY(ptr(Y, true));
   if (!in_range(T) || !in_range(K) || !in_range(N) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
-  const int64_t need = workspace_need(T, K, r);
+  const int64_t need = workspace_need(T, K, r, N);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return SLOPE_ERR_ALIGN;
   if (T == 0 || N == 0 || r == 0) return SLOPE_OK;
   hipStream_t s = (hipStream_t)stream;
-  float* xl = static_cast<float*>(workspace);
-  const int splits = slope::lowrank_splits(T, K);
-  hipError_t e = slope::launch_lowrank_down((Dt)in_dt, X, L, T, K, r, splits, xl, s);
+  const slope::LowrankWs w = slope::lowrank_layout((Dt)in_dt, workspace, T, K, r, N);
+  hipError_t e = slope::launch_lowrank_prepare((Dt)in_dt, X, L, R, T, K, r, N, w, s);
   if (e != hipSuccess) return SLOPE_ERR_HIP;
-  return from_hip(slope::launch_lowrank_up_add((Dt)in_dt, (Dt)out_dt, xl, splits, R, T, r, N, Y, s));
+  return from_hip(slope::launch_lowrank_up_add((Dt)in_dt, (Dt)out_dt, w, R, T, r, N, Y, s));
 }
 
 }  // extern "C"

@@ -1,0 +1,119 @@
+// Output-tile pieces shared by the sparse GEMM and the standalone adapter
+// kernels: tile geometry, the fused low-rank adapter term and the tile store.
+//
+// A tile is the transposed output Out^T[m][t] (m = output feature, t = token)
+// held by a grid of waves in 32 x 32 MFMA accumulators.  Element v of an
+// accumulator is row 8*(v/4) + 4*(lane/32) + v%4, column lane%32 (measured
+// layout of the gfx950 32x32 MFMA family).
+#pragma once
+#include "common.h"
+
+namespace slope {
+
+template <int BM_, int BT_, int NST_, int WGM_, int WGT_>
+struct Geo {
+  static constexpr int BM = BM_, BT = BT_;
+  static constexpr int WGM = WGM_, WGT = WGT_, WAVES = WGM * WGT;  // wave grid over the tile
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WGM, WT = BT / WGT;              // wave tile
+  static constexpr int FM = WM / 32, FT = WT / 32;
+  static constexpr int KS = 64;                   // dense k per LDS stage (two sparse-MFMA k steps)
+  static constexpr int NST = NST_;                // operand stages in the LDS ring
+  // stage layout (bytes): A [BM][64] (32 compressed values per row), B [BT][128] (64 values)
+  static constexpr int A_BYTES = BM * 64, B_BYTES = BT * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  // metadata: [BM][16] = four words (two stages) per row, in a ring of two slots
+  static constexpr int META_SLOT = BM * 16, META_BYTES = 2 * META_SLOT;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES + META_BYTES;
+  // buffer-to-LDS loads (1 KB each) per wave: A and B every stage, metadata every second stage
+  static constexpr int A_DMA = A_BYTES / 1024 / WAVES, B_DMA = B_BYTES / 1024 / WAVES;
+  static constexpr int META_WAVES = META_SLOT / 1024;  // waves that load one metadata KB each
+  static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "tile/wave split");
+  static_assert(META_WAVES <= WAVES, "metadata split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// acc[fm][ft] += R^T . (X L)^T over the adapter rank, from the prepared
+// workspace: rt [Npad][rpad] (R transposed) and the hi / lo bf16 parts of
+// X . L, xlh / xll [Tpad][rpad]; both padded with zeros so no bounds checks
+// are needed.  Dense 32x32x16 MFMA: A lane l = row l%32, k = 8*(l/32)+e; B lane
+// l = column l%32, same k.  hi and lo together keep ~16 bits of X . L.
+template <class G>
+__device__ __forceinline__ void adapter_mma(f32x16 (&acc)[G::FM][G::FT], const uint16_t* __restrict__ rt,
+                                            const uint16_t* __restrict__ xlh, const uint16_t* __restrict__ xll,
+                                            int rpad, int64_t m0, int64_t t0, int wm, int wt, int lane) {
+  const int kofs = 8 * (lane >> 5);
+  for (int jk = 0; jk < rpad; jk += 16) {
+    bf16x8 ra[G::FM];
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+      const int64_t m = m0 + wm * G::WM + fm * 32 + (lane & 31);
+      ra[fm] = *reinterpret_cast<const bf16x8*>(rt + m * rpad + jk + kofs);
+    }
+#pragma unroll
+    for (int ft = 0; ft < G::FT; ++ft) {
+      const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
+      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xlh + t * rpad + jk + kofs);
+      const bf16x8 xo = *reinterpret_cast<const bf16x8*>(xll + t * rpad + jk + kofs);
+#pragma unroll
+      for (int fm = 0; fm < G::FM; ++fm) {
+        acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xh, acc[fm][ft], 0, 0, 0);
+        acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xo, acc[fm][ft], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Store the transposed tile to Out[t][m] (row-major [T, M]); four consecutive
+// accumulator elements are four consecutive m: one 8-byte (bf16) or 16-byte
+// store.  Requires M % 4 == 0.
+template <class G, typename O>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FM][G::FT], O* __restrict__ Y, int64_t m0,
+                                           int64_t t0, int M, int T, int wm, int wt, int lane) {
+#pragma unroll
+  for (int ft = 0; ft < G::FT; ++ft) {
+    const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
+    if (t >= T) continue;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + wm * G::WM + fm * 32 + 8 * q + 4 * (lane >> 5);
+        if (m >= M) continue;
+        O* p = Y + t * M + m;
+        if constexpr (sizeof(O) == 2) {
+          u32x2 w;
+          w[0] = f32_to_bf16_bits(acc[fm][ft][4 * q]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 1]) << 16);
+          w[1] = f32_to_bf16_bits(acc[fm][ft][4 * q + 2]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 3]) << 16);
+          *reinterpret_cast<u32x2*>(p) = w;
+        } else {
+          f32x4 w = {acc[fm][ft][4 * q], acc[fm][ft][4 * q + 1], acc[fm][ft][4 * q + 2], acc[fm][ft][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(p) = w;
+        }
+      }
+    }
+  }
+}
+
+// Load the transposed tile from Out[t][m] (the inverse of store_tile; rows or
+// columns outside [T, M] read as 0).
+template <class G, typename O>
+__device__ __forceinline__ void load_tile(f32x16 (&acc)[G::FM][G::FT], const O* __restrict__ Y, int64_t m0,
+                                          int64_t t0, int M, int T, int wm, int wt, int lane) {
+#pragma unroll
+  for (int ft = 0; ft < G::FT; ++ft) {
+    const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + wm * G::WM + fm * 32 + 8 * q + 4 * (lane >> 5);
+        const bool ok = t < T && m < M;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[fm][ft][4 * q + i] = ok ? load_out(Y + t * M + m + i) : 0.f;
+      }
+    }
+  }
+}
+
+}  // namespace slope

@@ -16,26 +16,40 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s);
 
-// Number of K-splits of the adapter down-projection for T tokens and reduction K.
-int lowrank_splits(int64_t T, int64_t K);
+// Adapter workspace (caller-owned device memory), carved into:
+//   part [splits][T][r] fp32   partial sums of X . L over k-splits
+//   xlh, xll [Tpad][rpad] bf16 X . L split into hi + lo bf16 parts (zero padded)
+//   lt [rpad][Kpad] bf16       L transposed (zero padded)
+//   rt [Npad][rpad] bf16       R transposed (zero padded)
+// with rpad = r rounded up to 16, Tpad/Npad rounded up to 256, Kpad to 8.
+struct LowrankWs {
+  float* part = nullptr;
+  uint16_t *xlh = nullptr, *xll = nullptr, *lt = nullptr, *rt = nullptr;
+  int splits = 1;
+  int64_t rpad = 0, Tpad = 0, Kpad = 0, Npad = 0, kc = 0;
+  bool mfma = false;  // rt / xlh / xll are filled (bf16 inputs, K % 8 == 0, r <= 128)
+};
+int64_t lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N);
+LowrankWs lowrank_layout(Dt in, void* ws, int64_t T, int64_t K, int64_t r, int64_t N);
 
-// xl[s][t][j] = partial sums of X[t, :] . L[:, j] over split s (fp32).
-hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r, int splits,
-                               float* xl, hipStream_t s);
+// Fills the workspace for Y += (X . L) . R: the k-split partial sums and, on
+// the bf16 path, the transposed L and R and the hi/lo split of X . L.
+hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const void* R, int64_t T, int64_t K,
+                                  int64_t r, int64_t N, const LowrankWs& w, hipStream_t s);
 
-// Y[t][m] = B[t, :] . Adense[m, :]  (+ sum_s xl[s][t, :] . R[:, m] when xl != nullptr)
+// Y[t][m] = B[t, :] . Adense[m, :]  (+ (X . L)[t, :] . R[:, m] when ws != nullptr)
 // with Adense the decompressed 2:4 operand [M, Kred] and B row-major [T, Kred].
 hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
-                       const uint32_t* meta, int64_t M, const float* xl, int splits, int64_t r, const void* R,
-                       void* Y, hipStream_t s);
+                       const uint32_t* meta, int64_t M, const LowrankWs* ws, int64_t r, const void* R, void* Y,
+                       hipStream_t s);
 
 // dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional accumulation.
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
                                hipStream_t s);
 
-// Y[t][m] += sum_s xl[s][t, :] . R[:, m]
-hipError_t launch_lowrank_up_add(Dt in, Dt out, const float* xl, int splits, const void* R, int64_t T, int64_t r,
+// Y[t][m] += (X . L)[t, :] . R[:, m] from a prepared workspace.
+hipError_t launch_lowrank_up_add(Dt in, Dt out, const LowrankWs& w, const void* R, int64_t T, int64_t r,
                                  int64_t N, void* Y, hipStream_t s);
 
 // Y[t][m] = 0 (empty reductions).

@@ -1,0 +1,228 @@
+// Low-rank adapter term Y += (X . L) . R (SLoPe explainer, Technical Summary
+// 2.B: W_dense = W_sparse + L R; kept unmerged at inference per the discussion
+// page's "SLoPe inference computation"; 2.C fuses it with the sparse product).
+//
+// The down-projection X . L is computed once per call into the caller's
+// workspace (partial sums over k-splits, reduced in a fixed order, so results
+// are deterministic); the up-projection is an MFMA epilogue over the rank,
+// either fused into the sparse GEMM (spmm.hip) or run here on its own.
+#include "common.h"
+#include "dma.h"
+#include "gemm_tile.h"
+#include "launch.h"
+#include "tile_map.h"
+
+namespace slope {
+
+hipError_t launch_lowrank_down_generic(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r,
+                                       int splits, int64_t kc, float* xl, hipStream_t s);
+hipError_t launch_lowrank_up_generic(Dt in, Dt out, const float* xl, int splits, const void* R, int64_t T,
+                                     int64_t r, int64_t N, void* Y, hipStream_t s);
+
+namespace {
+
+constexpr int kDownRows = 128;   // tokens per down-projection block (32 per wave)
+constexpr int kDownK = 32;       // k per MFMA step
+constexpr int kRankMax = 128;    // largest rank of the MFMA down-projection
+
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// ------------------------------------------------------------------ layout helpers
+struct Sizes {
+  int splits;
+  int64_t kc, rpad, Tpad, Kpad, Npad, part, xl, lt, rt;
+};
+
+int choose_splits(int64_t T, int64_t K) {
+  const int64_t tblocks = cdiv(T, kDownRows) < 1 ? 1 : cdiv(T, kDownRows);
+  int64_t want = cdiv(1024, tblocks);            // enough blocks to fill 256 CUs
+  if (want > 16) want = 16;
+  const int64_t ksteps = cdiv(K, 64);
+  if (want > ksteps) want = ksteps;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+Sizes sizes(int64_t T, int64_t K, int64_t r, int64_t N) {
+  Sizes z{};
+  int splits = choose_splits(T, K);
+  z.kc = round_up(cdiv(K, splits), 64);
+  z.splits = z.kc > 0 ? (int)cdiv(K, z.kc) : 1;   // every split non-empty
+  if (z.splits < 1) z.splits = 1;
+  z.rpad = round_up(r, 16);
+  z.Tpad = round_up(T, 256);
+  z.Kpad = round_up(K, 8);
+  z.Npad = round_up(N, 256);
+  z.part = round_up((int64_t)z.splits * T * r * 4, 256);
+  z.xl = round_up(z.Tpad * z.rpad * 2, 256);
+  z.lt = round_up(z.rpad * z.Kpad * 2, 256);
+  z.rt = round_up(z.Npad * z.rpad * 2, 256);
+  return z;
+}
+
+// ------------------------------------------------------------------ prepare kernels
+// lt[j][k] = L[k][j] for j < r, k < K; 0 in the padding.
+__global__ __launch_bounds__(256) void transpose_l_kernel(const uint16_t* __restrict__ L, int64_t K, int64_t r,
+                                                          int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rpad * Kpad) return;
+  const int64_t j = i / Kpad, k = i % Kpad;
+  lt[i] = (j < r && k < K) ? L[k * r + j] : (uint16_t)0;
+}
+
+// rt[n][j] = R[j][n] for j < r, n < N; 0 in the padding.
+__global__ __launch_bounds__(256) void transpose_r_kernel(const uint16_t* __restrict__ R, int64_t r, int64_t N,
+                                                          int64_t rpad, int64_t Npad, uint16_t* __restrict__ rt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Npad * rpad) return;
+  const int64_t n = i / rpad, j = i % rpad;
+  rt[i] = (j < r && n < N) ? R[j * N + n] : (uint16_t)0;
+}
+
+// part[s][t][j] = sum over k in split s of X[t][k] lt[j][k].  A wave owns 32
+// tokens (two 16-row MFMA A operands) and every rank column; operands come
+// straight from global memory (16 contiguous bytes per lane).  Dense 16x16x32
+// MFMA: A lane l = row l%16, k = 8*(l/16)+e; B lane l = column l%16, same k;
+// D lane l = column l%16, rows 4*(l/16)+v.
+__global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ lt, int T, int K, int r,
+                                                           int rpad, int Kpad, int kc, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = blockIdx.y;
+  const int64_t tw = (int64_t)blockIdx.x * kDownRows + wave * 32;   // first token of this wave
+  const int kb = s * kc, ke = (kb + kc < K) ? kb + kc : K;
+  const int nj = rpad / 16;
+  // tokens past T read as 0 through the resource bound; k past the split is masked
+  const int64_t rows_left = (int64_t)T - tw;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (rows_left > 0 ? tw : 0) * K, rows_left > 0 ? rows_left * K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lt, (int64_t)rpad * Kpad * 2);
+  const int kl = 8 * (lane >> 4);
+  const uint32_t xa0 = (uint32_t)((lane & 15) * K) * 2, xa1 = (uint32_t)((16 + (lane & 15)) * K) * 2;
+  f32x4 acc0[kRankMax / 16], acc1[kRankMax / 16];
+#pragma unroll
+  for (int j = 0; j < kRankMax / 16; ++j) acc0[j] = acc1[j] = f32x4{};
+  for (int k0 = kb; k0 < ke; k0 += kDownK) {
+    const int k = k0 + kl;
+    const bool ok = k + 8 <= ke;
+    const u32x4 a0 = load16(rx, ok ? xa0 + k * 2 : kOutOfRange);
+    const u32x4 a1 = load16(rx, ok ? xa1 + k * 2 : kOutOfRange);
+#pragma unroll
+    for (int jb = 0; jb < kRankMax / 16; ++jb) {
+      if (jb < nj) {
+        const uint32_t lo = (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2;
+        const u32x4 b = load16(rl, ok ? lo : kOutOfRange);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, b);
+        acc0[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bb, acc0[jb], 0, 0, 0);
+        acc1[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bb, acc1[jb], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int jb = 0; jb < kRankMax / 16; ++jb) {
+    if (jb >= nj) break;
+    const int j = jb * 16 + (lane & 15);
+    if (j >= r) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t0 = tw + 4 * (lane >> 4) + v, t1 = t0 + 16;
+      if (t0 < T) part[((int64_t)s * T + t0) * r + j] = acc0[jb][v];
+      if (t1 < T) part[((int64_t)s * T + t1) * r + j] = acc1[jb][v];
+    }
+  }
+}
+
+// xl = sum over splits of part (in split order), split into bf16 hi + lo with
+// hi = rne(xl), lo = rne(xl - hi); zero in the padding.
+__global__ __launch_bounds__(256) void reduce_split_kernel(const float* __restrict__ part, int splits, int64_t T,
+                                                           int64_t r, int64_t rpad, int64_t Tpad,
+                                                           uint16_t* __restrict__ xlh, uint16_t* __restrict__ xll) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Tpad * rpad) return;
+  const int64_t t = i / rpad, j = i % rpad;
+  float x = 0.f;
+  if (t < T && j < r)
+    for (int s = 0; s < splits; ++s) x += part[((int64_t)s * T + t) * r + j];
+  const uint16_t hi = f32_to_bf16_bits(x);
+  xlh[i] = hi;
+  xll[i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// ------------------------------------------------------------------ standalone up-projection
+// Y[t][m] += (X . L)[t] . R[:, m] over one 256 x 256 output tile.
+template <class G, typename O>
+__global__ __launch_bounds__(G::THREADS, 1) void lowrank_up_add_kernel(const uint16_t* __restrict__ rt,
+                                                                       const uint16_t* __restrict__ xlh,
+                                                                       const uint16_t* __restrict__ xll, int rpad,
+                                                                       int T, int M, O* __restrict__ Y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % G::WGM, wt = wave / G::WGM;
+  const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
+  int tm, tt;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
+  const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
+  f32x16 acc[G::FM][G::FT];
+  load_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
+  adapter_mma<G>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
+  store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
+}
+
+typedef Geo<256, 256, 3, 2, 4> GeoUp;
+
+unsigned blocks_for(int64_t n) { return (unsigned)cdiv(n, 256); }
+
+}  // namespace
+
+int64_t lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N) {
+  if (T == 0 || r == 0) return 0;
+  const Sizes z = sizes(T, K, r, N);
+  return z.part + 2 * z.xl + z.lt + z.rt;
+}
+
+LowrankWs lowrank_layout(Dt in, void* ws, int64_t T, int64_t K, int64_t r, int64_t N) {
+  const Sizes z = sizes(T, K, r, N);
+  LowrankWs w;
+  char* p = static_cast<char*>(ws);
+  w.part = reinterpret_cast<float*>(p);
+  w.xlh = reinterpret_cast<uint16_t*>(p + z.part);
+  w.xll = reinterpret_cast<uint16_t*>(p + z.part + z.xl);
+  w.lt = reinterpret_cast<uint16_t*>(p + z.part + 2 * z.xl);
+  w.rt = reinterpret_cast<uint16_t*>(p + z.part + 2 * z.xl + z.lt);
+  w.splits = z.splits;
+  w.rpad = z.rpad;
+  w.Tpad = z.Tpad;
+  w.Kpad = z.Kpad;
+  w.Npad = z.Npad;
+  w.kc = z.kc;
+  w.mfma = in == Dt::BF16 && K % 8 == 0 && r <= kRankMax;
+  return w;
+}
+
+hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const void* R, int64_t T, int64_t K,
+                                  int64_t r, int64_t N, const LowrankWs& w, hipStream_t s) {
+  if (!w.mfma) return launch_lowrank_down_generic(in, X, L, T, K, r, w.splits, w.kc, w.part, s);
+  // bf16: transposed L and R, the split down-projection, the hi/lo reduction
+  transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
+  transpose_r_kernel<<<blocks_for(w.Npad * w.rpad), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
+  dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
+  lowrank_down_kernel<<<grid, 256, 0, s>>>((const uint16_t*)X, w.lt, (int)T, (int)K, (int)r, (int)w.rpad,
+                                           (int)w.Kpad, (int)w.kc, w.part);
+  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
+                                                                  w.xll);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_up_add(Dt in, Dt out, const LowrankWs& w, const void* R, int64_t T, int64_t r,
+                                 int64_t N, void* Y, hipStream_t s) {
+  if (!w.mfma || N % 4 != 0) return launch_lowrank_up_generic(in, out, w.part, w.splits, R, T, r, N, Y, s);
+  typedef GeoUp G;
+  const int64_t nb = cdiv(N, G::BM) * cdiv(T, G::BT);
+  if (out == Dt::BF16)
+    lowrank_up_add_kernel<G, uint16_t><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad, (int)T,
+                                                                          (int)N, (uint16_t*)Y);
+  else
+    lowrank_up_add_kernel<G, float><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad, (int)T,
+                                                                       (int)N, (float*)Y);
+  return hipGetLastError();
+}
+
+}  // namespace slope

@@ -24,193 +24,139 @@
 #include "common.h"
 #include "launch.h"
 #include "tile_map.h"
+#include "dma.h"
+#include "gemm_tile.h"
 
 namespace slope {
 
 hipError_t launch_spmm_generic(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
                                const uint32_t* meta, int64_t M, const float* xl, int splits, int64_t r,
                                const void* R, void* Y, hipStream_t s);
-hipError_t launch_lowrank_down_generic(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r,
-                                       int splits, int64_t kc, float* xl, hipStream_t s);
-hipError_t launch_lowrank_up_generic(Dt in, Dt out, const float* xl, int splits, const void* R, int64_t T,
-                                     int64_t r, int64_t N, void* Y, hipStream_t s);
 
 namespace {
 
-constexpr int kThreads = 256;
-
-// ------------------------------------------------------------------ tile geometry
-template <int BM_, int BT_>
-struct Geo {
-  static constexpr int BM = BM_, BT = BT_;
-  static constexpr int WM = BM / 2, WT = BT / 2;  // 2 x 2 waves
-  static constexpr int FM = WM / 32, FT = WT / 32;
-  static constexpr int KS = 64;                   // dense k per LDS stage
-  static constexpr int AP = 40;                   // A row pitch (bf16): 32 values + 8 pad
-  static constexpr int BP = 72;                   // B row pitch (bf16): 64 values + 8 pad
-  static constexpr int A_ELEMS = BM * AP, B_ELEMS = BT * BP, META_WORDS = 2 * BM;
-  static constexpr int STAGE_BYTES = A_ELEMS * 2 + B_ELEMS * 2 + META_WORDS * 4;
-  static constexpr int NA = BM * 4 / kThreads;    // 16-byte A chunks per thread per stage
-  static constexpr int NB = BT * 8 / kThreads;    // 16-byte B chunks per thread per stage
-  static constexpr int NMETA = 2 * BM / kThreads; // metadata words per thread per stage
-  // adapter epilogue staging (reuses the operand buffers)
-  static constexpr int RC = 32, RP = 40;
-  static constexpr int ADAPTER_BYTES = (BM + 2 * BT) * RP * 2;
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > ADAPTER_BYTES) ? 2 * STAGE_BYTES : ADAPTER_BYTES;
-};
-
-// ------------------------------------------------------------------ adapter epilogue
-// acc[fm][ft] (rows m, columns t of the transposed tile) += R^T . XL^T, with
-// XL summed over its k-splits in fixed order and split into bf16 hi + lo
-// parts so that the product keeps ~16 bits of XL.  Dense 32x32x16 MFMA:
-// A lane l = row l%32, k = 8*(l/32)+e; B lane l = column l%32, same k.
-template <class G>
-__device__ __forceinline__ void adapter_accumulate(f32x16 (&acc)[G::FM][G::FT], char* lds, int64_t m0, int64_t t0,
-                                                   int M, int T, const float* __restrict__ xl, int splits, int r,
-                                                   const uint16_t* __restrict__ R, int wm, int wt, int lane) {
-  uint16_t* Rt = reinterpret_cast<uint16_t*>(lds);        // [BM][RP]
-  uint16_t* Xh = Rt + G::BM * G::RP;                       // [BT][RP]
-  uint16_t* Xl = Xh + G::BT * G::RP;                       // [BT][RP]
-  const int tid = threadIdx.x;
-  for (int j0 = 0; j0 < r; j0 += G::RC) {
-    __syncthreads();
-    for (int i = tid; i < G::BM * G::RC; i += kThreads) {
-      const int m = i % G::BM, jj = i / G::BM;
-      const int64_t gm = m0 + m;
-      uint16_t v = 0;
-      if (j0 + jj < r && gm < M) v = R[(int64_t)(j0 + jj) * M + gm];
-      Rt[m * G::RP + jj] = v;
-    }
-    for (int i = tid; i < G::BT * G::RC; i += kThreads) {
-      const int jj = i % G::RC, t = i / G::RC;
-      const int64_t gt = t0 + t;
-      float x = 0.f;
-      if (j0 + jj < r && gt < T)
-        for (int s = 0; s < splits; ++s) x += xl[((int64_t)s * T + gt) * r + j0 + jj];
-      const uint16_t hi = f32_to_bf16_bits(x);
-      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      Xh[t * G::RP + jj] = hi;
-      Xl[t * G::RP + jj] = lo;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jk = 0; jk < G::RC / 16; ++jk) {
-      bf16x8 ra[G::FM];
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm)
-        ra[fm] = *reinterpret_cast<const bf16x8*>(Rt + (wm * G::WM + fm * 32 + (lane & 31)) * G::RP + jk * 16 + 8 * (lane >> 5));
-#pragma unroll
-      for (int ft = 0; ft < G::FT; ++ft) {
-        const int row = (wt * G::WT + ft * 32 + (lane & 31)) * G::RP + jk * 16 + 8 * (lane >> 5);
-        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(Xh + row);
-        const bf16x8 xlo = *reinterpret_cast<const bf16x8*>(Xl + row);
-#pragma unroll
-        for (int fm = 0; fm < G::FM; ++fm) {
-          acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xh, acc[fm][ft], 0, 0, 0);
-          acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xlo, acc[fm][ft], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-// Store the transposed tile: element v of acc[fm][ft] is Out[t][m] with
-// m = m0 + wm*WM + fm*32 + 8*(v/4) + 4*(lane/32) + v%4, t = t0 + wt*WT + ft*32 + lane%32.
-// Four consecutive v are four consecutive m: one 8-byte (bf16) or 16-byte store.
-template <class G, typename O>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FM][G::FT], O* __restrict__ Y, int64_t m0,
-                                           int64_t t0, int M, int T, int wm, int wt, int lane) {
-#pragma unroll
-  for (int ft = 0; ft < G::FT; ++ft) {
-    const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
-    if (t >= T) continue;
-#pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t m = m0 + wm * G::WM + fm * 32 + 8 * q + 4 * (lane >> 5);
-        if (m >= M) continue;
-        O* p = Y + t * M + m;
-        if constexpr (sizeof(O) == 2) {
-          u32x2 w;
-          w[0] = f32_to_bf16_bits(acc[fm][ft][4 * q]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 1]) << 16);
-          w[1] = f32_to_bf16_bits(acc[fm][ft][4 * q + 2]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 3]) << 16);
-          *reinterpret_cast<u32x2*>(p) = w;
-        } else {
-          f32x4 w = {acc[fm][ft][4 * q], acc[fm][ft][4 * q + 1], acc[fm][ft][4 * q + 2], acc[fm][ft][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(p) = w;
-        }
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ main kernel
 // Requirements (checked on the host): Kred % 16 == 0, M % 4 == 0, 16-byte
-// aligned base pointers.  Ragged M, T and Kred % 64 are zero-filled.
+// aligned base pointers.  Operands stream through a ring of NST LDS stages
+// filled by buffer loads that write LDS directly; rows past M or T and k past
+// Kred read as 0 through the resources' bounds, so every load is unconditional.
+//
+// Each stage covers 64 dense k: a 64-byte segment of every compressed A row
+// and a 128-byte segment of every B row, so each row of the tile costs one
+// cache line per stage.  The metadata of a row (4 bytes per 32 k) comes four
+// words at a time, every second stage.
+//
+// LDS granule swizzles keep fragment reads free of bank conflicts (measured on
+// gfx950: 64 four-byte banks, a 128-bit read serves 16 lanes per pass, so the
+// 16 rows of a pass must hit distinct 16-byte granules modulo 256 bytes):
+// A row r keeps 16-byte granule c at c ^ ((r>>2)&3), B row r keeps granule c
+// at c ^ ((r^(r>>3))&7).
+//
+// Schedule per stage s (one barrier): read the second k-step's fragments of s,
+// issue the first k-step's MFMAs, wait for stage s+1 and barrier, start the
+// loads of stage s+NST-1 into the slot stage s-1 used, read the first k-step's
+// fragments of s+1, issue the second k-step's MFMAs.
 template <class G, bool ADAPTER, typename O>
-__global__ __launch_bounds__(kThreads, 1) void spmm_smfmac_kernel(
+__global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
-    int T, int Kred, const float* __restrict__ xl, int splits, int r, const uint16_t* __restrict__ R,
-    O* __restrict__ Y) {
+    int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
+    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wt = wave >> 1;
+  const int wm = wave % G::WGM, wt = wave / G::WGM;
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
   const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
-  const int64_t vpitch = Kred / 2;                  // compressed values per row
   const int wpr = (Kred / 4 + 7) / 8;               // metadata words per row
   const int stages = (Kred + G::KS - 1) / G::KS;
+  const int rows_m = (int)((M - m0) < G::BM ? (M - m0) : G::BM);
+  const int rows_t = (int)((T - t0) < G::BT ? (T - t0) : G::BT);
 
-  u32x4 pa[G::NA], pb[G::NB];
-  uint32_t pm[G::NMETA];
+  // resources cover exactly this block's valid rows
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(vals + m0 * (Kred / 2), (int64_t)rows_m * Kred);
+  const __amdgpu_buffer_rsrc_t rmeta = make_rsrc(meta + m0 * wpr, (int64_t)rows_m * wpr * 4);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + t0 * Kred, (int64_t)rows_t * Kred * 2);
 
-  auto load = [&](int s) {
+  char* const meta_lds = lds + G::NST * G::STAGE_BYTES;
+  // per-lane DMA sources (stage 0); stage s adds s*64 (A) / s*128 (B) bytes
+  uint32_t a_src[G::A_DMA], b_src[G::B_DMA];
+  int a_k[G::A_DMA], b_k[G::B_DMA];
 #pragma unroll
-    for (int i = 0; i < G::NA; ++i) {
-      const int c = tid + kThreads * i, row = c >> 2, p = c & 3;
-      const int64_t gm = m0 + row;
-      const int kd = s * G::KS + 16 * p;           // first dense k of this chunk
-      pa[i] = (gm < M && kd + 16 <= Kred)
-                  ? *reinterpret_cast<const u32x4*>(vals + gm * vpitch + (kd >> 1))
-                  : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < G::A_DMA; ++j) {
+    const int row = wave * (G::BM / G::WAVES) + j * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    a_src[j] = (uint32_t)row * Kred + c * 16;
+    a_k[j] = c * 16;                                // compressed bytes of the granule within the stage
+  }
+#pragma unroll
+  for (int j = 0; j < G::B_DMA; ++j) {
+    const int row = wave * (G::BT / G::WAVES) + j * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    b_src[j] = (uint32_t)row * Kred * 2 + c * 16;
+    b_k[j] = c * 8;                                 // first k of the granule within the stage
+  }
+  const uint32_t m_src = (uint32_t)(wave * 64 + lane) * wpr * 4;   // waves < META_WAVES
+
+  auto issue = [&](int s) {
+    char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < G::A_DMA; ++j) {
+      const bool ok = s * 64 + a_k[j] < Kred;        // compressed bytes of a row = Kred
+      dma16(ra, base + wave * (G::A_BYTES / G::WAVES) + j * 1024, ok ? a_src[j] + s * 64 : kOutOfRange);
     }
 #pragma unroll
-    for (int i = 0; i < G::NB; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, p = c & 7;
-      const int64_t gt = t0 + row;
-      const int kd = s * G::KS + 8 * p;
-      pb[i] = (gt < T && kd + 8 <= Kred) ? *reinterpret_cast<const u32x4*>(Bm + gt * Kred + kd)
-                                         : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < G::B_DMA; ++j) {
+      const bool ok = s * 64 + b_k[j] < Kred;
+      dma16(rb, base + G::A_BYTES + wave * (G::B_BYTES / G::WAVES) + j * 1024, ok ? b_src[j] + s * 128 : kOutOfRange);
     }
-#pragma unroll
-    for (int i = 0; i < G::NMETA; ++i) {
-      const int c = tid + kThreads * i, row = c % G::BM, w = c / G::BM;
-      const int64_t gm = m0 + row;
-      const int wi = 2 * s + w;
-      pm[i] = (gm < M && wi < wpr) ? meta[gm * wpr + wi] : 0u;
+    if ((s & 1) == 0 && wave < G::META_WAVES) {      // words 2s .. 2s+3 of every row
+      const bool ok = 2 * s < wpr;
+      dma16(rmeta, meta_lds + ((s >> 1) & 1) * G::META_SLOT + wave * 1024, ok ? m_src + s * 8 : kOutOfRange);
     }
   };
-  auto store = [&](int buf) {
-    uint16_t* A = reinterpret_cast<uint16_t*>(lds + buf * G::STAGE_BYTES);
-    uint16_t* B = A + G::A_ELEMS;
-    uint32_t* Mt = reinterpret_cast<uint32_t*>(B + G::B_ELEMS);
+
+  // per-lane fragment offsets inside a stage (k-step ks adds nothing to the
+  // row, only selects granules)
+  int a_off[2][G::FM], m_off[G::FM], b_off[2][G::FT][2];
 #pragma unroll
-    for (int i = 0; i < G::NA; ++i) {
-      const int c = tid + kThreads * i, row = c >> 2, p = c & 3;
-      *reinterpret_cast<u32x4*>(A + row * G::AP + 8 * p) = pa[i];
+  for (int fm = 0; fm < G::FM; ++fm) {
+    const int row = wm * G::WM + fm * 32 + (lane & 31);
+    const int sw = (row >> 2) & 3;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a_off[ks][fm] = row * 64 + (((2 * ks + (lane >> 5)) ^ sw) * 16);
+    m_off[fm] = row * 16;
+  }
+#pragma unroll
+  for (int ft = 0; ft < G::FT; ++ft) {
+    const int row = wt * G::WT + ft * 32 + (lane & 31);
+    const int sw = (row ^ (row >> 3)) & 7;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      b_off[ks][ft][0] = G::A_BYTES + row * 128 + (((4 * ks + (lane >> 5)) ^ sw) * 16);
+      b_off[ks][ft][1] = G::A_BYTES + row * 128 + (((4 * ks + 2 + (lane >> 5)) ^ sw) * 16);
+    }
+  }
+  const int ix_shift = 16 * (lane >> 5);
+
+  struct Frags {
+    bf16x8 a[G::FM];
+    int ix[G::FM];
+    bf16x16 b[G::FT];
+  };
+  auto read_frags = [&](Frags& f, int s, int ks) {
+    const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+    const char* mbase = meta_lds + ((s >> 1) & 1) * G::META_SLOT + ((s & 1) * 2 + ks) * 4;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+      f.a[fm] = *reinterpret_cast<const bf16x8*>(base + a_off[ks][fm]);
+      f.ix[fm] = (int)(*reinterpret_cast<const uint32_t*>(mbase + m_off[fm]) >> ix_shift);
     }
 #pragma unroll
-    for (int i = 0; i < G::NB; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, p = c & 7;
-      *reinterpret_cast<u32x4*>(B + row * G::BP + 8 * p) = pb[i];
-    }
-#pragma unroll
-    for (int i = 0; i < G::NMETA; ++i) {
-      const int c = tid + kThreads * i;
-      Mt[c] = pm[i];  // [w][row]
+    for (int ft = 0; ft < G::FT; ++ft) {
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(base + b_off[ks][ft][0]);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(base + b_off[ks][ft][1]);
+      f.b[ft] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
   };
 
@@ -219,204 +165,73 @@ __global__ __launch_bounds__(kThreads, 1) void spmm_smfmac_kernel(
   for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
     for (int ft = 0; ft < G::FT; ++ft) acc[fm][ft] = f32x16{};
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int ft = 0; ft < G::FT; ++ft)
+#pragma unroll
+      for (int fm = 0; fm < G::FM; ++fm)
+        acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm], 0, 0);
+  };
 
-  if (stages > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
+  // prologue: stages 0 .. NST-2 in flight; stage 0 landed and visible
+#pragma unroll
+  for (int p = 0; p < G::NST - 1; ++p) issue(p);
+  wait_vmcnt<0>();
+  barrier();
+  Frags f0, f1;
+  read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < stages) load(s + 1);
-    const uint16_t* A = reinterpret_cast<const uint16_t*>(lds + buf * G::STAGE_BYTES);
-    const uint16_t* B = A + G::A_ELEMS;
-    const uint32_t* Mt = reinterpret_cast<const uint32_t*>(B + G::B_ELEMS);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[G::FM];
-      int ix[G::FM];
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm) {
-        const int row = wm * G::WM + fm * 32 + (lane & 31);
-        af[fm] = *reinterpret_cast<const bf16x8*>(A + row * G::AP + ks * 16 + 8 * (lane >> 5));
-        ix[fm] = (int)(Mt[ks * G::BM + row] >> (16 * (lane >> 5)));
-      }
-#pragma unroll
-      for (int ft = 0; ft < G::FT; ++ft) {
-        const int col = wt * G::WT + ft * 32 + (lane & 31);
-        const uint16_t* bp = B + col * G::BP + ks * 32 + 8 * (lane >> 5);
-        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(bp);
-        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(bp + 16);
-        const bf16x16 bfrag = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-#pragma unroll
-        for (int fm = 0; fm < G::FM; ++fm)
-          acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[fm], bfrag, acc[fm][ft], ix[fm], 0, 0);
-      }
-    }
-    if (s + 1 < stages) store(buf ^ 1);
-    __syncthreads();
+    read_frags(f1, s, 1);
+    mma(f0);
+    // keep the first k-step's MFMAs ahead of the wait: they run while it waits
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();                                  // this wave's loads of stage s+1 (and s+2..) landed
+    barrier();                                        // everyone's have; stage s-1 fully consumed
+    issue(s + G::NST - 1);                            // past the last stage these read as 0
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < stages) read_frags(f0, s + 1, 0);
+    mma(f1);
   }
-  if constexpr (ADAPTER) adapter_accumulate<G>(acc, lds, m0, t0, M, T, xl, splits, r, R, wm, wt, lane);
+  wait_vmcnt<0>();
+  if constexpr (ADAPTER) adapter_mma<G>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
   store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
 }
 
-// ------------------------------------------------------------------ standalone adapter
-// Y[t][m] += XL[t] . R[:, m] over one output tile: the same epilogue with the
-// accumulators loaded from Y.
-template <class G, typename O>
-__global__ __launch_bounds__(kThreads, 1) void lowrank_up_add_kernel(const float* __restrict__ xl, int splits,
-                                                                     const uint16_t* __restrict__ R, int T, int r,
-                                                                     int M, O* __restrict__ Y) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wt = wave >> 1;
-  const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
-  int tm, tt;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
-  const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
-  f32x16 acc[G::FM][G::FT];
-#pragma unroll
-  for (int ft = 0; ft < G::FT; ++ft) {
-    const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
-#pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * G::WM + fm * 32 + 8 * (v / 4) + 4 * (lane >> 5) + v % 4;
-        acc[fm][ft][v] = (t < T && m < M) ? load_out(Y + t * M + m) : 0.f;
-      }
-  }
-  adapter_accumulate<G>(acc, lds, m0, t0, M, T, xl, splits, r, R, wm, wt, lane);
-  store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
-}
-
-// ------------------------------------------------------------------ down projection
-// xl[s][t][j] = sum over split s of X[t][k] L[k][j].  Block: 64 tokens (16 per
-// wave) x one k-split; L staged transposed in LDS per 64-wide k step; dense
-// 16x16x32 MFMA (A lane l = row l%16, k = 8*(l/16)+e; B lane l = column l%16,
-// same k; D lane l = column l%16, rows 4*(l/16)+v).
-constexpr int LD_TT = 64, LD_KS = 64, LD_LP = 72, LD_RMAX = 128;
-
-__global__ __launch_bounds__(kThreads) void lowrank_down_kernel(const uint16_t* __restrict__ X,
-                                                                const uint16_t* __restrict__ L, int T, int K, int r,
-                                                                int kc, float* __restrict__ xl) {
-  __shared__ __attribute__((aligned(16))) uint16_t Lt[LD_RMAX * LD_LP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * LD_TT + wave * 16;
-  const int kbeg = s * kc, kend = (kbeg + kc < K) ? kbeg + kc : K;
-  const int rpad = (r + 15) & ~15;
-  const int nj = rpad / 16;
-  f32x4 acc[LD_RMAX / 16];
-#pragma unroll
-  for (int j = 0; j < LD_RMAX / 16; ++j) acc[j] = f32x4{};
-  const int64_t trow = t0 + (lane & 15);
-  for (int k0 = kbeg; k0 < kend; k0 += LD_KS) {
-    __syncthreads();
-    for (int i = tid; i < LD_KS * rpad; i += kThreads) {
-      const int kk = i / rpad, j = i % rpad;
-      const int k = k0 + kk;
-      Lt[j * LD_LP + kk] = (j < r && k < kend) ? L[(int64_t)k * r + j] : (uint16_t)0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-      const int k = k0 + kk2 * 32 + 8 * (lane >> 4);
-      const bf16x8 a = (trow < T && k + 8 <= kend) ? *reinterpret_cast<const bf16x8*>(X + trow * K + k) : bf16x8{};
-#pragma unroll
-      for (int jb = 0; jb < LD_RMAX / 16; ++jb) {
-        if (jb < nj) {
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(Lt + (jb * 16 + (lane & 15)) * LD_LP + kk2 * 32 + 8 * (lane >> 4));
-          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[jb], 0, 0, 0);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int jb = 0; jb < LD_RMAX / 16; ++jb) {
-    if (jb >= nj) break;
-    const int j = jb * 16 + (lane & 15);
-    if (j >= r) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t t = t0 + 4 * (lane >> 4) + v;
-      if (t < T) xl[((int64_t)s * T + t) * r + j] = acc[jb][v];
-    }
-  }
-}
-
-typedef Geo<256, 256> GeoBig;
+typedef Geo<256, 256, 3, 2, 4> GeoBig;
 
 template <bool ADAPTER, typename O>
 hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
-                      const float* xl, int splits, int r, const uint16_t* R, O* Y, hipStream_t s) {
+                      const LowrankWs* w, O* Y, hipStream_t s) {
   typedef GeoBig G;
   auto kern = spmm_smfmac_kernel<G, ADAPTER, O>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process (thread-safe static initialisation)
+  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const int64_t nb = cdiv(M, G::BM) * cdiv(T, G::BT);
-  kern<<<(unsigned)nb, kThreads, G::LDS_BYTES, s>>>(B, vals, meta, M, T, Kred, xl, splits, r, R, Y);
+  kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(B, vals, meta, M, T, Kred, w ? w->rt : nullptr,
+                                                     w ? w->xlh : nullptr, w ? w->xll : nullptr,
+                                                     w ? (int)w->rpad : 0, Y);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int lowrank_splits(int64_t T, int64_t K) {
-  const int64_t tblocks = cdiv(T, LD_TT);
-  int64_t want = cdiv(1024, tblocks < 1 ? 1 : tblocks);
-  if (want > 16) want = 16;
-  const int64_t ksteps = cdiv(K, LD_KS);
-  if (want > ksteps) want = ksteps;
-  if (want < 1) want = 1;
-  const int64_t kc = cdiv(cdiv(K, want), LD_KS) * LD_KS;
-  return kc > 0 ? (int)cdiv(K, kc) : 1;
-}
-
-static int64_t split_width(int64_t K, int splits) { return cdiv(cdiv(K, splits), LD_KS) * LD_KS; }
-
-hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r, int splits,
-                               float* xl, hipStream_t s) {
-  const int64_t kc = split_width(K, splits);
-  if (in == Dt::BF16 && K % 8 == 0 && r <= LD_RMAX) {
-    dim3 grid((unsigned)cdiv(T, LD_TT), (unsigned)splits);
-    lowrank_down_kernel<<<grid, kThreads, 0, s>>>((const uint16_t*)X, (const uint16_t*)L, (int)T, (int)K, (int)r,
-                                                  (int)kc, xl);
-    return hipGetLastError();
-  }
-  return launch_lowrank_down_generic(in, X, L, T, K, r, splits, kc, xl, s);
-}
-
 hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
-                       const uint32_t* meta, int64_t M, const float* xl, int splits, int64_t r, const void* R,
-                       void* Y, hipStream_t s) {
-  const bool fast = in == Dt::BF16 && Kred % 16 == 0 && M % 4 == 0;
-  if (!fast) return launch_spmm_generic(in, out, B, T, Kred, values, meta, M, xl, splits, r, R, Y, s);
-  const bool ad = xl != nullptr && r > 0;
+                       const uint32_t* meta, int64_t M, const LowrankWs* ws, int64_t r, const void* R, void* Y,
+                       hipStream_t s) {
+  // block resources stay below 2 GiB: 256 rows x Kred x 2 bytes
+  const bool fast = in == Dt::BF16 && Kred % 16 == 0 && M % 4 == 0 && Kred <= (1 << 21);
+  const bool ad = ws != nullptr && r > 0;
+  if (!fast || (ad && !ws->mfma))
+    return launch_spmm_generic(in, out, B, T, Kred, values, meta, M, ad ? ws->part : nullptr, ad ? ws->splits : 1,
+                               ad ? r : 0, R, Y, s);
   const uint16_t* Bb = (const uint16_t*)B;
   const uint16_t* vb = (const uint16_t*)values;
-  const uint16_t* Rb = (const uint16_t*)R;
   if (out == Dt::BF16)
-    return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, xl, splits, (int)r, Rb, (uint16_t*)Y, s)
-              : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, xl, splits, (int)r, Rb, (uint16_t*)Y, s);
-  return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, xl, splits, (int)r, Rb, (float*)Y, s)
-            : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, xl, splits, (int)r, Rb, (float*)Y, s);
-}
-
-hipError_t launch_lowrank_up_add(Dt in, Dt out, const float* xl, int splits, const void* R, int64_t T, int64_t r,
-                                 int64_t N, void* Y, hipStream_t s) {
-  if (in != Dt::BF16 || N % 4 != 0) return launch_lowrank_up_generic(in, out, xl, splits, R, T, r, N, Y, s);
-  typedef GeoBig G;
-  const int64_t nb = cdiv(N, G::BM) * cdiv(T, G::BT);
-  const int lds = G::ADAPTER_BYTES;
-  if (out == Dt::BF16)
-    lowrank_up_add_kernel<G, uint16_t><<<(unsigned)nb, kThreads, lds, s>>>(xl, splits, (const uint16_t*)R, (int)T, (int)r, (int)N, (uint16_t*)Y);
-  else
-    lowrank_up_add_kernel<G, float><<<(unsigned)nb, kThreads, lds, s>>>(xl, splits, (const uint16_t*)R, (int)T, (int)r, (int)N, (float*)Y);
-  return hipGetLastError();
+    return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (uint16_t*)Y, s)
+              : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (uint16_t*)Y, s);
+  return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (float*)Y, s)
+            : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (float*)Y, s);
 }
 
 }  // namespace slope

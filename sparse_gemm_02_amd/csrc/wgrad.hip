@@ -21,6 +21,7 @@
 #include "common.h"
 #include "launch.h"
 #include "tile_map.h"
+#include "dma.h"
 
 namespace slope {
 
@@ -31,17 +32,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int BK_, int BN_>
+template <int BK_, int BN_, int NST_, int WGK_, int WGN_>
 struct WGeo {
   static constexpr int BK = BK_, BN = BN_;         // tile rows (k) x columns (n) of dW^T
-  static constexpr int WK = BK / 2, WN = BN / 2;   // 2 x 2 waves
+  static constexpr int WGK = WGK_, WGN = WGN_, WAVES = WGK * WGN, THREADS = 64 * WAVES;
+  static constexpr int WK = BK / WGK, WN = BN / WGN;  // wave tile
   static constexpr int FK = WK / 32, FN = WN / 32;
   static constexpr int TS = 32;                    // tokens per LDS stage (two 16-deep MFMA steps)
-  static constexpr int XP = BK + 16, DP = BN + 16; // row pitches (bf16); 8 banks of skew per row
-  static constexpr int X_ELEMS = TS * XP, D_ELEMS = TS * DP;
-  static constexpr int STAGE_BYTES = (X_ELEMS + D_ELEMS) * 2;
-  static constexpr int NX = TS * BK / 8 / kThreads, ND = TS * BN / 8 / kThreads;  // 16-byte chunks per thread
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int NST = NST_;                 // stages in the LDS ring
+  static constexpr int XROW = BK * 2, DROW = BN * 2;              // bytes per token row of each tile
+  static constexpr int X_BYTES = TS * XROW, D_BYTES = TS * DROW;
+  static constexpr int STAGE_BYTES = X_BYTES + D_BYTES;
+  static constexpr int X_DMA = X_BYTES / 1024 / WAVES, D_DMA = D_BYTES / 1024 / WAVES;  // per wave per stage
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static_assert(XROW == 512 && DROW == 512, "DMA mapping assumes 512-byte token rows");
 };
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -72,66 +76,89 @@ __device__ __forceinline__ void store_quad(float* p, const float (&x)[4], int ac
   *reinterpret_cast<f32x4*>(p) = y;
 }
 
-// Eight consecutive tokens (rows tb .. tb+7) of column c0 + (lane % 32) of a
-// row-major LDS tile, as an MFMA operand fragment (two transposing loads).
-__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* tile, int pitch, int tb, int c0, int lane) {
+// Operand fragment from a token-major LDS tile: eight consecutive tokens (rows
+// tb .. tb+7) of column c0 + (lane % 32), with two transposing loads.  Tile rows
+// are 512 bytes; row r keeps its 16-byte granule q at q ^ ((r & 3) << 2), which
+// puts the four rows a 32-lane pass of the transposing load touches in four
+// different 64-byte bank groups.
+__device__ __forceinline__ bf16x8 frag_tr(const char* tile, int tb, int c0, int lane) {
   const int g = lane >> 4, j = lane & 15;
-  const int c = c0 + 16 * (g & 1) + 4 * (j & 3);
+  const int col = c0 + 16 * (g & 1) + 4 * (j & 3);      // element column of this lane's 4 values
   const int t = tb + 8 * (g >> 1) + (j >> 2);
-  const uint16_t* p0 = tile + t * pitch + c;
-  const uint16_t* p1 = p0 + 4 * pitch;
+  const int q = col >> 3, within = (col & 7) * 2;
+  const char* p0 = tile + t * 512 + ((q ^ ((t & 3) << 2)) << 4) + within;
+  const char* p1 = tile + (t + 4) * 512 + ((q ^ (((t + 4) & 3) << 2)) << 4) + within;
   s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
   s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  s16x4 lo = a, hi = b;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
 // Requirements (host-checked): K % 8 == 0, N % 8 == 0, 16-byte aligned bases.
+// Token rows of both operands stream through a ring of NST LDS stages filled
+// by buffer loads that write LDS directly (one barrier per stage, fragments
+// for the next 16 tokens read while the current ones multiply).  Columns past
+// K or N and tokens past T read as 0.
 template <class G, typename O>
-__global__ __launch_bounds__(kThreads, 1) void wgrad_mfma_kernel(const uint16_t* __restrict__ dY,
+__global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_t* __restrict__ dY,
                                                                  const uint16_t* __restrict__ X, int T, int N, int K,
                                                                  const uint32_t* __restrict__ meta,
                                                                  O* __restrict__ dWv, O* __restrict__ dWd,
                                                                  int accumulate) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wk = wave & 1, wn = wave >> 1;
+  const int wk = wave % G::WGK, wn = wave / G::WGK;
   const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
   int tk, tn;
   tile_of_block(blockIdx.x, gridDim.x, tiles_k, tiles_n, 8, tk, tn);
   const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
   const int stages = (T + G::TS - 1) / G::TS;
 
-  u32x4 px[G::NX], pd[G::ND];
-  auto load = [&](int s) {
+  // DMA lanes: row (token within the stage) and logical granule of each load
+  int x_row[G::X_DMA], x_q[G::X_DMA], d_row[G::D_DMA], d_q[G::D_DMA];
 #pragma unroll
-    for (int i = 0; i < G::NX; ++i) {
-      const int c = tid + kThreads * i, row = c / (G::BK / 8), p = c % (G::BK / 8);
-      const int64_t t = (int64_t)s * G::TS + row, k = k0 + 8 * p;
-      px[i] = (t < T && k + 8 <= K) ? *reinterpret_cast<const u32x4*>(X + t * K + k) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < G::X_DMA; ++j) {
+    const int row = wave * (G::TS / G::WAVES) + 2 * j + (lane >> 5);
+    x_row[j] = row;
+    x_q[j] = (lane & 31) ^ ((row & 3) << 2);
+  }
+#pragma unroll
+  for (int j = 0; j < G::D_DMA; ++j) {
+    const int row = wave * (G::TS / G::WAVES) + 2 * j + (lane >> 5);
+    d_row[j] = row;
+    d_q[j] = (lane & 31) ^ ((row & 3) << 2);
+  }
+  auto issue = [&](int s) {
+    char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+    const int64_t ts = (int64_t)s * G::TS;
+    // resources from this stage's first token to the end of each matrix
+    const int64_t xrem = (int64_t)T * K - (ts * K + k0), drem = (int64_t)T * N - (ts * N + n0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + ts * K + k0, xrem > 0 ? xrem * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dY + ts * N + n0, drem > 0 ? drem * 2 : 0);
+#pragma unroll
+    for (int j = 0; j < G::X_DMA; ++j) {
+      const bool ok = k0 + 8 * x_q[j] + 8 <= K;
+      dma16(rx, base + wave * (G::X_BYTES / G::WAVES) + j * 1024, ok ? (uint32_t)(x_row[j] * K * 2 + x_q[j] * 16) : kOutOfRange);
     }
 #pragma unroll
-    for (int i = 0; i < G::ND; ++i) {
-      const int c = tid + kThreads * i, row = c / (G::BN / 8), p = c % (G::BN / 8);
-      const int64_t t = (int64_t)s * G::TS + row, n = n0 + 8 * p;
-      pd[i] = (t < T && n + 8 <= N) ? *reinterpret_cast<const u32x4*>(dY + t * N + n) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < G::D_DMA; ++j) {
+      const bool ok = n0 + 8 * d_q[j] + 8 <= N;
+      dma16(rd, base + G::X_BYTES + wave * (G::D_BYTES / G::WAVES) + j * 1024,
+            ok ? (uint32_t)(d_row[j] * N * 2 + d_q[j] * 16) : kOutOfRange);
     }
   };
-  auto store = [&](int buf) {
-    uint16_t* Xs = reinterpret_cast<uint16_t*>(lds + buf * G::STAGE_BYTES);
-    uint16_t* Ds = Xs + G::X_ELEMS;
+
+  struct Frags {
+    bf16x8 x[G::FK];
+    bf16x8 d[G::FN];
+  };
+  auto read_frags = [&](Frags& f, int s, int sub) {
+    const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < G::NX; ++i) {
-      const int c = tid + kThreads * i, row = c / (G::BK / 8), p = c % (G::BK / 8);
-      *reinterpret_cast<u32x4*>(Xs + row * G::XP + 8 * p) = px[i];
-    }
+    for (int a = 0; a < G::FK; ++a) f.x[a] = frag_tr(base, 16 * sub, wk * G::WK + a * 32, lane);
 #pragma unroll
-    for (int i = 0; i < G::ND; ++i) {
-      const int c = tid + kThreads * i, row = c / (G::BN / 8), p = c % (G::BN / 8);
-      *reinterpret_cast<u32x4*>(Ds + row * G::DP + 8 * p) = pd[i];
-    }
+    for (int b = 0; b < G::FN; ++b) f.d[b] = frag_tr(base + G::X_BYTES, 16 * sub, wn * G::WN + b * 32, lane);
   };
 
   f32x16 acc[G::FK][G::FN];
@@ -139,33 +166,32 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_mfma_kernel(const uint16_t*
   for (int a = 0; a < G::FK; ++a)
 #pragma unroll
     for (int b = 0; b < G::FN; ++b) acc[a][b] = f32x16{};
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b)
+#pragma unroll
+      for (int a = 0; a < G::FK; ++a)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], f.d[b], acc[a][b], 0, 0, 0);
+  };
 
-  if (stages > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
+#pragma unroll
+  for (int p = 0; p < G::NST - 1; ++p) issue(p);
+  wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 2)>();
+  barrier();
+  Frags f0, f1;
+  read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < stages) load(s + 1);
-    const uint16_t* Xs = reinterpret_cast<const uint16_t*>(lds + buf * G::STAGE_BYTES);
-    const uint16_t* Ds = Xs + G::X_ELEMS;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      bf16x8 xa[G::FK];
-#pragma unroll
-      for (int a = 0; a < G::FK; ++a) xa[a] = frag_tr(Xs, G::XP, 16 * sub, wk * G::WK + a * 32, lane);
-#pragma unroll
-      for (int b = 0; b < G::FN; ++b) {
-        const bf16x8 db = frag_tr(Ds, G::DP, 16 * sub, wn * G::WN + b * 32, lane);
-#pragma unroll
-        for (int a = 0; a < G::FK; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], db, acc[a][b], 0, 0, 0);
-      }
-    }
-    if (s + 1 < stages) store(buf ^ 1);
-    __syncthreads();
+    read_frags(f1, s, 1);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);                     // MFMAs stay ahead of the wait
+    wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 3)>();   // stage s+1 landed (this wave's part)
+    barrier();                                             // everyone's part; stage s-1 consumed
+    issue(s + G::NST - 1);                                 // past the last stage these read as 0
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < stages) read_frags(f0, s + 1, 0);
+    mma(f1);
   }
+  wait_vmcnt<0>();
 
   // epilogue: rows k (4 consecutive = one group) x column n of this lane
   const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_mfma_kernel(const uint16_t*
   }
 }
 
-typedef WGeo<256, 256> WGeoBig;
+typedef WGeo<256, 256, 4, 2, 4> WGeoBig;
 
 }  // namespace
 
@@ -214,15 +240,15 @@ hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int
   const int64_t nb = cdiv(K, G::BK) * cdiv(N, G::BN);
   if (out == Dt::BF16) {
     auto kern = wgrad_mfma_kernel<G, uint16_t>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    kern<<<(unsigned)nb, kThreads, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
+    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
                                                       meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense, accumulate);
   } else {
     auto kern = wgrad_mfma_kernel<G, float>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    kern<<<(unsigned)nb, kThreads, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
+    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
                                                       meta_s, (float*)dW_values, (float*)dW_dense, accumulate);
   }
   return hipGetLastError();

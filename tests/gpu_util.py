@@ -83,6 +83,6 @@ class Compressed:
         assert self.values.numel() == nv and self.meta.numel() == nm
 
 
-def workspace(T, K, r):
-    b = S.slope_lowrank_workspace_bytes(T, K, r)
+def workspace(T, K, r, N):
+    b = S.slope_lowrank_workspace_bytes(T, K, r, N)
     return torch.empty(max(b, 16), dtype=torch.uint8, device=DEV)

@@ -46,9 +46,10 @@ def test_size_queries(lib):
     assert S.slope_compressed_sizes(3, 36) == (54, 6)        # ragged: ceil(36/32) = 2 words
     with pytest.raises(S.SlopeError):
         S.slope_compressed_sizes(3, 6)
-    assert S.slope_lowrank_workspace_bytes(64, 256, 8) % (64 * 8 * 4) == 0
-    assert S.slope_lowrank_workspace_bytes(64, 256, 0) == 0
-    assert S.slope_lowrank_workspace_bytes(0, 256, 8) == 0
+    assert S.slope_lowrank_workspace_bytes(64, 256, 8, 256) % 256 == 0
+    assert S.slope_lowrank_workspace_bytes(64, 256, 8, 256) >= 64 * 8 * 4 + 256 * 16 * 2
+    assert S.slope_lowrank_workspace_bytes(64, 256, 0, 256) == 0
+    assert S.slope_lowrank_workspace_bytes(0, 256, 8, 256) == 0
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails its checks first

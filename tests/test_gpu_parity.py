@@ -192,7 +192,7 @@ def test_spmm_fwd(T, N, K, adapter, out_dt):
     S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y,
                      L=dev(np.ascontiguousarray(L)) if adapter else None,
                      R=dev(np.ascontiguousarray(R)) if adapter else None,
-                     workspace=workspace(T, K, r) if adapter else None)
+                     workspace=workspace(T, K, r, N) if adapter else None)
     torch.cuda.synchronize()
     err = normwise(host_f64(Y), ref)
     assert err <= TOL["bf16"], err
@@ -250,7 +250,7 @@ def test_lowrank_add(T, N, K, r, out_dt):
     y0_bits = host(Y0)
     _, ref = oracle.lowrank_add(d["X"], d["L"], d["R"], Y_in=y0_bits)
     Y = Y0.clone()
-    S.slope_lowrank_add(dev(d["X"]), dev(d["L"]), dev(d["R"]), workspace(T, K, r), Y)
+    S.slope_lowrank_add(dev(d["X"]), dev(d["L"]), dev(d["R"]), workspace(T, K, r, N), Y)
     torch.cuda.synchronize()
     assert normwise(host_f64(Y), ref) <= TOL["bf16"]
 
@@ -264,7 +264,7 @@ def test_fp32_path(T, N, K):
     d = _layer(T, N, K, r, "f32", seed=T * N)
     Y = empty((T, N), torch.float32)
     S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y, L=dev(d["L"]), R=dev(d["R"]),
-                     workspace=workspace(T, K, r))
+                     workspace=workspace(T, K, r, N))
     dX = empty((T, K), torch.float32)
     S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
     dWv = empty((N, K // 2), torch.float32)
@@ -286,7 +286,7 @@ def test_integer_inputs_bit_exact(T, N, K):
     d = _layer(T, N, K, r, "bf16", seed=17, ints=True)
     Y = empty((T, N), torch.float32)
     S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Y, L=dev(d["L"]), R=dev(d["R"]),
-                     workspace=workspace(T, K, r))
+                     workspace=workspace(T, K, r, N))
     dX = empty((T, K), torch.float32)
     S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
     dWv = empty((N, K // 2), torch.float32)
@@ -328,7 +328,7 @@ def test_deterministic_repeat():
     outs = []
     for _ in range(2):
         Y = empty((T, N), torch.bfloat16)
-        S.slope_spmm_fwd(*args, Y, L=dev(d["L"]), R=dev(d["R"]), workspace=workspace(T, K, r))
+        S.slope_spmm_fwd(*args, Y, L=dev(d["L"]), R=dev(d["R"]), workspace=workspace(T, K, r, N))
         dW = empty((N, K // 2), torch.bfloat16)
         S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dW)
         torch.cuda.synchronize()
