@@ -223,6 +223,23 @@ def profile_mode(args, wl, T):
     print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
 
 
+def measured_traffic(op):
+    """HBM bytes per launch (fetched + written) of `op`'s kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has
+    changed since the counters were taken (or none were taken)."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[op]
+        src = open(os.path.join(ROOT, t["kernel_source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != t["source_sha256_16"]:
+        return None
+    return {"fetch_bytes_per_launch": t["fetch_bytes_per_launch"], "write_bytes_per_launch": t["write_bytes_per_launch"],
+            "bytes_per_launch": t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"],
+            "source": "profiles/traffic.json (rocprofv3 FETCH_SIZE x2.0, WRITE_SIZE x1.0 by copy calibration)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -296,7 +313,8 @@ def main():
     launches = [(l, sum(per[(l.name, dom)]) / len(per[(l.name, dom)])) for l in lins]
     achieved = sum(l.useful()[dom] for l, _ in launches) / (sum(t for _, t in launches) * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_DENSE_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_DENSE_TFLOPS, 4),
+                "traffic": measured_traffic(dom),
                 "flops_counted": "useful (T*N*K per launch: products with a kept weight / kept output)",
                 "avg_launch_ms": {l.name: round(t, 4) for l, t in launches}}
 

@@ -1,0 +1,155 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, checked on sampled outputs the oracle computes one by one and
+on properties that hold at any size.
+
+For every linear of every workload (toy fp32; GPT-2-small, BERT-Large, OPT-13B
+and OPT-66B layers in bf16; the decode token counts of OPT-13B and OPT-66B) the
+whole path runs on the GPU: prune24 -> compress24 -> double_prune ->
+spmm_fwd (+ adapter) -> spmm_bwd_dx -> masked_wgrad.  Then:
+
+* masks / compressed values / metadata: sampled rows bit-exact against the
+  oracle run on the same rows; every group of the full mask keeps exactly two;
+* double pruning: sampled column groups of W_s, pruned again by the oracle,
+  bit-exact against the matching rows of W_dp^T;
+* products: sampled token x feature blocks against the oracle (normwise 1e-2
+  for bf16 outputs, 1e-5 for the fp32 workload).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_02_amd as S
+from workloads import WORKLOADS, layer_inputs
+
+from gpu_util import TOL, Compressed, dev, host, host_f64, normwise, say, workspace
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(wl, i) for wl in WORKLOADS for i in range(len(WORKLOADS[wl].linears))]
+DECODE = [(wl, i, T) for wl in WORKLOADS for T in WORKLOADS[wl].decode_T for i in range(len(WORKLOADS[wl].linears))]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.library()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _group_cols(rng, K, n):
+    """n random column groups of 4 (start columns, multiples of 4)."""
+    return np.sort(rng.choice(K // 4, size=min(n, K // 4), replace=False)) * 4
+
+
+def _rows(rng, n, k):
+    return np.sort(rng.choice(n, size=min(k, n), replace=False))
+
+
+def _run_path(d, T, N, K, r, tdt):
+    """The whole hot path on the GPU; returns device tensors."""
+    W, X, dY, L, R = (dev(d[k]) for k in ("W", "X", "dY", "L", "R"))
+    out = {}
+    out["mask"] = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    S.slope_prune24(W, out["mask"])
+    c = Compressed(N, K, tdt)
+    S.slope_compress24(W, out["mask"], c.values, c.meta)
+    dp = Compressed(K, N, tdt)
+    S.slope_double_prune(c.values, c.meta, N, K, dp.values, dp.meta)
+    Y = torch.empty((T, N), dtype=tdt, device="cuda")
+    S.slope_spmm_fwd(X, c.values, c.meta, N, Y, L=L, R=R, workspace=workspace(T, K, r, N))
+    dX = torch.empty((T, K), dtype=tdt, device="cuda")
+    S.slope_spmm_bwd_dx(dY, dp.values, dp.meta, K, dX)
+    dW = torch.empty((N, K // 2), dtype=tdt, device="cuda")
+    S.slope_masked_wgrad(dY, X, c.meta, dW)
+    torch.cuda.synchronize()
+    out.update(vs=c.values, ms=c.meta, vdp=dp.values, mdp=dp.meta, Y=Y, dX=dX, dW=dW)
+    return out
+
+
+@pytest.mark.parametrize("wl,idx", CASES, ids=[f"{w}-{WORKLOADS[w].linears[i].name}" for w, i in CASES])
+def test_full_path_sampled(wl, idx):
+    w = WORKLOADS[wl]
+    lin = w.linears[idx]
+    T, N, K, r = w.T, lin.N, lin.K, w.r
+    say(f"[fullsize] {wl} {lin.name}: T={T} K={K} N={N} r={r} dtype={w.dtype}")
+    d = layer_inputs(K, N, T, r, w.dtype, seed=0, index=idx)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tol = TOL[w.dtype]
+    o = _run_path(d, T, N, K, r, tdt)
+    rng = np.random.default_rng(1000 + idx)
+
+    # --- masks and compression: every group keeps exactly two; sampled rows bit-exact
+    assert bool((o["mask"].view(-1, 4).sum(dim=1, dtype=torch.int32) == 2).all())
+    rows = _rows(rng, N, 24)
+    mask_ref, _ = oracle.prune24(d["W"][rows])
+    assert (host(o["mask"][rows]) == mask_ref).all()
+    v_ref, m_ref, _ = oracle.compress24(d["W"][rows], mask_ref)
+    assert (host(o["vs"][rows]) == v_ref).all()
+    assert (host(o["ms"][rows]) == m_ref).all()
+
+    # --- double pruning on sampled column groups (all N rows of W_s for 4 columns)
+    gcols = _group_cols(rng, K, 6)
+    for c0 in gcols:
+        Wc = np.ascontiguousarray(d["W"][:, c0:c0 + 4])
+        mc, _ = oracle.prune24(Wc)                 # W_s restricted to these columns
+        vc, mcw, _ = oracle.compress24(Wc, mc)
+        vdp_ref, mdp_ref, _ = oracle.double_prune(vc, mcw, N, 4)
+        assert (host(o["vdp"][c0:c0 + 4]) == vdp_ref).all(), c0
+        assert (host(o["mdp"][c0:c0 + 4]) == mdp_ref).all(), c0
+
+    # --- forward with adapter on a sampled token x feature block
+    ts = _rows(rng, T, 48)
+    ns = _rows(rng, N, 48)
+    vsub, msub, _ = oracle.compress24(d["W"][ns], oracle.prune24(d["W"][ns])[0])
+    y_ref = oracle.spmm_fwd(d["X"][ts], vsub, msub, K, d["L"], np.ascontiguousarray(d["R"][:, ns]))
+    assert normwise(host_f64(o["Y"][ts][:, ns]), y_ref) <= tol
+
+    # --- dX on sampled tokens x sampled column groups (W_dp columns from the oracle)
+    for c0 in gcols[:3]:
+        Wc = np.ascontiguousarray(d["W"][:, c0:c0 + 4])
+        mc, _ = oracle.prune24(Wc)
+        vc, mcw, _ = oracle.compress24(Wc, mc)
+        vdp_ref, mdp_ref, _ = oracle.double_prune(vc, mcw, N, 4)
+        dx_ref = oracle.spmm_bwd_dx(d["dY"][ts], vdp_ref, mdp_ref, N)
+        assert normwise(host_f64(o["dX"][ts][:, c0:c0 + 4]), dx_ref) <= tol
+
+    # --- dW on sampled rows x a 64-column window (full token reduction)
+    nw = _rows(rng, N, 16)
+    kw0 = int(rng.integers(0, max(1, K // 64))) * 64
+    kw = min(64, K - kw0)
+    Wsub = np.ascontiguousarray(d["W"][nw][:, kw0:kw0 + kw])
+    _, msub, _ = oracle.compress24(Wsub, oracle.prune24(Wsub)[0])
+    dwv_ref, _ = oracle.masked_wgrad(np.ascontiguousarray(d["dY"][:, nw]),
+                                     np.ascontiguousarray(d["X"][:, kw0:kw0 + kw]), msub, kw)
+    got = host_f64(o["dW"][nw][:, kw0 // 2:(kw0 + kw) // 2])
+    assert normwise(got, dwv_ref) <= tol
+    del o
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl,idx,T", DECODE, ids=[f"{w}-{WORKLOADS[w].linears[i].name}-T{t}" for w, i, t in DECODE])
+def test_decode_forward_sampled(wl, idx, T):
+    """Inference shapes: the forward with the unmerged adapter at T = 1..64."""
+    w = WORKLOADS[wl]
+    lin = w.linears[idx]
+    N, K, r = lin.N, lin.K, w.r
+    say(f"[decode] {wl} {lin.name}: T={T} K={K} N={N} r={r}")
+    d = layer_inputs(K, N, T, r, w.dtype, seed=7, index=idx, which=("W", "X", "L", "R"))
+    Wd = dev(d["W"])
+    mask = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    S.slope_prune24(Wd, mask)
+    c = Compressed(N, K, torch.bfloat16)
+    S.slope_compress24(Wd, mask, c.values, c.meta)
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    S.slope_spmm_fwd(dev(d["X"]), c.values, c.meta, N, Y, L=dev(d["L"]), R=dev(d["R"]),
+                     workspace=workspace(T, K, r, N))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(idx + T)
+    ns = _rows(rng, N, 64)
+    vsub, msub, _ = oracle.compress24(d["W"][ns], oracle.prune24(d["W"][ns])[0])
+    y_ref = oracle.spmm_fwd(d["X"], vsub, msub, K, d["L"], np.ascontiguousarray(d["R"][:, ns]))
+    assert normwise(host_f64(Y[:, ns]), y_ref) <= TOL["bf16"]
