@@ -22,11 +22,16 @@ struct Geo {
   // stage layout (bytes): A [BM][64] (32 compressed values per row), B [BT][128] (64 values)
   static constexpr int A_BYTES = BM * 64, B_BYTES = BT * 128;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  // metadata: [BM][16] = four words (two stages) per row, in a ring of two slots
-  static constexpr int META_SLOT = BM * 16, META_BYTES = 2 * META_SLOT;
-  static constexpr int LDS_BYTES = NST * STAGE_BYTES + META_BYTES;
-  // buffer-to-LDS loads (1 KB each) per wave: A and B every stage, metadata every second stage
+  // metadata: [BM][16] = four words (two stages) per row, in a ring of two slots,
+  // plus a 256-byte landing area per wave for the placeholder loads that keep
+  // every wave's per-stage load count equal
+  static constexpr int META_SLOT = BM * 16, META_BYTES = 2 * META_SLOT, PAD_BYTES = 256 * WAVES;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES + META_BYTES + PAD_BYTES;
+  // buffer-to-LDS loads per wave and stage: A and B (1 KB each) and one metadata
+  // load (a 1 KB slice every second stage for the first META_WAVES waves, else a
+  // 256-byte placeholder that reads nothing)
   static constexpr int A_DMA = A_BYTES / 1024 / WAVES, B_DMA = B_BYTES / 1024 / WAVES;
+  static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;
   static constexpr int META_WAVES = META_SLOT / 1024;  // waves that load one metadata KB each
   static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "tile/wave split");
   static_assert(META_WAVES <= WAVES, "metadata split");

@@ -113,6 +113,8 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     if ((s & 1) == 0 && wave < G::META_WAVES) {      // words 2s .. 2s+3 of every row
       const bool ok = 2 * s < wpr;
       dma16(rmeta, meta_lds + ((s >> 1) & 1) * G::META_SLOT + wave * 1024, ok ? m_src + s * 8 : kOutOfRange);
+    } else {                                         // placeholder: same load count on every wave and stage
+      dma4(rmeta, meta_lds + G::META_BYTES + wave * 256, kOutOfRange);
     }
   };
 
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   // prologue: stages 0 .. NST-2 in flight; stage 0 landed and visible
 #pragma unroll
   for (int p = 0; p < G::NST - 1; ++p) issue(p);
-  wait_vmcnt<0>();
+  wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();
   barrier();
   Frags f0, f1;
   read_frags(f0, 0, 0);
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     mma(f0);
     // keep the first k-step's MFMAs ahead of the wait: they run while it waits
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();                                  // this wave's loads of stage s+1 (and s+2..) landed
+    wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 3)>();   // this wave's loads of stage s+1 landed
     barrier();                                        // everyone's have; stage s-1 fully consumed
     issue(s + G::NST - 1);                            // past the last stage these read as 0
     __builtin_amdgcn_sched_barrier(0);
