@@ -80,6 +80,9 @@ class Linear:
         self.dW = torch.empty((N, K // 2), dtype=bf, device=dev)
         import sparse_gemm_02_amd as S
         self.ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, K, r, N)), dtype=torch.uint8, device=dev)
+        # weight-gradient operands as transposed token chunks
+        self.Xp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, K)), dtype=torch.uint8, device=dev)
+        self.dYp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, N)), dtype=torch.uint8, device=dev)
 
     def flops(self):
         T, N, K, r = self.T, self.N, self.K, self.r
@@ -91,7 +94,16 @@ class Linear:
         return {"spmm_fwd": T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": T * N * K, "masked_wgrad": T * N * K}
 
 
-OPS = ("prune24", "compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad")
+OPS = ("prune24", "compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "pack_tokens", "masked_wgrad")
+
+
+def pack(S, li):
+    S.slope_pack_tokens(li.X, li.Xp)
+    S.slope_pack_tokens(li.dY, li.dYp)
+
+
+def wgrad(S, li):
+    S.slope_masked_wgrad_packed(li.dYp, li.Xp, li.T, li.N, li.K, li.ms, li.dW)
 
 
 def step(lins, S, ev=None):
@@ -103,7 +115,8 @@ def step(lins, S, ev=None):
             ("double_prune", lambda: S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)),
             ("spmm_fwd", lambda: S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
             ("spmm_bwd_dx", lambda: S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)),
-            ("masked_wgrad", lambda: S.slope_masked_wgrad(li.dY, li.X, li.ms, li.dW)),
+            ("pack_tokens", lambda: pack(S, li)),
+            ("masked_wgrad", lambda: wgrad(S, li)),
         )
         for op, fn in calls:
             if ev is not None:
@@ -203,6 +216,7 @@ def profile_mode(args, wl, T):
         S.slope_prune24(li.W, li.mask)
         S.slope_compress24(li.W, li.mask, li.vs, li.ms)
         S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+        pack(S, li)
     torch.cuda.synchronize()
     op = args.profile_op
     for _ in range(args.repeat):
@@ -217,8 +231,10 @@ def profile_mode(args, wl, T):
                 S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
             elif op == "spmm_bwd_dx":
                 S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)
+            elif op == "pack_tokens":
+                pack(S, li)
             elif op == "masked_wgrad":
-                S.slope_masked_wgrad(li.dY, li.X, li.ms, li.dW)
+                wgrad(S, li)
     torch.cuda.synchronize()
     print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
 
@@ -302,9 +318,12 @@ def main():
         t = ops[op]["ms_per_step"] * 1e-3
         ops[op].update(useful_tflops=uf / t / 1e12, dense_equiv_tflops=df / t / 1e12,
                        frac_dense_peak_useful=uf / t / 1e12 / PEAK_BF16_DENSE_TFLOPS)
-    hbm = {"prune24": 3.0, "compress24": 4.125, "double_prune": 2.25}  # algorithmic bytes per weight
-    for op, bpe in hbm.items():
-        by = sum(l.N * l.K * bpe for l in lins)
+    # algorithmic HBM bytes: per weight for the pruning ops, per activation
+    # element (read + written once) for the packing pass
+    hbm = {"prune24": lambda l: 3.0 * l.N * l.K, "compress24": lambda l: 4.125 * l.N * l.K,
+           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
+    for op, f in hbm.items():
+        by = sum(f(l) for l in lins)
         ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9
         ops[op]["frac_hbm_peak"] = ops[op]["gbs"] / PEAK_HBM_GBS
 

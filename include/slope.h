@@ -61,9 +61,9 @@ typedef enum { SLOPE_F32 = 0, SLOPE_BF16 = 1 } slope_dtype;
 typedef enum {
   SLOPE_OK = 0,
   SLOPE_ERR_INVALID_ARG = -1, /* null pointer, unknown dtype, negative size */
-  SLOPE_ERR_SHAPE = -2,       /* a 2:4 dimension not a multiple of 4 */
+  SLOPE_ERR_SHAPE = -2,       /* a 2:4 dimension not a multiple of 4 (8 where stated) */
   SLOPE_ERR_ALIGN = -3,       /* a pointer not 16-byte aligned */
-  SLOPE_ERR_WORKSPACE = -4,   /* adapter workspace missing or too small */
+  SLOPE_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   SLOPE_ERR_HIP = -5,         /* the HIP runtime reported an error */
   SLOPE_ERR_UNSUPPORTED = -6  /* dtype combination or size beyond the limits */
 } slope_status;
@@ -87,6 +87,12 @@ slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_value
  * (float32), X . L as bf16 hi + lo parts, and transposed copies of L and R.
  * Host-only; 0 when T == 0 or r == 0. */
 slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
+
+/* Bytes of device workspace slope_masked_wgrad can use for T tokens, N
+ * outputs and K inputs: X and dY rewritten, transposed, into 256-column x
+ * 32-token chunks (bf16, zero padded; see slope_pack_tokens), X's first.
+ * Host-only. */
+slope_status slope_wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes);
 
 /* Magnitude 2:4 pruning of W [rows, cols] along its rows: the forward weight
  * W^R, pruned along rows (explainer 2.A; N:M = 2:4, summary page Approach).
@@ -157,10 +163,40 @@ slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void
  *             values_s)
  *   dW_dense  [N, K] out_dt masked dense copy, or NULL
  *   accumulate != 0: add to the existing contents instead of overwriting
- * Errors: SLOPE_ERR_SHAPE if K % 4 != 0. */
+ *   workspace: NULL, or device memory (16-byte aligned) of at least
+ *             slope_wgrad_workspace_bytes(T, N, K) bytes, owned by the caller
+ *             and overwritten; with it the bf16 path packs both operands
+ *             first and runs faster.  Results are identical either way.
+ * Errors: SLOPE_ERR_SHAPE if K % 4 != 0; SLOPE_ERR_WORKSPACE if a workspace
+ * is given and is short. */
 slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const void* dY, const void* X, int64_t T,
                                 int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
-                                void* dW_dense_or_null, int accumulate, void* stream);
+                                void* dW_dense_or_null, int accumulate, void* workspace_or_null,
+                                int64_t workspace_bytes, void* stream);
+
+/* Bytes of a bf16 matrix M [T, C] rewritten as token chunks (see
+ * slope_pack_tokens).  Host-only. */
+slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);
+
+/* Transposed token-chunk copy of a bf16 matrix M [T, C] (C % 8 == 0), the
+ * operand format of slope_masked_wgrad_packed: chunk (c, s) holds columns
+ * 256c .. 256c+255 (one 64-byte row each) x tokens 32s .. 32s+31, 16 KB, at
+ * byte offset (c * ceil(T/32) + s) * 16384; in a row, the 16-byte granule of
+ * tokens 8g .. 8g+7 sits at granule position g ^ ((row / 4) % 4); entries
+ * past T or C are 0.  packed: caller-owned device memory of at least
+ * slope_packed_tokens_bytes(T, C) bytes, overwritten.
+ * Errors: SLOPE_ERR_UNSUPPORTED for float32, SLOPE_ERR_SHAPE if C % 8 != 0,
+ * SLOPE_ERR_WORKSPACE if packed_bytes is short. */
+slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t C, void* packed,
+                               int64_t packed_bytes, void* stream);
+
+/* slope_masked_wgrad on operands already packed by slope_pack_tokens:
+ * dY_packed from dY [T, N], X_packed from X [T, K] (bf16).  Same outputs,
+ * bitwise, as slope_masked_wgrad.  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or
+ * K % 8 != 0. */
+slope_status slope_masked_wgrad_packed(slope_dtype out_dt, const void* dY_packed, const void* X_packed, int64_t T,
+                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                       void* dW_dense_or_null, int accumulate, void* stream);
 
 /* Low-rank adapter term on its own (explainer 2.B: W_dense = W_sparse + L R):
  *   Y [T, N] += (X [T, K] . L [K, r]) . R [r, N]

@@ -12,6 +12,7 @@ Tensor conventions (see include/slope.h):
   compressed values   [rows, cols/2], same dtype as the dense matrix
   compressed metadata [rows, ceil(cols/32)] torch.int32 holding the uint32 words
   adapter workspace   torch.uint8 (or any dtype) of slope_lowrank_workspace_bytes()
+  wgrad workspace     torch.uint8 (or any dtype) of slope_wgrad_workspace_bytes()
 """
 from __future__ import annotations
 
@@ -24,7 +25,8 @@ __all__ = [
     "SlopeError", "library", "library_path", "STATUS",
     "slope_version", "slope_compressed_sizes", "slope_lowrank_workspace_bytes",
     "slope_prune24", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
-    "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add",
+    "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
+    "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -49,7 +51,11 @@ _SIGS = {
     "slope_double_prune": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "slope_spmm_fwd": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "slope_spmm_bwd_dx": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp]),
-    "slope_masked_wgrad": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "slope_masked_wgrad": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "slope_wgrad_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
+    "slope_packed_tokens_bytes": (_i32, [_i64, _i64, _P_I64]),
+    "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
@@ -169,12 +175,40 @@ def slope_spmm_bwd_dx(dY, values_dpT, meta_dpT, K, dX, stream=None) -> None:
                                                             _nn(meta_dpT), K, _nn(dX), _s(stream)))
 
 
-def slope_masked_wgrad(dY, X, meta_s, dW_values, dW_dense=None, accumulate=False, stream=None) -> None:
+def slope_wgrad_workspace_bytes(T: int, N: int, K: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_wgrad_workspace_bytes", library().slope_wgrad_workspace_bytes(T, N, K, ctypes.byref(b)))
+    return b.value
+
+
+def slope_masked_wgrad(dY, X, meta_s, dW_values, dW_dense=None, accumulate=False, workspace=None,
+                       stream=None) -> None:
     T, N = dY.shape
     K = X.shape[1]
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_masked_wgrad", library().slope_masked_wgrad(_dt(dY), _dt(dW_values), _nn(dY), _nn(X), T, N, K,
                                                               _nn(meta_s), _nn(dW_values), _p(dW_dense),
-                                                              int(bool(accumulate)), _s(stream)))
+                                                              int(bool(accumulate)), _p(workspace), wb,
+                                                              _s(stream)))
+
+
+def slope_packed_tokens_bytes(T: int, C: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_packed_tokens_bytes", library().slope_packed_tokens_bytes(T, C, ctypes.byref(b)))
+    return b.value
+
+
+def slope_pack_tokens(M, packed, stream=None) -> None:
+    T, C = M.shape
+    nb = packed.numel() * packed.element_size()
+    _check("slope_pack_tokens", library().slope_pack_tokens(_dt(M), _nn(M), T, C, _nn(packed), nb, _s(stream)))
+
+
+def slope_masked_wgrad_packed(dY_packed, X_packed, T, N, K, meta_s, dW_values, dW_dense=None, accumulate=False,
+                              stream=None) -> None:
+    _check("slope_masked_wgrad_packed", library().slope_masked_wgrad_packed(
+        _dt(dW_values), _nn(dY_packed), _nn(X_packed), T, N, K, _nn(meta_s), _nn(dW_values), _p(dW_dense),
+        int(bool(accumulate)), _s(stream)))
 
 
 def slope_lowrank_add(X, L, R, workspace, Y, stream=None) -> None:

@@ -162,21 +162,69 @@ slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void
                                      dX, (hipStream_t)stream));
 }
 
+slope_status slope_wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::wgrad_workspace_bytes(T, N, K);
+  return SLOPE_OK;
+}
+
 slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const void* dY, const void* X, int64_t T,
                                 int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
-                                void* dW_dense_or_null, int accumulate, void* stream) {
+                                void* dW_dense_or_null, int accumulate, void* workspace_or_null,
+                                int64_t workspace_bytes, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY, true));
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(meta_s, true));
   SLOPE_TRY(ptr(dW_values, true));
   SLOPE_TRY(ptr(dW_dense_or_null, false));
+  SLOPE_TRY(ptr(workspace_or_null, false));
   if (K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  if (workspace_or_null && workspace_bytes < slope::wgrad_workspace_bytes(T, N, K)) return SLOPE_ERR_WORKSPACE;
   if (N == 0 || K == 0) return SLOPE_OK;
   return from_hip(slope::launch_masked_wgrad((Dt)in_dt, (Dt)out_dt, dY, X, T, N, K, meta_s, dW_values,
-                                             dW_dense_or_null, accumulate, (hipStream_t)stream));
+                                             dW_dense_or_null, accumulate, workspace_or_null,
+                                             (hipStream_t)stream));
+}
+
+slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes) {
+  if (!bytes || T < 0 || C < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(C)) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::packed_tokens_bytes(T, C);
+  return SLOPE_OK;
+}
+
+slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t C, void* packed,
+                               int64_t packed_bytes, void* stream) {
+  if (!dt_ok(dt)) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || C < 0 || packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(M, true));
+  SLOPE_TRY(ptr(packed, true));
+  if (dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (C % 8) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(C)) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_bytes < slope::packed_tokens_bytes(T, C)) return SLOPE_ERR_WORKSPACE;
+  return from_hip(slope::launch_pack_tokens(M, T, C, packed, (hipStream_t)stream));
+}
+
+slope_status slope_masked_wgrad_packed(slope_dtype out_dt, const void* dY_packed, const void* X_packed, int64_t T,
+                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                       void* dW_dense_or_null, int accumulate, void* stream) {
+  SLOPE_TRY(check_io(SLOPE_BF16, out_dt));
+  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(dY_packed, true));
+  SLOPE_TRY(ptr(X_packed, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(dW_values, true));
+  SLOPE_TRY(ptr(dW_dense_or_null, false));
+  if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return SLOPE_OK;
+  return from_hip(slope::launch_masked_wgrad_packed((Dt)out_dt, dY_packed, X_packed, T, N, K, meta_s, dW_values,
+                                                    dW_dense_or_null, accumulate, (hipStream_t)stream));
 }
 
 slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,

@@ -39,6 +39,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Wait until this wave's LDS reads (and other LGKM operations) have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the LDS
 // traffic it orders is waited for explicitly with wait_vmcnt / lgkmcnt.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }

@@ -43,10 +43,20 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
                        const uint32_t* meta, int64_t M, const LowrankWs* ws, int64_t r, const void* R, void* Y,
                        hipStream_t s);
 
-// dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional accumulation.
+// dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional
+// accumulation.  With a workspace of wgrad_workspace_bytes(T, N, K) bytes the
+// bf16 path first packs X and dY into transposed token chunks there.
+int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K);
+// Token chunks of a bf16 matrix [T, C] (C % 8 == 0): bytes, and the packing pass.
+int64_t packed_tokens_bytes(int64_t T, int64_t C);
+hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s);
+// The weight-gradient GEMM on packed bf16 operands (N % 8 == 0, K % 8 == 0).
+hipError_t launch_masked_wgrad_packed(Dt out, const void* dY_packed, const void* X_packed, int64_t T, int64_t N,
+                                      int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
+                                      int accumulate, hipStream_t s);
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
-                               hipStream_t s);
+                               void* workspace, hipStream_t s);
 
 // Y[t][m] += (X . L)[t, :] . R[:, m] from a prepared workspace.
 hipError_t launch_lowrank_up_add(Dt in, Dt out, const LowrankWs& w, const void* R, int64_t T, int64_t r,

@@ -53,9 +53,12 @@ namespace {
 // at c ^ ((r^(r>>3))&7).
 //
 // Schedule per stage s (one barrier): read the second k-step's fragments of s,
-// issue the first k-step's MFMAs, wait for stage s+1 and barrier, start the
-// loads of stage s+NST-1 into the slot stage s-1 used, read the first k-step's
-// fragments of s+1, issue the second k-step's MFMAs.
+// issue the first k-step's MFMAs, wait for this wave's LDS reads and for stage
+// s+1, barrier, start the loads of stage s+NST into the slot stage s used (its
+// fragments are all in registers by then), read the first k-step's fragments
+// of s+1, issue the second k-step's MFMAs.  NST-1 stages stay in flight
+// through most of the loop.  The metadata ring of two slots (four stages)
+// holds stages s .. s+3, which needs NST == 3.
 template <class G, bool ADAPTER, typename O>
 __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
+  static_assert(G::NST == 3, "metadata ring holds four stages");
   const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
   const int wpr = (Kred / 4 + 7) / 8;               // metadata words per row
   const int stages = (Kred + G::KS - 1) / G::KS;
@@ -175,21 +179,22 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
         acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm], 0, 0);
   };
 
-  // prologue: stages 0 .. NST-2 in flight; stage 0 landed and visible
+  // prologue: stages 0 .. NST-1 in flight; stage 0 landed and visible
 #pragma unroll
-  for (int p = 0; p < G::NST - 1; ++p) issue(p);
-  wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();
+  for (int p = 0; p < G::NST; ++p) issue(p);
+  wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 1)>();
   barrier();
   Frags f0, f1;
   read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {
     read_frags(f1, s, 1);
     mma(f0);
-    // keep the first k-step's MFMAs ahead of the wait: they run while it waits
+    // keep the first k-step's MFMAs ahead of the waits: they run meanwhile
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 3)>();   // this wave's loads of stage s+1 landed
-    barrier();                                        // everyone's have; stage s-1 fully consumed
-    issue(s + G::NST - 1);                            // past the last stage these read as 0
+    wait_lgkmcnt0();                                  // this wave's reads of stage s are in registers
+    wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();   // this wave's loads of stage s+1 landed
+    barrier();                                        // everyone's have; stage s fully read
+    issue(s + G::NST);                                // refill stage s's slot; past the end these read 0
     __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < stages) read_frags(f0, s + 1, 0);
     mma(f1);

@@ -95,10 +95,53 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int tb, int c0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Epilogue of both weight-gradient kernels: lane l of accumulator [a][b] holds
+// column n = n0 + wn*WN + b*32 + l%32 and rows k = k0 + wk*WK + a*32 + 8q + 4(l/32)
+// + i (i < 4) in elements 4q+i, i.e. one whole 2:4 group of k; keep the two
+// positions meta_s names and write them in slot order (plus the masked dense copy).
+template <class G, typename O>
+__device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], const uint32_t* __restrict__ meta,
+                                            int K, int N, int64_t k0, int64_t n0, int wk, int wn, int lane,
+                                            O* __restrict__ dWv, O* __restrict__ dWd, int accumulate) {
+  const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
+#pragma unroll
+  for (int b = 0; b < G::FN; ++b) {
+    const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
+    if (n >= N) continue;
+#pragma unroll
+    for (int a = 0; a < G::FK; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
+        if (k >= K) continue;
+        const int64_t g = k >> 2;
+        const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
+        const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+        const float r0 = acc[a][b][4 * q], r1 = acc[a][b][4 * q + 1];
+        const float r2 = acc[a][b][4 * q + 2], r3 = acc[a][b][4 * q + 3];
+        // i0 < i1: i0 in {0,1,2}, i1 in {1,2,3}; selects without indexing registers
+        float v0 = i0 == 0 ? r0 : (i0 == 1 ? r1 : r2);
+        float v1 = i1 == 3 ? r3 : (i1 == 2 ? r2 : r1);
+        O* vp = dWv + n * (K / 2) + 2 * g;
+        if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
+        store_pair(vp, v0, v1);
+        if (dWd) {
+          O* dp = dWd + n * K + k;
+          const float x[4] = {(i0 == 0) ? r0 : 0.f, (i0 == 1 || i1 == 1) ? r1 : 0.f,
+                              (i0 == 2 || i1 == 2) ? r2 : 0.f, (i1 == 3) ? r3 : 0.f};
+          store_quad(dp, x, accumulate);
+        }
+      }
+    }
+  }
+}
+
 // Requirements (host-checked): K % 8 == 0, N % 8 == 0, 16-byte aligned bases.
 // Token rows of both operands stream through a ring of NST LDS stages filled
 // by buffer loads that write LDS directly (one barrier per stage, fragments
-// for the next 16 tokens read while the current ones multiply).  Columns past
+// for the next 16 tokens read while the current ones multiply; a stage's slot
+// is refilled as soon as every wave holds its fragments, so NST-1 stages stay
+// in flight).  Columns past
 // K or N and tokens past T read as 0.
 template <class G, typename O>
 __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_t* __restrict__ dY,
@@ -175,67 +218,251 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
   };
 
 #pragma unroll
-  for (int p = 0; p < G::NST - 1; ++p) issue(p);
-  wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 2)>();
+  for (int p = 0; p < G::NST; ++p) issue(p);
+  wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 1)>();
   barrier();
   Frags f0, f1;
   read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {
     read_frags(f1, s, 1);
     mma(f0);
-    __builtin_amdgcn_sched_barrier(0);                     // MFMAs stay ahead of the wait
-    wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 3)>();   // stage s+1 landed (this wave's part)
-    barrier();                                             // everyone's part; stage s-1 consumed
-    issue(s + G::NST - 1);                                 // past the last stage these read as 0
+    __builtin_amdgcn_sched_barrier(0);                     // MFMAs stay ahead of the waits
+    wait_lgkmcnt0();                                       // this wave's reads of stage s are in registers
+    wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 2)>();   // stage s+1 landed (this wave's part)
+    barrier();                                             // everyone's part; stage s fully read
+    issue(s + G::NST);                                     // refill stage s's slot; past the end these read 0
     __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < stages) read_frags(f0, s + 1, 0);
     mma(f1);
   }
   wait_vmcnt<0>();
 
-  // epilogue: rows k (4 consecutive = one group) x column n of this lane
-  const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
+  wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+}
+
+// ---------------------------------------------------------------- packed path
+// Both operands are first rewritten, transposed, into "token chunks": for a
+// matrix M [T, C] (C = K for X, N for dY), chunk (c, s) holds columns
+// 256c .. 256c+255 (rows of the chunk) x tokens 32s .. 32s+31, 16 KB, at element
+// offset (c * Tch + s) * 8192 (Tch = ceil(T / 32)).  A chunk row is 64 bytes:
+// four 16-byte granules of 8 tokens, granule g stored at g ^ ((row >> 2) & 3) so
+// that MFMA fragment reads from LDS are free of bank conflicts.  Entries past T
+// or C are 0.  Each stage of the GEMM then loads one contiguous chunk per
+// operand, and fragments are plain 128-bit LDS reads.
+constexpr int kChunkRows = 256, kChunkTokens = 32, kChunkElems = kChunkRows * kChunkTokens;
+
+__global__ __launch_bounds__(256) void pack_tokens_kernel(const uint16_t* __restrict__ src, int T, int C,
+                                                          int64_t chunks_c, int64_t Tch, uint16_t* __restrict__ dst) {
+  constexpr int kPitch = 264;                       // LDS row pitch in elements (528 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kChunkTokens * kPitch];
+  const int tid = threadIdx.x;
+  const int64_t nchunks = chunks_c * Tch;
+  for (int64_t q = blockIdx.x; q < nchunks; q += gridDim.x) {
+    const int64_t cb = q % chunks_c, ts = q / chunks_c;
+    // 32 token rows x 512 bytes, 16 bytes per load
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + 256 * j, t = piece >> 5, g = piece & 31;
+      const int64_t tg = ts * kChunkTokens + t, cg = cb * kChunkRows + 8 * g;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tg < T && cg < C) v = *reinterpret_cast<const u32x4*>(src + tg * C + cg);   // C % 8 == 0
+      *reinterpret_cast<u32x4*>(&tile[t * kPitch + 8 * g]) = v;
+    }
+    __syncthreads();
+    // thread r writes chunk row r: 8 tokens per granule
+    const int r = tid;
+    uint16_t* out = dst + (cb * Tch + ts) * kChunkElems + r * kChunkTokens;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (uint32_t)tile[(8 * g + 2 * e) * kPitch + r] | ((uint32_t)tile[(8 * g + 2 * e + 1) * kPitch + r] << 16);
+      *reinterpret_cast<u32x4*>(out + 8 * (g ^ ((r >> 2) & 3))) = v;
+    }
+    __syncthreads();
+  }
+}
+
+template <int BK_, int BN_, int NST_, int WGK_, int WGN_>
+struct PGeo {
+  static constexpr int BK = BK_, BN = BN_;
+  static constexpr int WGK = WGK_, WGN = WGN_, WAVES = WGK * WGN, THREADS = 64 * WAVES;
+  static constexpr int WK = BK / WGK, WN = BN / WGN;
+  static constexpr int FK = WK / 32, FN = WN / 32;
+  static constexpr int NST = NST_;
+  static constexpr int CHUNK_BYTES = kChunkElems * 2;              // 16 KB per operand and stage
+  static constexpr int STAGE_BYTES = 2 * CHUNK_BYTES;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int DMA = CHUNK_BYTES / 1024 / WAVES;           // loads per wave, operand and stage
+  static constexpr int DMA_PER_STAGE = 2 * DMA;
+  static_assert(BK == kChunkRows && BN == kChunkRows, "tiles are one chunk wide");
+  static_assert(CHUNK_BYTES % (1024 * WAVES) == 0, "chunk/wave split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// dW^T tile [256 k][256 n] from packed X (xp) and dY (dp): a dense MFMA GEMM
+// over tokens, 32 per stage, through a ring of NST LDS stages filled by
+// buffer-to-LDS loads of whole chunks (same schedule as the sparse GEMM).
+template <class G, typename O>
+__global__ __launch_bounds__(G::THREADS, 1) void wgrad_packed_kernel(const uint16_t* __restrict__ dp,
+                                                                   const uint16_t* __restrict__ xp, int T, int N,
+                                                                   int K, const uint32_t* __restrict__ meta,
+                                                                   O* __restrict__ dWv, O* __restrict__ dWd,
+                                                                   int accumulate) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wk = wave % G::WGK, wn = wave / G::WGK;
+  const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
+  int tk, tn;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_k, tiles_n, 8, tk, tn);
+  const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
+  const int64_t Tch = (T + kChunkTokens - 1) / kChunkTokens;
+  const int stages = (int)Tch;
+  const uint16_t* const xs = xp + (int64_t)tk * Tch * kChunkElems;
+  const uint16_t* const ds = dp + (int64_t)tn * Tch * kChunkElems;
+  const uint32_t src0 = (uint32_t)(wave * G::DMA * 1024);      // this wave's part of a chunk
+  const uint32_t lane_off = (uint32_t)(lane * 16);
+
+  auto issue = [&](int s) {
+    char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+    const bool live = s < stages;                   // past the end: empty resources read 0
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs + (int64_t)s * kChunkElems, live ? G::CHUNK_BYTES : 0);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(ds + (int64_t)s * kChunkElems, live ? G::CHUNK_BYTES : 0);
+#pragma unroll
+    for (int j = 0; j < G::DMA; ++j) dma16(rx, base + src0 + j * 1024, src0 + j * 1024 + lane_off);
+#pragma unroll
+    for (int j = 0; j < G::DMA; ++j) dma16(rd, base + G::CHUNK_BYTES + src0 + j * 1024, src0 + j * 1024 + lane_off);
+  };
+
+  // fragment offsets: row r, 16-token step ks uses granule 2*ks + lane/32
+  int x_off[2][G::FK], d_off[2][G::FN];
+#pragma unroll
+  for (int a = 0; a < G::FK; ++a) {
+    const int row = wk * G::WK + a * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) x_off[ks][a] = row * 64 + (((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)) << 4);
+  }
 #pragma unroll
   for (int b = 0; b < G::FN; ++b) {
-    const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
-    if (n >= N) continue;
+    const int row = wn * G::WN + b * 32 + (lane & 31);
 #pragma unroll
-    for (int a = 0; a < G::FK; ++a) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
-        if (k >= K) continue;
-        const int64_t g = k >> 2;
-        const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
-        const uint32_t i0 = nib & 3u, i1 = nib >> 2;
-        const float r0 = acc[a][b][4 * q], r1 = acc[a][b][4 * q + 1];
-        const float r2 = acc[a][b][4 * q + 2], r3 = acc[a][b][4 * q + 3];
-        // i0 < i1: i0 in {0,1,2}, i1 in {1,2,3}; selects without indexing registers
-        float v0 = i0 == 0 ? r0 : (i0 == 1 ? r1 : r2);
-        float v1 = i1 == 3 ? r3 : (i1 == 2 ? r2 : r1);
-        O* vp = dWv + n * (K / 2) + 2 * g;
-        if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
-        store_pair(vp, v0, v1);
-        if (dWd) {
-          O* dp = dWd + n * K + k;
-          const float x[4] = {(i0 == 0) ? r0 : 0.f, (i0 == 1 || i1 == 1) ? r1 : 0.f,
-                              (i0 == 2 || i1 == 2) ? r2 : 0.f, (i1 == 3) ? r3 : 0.f};
-          store_quad(dp, x, accumulate);
-        }
-      }
-    }
+    for (int ks = 0; ks < 2; ++ks)
+      d_off[ks][b] = G::CHUNK_BYTES + row * 64 + (((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)) << 4);
   }
+
+  struct Frags {
+    bf16x8 x[G::FK];
+    bf16x8 d[G::FN];
+  };
+  auto read_frags = [&](Frags& f, int s, int ks) {
+    const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+#pragma unroll
+    for (int a = 0; a < G::FK; ++a) f.x[a] = *reinterpret_cast<const bf16x8*>(base + x_off[ks][a]);
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b) f.d[b] = *reinterpret_cast<const bf16x8*>(base + d_off[ks][b]);
+  };
+
+  f32x16 acc[G::FK][G::FN];
+#pragma unroll
+  for (int a = 0; a < G::FK; ++a)
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b) acc[a][b] = f32x16{};
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b)
+#pragma unroll
+      for (int a = 0; a < G::FK; ++a)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], f.d[b], acc[a][b], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int p = 0; p < G::NST; ++p) issue(p);
+  wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 1)>();
+  barrier();
+  Frags f0, f1;
+  read_frags(f0, 0, 0);
+  for (int s = 0; s < stages; ++s) {
+    read_frags(f1, s, 1);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);                 // MFMAs stay ahead of the waits
+    wait_lgkmcnt0();                                   // this wave's reads of stage s are in registers
+    wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();    // stage s+1 landed (this wave's part)
+    barrier();                                         // everyone's part; stage s fully read
+    issue(s + G::NST);                                 // refill stage s's slot
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < stages) read_frags(f0, s + 1, 0);
+    mma(f1);
+  }
+  wait_vmcnt<0>();
+  wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+}
+
+typedef PGeo<256, 256, 4, 2, 4> PGeoBig;
+
+int64_t chunks_of(int64_t C) { return (C + kChunkRows - 1) / kChunkRows; }
+int64_t token_chunks(int64_t T) { return (T + kChunkTokens - 1) / kChunkTokens; }
+
+hipError_t launch_pack(const uint16_t* src, int64_t T, int64_t C, uint16_t* dst, hipStream_t s) {
+  const int64_t n = chunks_of(C) * token_chunks(T);
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(n < (1 << 20) ? n : (1 << 20));
+  pack_tokens_kernel<<<grid, 256, 0, s>>>(src, (int)T, (int)C, chunks_of(C), token_chunks(T), dst);
+  return hipGetLastError();
+}
+
+template <typename O>
+hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int64_t N, int64_t K,
+                         const uint32_t* meta, O* dWv, O* dWd, int accumulate, hipStream_t s) {
+  typedef PGeoBig G;
+  auto kern = wgrad_packed_kernel<G, O>;
+  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t nb = chunks_of(K) * chunks_of(N);
+  kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv, dWd, accumulate);
+  return hipGetLastError();
 }
 
 typedef WGeo<256, 256, 4, 2, 4> WGeoBig;
 
 }  // namespace
 
+int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K) {
+  return (chunks_of(K) + chunks_of(N)) * token_chunks(T) * kChunkElems * 2;
+}
+
+
+int64_t packed_tokens_bytes(int64_t T, int64_t C) { return chunks_of(C) * token_chunks(T) * kChunkElems * 2; }
+
+hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s) {
+  return launch_pack((const uint16_t*)M, T, C, (uint16_t*)packed, s);
+}
+
+hipError_t launch_masked_wgrad_packed(Dt out, const void* dY_packed, const void* X_packed, int64_t T, int64_t N,
+                                      int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
+                                      int accumulate, hipStream_t s) {
+  const uint16_t* dp = (const uint16_t*)dY_packed;
+  const uint16_t* xp = (const uint16_t*)X_packed;
+  if (out == Dt::BF16)
+    return launch_packed(dp, xp, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense, accumulate, s);
+  return launch_packed(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
+}
+
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
-                               hipStream_t s) {
+                               void* workspace, hipStream_t s) {
   const bool fast = in == Dt::BF16 && K % 8 == 0 && N % 8 == 0;
   if (!fast) return launch_wgrad_generic(in, out, dY, X, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
+  if (workspace != nullptr) {
+    // packed path: transpose both operands into token chunks, then one GEMM
+    char* xp = (char*)workspace;
+    char* dp = xp + packed_tokens_bytes(T, K);
+    hipError_t e = launch_pack_tokens(X, T, K, xp, s);
+    if (e != hipSuccess) return e;
+    e = launch_pack_tokens(dY, T, N, dp, s);
+    if (e != hipSuccess) return e;
+    return launch_masked_wgrad_packed(out, dp, xp, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
+  }
   typedef WGeoBig G;
   const int64_t nb = cdiv(K, G::BK) * cdiv(N, G::BN);
   if (out == Dt::BF16) {

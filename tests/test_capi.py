@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -50,6 +50,13 @@ def test_size_queries(lib):
     assert S.slope_lowrank_workspace_bytes(64, 256, 8, 256) >= 64 * 8 * 4 + 256 * 16 * 2
     assert S.slope_lowrank_workspace_bytes(64, 256, 0, 256) == 0
     assert S.slope_lowrank_workspace_bytes(0, 256, 8, 256) == 0
+    # wgrad: X and dY as 256-column x 32-token bf16 chunks
+    assert S.slope_wgrad_workspace_bytes(8192, 27648, 9216) == (36 + 108) * 256 * 256 * 32 * 2
+    assert S.slope_wgrad_workspace_bytes(33, 8, 260) == (2 + 1) * 2 * 256 * 32 * 2
+    assert S.slope_wgrad_workspace_bytes(0, 8, 8) == 0
+    assert S.slope_packed_tokens_bytes(8192, 9216) == 36 * 256 * 16384
+    assert S.slope_packed_tokens_bytes(33, 260) + S.slope_packed_tokens_bytes(33, 8) == \
+        S.slope_wgrad_workspace_bytes(33, 8, 260)
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails its checks first
@@ -74,8 +81,21 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
     assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, FAKE, 16, FAKE, None) == -4
     assert lib.slope_spmm_bwd_dx(bf, bf, FAKE, 4, 6, FAKE, FAKE, 8, FAKE, None) == -2
-    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 4, 8, 6, FAKE, FAKE, None, 0, None) == -2
-    assert lib.slope_masked_wgrad(bf, bf, FAKE, None, 4, 8, 8, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 4, 8, 6, FAKE, FAKE, None, 0, None, 0, None) == -2
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, None, 4, 8, 8, FAKE, FAKE, None, 0, None, 0, None) == -1
+    # a workspace that is given must be large enough and aligned
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, FAKE, 16, None) == -4
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, FAKE + 8, 1 << 30,
+                                  None) == -3
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, FAKE, -1, None) == -1
+    # packing: bf16 only, C % 8, enough room
+    assert lib.slope_pack_tokens(f32, FAKE, 32, 256, FAKE, 1 << 30, None) == -6
+    assert lib.slope_pack_tokens(bf, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
+    assert lib.slope_pack_tokens(bf, FAKE, 32, 256, FAKE, 1024, None) == -4
+    assert lib.slope_pack_tokens(bf, None, 32, 256, FAKE, 1 << 30, None) == -1
+    assert lib.slope_masked_wgrad_packed(bf, FAKE, FAKE, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
+    assert lib.slope_masked_wgrad_packed(bf, FAKE, None, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(7, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
 

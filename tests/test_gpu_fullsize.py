@@ -12,7 +12,8 @@ spmm_fwd (+ adapter) -> spmm_bwd_dx -> masked_wgrad.  Then:
 * double pruning: sampled column groups of W_s, pruned again by the oracle,
   bit-exact against the matching rows of W_dp^T;
 * products: sampled token x feature blocks against the oracle (normwise 1e-2
-  for bf16 outputs, 1e-5 for the fp32 workload).
+  for bf16 outputs, 1e-5 for the fp32 workload); the weight gradient goes
+  through the packed operands as the benchmark runs it.
 """
 import numpy as np
 import pytest
@@ -64,7 +65,14 @@ def _run_path(d, T, N, K, r, tdt):
     dX = torch.empty((T, K), dtype=tdt, device="cuda")
     S.slope_spmm_bwd_dx(dY, dp.values, dp.meta, K, dX)
     dW = torch.empty((N, K // 2), dtype=tdt, device="cuda")
-    S.slope_masked_wgrad(dY, X, c.meta, dW)
+    if tdt == torch.bfloat16:   # the benchmark's form: packed operands, then the GEMM
+        Xp = torch.empty(S.slope_packed_tokens_bytes(T, K), dtype=torch.uint8, device="cuda")
+        dYp = torch.empty(S.slope_packed_tokens_bytes(T, N), dtype=torch.uint8, device="cuda")
+        S.slope_pack_tokens(X, Xp)
+        S.slope_pack_tokens(dY, dYp)
+        S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, c.meta, dW)
+    else:
+        S.slope_masked_wgrad(dY, X, c.meta, dW)
     torch.cuda.synchronize()
     out.update(vs=c.values, ms=c.meta, vdp=dp.values, mdp=dp.meta, Y=Y, dX=dX, dW=dW)
     return out

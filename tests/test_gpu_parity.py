@@ -219,15 +219,21 @@ WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68)
                 (0, 64, 64), (257, 264, 520)]
 
 
+def wgrad_ws(T, N, K):
+    return torch.empty(max(16, S.slope_wgrad_workspace_bytes(T, N, K)), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["direct", "packed"])
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 @pytest.mark.parametrize("T,N,K", WGRAD_SHAPES)
-def test_masked_wgrad(T, N, K, out_dt):
-    say(f"masked_wgrad T={T} N={N} K={K} out={out_dt}")
+def test_masked_wgrad(T, N, K, out_dt, packed):
+    say(f"masked_wgrad T={T} N={N} K={K} out={out_dt} packed={packed}")
     d = _layer(T, N, K, 1, "bf16", seed=5 * T + N + K)
     v_ref, d_ref = oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)
+    ws = wgrad_ws(T, N, K) if packed else None
     dWv = empty((N, K // 2), torch_dtype(out_dt))
     dWd = empty((N, K), torch_dtype(out_dt))
-    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv, dWd)
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv, dWd, workspace=ws)
     torch.cuda.synchronize()
     assert normwise(host_f64(dWv), v_ref) <= TOL["bf16"]
     assert normwise(host_f64(dWd), d_ref) <= TOL["bf16"]
@@ -235,9 +241,83 @@ def test_masked_wgrad(T, N, K, out_dt):
     # accumulation adds to what is there
     base = torch.randn((N, K // 2), device="cuda").to(torch_dtype(out_dt))
     acc = base.clone()
-    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), acc, accumulate=True)
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), acc, accumulate=True, workspace=ws)
     torch.cuda.synchronize()
     assert normwise(host_f64(acc), v_ref + host_f64(base)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T,N,K", [(300, 520, 272), (257, 264, 520), (1, 64, 128), (2048, 512, 768)])
+def test_masked_wgrad_packed_matches_direct(T, N, K):
+    """Both kernels feed the same operands to the same MFMA positions in the
+    same token order, so with and without the workspace results are bitwise equal."""
+    say(f"masked_wgrad packed==direct T={T} N={N} K={K}")
+    d = _layer(T, N, K, 1, "bf16", seed=11 * T + N + K)
+    out = []
+    for ws in (None, wgrad_ws(T, N, K)):
+        dWv = empty((N, K // 2), torch.bfloat16)
+        S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv, workspace=ws)
+        torch.cuda.synchronize()
+        out.append(host(dWv))
+    assert np.array_equal(out[0], out[1])
+
+
+def _pack_reference(bits, T, C):
+    """The token-chunk layout as include/slope.h states it, built with numpy."""
+    Tch, Cch = -(-T // 32), -(-C // 256)
+    pad = np.zeros((Tch * 32, Cch * 256), dtype=np.uint16)
+    pad[:T, :C] = bits
+    out = np.zeros((Cch, Tch, 256, 4, 8), dtype=np.uint16)
+    for c in range(Cch):
+        for s in range(Tch):
+            blk = pad[32 * s:32 * s + 32, 256 * c:256 * c + 256].T.reshape(256, 4, 8)   # [row][granule][token]
+            for row in range(256):
+                for g in range(4):
+                    out[c, s, row, g ^ ((row >> 2) & 3)] = blk[row, g]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("T,C", [(32, 256), (70, 264), (1, 8), (257, 520)])
+def test_pack_tokens_layout(T, C):
+    say(f"pack_tokens T={T} C={C}")
+    rng = np.random.default_rng(T * 1000 + C)
+    bits = rng.integers(0, 1 << 16, size=(T, C), dtype=np.uint16)
+    packed = torch.empty(S.slope_packed_tokens_bytes(T, C), dtype=torch.uint8, device="cuda")
+    packed.fill_(0xAB)
+    S.slope_pack_tokens(dev(bits), packed)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _pack_reference(bits, T, C))
+
+
+@pytest.mark.parametrize("T,N,K", [(300, 520, 272), (33, 8, 1032)])
+def test_masked_wgrad_packed_entry(T, N, K):
+    """Packing by hand and calling the packed GEMM equals the one-call form."""
+    say(f"masked_wgrad_packed T={T} N={N} K={K}")
+    d = _layer(T, N, K, 1, "bf16", seed=T + 7 * K)
+    Xd, dYd = dev(d["X"]), dev(d["dY"])
+    Xp = torch.empty(S.slope_packed_tokens_bytes(T, K), dtype=torch.uint8, device="cuda")
+    dYp = torch.empty(S.slope_packed_tokens_bytes(T, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_tokens(Xd, Xp)
+    S.slope_pack_tokens(dYd, dYp)
+    a = empty((N, K // 2), torch.bfloat16)
+    dd = empty((N, K), torch.bfloat16)
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, dev_meta(d["ms"]), a, dd)
+    b = empty((N, K // 2), torch.bfloat16)
+    S.slope_masked_wgrad(dYd, Xd, dev_meta(d["ms"]), b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), host(b))
+    v_ref, d_ref = oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)
+    assert normwise(host_f64(a), v_ref) <= TOL["bf16"]
+    assert normwise(host_f64(dd), d_ref) <= TOL["bf16"]
+
+
+def test_masked_wgrad_short_workspace():
+    T, N, K = 64, 256, 256
+    d = _layer(T, N, K, 1, "bf16", seed=1)
+    dWv = empty((N, K // 2), torch.bfloat16)
+    short = torch.empty(S.slope_wgrad_workspace_bytes(T, N, K) - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(S.SlopeError):
+        S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv, workspace=short)
 
 
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
@@ -291,10 +371,14 @@ def test_integer_inputs_bit_exact(T, N, K):
     S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dX)
     dWv = empty((N, K // 2), torch.float32)
     S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWv)
+    dWp = empty((N, K // 2), torch.float32)
+    S.slope_masked_wgrad(dev(d["dY"]), dev(d["X"]), dev_meta(d["ms"]), dWp, workspace=wgrad_ws(T, N, K))
     torch.cuda.synchronize()
     assert np.array_equal(host_f64(Y), oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"]))
     assert np.array_equal(host_f64(dX), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N))
-    assert np.array_equal(host_f64(dWv), oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)[0])
+    dw_ref = oracle.masked_wgrad(d["dY"], d["X"], d["ms"], K)[0]
+    assert np.array_equal(host_f64(dWv), dw_ref)
+    assert np.array_equal(host_f64(dWp), dw_ref)
 
 
 def test_empty_and_degenerate():
