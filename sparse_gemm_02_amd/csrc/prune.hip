@@ -204,6 +204,99 @@ __global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restr
   }
 }
 
+// Wide-access variant for bf16 with K % 16 == 0 and N % 16 == 0.  Block tile:
+// 128 rows n x 128 columns k.  Phase 1: eight lanes per row read one 128-byte
+// line of compressed values and the matching metadata words, decompress four
+// groups each with selects and write 32 bytes of the dense row to LDS.  Phase
+// 2: thread (column pair cp, quarter q) reads rows 32q .. 32q+31 of columns
+// 2cp and 2cp+1 as 32-bit words, prunes each column's eight groups of four and
+// writes 32 bytes of values, one metadata word (and 32 mask bytes) per column;
+// the four quarters of a column are adjacent lanes, so each output row is
+// written as one 128-byte run.  LDS rows are 68 words (4 of padding) with word
+// w of row n stored at w ^ (16 * ((n / 32) % 4)): both phases are free of bank
+// conflicts.
+constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit words
+
+__global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(const uint16_t* __restrict__ vals,
+                                                                    const uint32_t* __restrict__ meta, int64_t N,
+                                                                    int64_t K, uint16_t* __restrict__ out_vals,
+                                                                    uint32_t* __restrict__ out_meta,
+                                                                    uint8_t* __restrict__ out_mask) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[DW_T * DW_PITCH];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.y * DW_T, k0 = (int64_t)blockIdx.x * DW_T;
+  const int64_t in_wpr = cdiv(K / 4, 8), out_wpr = cdiv(N / 4, 8);
+
+  // phase 1: row r, dense columns 16c .. 16c+15 (compressed groups 4c .. 4c+3)
+  const int c = tid & 7;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 32 + (tid >> 3);
+    const int64_t row = n0 + r, kc = k0 + 16 * c;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    uint32_t nibs = 0;
+    if (row < N && kc < K) {                          // K % 16 == 0: the 16 columns are all in or all out
+      v = *reinterpret_cast<const u32x4*>(vals + row * (K / 2) + kc / 2);
+      nibs = meta[row * in_wpr + (kc >> 5)] >> (16 * (c & 1));
+    }
+    uint32_t d[8];                                    // 16 dense bf16, two per word
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t nib = (nibs >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
+      const uint32_t w = v[g], v0 = w & 0xFFFFu, v1 = w >> 16;
+      uint32_t e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = i1 == (uint32_t)j ? v1 : (i0 == (uint32_t)j ? v0 : 0u);
+      d[2 * g] = e[0] | (e[1] << 16);
+      d[2 * g + 1] = e[2] | (e[3] << 16);
+    }
+    const int swz = 16 * ((r >> 5) & 3);
+    uint32_t* dst = tile + r * DW_PITCH;
+    *reinterpret_cast<u32x4*>(dst + ((8 * c) ^ swz)) = u32x4{d[0], d[1], d[2], d[3]};
+    *reinterpret_cast<u32x4*>(dst + ((8 * c + 4) ^ swz)) = u32x4{d[4], d[5], d[6], d[7]};
+  }
+  __syncthreads();
+
+  // phase 2: columns 2cp, 2cp+1 of the tile, rows 32q .. 32q+31
+  const int q = tid & 3, cp = tid >> 2;
+  uint32_t col[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) col[i] = tile[(32 * q + i) * DW_PITCH + (cp ^ (16 * q))];
+  const int64_t g0 = (n0 >> 2) + 8 * q;               // first output group (n / 4)
+  const int64_t left = N / 4 - g0;
+  const int ngroups = left <= 0 ? 0 : (left < 8 ? (int)left : 8);   // 0, 4 or 8 (N % 16 == 0)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t krow = k0 + 2 * cp + h;
+    if (krow >= K || ngroups == 0) continue;
+    uint32_t word = 0, ov[8], mw[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint16_t e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = (uint16_t)(col[4 * g + j] >> (16 * h));
+      const uint32_t keep = top2_of_4(mag_key(e[0]), mag_key(e[1]), mag_key(e[2]), mag_key(e[3]));
+      const uint32_t nib = pair_nibble(keep);
+      word |= nib << (4 * g);
+      const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+      const uint32_t a = i0 == 0 ? e[0] : (i0 == 1 ? e[1] : e[2]);
+      const uint32_t b = i1 == 3 ? e[3] : (i1 == 2 ? e[2] : e[1]);
+      ov[g] = a | (b << 16);
+      mw[g] = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
+    }
+    if (ngroups < 8) word &= 0xFFFFu;
+    out_meta[krow * out_wpr + (g0 >> 3)] = word;
+    uint32_t* ovp = reinterpret_cast<uint32_t*>(out_vals + krow * (N / 2) + 2 * g0);
+    *reinterpret_cast<u32x4*>(ovp) = u32x4{ov[0], ov[1], ov[2], ov[3]};
+    if (ngroups == 8) *reinterpret_cast<u32x4*>(ovp + 4) = u32x4{ov[4], ov[5], ov[6], ov[7]};
+    if (out_mask) {
+      uint32_t* mp = reinterpret_cast<uint32_t*>(out_mask + krow * N + 4 * g0);
+      *reinterpret_cast<u32x4*>(mp) = u32x4{mw[0], mw[1], mw[2], mw[3]};
+      if (ngroups == 8) *reinterpret_cast<u32x4*>(mp + 4) = u32x4{mw[4], mw[5], mw[6], mw[7]};
+    }
+  }
+}
+
 int grid_for(int64_t work, int per_block) {
   int64_t b = cdiv(work, per_block);
   const int64_t cap = 256 * 32;  // enough waves in flight on 256 CUs
@@ -240,6 +333,12 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
   if (N == 0 || K == 0) return hipSuccess;
+  if (dt == Dt::BF16 && K % 16 == 0 && N % 16 == 0) {
+    dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
+    double_prune_wide_kernel<<<g, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,
+                                                    meta_dpT, mask_dpT);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)cdiv(K, DP_TK), (unsigned)cdiv(N, DP_TN));
   if (dt == Dt::BF16)
     double_prune_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,

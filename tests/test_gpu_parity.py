@@ -114,7 +114,8 @@ def test_compress24_user_masks(dt):
     assert int(inv.item()) == inv_ref
 
 
-DP_SHAPES = [(64, 128), (100, 68), (256, 384), (36, 260), (4, 4), (520, 132)]
+DP_SHAPES = [(64, 128), (100, 68), (256, 384), (36, 260), (4, 4), (520, 132),
+             (144, 272), (400, 528), (16, 16), (1040, 144), (1024, 2048)]  # last five: 16-aligned kernel
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
