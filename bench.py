@@ -4,8 +4,12 @@ One step is one pass of the whole hot path over the four linears of an OPT-66B
 transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 36864->9216; T = 8192 tokens, adapter rank 72, bf16 with fp32 accumulation):
 
-    prune24 -> compress24 -> double_prune -> spmm_fwd (+ fused adapter)
-            -> spmm_bwd_dx -> masked_wgrad
+    prune24 -> compress24 -> double_prune -> pack_sparse (W_s and W_dp^T
+    into tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx
+    -> pack_tokens (X and dY into token chunks) -> masked_wgrad
+
+The three products run on the packed operands (the *_packed entry points);
+the packing passes are part of the step.
 
 prune24 and compress24 run once per layer in training (the forward mask is
 static); they are kept inside the timed step so the step covers every kernel of
@@ -80,6 +84,9 @@ class Linear:
         self.dW = torch.empty((N, K // 2), dtype=bf, device=dev)
         import sparse_gemm_02_amd as S
         self.ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, K, r, N)), dtype=torch.uint8, device=dev)
+        # sparse operands as tile chunks (W_s for the forward, W_dp^T for dX)
+        self.ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device=dev)
+        self.pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device=dev)
         # weight-gradient operands as transposed token chunks
         self.Xp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, K)), dtype=torch.uint8, device=dev)
         self.dYp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, N)), dtype=torch.uint8, device=dev)
@@ -94,7 +101,13 @@ class Linear:
         return {"spmm_fwd": T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": T * N * K, "masked_wgrad": T * N * K}
 
 
-OPS = ("prune24", "compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "pack_tokens", "masked_wgrad")
+OPS = ("prune24", "compress24", "double_prune", "pack_sparse", "spmm_fwd", "spmm_bwd_dx", "pack_tokens",
+       "masked_wgrad")
+
+
+def pack_sparse(S, li):
+    S.slope_pack_sparse(li.vs, li.ms, li.N, li.K, li.ps)
+    S.slope_pack_sparse(li.vdp, li.mdp, li.K, li.N, li.pd)
 
 
 def pack(S, li):
@@ -113,8 +126,9 @@ def step(lins, S, ev=None):
             ("prune24", lambda: S.slope_prune24(li.W, li.mask)),
             ("compress24", lambda: S.slope_compress24(li.W, li.mask, li.vs, li.ms)),
             ("double_prune", lambda: S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)),
-            ("spmm_fwd", lambda: S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
-            ("spmm_bwd_dx", lambda: S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)),
+            ("pack_sparse", lambda: pack_sparse(S, li)),
+            ("spmm_fwd", lambda: S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
+            ("spmm_bwd_dx", lambda: S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX)),
             ("pack_tokens", lambda: pack(S, li)),
             ("masked_wgrad", lambda: wgrad(S, li)),
         )
@@ -216,6 +230,7 @@ def profile_mode(args, wl, T):
         S.slope_prune24(li.W, li.mask)
         S.slope_compress24(li.W, li.mask, li.vs, li.ms)
         S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+        pack_sparse(S, li)
         pack(S, li)
     torch.cuda.synchronize()
     op = args.profile_op
@@ -227,10 +242,12 @@ def profile_mode(args, wl, T):
                 S.slope_compress24(li.W, li.mask, li.vs, li.ms)
             elif op == "double_prune":
                 S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+            elif op == "pack_sparse":
+                pack_sparse(S, li)
             elif op == "spmm_fwd":
-                S.slope_spmm_fwd(li.X, li.vs, li.ms, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
+                S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
             elif op == "spmm_bwd_dx":
-                S.slope_spmm_bwd_dx(li.dY, li.vdp, li.mdp, li.K, li.dX)
+                S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX)
             elif op == "pack_tokens":
                 pack(S, li)
             elif op == "masked_wgrad":
@@ -321,7 +338,8 @@ def main():
     # algorithmic HBM bytes: per weight for the pruning ops, per activation
     # element (read + written once) for the packing pass
     hbm = {"prune24": lambda l: 3.0 * l.N * l.K, "compress24": lambda l: 4.125 * l.N * l.K,
-           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
+           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_sparse": lambda l: 2 * 2 * 1.125 * l.N * l.K,
+           "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
     for op, f in hbm.items():
         by = sum(f(l) for l in lins)
         ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9

@@ -174,6 +174,42 @@ slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const voi
                                 void* dW_dense_or_null, int accumulate, void* workspace_or_null,
                                 int64_t workspace_bytes, void* stream);
 
+/* Bytes of the tile-chunk form of a compressed bf16 matrix [rows, cols] (see
+ * slope_pack_sparse).  Host-only; SLOPE_ERR_SHAPE if cols % 16 != 0,
+ * SLOPE_ERR_UNSUPPORTED if cols > 2^21. */
+slope_status slope_packed_sparse_bytes(int64_t rows, int64_t cols, int64_t* bytes);
+
+/* Tile-chunk copy of a compressed bf16 matrix (values [rows, cols/2],
+ * meta [rows, ceil(cols/32)] as written by slope_compress24 or
+ * slope_double_prune), the operand format of the *_packed products.  Chunk
+ * (t, s) holds rows 256t .. 256t+255 and dense columns 64s .. 64s+63, 18432
+ * bytes at offset (t * ceil(cols/64) + s) * 18432: first the 32 values of
+ * each row (64 bytes at row*64; the 16-byte granule c of a row sits at
+ * c ^ ((row / 4) % 4)), then the row's two metadata words (8 bytes at
+ * 16384 + row*8).  Rows past `rows` and columns past `cols` are 0.  packed:
+ * caller-owned device memory of slope_packed_sparse_bytes(rows, cols) bytes,
+ * overwritten.  Errors: SLOPE_ERR_UNSUPPORTED for float32 or cols > 2^21,
+ * SLOPE_ERR_SHAPE if cols % 16 != 0, SLOPE_ERR_WORKSPACE if packed_bytes is
+ * short. */
+slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_t* meta, int64_t rows, int64_t cols,
+                               void* packed, int64_t packed_bytes, void* stream);
+
+/* slope_spmm_fwd with W_s given in tile-chunk form (slope_pack_sparse of
+ * values_s, meta_s; rows N, cols K): same result, bitwise.  bf16 inputs only;
+ * K % 16 == 0, K <= 2^21, N % 4 == 0, adapter rank r <= 128.  Errors as
+ * slope_spmm_fwd, plus SLOPE_ERR_UNSUPPORTED / SLOPE_ERR_SHAPE for the limits
+ * above. */
+slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
+                                   int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* Y,
+                                   void* stream);
+
+/* slope_spmm_bwd_dx with W_dpT given in tile-chunk form (slope_pack_sparse of
+ * values_dpT, meta_dpT; rows K, cols N): same result, bitwise.  bf16 inputs
+ * only; N % 16 == 0, N <= 2^21, K % 4 == 0. */
+slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                                      const void* packed_dpT, int64_t K, void* dX, void* stream);
+
 /* Bytes of a bf16 matrix M [T, C] rewritten as token chunks (see
  * slope_pack_tokens).  Host-only. */
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);

@@ -13,6 +13,8 @@ Tensor conventions (see include/slope.h):
   compressed metadata [rows, ceil(cols/32)] torch.int32 holding the uint32 words
   adapter workspace   torch.uint8 (or any dtype) of slope_lowrank_workspace_bytes()
   wgrad workspace     torch.uint8 (or any dtype) of slope_wgrad_workspace_bytes()
+  packed operands     torch.uint8 buffers of slope_packed_sparse_bytes() (sparse
+                      tile chunks) or slope_packed_tokens_bytes() (token chunks)
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ __all__ = [
     "slope_prune24", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
+    "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -54,6 +57,10 @@ _SIGS = {
     "slope_masked_wgrad": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _i64, _vp]),
     "slope_wgrad_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
     "slope_packed_tokens_bytes": (_i32, [_i64, _i64, _P_I64]),
+    "slope_packed_sparse_bytes": (_i32, [_i64, _i64, _P_I64]),
+    "slope_pack_sparse": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
@@ -190,6 +197,33 @@ def slope_masked_wgrad(dY, X, meta_s, dW_values, dW_dense=None, accumulate=False
                                                               _nn(meta_s), _nn(dW_values), _p(dW_dense),
                                                               int(bool(accumulate)), _p(workspace), wb,
                                                               _s(stream)))
+
+
+def slope_packed_sparse_bytes(rows: int, cols: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_packed_sparse_bytes", library().slope_packed_sparse_bytes(rows, cols, ctypes.byref(b)))
+    return b.value
+
+
+def slope_pack_sparse(values, meta, rows, cols, packed, stream=None) -> None:
+    nb = packed.numel() * packed.element_size()
+    _check("slope_pack_sparse", library().slope_pack_sparse(_dt(values), _nn(values), _nn(meta), rows, cols,
+                                                            _nn(packed), nb, _s(stream)))
+
+
+def slope_spmm_fwd_packed(X, packed_s, N, Y, L=None, R=None, workspace=None, stream=None) -> None:
+    T, K = X.shape
+    r = int(L.shape[1]) if L is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_spmm_fwd_packed", library().slope_spmm_fwd_packed(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), N,
+                                                                    _p(L), _p(R), r, _p(workspace), wb, _nn(Y),
+                                                                    _s(stream)))
+
+
+def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, stream=None) -> None:
+    T, N = dY.shape
+    _check("slope_spmm_bwd_dx_packed", library().slope_spmm_bwd_dx_packed(_dt(dY), _dt(dX), _nn(dY), T, N,
+                                                                          _nn(packed_dpT), K, _nn(dX), _s(stream)))
 
 
 def slope_packed_tokens_bytes(T: int, C: int) -> int:

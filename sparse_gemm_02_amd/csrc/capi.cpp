@@ -36,6 +36,10 @@ slope_status ptr(const void* p, bool required) {
     if (_st != SLOPE_OK) return _st;       \
   } while (0)
 
+// Packed sparse operands: reduction width up to 2^21 (chunk resources stay
+// below 2 GiB), adapter rank up to 128 (the MFMA epilogue).
+constexpr int64_t kPackedMaxCols = 1 << 21, kPackedMaxRank = 128;
+
 int64_t workspace_need(int64_t T, int64_t K, int64_t r, int64_t N) { return slope::lowrank_workspace_bytes(T, K, r, N); }
 
 }  // namespace
@@ -188,6 +192,74 @@ slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const voi
   return from_hip(slope::launch_masked_wgrad((Dt)in_dt, (Dt)out_dt, dY, X, T, N, K, meta_s, dW_values,
                                              dW_dense_or_null, accumulate, workspace_or_null,
                                              (hipStream_t)stream));
+}
+
+slope_status slope_packed_sparse_bytes(int64_t rows, int64_t cols, int64_t* bytes) {
+  if (!bytes || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  if (cols % 16) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::packed_sparse_bytes(rows, cols);
+  return SLOPE_OK;
+}
+
+slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_t* meta, int64_t rows, int64_t cols,
+                               void* packed, int64_t packed_bytes, void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0 || packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values, true));
+  SLOPE_TRY(ptr(meta, true));
+  SLOPE_TRY(ptr(packed, true));
+  if (dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (cols % 16) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_bytes < slope::packed_sparse_bytes(rows, cols)) return SLOPE_ERR_WORKSPACE;
+  return from_hip(slope::launch_pack_sparse(values, meta, rows, cols, packed, (hipStream_t)stream));
+}
+
+slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
+                                   int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* Y,
+                                   void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(packed_s, true));
+  SLOPE_TRY(ptr(Y, true));
+  const bool adapter = L_or_null && R_or_null && r > 0;
+  if (adapter) {
+    SLOPE_TRY(ptr(L_or_null, true));
+    SLOPE_TRY(ptr(R_or_null, true));
+  }
+  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (adapter) {
+    const int64_t need = workspace_need(T, K, r, N);
+    if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
+    if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
+  }
+  if (T == 0 || N == 0) return SLOPE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  slope::LowrankWs w;
+  if (adapter) {
+    w = slope::lowrank_layout((Dt)in_dt, workspace_or_null, T, K, r, N);
+    hipError_t e = slope::launch_lowrank_prepare((Dt)in_dt, X, L_or_null, R_or_null, T, K, r, N, w, s);
+    if (e != hipSuccess) return SLOPE_ERR_HIP;
+  }
+  return from_hip(slope::launch_spmm_packed((Dt)out_dt, X, T, K, packed_s, N, adapter ? &w : nullptr, Y, s));
+}
+
+slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                                      const void* packed_dpT, int64_t K, void* dX, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(dY, true));
+  SLOPE_TRY(ptr(packed_dpT, true));
+  SLOPE_TRY(ptr(dX, true));
+  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (N % 16 || K % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || N > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (T == 0 || K == 0) return SLOPE_OK;
+  return from_hip(slope::launch_spmm_packed((Dt)out_dt, dY, T, N, packed_dpT, K, nullptr, dX, (hipStream_t)stream));
 }
 
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes) {

@@ -33,9 +33,15 @@ struct Geo {
   static constexpr int A_DMA = A_BYTES / 1024 / WAVES, B_DMA = B_BYTES / 1024 / WAVES;
   static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + 1;
   static constexpr int META_WAVES = META_SLOT / 1024;  // waves that load one metadata KB each
+  // packed operand (tile chunks): a chunk holds one stage of a 256-row tile,
+  // the A slice (A_BYTES, already swizzled) then two metadata words per row;
+  // the stage's metadata sits in LDS after its B slice (one 4-byte load per lane)
+  static constexpr int META_STAGE = BM * 8, CHUNK_BYTES = A_BYTES + META_STAGE;
+  static constexpr int PSTAGE_BYTES = STAGE_BYTES + META_STAGE, PLDS_BYTES = NST * PSTAGE_BYTES;
   static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "tile/wave split");
   static_assert(META_WAVES <= WAVES, "metadata split");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES <= 160 * 1024 && PLDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(META_STAGE == 256 * WAVES, "one metadata load per wave and stage");
 };
 
 // acc[fm][ft] += R^T . (X L)^T over the adapter rank, from the prepared

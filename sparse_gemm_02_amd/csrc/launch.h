@@ -43,6 +43,15 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
                        const uint32_t* meta, int64_t M, const LowrankWs* ws, int64_t r, const void* R, void* Y,
                        hipStream_t s);
 
+// Tile chunks of a compressed bf16 operand [M, Kred] (Kred % 16 == 0,
+// Kred <= 2^21): size in bytes and the packing pass; launch_spmm_packed is
+// launch_spmm on that form (bf16 B; ws with ws->mfma, or nullptr).
+int64_t packed_sparse_bytes(int64_t M, int64_t Kred);
+hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t M, int64_t Kred, void* packed,
+                              hipStream_t s);
+hipError_t launch_spmm_packed(Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
+                              const LowrankWs* ws, void* Y, hipStream_t s);
+
 // dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional
 // accumulation.  With a workspace of wgrad_workspace_bytes(T, N, K) bytes the
 // bf16 path first packs X and dY into transposed token chunks there.

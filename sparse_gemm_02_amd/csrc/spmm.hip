@@ -54,12 +54,18 @@ namespace {
 //
 // Schedule per stage s (one barrier): read the second k-step's fragments of s,
 // issue the first k-step's MFMAs, wait for this wave's LDS reads and for stage
-// s+1, barrier, start the loads of stage s+NST into the slot stage s used (its
-// fragments are all in registers by then), read the first k-step's fragments
-// of s+1, issue the second k-step's MFMAs.  NST-1 stages stay in flight
-// through most of the loop.  The metadata ring of two slots (four stages)
-// holds stages s .. s+3, which needs NST == 3.
-template <class G, bool ADAPTER, typename O>
+// s+1, barrier, read the first k-step's fragments of s+1, issue the second
+// k-step's MFMAs with the loads of stage s+NST (into the slot stage s used,
+// whose fragments are all in registers by then) placed among them.  NST-1
+// stages stay in flight through most of the loop.  The metadata ring of two
+// slots (four stages) holds stages s .. s+3, which needs NST == 3.  Each lane
+// reads its own 16-bit half of a metadata word, so the index operand needs no
+// shift.
+//
+// PK: the sparse operand comes as tile chunks (see pack_sparse_kernel): each
+// stage loads one contiguous 18 KB chunk (values then metadata) instead of 256
+// separate 64-byte row pieces and a strided metadata read.
+template <class G, bool ADAPTER, typename O, bool PK>
 __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
     int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
@@ -70,7 +76,8 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
-  static_assert(G::NST == 3, "metadata ring holds four stages");
+  static_assert(PK || G::NST == 3, "metadata ring holds four stages");
+  constexpr int SLOT = PK ? G::PSTAGE_BYTES : G::STAGE_BYTES;
   const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
   const int wpr = (Kred / 4 + 7) / 8;               // metadata words per row
   const int stages = (Kred + G::KS - 1) / G::KS;
@@ -78,7 +85,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   const int rows_t = (int)((T - t0) < G::BT ? (T - t0) : G::BT);
 
   // resources cover exactly this block's valid rows
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(vals + m0 * (Kred / 2), (int64_t)rows_m * Kred);
+  const __amdgpu_buffer_rsrc_t ra =
+      PK ? make_rsrc(vals + (int64_t)tm * stages * (G::CHUNK_BYTES / 2), (int64_t)stages * G::CHUNK_BYTES)
+         : make_rsrc(vals + m0 * (Kred / 2), (int64_t)rows_m * Kred);
   const __amdgpu_buffer_rsrc_t rmeta = make_rsrc(meta + m0 * wpr, (int64_t)rows_m * wpr * 4);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bm + t0 * Kred, (int64_t)rows_t * Kred * 2);
 
@@ -103,18 +112,27 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   const uint32_t m_src = (uint32_t)(wave * 64 + lane) * wpr * 4;   // waves < META_WAVES
 
   auto issue = [&](int s) {
-    char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+    char* base = lds + (s % G::NST) * SLOT;
+    const uint32_t chunk = (uint32_t)s * G::CHUNK_BYTES;           // PK: this stage's chunk
 #pragma unroll
     for (int j = 0; j < G::A_DMA; ++j) {
-      const bool ok = s * 64 + a_k[j] < Kred;        // compressed bytes of a row = Kred
-      dma16(ra, base + wave * (G::A_BYTES / G::WAVES) + j * 1024, ok ? a_src[j] + s * 64 : kOutOfRange);
+      const uint32_t part = wave * (G::A_BYTES / G::WAVES) + j * 1024;
+      if (PK) {
+        dma16(ra, base + part, s < stages ? chunk + part + lane * 16 : kOutOfRange);
+      } else {
+        const bool ok = s * 64 + a_k[j] < Kred;      // compressed bytes of a row = Kred
+        dma16(ra, base + part, ok ? a_src[j] + s * 64 : kOutOfRange);
+      }
     }
 #pragma unroll
     for (int j = 0; j < G::B_DMA; ++j) {
       const bool ok = s * 64 + b_k[j] < Kred;
       dma16(rb, base + G::A_BYTES + wave * (G::B_BYTES / G::WAVES) + j * 1024, ok ? b_src[j] + s * 128 : kOutOfRange);
     }
-    if ((s & 1) == 0 && wave < G::META_WAVES) {      // words 2s .. 2s+3 of every row
+    if (PK) {                                        // the stage's metadata words
+      dma4(ra, base + G::A_BYTES + G::B_BYTES + wave * 256,
+           s < stages ? chunk + G::A_BYTES + wave * 256 + lane * 4 : kOutOfRange);
+    } else if ((s & 1) == 0 && wave < G::META_WAVES) {      // words 2s .. 2s+3 of every row
       const bool ok = 2 * s < wpr;
       dma16(rmeta, meta_lds + ((s >> 1) & 1) * G::META_SLOT + wave * 1024, ok ? m_src + s * 8 : kOutOfRange);
     } else {                                         // placeholder: same load count on every wave and stage
@@ -131,7 +149,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const int sw = (row >> 2) & 3;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_off[ks][fm] = row * 64 + (((2 * ks + (lane >> 5)) ^ sw) * 16);
-    m_off[fm] = row * 16;
+    m_off[fm] = row * (PK ? 8 : 16) + 2 * (lane >> 5);   // this lane's 16-bit half of the word
   }
 #pragma unroll
   for (int ft = 0; ft < G::FT; ++ft) {
@@ -143,7 +161,6 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
       b_off[ks][ft][1] = G::A_BYTES + row * 128 + (((4 * ks + 2 + (lane >> 5)) ^ sw) * 16);
     }
   }
-  const int ix_shift = 16 * (lane >> 5);
 
   struct Frags {
     bf16x8 a[G::FM];
@@ -151,12 +168,13 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     bf16x16 b[G::FT];
   };
   auto read_frags = [&](Frags& f, int s, int ks) {
-    const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
-    const char* mbase = meta_lds + ((s >> 1) & 1) * G::META_SLOT + ((s & 1) * 2 + ks) * 4;
+    const char* base = lds + (s % G::NST) * SLOT;
+    const char* mbase = PK ? base + G::A_BYTES + G::B_BYTES + ks * 4
+                           : meta_lds + ((s >> 1) & 1) * G::META_SLOT + ((s & 1) * 2 + ks) * 4;
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm) {
       f.a[fm] = *reinterpret_cast<const bf16x8*>(base + a_off[ks][fm]);
-      f.ix[fm] = (int)(*reinterpret_cast<const uint32_t*>(mbase + m_off[fm]) >> ix_shift);
+      f.ix[fm] = (int)*reinterpret_cast<const uint16_t*>(mbase + m_off[fm]);
     }
 #pragma unroll
     for (int ft = 0; ft < G::FT; ++ft) {
@@ -171,12 +189,14 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
     for (int ft = 0; ft < G::FT; ++ft) acc[fm][ft] = f32x16{};
+  auto mma_col = [&](const Frags& f, int ft) {
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
+      acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm], 0, 0);
+  };
   auto mma = [&](const Frags& f) {
 #pragma unroll
-    for (int ft = 0; ft < G::FT; ++ft)
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm)
-        acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm], 0, 0);
+    for (int ft = 0; ft < G::FT; ++ft) mma_col(f, ft);
   };
 
   // prologue: stages 0 .. NST-1 in flight; stage 0 landed and visible
@@ -194,10 +214,15 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     wait_lgkmcnt0();                                  // this wave's reads of stage s are in registers
     wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();   // this wave's loads of stage s+1 landed
     barrier();                                        // everyone's have; stage s fully read
-    issue(s + G::NST);                                // refill stage s's slot; past the end these read 0
-    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < stages) read_frags(f0, s + 1, 0);
-    mma(f1);
+    // the second k-step's MFMAs need nothing from the barrier: start them, and
+    // refill stage s's slot while they run (past the end these loads read 0)
+    mma_col(f1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + G::NST);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ft = 1; ft < G::FT; ++ft) mma_col(f1, ft);
   }
   wait_vmcnt<0>();
   if constexpr (ADAPTER) adapter_mma<G>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
@@ -206,19 +231,67 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
 
 typedef Geo<256, 256, 3, 2, 4> GeoBig;
 
-template <bool ADAPTER, typename O>
+// Tile chunks of a compressed bf16 matrix [M, Kred] (values [M, Kred/2],
+// metadata [M, ceil(Kred/32)]): chunk (tm, s) covers rows 256tm .. 256tm+255
+// and dense columns 64s .. 64s+63, at byte offset (tm * S + s) * CHUNK_BYTES
+// (S = ceil(Kred/64)): first the 32 values of each row (64 bytes at row*64,
+// 16-byte granule c at c ^ ((row/4) % 4)), then the two metadata words of each
+// row (8 bytes at A_BYTES + row*8).  Rows past M and columns past Kred are 0.
+template <class G>
+__global__ __launch_bounds__(256) void pack_sparse_kernel(const uint16_t* __restrict__ vals,
+                                                          const uint32_t* __restrict__ meta, int64_t M, int64_t Kred,
+                                                          int64_t stages, int64_t nchunks, char* __restrict__ out) {
+  static_assert(G::BM == 256 && G::KS == 64, "chunk geometry");
+  const int tid = threadIdx.x;
+  const int64_t wpr = (Kred / 4 + 7) / 8;
+  for (int64_t q = blockIdx.x; q < nchunks; q += gridDim.x) {
+    const int64_t tm = q / stages, s = q % stages;
+    char* chunk = out + q * G::CHUNK_BYTES;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {               // 256 rows x four 16-byte granules
+      const int r = it * 64 + (tid >> 2), c = tid & 3;
+      const int64_t row = tm * 256 + r, kb = s * 64 + c * 16;   // compressed byte offset within the row
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < M && kb < Kred) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vals) + row * Kred + kb);
+      *reinterpret_cast<u32x4*>(chunk + r * 64 + ((c ^ ((r >> 2) & 3)) << 4)) = v;
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {               // 256 rows x two metadata words
+      const int idx = it * 256 + tid, r = idx >> 1, w = idx & 1;
+      const int64_t row = tm * 256 + r, word = 2 * s + w;
+      const uint32_t m = (row < M && word < wpr) ? meta[row * wpr + word] : 0u;
+      *reinterpret_cast<uint32_t*>(chunk + G::A_BYTES + r * 8 + w * 4) = m;
+    }
+  }
+}
+
+template <bool ADAPTER, typename O, bool PK>
 hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
                       const LowrankWs* w, O* Y, hipStream_t s) {
   typedef GeoBig G;
-  auto kern = spmm_smfmac_kernel<G, ADAPTER, O>;
+  auto kern = spmm_smfmac_kernel<G, ADAPTER, O, PK>;
+  constexpr int lds_bytes = PK ? G::PLDS_BYTES : G::LDS_BYTES;
   // once per process (thread-safe static initialisation)
-  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (attr != hipSuccess) return attr;
   const int64_t nb = cdiv(M, G::BM) * cdiv(T, G::BT);
-  kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(B, vals, meta, M, T, Kred, w ? w->rt : nullptr,
-                                                     w ? w->xlh : nullptr, w ? w->xll : nullptr,
-                                                     w ? (int)w->rpad : 0, Y);
+  kern<<<(unsigned)nb, G::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, w ? w->rt : nullptr,
+                                                   w ? w->xlh : nullptr, w ? w->xll : nullptr,
+                                                   w ? (int)w->rpad : 0, Y);
   return hipGetLastError();
+}
+
+template <bool PK>
+hipError_t dispatch_big(Dt out, const void* B, int64_t T, int64_t Kred, const void* values, const uint32_t* meta,
+                        int64_t M, const LowrankWs* ws, void* Y, hipStream_t s) {
+  const uint16_t* Bb = (const uint16_t*)B;
+  const uint16_t* vb = (const uint16_t*)values;
+  const bool ad = ws != nullptr;
+  if (out == Dt::BF16)
+    return ad ? launch_big<true, uint16_t, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (uint16_t*)Y, s)
+              : launch_big<false, uint16_t, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (uint16_t*)Y, s);
+  return ad ? launch_big<true, float, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (float*)Y, s)
+            : launch_big<false, float, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (float*)Y, s);
 }
 
 }  // namespace
@@ -232,13 +305,25 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
   if (!fast || (ad && !ws->mfma))
     return launch_spmm_generic(in, out, B, T, Kred, values, meta, M, ad ? ws->part : nullptr, ad ? ws->splits : 1,
                                ad ? r : 0, R, Y, s);
-  const uint16_t* Bb = (const uint16_t*)B;
-  const uint16_t* vb = (const uint16_t*)values;
-  if (out == Dt::BF16)
-    return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (uint16_t*)Y, s)
-              : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (uint16_t*)Y, s);
-  return ad ? launch_big<true>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (float*)Y, s)
-            : launch_big<false>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (float*)Y, s);
+  return dispatch_big<false>(out, B, T, Kred, values, meta, M, ad ? ws : nullptr, Y, s);
+}
+
+int64_t packed_sparse_bytes(int64_t M, int64_t Kred) {
+  return cdiv(M, GeoBig::BM) * cdiv(Kred, GeoBig::KS) * GeoBig::CHUNK_BYTES;
+}
+
+hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t M, int64_t Kred, void* packed,
+                              hipStream_t s) {
+  const int64_t stages = cdiv(Kred, GeoBig::KS), n = cdiv(M, GeoBig::BM) * stages;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(n < (1 << 20) ? n : (1 << 20));
+  pack_sparse_kernel<GeoBig><<<grid, 256, 0, s>>>((const uint16_t*)values, meta, M, Kred, stages, n, (char*)packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_spmm_packed(Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
+                              const LowrankWs* ws, void* Y, hipStream_t s) {
+  return dispatch_big<true>(out, B, T, Kred, packed, nullptr, M, ws, Y, s);
 }
 
 }  // namespace slope

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -55,6 +55,10 @@ def test_size_queries(lib):
     assert S.slope_wgrad_workspace_bytes(33, 8, 260) == (2 + 1) * 2 * 256 * 32 * 2
     assert S.slope_wgrad_workspace_bytes(0, 8, 8) == 0
     assert S.slope_packed_tokens_bytes(8192, 9216) == 36 * 256 * 16384
+    assert S.slope_packed_sparse_bytes(9216, 27648) == 36 * 432 * 18432
+    assert S.slope_packed_sparse_bytes(300, 272) == 2 * 5 * 18432
+    with pytest.raises(S.SlopeError):
+        S.slope_packed_sparse_bytes(256, 264)
     assert S.slope_packed_tokens_bytes(33, 260) + S.slope_packed_tokens_bytes(33, 8) == \
         S.slope_wgrad_workspace_bytes(33, 8, 260)
 
@@ -96,6 +100,19 @@ def test_argument_errors(lib):
     assert lib.slope_masked_wgrad_packed(bf, FAKE, FAKE, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
     assert lib.slope_masked_wgrad_packed(bf, FAKE, None, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
     assert lib.slope_masked_wgrad_packed(7, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    # sparse tile chunks: bf16 only, cols % 16, enough room; packed products' limits
+    assert lib.slope_pack_sparse(f32, FAKE, FAKE, 256, 256, FAKE, 1 << 30, None) == -6
+    assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 264, FAKE, 1 << 30, None) == -2
+    assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 256, FAKE, 1024, None) == -4
+    assert lib.slope_pack_sparse(bf, FAKE, None, 256, 256, FAKE, 1 << 30, None) == -1
+    assert lib.slope_spmm_fwd_packed(f32, f32, FAKE, 64, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 264, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 66, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
+                                     None) == -6
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, 64, FAKE, None) == -2
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, 64, FAKE, None) == -1
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
 

@@ -13,7 +13,8 @@ spmm_fwd (+ adapter) -> spmm_bwd_dx -> masked_wgrad.  Then:
   bit-exact against the matching rows of W_dp^T;
 * products: sampled token x feature blocks against the oracle (normwise 1e-2
   for bf16 outputs, 1e-5 for the fp32 workload); the weight gradient goes
-  through the packed operands as the benchmark runs it.
+  through the packed operands as the benchmark runs it, and so do the sparse
+  products (tile-chunk weights).
 """
 import numpy as np
 import pytest
@@ -61,9 +62,18 @@ def _run_path(d, T, N, K, r, tdt):
     dp = Compressed(K, N, tdt)
     S.slope_double_prune(c.values, c.meta, N, K, dp.values, dp.meta)
     Y = torch.empty((T, N), dtype=tdt, device="cuda")
-    S.slope_spmm_fwd(X, c.values, c.meta, N, Y, L=L, R=R, workspace=workspace(T, K, r, N))
     dX = torch.empty((T, K), dtype=tdt, device="cuda")
-    S.slope_spmm_bwd_dx(dY, dp.values, dp.meta, K, dX)
+    if tdt == torch.bfloat16:   # the benchmark's form: tile-chunk weights
+        ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+        pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+        S.slope_pack_sparse(c.values, c.meta, N, K, ps)
+        S.slope_pack_sparse(dp.values, dp.meta, K, N, pd)
+        S.slope_spmm_fwd_packed(X, ps, N, Y, L=L, R=R, workspace=workspace(T, K, r, N))
+        S.slope_spmm_bwd_dx_packed(dY, pd, K, dX)
+        del ps, pd
+    else:
+        S.slope_spmm_fwd(X, c.values, c.meta, N, Y, L=L, R=R, workspace=workspace(T, K, r, N))
+        S.slope_spmm_bwd_dx(dY, dp.values, dp.meta, K, dX)
     dW = torch.empty((N, K // 2), dtype=tdt, device="cuda")
     if tdt == torch.bfloat16:   # the benchmark's form: packed operands, then the GEMM
         Xp = torch.empty(S.slope_packed_tokens_bytes(T, K), dtype=torch.uint8, device="cuda")

@@ -216,6 +216,80 @@ def test_spmm_bwd_dx(T, N, K, out_dt):
     assert err <= TOL["bf16"], err
 
 
+# ------------------------------------------------------------------ packed sparse operands (tile chunks)
+
+def _pack_sparse_reference(vals_bits, meta_words, rows, cols):
+    """The tile-chunk layout as include/slope.h states it, built with numpy."""
+    S_ = -(-cols // 64)
+    tiles = -(-rows // 256)
+    wpr = meta_words.shape[1]
+    out = np.zeros((tiles, S_, 18432), dtype=np.uint8)
+    vb = np.zeros((tiles * 256, S_ * 32), dtype=np.uint16)
+    vb[:rows, :cols // 2] = vals_bits
+    mw = np.zeros((tiles * 256, 2 * S_), dtype=np.uint32)
+    mw[:rows, :wpr] = meta_words
+    for t in range(tiles):
+        for s_ in range(S_):
+            blk = vb[256 * t:256 * t + 256, 32 * s_:32 * s_ + 32].reshape(256, 4, 8)   # [row][granule][value]
+            a = np.zeros((256, 4, 8), dtype=np.uint16)
+            for r in range(256):
+                for c in range(4):
+                    a[r, c ^ ((r >> 2) & 3)] = blk[r, c]
+            out[t, s_, :16384] = a.reshape(-1).view(np.uint8)
+            out[t, s_, 16384:] = np.ascontiguousarray(mw[256 * t:256 * t + 256, 2 * s_:2 * s_ + 2]).view(np.uint8).reshape(-1)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 64), (300, 272), (4, 16), (520, 1040)])
+def test_pack_sparse_layout(rows, cols):
+    say(f"pack_sparse rows={rows} cols={cols}")
+    W = _special_matrix(rows, cols, "bf16", rows + cols)
+    mask, _ = oracle.prune24(W)
+    vs, ms, _ = oracle.compress24(W, mask)
+    packed = torch.empty(S.slope_packed_sparse_bytes(rows, cols), dtype=torch.uint8, device="cuda")
+    packed.fill_(0xCD)
+    S.slope_pack_sparse(dev(vs), dev_meta(ms), rows, cols, packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), _pack_sparse_reference(vs, ms, rows, cols))
+
+
+PACKED_SHAPES = [(64, 256, 256), (300, 528, 272), (512, 768, 1024), (1, 64, 128), (257, 272, 528), (0, 64, 64),
+                 (700, 1040, 1296)]
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("adapter", [False, True])
+@pytest.mark.parametrize("T,N,K", PACKED_SHAPES)
+def test_spmm_packed_matches_unpacked(T, N, K, adapter, out_dt):
+    """The packed products read the same values in the same order: bitwise
+    equal to the unpacked ones, and within tolerance of the oracle."""
+    say(f"spmm packed T={T} N={N} K={K} adapter={adapter} out={out_dt}")
+    r = 8 if adapter else 0
+    d = _layer(T, N, K, max(r, 1), "bf16", seed=7 * T + N + K)
+    L = dev(np.ascontiguousarray(d["L"][:, :r])) if adapter else None
+    R = dev(np.ascontiguousarray(d["R"][:r])) if adapter else None
+    ws = workspace(T, K, r, N) if adapter else None
+    od = torch_dtype(out_dt)
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    Yp, Yu = empty((T, N), od), empty((T, N), od)
+    S.slope_spmm_fwd_packed(dev(d["X"]), ps, N, Yp, L=L, R=R, workspace=ws)
+    S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Yu, L=L, R=R, workspace=ws)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vdp"]), dev_meta(d["mdp"]), K, N, pd)
+    dXp, dXu = empty((T, K), od), empty((T, K), od)
+    S.slope_spmm_bwd_dx_packed(dev(d["dY"]), pd, K, dXp)
+    S.slope_spmm_bwd_dx(dev(d["dY"]), dev(d["vdp"]), dev_meta(d["mdp"]), K, dXu)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Yp), host(Yu))
+    assert np.array_equal(host(dXp), host(dXu))
+    if T:
+        ref = oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"][:, :r] if adapter else None,
+                              d["R"][:r] if adapter else None)
+        assert normwise(host_f64(Yp), ref) <= TOL["bf16"]
+        assert normwise(host_f64(dXp), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N)) <= TOL["bf16"]
+
+
 WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
                 (0, 64, 64), (257, 264, 520)]
 
