@@ -210,6 +210,26 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
                                       const void* packed_dpT, int64_t K, void* dX, void* stream);
 
+/* Bytes of device workspace slope_spmm_fwd_decode needs for T <= 64 tokens:
+ * fp32 split partial sums, plus the adapter's workspace
+ * (slope_lowrank_workspace_bytes) when r > 0.  Host-only;
+ * SLOPE_ERR_UNSUPPORTED if T > 64 or r > 128. */
+slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
+
+/* Few-token forward (T <= 64; the inference case of the discussion page's
+ * "SLoPe inference computation": weight kept sparse, adapter unmerged):
+ *   Y [T, N] = X [T, K] . W_s^T (+ (X . L) . R)
+ * with W_s in tile-chunk form (slope_pack_sparse, rows N, cols K).  The
+ * compressed weight is streamed once, split along K over enough waves to
+ * keep HBM busy; partial sums are added in a fixed order (deterministic).
+ * workspace: caller-owned device memory of slope_decode_workspace_bytes(T,
+ * K, r, N) bytes (16-byte aligned; scratch, overwritten).  bf16 inputs only;
+ * K % 16 == 0, N % 4 == 0, r <= 128.  Errors: SLOPE_ERR_UNSUPPORTED for
+ * T > 64 or the dtype/size limits, SLOPE_ERR_SHAPE, SLOPE_ERR_WORKSPACE. */
+slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
+                                   int64_t r, void* workspace, int64_t workspace_bytes, void* Y, void* stream);
+
 /* Bytes of a bf16 matrix M [T, C] rewritten as token chunks (see
  * slope_pack_tokens).  Host-only. */
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);

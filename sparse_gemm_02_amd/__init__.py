@@ -30,6 +30,7 @@ __all__ = [
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
+    "slope_decode_workspace_bytes", "slope_spmm_fwd_decode",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -58,6 +59,8 @@ _SIGS = {
     "slope_wgrad_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
     "slope_packed_tokens_bytes": (_i32, [_i64, _i64, _P_I64]),
     "slope_packed_sparse_bytes": (_i32, [_i64, _i64, _P_I64]),
+    "slope_decode_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
+    "slope_spmm_fwd_decode": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "slope_pack_sparse": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
@@ -216,6 +219,21 @@ def slope_spmm_fwd_packed(X, packed_s, N, Y, L=None, R=None, workspace=None, str
     r = int(L.shape[1]) if L is not None else 0
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_spmm_fwd_packed", library().slope_spmm_fwd_packed(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), N,
+                                                                    _p(L), _p(R), r, _p(workspace), wb, _nn(Y),
+                                                                    _s(stream)))
+
+
+def slope_decode_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_decode_workspace_bytes", library().slope_decode_workspace_bytes(T, K, r, N, ctypes.byref(b)))
+    return b.value
+
+
+def slope_spmm_fwd_decode(X, packed_s, N, Y, workspace, L=None, R=None, stream=None) -> None:
+    T, K = X.shape
+    r = int(L.shape[1]) if L is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_spmm_fwd_decode", library().slope_spmm_fwd_decode(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), N,
                                                                     _p(L), _p(R), r, _p(workspace), wb, _nn(Y),
                                                                     _s(stream)))
 

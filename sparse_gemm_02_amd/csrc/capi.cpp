@@ -39,6 +39,7 @@ slope_status ptr(const void* p, bool required) {
 // Packed sparse operands: reduction width up to 2^21 (chunk resources stay
 // below 2 GiB), adapter rank up to 128 (the MFMA epilogue).
 constexpr int64_t kPackedMaxCols = 1 << 21, kPackedMaxRank = 128;
+constexpr int64_t kDecodeMaxTokens = 64;   // the few-token forward
 
 int64_t workspace_need(int64_t T, int64_t K, int64_t r, int64_t N) { return slope::lowrank_workspace_bytes(T, K, r, N); }
 
@@ -246,6 +247,37 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
   return from_hip(slope::launch_spmm_packed((Dt)out_dt, X, T, K, packed_s, N, adapter ? &w : nullptr, Y, s));
+}
+
+slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || r < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T > kDecodeMaxTokens || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::decode_workspace_bytes(T, K, r, N);
+  return SLOPE_OK;
+}
+
+slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
+                                   int64_t r, void* workspace, int64_t workspace_bytes, void* Y, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(packed_s, true));
+  SLOPE_TRY(ptr(Y, true));
+  SLOPE_TRY(ptr(workspace, false));
+  const bool adapter = L_or_null && R_or_null && r > 0;
+  if (adapter) {
+    SLOPE_TRY(ptr(L_or_null, true));
+    SLOPE_TRY(ptr(R_or_null, true));
+  }
+  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
+  if (T > kDecodeMaxTokens || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  const int64_t need = slope::decode_workspace_bytes(T, K, adapter ? r : 0, N);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
+  if (T == 0 || N == 0) return SLOPE_OK;
+  return from_hip(slope::launch_spmm_decode((Dt)out_dt, X, T, K, packed_s, N, L_or_null, R_or_null, adapter ? r : 0,
+                                            workspace, Y, (hipStream_t)stream));
 }
 
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,

@@ -37,6 +37,10 @@ LowrankWs lowrank_layout(Dt in, void* ws, int64_t T, int64_t K, int64_t r, int64
 hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const void* R, int64_t T, int64_t K,
                                   int64_t r, int64_t N, const LowrankWs& w, hipStream_t s);
 
+// Only the down-projection part (bf16, w.mfma): X . L as the hi/lo pair in w.
+hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r,
+                               const LowrankWs& w, hipStream_t s);
+
 // Y[t][m] = B[t, :] . Adense[m, :]  (+ (X . L)[t, :] . R[:, m] when ws != nullptr)
 // with Adense the decompressed 2:4 operand [M, Kred] and B row-major [T, Kred].
 hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
@@ -51,6 +55,13 @@ hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t 
                               hipStream_t s);
 hipError_t launch_spmm_packed(Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
                               const LowrankWs* ws, void* Y, hipStream_t s);
+
+// Forward for T <= 64 tokens on tile-chunk weights (bf16): split-k partial
+// sums reduced in order, plus the adapter term when r > 0 (L [K, r],
+// R [r, N]); workspace of decode_workspace_bytes(T, K, r, N) bytes.
+int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N);
+hipError_t launch_spmm_decode(Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
+                              const void* L, const void* R, int64_t r, void* workspace, void* Y, hipStream_t s);
 
 // dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional
 // accumulation.  With a workspace of wgrad_workspace_bytes(T, N, K) bytes the

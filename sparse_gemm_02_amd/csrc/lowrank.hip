@@ -36,7 +36,7 @@ struct Sizes {
 int choose_splits(int64_t T, int64_t K) {
   const int64_t tblocks = cdiv(T, kDownRows) < 1 ? 1 : cdiv(T, kDownRows);
   int64_t want = cdiv(1024, tblocks);            // enough blocks to fill 256 CUs
-  if (want > 16) want = 16;
+  if (want > (tblocks == 1 ? 64 : 16)) want = tblocks == 1 ? 64 : 16;   // one token block: split K further
   const int64_t ksteps = cdiv(K, 64);
   if (want > ksteps) want = ksteps;
   if (want < 1) want = 1;
@@ -61,22 +61,38 @@ Sizes sizes(int64_t T, int64_t K, int64_t r, int64_t N) {
 }
 
 // ------------------------------------------------------------------ prepare kernels
-// lt[j][k] = L[k][j] for j < r, k < K; 0 in the padding.
+// lt[j][k] = L[k][j] for j < r, k < K; 0 in the padding.  Thread (k-group of
+// eight, j) with j fastest: the reads of a wave cover consecutive j of eight
+// rows of L, the write is one 16-byte piece of a row of lt (Kpad % 8 == 0).
 __global__ __launch_bounds__(256) void transpose_l_kernel(const uint16_t* __restrict__ L, int64_t K, int64_t r,
                                                           int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rpad * Kpad) return;
-  const int64_t j = i / Kpad, k = i % Kpad;
-  lt[i] = (j < r && k < K) ? L[k * r + j] : (uint16_t)0;
+  if (i >= rpad * (Kpad / 8)) return;
+  const int64_t j = i % rpad, k0 = (i / rpad) * 8;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (j < r && k0 + e < K) ? L[(k0 + e) * r + j] : (uint16_t)0;
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+  *reinterpret_cast<u32x4*>(lt + j * Kpad + k0) = w;
 }
 
-// rt[n][j] = R[j][n] for j < r, n < N; 0 in the padding.
+// rt[n][j] = R[j][n] for j < r, n < N; 0 in the padding.  Thread (n, j-group
+// of eight) with n fastest: reads cover consecutive n of eight rows of R, the
+// write is one 16-byte piece of a row of rt (rpad % 8 == 0).
 __global__ __launch_bounds__(256) void transpose_r_kernel(const uint16_t* __restrict__ R, int64_t r, int64_t N,
                                                           int64_t rpad, int64_t Npad, uint16_t* __restrict__ rt) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= Npad * rpad) return;
-  const int64_t n = i / rpad, j = i % rpad;
-  rt[i] = (j < r && n < N) ? R[j * N + n] : (uint16_t)0;
+  if (i >= Npad * (rpad / 8)) return;
+  const int64_t n = i % Npad, j0 = (i / Npad) * 8;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (j0 + e < r && n < N) ? R[(j0 + e) * N + n] : (uint16_t)0;
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+  *reinterpret_cast<u32x4*>(rt + n * rpad + j0) = w;
 }
 
 // part[s][t][j] = sum over k in split s of X[t][k] lt[j][k].  A wave owns 32
@@ -101,21 +117,37 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
   f32x4 acc0[kRankMax / 16], acc1[kRankMax / 16];
 #pragma unroll
   for (int j = 0; j < kRankMax / 16; ++j) acc0[j] = acc1[j] = f32x4{};
-  for (int k0 = kb; k0 < ke; k0 += kDownK) {
+  // operands of one 32-wide k step; the next step's loads are issued before
+  // the current step's MFMAs
+  struct Ops {
+    u32x4 a0, a1, b[kRankMax / 16];
+  };
+  auto load = [&](Ops& o, int k0) {
     const int k = k0 + kl;
-    const bool ok = k + 8 <= ke;
-    const u32x4 a0 = load16(rx, ok ? xa0 + k * 2 : kOutOfRange);
-    const u32x4 a1 = load16(rx, ok ? xa1 + k * 2 : kOutOfRange);
+    const bool ok = k0 < ke && k + 8 <= ke;
+    o.a0 = load16(rx, ok ? xa0 + k * 2 : kOutOfRange);
+    o.a1 = load16(rx, ok ? xa1 + k * 2 : kOutOfRange);
+#pragma unroll
+    for (int jb = 0; jb < kRankMax / 16; ++jb)
+      if (jb < nj) o.b[jb] = load16(rl, ok ? (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2 : kOutOfRange);
+  };
+  auto mma = [&](const Ops& o) {
 #pragma unroll
     for (int jb = 0; jb < kRankMax / 16; ++jb) {
       if (jb < nj) {
-        const uint32_t lo = (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2;
-        const u32x4 b = load16(rl, ok ? lo : kOutOfRange);
-        const bf16x8 bb = __builtin_bit_cast(bf16x8, b);
-        acc0[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bb, acc0[jb], 0, 0, 0);
-        acc1[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bb, acc1[jb], 0, 0, 0);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, o.b[jb]);
+        acc0[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a0), bb, acc0[jb], 0, 0, 0);
+        acc1[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a1), bb, acc1[jb], 0, 0, 0);
       }
     }
+  };
+  Ops p0, p1;
+  load(p0, kb);
+  for (int k0 = kb; k0 < ke; k0 += 2 * kDownK) {
+    load(p1, k0 + kDownK);
+    mma(p0);
+    load(p0, k0 + 2 * kDownK);
+    mma(p1);
   }
 #pragma unroll
   for (int jb = 0; jb < kRankMax / 16; ++jb) {
@@ -140,8 +172,10 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(const float* __restri
   if (i >= Tpad * rpad) return;
   const int64_t t = i / rpad, j = i % rpad;
   float x = 0.f;
-  if (t < T && j < r)
+  if (t < T && j < r) {
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) x += part[((int64_t)s * T + t) * r + j];
+  }
   const uint16_t hi = f32_to_bf16_bits(x);
   xlh[i] = hi;
   xll[i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
@@ -201,8 +235,20 @@ hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const voi
                                   int64_t r, int64_t N, const LowrankWs& w, hipStream_t s) {
   if (!w.mfma) return launch_lowrank_down_generic(in, X, L, T, K, r, w.splits, w.kc, w.part, s);
   // bf16: transposed L and R, the split down-projection, the hi/lo reduction
-  transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
-  transpose_r_kernel<<<blocks_for(w.Npad * w.rpad), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
+  transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
+  transpose_r_kernel<<<blocks_for(w.Npad * w.rpad / 8), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
+  dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
+  lowrank_down_kernel<<<grid, 256, 0, s>>>((const uint16_t*)X, w.lt, (int)T, (int)K, (int)r, (int)w.rpad,
+                                           (int)w.Kpad, (int)w.kc, w.part);
+  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
+                                                                  w.xll);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r,
+                               const LowrankWs& w, hipStream_t s) {
+  if (!w.mfma) return hipErrorInvalidValue;
+  transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
   dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
   lowrank_down_kernel<<<grid, 256, 0, s>>>((const uint16_t*)X, w.lt, (int)T, (int)K, (int)r, (int)w.rpad,
                                            (int)w.Kpad, (int)w.kc, w.part);

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -57,6 +57,13 @@ def test_size_queries(lib):
     assert S.slope_packed_tokens_bytes(8192, 9216) == 36 * 256 * 16384
     assert S.slope_packed_sparse_bytes(9216, 27648) == 36 * 432 * 18432
     assert S.slope_packed_sparse_bytes(300, 272) == 2 * 5 * 18432
+    # decode: fp32 partials (splits x T x padded N) plus the adapter's workspace
+    b0 = S.slope_decode_workspace_bytes(1, 9216, 0, 27648)
+    assert b0 > 0 and b0 % 256 == 0 and b0 % (27648 * 4) == 0
+    assert S.slope_decode_workspace_bytes(1, 9216, 72, 27648) == b0 + S.slope_lowrank_workspace_bytes(1, 9216, 72, 27648)
+    assert S.slope_decode_workspace_bytes(0, 9216, 0, 27648) == 0
+    with pytest.raises(S.SlopeError):
+        S.slope_decode_workspace_bytes(65, 256, 0, 256)
     with pytest.raises(S.SlopeError):
         S.slope_packed_sparse_bytes(256, 264)
     assert S.slope_packed_tokens_bytes(33, 260) + S.slope_packed_tokens_bytes(33, 8) == \
@@ -113,6 +120,12 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
     assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, 64, FAKE, None) == -2
     assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, 64, FAKE, None) == -1
+    # few-token forward: T <= 64, bf16, a workspace of the queried size
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_decode(f32, f32, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 264, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 16, FAKE, None) == -4
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
 

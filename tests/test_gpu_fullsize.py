@@ -151,7 +151,7 @@ def test_full_path_sampled(wl, idx):
 
 @pytest.mark.parametrize("wl,idx,T", DECODE, ids=[f"{w}-{WORKLOADS[w].linears[i].name}-T{t}" for w, i, t in DECODE])
 def test_decode_forward_sampled(wl, idx, T):
-    """Inference shapes: the forward with the unmerged adapter at T = 1..64."""
+    """Inference shapes: the few-token forward with the unmerged adapter at T = 1..64."""
     w = WORKLOADS[wl]
     lin = w.linears[idx]
     N, K, r = lin.N, lin.K, w.r
@@ -163,8 +163,10 @@ def test_decode_forward_sampled(wl, idx, T):
     c = Compressed(N, K, torch.bfloat16)
     S.slope_compress24(Wd, mask, c.values, c.meta)
     Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
-    S.slope_spmm_fwd(dev(d["X"]), c.values, c.meta, N, Y, L=dev(d["L"]), R=dev(d["R"]),
-                     workspace=workspace(T, K, r, N))
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(c.values, c.meta, N, K, ps)
+    ws = torch.empty(S.slope_decode_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    S.slope_spmm_fwd_decode(dev(d["X"]), ps, N, Y, ws, L=dev(d["L"]), R=dev(d["R"]))
     torch.cuda.synchronize()
     rng = np.random.default_rng(idx + T)
     ns = _rows(rng, N, 64)

@@ -290,6 +290,51 @@ def test_spmm_packed_matches_unpacked(T, N, K, adapter, out_dt):
         assert normwise(host_f64(dXp), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N)) <= TOL["bf16"]
 
 
+DECODE_SHAPES = [(1, 256, 256), (5, 520, 272), (16, 768, 1024), (33, 260, 528), (64, 1040, 1296), (0, 64, 64),
+                 (3, 64, 4096)]
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("adapter", [False, True])
+@pytest.mark.parametrize("T,N,K", DECODE_SHAPES)
+def test_spmm_fwd_decode(T, N, K, adapter, out_dt):
+    say(f"spmm_fwd_decode T={T} N={N} K={K} adapter={adapter} out={out_dt}")
+    r = 8 if adapter else 0
+    d = _layer(T, N, K, max(r, 1), "bf16", seed=11 * T + N + K)
+    L = dev(np.ascontiguousarray(d["L"][:, :r])) if adapter else None
+    R = dev(np.ascontiguousarray(d["R"][:r])) if adapter else None
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    ws = torch.empty(max(16, S.slope_decode_workspace_bytes(T, K, r, N)), dtype=torch.uint8, device="cuda")
+    Y = empty((T, N), torch_dtype(out_dt))
+    S.slope_spmm_fwd_decode(dev(d["X"]), ps, N, Y, ws, L=L, R=R)
+    Y2 = empty((T, N), torch_dtype(out_dt))
+    S.slope_spmm_fwd_decode(dev(d["X"]), ps, N, Y2, ws, L=L, R=R)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Y), host(Y2))          # fixed reduction order
+    if T:
+        ref = oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"][:, :r] if adapter else None,
+                              d["R"][:r] if adapter else None)
+        err = normwise(host_f64(Y), ref)
+        assert err <= TOL["bf16"], err
+        if out_dt == "f32":
+            assert err <= 2e-5 * max(1.0, np.sqrt(K / 256)), err
+
+
+def test_spmm_fwd_decode_integer_exact():
+    """Integer inputs: every partial sum is exact, so fp32 output equals the oracle."""
+    T, N, K, r = 7, 520, 1040, 4
+    say("decode integer probe")
+    d = _layer(T, N, K, r, "bf16", seed=23, ints=True)
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    ws = torch.empty(S.slope_decode_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    Y = empty((T, N), torch.float32)
+    S.slope_spmm_fwd_decode(dev(d["X"]), ps, N, Y, ws, L=dev(d["L"]), R=dev(d["R"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(Y), oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"]))
+
+
 WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
                 (0, 64, 64), (257, 264, 520)]
 
