@@ -9,7 +9,9 @@ transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
     -> pack_tokens (X and dY into token chunks) -> masked_wgrad
 
 The three products run on the packed operands (the *_packed entry points);
-the packing passes are part of the step.
+the packing passes are part of the step.  A `decode` object adds the
+few-token forward (slope_spmm_fwd_decode) at the workload's inference token
+counts, as HBM bytes per second.
 
 prune24 and compress24 run once per layer in training (the forward mask is
 static); they are kept inside the timed step so the step covers every kernel of
@@ -256,6 +258,39 @@ def profile_mode(args, wl, T):
     print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
 
 
+def decode_pass(lins, wl, S, torch, reps=20):
+    """The few-token forward (slope_spmm_fwd_decode, adapter on) over the layer's
+    linears at each of the workload's inference token counts, on the packed
+    weights the step already holds.  HBM bound: reported as algorithmic bytes
+    (compressed weight 1.125 B per weight, X, Y, L, R) per second."""
+    out = {}
+    for T in wl.decode_T:
+        calls, nbytes = [], 0
+        for li in lins:
+            X = torch.randn((T, li.K), device="cuda").to(torch.bfloat16)
+            Y = torch.empty((T, li.N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(max(16, S.slope_decode_workspace_bytes(T, li.K, li.r, li.N)), dtype=torch.uint8,
+                             device="cuda")
+            calls.append((li, X, Y, ws))
+            nbytes += 1.125 * li.N * li.K + 2 * T * (li.K + li.N) + 2 * li.r * (li.K + li.N)
+        run = lambda: [S.slope_spmm_fwd_decode(X, li.ps, li.N, Y, ws, L=li.L, R=li.R) for li, X, Y, ws in calls]
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"T={T}"] = {"us_per_layer": round(ms * 1e3, 1), "bytes": int(nbytes), "gbs": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del calls
+    return out
+
+
 def measured_traffic(op):
     """HBM bytes per launch (fetched + written) of `op`'s kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has
@@ -367,6 +402,8 @@ def main():
            "ideal_step_ms": round(useful_flops / (PEAK_BF16_DENSE_TFLOPS * 1e12) * 1e3, 3),
            "ops": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
            "roofline": roofline}
+    if wl.decode_T:
+        out["decode"] = decode_pass(lins, wl, S, torch)
     # free the layer before the CPU leg
     del lins
     torch.cuda.empty_cache()
