@@ -23,6 +23,7 @@ Conventions (W is [N, K] = [out, in] as for a linear layer):
     dX = dY . W_dp            W_dp^T = prune24(W_s^T): 2:4 groups along N
     dW = (dY^T . X) (.) M_s   kept only at the static forward mask
     Y += (X . L) . R          L [K, r], R [r, N]  (W_dense = W_sparse + L R)
+    dX += (dY . R^T) . L^T, dL = X^T . (dY . R^T), dR = (X . L)^T . dY
 
 Tensors arrive as raw bit patterns (uint16 = bf16, uint32 = fp32), so every
 selection is made on the exact stored values.  Products and sums are done in
@@ -47,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "widen", "prune24", "compress24", "decompress24", "mask_from_meta",
-    "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add",
+    "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add", "lowrank_bwd",
     "storage_accounting", "LEGAL_NIBBLES",
 ]
 
@@ -265,6 +266,21 @@ def lowrank_add(X, L, R, Y_in=None):
     if Y_in is not None:
         Y = Y + widen(Y_in)
     return XL, Y
+
+
+def lowrank_bwd(X, dY, L, R):
+    """Gradients of the adapter term Y += (X . L) . R (explainer 2.B) for an
+    output gradient dY: the term is bilinear, so with G = dY . R^T [T, r]
+
+        dX += G . L^T        [T, K]
+        dL  = X^T . G        [K, r]
+        dR  = (X . L)^T . dY [r, N]
+
+    Returns (dX_term, dL, dR) as float64 (not rounded).
+    """
+    Xw, dYw, Lw, Rw = widen(X), widen(dY), widen(L), widen(R)
+    G = dYw @ Rw.T
+    return G @ Lw.T, Xw.T @ G, (Xw @ Lw).T @ dYw
 
 
 # --------------------------------------------------------------------------- accounting
