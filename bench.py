@@ -5,8 +5,9 @@ transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 36864->9216; T = 8192 tokens, adapter rank 72, bf16 with fp32 accumulation):
 
     prune24 -> compress24 -> double_prune -> pack_sparse (W_s and W_dp^T
-    into tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx
-    -> pack_tokens (X and dY into token chunks) -> masked_wgrad
+    into tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx (+ the
+    adapter's dX term) -> pack_tokens (X and dY into token chunks)
+    -> masked_wgrad -> lowrank_grads (dL, dR)
 
 The three products run on the packed operands (the *_packed entry points);
 the packing passes are part of the step.  A `decode` object adds the
@@ -19,8 +20,9 @@ the path.  Inputs are synthetic (seeded Gaussian, see workloads/) and resident i
 HBM before the timed region starts.
 
 Prints one JSON line.  `value` is dense-equivalent TFLOP/s of the step's GEMMs
-(3 x 2*T*N*K per linear plus the adapter's 2*T*r*(K+N)); `useful_tflops` counts
-only products with a kept weight (T*N*K per GEMM).  `roofline` reports the
+(3 x 2*T*N*K per linear plus the adapter's 2*T*r*(K+N) forward and 4*T*r*(K+N)
+backward); `useful_tflops` counts only products with a kept weight (T*N*K per
+sparse GEMM) plus the adapter's.  `roofline` reports the
 kernel with the largest share of the step against the dense bf16 MFMA peak
 (2.5 PFLOP/s) using useful flops.  `cpu_baseline` times the CPU oracle on a
 bounded slice of the same layer on this host.
@@ -89,22 +91,31 @@ class Linear:
         # sparse operands as tile chunks (W_s for the forward, W_dp^T for dX)
         self.ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device=dev)
         self.pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device=dev)
+        # adapter backward: the dX term's workspace (reduction over N, output over K)
+        # and the adapter weight gradients
+        self.ws_bwd = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, N, r, K)), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_grads = torch.empty(max(16, S.slope_lowrank_grads_workspace_bytes(T, K, r, N)), dtype=torch.uint8,
+                                    device=dev)
+        self.dL = torch.empty((K, r), dtype=bf, device=dev)
+        self.dR = torch.empty((r, N), dtype=bf, device=dev)
         # weight-gradient operands as transposed token chunks
         self.Xp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, K)), dtype=torch.uint8, device=dev)
         self.dYp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, N)), dtype=torch.uint8, device=dev)
 
     def flops(self):
         T, N, K, r = self.T, self.N, self.K, self.r
-        return {"spmm_fwd": 2 * T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": 2 * T * N * K,
-                "masked_wgrad": 2 * T * N * K}
+        return {"spmm_fwd": 2 * T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": 2 * T * N * K + 2 * T * r * (K + N),
+                "masked_wgrad": 2 * T * N * K, "lowrank_grads": 2 * T * r * (K + N)}
 
     def useful(self):
         T, N, K, r = self.T, self.N, self.K, self.r
-        return {"spmm_fwd": T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": T * N * K, "masked_wgrad": T * N * K}
+        return {"spmm_fwd": T * N * K + 2 * T * r * (K + N), "spmm_bwd_dx": T * N * K + 2 * T * r * (K + N),
+                "masked_wgrad": T * N * K, "lowrank_grads": 2 * T * r * (K + N)}
 
 
 OPS = ("prune24", "compress24", "double_prune", "pack_sparse", "spmm_fwd", "spmm_bwd_dx", "pack_tokens",
-       "masked_wgrad")
+       "masked_wgrad", "lowrank_grads")
 
 
 def pack_sparse(S, li):
@@ -121,6 +132,14 @@ def wgrad(S, li):
     S.slope_masked_wgrad_packed(li.dYp, li.Xp, li.T, li.N, li.K, li.ms, li.dW)
 
 
+def bwd_dx(S, li):
+    S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX, L=li.L, R=li.R, workspace=li.ws_bwd)
+
+
+def lowrank_grads(S, li):
+    S.slope_lowrank_grads_packed(li.X, li.dY, li.Xp, li.dYp, li.L, li.R, li.ws_grads, li.dL, li.dR)
+
+
 def step(lins, S, ev=None):
     """One pass of the hot path over every linear; optional per-op events."""
     for li in lins:
@@ -130,9 +149,10 @@ def step(lins, S, ev=None):
             ("double_prune", lambda: S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)),
             ("pack_sparse", lambda: pack_sparse(S, li)),
             ("spmm_fwd", lambda: S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
-            ("spmm_bwd_dx", lambda: S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX)),
+            ("spmm_bwd_dx", lambda: bwd_dx(S, li)),
             ("pack_tokens", lambda: pack(S, li)),
             ("masked_wgrad", lambda: wgrad(S, li)),
+            ("lowrank_grads", lambda: lowrank_grads(S, li)),
         )
         for op, fn in calls:
             if ev is not None:
@@ -167,7 +187,8 @@ class Events:
 def cpu_baseline(workload, budget_s):
     """The CPU oracle on a bounded slice of the layer: for each linear in turn, the
     first 256 output rows (N' = 256) and 256 tokens (T' = 256), running prune24,
-    compress24, double_prune (of the slice), forward with adapter, dX and dW.
+    compress24, double_prune (of the slice), forward with adapter, dX and dW, and
+    the adapter's backward.
     Repeats over the linears until the budget is spent; rate in dense-equivalent
     TFLOP/s of the slice's GEMMs (the same count as the GPU `value`)."""
     import numpy as np
@@ -197,8 +218,9 @@ def cpu_baseline(workload, budget_s):
             oracle.spmm_fwd(d["X"], vs, ms, K, d["L"], d["R"])
             oracle.spmm_bwd_dx(d["dY"], vdp, mdp, Nn)
             oracle.masked_wgrad(d["dY"], d["X"], ms, K)
+            oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])
             spent += time.perf_counter() - t0
-            flops += 3 * 2 * Tn * Nn * K + 2 * Tn * workload.r * (K + Nn)
+            flops += 3 * 2 * Tn * Nn * K + 6 * Tn * workload.r * (K + Nn)
             runs += 1
             if spent >= budget_s:
                 break
@@ -206,7 +228,7 @@ def cpu_baseline(workload, budget_s):
             break
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{runs} linear slices of N'={Nn} output rows x T'={Tn} tokens (full K) of the "
-                      f"{workload.name} layer, whole path (prune, compress, double prune, fwd+adapter, dX, dW), "
+                      f"{workload.name} layer, whole path (prune, compress, double prune, fwd+adapter, dX, dW, adapter gradients), "
                       f"{spent:.1f} s of CPU work, numpy fp64 with {threads} BLAS threads on {os.cpu_count()} host cores"}
 
 
@@ -249,7 +271,9 @@ def profile_mode(args, wl, T):
             elif op == "spmm_fwd":
                 S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
             elif op == "spmm_bwd_dx":
-                S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX)
+                bwd_dx(S, li)
+            elif op == "lowrank_grads":
+                lowrank_grads(S, li)
             elif op == "pack_tokens":
                 pack(S, li)
             elif op == "masked_wgrad":
@@ -364,7 +388,7 @@ def main():
     for op in OPS:
         t = sum(sum(per[(l.name, op)]) / len(per[(l.name, op)]) for l in lins)
         ops[op] = {"ms_per_step": t}
-    for op in ("spmm_fwd", "spmm_bwd_dx", "masked_wgrad"):
+    for op in ("spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_grads"):
         uf = sum(l.useful()[op] for l in lins)
         df = sum(l.flops()[op] for l in lins)
         t = ops[op]["ms_per_step"] * 1e-3
@@ -380,8 +404,10 @@ def main():
         ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9
         ops[op]["frac_hbm_peak"] = ops[op]["gbs"] / PEAK_HBM_GBS
 
-    # dominant single-kernel call (spmm_fwd also launches the adapter down-projection)
-    dom = max(("spmm_bwd_dx", "masked_wgrad"), key=lambda o: ops[o]["ms_per_step"])
+    # dominant kernel: the weight-gradient GEMM (one kernel per call; the two
+    # sparse products also launch the adapter's small kernels, so their call
+    # time is not one kernel's)
+    dom = "masked_wgrad"
     launches = [(l, sum(per[(l.name, dom)]) / len(per[(l.name, dom)])) for l in lins]
     achieved = sum(l.useful()[dom] for l, _ in launches) / (sum(t for _, t in launches) * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_DENSE_TFLOPS,

@@ -205,10 +205,35 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
                                    void* stream);
 
 /* slope_spmm_bwd_dx with W_dpT given in tile-chunk form (slope_pack_sparse of
- * values_dpT, meta_dpT; rows K, cols N): same result, bitwise.  bf16 inputs
- * only; N % 16 == 0, N <= 2^21, K % 4 == 0. */
+ * values_dpT, meta_dpT; rows K, cols N): same result, bitwise.  With L [K, r]
+ * and R [r, N] (r > 0) it also adds the adapter's share of the input gradient
+ * (the derivative of explainer 2.B's term):
+ *   dX [T, K] = dY . W_dp (+ (dY . R^T) . L^T)
+ * using workspace_or_null of slope_lowrank_workspace_bytes(T, N, r, K) bytes
+ * (note the order: the reduction runs over N, the output over K).  bf16
+ * inputs only; N % 16 == 0, N <= 2^21, K % 4 == 0, r <= 128. */
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
-                                      const void* packed_dpT, int64_t K, void* dX, void* stream);
+                                      const void* packed_dpT, int64_t K, const void* L_or_null,
+                                      const void* R_or_null, int64_t r, void* workspace_or_null,
+                                      int64_t workspace_bytes, void* dX, void* stream);
+
+/* Bytes of device workspace slope_lowrank_grads_packed needs.  Host-only;
+ * SLOPE_ERR_UNSUPPORTED if r > 128. */
+slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
+
+/* Weight gradients of the adapter term of explainer 2.B (Y += (X . L) . R):
+ *   dL [K, r] = X^T . (dY . R^T),   dR [r, N] = (X . L)^T . dY
+ * X [T, K], dY [T, N], L, R bf16 row-major; X_packed, dY_packed: the same
+ * matrices in token-chunk form (slope_pack_tokens), as the weight gradient
+ * uses them.  dL, dR in out_dt (BF16 or F32), overwritten, or added to when
+ * accumulate != 0.  workspace: slope_lowrank_grads_workspace_bytes(T, K, r,
+ * N) bytes, scratch.  Sums over tokens run in a fixed order.  Errors:
+ * SLOPE_ERR_SHAPE unless K % 8 == 0 and N % 8 == 0; SLOPE_ERR_UNSUPPORTED
+ * for r > 128; SLOPE_ERR_WORKSPACE. */
+slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
+                                        const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
+                                        const void* L, const void* R, void* workspace, int64_t workspace_bytes,
+                                        void* dL, void* dR, int accumulate, void* stream);
 
 /* Bytes of device workspace slope_spmm_fwd_decode needs for T <= 64 tokens:
  * fp32 split partial sums, plus the adapter's workspace

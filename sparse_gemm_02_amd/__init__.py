@@ -30,7 +30,8 @@ __all__ = [
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
-    "slope_decode_workspace_bytes", "slope_spmm_fwd_decode",
+    "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_lowrank_grads_workspace_bytes",
+    "slope_lowrank_grads_packed",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -63,7 +64,11 @@ _SIGS = {
     "slope_spmm_fwd_decode": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
     "slope_pack_sparse": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
-    "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                        _vp]),
+    "slope_lowrank_grads_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
+    "slope_lowrank_grads_packed": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64,
+                                          _vp, _vp, _i32, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
@@ -238,10 +243,31 @@ def slope_spmm_fwd_decode(X, packed_s, N, Y, workspace, L=None, R=None, stream=N
                                                                     _s(stream)))
 
 
-def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, stream=None) -> None:
+def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, L=None, R=None, workspace=None, stream=None) -> None:
     T, N = dY.shape
+    r = int(L.shape[1]) if L is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_spmm_bwd_dx_packed", library().slope_spmm_bwd_dx_packed(_dt(dY), _dt(dX), _nn(dY), T, N,
-                                                                          _nn(packed_dpT), K, _nn(dX), _s(stream)))
+                                                                          _nn(packed_dpT), K, _p(L), _p(R), r,
+                                                                          _p(workspace), wb, _nn(dX), _s(stream)))
+
+
+def slope_lowrank_grads_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_lowrank_grads_workspace_bytes",
+           library().slope_lowrank_grads_workspace_bytes(T, K, r, N, ctypes.byref(b)))
+    return b.value
+
+
+def slope_lowrank_grads_packed(X, dY, X_packed, dY_packed, L, R, workspace, dL, dR, accumulate=False,
+                               stream=None) -> None:
+    T, K = X.shape
+    N = dY.shape[1]
+    r = int(L.shape[1])
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_lowrank_grads_packed", library().slope_lowrank_grads_packed(
+        _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(workspace), wb,
+        _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
 
 
 def slope_packed_tokens_bytes(T: int, C: int) -> int:

@@ -281,17 +281,111 @@ slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const 
 }
 
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
-                                      const void* packed_dpT, int64_t K, void* dX, void* stream) {
+                                      const void* packed_dpT, int64_t K, const void* L_or_null,
+                                      const void* R_or_null, int64_t r, void* workspace_or_null,
+                                      int64_t workspace_bytes, void* dX, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY, true));
   SLOPE_TRY(ptr(packed_dpT, true));
   SLOPE_TRY(ptr(dX, true));
+  const bool adapter = L_or_null && R_or_null && r > 0;
+  if (adapter) {
+    SLOPE_TRY(ptr(L_or_null, true));
+    SLOPE_TRY(ptr(R_or_null, true));
+  }
   if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
   if (N % 16 || K % 4) return SLOPE_ERR_SHAPE;
-  if (!in_range(T) || !in_range(K) || N > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (!in_range(T) || !in_range(K) || N > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (adapter) {
+    // the forward's adapter workspace with the roles of K and N exchanged
+    const int64_t need = workspace_need(T, N, r, K);
+    if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
+    if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
+  }
   if (T == 0 || K == 0) return SLOPE_OK;
-  return from_hip(slope::launch_spmm_packed((Dt)out_dt, dY, T, N, packed_dpT, K, nullptr, dX, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  slope::LowrankWs w;
+  if (adapter) {
+    w = slope::lowrank_layout(Dt::BF16, workspace_or_null, T, N, r, K);
+    hipError_t e = slope::launch_lowrank_prepare_bwd(dY, L_or_null, R_or_null, T, N, r, K, w, s);
+    if (e != hipSuccess) return SLOPE_ERR_HIP;
+  }
+  return from_hip(slope::launch_spmm_packed((Dt)out_dt, dY, T, N, packed_dpT, K, adapter ? &w : nullptr, dX, s));
+}
+
+namespace {
+// Workspace of slope_lowrank_grads_packed: the forward adapter layout (X . L),
+// the backward one (dY . R^T), both hi/lo pairs transposed, the two partial sums.
+struct GradsWs {
+  int64_t fwd, bwd, trans, part_r, part_l, total;
+};
+GradsWs grads_ws(int64_t T, int64_t K, int64_t r, int64_t N) {
+  GradsWs g{};
+  g.fwd = workspace_need(T, K, r, N);
+  g.bwd = workspace_need(T, N, r, K);
+  const int64_t Tpad = (T + 255) / 256 * 256, r32 = (r + 31) / 32 * 32;
+  g.trans = (r32 * Tpad * 2 + 255) / 256 * 256;
+  g.part_r = slope::lr_wgrad_part_bytes(T, N, r);
+  g.part_l = slope::lr_wgrad_part_bytes(T, K, r);
+  g.total = (T == 0 || r == 0) ? 0 : g.fwd + g.bwd + 4 * g.trans + g.part_r + g.part_l;
+  return g;
+}
+}  // namespace
+
+slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || r < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = grads_ws(T, K, r, N).total;
+  return SLOPE_OK;
+}
+
+slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
+                                        const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
+                                        const void* L, const void* R, void* workspace, int64_t workspace_bytes,
+                                        void* dL, void* dR, int accumulate, void* stream) {
+  SLOPE_TRY(check_io(SLOPE_BF16, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(dY, true));
+  SLOPE_TRY(ptr(X_packed, true));
+  SLOPE_TRY(ptr(dY_packed, true));
+  SLOPE_TRY(ptr(L, true));
+  SLOPE_TRY(ptr(R, true));
+  SLOPE_TRY(ptr(dL, true));
+  SLOPE_TRY(ptr(dR, true));
+  SLOPE_TRY(ptr(workspace, false));
+  if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  const GradsWs g = grads_ws(T, K, r, N);
+  if (g.total > 0 && (!workspace || workspace_bytes < g.total)) return SLOPE_ERR_WORKSPACE;
+  if (r == 0 || K == 0 || N == 0) return SLOPE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {   // empty sums: dL = dR = 0 (or unchanged when accumulating)
+    if (accumulate) return SLOPE_OK;
+    hipError_t e = slope::launch_fill_zero((Dt)out_dt, dL, K * r, s);
+    if (e == hipSuccess) e = slope::launch_fill_zero((Dt)out_dt, dR, r * N, s);
+    return from_hip(e);
+  }
+  char* p = static_cast<char*>(workspace);
+  const slope::LowrankWs wf = slope::lowrank_layout(Dt::BF16, p, T, K, r, N);
+  const slope::LowrankWs wb = slope::lowrank_layout(Dt::BF16, p + g.fwd, T, N, r, K);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + g.trans);
+  uint16_t* gh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + 2 * g.trans);
+  uint16_t* gl = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + 3 * g.trans);
+  float* pr = reinterpret_cast<float*>(p + g.fwd + g.bwd + 4 * g.trans);
+  float* pl = reinterpret_cast<float*>(p + g.fwd + g.bwd + 4 * g.trans + g.part_r);
+  const int64_t r32 = (r + 31) / 32 * 32;
+  hipError_t e = slope::launch_lowrank_down(Dt::BF16, X, L, T, K, r, wf, s);              // X . L
+  if (e == hipSuccess) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
+  if (e == hipSuccess) e = slope::launch_transpose_hilo(wf, r32, xh, xl, s);
+  if (e == hipSuccess) e = slope::launch_transpose_hilo(wb, r32, gh, gl, s);
+  if (e == hipSuccess)
+    e = slope::launch_lr_wgrad((Dt)out_dt, dY_packed, T, N, r, xh, xl, wf.Tpad, pr, dR, false, accumulate, s);
+  if (e == hipSuccess)
+    e = slope::launch_lr_wgrad((Dt)out_dt, X_packed, T, K, r, gh, gl, wb.Tpad, pl, dL, true, accumulate, s);
+  return from_hip(e);
 }
 
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes) {

@@ -41,6 +41,23 @@ hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const voi
 hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, int64_t K, int64_t r,
                                const LowrankWs& w, hipStream_t s);
 
+// Adapter backward, dX term: G = dY . R^T into w (hi/lo) with L as the
+// epilogue operand, w laid out by lowrank_layout(BF16, ws, T, N, r, K): the
+// forward's roles with (X, L, R, K, N) -> (dY, R^T, L^T, N, K).
+hipError_t launch_lowrank_prepare_bwd(const void* dY, const void* L, const void* R, int64_t T, int64_t N, int64_t r,
+                                      int64_t K, const LowrankWs& w, hipStream_t s);
+// The hi/lo pair of w transposed to [rpad32][Tpad] (rows past rpad zero).
+hipError_t launch_transpose_hilo(const LowrankWs& w, int64_t rpad32, uint16_t* xht, uint16_t* xlt, hipStream_t s);
+
+// Adapter weight gradients from token chunks: out = A^T . B over the tokens with
+// A the chunks of a [T, C] matrix and B given as a transposed hi/lo pair
+// [32*ceil(r/32)][Tpad]; written as out[j][c] (dR) or, trans, out[c][j] (dL).
+// part: lr_wgrad_part_bytes(T, C, r) of fp32 scratch.
+int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r);
+hipError_t launch_lr_wgrad(Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
+                           const uint16_t* bl, int64_t Tpad, float* part, void* dst, bool trans, int accumulate,
+                           hipStream_t s);
+
 // Y[t][m] = B[t, :] . Adense[m, :]  (+ (X . L)[t, :] . R[:, m] when ws != nullptr)
 // with Adense the decompressed 2:4 operand [M, Kred] and B row-major [T, Kred].
 hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,

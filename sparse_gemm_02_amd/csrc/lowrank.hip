@@ -21,7 +21,8 @@ hipError_t launch_lowrank_up_generic(Dt in, Dt out, const float* xl, int splits,
 
 namespace {
 
-constexpr int kDownRows = 128;   // tokens per down-projection block (32 per wave)
+constexpr int kDownWaveRows = 64;                  // tokens per down-projection wave
+constexpr int kDownRows = 4 * kDownWaveRows;       // tokens per down-projection block
 constexpr int kDownK = 32;       // k per MFMA step
 constexpr int kRankMax = 128;    // largest rank of the MFMA down-projection
 
@@ -95,50 +96,81 @@ __global__ __launch_bounds__(256) void transpose_r_kernel(const uint16_t* __rest
   *reinterpret_cast<u32x4*>(rt + n * rpad + j0) = w;
 }
 
-// part[s][t][j] = sum over k in split s of X[t][k] lt[j][k].  A wave owns 32
-// tokens (two 16-row MFMA A operands) and every rank column; operands come
-// straight from global memory (16 contiguous bytes per lane).  Dense 16x16x32
-// MFMA: A lane l = row l%16, k = 8*(l/16)+e; B lane l = column l%16, same k;
-// D lane l = column l%16, rows 4*(l/16)+v.
+// dst[i][j] = src[i][j] for i < rows, j < cols (src row-major, cols wide); 0 in
+// the padding up to [rows_pad, cols_pad].  The adapter backward uses it for the
+// operands that need no transposition there: R [r, N] as the down-projection's
+// [rpad, Kpad] operand and L [K, r] as the epilogue's [Npad, rpad] operand.
+__global__ __launch_bounds__(256) void pad_copy_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+                                                       int64_t rows_pad, int64_t cols_pad,
+                                                       uint16_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows_pad * cols_pad) return;
+  const int64_t a = i / cols_pad, b = i % cols_pad;
+  dst[i] = (a < rows && b < cols) ? src[a * cols + b] : (uint16_t)0;
+}
+
+// xt[j][t] = x[t][j] for the hi and lo parts (x [Tpad][rpad] -> xt [rpad32][Tpad],
+// rows j >= rpad zero).  Thread (j, t) with t fastest: coalesced writes.
+__global__ __launch_bounds__(256) void transpose_hilo_kernel(const uint16_t* __restrict__ xh,
+                                                             const uint16_t* __restrict__ xl, int64_t Tpad,
+                                                             int64_t rpad, int64_t rpad32, uint16_t* __restrict__ xht,
+                                                             uint16_t* __restrict__ xlt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rpad32 * Tpad) return;
+  const int64_t j = i / Tpad, t = i % Tpad;
+  const bool in = j < rpad;
+  xht[i] = in ? xh[t * rpad + j] : (uint16_t)0;
+  xlt[i] = in ? xl[t * rpad + j] : (uint16_t)0;
+}
+
+// part[s][t][j] = sum over k in split s of X[t][k] lt[j][k].  A wave owns 64
+// tokens (four 16-row MFMA A operands) and every rank column (NJ blocks of
+// 16), so each 16-byte piece of lt it loads serves four operands; operands
+// come straight from global memory and the next 32-wide k step's loads are
+// issued before the current step's MFMAs.  Dense 16x16x32 MFMA: A lane l = row
+// l%16, k = 8*(l/16)+e; B lane l = column l%16, same k; D lane l = column l%16,
+// rows 4*(l/16)+v.
+template <int NJ>
 __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ lt, int T, int K, int r,
                                                            int rpad, int Kpad, int kc, float* __restrict__ part) {
+  constexpr int G = kDownWaveRows / 16;                         // 16-token operands per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.y;
-  const int64_t tw = (int64_t)blockIdx.x * kDownRows + wave * 32;   // first token of this wave
+  const int64_t tw = (int64_t)blockIdx.x * kDownRows + wave * kDownWaveRows;   // first token of this wave
   const int kb = s * kc, ke = (kb + kc < K) ? kb + kc : K;
-  const int nj = rpad / 16;
   // tokens past T read as 0 through the resource bound; k past the split is masked
   const int64_t rows_left = (int64_t)T - tw;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (rows_left > 0 ? tw : 0) * K, rows_left > 0 ? rows_left * K * 2 : 0);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(lt, (int64_t)rpad * Kpad * 2);
   const int kl = 8 * (lane >> 4);
-  const uint32_t xa0 = (uint32_t)((lane & 15) * K) * 2, xa1 = (uint32_t)((16 + (lane & 15)) * K) * 2;
-  f32x4 acc0[kRankMax / 16], acc1[kRankMax / 16];
+  uint32_t xa[G];
 #pragma unroll
-  for (int j = 0; j < kRankMax / 16; ++j) acc0[j] = acc1[j] = f32x4{};
-  // operands of one 32-wide k step; the next step's loads are issued before
-  // the current step's MFMAs
+  for (int g = 0; g < G; ++g) xa[g] = (uint32_t)((g * 16 + (lane & 15)) * K) * 2;
+  f32x4 acc[G][NJ];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[g][j] = f32x4{};
   struct Ops {
-    u32x4 a0, a1, b[kRankMax / 16];
+    u32x4 a[G], b[NJ];
   };
   auto load = [&](Ops& o, int k0) {
     const int k = k0 + kl;
     const bool ok = k0 < ke && k + 8 <= ke;
-    o.a0 = load16(rx, ok ? xa0 + k * 2 : kOutOfRange);
-    o.a1 = load16(rx, ok ? xa1 + k * 2 : kOutOfRange);
 #pragma unroll
-    for (int jb = 0; jb < kRankMax / 16; ++jb)
-      if (jb < nj) o.b[jb] = load16(rl, ok ? (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2 : kOutOfRange);
+    for (int g = 0; g < G; ++g) o.a[g] = load16(rx, ok ? xa[g] + k * 2 : kOutOfRange);
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb)
+      o.b[jb] = load16(rl, ok ? (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2 : kOutOfRange);
   };
   auto mma = [&](const Ops& o) {
 #pragma unroll
-    for (int jb = 0; jb < kRankMax / 16; ++jb) {
-      if (jb < nj) {
-        const bf16x8 bb = __builtin_bit_cast(bf16x8, o.b[jb]);
-        acc0[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a0), bb, acc0[jb], 0, 0, 0);
-        acc1[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a1), bb, acc1[jb], 0, 0, 0);
-      }
+    for (int jb = 0; jb < NJ; ++jb) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, o.b[jb]);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc[g][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a[g]), bb, acc[g][jb], 0, 0, 0);
     }
   };
   Ops p0, p1;
@@ -150,17 +182,41 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
     mma(p1);
   }
 #pragma unroll
-  for (int jb = 0; jb < kRankMax / 16; ++jb) {
-    if (jb >= nj) break;
+  for (int jb = 0; jb < NJ; ++jb) {
     const int j = jb * 16 + (lane & 15);
     if (j >= r) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t t0 = tw + 4 * (lane >> 4) + v, t1 = t0 + 16;
-      if (t0 < T) part[((int64_t)s * T + t0) * r + j] = acc0[jb][v];
-      if (t1 < T) part[((int64_t)s * T + t1) * r + j] = acc1[jb][v];
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tw + 16 * g + 4 * (lane >> 4) + v;
+        if (t < T) part[((int64_t)s * T + t) * r + j] = acc[g][jb][v];
+      }
   }
+}
+
+template <int NJ>
+void down_nj(dim3 grid, const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
+             hipStream_t s) {
+  lowrank_down_kernel<NJ><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad, (int)w.kc,
+                                               w.part);
+}
+
+hipError_t launch_down(const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
+  switch (w.rpad / 16) {
+    case 1: down_nj<1>(grid, X, lt, T, K, r, w, s); break;
+    case 2: down_nj<2>(grid, X, lt, T, K, r, w, s); break;
+    case 3: down_nj<3>(grid, X, lt, T, K, r, w, s); break;
+    case 4: down_nj<4>(grid, X, lt, T, K, r, w, s); break;
+    case 5: down_nj<5>(grid, X, lt, T, K, r, w, s); break;
+    case 6: down_nj<6>(grid, X, lt, T, K, r, w, s); break;
+    case 7: down_nj<7>(grid, X, lt, T, K, r, w, s); break;
+    case 8: down_nj<8>(grid, X, lt, T, K, r, w, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // xl = sum over splits of part (in split order), split into bf16 hi + lo with
@@ -237,9 +293,8 @@ hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const voi
   // bf16: transposed L and R, the split down-projection, the hi/lo reduction
   transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
   transpose_r_kernel<<<blocks_for(w.Npad * w.rpad / 8), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
-  dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
-  lowrank_down_kernel<<<grid, 256, 0, s>>>((const uint16_t*)X, w.lt, (int)T, (int)K, (int)r, (int)w.rpad,
-                                           (int)w.Kpad, (int)w.kc, w.part);
+  const hipError_t ed = launch_down((const uint16_t*)X, w.lt, T, K, r, w, s);
+  if (ed != hipSuccess) return ed;
   reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
                                                                   w.xll);
   return hipGetLastError();
@@ -249,11 +304,28 @@ hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, i
                                const LowrankWs& w, hipStream_t s) {
   if (!w.mfma) return hipErrorInvalidValue;
   transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
-  dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
-  lowrank_down_kernel<<<grid, 256, 0, s>>>((const uint16_t*)X, w.lt, (int)T, (int)K, (int)r, (int)w.rpad,
-                                           (int)w.Kpad, (int)w.kc, w.part);
+  const hipError_t ed = launch_down((const uint16_t*)X, w.lt, T, K, r, w, s);
+  if (ed != hipSuccess) return ed;
   reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
                                                                   w.xll);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_prepare_bwd(const void* dY, const void* L, const void* R, int64_t T, int64_t N, int64_t r,
+                                      int64_t K, const LowrankWs& w, hipStream_t s) {
+  if (!w.mfma) return hipErrorInvalidValue;
+  // down-projection operand: R as [rpad][Kpad] (its own layout, padded); epilogue operand: L as [Npad][rpad]
+  pad_copy_kernel<<<blocks_for(w.rpad * w.Kpad), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Kpad, w.lt);
+  pad_copy_kernel<<<blocks_for(w.Npad * w.rpad), 256, 0, s>>>((const uint16_t*)L, K, r, w.Npad, w.rpad, w.rt);
+  const hipError_t ed = launch_down((const uint16_t*)dY, w.lt, T, N, r, w, s);
+  if (ed != hipSuccess) return ed;
+  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
+                                                                  w.xll);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_hilo(const LowrankWs& w, int64_t rpad32, uint16_t* xht, uint16_t* xlt, hipStream_t s) {
+  transpose_hilo_kernel<<<blocks_for(rpad32 * w.Tpad), 256, 0, s>>>(w.xlh, w.xll, w.Tpad, w.rpad, rpad32, xht, xlt);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -62,6 +62,9 @@ def test_size_queries(lib):
     assert b0 > 0 and b0 % 256 == 0 and b0 % (27648 * 4) == 0
     assert S.slope_decode_workspace_bytes(1, 9216, 72, 27648) == b0 + S.slope_lowrank_workspace_bytes(1, 9216, 72, 27648)
     assert S.slope_decode_workspace_bytes(0, 9216, 0, 27648) == 0
+    g = S.slope_lowrank_grads_workspace_bytes(8192, 9216, 72, 27648)
+    assert g > S.slope_lowrank_workspace_bytes(8192, 9216, 72, 27648) + S.slope_lowrank_workspace_bytes(8192, 27648, 72, 9216)
+    assert S.slope_lowrank_grads_workspace_bytes(8192, 9216, 0, 27648) == 0
     with pytest.raises(S.SlopeError):
         S.slope_decode_workspace_bytes(65, 256, 0, 256)
     with pytest.raises(S.SlopeError):
@@ -118,8 +121,21 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
                                      None) == -6
     assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, 64, FAKE, None) == -2
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, 64, FAKE, None) == -1
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, 64, None, None, 0, None, 0, FAKE, None) == -1
+    # the adapter's dX term needs the (N, K)-exchanged adapter workspace
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
+                                        None) == -6
+    # adapter weight gradients
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, FAKE, 1 << 30,
+                                          FAKE, FAKE, 0, None) == -2
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, FAKE, 16,
+                                          FAKE, FAKE, 0, None) == -4
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, FAKE, 1 << 30,
+                                          FAKE, FAKE, 0, None) == -6
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, FAKE, 1 << 30,
+                                          FAKE, FAKE, 0, None) == -1
     # few-token forward: T <= 64, bf16, a workspace of the queried size
     assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
     assert lib.slope_spmm_fwd_decode(f32, f32, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6

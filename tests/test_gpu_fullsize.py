@@ -173,3 +173,59 @@ def test_decode_forward_sampled(wl, idx, T):
     vsub, msub, _ = oracle.compress24(d["W"][ns], oracle.prune24(d["W"][ns])[0])
     y_ref = oracle.spmm_fwd(d["X"], vsub, msub, K, d["L"], np.ascontiguousarray(d["R"][:, ns]))
     assert normwise(host_f64(Y[:, ns]), y_ref) <= TOL["bf16"]
+
+
+ADAPTER_CASES = [(wl, i) for wl in ("gpt2_small", "bert_large") for i in range(len(WORKLOADS[wl].linears))]
+
+
+@pytest.mark.parametrize("wl,idx", ADAPTER_CASES, ids=[f"{w}-{WORKLOADS[w].linears[i].name}" for w, i in ADAPTER_CASES])
+def test_adapter_backward_sampled(wl, idx):
+    """The adapter's backward at full size: the dX term through the packed dX
+    product, dL and dR from token chunks; sampled rows / columns against the oracle."""
+    w = WORKLOADS[wl]
+    lin = w.linears[idx]
+    T, N, K, r = w.T, lin.N, lin.K, w.r
+    say(f"[fullsize-adapter] {wl} {lin.name}: T={T} K={K} N={N} r={r}")
+    d = layer_inputs(K, N, T, r, w.dtype, seed=0, index=idx)
+    W, X, dY, L, R = (dev(d[k]) for k in ("W", "X", "dY", "L", "R"))
+    mask = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    S.slope_prune24(W, mask)
+    c = Compressed(N, K, torch.bfloat16)
+    S.slope_compress24(W, mask, c.values, c.meta)
+    dp = Compressed(K, N, torch.bfloat16)
+    S.slope_double_prune(c.values, c.meta, N, K, dp.values, dp.meta)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dp.values, dp.meta, K, N, pd)
+    dX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    wsx = torch.empty(S.slope_lowrank_workspace_bytes(T, N, r, K), dtype=torch.uint8, device="cuda")
+    S.slope_spmm_bwd_dx_packed(dY, pd, K, dX, L=L, R=R, workspace=wsx)
+    Xp = torch.empty(S.slope_packed_tokens_bytes(T, K), dtype=torch.uint8, device="cuda")
+    dYp = torch.empty(S.slope_packed_tokens_bytes(T, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_tokens(X, Xp)
+    S.slope_pack_tokens(dY, dYp)
+    dL = torch.empty((K, r), dtype=torch.bfloat16, device="cuda")
+    dR = torch.empty((r, N), dtype=torch.bfloat16, device="cuda")
+    wsg = torch.empty(S.slope_lowrank_grads_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    S.slope_lowrank_grads_packed(X, dY, Xp, dYp, L, R, wsg, dL, dR)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2000 + idx)
+    tol = TOL[w.dtype]
+    # dX on sampled tokens: the sparse product (oracle double prune of sampled column groups) + the adapter term
+    ts = _rows(rng, T, 32)
+    term = oracle.lowrank_bwd(d["X"][ts], d["dY"][ts], d["L"], d["R"])[0]
+    for c0 in _group_cols(rng, K, 3):
+        Wc = np.ascontiguousarray(d["W"][:, c0:c0 + 4])
+        mc, _ = oracle.prune24(Wc)
+        vc, mcw, _ = oracle.compress24(Wc, mc)
+        vdp_ref, mdp_ref, _ = oracle.double_prune(vc, mcw, N, 4)
+        ref = oracle.spmm_bwd_dx(d["dY"][ts], vdp_ref, mdp_ref, N) + term[:, c0:c0 + 4]
+        assert normwise(host_f64(dX[ts][:, c0:c0 + 4]), ref) <= tol
+    # dR on sampled columns (all tokens), dL on sampled rows (all tokens)
+    ns = _rows(rng, N, 48)
+    dR_ref = oracle.lowrank_bwd(d["X"], np.ascontiguousarray(d["dY"][:, ns]), d["L"],
+                                np.ascontiguousarray(d["R"][:, ns]))[2]
+    assert normwise(host_f64(dR[:, ns]), dR_ref) <= tol
+    ks = _rows(rng, K, 48)
+    dL_ref = oracle.lowrank_bwd(np.ascontiguousarray(d["X"][:, ks]), d["dY"], np.ascontiguousarray(d["L"][ks]),
+                                d["R"])[1]
+    assert normwise(host_f64(dL[ks]), dL_ref) <= tol

@@ -335,6 +335,84 @@ def test_spmm_fwd_decode_integer_exact():
     assert np.array_equal(host_f64(Y), oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"]))
 
 
+# ------------------------------------------------------------------ adapter backward
+
+ADAPTER_BWD_SHAPES = [(64, 256, 256, 8), (300, 528, 272, 40), (37, 64, 136, 72), (512, 768, 1024, 128),
+                      (1, 64, 64, 1), (130, 272, 520, 33)]
+
+
+def _chunks(M):
+    T, C = M.shape
+    p = torch.empty(S.slope_packed_tokens_bytes(T, C), dtype=torch.uint8, device="cuda")
+    S.slope_pack_tokens(M, p)
+    return p
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,N,K,r", ADAPTER_BWD_SHAPES)
+def test_spmm_bwd_dx_packed_with_adapter(T, N, K, r, out_dt):
+    say(f"bwd dX + adapter T={T} N={N} K={K} r={r} out={out_dt}")
+    d = _layer(T, N, K, r, "bf16", seed=13 * T + N + K + r)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vdp"]), dev_meta(d["mdp"]), K, N, pd)
+    ws = torch.empty(max(16, S.slope_lowrank_workspace_bytes(T, N, r, K)), dtype=torch.uint8, device="cuda")
+    dX = empty((T, K), torch_dtype(out_dt))
+    S.slope_spmm_bwd_dx_packed(dev(d["dY"]), pd, K, dX, L=dev(d["L"]), R=dev(d["R"]), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N) + oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])[0]
+    err = normwise(host_f64(dX), ref)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("T,N,K,r", ADAPTER_BWD_SHAPES + [(0, 64, 64, 8)])
+def test_lowrank_grads_packed(T, N, K, r, out_dt):
+    say(f"adapter grads T={T} N={N} K={K} r={r} out={out_dt}")
+    d = _layer(T, N, K, r, "bf16", seed=17 * T + N + K + r)
+    X, dY, L, R = dev(d["X"]), dev(d["dY"]), dev(d["L"]), dev(d["R"])
+    ws = torch.empty(max(16, S.slope_lowrank_grads_workspace_bytes(T, K, r, N)), dtype=torch.uint8, device="cuda")
+    od = torch_dtype(out_dt)
+    dL, dR = empty((K, r), od), empty((r, N), od)
+    S.slope_lowrank_grads_packed(X, dY, _chunks(X), _chunks(dY), L, R, ws, dL, dR)
+    dL2, dR2 = empty((K, r), od), empty((r, N), od)
+    S.slope_lowrank_grads_packed(X, dY, _chunks(X), _chunks(dY), L, R, ws, dL2, dR2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dL), host(dL2)) and np.array_equal(host(dR), host(dR2))   # fixed order
+    _, dL_ref, dR_ref = oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])
+    assert normwise(host_f64(dL), dL_ref) <= TOL["bf16"]
+    assert normwise(host_f64(dR), dR_ref) <= TOL["bf16"]
+    # accumulation adds to what is there
+    bL = torch.randn((K, r), device="cuda").to(od)
+    bR = torch.randn((r, N), device="cuda").to(od)
+    aL, aR = bL.clone(), bR.clone()
+    S.slope_lowrank_grads_packed(X, dY, _chunks(X), _chunks(dY), L, R, ws, aL, aR, accumulate=True)
+    torch.cuda.synchronize()
+    assert normwise(host_f64(aL), dL_ref + host_f64(bL)) <= TOL["bf16"]
+    assert normwise(host_f64(aR), dR_ref + host_f64(bR)) <= TOL["bf16"]
+
+
+def test_adapter_backward_integer_exact():
+    """Integer inputs: X . L and dY . R^T are exact in the hi/lo pair, every
+    product and sum is exact in fp32, so fp32 outputs equal the oracle."""
+    T, N, K, r = 70, 272, 528, 12
+    say("adapter backward integer probe")
+    d = _layer(T, N, K, r, "bf16", seed=29, ints=True)
+    X, dY, L, R = dev(d["X"]), dev(d["dY"]), dev(d["L"]), dev(d["R"])
+    ws = torch.empty(S.slope_lowrank_grads_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    dL, dR = empty((K, r), torch.float32), empty((r, N), torch.float32)
+    S.slope_lowrank_grads_packed(X, dY, _chunks(X), _chunks(dY), L, R, ws, dL, dR)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vdp"]), dev_meta(d["mdp"]), K, N, pd)
+    wsx = torch.empty(S.slope_lowrank_workspace_bytes(T, N, r, K), dtype=torch.uint8, device="cuda")
+    dX = empty((T, K), torch.float32)
+    S.slope_spmm_bwd_dx_packed(dY, pd, K, dX, L=L, R=R, workspace=wsx)
+    torch.cuda.synchronize()
+    dXa, dL_ref, dR_ref = oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])
+    assert np.array_equal(host_f64(dL), dL_ref)
+    assert np.array_equal(host_f64(dR), dR_ref)
+    assert np.array_equal(host_f64(dX), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N) + dXa)
+
+
 WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
                 (0, 64, 64), (257, 264, 520)]
 
