@@ -137,7 +137,9 @@ def bwd_dx(S, li):
 
 
 def lowrank_grads(S, li):
-    S.slope_lowrank_grads_packed(li.X, li.dY, li.Xp, li.dYp, li.L, li.R, li.ws_grads, li.dL, li.dR)
+    # X . L and dY . R^T come from the forward's and the dX product's workspaces
+    S.slope_lowrank_grads_packed(li.X, li.dY, li.Xp, li.dYp, li.L, li.R, li.ws_grads, li.dL, li.dR,
+                                 fwd_workspace=li.ws, bwd_workspace=li.ws_bwd)
 
 
 def step(lins, S, ev=None):
@@ -256,6 +258,8 @@ def profile_mode(args, wl, T):
         S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
         pack_sparse(S, li)
         pack(S, li)
+        S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
+        bwd_dx(S, li)
     torch.cuda.synchronize()
     op = args.profile_op
     for _ in range(args.repeat):

@@ -225,14 +225,19 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
  *   dL [K, r] = X^T . (dY . R^T),   dR [r, N] = (X . L)^T . dY
  * X [T, K], dY [T, N], L, R bf16 row-major; X_packed, dY_packed: the same
  * matrices in token-chunk form (slope_pack_tokens), as the weight gradient
- * uses them.  dL, dR in out_dt (BF16 or F32), overwritten, or added to when
+ * uses them.  fwd_workspace_or_null / bwd_workspace_or_null: the adapter
+ * workspaces that slope_spmm_fwd_packed (X, L, R) and slope_spmm_bwd_dx_packed
+ * (dY, L, R) filled for these same operands, untouched since (they hold
+ * X . L and dY . R^T, which are then not recomputed); NULL to compute them
+ * here.  dL, dR in out_dt (BF16 or F32), overwritten, or added to when
  * accumulate != 0.  workspace: slope_lowrank_grads_workspace_bytes(T, K, r,
  * N) bytes, scratch.  Sums over tokens run in a fixed order.  Errors:
  * SLOPE_ERR_SHAPE unless K % 8 == 0 and N % 8 == 0; SLOPE_ERR_UNSUPPORTED
  * for r > 128; SLOPE_ERR_WORKSPACE. */
 slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
                                         const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
-                                        const void* L, const void* R, void* workspace, int64_t workspace_bytes,
+                                        const void* L, const void* R, const void* fwd_workspace_or_null,
+                                        const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
                                         void* dL, void* dR, int accumulate, void* stream);
 
 /* Bytes of device workspace slope_spmm_fwd_decode needs for T <= 64 tokens:

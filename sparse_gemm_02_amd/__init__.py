@@ -67,8 +67,8 @@ _SIGS = {
     "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                         _vp]),
     "slope_lowrank_grads_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
-    "slope_lowrank_grads_packed": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64,
-                                          _vp, _vp, _i32, _vp]),
+    "slope_lowrank_grads_packed": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                          _vp, _i64, _vp, _vp, _i32, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
@@ -260,14 +260,14 @@ def slope_lowrank_grads_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
 
 
 def slope_lowrank_grads_packed(X, dY, X_packed, dY_packed, L, R, workspace, dL, dR, accumulate=False,
-                               stream=None) -> None:
+                               fwd_workspace=None, bwd_workspace=None, stream=None) -> None:
     T, K = X.shape
     N = dY.shape[1]
     r = int(L.shape[1])
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_lowrank_grads_packed", library().slope_lowrank_grads_packed(
-        _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(workspace), wb,
-        _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
+        _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(fwd_workspace),
+        _p(bwd_workspace), _p(workspace), wb, _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
 
 
 def slope_packed_tokens_bytes(T: int, C: int) -> int:

@@ -342,7 +342,8 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
 
 slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
                                         const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
-                                        const void* L, const void* R, void* workspace, int64_t workspace_bytes,
+                                        const void* L, const void* R, const void* fwd_workspace_or_null,
+                                        const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
                                         void* dL, void* dR, int accumulate, void* stream) {
   SLOPE_TRY(check_io(SLOPE_BF16, out_dt));
   if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
@@ -355,6 +356,8 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
   SLOPE_TRY(ptr(dL, true));
   SLOPE_TRY(ptr(dR, true));
   SLOPE_TRY(ptr(workspace, false));
+  SLOPE_TRY(ptr(fwd_workspace_or_null, false));
+  SLOPE_TRY(ptr(bwd_workspace_or_null, false));
   if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   const GradsWs g = grads_ws(T, K, r, N);
@@ -368,8 +371,13 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
     return from_hip(e);
   }
   char* p = static_cast<char*>(workspace);
-  const slope::LowrankWs wf = slope::lowrank_layout(Dt::BF16, p, T, K, r, N);
-  const slope::LowrankWs wb = slope::lowrank_layout(Dt::BF16, p + g.fwd, T, N, r, K);
+  // X . L and dY . R^T: taken from the forward's / the dX product's adapter
+  // workspace when the caller hands them over, else computed here
+  const bool have_f = fwd_workspace_or_null != nullptr, have_b = bwd_workspace_or_null != nullptr;
+  const slope::LowrankWs wf =
+      slope::lowrank_layout(Dt::BF16, have_f ? const_cast<void*>(fwd_workspace_or_null) : (void*)p, T, K, r, N);
+  const slope::LowrankWs wb = slope::lowrank_layout(
+      Dt::BF16, have_b ? const_cast<void*>(bwd_workspace_or_null) : (void*)(p + g.fwd), T, N, r, K);
   uint16_t* xh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd);
   uint16_t* xl = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + g.trans);
   uint16_t* gh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + 2 * g.trans);
@@ -377,8 +385,9 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
   float* pr = reinterpret_cast<float*>(p + g.fwd + g.bwd + 4 * g.trans);
   float* pl = reinterpret_cast<float*>(p + g.fwd + g.bwd + 4 * g.trans + g.part_r);
   const int64_t r32 = (r + 31) / 32 * 32;
-  hipError_t e = slope::launch_lowrank_down(Dt::BF16, X, L, T, K, r, wf, s);              // X . L
-  if (e == hipSuccess) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
+  hipError_t e = hipSuccess;
+  if (!have_f) e = slope::launch_lowrank_down(Dt::BF16, X, L, T, K, r, wf, s);                        // X . L
+  if (e == hipSuccess && !have_b) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
   if (e == hipSuccess) e = slope::launch_transpose_hilo(wf, r32, xh, xl, s);
   if (e == hipSuccess) e = slope::launch_transpose_hilo(wb, r32, gh, gl, s);
   if (e == hipSuccess)

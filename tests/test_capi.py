@@ -128,14 +128,14 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
                                         None) == -6
     # adapter weight gradients
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, FAKE, 1 << 30,
-                                          FAKE, FAKE, 0, None) == -2
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, FAKE, 16,
-                                          FAKE, FAKE, 0, None) == -4
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, FAKE, 1 << 30,
-                                          FAKE, FAKE, 0, None) == -6
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, FAKE, 1 << 30,
-                                          FAKE, FAKE, 0, None) == -1
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, None, None, FAKE,
+                                          1 << 30, FAKE, FAKE, 0, None) == -2
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
+                                          16, FAKE, FAKE, 0, None) == -4
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, None, None,
+                                          FAKE, 1 << 30, FAKE, FAKE, 0, None) == -6
+    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
+                                          1 << 30, FAKE, FAKE, 0, None) == -1
     # few-token forward: T <= 64, bf16, a workspace of the queried size
     assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
     assert lib.slope_spmm_fwd_decode(f32, f32, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6

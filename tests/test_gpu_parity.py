@@ -391,6 +391,32 @@ def test_lowrank_grads_packed(T, N, K, r, out_dt):
     assert normwise(host_f64(aR), dR_ref + host_f64(bR)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("T,N,K,r", [(300, 528, 272, 40), (64, 256, 256, 8)])
+def test_lowrank_grads_reuse_workspaces(T, N, K, r):
+    """Handing over the forward's and the dX product's adapter workspaces skips
+    recomputing X . L and dY . R^T; the gradients are bitwise the same."""
+    say(f"adapter grads with reused workspaces T={T} N={N} K={K} r={r}")
+    d = _layer(T, N, K, r, "bf16", seed=31 * T + r)
+    X, dY, L, R = dev(d["X"]), dev(d["dY"]), dev(d["L"]), dev(d["R"])
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vdp"]), dev_meta(d["mdp"]), K, N, pd)
+    wf = torch.empty(S.slope_lowrank_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(S.slope_lowrank_workspace_bytes(T, N, r, K), dtype=torch.uint8, device="cuda")
+    S.slope_spmm_fwd_packed(X, ps, N, empty((T, N), torch.bfloat16), L=L, R=R, workspace=wf)
+    S.slope_spmm_bwd_dx_packed(dY, pd, K, empty((T, K), torch.bfloat16), L=L, R=R, workspace=wb)
+    ws = torch.empty(S.slope_lowrank_grads_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    out = []
+    for reuse in (False, True):
+        dL, dR = empty((K, r), torch.bfloat16), empty((r, N), torch.bfloat16)
+        S.slope_lowrank_grads_packed(X, dY, _chunks(X), _chunks(dY), L, R, ws, dL, dR,
+                                     fwd_workspace=wf if reuse else None, bwd_workspace=wb if reuse else None)
+        torch.cuda.synchronize()
+        out.append((host(dL), host(dR)))
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
+
+
 def test_adapter_backward_integer_exact():
     """Integer inputs: X . L and dY . R^T are exact in the hi/lo pair, every
     product and sum is exact in fp32, so fp32 outputs equal the oracle."""
