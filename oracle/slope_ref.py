@@ -14,8 +14,8 @@ Lazy Low-Rank Adapter Pretraining of LLMs"):
   Adapters), 2.C (Optimized CUDA Kernels),
 * the OpenReview discussion (paperhub.cn), sections "Impact of Introducing
   Additional Zeros in N:M Pattern", "Memory Footprint Reduction During
-  Pretraining and Inference" and "Clarification on Inference Speedup and Sparse
-  Pre-Training".
+  Pretraining and Inference", "Clarification on Inference Speedup and Sparse
+  Pre-Training" and "Choice of Optimizer".
 
 Conventions (W is [N, K] = [out, in] as for a linear layer):
 
@@ -24,6 +24,8 @@ Conventions (W is [N, K] = [out, in] as for a linear layer):
     dW = (dY^T . X) (.) M_s   kept only at the static forward mask
     Y += (X . L) . R          L [K, r], R [r, N]  (W_dense = W_sparse + L R)
     dX += (dY . R^T) . L^T, dL = X^T . (dY . R^T), dR = (X . L)^T . dY
+    AdamW on the compressed values of W_s (moments only for the kept slots),
+    then the double prune of the updated W_s
 
 Tensors arrive as raw bit patterns (uint16 = bf16, uint32 = fp32), so every
 selection is made on the exact stored values.  Products and sums are done in
@@ -49,6 +51,7 @@ import numpy as np
 __all__ = [
     "widen", "prune24", "compress24", "decompress24", "mask_from_meta",
     "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add", "lowrank_bwd",
+    "round_bf16", "round_f32", "adamw_update", "adamw_compressed", "adamw_double_prune",
     "storage_accounting", "LEGAL_NIBBLES",
 ]
 
@@ -281,6 +284,87 @@ def lowrank_bwd(X, dY, L, R):
     Xw, dYw, Lw, Rw = widen(X), widen(dY), widen(L), widen(R)
     G = dYw @ Rw.T
     return G @ Lw.T, Xw.T @ G, (Xw @ Lw).T @ dYw
+
+
+# --------------------------------------------------------------------------- optimizer
+
+def round_bf16(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) nearest to float64 values, ties to even.
+
+    Rounds once, straight from float64 (no intermediate fp32 rounding): the
+    value is scaled so that the bf16 quantum of its binade (2**(e-8) for
+    2**(e-1) <= |x| < 2**e, never below the subnormal quantum 2**-133) becomes
+    1, rounded half-to-even, and scaled back; past the largest finite bf16 it
+    becomes an infinity, NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.ldexp(np.rint(np.ldexp(x, -q)), q).astype(np.float32)
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_f32(x) -> np.ndarray:
+    """fp32 values nearest to float64 values, ties to even (IEEE conversion)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def adamw_update(p, g, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01):
+    """One AdamW step in float64: Adam moments with bias correction and weight
+    decay decoupled from the gradient (Loshchilov and Hutter, "Decoupled
+    Weight Decay Regularization", Algorithm 2), in the common library form
+    where the learning rate scales both terms:
+
+        m <- beta1 m + (1 - beta1) g
+        v <- beta2 v + (1 - beta2) g^2
+        p <- p - lr * weight_decay * p - lr * m_hat / (sqrt(v_hat) + eps)
+        m_hat = m / (1 - beta1^step), v_hat = v / (1 - beta2^step)
+
+    step counts updates from 1.  Returns (p, m, v) as float64, unrounded.
+    """
+    p, g, m, v = (np.asarray(a, dtype=np.float64) for a in (p, g, m, v))
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** step)
+    v_hat = v / (1.0 - beta2 ** step)
+    p = p - lr * weight_decay * p - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return p, m, v
+
+
+def adamw_compressed(values, grads, m, v, step, **hp):
+    """AdamW on the stored non-zeros of a 2:4 weight.
+
+    The discussion page trains SLoPe with AdamW ("Choice of Optimizer") and
+    counts the optimizer state as two 32-bit moments for each of the two
+    non-zeros of every four weights ("Memory Footprint Reduction During
+    Pretraining and Inference"): the update runs on the compressed values, the
+    pruned positions have no state and stay zero, the mask does not move.
+
+    values: raw bits of the compressed values (uint16 bf16 or uint32 fp32);
+    grads: raw bits of the gradient in the same slot order (bf16 or fp32);
+    m, v: float32 moments of the same shape.  The step is computed in float64
+    and stored once: values rounded to their own format, moments to fp32.
+    Returns (values bits, m float32, v float32).
+    """
+    values = np.asarray(values)
+    p, m1, v1 = adamw_update(widen(values), widen(grads), np.asarray(m, np.float32),
+                             np.asarray(v, np.float32), step, **hp)
+    out = round_bf16(p) if values.dtype == np.uint16 else round_f32(p).view(np.uint32)
+    return out, round_f32(m1), round_f32(v1)
+
+
+def adamw_double_prune(values_s, meta_s, dW_values, m, v, N, K, step, **hp):
+    """The weight update of one SLoPe training step: AdamW on the compressed
+    values of W_s (static mask, metadata unchanged), then the double-pruned
+    transposed copy of the updated weight for the next backward pass
+    (explainer 2.A: the column mask follows the current weights).
+
+    Returns (values_s bits, m, v, values_dpT, meta_dpT, mask_dpT).
+    """
+    vals, m1, v1 = adamw_compressed(values_s, dW_values, m, v, step, **hp)
+    return (vals, m1, v1) + tuple(double_prune(vals, meta_s, N, K))
 
 
 # --------------------------------------------------------------------------- accounting
