@@ -12,7 +12,9 @@ transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 The three products run on the packed operands (the *_packed entry points);
 the packing passes are part of the step.  A `decode` object adds the
 few-token forward (slope_spmm_fwd_decode) at the workload's inference token
-counts, as HBM bytes per second.
+counts, as HBM bytes per second, and a `weight_update` object times the optimizer
+step (AdamW on the compressed values fused with the double prune, and on the
+adapter factors), also as HBM bytes per second.
 
 prune24 and compress24 run once per layer in training (the forward mask is
 static); they are kept inside the timed step so the step covers every kernel of
@@ -52,7 +54,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
-    ap.add_argument("--profile-op", choices=OPS + ("copy",), default=None,
+    ap.add_argument("--profile-op", choices=OPS + ("adamw_double_prune", "copy"), default=None,
                     help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
     ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
     ap.add_argument("--repeat", type=int, default=10)
@@ -260,6 +262,10 @@ def profile_mode(args, wl, T):
         pack(S, li)
         S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
         bwd_dx(S, li)
+        wgrad(S, li)
+        if args.profile_op == "adamw_double_prune":
+            li.opt_m = torch.zeros(li.vs.numel(), device="cuda")
+            li.opt_v = torch.zeros(li.vs.numel(), device="cuda")
     torch.cuda.synchronize()
     op = args.profile_op
     for _ in range(args.repeat):
@@ -282,6 +288,9 @@ def profile_mode(args, wl, T):
                 pack(S, li)
             elif op == "masked_wgrad":
                 wgrad(S, li)
+            elif op == "adamw_double_prune":
+                S.slope_adamw_double_prune(li.vs, li.ms, li.dW, li.opt_m, li.opt_v, li.N, li.K, li.vdp, li.mdp,
+                                           1, lr=1e-4)
     torch.cuda.synchronize()
     print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
 
@@ -317,6 +326,50 @@ def decode_pass(lins, wl, S, torch, reps=20):
                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         del calls
     return out
+
+
+def update_pass(lins, S, torch, reps=10):
+    """The weight update of a training step, timed apart from the GEMM step:
+    AdamW on the compressed values fused with the double prune of the updated
+    weight (slope_adamw_double_prune) on every linear, plus AdamW on the
+    adapter factors L and R (slope_adamw), with fp32 moments.  HBM bound:
+    algorithmic bytes are 12.25 B per weight (values, gradient and metadata
+    read, values and moments read and written, the double-pruned copy written)
+    and 22 B per adapter element."""
+    hp = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    state, nbytes = [], 0
+    for li in lins:
+        n = li.vs.numel()
+        m = torch.randn(n, device="cuda") * 1e-3
+        v = torch.rand(n, device="cuda") * 1e-6
+        aL = [torch.zeros(li.L.numel(), device="cuda") for _ in range(2)]
+        aR = [torch.zeros(li.R.numel(), device="cuda") for _ in range(2)]
+        state.append((li, m, v, aL, aR))
+        nbytes += 12.25 * li.N * li.K + 22 * (li.L.numel() + li.R.numel())
+    k = [0]
+
+    def run():
+        k[0] += 1
+        for li, m, v, aL, aR in state:
+            S.slope_adamw_double_prune(li.vs, li.ms, li.dW, m, v, li.N, li.K, li.vdp, li.mdp, k[0], **hp)
+            S.slope_adamw(li.L, li.dL, aL[0], aL[1], k[0], **hp)
+            S.slope_adamw(li.R, li.dR, aR[0], aR[1], k[0], **hp)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del state
+    return {"ms_per_layer": round(ms, 4), "bytes": int(nbytes), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "what": "AdamW on the compressed values fused with the double prune (four linears) "
+                    "+ AdamW on the adapter factors; fp32 moments"}
 
 
 def measured_traffic(op):
@@ -434,6 +487,7 @@ def main():
            "roofline": roofline}
     if wl.decode_T:
         out["decode"] = decode_pass(lins, wl, S, torch)
+    out["weight_update"] = update_pass(lins, S, torch)
     # free the layer before the CPU leg
     del lins
     torch.cuda.empty_cache()

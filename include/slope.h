@@ -293,6 +293,43 @@ slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void
                                int64_t T, int64_t K, int64_t r, int64_t N, void* workspace,
                                int64_t workspace_bytes, void* Y, void* stream);
 
+/* Hyper-parameters of one AdamW update (the discussion page, "Choice of
+ * Optimizer": SLoPe trains with AdamW).  Plain host struct, read during the
+ * call only.  step numbers this update, counting from 1 (bias correction). */
+typedef struct slope_adamw_params {
+  double lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} slope_adamw_params;
+
+/* One AdamW step (decoupled weight decay, bias-corrected moments) on n stored
+ * values, elementwise:
+ *   m = beta1 m + (1 - beta1) g;   v = beta2 v + (1 - beta2) g^2
+ *   p = p (1 - lr wd) - lr / (1 - beta1^step) * m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ * params [n] param_dt (updated in place): the compressed values of a 2:4
+ * weight (the discussion page, "Memory Footprint", keeps optimizer state only
+ * for the two non-zeros of every four) or a dense adapter factor L or R;
+ * grads [n] grad_dt (BF16 or F32) in the same order; m, v [n] fp32 moments,
+ * updated in place.  fp32 arithmetic (constants derived in double on the
+ * host), one rounding of each new value to param_dt.  hp: host pointer.
+ * Errors: SLOPE_ERR_INVALID_ARG for a null pointer, unknown dtype, n < 0,
+ * step < 1, a beta outside [0, 1), eps < 0 or non-finite lr / weight_decay;
+ * SLOPE_ERR_UNSUPPORTED for n > 2^40. */
+slope_status slope_adamw(slope_dtype param_dt, slope_dtype grad_dt, void* params, const void* grads, float* m,
+                         float* v, int64_t n, const slope_adamw_params* hp, void* stream);
+
+/* The weight update of one SLoPe training step, fused: slope_adamw on the
+ * compressed values of W_s (values_s [N, K/2] and m, v [N, K/2] updated in
+ * place; meta_s unchanged, the mask is static), then slope_double_prune of the
+ * updated W_s (explainer 2.A: the backward weight is pruned again from the
+ * current weight) into values_dpT [K, N/2], meta_dpT [K, ceil(N/32)] and, if
+ * given, mask_dpT [K, N].  dW_values [N, K/2] grad_dt, in W_s's slot order (as
+ * slope_masked_wgrad writes it).  Results equal slope_adamw followed by
+ * slope_double_prune.  Errors: those of both calls. */
+slope_status slope_adamw_double_prune(slope_dtype dt, slope_dtype grad_dt, void* values_s, const uint32_t* meta_s,
+                                      const void* dW_values, float* m, float* v, int64_t N, int64_t K,
+                                      const slope_adamw_params* hp, void* values_dpT, uint32_t* meta_dpT,
+                                      uint8_t* mask_dpT_or_null, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ __all__ = [
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
     "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_lowrank_grads_workspace_bytes",
-    "slope_lowrank_grads_packed",
+    "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +44,15 @@ STATUS = {0: "SLOPE_OK", -1: "SLOPE_ERR_INVALID_ARG", -2: "SLOPE_ERR_SHAPE", -3:
 _F32, _BF16 = 0, 1
 _i64, _vp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 _P_I64 = ctypes.POINTER(ctypes.c_int64)
+
+
+class AdamWParams(ctypes.Structure):
+    """slope_adamw_params: hyper-parameters of one AdamW update (step counts from 1)."""
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
+_P_HP = ctypes.POINTER(AdamWParams)
 
 # name -> (restype, argtypes)
 _SIGS = {
@@ -72,6 +81,9 @@ _SIGS = {
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "slope_adamw": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _P_HP, _vp]),
+    "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
+                                        _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -295,3 +307,37 @@ def slope_lowrank_add(X, L, R, workspace, Y, stream=None) -> None:
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_lowrank_add", library().slope_lowrank_add(_dt(X), _dt(Y), _nn(X), _nn(L), _nn(R), T, K, r, N,
                                                             _p(workspace), wb, _nn(Y), _s(stream)))
+
+
+def _hp(step, lr, beta1, beta2, eps, weight_decay):
+    return AdamWParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+
+
+def _f32(t):
+    if t.dtype != torch.float32:
+        raise TypeError(f"optimizer moments must be float32, got {t.dtype}")
+    return _nn(t)
+
+
+def slope_adamw(params, grads, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
+                stream=None) -> None:
+    """One AdamW step on params (updated in place) with float32 moments m, v."""
+    n = params.numel()
+    if grads.numel() != n or m.numel() != n or v.numel() != n:
+        raise ValueError("params, grads, m and v must have the same number of elements")
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay)
+    _check("slope_adamw", library().slope_adamw(_dt(params), _dt(grads), _nn(params), _nn(grads), _f32(m), _f32(v),
+                                                n, ctypes.byref(hp), _s(stream)))
+
+
+def slope_adamw_double_prune(values_s, meta_s, dW_values, m, v, N, K, values_dpT, meta_dpT, step, lr, beta1=0.9,
+                             beta2=0.999, eps=1e-8, weight_decay=0.01, mask_dpT=None, stream=None) -> None:
+    """AdamW on the compressed values of W_s (in place), then the double prune of the updated W_s."""
+    n = values_s.numel()
+    if dW_values.numel() != n or m.numel() != n or v.numel() != n:
+        raise ValueError("values_s, dW_values, m and v must have the same number of elements")
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay)
+    _check("slope_adamw_double_prune", library().slope_adamw_double_prune(
+        _dt(values_s), _dt(dW_values), _nn(values_s), _nn(meta_s), _nn(dW_values), _f32(m), _f32(v), N, K,
+        ctypes.byref(hp), _nn(values_dpT), _nn(meta_dpT), _p(mask_dpT), _s(stream)))
+

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libslope.so")
-SOURCES = ["capi.cpp", "prune.hip", "generic.hip", "spmm.hip", "lowrank.hip", "wgrad.hip", "decode.hip", "lowrank_bwd.hip"]
+SOURCES = ["capi.cpp", "prune.hip", "generic.hip", "spmm.hip", "lowrank.hip", "wgrad.hip", "decode.hip", "lowrank_bwd.hip", "adamw.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

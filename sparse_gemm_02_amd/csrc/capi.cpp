@@ -3,6 +3,8 @@
 // untouched.  Declarations and the meaning of every argument: include/slope.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "../../include/slope.h"
 #include "launch.h"
 
@@ -42,6 +44,27 @@ constexpr int64_t kPackedMaxCols = 1 << 21, kPackedMaxRank = 128;
 constexpr int64_t kDecodeMaxTokens = 64;   // the few-token forward
 
 int64_t workspace_need(int64_t T, int64_t K, int64_t r, int64_t N) { return slope::lowrank_workspace_bytes(T, K, r, N); }
+
+// Checks AdamW hyper-parameters and derives the per-update fp32 constants.
+slope_status adamw_step(const slope_adamw_params* hp, slope::AdamWStep* c) {
+  if (!hp) return SLOPE_ERR_INVALID_ARG;
+  if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) ||
+      !(hp->eps >= 0.0) || !std::isfinite(hp->eps) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+    return SLOPE_ERR_INVALID_ARG;
+  const double t = (double)hp->step;
+  const double bc1 = 1.0 - std::pow(hp->beta1, t), bc2 = 1.0 - std::pow(hp->beta2, t);
+  c->decay = (float)(1.0 - hp->lr * hp->weight_decay);
+  c->beta1 = (float)hp->beta1;
+  c->omb1 = (float)(1.0 - hp->beta1);
+  c->beta2 = (float)hp->beta2;
+  c->omb2 = (float)(1.0 - hp->beta2);
+  c->step_size = (float)(hp->lr / bc1);
+  c->inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  c->eps = (float)hp->eps;
+  return SLOPE_OK;
+}
+
+constexpr int64_t kAdamwMaxElems = int64_t(1) << 40;
 
 }  // namespace
 
@@ -453,6 +476,40 @@ slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void
   hipError_t e = slope::launch_lowrank_prepare((Dt)in_dt, X, L, R, T, K, r, N, w, s);
   if (e != hipSuccess) return SLOPE_ERR_HIP;
   return from_hip(slope::launch_lowrank_up_add((Dt)in_dt, (Dt)out_dt, w, R, T, r, N, Y, s));
+}
+
+slope_status slope_adamw(slope_dtype param_dt, slope_dtype grad_dt, void* params, const void* grads, float* m,
+                         float* v, int64_t n, const slope_adamw_params* hp, void* stream) {
+  if (!dt_ok(param_dt) || !dt_ok(grad_dt) || n < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(params, true));
+  SLOPE_TRY(ptr(grads, true));
+  SLOPE_TRY(ptr(m, true));
+  SLOPE_TRY(ptr(v, true));
+  slope::AdamWStep c;
+  SLOPE_TRY(adamw_step(hp, &c));
+  if (n > kAdamwMaxElems) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_adamw((Dt)param_dt, (Dt)grad_dt, params, grads, m, v, n, c, (hipStream_t)stream));
+}
+
+slope_status slope_adamw_double_prune(slope_dtype dt, slope_dtype grad_dt, void* values_s, const uint32_t* meta_s,
+                                      const void* dW_values, float* m, float* v, int64_t N, int64_t K,
+                                      const slope_adamw_params* hp, void* values_dpT, uint32_t* meta_dpT,
+                                      uint8_t* mask_dpT_or_null, void* stream) {
+  if (!dt_ok(dt) || !dt_ok(grad_dt) || N < 0 || K < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values_s, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(dW_values, true));
+  SLOPE_TRY(ptr(m, true));
+  SLOPE_TRY(ptr(v, true));
+  SLOPE_TRY(ptr(values_dpT, true));
+  SLOPE_TRY(ptr(meta_dpT, true));
+  SLOPE_TRY(ptr(mask_dpT_or_null, false));
+  slope::AdamWStep c;
+  SLOPE_TRY(adamw_step(hp, &c));
+  if (N % 4 || K % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(N) || !in_range(K)) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_adamw_double_prune((Dt)dt, (Dt)grad_dt, values_s, meta_s, dW_values, m, v, N, K, c,
+                                                   values_dpT, meta_dpT, mask_dpT_or_null, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -16,6 +16,20 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s);
 
+// Per-update constants of AdamW, derived on the host in double precision and
+// rounded once to fp32:
+//   p' = p * decay - step_size * m' / (sqrt(v') * inv_sqrt_bc2 + eps)
+//   m' = beta1 m + omb1 g,  v' = beta2 v + omb2 g^2
+struct AdamWStep {
+  float decay, beta1, omb1, beta2, omb2, step_size, inv_sqrt_bc2, eps;
+};
+hipError_t launch_adamw(Dt param, Dt grad, void* params, const void* grads, float* m, float* v, int64_t n,
+                        const AdamWStep& c, hipStream_t s);
+// AdamW on the compressed values of W_s, then the double prune of the result.
+hipError_t launch_adamw_double_prune(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s, const void* grads,
+                                     float* m, float* v, int64_t N, int64_t K, const AdamWStep& c,
+                                     void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s);
+
 // Adapter workspace (caller-owned device memory), carved into:
 //   part [splits][T][r] fp32   partial sums of X . L over k-splits
 //   xlh, xll [Tpad][rpad] bf16 X . L split into hi + lo bf16 parts (zero padded)

@@ -6,6 +6,7 @@
 // Footprint" section keeps each as two 16-bit values plus indices per group of
 // four.  Selection rule: the two largest magnitudes, equal magnitudes to the
 // lower position, NaN above every number.
+#include "adamw.h"
 #include "common.h"
 #include "launch.h"
 
@@ -217,11 +218,20 @@ __global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restr
 // conflicts.
 constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit words
 
-__global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(const uint16_t* __restrict__ vals,
-                                                                    const uint32_t* __restrict__ meta, int64_t N,
-                                                                    int64_t K, uint16_t* __restrict__ out_vals,
+//
+// With UPD the kernel first applies one AdamW step to the compressed values it
+// loads (gradient GT, fp32 moments m and v at the same element index), writes
+// the new values and moments back in place and double-prunes the new values:
+// the optimizer's pass over the weight and the double prune share one read.
+template <bool UPD, typename GT>
+__global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* vals, const uint32_t* __restrict__ meta,
+                                                                    int64_t N, int64_t K,
+                                                                    uint16_t* __restrict__ out_vals,
                                                                     uint32_t* __restrict__ out_meta,
-                                                                    uint8_t* __restrict__ out_mask) {
+                                                                    uint8_t* __restrict__ out_mask,
+                                                                    const GT* __restrict__ grads,
+                                                                    float* __restrict__ m, float* __restrict__ v,
+                                                                    AdamWStep hp) {
   __shared__ __attribute__((aligned(16))) uint32_t tile[DW_T * DW_PITCH];
   const int tid = threadIdx.x;
   const int64_t n0 = (int64_t)blockIdx.y * DW_T, k0 = (int64_t)blockIdx.x * DW_T;
@@ -233,17 +243,22 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(const uint1
   for (int it = 0; it < 4; ++it) {
     const int r = it * 32 + (tid >> 3);
     const int64_t row = n0 + r, kc = k0 + 16 * c;
-    u32x4 v = {0u, 0u, 0u, 0u};
+    u32x4 w4 = {0u, 0u, 0u, 0u};
     uint32_t nibs = 0;
     if (row < N && kc < K) {                          // K % 16 == 0: the 16 columns are all in or all out
-      v = *reinterpret_cast<const u32x4*>(vals + row * (K / 2) + kc / 2);
+      const int64_t e = row * (K / 2) + kc / 2;       // the thread's eight compressed values
+      w4 = *reinterpret_cast<const u32x4*>(vals + e);
       nibs = meta[row * in_wpr + (kc >> 5)] >> (16 * (c & 1));
+      if constexpr (UPD) {
+        w4 = adamw8_bf16(w4, grads + e, m + e, v + e, hp);
+        *reinterpret_cast<u32x4*>(vals + e) = w4;
+      }
     }
     uint32_t d[8];                                    // 16 dense bf16, two per word
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t nib = (nibs >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
-      const uint32_t w = v[g], v0 = w & 0xFFFFu, v1 = w >> 16;
+      const uint32_t w = w4[g], v0 = w & 0xFFFFu, v1 = w >> 16;
       uint32_t e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = i1 == (uint32_t)j ? v1 : (i0 == (uint32_t)j ? v0 : 0u);
@@ -335,8 +350,9 @@ hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta
   if (N == 0 || K == 0) return hipSuccess;
   if (dt == Dt::BF16 && K % 16 == 0 && N % 16 == 0) {
     dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
-    double_prune_wide_kernel<<<g, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,
-                                                    meta_dpT, mask_dpT);
+    double_prune_wide_kernel<false, uint16_t><<<g, kThreads, 0, s>>>(
+        const_cast<uint16_t*>((const uint16_t*)values_s), meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT,
+        nullptr, nullptr, nullptr, AdamWStep{});
     return hipGetLastError();
   }
   dim3 grid((unsigned)cdiv(K, DP_TK), (unsigned)cdiv(N, DP_TN));
@@ -347,6 +363,28 @@ hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta
     double_prune_kernel<uint32_t><<<grid, kThreads, 0, s>>>((const uint32_t*)values_s, meta_s, N, K, (uint32_t*)values_dpT,
                                                             meta_dpT, mask_dpT);
   return hipGetLastError();
+}
+
+hipError_t launch_adamw_double_prune(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s, const void* grads,
+                                     float* m, float* v, int64_t N, int64_t K, const AdamWStep& c,
+                                     void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
+  if (N == 0 || K == 0) return hipSuccess;
+  if (dt == Dt::BF16 && K % 16 == 0 && N % 16 == 0) {
+    dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
+    if (grad == Dt::BF16)
+      double_prune_wide_kernel<true, uint16_t><<<g, kThreads, 0, s>>>((uint16_t*)values_s, meta_s, N, K,
+                                                                      (uint16_t*)values_dpT, meta_dpT, mask_dpT,
+                                                                      (const uint16_t*)grads, m, v, c);
+    else
+      double_prune_wide_kernel<true, float><<<g, kThreads, 0, s>>>((uint16_t*)values_s, meta_s, N, K,
+                                                                   (uint16_t*)values_dpT, meta_dpT, mask_dpT,
+                                                                   (const float*)grads, m, v, c);
+    return hipGetLastError();
+  }
+  // other shapes and fp32 weights: the elementwise update, then the double prune
+  hipError_t e = launch_adamw(dt, grad, values_s, grads, m, v, N * (K / 2), c, s);
+  if (e != hipSuccess) return e;
+  return launch_double_prune(dt, values_s, meta_s, N, K, values_dpT, meta_dpT, mask_dpT, s);
 }
 
 }  // namespace slope

@@ -4,6 +4,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle
 import sparse_gemm_02_amd as S
 
 DEV = "cuda:0"
@@ -86,3 +87,34 @@ class Compressed:
 def workspace(T, K, r, N):
     b = S.slope_lowrank_workspace_bytes(T, K, r, N)
     return torch.empty(max(b, 16), dtype=torch.uint8, device=DEV)
+
+
+def spacing(x, fmt):
+    """Distance between neighbouring representable values at |x| (bf16 or fp32)."""
+    mant = 8 if fmt == "bf16" else 24
+    tiny = -133 if fmt == "bf16" else -149
+    _, e = np.frexp(np.abs(np.asarray(x, np.float64)))
+    return np.ldexp(1.0, np.maximum(e - mant, tiny))
+
+
+def check_adamw_update(p0, g, m0, v0, step, hp, p_gpu, m_gpu, v_gpu):
+    """Stored values and moments against the oracle, within the derived bound."""
+    fmt = "bf16" if p0.dtype == np.uint16 else "f32"
+    p_ref, m_ref, v_ref = oracle.adamw_compressed(p0, g, m0, v0, step, **hp)
+    pe, me, ve = oracle.adamw_update(oracle.widen(p0), oracle.widen(g), m0, v0, step, **hp)
+    gw = oracle.widen(g)
+    b1, b2 = hp["beta1"], hp["beta2"]
+    step_size = hp["lr"] / (1 - b1 ** step)
+    den = np.sqrt(ve / (1 - b2 ** step)) + hp["eps"]
+    m_terms = b1 * np.abs(m0) + (1 - b1) * np.abs(gw)
+    v_terms = b2 * v0 + (1 - b2) * gw * gw
+    upd = step_size * np.abs(me) / den
+    err = 2.0 ** -20 * np.abs(oracle.widen(p0)) + 2.0 ** -18 * (upd + step_size * m_terms / den)
+    got, want = oracle.widen(p_gpu), oracle.widen(p_ref)
+    bound = spacing(np.maximum(np.abs(got), np.abs(want)), fmt) + err
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (np.flatnonzero(bad)[:5], got[bad][:5], want[bad][:5], pe[bad][:5])
+    if fmt == "bf16":       # the fp32 error is far below a bf16 spacing: nearly every value rounds alike
+        assert (p_gpu == p_ref).mean() >= 0.99
+    assert (np.abs(m_gpu.astype(np.float64) - m_ref) <= spacing(m_ref, "f32") + 2.0 ** -20 * m_terms).all()
+    assert (np.abs(v_gpu.astype(np.float64) - v_ref) <= spacing(v_ref, "f32") + 2.0 ** -20 * v_terms).all()

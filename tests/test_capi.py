@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -144,6 +144,38 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
+
+
+def test_adamw_argument_errors(lib):
+    bf, f32 = 1, 0
+    ok = S.AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    bad = [S.AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0),             # step counts from 1
+           S.AdamWParams(1e-3, 1.0, 0.999, 1e-8, 0.01, 1),             # beta1 outside [0, 1)
+           S.AdamWParams(1e-3, 0.9, -0.1, 1e-8, 0.01, 1),              # beta2 outside [0, 1)
+           S.AdamWParams(1e-3, 0.9, 0.999, -1.0, 0.01, 1),             # eps < 0
+           S.AdamWParams(float("nan"), 0.9, 0.999, 1e-8, 0.01, 1),     # lr not finite
+           S.AdamWParams(1e-3, 0.9, 0.999, 1e-8, float("inf"), 1),     # decay not finite
+           S.AdamWParams(1e-3, float("nan"), 0.999, 1e-8, 0.01, 1)]
+    for hp in bad:
+        assert lib.slope_adamw(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, ctypes.byref(hp), None) == -1
+        assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, ctypes.byref(hp), FAKE,
+                                            FAKE, None, None) == -1
+    assert lib.slope_adamw(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, None, None) == -1            # no hyper-parameters
+    assert lib.slope_adamw(7, bf, FAKE, FAKE, FAKE, FAKE, 64, ctypes.byref(ok), None) == -1
+    assert lib.slope_adamw(bf, bf, FAKE, FAKE, None, FAKE, 64, ctypes.byref(ok), None) == -1
+    assert lib.slope_adamw(bf, bf, FAKE, FAKE, FAKE, FAKE, -1, ctypes.byref(ok), None) == -1
+    assert lib.slope_adamw(bf, f32, FAKE, FAKE + 4, FAKE, FAKE, 64, ctypes.byref(ok), None) == -3
+    assert lib.slope_adamw(bf, bf, FAKE, FAKE, FAKE, FAKE, (1 << 40) + 1, ctypes.byref(ok), None) == -6
+    assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 66, 64, ctypes.byref(ok), FAKE, FAKE,
+                                        None, None) == -2
+    assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 62, ctypes.byref(ok), FAKE, FAKE,
+                                        None, None) == -2
+    assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, None, FAKE, FAKE, 64, 64, ctypes.byref(ok), FAKE, FAKE,
+                                        None, None) == -1
+    assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, ctypes.byref(ok), FAKE, FAKE,
+                                        FAKE + 1, None) == -3
+    assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 64, (1 << 22) + 4, ctypes.byref(ok),
+                                        FAKE, FAKE, None, None) == -6
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -14,7 +14,11 @@ spmm_fwd (+ adapter) -> spmm_bwd_dx -> masked_wgrad.  Then:
 * products: sampled token x feature blocks against the oracle (normwise 1e-2
   for bf16 outputs, 1e-5 for the fp32 workload); the weight gradient goes
   through the packed operands as the benchmark runs it, and so do the sparse
-  products (tile-chunk weights).
+  products (tile-chunk weights);
+* the weight update (AdamW on the compressed values fused with the double
+  prune): sampled rows of values and moments within the bound the optimizer
+  tests derive; sampled column groups of the new W_dp^T bit-exact against the
+  oracle's double prune of the values the GPU stored.
 """
 import numpy as np
 import pytest
@@ -22,9 +26,9 @@ import torch
 
 import oracle
 import sparse_gemm_02_amd as S
-from workloads import WORKLOADS, layer_inputs
+from workloads import WORKLOADS, layer_inputs, optimizer_inputs
 
-from gpu_util import TOL, Compressed, dev, host, host_f64, normwise, say, workspace
+from gpu_util import TOL, Compressed, check_adamw_update as _check_update, dev, host, host_f64, normwise, say, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -229,3 +233,54 @@ def test_adapter_backward_sampled(wl, idx):
     dL_ref = oracle.lowrank_bwd(np.ascontiguousarray(d["X"][:, ks]), d["dY"], np.ascontiguousarray(d["L"][ks]),
                                 d["R"])[1]
     assert normwise(host_f64(dL[ks]), dL_ref) <= tol
+
+
+UPDATE_HP = dict(lr=2e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+
+
+@pytest.mark.parametrize("wl,idx", CASES, ids=[f"{w}-{WORKLOADS[w].linears[i].name}" for w, i in CASES])
+def test_weight_update_sampled(wl, idx):
+    """AdamW on the compressed values fused with the double prune, at full size."""
+    w = WORKLOADS[wl]
+    lin = w.linears[idx]
+    N, K = lin.N, lin.K
+    say(f"[fullsize-update] {wl} {lin.name}: K={K} N={N} dtype={w.dtype}")
+    Wb = layer_inputs(K, N, w.T, w.r, w.dtype, seed=0, index=idx, which=("W",))["W"]
+    opt = optimizer_inputs(N, K, w.dtype, seed=0, index=idx)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Wd = dev(Wb)
+    mask = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    S.slope_prune24(Wd, mask)
+    c = Compressed(N, K, tdt)
+    S.slope_compress24(Wd, mask, c.values, c.meta)
+    del Wd, mask
+    G = dev(opt["G"])
+    M = torch.from_numpy(opt["M"]).to("cuda:0")
+    V = torch.from_numpy(opt["V"]).to("cuda:0")
+    dp = Compressed(K, N, tdt)
+    step = 11
+    S.slope_adamw_double_prune(c.values, c.meta, G, M, V, N, K, dp.values, dp.meta, step, **UPDATE_HP)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3000 + idx)
+    # sampled rows: the oracle's own compression of W, then its update
+    rows = _rows(rng, N, 16)
+    mask_ref, _ = oracle.prune24(Wb[rows])
+    v0, m_ref, _ = oracle.compress24(Wb[rows], mask_ref)
+    assert (host(c.meta[rows]) == m_ref).all()
+    _check_update(v0, opt["G"][rows], opt["M"][rows], opt["V"][rows], step, UPDATE_HP, host(c.values[rows]),
+                  M[rows].cpu().numpy(), V[rows].cpu().numpy())
+    # sampled column groups: all N rows of W_s for 4 columns
+    for c0 in _group_cols(rng, K, 4):
+        Wc = np.ascontiguousarray(Wb[:, c0:c0 + 4])
+        mc, _ = oracle.prune24(Wc)
+        vc, mcw, _ = oracle.compress24(Wc, mc)
+        sl = slice(c0 // 2, c0 // 2 + 2)
+        new_vc = host(c.values[:, sl])
+        _check_update(vc, opt["G"][:, sl], opt["M"][:, sl], opt["V"][:, sl], step, UPDATE_HP, new_vc,
+                      M[:, sl].cpu().numpy(), V[:, sl].cpu().numpy())
+        vdp_ref, mdp_ref, _ = oracle.double_prune(new_vc, mcw, N, 4)
+        assert (host(dp.values[c0:c0 + 4]) == vdp_ref).all(), c0
+        assert (host(dp.meta[c0:c0 + 4]) == mdp_ref).all(), c0
+    del c, dp, G, M, V
+    torch.cuda.empty_cache()
+

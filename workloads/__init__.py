@@ -22,6 +22,12 @@ float64 standard normals, scaled by the tensor's sigma, then cast to float32
 (round to nearest even) and, for bf16 workloads, rounded to bf16 (round to
 nearest even on the float32 bit pattern).  Tensors are returned as raw bit
 patterns: ``uint16`` for bf16 and ``uint32`` for fp32.
+
+Optimizer-step inputs of linear ``i`` (``optimizer_inputs``): a gradient in
+the compressed slot order G [N, K/2] ~ N(0, 1) in the workload's precision and
+two fp32 moment arrays M ~ N(0, 0.1) and V = Z^2 with Z ~ N(0, 0.1), from the
+children of ``SeedSequence([s, i, 1]).spawn(3)``, drawn with the same chunked
+recipe.
 """
 from __future__ import annotations
 
@@ -33,7 +39,7 @@ import numpy as np
 
 __all__ = [
     "Linear", "Workload", "WORKLOADS", "SIGMA", "CHUNK_ROWS",
-    "f32_to_bf16_bits", "bits_to_float32", "draw", "layer_inputs",
+    "f32_to_bf16_bits", "bits_to_float32", "draw", "layer_inputs", "optimizer_inputs",
 ]
 
 CHUNK_ROWS = 1024
@@ -147,3 +153,20 @@ def layer_inputs(K: int, N: int, T: int, r: int, dtype: str, seed: int = 0,
     shapes = {"W": (N, K), "X": (T, K), "dY": (T, N), "L": (K, r), "R": (r, N)}
     return {name: draw(kids[name], shapes[name], SIGMA[name], dtype, threads)
             for name in _ORDER if name in which}
+
+
+def optimizer_inputs(N: int, K: int, dtype: str, seed: int = 0, index: int = 0,
+                     threads: int | None = None) -> dict:
+    """Gradient (raw bits) and fp32 moments of one compressed [N, K/2] weight.
+
+    Returns {"G": bits [N, K/2], "M": float32 [N, K/2], "V": float32 [N, K/2]}.
+    """
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
+    kg, km, kv = np.random.SeedSequence([seed, index, 1]).spawn(3)
+    shape = (N, K // 2)
+    G = draw(kg, shape, 1.0, dtype, threads)
+    M = draw(km, shape, 0.1, "f32", threads).view(np.float32)
+    Z = draw(kv, shape, 0.1, "f32", threads).view(np.float32)
+    return {"G": G, "M": M, "V": Z * Z}
+
