@@ -1,0 +1,232 @@
+"""Training-side wrappers over the C ABI: a 2:4 sparse linear layer with an
+optional low-rank adapter, its autograd function, and AdamW on its compressed
+values.
+
+Orchestration only: every arithmetic step runs in libslope.so through the
+binding in this package (the forward product with the fused adapter term, the
+double-pruned dX product with the adapter's dX term, the weight gradient at the
+static mask, the adapter gradients, the optimizer step fused with the double
+prune, and the operand packing).  torch provides device memory, streams and
+the autograd graph.
+
+Layer state, per SLoPe (explainer 2.A and 2.B; discussion page, "Memory
+Footprint Reduction During Pretraining and Inference" and "Choice of
+Optimizer"):
+
+    values  [N, K/2] bf16   kept weights of W_s (an nn.Parameter; its .grad is
+                            the weight gradient in the same slot order)
+    meta    [N, K/32] int32 positions of the kept weights (static mask)
+    values_dpT, meta_dpT    the double-pruned transposed weight W_dp^T
+    packed_s, packed_dpT    tile-chunk copies of both for the GEMM kernels
+    L [K, r], R [r, N]      the adapter (nn.Parameters), when rank > 0
+
+Shapes: bf16 weights with K and N multiples of 16 (the packed operand format).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (slope_adamw, slope_adamw_double_prune, slope_compress24, slope_double_prune,
+               slope_lowrank_grads_packed, slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes,
+               slope_masked_wgrad_packed, slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes,
+               slope_packed_tokens_bytes, slope_prune24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed)
+
+__all__ = ["SparseLinear", "SparseAdamW", "training_state_bytes"]
+
+
+def _bytes(n, device):
+    return torch.empty(max(16, n), dtype=torch.uint8, device=device)
+
+
+class _SparseLinearFn(torch.autograd.Function):
+    """Y = X . W_s^T (+ (X . L) . R); gradients dX (through W_dp), dW at the
+    static mask, dL and dR."""
+
+    @staticmethod
+    def forward(ctx, X, values, L, R, layer):
+        T = X.shape[0]
+        N, K, r = layer.out_features, layer.in_features, layer.rank
+        Y = torch.empty((T, N), dtype=X.dtype, device=X.device)
+        ws = None
+        if r > 0:
+            ws = _bytes(slope_lowrank_workspace_bytes(T, K, r, N), X.device)
+            slope_spmm_fwd_packed(X, layer.packed_s, N, Y, L=L, R=R, workspace=ws)
+        else:
+            slope_spmm_fwd_packed(X, layer.packed_s, N, Y)
+        ctx.layer, ctx.ws = layer, ws
+        ctx.save_for_backward(X, L, R)
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, L, R = ctx.saved_tensors
+        layer = ctx.layer
+        dY = dY.contiguous()
+        T = X.shape[0]
+        N, K, r = layer.out_features, layer.in_features, layer.rank
+        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        need_a = r > 0 and (ctx.needs_input_grad[2] or ctx.needs_input_grad[3])
+        dX = dW = dL = dR = None
+        ws_bwd = None
+        if need_x:
+            dX = torch.empty((T, K), dtype=dY.dtype, device=dY.device)
+            if r > 0:
+                ws_bwd = _bytes(slope_lowrank_workspace_bytes(T, N, r, K), dY.device)
+                slope_spmm_bwd_dx_packed(dY, layer.packed_dpT, K, dX, L=L, R=R, workspace=ws_bwd)
+            else:
+                slope_spmm_bwd_dx_packed(dY, layer.packed_dpT, K, dX)
+        if need_w or need_a:
+            Xp = _bytes(slope_packed_tokens_bytes(T, K), X.device)
+            dYp = _bytes(slope_packed_tokens_bytes(T, N), X.device)
+            slope_pack_tokens(X, Xp)
+            slope_pack_tokens(dY, dYp)
+            if need_w:
+                dW = torch.empty_like(layer.values)
+                slope_masked_wgrad_packed(dYp, Xp, T, N, K, layer.meta, dW)
+            if need_a:
+                dL, dR = torch.empty_like(L), torch.empty_like(R)
+                wsg = _bytes(slope_lowrank_grads_workspace_bytes(T, K, r, N), X.device)
+                slope_lowrank_grads_packed(X, dY, Xp, dYp, L, R, wsg, dL, dR, fwd_workspace=ctx.ws,
+                                           bwd_workspace=ws_bwd)
+        ctx.ws = None
+        return dX, dW, dL, dR, None
+
+
+class SparseLinear(torch.nn.Module):
+    """2:4 sparse linear layer y = x . W_s^T (+ (x . L) . R), built from a dense
+    bf16 weight [out_features, in_features] on the GPU: magnitude 2:4 pruning
+    along the input dimension (the mask is fixed from then on), compression,
+    the double-pruned transposed copy and the packed operands."""
+
+    def __init__(self, weight: torch.Tensor, L: torch.Tensor | None = None, R: torch.Tensor | None = None):
+        super().__init__()
+        if weight.dtype != torch.bfloat16 or not weight.is_cuda or weight.dim() != 2:
+            raise ValueError("weight must be a 2-D bfloat16 GPU tensor [out_features, in_features]")
+        N, K = weight.shape
+        if K % 16 or N % 16:
+            raise ValueError("in_features and out_features must be multiples of 16")
+        if (L is None) != (R is None):
+            raise ValueError("give both adapter factors L [K, r] and R [r, N], or neither")
+        dev = weight.device
+        self.in_features, self.out_features = K, N
+        weight = weight.contiguous()
+        mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        slope_prune24(weight, mask)
+        values = torch.empty((N, K // 2), dtype=torch.bfloat16, device=dev)
+        meta = torch.empty((N, (K // 4 + 7) // 8), dtype=torch.int32, device=dev)
+        slope_compress24(weight, mask, values, meta)
+        del mask
+        self.values = torch.nn.Parameter(values)
+        self.register_buffer("meta", meta)
+        self.register_buffer("values_dpT", torch.empty((K, N // 2), dtype=torch.bfloat16, device=dev))
+        self.register_buffer("meta_dpT", torch.empty((K, (N // 4 + 7) // 8), dtype=torch.int32, device=dev))
+        self.register_buffer("packed_s", _bytes(slope_packed_sparse_bytes(N, K), dev))
+        self.register_buffer("packed_dpT", _bytes(slope_packed_sparse_bytes(K, N), dev))
+        if L is not None:
+            if L.shape[0] != K or R.shape[1] != N or L.shape[1] != R.shape[0]:
+                raise ValueError("adapter shapes must be L [K, r] and R [r, N]")
+            self.L = torch.nn.Parameter(L.detach().to(torch.bfloat16).contiguous())
+            self.R = torch.nn.Parameter(R.detach().to(torch.bfloat16).contiguous())
+            self.rank = L.shape[1]
+        else:
+            self.L = self.R = None
+            self.rank = 0
+        self.refresh()
+
+    @torch.no_grad()
+    def refresh(self) -> None:
+        """Re-derive W_dp^T and the packed operands from the current values
+        (needed after changing `values` by other means than SparseAdamW)."""
+        slope_double_prune(self.values, self.meta, self.out_features, self.in_features, self.values_dpT,
+                           self.meta_dpT)
+        self.repack()
+
+    @torch.no_grad()
+    def repack(self) -> None:
+        """Rewrite the tile-chunk operands from values / values_dpT."""
+        N, K = self.out_features, self.in_features
+        slope_pack_sparse(self.values, self.meta, N, K, self.packed_s)
+        slope_pack_sparse(self.values_dpT, self.meta_dpT, K, N, self.packed_dpT)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features or x.dtype != torch.bfloat16:
+            raise ValueError("input must be bfloat16 with in_features columns")
+        lead = x.shape[:-1]
+        y = _SparseLinearFn.apply(x.reshape(-1, self.in_features).contiguous(), self.values, self.L, self.R, self)
+        return y.reshape(*lead, self.out_features)
+
+
+class SparseAdamW(torch.optim.Optimizer):
+    """AdamW for SparseLinear layers (and any other bf16 / fp32 parameters).
+
+    The compressed values of each layer are updated by the fused kernel that
+    also re-derives the double-pruned transposed weight, after which the
+    layer's packed operands are rewritten; other parameters (the adapter
+    factors) take the elementwise kernel.  Moments are fp32, two per stored
+    value: the optimizer state of a 2:4 weight is half that of a dense one."""
+
+    def __init__(self, modules, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, extra_params=()):
+        modules = list(modules)
+        self._layer_of = {}
+        params = []
+        for m in modules:
+            for layer in (m.modules() if isinstance(m, torch.nn.Module) else [m]):
+                if isinstance(layer, SparseLinear):
+                    self._layer_of[layer.values] = layer
+        for m in modules:
+            params.extend(p for p in m.parameters() if p.requires_grad)
+        params.extend(extra_params)
+        seen, uniq = set(), []
+        for p in params:
+            if id(p) not in seen:
+                seen.add(id(p))
+                uniq.append(p)
+        super().__init__(uniq, dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay))
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = closure() if closure is not None else None
+        for group in self.param_groups:
+            b1, b2 = group["betas"]
+            hp = dict(lr=group["lr"], beta1=b1, beta2=b2, eps=group["eps"], weight_decay=group["weight_decay"])
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                st = self.state[p]
+                if not st:
+                    st["step"] = 0
+                    st["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                    st["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                st["step"] += 1
+                g = p.grad.contiguous()
+                layer = self._layer_of.get(p)
+                if layer is not None:
+                    slope_adamw_double_prune(p, layer.meta, g, st["exp_avg"], st["exp_avg_sq"], layer.out_features,
+                                             layer.in_features, layer.values_dpT, layer.meta_dpT, st["step"], **hp)
+                    layer.repack()
+                else:
+                    slope_adamw(p, g, st["exp_avg"], st["exp_avg_sq"], st["step"], **hp)
+        return loss
+
+
+def training_state_bytes(layer: SparseLinear, optimizer: SparseAdamW | None = None) -> dict:
+    """Bytes the layer's training state occupies on the GPU, next to a dense
+    bf16 layer of the same shape trained with AdamW (weight, gradient, two fp32
+    moments).  `canonical` counts what the pages' accounting counts (the
+    compressed weight and its double-pruned copy, the gradient at the kept
+    weights, two moments per kept weight; no separate binary mask is kept:
+    the metadata is the mask); `packed` adds the tile-chunk operand copies."""
+    def nb(t):
+        return 0 if t is None else t.numel() * t.element_size()
+    N, K = layer.out_features, layer.in_features
+    vals = layer.values
+    grad = vals.numel() * vals.element_size()
+    if optimizer is not None and vals in optimizer.state and optimizer.state[vals]:
+        moments = nb(optimizer.state[vals]["exp_avg"]) + nb(optimizer.state[vals]["exp_avg_sq"])
+    else:
+        moments = 2 * 4 * vals.numel()
+    canonical = nb(vals) + nb(layer.meta) + nb(layer.values_dpT) + nb(layer.meta_dpT) + grad + moments
+    dense = N * K * (2 + 2 + 4 + 4)
+    packed = canonical + nb(layer.packed_s) + nb(layer.packed_dpT)
+    return {"canonical": canonical, "with_packed_operands": packed, "dense_adamw": dense,
+            "canonical_ratio": canonical / dense, "with_packed_ratio": packed / dense}

@@ -183,3 +183,12 @@ def test_binding_refuses_host_tensors(lib):
     W = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.slope_prune24(W, torch.zeros(4, 8, dtype=torch.uint8))
+
+
+def test_layer_refuses_bad_weights():
+    import torch
+    from sparse_gemm_02_amd.layer import SparseLinear
+    with pytest.raises(ValueError):
+        SparseLinear(torch.zeros(32, 32, dtype=torch.bfloat16))          # host tensor
+    with pytest.raises(ValueError):
+        SparseLinear(torch.zeros(32, 32, dtype=torch.float32))           # not bf16
