@@ -31,6 +31,13 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Compiler-only fence (emits no instruction): no load, store or LDS access of
+// this wave is moved across it.  The waits and the barrier below are not
+// memory operations to the compiler, so a kernel whose loads must stay on one
+// side of them (register loads counted by a following wait_vmcnt, LDS reads
+// that must follow a barrier with nothing in between to pin them) places one.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
 template <int N>

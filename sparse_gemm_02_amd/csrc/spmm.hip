@@ -204,6 +204,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   for (int p = 0; p < G::NST; ++p) issue(p);
   wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 1)>();
   barrier();
+  compiler_fence();                                   // the first LDS reads stay after the barrier
   Frags f0, f1;
   read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {

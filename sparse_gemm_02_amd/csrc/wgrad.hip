@@ -221,6 +221,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
   for (int p = 0; p < G::NST; ++p) issue(p);
   wait_vmcnt<(G::X_DMA + G::D_DMA) * (G::NST - 1)>();
   barrier();
+  compiler_fence();                                        // the first LDS reads stay after the barrier
   Frags f0, f1;
   read_frags(f0, 0, 0);
   for (int s = 0; s < stages; ++s) {
@@ -247,8 +248,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
 // offset (c * Tch + s) * 8192 (Tch = ceil(T / 32)).  A chunk row is 64 bytes:
 // four 16-byte granules of 8 tokens, granule g stored at g ^ ((row >> 2) & 3) so
 // that MFMA fragment reads from LDS are free of bank conflicts.  Entries past T
-// or C are 0.  Each stage of the GEMM then loads one contiguous chunk per
-// operand, and fragments are plain 128-bit LDS reads.
+// or C are 0.  Each stage of the GEMM then takes one contiguous chunk per
+// operand, and every MFMA fragment is one 16-byte piece of a chunk row (a
+// plain 128-bit LDS read for X, a 128-bit load from memory for dY).
 constexpr int kChunkRows = 256, kChunkTokens = 32, kChunkElems = kChunkRows * kChunkTokens;
 
 __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint16_t* __restrict__ src, int T, int C,
@@ -284,28 +286,37 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint16_t* __rest
   }
 }
 
-template <int BK_, int BN_, int NST_, int WGK_, int WGN_>
-struct PGeo {
-  static constexpr int BK = BK_, BN = BN_;
-  static constexpr int WGK = WGK_, WGN = WGN_, WAVES = WGK * WGN, THREADS = 64 * WAVES;
-  static constexpr int WK = BK / WGK, WN = BN / WGN;
-  static constexpr int FK = WK / 32, FN = WN / 32;
-  static constexpr int NST = NST_;
-  static constexpr int CHUNK_BYTES = kChunkElems * 2;              // 16 KB per operand and stage
-  static constexpr int STAGE_BYTES = 2 * CHUNK_BYTES;
-  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
-  static constexpr int DMA = CHUNK_BYTES / 1024 / WAVES;           // loads per wave, operand and stage
-  static constexpr int DMA_PER_STAGE = 2 * DMA;
-  static_assert(BK == kChunkRows && BN == kChunkRows, "tiles are one chunk wide");
-  static_assert(CHUNK_BYTES % (1024 * WAVES) == 0, "chunk/wave split");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
 
 // dW^T tile [256 k][256 n] from packed X (xp) and dY (dp): a dense MFMA GEMM
-// over tokens, 32 per stage, through a ring of NST LDS stages filled by
-// buffer-to-LDS loads of whole chunks (same schedule as the sparse GEMM).
+// over tokens, 32 per stage.  X's chunk of each stage passes through a ring of
+// NST LDS stages filled by buffer-to-LDS loads (one barrier per stage, the
+// same schedule as the sparse GEMM); the dY operand goes straight from its
+// token chunks into registers, PD stages ahead of use, through a ring of
+// PD + 1 register sets (a wave's dY fragments are 16-byte pieces of its 64
+// chunk rows; past the last token chunk the loads read 0).  Compared with
+// staging both operands in LDS this halves the LDS fill traffic and cuts the
+// LDS fragment reads by a third.  Operands meet the MFMAs in the same
+// positions and order as in the token-major kernel, so results are identical.
+template <int NST_, int PD_>
+struct DGeo {
+  static constexpr int BK = 256, BN = 256, WGK = 2, WGN = 4, WAVES = 8, THREADS = 512;
+  static constexpr int WK = BK / WGK, WN = BN / WGN, FK = WK / 32, FN = WN / 32;
+  static constexpr int NST = NST_, PD = PD_, RING = PD_ + 1;
+  static constexpr int CHUNK_BYTES = kChunkElems * 2;
+  static constexpr int LDS_BYTES = NST * CHUNK_BYTES;
+  static constexpr int DMA = CHUNK_BYTES / 1024 / WAVES;           // X loads per wave and stage
+  static constexpr int DLOADS = 2 * FN;                            // dY loads per wave and stage
+  // outstanding vector-memory operations allowed when X's next stage must have landed:
+  // the later of the prologue's and the steady state's counts (both exact at their first use)
+  static constexpr int W1 = (DMA + DLOADS) * (NST - 2) + DLOADS;
+  static constexpr int W0 = DMA * (NST - 2) + DLOADS * PD;
+  static constexpr int XWAIT = W1 < W0 ? W1 : W0;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NST >= 2 && PD >= 1, "pipeline depth");
+};
+
 template <class G, typename O>
-__global__ __launch_bounds__(G::THREADS, 1) void wgrad_packed_kernel(const uint16_t* __restrict__ dp,
+__global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint16_t* __restrict__ dp,
                                                                    const uint16_t* __restrict__ xp, int T, int N,
                                                                    int K, const uint32_t* __restrict__ meta,
                                                                    O* __restrict__ dWv, O* __restrict__ dWd,
@@ -321,22 +332,18 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_packed_kernel(const uint1
   const int stages = (int)Tch;
   const uint16_t* const xs = xp + (int64_t)tk * Tch * kChunkElems;
   const uint16_t* const ds = dp + (int64_t)tn * Tch * kChunkElems;
-  const uint32_t src0 = (uint32_t)(wave * G::DMA * 1024);      // this wave's part of a chunk
+  const uint32_t src0 = (uint32_t)(wave * G::DMA * 1024);
   const uint32_t lane_off = (uint32_t)(lane * 16);
 
-  auto issue = [&](int s) {
-    char* base = lds + (s % G::NST) * G::STAGE_BYTES;
-    const bool live = s < stages;                   // past the end: empty resources read 0
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs + (int64_t)s * kChunkElems, live ? G::CHUNK_BYTES : 0);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(ds + (int64_t)s * kChunkElems, live ? G::CHUNK_BYTES : 0);
+  auto issue_x = [&](int s) {
+    char* base = lds + (s % G::NST) * G::CHUNK_BYTES;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xs + (int64_t)s * kChunkElems, s < stages ? G::CHUNK_BYTES : 0);
 #pragma unroll
     for (int j = 0; j < G::DMA; ++j) dma16(rx, base + src0 + j * 1024, src0 + j * 1024 + lane_off);
-#pragma unroll
-    for (int j = 0; j < G::DMA; ++j) dma16(rd, base + G::CHUNK_BYTES + src0 + j * 1024, src0 + j * 1024 + lane_off);
   };
 
-  // fragment offsets: row r, 16-token step ks uses granule 2*ks + lane/32
-  int x_off[2][G::FK], d_off[2][G::FN];
+  int x_off[2][G::FK];
+  uint32_t d_off[2][G::FN];
 #pragma unroll
   for (int a = 0; a < G::FK; ++a) {
     const int row = wk * G::WK + a * 32 + (lane & 31);
@@ -347,20 +354,26 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_packed_kernel(const uint1
   for (int b = 0; b < G::FN; ++b) {
     const int row = wn * G::WN + b * 32 + (lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      d_off[ks][b] = G::CHUNK_BYTES + row * 64 + (((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)) << 4);
+    for (int ks = 0; ks < 2; ++ks) d_off[ks][b] = (uint32_t)(row * 64 + (((2 * ks + (lane >> 5)) ^ ((row >> 2) & 3)) << 4));
   }
 
-  struct Frags {
-    bf16x8 x[G::FK];
-    bf16x8 d[G::FN];
+  struct DFrags {
+    bf16x8 d[2][G::FN];
   };
-  auto read_frags = [&](Frags& f, int s, int ks) {
-    const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
+  auto load_d = [&](DFrags& f, int s) {
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(ds + (int64_t)s * kChunkElems, s < stages ? G::CHUNK_BYTES : 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int b = 0; b < G::FN; ++b) f.d[ks][b] = __builtin_bit_cast(bf16x8, load16(rd, d_off[ks][b]));
+  };
+  struct XFrags {
+    bf16x8 x[G::FK];
+  };
+  auto read_x = [&](XFrags& f, int s, int ks) {
+    const char* base = lds + (s % G::NST) * G::CHUNK_BYTES;
 #pragma unroll
     for (int a = 0; a < G::FK; ++a) f.x[a] = *reinterpret_cast<const bf16x8*>(base + x_off[ks][a]);
-#pragma unroll
-    for (int b = 0; b < G::FN; ++b) f.d[b] = *reinterpret_cast<const bf16x8*>(base + d_off[ks][b]);
   };
 
   f32x16 acc[G::FK][G::FN];
@@ -368,37 +381,55 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_packed_kernel(const uint1
   for (int a = 0; a < G::FK; ++a)
 #pragma unroll
     for (int b = 0; b < G::FN; ++b) acc[a][b] = f32x16{};
-  auto mma = [&](const Frags& f) {
+  auto mma = [&](const XFrags& f, const DFrags& d, int ks) {
 #pragma unroll
     for (int b = 0; b < G::FN; ++b)
 #pragma unroll
       for (int a = 0; a < G::FK; ++a)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], f.d[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], d.d[ks][b], acc[a][b], 0, 0, 0);
   };
 
+  DFrags ring[G::RING];
 #pragma unroll
-  for (int p = 0; p < G::NST; ++p) issue(p);
-  wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 1)>();
+  for (int p = 0; p < G::NST; ++p) issue_x(p);
+#pragma unroll
+  for (int p = 0; p < G::PD; ++p) load_d(ring[p], p);
+  compiler_fence();                                              // the loads above are counted by the wait
+  wait_vmcnt<G::DMA * (G::NST - 1) + G::DLOADS * G::PD>();     // X's stage 0 landed (this wave's part)
   barrier();
-  Frags f0, f1;
-  read_frags(f0, 0, 0);
-  for (int s = 0; s < stages; ++s) {
-    read_frags(f1, s, 1);
-    mma(f0);
-    __builtin_amdgcn_sched_barrier(0);                 // MFMAs stay ahead of the waits
-    wait_lgkmcnt0();                                   // this wave's reads of stage s are in registers
-    wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();    // stage s+1 landed (this wave's part)
-    barrier();                                         // everyone's part; stage s fully read
-    issue(s + G::NST);                                 // refill stage s's slot
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < stages) read_frags(f0, s + 1, 0);
-    mma(f1);
-  }
+  compiler_fence();                                              // the first LDS reads stay after the barrier
+  XFrags x0, x1;
+  read_x(x0, 0, 0);
+  // whole groups of RING stages, at least one (the ring index stays static, no
+  // early exit leaves the compiler's wait counting pessimistic, and no branch
+  // around the loop lets the prologue's loads sink past its wait); stages past
+  // the last token chunk read zeros and add nothing
+  const int stages_pad = stages <= G::RING ? G::RING : (stages + G::RING - 1) / G::RING * G::RING;
+  int s0 = 0;
+  do {
+#pragma unroll
+    for (int u = 0; u < G::RING; ++u) {
+      const int s = s0 + u;
+      read_x(x1, s, 1);                                  // issued ahead of the MFMAs they overlap
+      __builtin_amdgcn_sched_barrier(0);
+      mma(x0, ring[u], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();                                   // this wave's reads of stage s are in registers
+      wait_vmcnt<G::XWAIT>();                            // X's stage s+1 landed (this wave's part)
+      barrier();                                         // everyone's part; stage s fully read
+      issue_x(s + G::NST);
+      load_d(ring[(u + G::PD) % G::RING], s + G::PD);    // the set consumed one stage ago
+      read_x(x0, s + 1, 0);
+      mma(x1, ring[u], 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s0 += G::RING;
+  } while (s0 < stages_pad);
   wait_vmcnt<0>();
   wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
 }
 
-typedef PGeo<256, 256, 4, 2, 4> PGeoBig;
+typedef DGeo<4, 3> DGeoBig;
 
 int64_t chunks_of(int64_t C) { return (C + kChunkRows - 1) / kChunkRows; }
 int64_t token_chunks(int64_t T) { return (T + kChunkTokens - 1) / kChunkTokens; }
@@ -414,8 +445,8 @@ hipError_t launch_pack(const uint16_t* src, int64_t T, int64_t C, uint16_t* dst,
 template <typename O>
 hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int64_t N, int64_t K,
                          const uint32_t* meta, O* dWv, O* dWd, int accumulate, hipStream_t s) {
-  typedef PGeoBig G;
-  auto kern = wgrad_packed_kernel<G, O>;
+  typedef DGeoBig G;
+  auto kern = wgrad_direct_kernel<G, O>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const int64_t nb = chunks_of(K) * chunks_of(N);

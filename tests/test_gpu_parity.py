@@ -470,7 +470,8 @@ def test_masked_wgrad(T, N, K, out_dt, packed):
     assert normwise(host_f64(acc), v_ref + host_f64(base)) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("T,N,K", [(300, 520, 272), (257, 264, 520), (1, 64, 128), (2048, 512, 768)])
+@pytest.mark.parametrize("T,N,K", [(300, 520, 272), (257, 264, 520), (1, 64, 128), (2048, 512, 768), (32, 8, 1032),
+                                   (64, 256, 1032), (97, 264, 776)])
 def test_masked_wgrad_packed_matches_direct(T, N, K):
     """Both kernels feed the same operands to the same MFMA positions in the
     same token order, so with and without the workspace results are bitwise equal."""
