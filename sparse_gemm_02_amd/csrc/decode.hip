@@ -128,52 +128,93 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
 
 // Y[t][n] = sum over the splits (in order) of part + sum_j xl[t][j] R[j][n],
 // rounded once, with xl = xlh + xll (X . L as a bf16 hi/lo pair, prepared by
-// the adapter's down-projection).  Thread n, four tokens (blockIdx.y picks
-// which); R is read in its own [r, N] layout, consecutive n across lanes,
-// eight rank rows at a time so that the loads overlap.
-template <typename O>
+// the adapter's down-projection; their fp32 sum is exact).  A block covers 64
+// consecutive n (one per lane) and TB tokens; its four waves split the work
+// into quarters (wave w: the w-th quarter of the splits, in order, and the
+// w-th quarter of the rank rows), each wave issuing a batch of Q loads before
+// using them, and the four partial sums are added in wave order through LDS
+// (deterministic).  The block's xl rows are staged in LDS once and read as
+// broadcasts; R is read in its own [r, N] layout.
+constexpr int kReduceMaxRank = 128;
+
+template <typename O, int TB, int Q>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part, int splits, int T,
                                                             int64_t N, int64_t Npad, const uint16_t* __restrict__ R,
                                                             const uint16_t* __restrict__ xlh,
                                                             const uint16_t* __restrict__ xll, int r, int rpad,
                                                             O* __restrict__ Y) {
-  constexpr int TB = 4;
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float xl[TB][kReduceMaxRank];
+  __shared__ float sum[4][TB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + lane;
+  const bool col = n < N;
   const int tb = blockIdx.y * TB;
-  if (n >= N) return;
+  if (R) {
+    for (int e = threadIdx.x; e < TB * rpad; e += 256) {
+      const int i = e / rpad, j = e % rpad;
+      xl[i][j] = tb + i < T ? bf16_bits_to_f32(xlh[(tb + i) * rpad + j]) + bf16_bits_to_f32(xll[(tb + i) * rpad + j])
+                           : 0.f;
+    }
+  }
   float y[TB];
 #pragma unroll
   for (int i = 0; i < TB; ++i) y[i] = 0.f;
-#pragma unroll 4
-  for (int sp = 0; sp < splits; ++sp)
+  // the wave's quarter of the splits, Q at a time
+  const int sq = (splits + 3) / 4, sp0 = wave * sq, sp1 = sp0 + sq < splits ? sp0 + sq : splits;
+  for (int c0 = sp0; c0 < sp1; c0 += Q) {
+    float v[Q][TB];
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
-      if (tb + i < T) y[i] += part[((int64_t)sp * T + tb + i) * Npad + n];
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+        v[q][i] = (col && c0 + q < sp1 && tb + i < T) ? part[((int64_t)(c0 + q) * T + tb + i) * Npad + n] : 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < TB; ++i) y[i] += v[q][i];
+  }
+  __syncthreads();                                 // xl staged
   if (R) {
-    float a[TB];
+    // the wave's quarter of the (zero-padded) rank rows
+    const int rq = rpad / 4, j0 = wave * rq;
+    for (int c0 = j0; c0 < j0 + rq; c0 += 4 * Q) {
+      float rv[4 * Q];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) a[i] = 0.f;
-    for (int j0 = 0; j0 < rpad; j0 += 8) {          // xlh / xll are zero past r
-      float rv[8];
+      for (int q = 0; q < 4 * Q; ++q) {
+        const int j = c0 + q;
+        rv[q] = (col && j < j0 + rq && j < r) ? bf16_bits_to_f32(R[(int64_t)j * N + n]) : 0.f;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rv[e] = j0 + e < r ? bf16_bits_to_f32(R[(int64_t)(j0 + e) * N + n]) : 0.f;
+      for (int q = 0; q < 4 * Q; ++q) {
+        if (c0 + q >= j0 + rq) break;
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        if (tb + i >= T) continue;
-        const int x = (tb + i) * rpad + j0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[i] += rv[e] * bf16_bits_to_f32(xlh[x + e]);
-          a[i] += rv[e] * bf16_bits_to_f32(xll[x + e]);
-        }
+        for (int i = 0; i < TB; ++i) y[i] += rv[q] * xl[i][c0 + q];
       }
     }
-#pragma unroll
-    for (int i = 0; i < TB; ++i) y[i] += a[i];
   }
 #pragma unroll
-  for (int i = 0; i < TB; ++i)
-    if (tb + i < T) store_out(Y + (tb + i) * N + n, y[i]);
+  for (int i = 0; i < TB; ++i) sum[wave][i][lane] = y[i];
+  __syncthreads();
+  if (wave == 0 && col) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      if (tb + i >= T) continue;
+      const float out = ((sum[0][i][lane] + sum[1][i][lane]) + sum[2][i][lane]) + sum[3][i][lane];
+      store_out(Y + (tb + i) * N + n, out);
+    }
+  }
+}
+
+template <typename O>
+void launch_decode_reduce(const float* part, int splits, int64_t T, int64_t N, int64_t Npad, const uint16_t* R,
+                          const uint16_t* xh, const uint16_t* xo, int r, int rpad, O* Y, hipStream_t s) {
+  if (T <= 4) {
+    dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 4));
+    decode_reduce_kernel<O, 4, 16><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
+  } else {
+    dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 16));
+    decode_reduce_kernel<O, 16, 4><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
+  }
 }
 
 struct DecodePlan {
@@ -226,20 +267,18 @@ hipError_t launch_spmm_decode(Dt out, const void* X, int64_t T, int64_t K, const
   else
     decode_partial_kernel<2><<<grid, 256, 0, s>>>((const uint16_t*)X, (const char*)packed, (int)T, (int)K, p.stages,
                                                   p.kc, p.Npad, part);
-  dim3 rgrid((unsigned)cdiv(N, 256), (unsigned)cdiv(T, 4));
   const uint16_t* Ra = ad ? (const uint16_t*)R : nullptr;
   const uint16_t* xh = ad ? w.xlh : nullptr;
   const uint16_t* xo = ad ? w.xll : nullptr;
   const int rp = ad ? (int)w.rpad : 0;
   if (out == Dt::BF16)
-    decode_reduce_kernel<uint16_t><<<rgrid, 256, 0, s>>>(part, p.splits, (int)T, N, p.Npad, Ra, xh, xo, (int)r, rp,
-                                                         (uint16_t*)Y);
+    launch_decode_reduce(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (uint16_t*)Y, s);
   else
-    decode_reduce_kernel<float><<<rgrid, 256, 0, s>>>(part, p.splits, (int)T, N, p.Npad, Ra, xh, xo, (int)r, rp,
-                                                      (float*)Y);
+    launch_decode_reduce(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (float*)Y, s);
   return hipGetLastError();
 }
 
 static_assert(kDecodeMaxT == 64, "two 32-token tiles at most");
+static_assert(kReduceMaxRank >= 128, "adapter ranks up to 128 (rank rows padded to 16)");
 
 }  // namespace slope
