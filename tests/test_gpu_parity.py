@@ -321,10 +321,27 @@ def test_spmm_fwd_decode(T, N, K, adapter, out_dt):
             assert err <= 2e-5 * max(1.0, np.sqrt(K / 256)), err
 
 
-def test_spmm_fwd_decode_integer_exact():
+@pytest.mark.parametrize("T,N,K,r", [(1, 256, 9216, 72), (4, 520, 1040, 128), (2, 64, 131072, 33), (1, 64, 16, 1),
+                                     (3, 272, 4112, 17)])
+def test_spmm_fwd_decode_adapter_ranks(T, N, K, r):
+    """Few tokens with the adapter: ranks up to 128, long reductions, ragged sizes."""
+    say(f"spmm_fwd_decode adapter T={T} N={N} K={K} r={r}")
+    d = _layer(T, N, K, r, "bf16", seed=5 * T + N + K + r)
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    ws = torch.empty(S.slope_decode_workspace_bytes(T, K, r, N), dtype=torch.uint8, device="cuda")
+    Y = empty((T, N), torch.float32)
+    S.slope_spmm_fwd_decode(dev(d["X"]), ps, N, Y, ws, L=dev(d["L"]), R=dev(d["R"]))
+    torch.cuda.synchronize()
+    ref = oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"])
+    assert normwise(host_f64(Y), ref) <= 2e-5 * max(1.0, np.sqrt(K / 256))
+
+
+@pytest.mark.parametrize("T", [3, 7])
+def test_spmm_fwd_decode_integer_exact(T):
     """Integer inputs: every partial sum is exact, so fp32 output equals the oracle."""
-    T, N, K, r = 7, 520, 1040, 4
-    say("decode integer probe")
+    N, K, r = 520, 1040, 4
+    say(f"decode integer probe T={T}")
     d = _layer(T, N, K, r, "bf16", seed=23, ints=True)
     ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
     S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
