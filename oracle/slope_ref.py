@@ -27,8 +27,8 @@ Conventions (W is [N, K] = [out, in] as for a linear layer):
     AdamW on the compressed values of W_s (moments only for the kept slots),
     then the double prune of the updated W_s
 
-Tensors arrive as raw bit patterns (uint16 = bf16, uint32 = fp32), so every
-selection is made on the exact stored values.  Products and sums are done in
+Tensors arrive as raw bit patterns (uint16 = bf16, uint32 = fp32) or as numpy
+float16 arrays (fp16), so every selection is made on the exact stored values.  Products and sums are done in
 float64 on the exactly widened inputs and returned unrounded.
 
 Readings where the pages leave a step open (each is listed with its reason in
@@ -51,7 +51,7 @@ import numpy as np
 __all__ = [
     "widen", "prune24", "compress24", "decompress24", "mask_from_meta",
     "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add", "lowrank_bwd",
-    "round_bf16", "round_f32", "adamw_update", "adamw_compressed", "adamw_double_prune",
+    "round_bf16", "round_f16", "round_f32", "adamw_update", "adamw_compressed", "adamw_double_prune",
     "storage_accounting", "LEGAL_NIBBLES",
 ]
 
@@ -62,14 +62,17 @@ LEGAL_NIBBLES = frozenset(i0 | (i1 << 2) for i0 in range(4) for i1 in range(i0 +
 # --------------------------------------------------------------------------- values
 
 def widen(bits: np.ndarray) -> np.ndarray:
-    """Exact float64 values of raw bf16 (uint16) or fp32 (uint32) bit patterns."""
+    """Exact float64 values of raw bf16 (uint16) or fp32 (uint32) bit patterns,
+    or of fp16 values (numpy float16 arrays)."""
     bits = np.asarray(bits)
     if bits.dtype == np.uint16:
         f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
     elif bits.dtype == np.uint32:
         f32 = bits.view(np.float32)
+    elif bits.dtype == np.float16:
+        return bits.astype(np.float64)
     else:
-        raise TypeError(f"raw bits must be uint16 (bf16) or uint32 (fp32), got {bits.dtype}")
+        raise TypeError(f"raw bits must be uint16 (bf16), uint32 (fp32) or float16, got {bits.dtype}")
     return f32.astype(np.float64)
 
 
@@ -305,6 +308,13 @@ def round_bf16(x) -> np.ndarray:
     return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def round_f16(x) -> np.ndarray:
+    """fp16 values nearest to float64 values, ties to even (one rounding,
+    straight from float64; past the largest finite fp16 an infinity)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
 def round_f32(x) -> np.ndarray:
     """fp32 values nearest to float64 values, ties to even (IEEE conversion)."""
     with np.errstate(over="ignore"):
@@ -342,8 +352,8 @@ def adamw_compressed(values, grads, m, v, step, **hp):
     Pretraining and Inference"): the update runs on the compressed values, the
     pruned positions have no state and stay zero, the mask does not move.
 
-    values: raw bits of the compressed values (uint16 bf16 or uint32 fp32);
-    grads: raw bits of the gradient in the same slot order (bf16 or fp32);
+    values: the compressed values (uint16 bf16 bits, float16, or uint32 fp32
+    bits); grads: the gradient in the same slot order (any of those formats);
     m, v: float32 moments of the same shape.  The step is computed in float64
     and stored once: values rounded to their own format, moments to fp32.
     Returns (values bits, m float32, v float32).
@@ -351,7 +361,12 @@ def adamw_compressed(values, grads, m, v, step, **hp):
     values = np.asarray(values)
     p, m1, v1 = adamw_update(widen(values), widen(grads), np.asarray(m, np.float32),
                              np.asarray(v, np.float32), step, **hp)
-    out = round_bf16(p) if values.dtype == np.uint16 else round_f32(p).view(np.uint32)
+    if values.dtype == np.uint16:
+        out = round_bf16(p)
+    elif values.dtype == np.float16:
+        out = round_f16(p)
+    else:
+        out = round_f32(p).view(np.uint32)
     return out, round_f32(m1), round_f32(v1)
 
 

@@ -54,6 +54,28 @@ def test_round_bf16_is_nearest_ties_to_even():
         assert ((b[tie] & 1) == 0).all()                          # ties go to the even pattern
 
 
+def test_round_f16_is_nearest_ties_to_even():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.normal(size=20000) * 100,
+                        rng.normal(size=4000) * 2.0 ** rng.integers(-30, -14, size=4000),   # subnormal range
+                        # exact midpoints between neighbouring fp16 values
+                        (rng.integers(-2 ** 10, 2 ** 10, size=4000) * 2 + 1) * 2.0 ** rng.integers(-20, 4, size=4000)
+                        * 2.0 ** -11])
+    h = oracle.round_f16(x)
+    assert h.dtype == np.float16 and np.isfinite(h).all()
+    b = h.view(np.uint16).astype(np.int32)
+    for step in (-1, 1):                                   # neighbours by bit pattern (same sign)
+        nb = b + step
+        ok = ((nb & 0x7FFF) < 0x7C00) & (nb >= 0) & ((nb & 0x7FFF) != 0x7FFF)
+        alt = nb[ok].astype(np.uint16).view(np.float16).astype(np.float64)
+        err, d = np.abs(x[ok] - h[ok].astype(np.float64)), np.abs(x[ok] - alt)
+        assert (err <= d).all()
+        tie = (err == d) & (err > 0)
+        assert ((b[ok][tie] & 1) == 0).all()
+    zero_cross = (b & 0x7FFF) == 0                          # nearest across zero: the other sign's smallest
+    assert (np.abs(x[zero_cross]) <= 2.0 ** -25).all()
+
+
 def test_round_bf16_exact_values_and_specials():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = oracle.widen(bits)
@@ -100,18 +122,18 @@ def test_adamw_first_step_closed_form():
     np.testing.assert_allclose(p2, p * (1 - lr * wd), rtol=1e-15)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_adamw_compressed_sign_descent_is_exact(dt):
     # beta1 = beta2 = 0, eps = 0, no decay: the step is p - lr * sign(g), m = g, v = g^2, all exact
     rng = np.random.default_rng(14)
     pv = rng.integers(-40, 41, size=(6, 8)).astype(np.float32) / 16
     gv = rng.integers(1, 9, size=(6, 8)).astype(np.float32) * rng.choice([-1.0, 1.0], size=(6, 8)).astype(np.float32)
-    enc = (lambda a: f32_to_bf16_bits(a)) if dt == "bf16" else (lambda a: a.view(np.uint32))
+    enc = {"bf16": f32_to_bf16_bits, "f16": lambda a: a.astype(np.float16), "f32": lambda a: a.view(np.uint32)}[dt]
     m0 = rng.normal(size=(6, 8)).astype(np.float32)                   # ignored when beta1 = 0
     v0 = np.abs(rng.normal(size=(6, 8))).astype(np.float32)
     vals, m1, v1 = oracle.adamw_compressed(enc(pv), enc(gv), m0, v0, 3, lr=0.25, beta1=0.0, beta2=0.0, eps=0.0,
                                            weight_decay=0.0)
-    assert vals.dtype == (np.uint16 if dt == "bf16" else np.uint32)
+    assert vals.dtype == {"bf16": np.uint16, "f16": np.float16, "f32": np.uint32}[dt]
     assert np.array_equal(oracle.widen(vals), pv - 0.25 * np.sign(gv))
     assert m1.dtype == np.float32 and np.array_equal(m1, gv)
     assert v1.dtype == np.float32 and np.array_equal(v1, gv * gv)

@@ -37,10 +37,12 @@ def _all_groups(alphabet):
 
 def _bits(vals, dtype):
     f = np.asarray(vals, dtype=np.float32)
+    if dtype == "f16":
+        return f.astype(np.float16)
     return f32_to_bf16_bits(f) if dtype == "bf16" else f.view(np.uint32).copy()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_exhaustive_small_alphabet_with_ties(dtype):
     # +0, -0 and +-1, +-2, +-3: 8^4 = 4096 groups, ties and signed zeros everywhere.
     alphabet = [0.0, -0.0, 1.0, -1.0, 2.0, -2.0, 3.0, -3.0]
@@ -79,13 +81,25 @@ def test_exhaustive_special_values_bf16():
         assert set(np.flatnonzero(mask[g])) == {a, b}
 
 
+def test_exhaustive_special_values_f16():
+    # fp16 subnormals 0x0001 and 0x8002, inf, -inf, NaN, 1, -max (65504)
+    pats = [0x0000, 0x0001, 0x8002, 0x7C00, 0xFC00, 0x7E00, 0x3C00, 0xFBFF]
+    groups = _all_groups(pats).astype(np.uint16).view(np.float16)
+    mask, _ = oracle.prune24(groups)
+    vals = oracle.widen(groups)
+    assert vals[1, 3] == 2.0 ** -24 and np.isnan(vals[5 * 8 ** 3, 0]) and vals[7 * 8 ** 3, 0] == -65504.0
+    for g in range(groups.shape[0]):
+        a, b = pair_enumerator(vals[g])
+        assert set(np.flatnonzero(mask[g])) == {a, b}
+
+
 def test_nan_payloads_tie_and_go_to_lower_index():
     g = np.array([[0x7FC1, 0x7FFF, 0x7FC0, 0x3F80]], dtype=np.uint16)
     mask, _ = oracle.prune24(g)
     assert mask.tolist() == [[1, 1, 0, 0]]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_invariants_random(dtype):
     rng = np.random.default_rng(7)
     v = (rng.standard_normal((64, 128)) * 0.02).astype(np.float32)

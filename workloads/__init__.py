@@ -20,8 +20,9 @@ the order W, X, dY, L, R.  A tensor is drawn in row chunks of ``CHUNK_ROWS``
 rows; chunk ``c`` uses ``default_rng(child.spawn(n_chunks)[c])`` and draws
 float64 standard normals, scaled by the tensor's sigma, then cast to float32
 (round to nearest even) and, for bf16 workloads, rounded to bf16 (round to
-nearest even on the float32 bit pattern).  Tensors are returned as raw bit
-patterns: ``uint16`` for bf16 and ``uint32`` for fp32.
+nearest even on the float32 bit pattern), for fp16 ones to fp16 (numpy's
+conversion, nearest even).  Tensors are returned as raw bit patterns:
+``uint16`` for bf16 and ``uint32`` for fp32; fp16 tensors as numpy ``float16``.
 
 Optimizer-step inputs of linear ``i`` (``optimizer_inputs``): a gradient in
 the compressed slot order G [N, K/2] ~ N(0, 1) in the workload's precision and
@@ -105,11 +106,16 @@ def bits_to_float32(bits: np.ndarray) -> np.ndarray:
     raise TypeError(f"expected uint16 or uint32 bits, got {bits.dtype}")
 
 
+_STORE = {"bf16": np.uint16, "f16": np.float16, "f32": np.uint32}
+
+
 def _draw_chunk(seed_seq, rows, cols, sigma, dtype):
     g = np.random.default_rng(seed_seq)
     v = (g.standard_normal((rows, cols)) * sigma).astype(np.float32)
     if dtype == "bf16":
         return f32_to_bf16_bits(v)
+    if dtype == "f16":
+        return v.astype(np.float16)
     return v.view(np.uint32).copy()
 
 
@@ -123,7 +129,7 @@ def draw(seed_seq: np.random.SeedSequence, shape, sigma: float, dtype: str,
     base = tuple(seed_seq.spawn_key)
     kids = [np.random.SeedSequence(seed_seq.entropy, spawn_key=base + (c,),
                                    pool_size=seed_seq.pool_size) for c in range(n_chunks)]
-    out = np.empty((rows, cols), dtype=np.uint16 if dtype == "bf16" else np.uint32)
+    out = np.empty((rows, cols), dtype=_STORE[dtype])
     spans = [(c * CHUNK_ROWS, min(rows, (c + 1) * CHUNK_ROWS)) for c in range(n_chunks)]
 
     def work(c):
@@ -147,7 +153,7 @@ def layer_inputs(K: int, N: int, T: int, r: int, dtype: str, seed: int = 0,
     ``which`` restricts the tensors drawn (the others are not generated); the
     draws of a tensor do not depend on which others are requested.
     """
-    if dtype not in ("bf16", "f32"):
+    if dtype not in _STORE:
         raise ValueError(dtype)
     kids = dict(zip(_ORDER, np.random.SeedSequence([seed, index]).spawn(len(_ORDER))))
     shapes = {"W": (N, K), "X": (T, K), "dY": (T, N), "L": (K, r), "R": (r, N)}
@@ -161,7 +167,7 @@ def optimizer_inputs(N: int, K: int, dtype: str, seed: int = 0, index: int = 0,
 
     Returns {"G": bits [N, K/2], "M": float32 [N, K/2], "V": float32 [N, K/2]}.
     """
-    if dtype not in ("bf16", "f32"):
+    if dtype not in _STORE:
         raise ValueError(dtype)
     kg, km, kv = np.random.SeedSequence([seed, index, 1]).spawn(3)
     shape = (N, K // 2)
