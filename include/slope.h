@@ -17,9 +17,13 @@
  *   dX    = dY . W_dp
  *   dW    = (dY^T . X) kept at W_s's mask
  *
- * Data types.  SLOPE_BF16 tensors hold raw bfloat16 values, SLOPE_F32 raw
- * float32 values.  Products accumulate in float32; bf16 outputs are rounded
- * to nearest even once, at the end.  An F32-input call must use F32 outputs.
+ * Data types.  SLOPE_BF16 tensors hold raw bfloat16 values, SLOPE_F16 raw
+ * IEEE binary16 values, SLOPE_F32 raw float32 values.  Products accumulate in
+ * float32; 16-bit outputs are rounded to nearest even once, at the end.  A
+ * call's outputs are in its input format or float32 (an F32-input call uses
+ * F32 outputs).  The tile-chunk, token-chunk and few-token entry points take
+ * the two 16-bit formats; the fp16 adapter keeps X . L as an fp16 hi/lo pair,
+ * so |X . L| must stay below the fp16 range (65504).
  *
  * Selection rule (prune24, double_prune): within a group of four, the two
  * largest magnitudes are kept; equal magnitudes (including +0/-0 and x/-x) go
@@ -56,7 +60,7 @@
 extern "C" {
 #endif
 
-typedef enum { SLOPE_F32 = 0, SLOPE_BF16 = 1 } slope_dtype;
+typedef enum { SLOPE_F32 = 0, SLOPE_BF16 = 1, SLOPE_F16 = 2 } slope_dtype;
 
 typedef enum {
   SLOPE_OK = 0,
@@ -84,13 +88,13 @@ slope_status slope_compressed_sizes(int64_t rows, int64_t cols, int64_t* n_value
 
 /* Bytes of device workspace the low-rank adapter needs for T tokens, input
  * width K, rank r and output width N: the split partial sums of X . L
- * (float32), X . L as bf16 hi + lo parts, and transposed copies of L and R.
+ * (float32), X . L as 16-bit hi + lo parts, and transposed copies of L and R.
  * Host-only; 0 when T == 0 or r == 0. */
 slope_status slope_lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
 
 /* Bytes of device workspace slope_masked_wgrad can use for T tokens, N
  * outputs and K inputs: X and dY rewritten, transposed, into 256-column x
- * 32-token chunks (bf16, zero padded; see slope_pack_tokens), X's first.
+ * 32-token chunks (16-bit, zero padded; see slope_pack_tokens), X's first.
  * Host-only. */
 slope_status slope_wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes);
 
@@ -165,7 +169,7 @@ slope_status slope_spmm_bwd_dx(slope_dtype in_dt, slope_dtype out_dt, const void
  *   accumulate != 0: add to the existing contents instead of overwriting
  *   workspace: NULL, or device memory (16-byte aligned) of at least
  *             slope_wgrad_workspace_bytes(T, N, K) bytes, owned by the caller
- *             and overwritten; with it the bf16 path packs both operands
+ *             and overwritten; with it the 16-bit path packs both operands
  *             first and runs faster.  Results are identical either way.
  * Errors: SLOPE_ERR_SHAPE if K % 4 != 0; SLOPE_ERR_WORKSPACE if a workspace
  * is given and is short. */
@@ -174,12 +178,12 @@ slope_status slope_masked_wgrad(slope_dtype in_dt, slope_dtype out_dt, const voi
                                 void* dW_dense_or_null, int accumulate, void* workspace_or_null,
                                 int64_t workspace_bytes, void* stream);
 
-/* Bytes of the tile-chunk form of a compressed bf16 matrix [rows, cols] (see
+/* Bytes of the tile-chunk form of a compressed 16-bit matrix [rows, cols] (see
  * slope_pack_sparse).  Host-only; SLOPE_ERR_SHAPE if cols % 16 != 0,
  * SLOPE_ERR_UNSUPPORTED if cols > 2^21. */
 slope_status slope_packed_sparse_bytes(int64_t rows, int64_t cols, int64_t* bytes);
 
-/* Tile-chunk copy of a compressed bf16 matrix (values [rows, cols/2],
+/* Tile-chunk copy of a compressed 16-bit matrix (values [rows, cols/2],
  * meta [rows, ceil(cols/32)] as written by slope_compress24 or
  * slope_double_prune), the operand format of the *_packed products.  Chunk
  * (t, s) holds rows 256t .. 256t+255 and dense columns 64s .. 64s+63, 18432
@@ -195,7 +199,7 @@ slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_
                                void* packed, int64_t packed_bytes, void* stream);
 
 /* slope_spmm_fwd with W_s given in tile-chunk form (slope_pack_sparse of
- * values_s, meta_s; rows N, cols K): same result, bitwise.  bf16 inputs only;
+ * values_s, meta_s; rows N, cols K): same result, bitwise.  16-bit inputs only;
  * K % 16 == 0, K <= 2^21, N % 4 == 0, adapter rank r <= 128.  Errors as
  * slope_spmm_fwd, plus SLOPE_ERR_UNSUPPORTED / SLOPE_ERR_SHAPE for the limits
  * above. */
@@ -210,7 +214,7 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
  * (the derivative of explainer 2.B's term):
  *   dX [T, K] = dY . W_dp (+ (dY . R^T) . L^T)
  * using workspace_or_null of slope_lowrank_workspace_bytes(T, N, r, K) bytes
- * (note the order: the reduction runs over N, the output over K).  bf16
+ * (note the order: the reduction runs over N, the output over K).  16-bit
  * inputs only; N % 16 == 0, N <= 2^21, K % 4 == 0, r <= 128. */
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
                                       const void* packed_dpT, int64_t K, const void* L_or_null,
@@ -223,18 +227,20 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
 
 /* Weight gradients of the adapter term of explainer 2.B (Y += (X . L) . R):
  *   dL [K, r] = X^T . (dY . R^T),   dR [r, N] = (X . L)^T . dY
- * X [T, K], dY [T, N], L, R bf16 row-major; X_packed, dY_packed: the same
+ * X [T, K], dY [T, N], L, R in_dt (BF16 or F16) row-major; X_packed, dY_packed: the same
  * matrices in token-chunk form (slope_pack_tokens), as the weight gradient
  * uses them.  fwd_workspace_or_null / bwd_workspace_or_null: the adapter
  * workspaces that slope_spmm_fwd_packed (X, L, R) and slope_spmm_bwd_dx_packed
  * (dY, L, R) filled for these same operands, untouched since (they hold
  * X . L and dY . R^T, which are then not recomputed); NULL to compute them
- * here.  dL, dR in out_dt (BF16 or F32), overwritten, or added to when
+ * here (workspaces filled for the same in_dt).  dL, dR in out_dt (in_dt or
+ * F32), overwritten, or added to when
  * accumulate != 0.  workspace: slope_lowrank_grads_workspace_bytes(T, K, r,
  * N) bytes, scratch.  Sums over tokens run in a fixed order.  Errors:
  * SLOPE_ERR_SHAPE unless K % 8 == 0 and N % 8 == 0; SLOPE_ERR_UNSUPPORTED
  * for r > 128; SLOPE_ERR_WORKSPACE. */
-slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
+slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* dY,
+                                        const void* X_packed,
                                         const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
                                         const void* L, const void* R, const void* fwd_workspace_or_null,
                                         const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
@@ -253,18 +259,19 @@ slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64
  * compressed weight is streamed once, split along K over enough waves to
  * keep HBM busy; partial sums are added in a fixed order (deterministic).
  * workspace: caller-owned device memory of slope_decode_workspace_bytes(T,
- * K, r, N) bytes (16-byte aligned; scratch, overwritten).  bf16 inputs only;
- * K % 16 == 0, N % 4 == 0, r <= 128.  Errors: SLOPE_ERR_UNSUPPORTED for
+ * K, r, N) bytes (16-byte aligned; scratch, overwritten).  16-bit inputs
+ * only; K % 16 == 0, N % 4 == 0, r <= 128.  Errors: SLOPE_ERR_UNSUPPORTED for
  * T > 64 or the dtype/size limits, SLOPE_ERR_SHAPE, SLOPE_ERR_WORKSPACE. */
 slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
                                    const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
                                    int64_t r, void* workspace, int64_t workspace_bytes, void* Y, void* stream);
 
-/* Bytes of a bf16 matrix M [T, C] rewritten as token chunks (see
+/* Bytes of a 16-bit matrix M [T, C] rewritten as token chunks (see
  * slope_pack_tokens).  Host-only. */
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);
 
-/* Transposed token-chunk copy of a bf16 matrix M [T, C] (C % 8 == 0), the
+/* Transposed token-chunk copy of a 16-bit (bf16 or fp16) matrix M [T, C]
+ * (C % 8 == 0), the
  * operand format of slope_masked_wgrad_packed: chunk (c, s) holds columns
  * 256c .. 256c+255 (one 64-byte row each) x tokens 32s .. 32s+31, 16 KB, at
  * byte offset (c * ceil(T/32) + s) * 16384; in a row, the 16-byte granule of
@@ -277,10 +284,12 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
                                int64_t packed_bytes, void* stream);
 
 /* slope_masked_wgrad on operands already packed by slope_pack_tokens:
- * dY_packed from dY [T, N], X_packed from X [T, K] (bf16).  Same outputs,
- * bitwise, as slope_masked_wgrad.  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or
+ * dY_packed from dY [T, N], X_packed from X [T, K], both in_dt (BF16 or
+ * F16; the chunks do not record it).  Same outputs, bitwise, as
+ * slope_masked_wgrad.  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or
  * K % 8 != 0. */
-slope_status slope_masked_wgrad_packed(slope_dtype out_dt, const void* dY_packed, const void* X_packed, int64_t T,
+slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
+                                       const void* X_packed, int64_t T,
                                        int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
                                        void* dW_dense_or_null, int accumulate, void* stream);
 

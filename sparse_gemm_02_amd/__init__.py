@@ -7,7 +7,7 @@ stream.  All computation happens in the library's HIP kernels; there is no
 fallback.  If the shared library has not been built, every call raises.
 
 Tensor conventions (see include/slope.h):
-  dense matrices      torch.bfloat16 or torch.float32, row-major
+  dense matrices      torch.bfloat16, torch.float16 or torch.float32, row-major
   masks               torch.uint8, 1 = kept
   compressed values   [rows, cols/2], same dtype as the dense matrix
   compressed metadata [rows, ceil(cols/32)] torch.int32 holding the uint32 words
@@ -41,7 +41,7 @@ library_path = os.path.join(_HERE, "libslope.so")
 STATUS = {0: "SLOPE_OK", -1: "SLOPE_ERR_INVALID_ARG", -2: "SLOPE_ERR_SHAPE", -3: "SLOPE_ERR_ALIGN",
           -4: "SLOPE_ERR_WORKSPACE", -5: "SLOPE_ERR_HIP", -6: "SLOPE_ERR_UNSUPPORTED"}
 
-_F32, _BF16 = 0, 1
+_F32, _BF16, _F16 = 0, 1, 2
 _i64, _vp, _i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 _P_I64 = ctypes.POINTER(ctypes.c_int64)
 
@@ -76,10 +76,10 @@ _SIGS = {
     "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                         _vp]),
     "slope_lowrank_grads_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
-    "slope_lowrank_grads_packed": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
-                                          _vp, _i64, _vp, _vp, _i32, _vp]),
+    "slope_lowrank_grads_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                          _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
-    "slope_masked_wgrad_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "slope_masked_wgrad_packed": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "slope_adamw": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _P_HP, _vp]),
     "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
@@ -123,12 +123,16 @@ def _check(fn: str, status: int) -> None:
         raise SlopeError(fn, status)
 
 
-def _dt(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dt(t) -> int:
+    """Library dtype code of a tensor (or of a torch dtype)."""
+    d = t if isinstance(t, torch.dtype) else t.dtype
+    if d == torch.bfloat16:
         return _BF16
-    if t.dtype == torch.float32:
+    if d == torch.float16:
+        return _F16
+    if d == torch.float32:
         return _F32
-    raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+    raise TypeError(f"expected bfloat16, float16 or float32, got {d}")
 
 
 def _p(t):
@@ -278,7 +282,7 @@ def slope_lowrank_grads_packed(X, dY, X_packed, dY_packed, L, R, workspace, dL, 
     r = int(L.shape[1])
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_lowrank_grads_packed", library().slope_lowrank_grads_packed(
-        _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(fwd_workspace),
+        _dt(X), _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(fwd_workspace),
         _p(bwd_workspace), _p(workspace), wb, _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
 
 
@@ -295,9 +299,13 @@ def slope_pack_tokens(M, packed, stream=None) -> None:
 
 
 def slope_masked_wgrad_packed(dY_packed, X_packed, T, N, K, meta_s, dW_values, dW_dense=None, accumulate=False,
-                              stream=None) -> None:
+                              stream=None, in_dtype=None) -> None:
+    """in_dtype: torch dtype the packed operands hold (the chunks do not record
+    it); defaults to dW_values' dtype when that is 16-bit, else bfloat16."""
+    if in_dtype is None:
+        in_dtype = dW_values.dtype if dW_values.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
     _check("slope_masked_wgrad_packed", library().slope_masked_wgrad_packed(
-        _dt(dW_values), _nn(dY_packed), _nn(X_packed), T, N, K, _nn(meta_s), _nn(dW_values), _p(dW_dense),
+        _dt(in_dtype), _dt(dW_values), _nn(dY_packed), _nn(X_packed), T, N, K, _nn(meta_s), _nn(dW_values), _p(dW_dense),
         int(bool(accumulate)), _s(stream)))
 
 

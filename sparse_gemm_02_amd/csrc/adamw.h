@@ -31,6 +31,14 @@ __device__ __forceinline__ void load8_f32(const uint16_t* p, float out[8]) {
     out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
+__device__ __forceinline__ void load8_f32(const _Float16* p, float out[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = f16_bits_to_f32((uint16_t)(w[i] & 0xFFFFu));
+    out[2 * i + 1] = f16_bits_to_f32((uint16_t)(w[i] >> 16));
+  }
+}
 __device__ __forceinline__ void load8_f32(const float* p, float out[8]) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
@@ -44,10 +52,12 @@ __device__ __forceinline__ void store8_f32(float* p, const float in[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{in[4], in[5], in[6], in[7]};
 }
 
-// AdamW on eight consecutive values held as four words of bf16 pairs (low
-// half first); g, m, v point at the matching eight gradient / moment entries.
-template <typename GT>
-__device__ __forceinline__ u32x4 adamw8_bf16(u32x4 w, const GT* g, float* m, float* v, const AdamWStep& c) {
+// AdamW on eight consecutive 16-bit values (bf16, or fp16 with H) held as
+// four words of pairs (low half first); g, m, v point at the matching eight
+// gradient / moment entries.
+template <bool H, typename GT>
+__device__ __forceinline__ u32x4 adamw8_16(u32x4 w, const GT* g, float* m, float* v, const AdamWStep& c) {
+  typedef Fmt16<H> F;
   float gf[8], mf[8], vf[8];
   load8_f32(g, gf);
   load8_f32(m, mf);
@@ -55,9 +65,9 @@ __device__ __forceinline__ u32x4 adamw8_bf16(u32x4 w, const GT* g, float* m, flo
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = adamw_apply(__uint_as_float(w[i] << 16), gf[2 * i], mf[2 * i], vf[2 * i], c);
-    const float hi = adamw_apply(__uint_as_float(w[i] & 0xFFFF0000u), gf[2 * i + 1], mf[2 * i + 1], vf[2 * i + 1], c);
-    out[i] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    const float lo = adamw_apply(F::to_f32((uint16_t)(w[i] & 0xFFFFu)), gf[2 * i], mf[2 * i], vf[2 * i], c);
+    const float hi = adamw_apply(F::to_f32((uint16_t)(w[i] >> 16)), gf[2 * i + 1], mf[2 * i + 1], vf[2 * i + 1], c);
+    out[i] = (uint32_t)F::from_f32(lo) | ((uint32_t)F::from_f32(hi) << 16);
   }
   store8_f32(m, mf);
   store8_f32(v, vf);

@@ -3,6 +3,8 @@
 // elementwise HBM-bound pass: 8 values per thread and iteration with 16-byte
 // loads and stores, a scalar loop for the last n % 8.  The fused form that
 // also double-prunes the updated weight lives with the double prune kernel.
+#include <type_traits>
+
 #include "adamw.h"
 
 namespace slope {
@@ -12,6 +14,7 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ float load1(const _Float16* p) { return (float)*p; }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
 template <typename PT, typename GT>
@@ -23,8 +26,9 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(PT* __restrict__ p, con
   for (int64_t i = t0; i < n8; i += stride) {
     const int64_t e = 8 * i;
     if constexpr (sizeof(PT) == 2) {
+      constexpr bool H = std::is_same<PT, _Float16>::value;
       u32x4 w = *reinterpret_cast<const u32x4*>(p + e);
-      *reinterpret_cast<u32x4*>(p + e) = adamw8_bf16(w, g + e, m + e, v + e, c);
+      *reinterpret_cast<u32x4*>(p + e) = adamw8_16<H>(w, g + e, m + e, v + e, c);
     } else {
       float pf[8], gf[8], mf[8], vf[8];
       load8_f32(p + e, pf);
@@ -58,14 +62,22 @@ hipError_t run(void* p, const void* g, float* m, float* v, int64_t n, const Adam
 
 }  // namespace
 
+namespace {
+template <typename PT>
+hipError_t run_grad(Dt grad, void* params, const void* grads, float* m, float* v, int64_t n, const AdamWStep& c,
+                    hipStream_t s) {
+  if (grad == Dt::BF16) return run<PT, uint16_t>(params, grads, m, v, n, c, s);
+  if (grad == Dt::F16) return run<PT, _Float16>(params, grads, m, v, n, c, s);
+  return run<PT, float>(params, grads, m, v, n, c, s);
+}
+}  // namespace
+
 hipError_t launch_adamw(Dt param, Dt grad, void* params, const void* grads, float* m, float* v, int64_t n,
                         const AdamWStep& c, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (param == Dt::BF16)
-    return grad == Dt::BF16 ? run<uint16_t, uint16_t>(params, grads, m, v, n, c, s)
-                            : run<uint16_t, float>(params, grads, m, v, n, c, s);
-  return grad == Dt::BF16 ? run<float, uint16_t>(params, grads, m, v, n, c, s)
-                          : run<float, float>(params, grads, m, v, n, c, s);
+  if (param == Dt::BF16) return run_grad<uint16_t>(grad, params, grads, m, v, n, c, s);
+  if (param == Dt::F16) return run_grad<_Float16>(grad, params, grads, m, v, n, c, s);
+  return run_grad<float>(grad, params, grads, m, v, n, c, s);
 }
 
 }  // namespace slope

@@ -14,7 +14,7 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool dt_ok(int d) { return d == SLOPE_F32 || d == SLOPE_BF16; }
+bool dt_ok(int d) { return d == SLOPE_F32 || d == SLOPE_BF16 || d == SLOPE_F16; }
 
 bool in_range(int64_t v) { return v >= 0 && v <= SLOPE_MAX_DIM; }
 
@@ -22,7 +22,8 @@ slope_status from_hip(hipError_t e) { return e == hipSuccess ? SLOPE_OK : SLOPE_
 
 slope_status check_io(slope_dtype in, slope_dtype out) {
   if (!dt_ok(in) || !dt_ok(out)) return SLOPE_ERR_INVALID_ARG;
-  if (in == SLOPE_F32 && out != SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
+  // outputs: the input's own format, or fp32
+  if (out != SLOPE_F32 && out != in) return SLOPE_ERR_UNSUPPORTED;
   return SLOPE_OK;
 }
 
@@ -232,7 +233,7 @@ slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_
   SLOPE_TRY(ptr(values, true));
   SLOPE_TRY(ptr(meta, true));
   SLOPE_TRY(ptr(packed, true));
-  if (dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // 16-bit values only
   if (cols % 16) return SLOPE_ERR_SHAPE;
   if (!in_range(rows) || cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
   if (packed_bytes < slope::packed_sparse_bytes(rows, cols)) return SLOPE_ERR_WORKSPACE;
@@ -253,7 +254,7 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
     SLOPE_TRY(ptr(L_or_null, true));
     SLOPE_TRY(ptr(R_or_null, true));
   }
-  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   if (adapter) {
@@ -269,7 +270,8 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
     hipError_t e = slope::launch_lowrank_prepare((Dt)in_dt, X, L_or_null, R_or_null, T, K, r, N, w, s);
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
-  return from_hip(slope::launch_spmm_packed((Dt)out_dt, X, T, K, packed_s, N, adapter ? &w : nullptr, Y, s));
+  return from_hip(slope::launch_spmm_packed((Dt)in_dt, (Dt)out_dt, X, T, K, packed_s, N, adapter ? &w : nullptr, Y,
+                                            s));
 }
 
 slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes) {
@@ -293,13 +295,13 @@ slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const 
     SLOPE_TRY(ptr(L_or_null, true));
     SLOPE_TRY(ptr(R_or_null, true));
   }
-  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
   if (T > kDecodeMaxTokens || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   const int64_t need = slope::decode_workspace_bytes(T, K, adapter ? r : 0, N);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
   if (T == 0 || N == 0) return SLOPE_OK;
-  return from_hip(slope::launch_spmm_decode((Dt)out_dt, X, T, K, packed_s, N, L_or_null, R_or_null, adapter ? r : 0,
+  return from_hip(slope::launch_spmm_decode((Dt)in_dt, (Dt)out_dt, X, T, K, packed_s, N, L_or_null, R_or_null, adapter ? r : 0,
                                             workspace, Y, (hipStream_t)stream));
 }
 
@@ -317,7 +319,7 @@ slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, con
     SLOPE_TRY(ptr(L_or_null, true));
     SLOPE_TRY(ptr(R_or_null, true));
   }
-  if (in_dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (N % 16 || K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || N > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   if (adapter) {
@@ -330,11 +332,12 @@ slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, con
   hipStream_t s = (hipStream_t)stream;
   slope::LowrankWs w;
   if (adapter) {
-    w = slope::lowrank_layout(Dt::BF16, workspace_or_null, T, N, r, K);
+    w = slope::lowrank_layout((Dt)in_dt, workspace_or_null, T, N, r, K);
     hipError_t e = slope::launch_lowrank_prepare_bwd(dY, L_or_null, R_or_null, T, N, r, K, w, s);
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
-  return from_hip(slope::launch_spmm_packed((Dt)out_dt, dY, T, N, packed_dpT, K, adapter ? &w : nullptr, dX, s));
+  return from_hip(slope::launch_spmm_packed((Dt)in_dt, (Dt)out_dt, dY, T, N, packed_dpT, K, adapter ? &w : nullptr,
+                                            dX, s));
 }
 
 namespace {
@@ -363,12 +366,13 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
   return SLOPE_OK;
 }
 
-slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const void* dY, const void* X_packed,
+slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* dY,
+                                        const void* X_packed,
                                         const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
                                         const void* L, const void* R, const void* fwd_workspace_or_null,
                                         const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
                                         void* dL, void* dR, int accumulate, void* stream) {
-  SLOPE_TRY(check_io(SLOPE_BF16, out_dt));
+  SLOPE_TRY(check_io(in_dt, out_dt));
   if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(dY, true));
@@ -381,6 +385,7 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
   SLOPE_TRY(ptr(workspace, false));
   SLOPE_TRY(ptr(fwd_workspace_or_null, false));
   SLOPE_TRY(ptr(bwd_workspace_or_null, false));
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   const GradsWs g = grads_ws(T, K, r, N);
@@ -398,9 +403,9 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
   // workspace when the caller hands them over, else computed here
   const bool have_f = fwd_workspace_or_null != nullptr, have_b = bwd_workspace_or_null != nullptr;
   const slope::LowrankWs wf =
-      slope::lowrank_layout(Dt::BF16, have_f ? const_cast<void*>(fwd_workspace_or_null) : (void*)p, T, K, r, N);
+      slope::lowrank_layout((Dt)in_dt, have_f ? const_cast<void*>(fwd_workspace_or_null) : (void*)p, T, K, r, N);
   const slope::LowrankWs wb = slope::lowrank_layout(
-      Dt::BF16, have_b ? const_cast<void*>(bwd_workspace_or_null) : (void*)(p + g.fwd), T, N, r, K);
+      (Dt)in_dt, have_b ? const_cast<void*>(bwd_workspace_or_null) : (void*)(p + g.fwd), T, N, r, K);
   uint16_t* xh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd);
   uint16_t* xl = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + g.trans);
   uint16_t* gh = reinterpret_cast<uint16_t*>(p + g.fwd + g.bwd + 2 * g.trans);
@@ -409,14 +414,16 @@ slope_status slope_lowrank_grads_packed(slope_dtype out_dt, const void* X, const
   float* pl = reinterpret_cast<float*>(p + g.fwd + g.bwd + 4 * g.trans + g.part_r);
   const int64_t r32 = (r + 31) / 32 * 32;
   hipError_t e = hipSuccess;
-  if (!have_f) e = slope::launch_lowrank_down(Dt::BF16, X, L, T, K, r, wf, s);                        // X . L
+  if (!have_f) e = slope::launch_lowrank_down((Dt)in_dt, X, L, T, K, r, wf, s);                      // X . L
   if (e == hipSuccess && !have_b) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
   if (e == hipSuccess) e = slope::launch_transpose_hilo(wf, r32, xh, xl, s);
   if (e == hipSuccess) e = slope::launch_transpose_hilo(wb, r32, gh, gl, s);
   if (e == hipSuccess)
-    e = slope::launch_lr_wgrad((Dt)out_dt, dY_packed, T, N, r, xh, xl, wf.Tpad, pr, dR, false, accumulate, s);
+    e = slope::launch_lr_wgrad((Dt)in_dt, (Dt)out_dt, dY_packed, T, N, r, xh, xl, wf.Tpad, pr, dR, false, accumulate,
+                               s);
   if (e == hipSuccess)
-    e = slope::launch_lr_wgrad((Dt)out_dt, X_packed, T, K, r, gh, gl, wb.Tpad, pl, dL, true, accumulate, s);
+    e = slope::launch_lr_wgrad((Dt)in_dt, (Dt)out_dt, X_packed, T, K, r, gh, gl, wb.Tpad, pl, dL, true, accumulate,
+                               s);
   return from_hip(e);
 }
 
@@ -433,28 +440,29 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
   if (T < 0 || C < 0 || packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(M, true));
   SLOPE_TRY(ptr(packed, true));
-  if (dt != SLOPE_BF16) return SLOPE_ERR_UNSUPPORTED;
+  if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // 16-bit values only
   if (C % 8) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(C)) return SLOPE_ERR_UNSUPPORTED;
   if (packed_bytes < slope::packed_tokens_bytes(T, C)) return SLOPE_ERR_WORKSPACE;
   return from_hip(slope::launch_pack_tokens(M, T, C, packed, (hipStream_t)stream));
 }
 
-slope_status slope_masked_wgrad_packed(slope_dtype out_dt, const void* dY_packed, const void* X_packed, int64_t T,
-                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
-                                       void* dW_dense_or_null, int accumulate, void* stream) {
-  SLOPE_TRY(check_io(SLOPE_BF16, out_dt));
+slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
+                                       const void* X_packed, int64_t T, int64_t N, int64_t K, const uint32_t* meta_s,
+                                       void* dW_values, void* dW_dense_or_null, int accumulate, void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
   if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY_packed, true));
   SLOPE_TRY(ptr(X_packed, true));
   SLOPE_TRY(ptr(meta_s, true));
   SLOPE_TRY(ptr(dW_values, true));
   SLOPE_TRY(ptr(dW_dense_or_null, false));
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
   if (N == 0 || K == 0) return SLOPE_OK;
-  return from_hip(slope::launch_masked_wgrad_packed((Dt)out_dt, dY_packed, X_packed, T, N, K, meta_s, dW_values,
-                                                    dW_dense_or_null, accumulate, (hipStream_t)stream));
+  return from_hip(slope::launch_masked_wgrad_packed((Dt)in_dt, (Dt)out_dt, dY_packed, X_packed, T, N, K, meta_s,
+                                                    dW_values, dW_dense_or_null, accumulate, (hipStream_t)stream));
 }
 
 slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,

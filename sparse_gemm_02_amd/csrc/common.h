@@ -7,6 +7,8 @@ namespace slope {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -19,6 +21,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t mag_key(uint16_t b) {
   uint32_t m = b & 0x7FFFu;
   return m > 0x7F80u ? 0x7F81u : m;
+}
+// fp16 storage: NaN above the fp16 infinity 0x7C00
+__device__ __forceinline__ uint32_t mag_key(_Float16 h) {
+  uint32_t m = __builtin_bit_cast(uint16_t, h) & 0x7FFFu;
+  return m > 0x7C00u ? 0x7C01u : m;
 }
 __device__ __forceinline__ uint32_t mag_key(uint32_t b) {
   uint32_t m = b & 0x7FFFFFFFu;
@@ -56,11 +63,58 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Output element stores (bf16 bits or fp32).
+// fp16 storage is the _Float16 type; conversions round to nearest even.
+__device__ __forceinline__ float to_f32(_Float16 h) { return (float)h; }
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Output element stores: uint16_t holds bf16 bits, _Float16 fp16, float fp32.
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+__device__ __forceinline__ void store_out(_Float16* p, float v) { *p = (_Float16)v; }
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ float load_out(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ float load_out(const _Float16* p) { return (float)*p; }
 __device__ __forceinline__ float load_out(const float* p) { return *p; }
+
+// 16-bit output patterns: bf16 for uint16_t outputs, fp16 for _Float16 ones.
+template <typename O> __device__ __forceinline__ uint16_t out16_bits(float v);
+template <> __device__ __forceinline__ uint16_t out16_bits<uint16_t>(float v) { return f32_to_bf16_bits(v); }
+template <> __device__ __forceinline__ uint16_t out16_bits<_Float16>(float v) { return f32_to_f16_bits(v); }
+
+// The two 16-bit input formats of the matrix kernels, selected by H (fp16)
+// or not (bf16): operand vectors, conversions of raw 16-bit patterns, and the
+// MFMA / sparse MFMA instructions of that format.
+template <bool H> struct Fmt16;
+template <> struct Fmt16<false> {
+  typedef bf16x8 v8;
+  typedef bf16x16 v16;
+  static __device__ __forceinline__ float to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
+  static __device__ __forceinline__ uint16_t from_f32(float f) { return f32_to_bf16_bits(f); }
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x32(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 smfmac32x32x32(v8 a, v16 b, f32x16 c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, 0);
+  }
+};
+template <> struct Fmt16<true> {
+  typedef f16x8 v8;
+  typedef f16x16 v16;
+  static __device__ __forceinline__ float to_f32(uint16_t b) { return f16_bits_to_f32(b); }
+  static __device__ __forceinline__ uint16_t from_f32(float f) { return f32_to_f16_bits(f); }
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x32(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 smfmac32x32x32(v8 a, v16 b, f32x16 c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, 0);
+  }
+};
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -28,7 +28,7 @@ constexpr int kUnroll = 4;                       // stages whose loads are issue
 // part[split][t][n] (n < Npad) = sum over this split's k of X[t][k] W_s[n][k].
 // Block = 4 waves = one 256-row tile; wave w rows 64w .. 64w+63 (two 32-row
 // A operands), FT = 1 or 2 token tiles of 32.
-template <int FT>
+template <int FT, bool H>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ X,
                                                              const char* __restrict__ packed, int T, int K,
                                                              int stages, int kc, int64_t Npad,
@@ -65,9 +65,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
     for (int ft = 0; ft < FT; ++ft) acc[fm][ft] = f32x16{};
 
   for (int sb = s0; sb < s1; sb += kUnroll) {
-    bf16x8 a[kUnroll][2][2];
+    typedef typename Fmt16<H>::v8 v8;
+    v8 a[kUnroll][2][2];
     int ix[kUnroll][2][2];
-    bf16x16 b[kUnroll][2][FT];
+    typename Fmt16<H>::v16 b[kUnroll][2][FT];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int s = sb + u;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
       for (int fm = 0; fm < 2; ++fm) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          a[u][fm][ks] = __builtin_bit_cast(bf16x8, load16(ra, live ? c + a_off[fm][ks] : kOutOfRange));
+          a[u][fm][ks] = __builtin_bit_cast(v8, load16(ra, live ? c + a_off[fm][ks] : kOutOfRange));
           const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(ra, live ? c + m_off[fm] + ks * 4 : kOutOfRange, 0, 0);
           ix[u][fm][ks] = (int)(w >> ix_shift);    // this lane's half of the word
         }
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
           const bool valid = x_off[ft] != kOutOfRange;
           const u32x4 lo = load16(rx, valid && ok_lo ? x_off[ft] + kb : kOutOfRange);
           const u32x4 hi = load16(rx, valid && ok_hi ? x_off[ft] + kb + 32 : kOutOfRange);
-          b[u][ks][ft] = __builtin_shufflevector(__builtin_bit_cast(bf16x8, lo), __builtin_bit_cast(bf16x8, hi), 0, 1,
-                                                 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+          b[u][ks][ft] = __builtin_shufflevector(__builtin_bit_cast(v8, lo), __builtin_bit_cast(v8, hi), 0, 1, 2, 3, 4,
+                                                 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
         }
       }
     }
@@ -106,8 +107,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
         for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
           for (int fm = 0; fm < 2; ++fm)
-            acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[u][fm][ks], b[u][ks][ft], acc[fm][ft],
-                                                                    ix[u][fm][ks], 0, 0);
+            acc[fm][ft] = Fmt16<H>::smfmac32x32x32(a[u][fm][ks], b[u][ks][ft], acc[fm][ft], ix[u][fm][ks]);
   }
 
   // lane holds token ft*32 + lane%32, rows 8*(v/4) + 4*(lane/32) + v%4 of each 32-row block
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
 // broadcasts; R is read in its own [r, N] layout.
 constexpr int kReduceMaxRank = 128;
 
-template <typename O, int TB, int Q>
+template <typename O, int TB, int Q, bool H>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part, int splits, int T,
                                                             int64_t N, int64_t Npad, const uint16_t* __restrict__ R,
                                                             const uint16_t* __restrict__ xlh,
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   if (R) {
     for (int e = threadIdx.x; e < TB * rpad; e += 256) {
       const int i = e / rpad, j = e % rpad;
-      xl[i][j] = tb + i < T ? bf16_bits_to_f32(xlh[(tb + i) * rpad + j]) + bf16_bits_to_f32(xll[(tb + i) * rpad + j])
+      xl[i][j] = tb + i < T ? Fmt16<H>::to_f32(xlh[(tb + i) * rpad + j]) + Fmt16<H>::to_f32(xll[(tb + i) * rpad + j])
                            : 0.f;
     }
   }
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
 #pragma unroll
       for (int q = 0; q < 4 * Q; ++q) {
         const int j = c0 + q;
-        rv[q] = (col && j < j0 + rq && j < r) ? bf16_bits_to_f32(R[(int64_t)j * N + n]) : 0.f;
+        rv[q] = (col && j < j0 + rq && j < r) ? Fmt16<H>::to_f32(R[(int64_t)j * N + n]) : 0.f;
       }
 #pragma unroll
       for (int q = 0; q < 4 * Q; ++q) {
@@ -205,15 +205,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   }
 }
 
-template <typename O>
+template <typename O, bool H>
 void launch_decode_reduce(const float* part, int splits, int64_t T, int64_t N, int64_t Npad, const uint16_t* R,
                           const uint16_t* xh, const uint16_t* xo, int r, int rpad, O* Y, hipStream_t s) {
   if (T <= 4) {
     dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 4));
-    decode_reduce_kernel<O, 4, 16><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
+    decode_reduce_kernel<O, 4, 16, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
   } else {
     dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 16));
-    decode_reduce_kernel<O, 16, 4><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
+    decode_reduce_kernel<O, 16, 4, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xh, xo, r, rpad, Y);
   }
 }
 
@@ -248,7 +248,20 @@ int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N) {
   return decode_plan(T, K, N).part_bytes + (r > 0 ? lowrank_workspace_bytes(T, K, r, N) : 0);
 }
 
-hipError_t launch_spmm_decode(Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
+namespace {
+template <bool H>
+void decode_partial_launch(int64_t T, dim3 grid, const void* X, const void* packed, int64_t K, const DecodePlan& p,
+                           float* part, hipStream_t s) {
+  if (T <= 32)
+    decode_partial_kernel<1, H><<<grid, 256, 0, s>>>((const uint16_t*)X, (const char*)packed, (int)T, (int)K,
+                                                     p.stages, p.kc, p.Npad, part);
+  else
+    decode_partial_kernel<2, H><<<grid, 256, 0, s>>>((const uint16_t*)X, (const char*)packed, (int)T, (int)K,
+                                                     p.stages, p.kc, p.Npad, part);
+}
+}  // namespace
+
+hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
                               const void* L, const void* R, int64_t r, void* workspace, void* Y, hipStream_t s) {
   if (T == 0 || N == 0) return hipSuccess;
   const DecodePlan p = decode_plan(T, K, N);
@@ -256,25 +269,27 @@ hipError_t launch_spmm_decode(Dt out, const void* X, int64_t T, int64_t K, const
   const bool ad = r > 0 && L != nullptr && R != nullptr;
   LowrankWs w;
   if (ad) {
-    w = lowrank_layout(Dt::BF16, (char*)workspace + p.part_bytes, T, K, r, N);
-    const hipError_t e = launch_lowrank_down(Dt::BF16, X, L, T, K, r, w, s);
+    w = lowrank_layout(in, (char*)workspace + p.part_bytes, T, K, r, N);
+    const hipError_t e = launch_lowrank_down(in, X, L, T, K, r, w, s);
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
-  if (T <= 32)
-    decode_partial_kernel<1><<<grid, 256, 0, s>>>((const uint16_t*)X, (const char*)packed, (int)T, (int)K, p.stages,
-                                                  p.kc, p.Npad, part);
+  if (in == Dt::F16)
+    decode_partial_launch<true>(T, grid, X, packed, K, p, part, s);
   else
-    decode_partial_kernel<2><<<grid, 256, 0, s>>>((const uint16_t*)X, (const char*)packed, (int)T, (int)K, p.stages,
-                                                  p.kc, p.Npad, part);
+    decode_partial_launch<false>(T, grid, X, packed, K, p, part, s);
   const uint16_t* Ra = ad ? (const uint16_t*)R : nullptr;
   const uint16_t* xh = ad ? w.xlh : nullptr;
   const uint16_t* xo = ad ? w.xll : nullptr;
   const int rp = ad ? (int)w.rpad : 0;
   if (out == Dt::BF16)
-    launch_decode_reduce(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (uint16_t*)Y, s);
+    launch_decode_reduce<uint16_t, false>(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (uint16_t*)Y, s);
+  else if (out == Dt::F16)
+    launch_decode_reduce<_Float16, true>(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (_Float16*)Y, s);
+  else if (in == Dt::F16)
+    launch_decode_reduce<float, true>(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (float*)Y, s);
   else
-    launch_decode_reduce(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (float*)Y, s);
+    launch_decode_reduce<float, false>(part, p.splits, T, N, p.Npad, Ra, xh, xo, (int)r, rp, (float*)Y, s);
   return hipGetLastError();
 }
 

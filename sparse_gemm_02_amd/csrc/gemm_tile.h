@@ -46,38 +46,41 @@ struct Geo {
 
 // acc[fm][ft] += R^T . (X L)^T over the adapter rank, from the prepared
 // workspace: rt [Npad][rpad] (R transposed) and the hi / lo bf16 parts of
-// X . L, xlh / xll [Tpad][rpad]; both padded with zeros so no bounds checks
-// are needed.  Dense 32x32x16 MFMA: A lane l = row l%32, k = 8*(l/32)+e; B lane
-// l = column l%32, same k.  hi and lo together keep ~16 bits of X . L.
-template <class G>
+// X . L, xlh / xll [Tpad][rpad], in the input format (bf16, or fp16 with H);
+// both padded with zeros so no bounds checks are needed.  Dense 32x32x16
+// MFMA: A lane l = row l%32, k = 8*(l/32)+e; B lane l = column l%32, same k.
+// hi and lo together keep about twice the format's mantissa of X . L.
+template <class G, bool H = false>
 __device__ __forceinline__ void adapter_mma(f32x16 (&acc)[G::FM][G::FT], const uint16_t* __restrict__ rt,
                                             const uint16_t* __restrict__ xlh, const uint16_t* __restrict__ xll,
                                             int rpad, int64_t m0, int64_t t0, int wm, int wt, int lane) {
+  typedef Fmt16<H> F;
+  typedef typename F::v8 v8;
   const int kofs = 8 * (lane >> 5);
   for (int jk = 0; jk < rpad; jk += 16) {
-    bf16x8 ra[G::FM];
+    v8 ra[G::FM];
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm) {
       const int64_t m = m0 + wm * G::WM + fm * 32 + (lane & 31);
-      ra[fm] = *reinterpret_cast<const bf16x8*>(rt + m * rpad + jk + kofs);
+      ra[fm] = *reinterpret_cast<const v8*>(rt + m * rpad + jk + kofs);
     }
 #pragma unroll
     for (int ft = 0; ft < G::FT; ++ft) {
       const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
-      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xlh + t * rpad + jk + kofs);
-      const bf16x8 xo = *reinterpret_cast<const bf16x8*>(xll + t * rpad + jk + kofs);
+      const v8 xh = *reinterpret_cast<const v8*>(xlh + t * rpad + jk + kofs);
+      const v8 xo = *reinterpret_cast<const v8*>(xll + t * rpad + jk + kofs);
 #pragma unroll
       for (int fm = 0; fm < G::FM; ++fm) {
-        acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xh, acc[fm][ft], 0, 0, 0);
-        acc[fm][ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[fm], xo, acc[fm][ft], 0, 0, 0);
+        acc[fm][ft] = F::mfma32x32x16(ra[fm], xh, acc[fm][ft]);
+        acc[fm][ft] = F::mfma32x32x16(ra[fm], xo, acc[fm][ft]);
       }
     }
   }
 }
 
 // Store the transposed tile to Out[t][m] (row-major [T, M]); four consecutive
-// accumulator elements are four consecutive m: one 8-byte (bf16) or 16-byte
-// store.  Requires M % 4 == 0.
+// accumulator elements are four consecutive m: one 8-byte (16-bit output) or
+// 16-byte (fp32) store.  Requires M % 4 == 0.
 template <class G, typename O>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FM][G::FT], O* __restrict__ Y, int64_t m0,
                                            int64_t t0, int M, int T, int wm, int wt, int lane) {
@@ -94,8 +97,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FM][G::FT], O*
         O* p = Y + t * M + m;
         if constexpr (sizeof(O) == 2) {
           u32x2 w;
-          w[0] = f32_to_bf16_bits(acc[fm][ft][4 * q]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 1]) << 16);
-          w[1] = f32_to_bf16_bits(acc[fm][ft][4 * q + 2]) | ((uint32_t)f32_to_bf16_bits(acc[fm][ft][4 * q + 3]) << 16);
+          w[0] = out16_bits<O>(acc[fm][ft][4 * q]) | ((uint32_t)out16_bits<O>(acc[fm][ft][4 * q + 1]) << 16);
+          w[1] = out16_bits<O>(acc[fm][ft][4 * q + 2]) | ((uint32_t)out16_bits<O>(acc[fm][ft][4 * q + 3]) << 16);
           *reinterpret_cast<u32x2*>(p) = w;
         } else {
           f32x4 w = {acc[fm][ft][4 * q], acc[fm][ft][4 * q + 1], acc[fm][ft][4 * q + 2], acc[fm][ft][4 * q + 3]};

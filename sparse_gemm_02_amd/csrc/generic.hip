@@ -1,5 +1,5 @@
-// Generic LDS-tiled SIMT kernels: the fp32 path and the bf16 path for shapes
-// whose rows are not 16-byte aligned.  Accumulation in fp32.
+// Generic LDS-tiled SIMT kernels: the fp32 path and the 16-bit paths (bf16,
+// fp16) for shapes whose rows are not 16-byte aligned.  Accumulation in fp32.
 //
 // Operations (SLoPe explainer, Technical Summary 2.A and 2.B; discussion page,
 // "Memory Footprint" and "SLoPe inference computation"):
@@ -173,16 +173,44 @@ __global__ void fill_zero_kernel(O* __restrict__ Y, int64_t count) {
 
 }  // namespace
 
+namespace {
+
+// storage type of each input format: bf16 bits, fp16, fp32 bits
+template <typename E, typename O>
+void spmm_generic(dim3 grid, const void* B, const void* values, const uint32_t* meta, int64_t M, int64_t T,
+                  int64_t Kred, const float* xl, int splits, int64_t r, const void* R, void* Y, hipStream_t s) {
+  spmm_generic_kernel<E, O><<<grid, 256, 0, s>>>((const E*)B, (const E*)values, meta, M, T, Kred, xl, splits, r,
+                                                 (const E*)R, (O*)Y);
+}
+template <typename E, typename O>
+void wgrad_generic(dim3 grid, const void* dY, const void* X, int64_t T, int64_t N, int64_t K, const uint32_t* meta,
+                   void* dWv, void* dWd, int accumulate, hipStream_t s) {
+  wgrad_generic_kernel<E, O><<<grid, 256, 0, s>>>((const E*)dY, (const E*)X, T, N, K, meta, (O*)dWv, (O*)dWd,
+                                                  accumulate);
+}
+template <typename E, typename O>
+void up_generic(unsigned grid, const float* xl, int splits, const void* R, int64_t T, int64_t r, int64_t N, void* Y,
+                hipStream_t s) {
+  lowrank_up_generic_kernel<E, O><<<grid, 256, 0, s>>>(xl, splits, (const E*)R, T, r, N, (O*)Y);
+}
+
+}  // namespace
+
+// in: the input format; out: the input format or F32 (F32 inputs take F32 outputs)
 hipError_t launch_spmm_generic(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
                                const uint32_t* meta, int64_t M, const float* xl, int splits, int64_t r,
                                const void* R, void* Y, hipStream_t s) {
   dim3 grid((unsigned)cdiv(M, TILE), (unsigned)cdiv(T, TILE));
   if (in == Dt::BF16 && out == Dt::BF16)
-    spmm_generic_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)B, (const uint16_t*)values, meta, M, T, Kred, xl, splits, r, (const uint16_t*)R, (uint16_t*)Y);
+    spmm_generic<uint16_t, uint16_t>(grid, B, values, meta, M, T, Kred, xl, splits, r, R, Y, s);
   else if (in == Dt::BF16)
-    spmm_generic_kernel<uint16_t, float><<<grid, 256, 0, s>>>((const uint16_t*)B, (const uint16_t*)values, meta, M, T, Kred, xl, splits, r, (const uint16_t*)R, (float*)Y);
+    spmm_generic<uint16_t, float>(grid, B, values, meta, M, T, Kred, xl, splits, r, R, Y, s);
+  else if (in == Dt::F16 && out == Dt::F16)
+    spmm_generic<_Float16, _Float16>(grid, B, values, meta, M, T, Kred, xl, splits, r, R, Y, s);
+  else if (in == Dt::F16)
+    spmm_generic<_Float16, float>(grid, B, values, meta, M, T, Kred, xl, splits, r, R, Y, s);
   else
-    spmm_generic_kernel<uint32_t, float><<<grid, 256, 0, s>>>((const uint32_t*)B, (const uint32_t*)values, meta, M, T, Kred, xl, splits, r, (const uint32_t*)R, (float*)Y);
+    spmm_generic<uint32_t, float>(grid, B, values, meta, M, T, Kred, xl, splits, r, R, Y, s);
   return hipGetLastError();
 }
 
@@ -190,11 +218,15 @@ hipError_t launch_wgrad_generic(Dt in, Dt out, const void* dY, const void* X, in
                                 const uint32_t* meta_s, void* dWv, void* dWd, int accumulate, hipStream_t s) {
   dim3 grid((unsigned)cdiv(K, TILE), (unsigned)cdiv(N, TILE));
   if (in == Dt::BF16 && out == Dt::BF16)
-    wgrad_generic_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)dY, (const uint16_t*)X, T, N, K, meta_s, (uint16_t*)dWv, (uint16_t*)dWd, accumulate);
+    wgrad_generic<uint16_t, uint16_t>(grid, dY, X, T, N, K, meta_s, dWv, dWd, accumulate, s);
   else if (in == Dt::BF16)
-    wgrad_generic_kernel<uint16_t, float><<<grid, 256, 0, s>>>((const uint16_t*)dY, (const uint16_t*)X, T, N, K, meta_s, (float*)dWv, (float*)dWd, accumulate);
+    wgrad_generic<uint16_t, float>(grid, dY, X, T, N, K, meta_s, dWv, dWd, accumulate, s);
+  else if (in == Dt::F16 && out == Dt::F16)
+    wgrad_generic<_Float16, _Float16>(grid, dY, X, T, N, K, meta_s, dWv, dWd, accumulate, s);
+  else if (in == Dt::F16)
+    wgrad_generic<_Float16, float>(grid, dY, X, T, N, K, meta_s, dWv, dWd, accumulate, s);
   else
-    wgrad_generic_kernel<uint32_t, float><<<grid, 256, 0, s>>>((const uint32_t*)dY, (const uint32_t*)X, T, N, K, meta_s, (float*)dWv, (float*)dWd, accumulate);
+    wgrad_generic<uint32_t, float>(grid, dY, X, T, N, K, meta_s, dWv, dWd, accumulate, s);
   return hipGetLastError();
 }
 
@@ -204,6 +236,8 @@ hipError_t launch_lowrank_down_generic(Dt in, const void* X, const void* L, int6
   dim3 grid((unsigned)cdiv(T * r, 256), (unsigned)splits);
   if (in == Dt::BF16)
     lowrank_down_generic_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)X, (const uint16_t*)L, T, K, r, kc, xl);
+  else if (in == Dt::F16)
+    lowrank_down_generic_kernel<_Float16><<<grid, 256, 0, s>>>((const _Float16*)X, (const _Float16*)L, T, K, r, kc, xl);
   else
     lowrank_down_generic_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)X, (const uint32_t*)L, T, K, r, kc, xl);
   return hipGetLastError();
@@ -213,19 +247,23 @@ hipError_t launch_lowrank_up_generic(Dt in, Dt out, const float* xl, int splits,
                                      int64_t r, int64_t N, void* Y, hipStream_t s) {
   const unsigned grid = (unsigned)cdiv(T * N, 256);
   if (in == Dt::BF16 && out == Dt::BF16)
-    lowrank_up_generic_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>(xl, splits, (const uint16_t*)R, T, r, N, (uint16_t*)Y);
+    up_generic<uint16_t, uint16_t>(grid, xl, splits, R, T, r, N, Y, s);
   else if (in == Dt::BF16)
-    lowrank_up_generic_kernel<uint16_t, float><<<grid, 256, 0, s>>>(xl, splits, (const uint16_t*)R, T, r, N, (float*)Y);
+    up_generic<uint16_t, float>(grid, xl, splits, R, T, r, N, Y, s);
+  else if (in == Dt::F16 && out == Dt::F16)
+    up_generic<_Float16, _Float16>(grid, xl, splits, R, T, r, N, Y, s);
+  else if (in == Dt::F16)
+    up_generic<_Float16, float>(grid, xl, splits, R, T, r, N, Y, s);
   else
-    lowrank_up_generic_kernel<uint32_t, float><<<grid, 256, 0, s>>>(xl, splits, (const uint32_t*)R, T, r, N, (float*)Y);
+    up_generic<uint32_t, float>(grid, xl, splits, R, T, r, N, Y, s);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(Dt out, void* Y, int64_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;
   const unsigned grid = (unsigned)(cdiv(count, 256) < 4096 ? cdiv(count, 256) : 4096);
-  if (out == Dt::BF16) fill_zero_kernel<uint16_t><<<grid, 256, 0, s>>>((uint16_t*)Y, count);
-  else fill_zero_kernel<float><<<grid, 256, 0, s>>>((float*)Y, count);
+  if (out == Dt::F32) fill_zero_kernel<float><<<grid, 256, 0, s>>>((float*)Y, count);
+  else fill_zero_kernel<uint16_t><<<grid, 256, 0, s>>>((uint16_t*)Y, count);   // +0 in bf16 and fp16
   return hipGetLastError();
 }
 

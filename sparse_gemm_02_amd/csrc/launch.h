@@ -7,7 +7,7 @@
 
 namespace slope {
 
-enum class Dt { F32 = 0, BF16 = 1 };
+enum class Dt { F32 = 0, BF16 = 1, F16 = 2 };
 
 hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* W_s,
                           hipStream_t s);
@@ -41,7 +41,8 @@ struct LowrankWs {
   uint16_t *xlh = nullptr, *xll = nullptr, *lt = nullptr, *rt = nullptr;
   int splits = 1;
   int64_t rpad = 0, Tpad = 0, Kpad = 0, Npad = 0, kc = 0;
-  bool mfma = false;  // rt / xlh / xll are filled (bf16 inputs, K % 8 == 0, r <= 128)
+  bool mfma = false;  // rt / xlh / xll are filled (16-bit inputs, K % 8 == 0, r <= 128)
+  bool h16 = false;   // the 16-bit format is fp16 (else bf16): lt, rt, xlh, xll hold fp16
 };
 int64_t lowrank_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N);
 LowrankWs lowrank_layout(Dt in, void* ws, int64_t T, int64_t K, int64_t r, int64_t N);
@@ -68,7 +69,7 @@ hipError_t launch_transpose_hilo(const LowrankWs& w, int64_t rpad32, uint16_t* x
 // [32*ceil(r/32)][Tpad]; written as out[j][c] (dR) or, trans, out[c][j] (dL).
 // part: lr_wgrad_part_bytes(T, C, r) of fp32 scratch.
 int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r);
-hipError_t launch_lr_wgrad(Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
+hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
                            const uint16_t* bl, int64_t Tpad, float* part, void* dst, bool trans, int accumulate,
                            hipStream_t s);
 
@@ -84,14 +85,14 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
 int64_t packed_sparse_bytes(int64_t M, int64_t Kred);
 hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t M, int64_t Kred, void* packed,
                               hipStream_t s);
-hipError_t launch_spmm_packed(Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
+hipError_t launch_spmm_packed(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
                               const LowrankWs* ws, void* Y, hipStream_t s);
 
 // Forward for T <= 64 tokens on tile-chunk weights (bf16): split-k partial
 // sums reduced in order, plus the adapter term when r > 0 (L [K, r],
 // R [r, N]); workspace of decode_workspace_bytes(T, K, r, N) bytes.
 int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N);
-hipError_t launch_spmm_decode(Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
+hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
                               const void* L, const void* R, int64_t r, void* workspace, void* Y, hipStream_t s);
 
 // dW = (dY^T . X) kept at meta_s, written compressed (+ dense) with optional
@@ -102,8 +103,8 @@ int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K);
 int64_t packed_tokens_bytes(int64_t T, int64_t C);
 hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s);
 // The weight-gradient GEMM on packed bf16 operands (N % 8 == 0, K % 8 == 0).
-hipError_t launch_masked_wgrad_packed(Dt out, const void* dY_packed, const void* X_packed, int64_t T, int64_t N,
-                                      int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
+hipError_t launch_masked_wgrad_packed(Dt in, Dt out, const void* dY_packed, const void* X_packed, int64_t T,
+                                      int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
                                       int accumulate, hipStream_t s);
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void transpose_hilo_kernel(const uint16_t* __r
 // issued before the current step's MFMAs.  Dense 16x16x32 MFMA: A lane l = row
 // l%16, k = 8*(l/16)+e; B lane l = column l%16, same k; D lane l = column l%16,
 // rows 4*(l/16)+v.
-template <int NJ>
+template <int NJ, bool H>
 __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ lt, int T, int K, int r,
                                                            int rpad, int Kpad, int kc, float* __restrict__ part) {
@@ -167,10 +167,10 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
   auto mma = [&](const Ops& o) {
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
-      const bf16x8 bb = __builtin_bit_cast(bf16x8, o.b[jb]);
+      typedef typename Fmt16<H>::v8 v8;
+      const v8 bb = __builtin_bit_cast(v8, o.b[jb]);
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        acc[g][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a[g]), bb, acc[g][jb], 0, 0, 0);
+      for (int g = 0; g < G; ++g) acc[g][jb] = Fmt16<H>::mfma16x16x32(__builtin_bit_cast(v8, o.a[g]), bb, acc[g][jb]);
     }
   };
   Ops p0, p1;
@@ -198,8 +198,12 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
 template <int NJ>
 void down_nj(dim3 grid, const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
              hipStream_t s) {
-  lowrank_down_kernel<NJ><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad, (int)w.kc,
-                                               w.part);
+  if (w.h16)
+    lowrank_down_kernel<NJ, true><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad,
+                                                       (int)w.kc, w.part);
+  else
+    lowrank_down_kernel<NJ, false><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad,
+                                                        (int)w.kc, w.part);
 }
 
 hipError_t launch_down(const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
@@ -219,8 +223,10 @@ hipError_t launch_down(const uint16_t* X, const uint16_t* lt, int64_t T, int64_t
   return hipGetLastError();
 }
 
-// xl = sum over splits of part (in split order), split into bf16 hi + lo with
-// hi = rne(xl), lo = rne(xl - hi); zero in the padding.
+// xl = sum over splits of part (in split order), split into a 16-bit hi + lo
+// (bf16, or fp16 with H) with hi = rne(xl), lo = rne(xl - hi); zero in the
+// padding.
+template <bool H>
 __global__ __launch_bounds__(256) void reduce_split_kernel(const float* __restrict__ part, int splits, int64_t T,
                                                            int64_t r, int64_t rpad, int64_t Tpad,
                                                            uint16_t* __restrict__ xlh, uint16_t* __restrict__ xll) {
@@ -232,14 +238,14 @@ __global__ __launch_bounds__(256) void reduce_split_kernel(const float* __restri
 #pragma unroll 8
     for (int s = 0; s < splits; ++s) x += part[((int64_t)s * T + t) * r + j];
   }
-  const uint16_t hi = f32_to_bf16_bits(x);
+  const uint16_t hi = Fmt16<H>::from_f32(x);
   xlh[i] = hi;
-  xll[i] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+  xll[i] = Fmt16<H>::from_f32(x - Fmt16<H>::to_f32(hi));
 }
 
 // ------------------------------------------------------------------ standalone up-projection
 // Y[t][m] += (X . L)[t] . R[:, m] over one 256 x 256 output tile.
-template <class G, typename O>
+template <class G, typename O, bool H>
 __global__ __launch_bounds__(G::THREADS, 1) void lowrank_up_add_kernel(const uint16_t* __restrict__ rt,
                                                                        const uint16_t* __restrict__ xlh,
                                                                        const uint16_t* __restrict__ xll, int rpad,
@@ -252,13 +258,22 @@ __global__ __launch_bounds__(G::THREADS, 1) void lowrank_up_add_kernel(const uin
   const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
   f32x16 acc[G::FM][G::FT];
   load_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
-  adapter_mma<G>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
+  adapter_mma<G, H>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
   store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
 }
 
 typedef Geo<256, 256, 3, 2, 4> GeoUp;
 
 unsigned blocks_for(int64_t n) { return (unsigned)cdiv(n, 256); }
+
+void reduce_split(const LowrankWs& w, int64_t T, int64_t r, hipStream_t s) {
+  if (w.h16)
+    reduce_split_kernel<true><<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad,
+                                                                        w.xlh, w.xll);
+  else
+    reduce_split_kernel<false><<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad,
+                                                                         w.xlh, w.xll);
+}
 
 }  // namespace
 
@@ -283,20 +298,20 @@ LowrankWs lowrank_layout(Dt in, void* ws, int64_t T, int64_t K, int64_t r, int64
   w.Kpad = z.Kpad;
   w.Npad = z.Npad;
   w.kc = z.kc;
-  w.mfma = in == Dt::BF16 && K % 8 == 0 && r <= kRankMax;
+  w.mfma = in != Dt::F32 && K % 8 == 0 && r <= kRankMax;
+  w.h16 = in == Dt::F16;
   return w;
 }
 
 hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const void* R, int64_t T, int64_t K,
                                   int64_t r, int64_t N, const LowrankWs& w, hipStream_t s) {
   if (!w.mfma) return launch_lowrank_down_generic(in, X, L, T, K, r, w.splits, w.kc, w.part, s);
-  // bf16: transposed L and R, the split down-projection, the hi/lo reduction
+  // 16-bit inputs: transposed L and R, the split down-projection, the hi/lo reduction
   transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
   transpose_r_kernel<<<blocks_for(w.Npad * w.rpad / 8), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
   const hipError_t ed = launch_down((const uint16_t*)X, w.lt, T, K, r, w, s);
   if (ed != hipSuccess) return ed;
-  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
-                                                                  w.xll);
+  reduce_split(w, T, r, s);
   return hipGetLastError();
 }
 
@@ -306,8 +321,7 @@ hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, i
   transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
   const hipError_t ed = launch_down((const uint16_t*)X, w.lt, T, K, r, w, s);
   if (ed != hipSuccess) return ed;
-  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
-                                                                  w.xll);
+  reduce_split(w, T, r, s);
   return hipGetLastError();
 }
 
@@ -319,8 +333,7 @@ hipError_t launch_lowrank_prepare_bwd(const void* dY, const void* L, const void*
   pad_copy_kernel<<<blocks_for(w.Npad * w.rpad), 256, 0, s>>>((const uint16_t*)L, K, r, w.Npad, w.rpad, w.rt);
   const hipError_t ed = launch_down((const uint16_t*)dY, w.lt, T, N, r, w, s);
   if (ed != hipSuccess) return ed;
-  reduce_split_kernel<<<blocks_for(w.Tpad * w.rpad), 256, 0, s>>>(w.part, w.splits, T, r, w.rpad, w.Tpad, w.xlh,
-                                                                  w.xll);
+  reduce_split(w, T, r, s);
   return hipGetLastError();
 }
 
@@ -335,11 +348,17 @@ hipError_t launch_lowrank_up_add(Dt in, Dt out, const LowrankWs& w, const void* 
   typedef GeoUp G;
   const int64_t nb = cdiv(N, G::BM) * cdiv(T, G::BT);
   if (out == Dt::BF16)
-    lowrank_up_add_kernel<G, uint16_t><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad, (int)T,
-                                                                          (int)N, (uint16_t*)Y);
+    lowrank_up_add_kernel<G, uint16_t, false><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad,
+                                                                                 (int)T, (int)N, (uint16_t*)Y);
+  else if (out == Dt::F16)
+    lowrank_up_add_kernel<G, _Float16, true><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad,
+                                                                                (int)T, (int)N, (_Float16*)Y);
+  else if (w.h16)
+    lowrank_up_add_kernel<G, float, true><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad,
+                                                                             (int)T, (int)N, (float*)Y);
   else
-    lowrank_up_add_kernel<G, float><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad, (int)T,
-                                                                       (int)N, (float*)Y);
+    lowrank_up_add_kernel<G, float, false><<<(unsigned)nb, G::THREADS, 0, s>>>(w.rt, w.xlh, w.xll, (int)w.rpad,
+                                                                              (int)T, (int)N, (float*)Y);
   return hipGetLastError();
 }
 

@@ -7,7 +7,8 @@
 // most 128), so they share one kernel: out^T[c][j] = sum_t A[t][c] B[t][j]
 // with A the large operand (dY or X) in token-chunk form (pack_tokens: one
 // 64-byte row of 32 tokens per column c) and B the small one (X . L or
-// dY . R^T) as a transposed bf16 hi/lo pair [rpad32][Tpad].  Each block takes
+// dY . R^T) as a transposed 16-bit hi/lo pair [rpad32][Tpad] (the operands'
+// format: bf16, or fp16 with H).  Each block takes
 // one 256-column chunk column over a range of token chunks (B's slice staged
 // in LDS once per chunk for the block's four waves); the fp32 partial
 // sums are added in range order by a second kernel, which also writes the
@@ -28,7 +29,7 @@ constexpr int kChunkRows = 256, kChunkTokens = 32, kChunkBytes = kChunkRows * kC
 // from memory; the block stages each chunk's slice of B (FJ*32 rows x 32
 // tokens, hi and lo) in LDS once, in a double buffer, with 16-byte granule g
 // of row j at g ^ ((j/4) % 4) so that fragment reads are free of conflicts.
-template <int FJ>
+template <int FJ, bool H>
 __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __restrict__ chunks, int64_t Tch,
                                                                int per_split, const uint16_t* __restrict__ bh,
                                                                const uint16_t* __restrict__ bl, int64_t Tpad,
@@ -77,11 +78,11 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
 
   for (int64_t s = s0; s < s1; ++s) {
     const uint32_t c = (uint32_t)(s - s0) * kChunkBytes;
-    bf16x8 a[2][2];
+    typename Fmt16<H>::v8 a[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) a[ks][fm] = __builtin_bit_cast(bf16x8, load16(ra, c + a_off[fm][ks]));
+      for (int fm = 0; fm < 2; ++fm) a[ks][fm] = __builtin_bit_cast(typename Fmt16<H>::v8, load16(ra, c + a_off[fm][ks]));
     char* buf = bs[s & 1];
     const uint32_t tb = (uint32_t)(s * kChunkTokens) * 2;
 #pragma unroll
@@ -92,18 +93,18 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
     __syncthreads();                                   // slice s staged; slice s-2's buffer no longer read
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 h[FJ], l[FJ];
+      typename Fmt16<H>::v8 h[FJ], l[FJ];
 #pragma unroll
       for (int fj = 0; fj < FJ; ++fj) {
-        h[fj] = *reinterpret_cast<const bf16x8*>(buf + b_off[ks][fj]);
-        l[fj] = *reinterpret_cast<const bf16x8*>(buf + BROWS * 64 + b_off[ks][fj]);
+        h[fj] = *reinterpret_cast<const typename Fmt16<H>::v8*>(buf + b_off[ks][fj]);
+        l[fj] = *reinterpret_cast<const typename Fmt16<H>::v8*>(buf + BROWS * 64 + b_off[ks][fj]);
       }
 #pragma unroll
       for (int fj = 0; fj < FJ; ++fj)
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm) {
-          acc[fm][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][fm], h[fj], acc[fm][fj], 0, 0, 0);
-          acc[fm][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][fm], l[fj], acc[fm][fj], 0, 0, 0);
+          acc[fm][fj] = Fmt16<H>::mfma32x32x16(a[ks][fm], h[fj], acc[fm][fj]);
+          acc[fm][fj] = Fmt16<H>::mfma32x32x16(a[ks][fm], l[fj], acc[fm][fj]);
         }
     }
   }
@@ -151,10 +152,23 @@ int64_t split_count(int64_t tiles, int64_t Tch, int64_t brows) {
 }
 
 template <int FJ>
-void launch_partial(const char* chunks, int64_t tiles, int64_t Tch, int per, int64_t splits, const uint16_t* bh,
-                    const uint16_t* bl, int64_t Tpad, int64_t Cpad, float* part, hipStream_t s) {
-  lr_wgrad_partial_kernel<FJ><<<dim3((unsigned)tiles, (unsigned)splits), 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad,
-                                                                                       Cpad, part);
+void launch_partial(bool h16, const char* chunks, int64_t tiles, int64_t Tch, int per, int64_t splits,
+                    const uint16_t* bh, const uint16_t* bl, int64_t Tpad, int64_t Cpad, float* part, hipStream_t s) {
+  const dim3 grid((unsigned)tiles, (unsigned)splits);
+  if (h16)
+    lr_wgrad_partial_kernel<FJ, true><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+  else
+    lr_wgrad_partial_kernel<FJ, false><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+}
+
+template <typename O>
+void launch_reduce(const float* part, int sp, int r, int rows, int64_t C, int64_t Cpad, int accumulate, bool trans,
+                   void* dst, hipStream_t s) {
+  const unsigned rb = (unsigned)cdiv((int64_t)r * C, 256);
+  if (trans)
+    lr_wgrad_reduce_kernel<O, true><<<rb, 256, 0, s>>>(part, sp, r, rows, C, Cpad, accumulate, (O*)dst);
+  else
+    lr_wgrad_reduce_kernel<O, false><<<rb, 256, 0, s>>>(part, sp, r, rows, C, Cpad, accumulate, (O*)dst);
 }
 
 }  // namespace
@@ -165,7 +179,7 @@ int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r) {
   return cdiv(splits * cdiv(r, 32) * 32 * tiles * kChunkRows * 4, 256) * 256;
 }
 
-hipError_t launch_lr_wgrad(Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
+hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
                            const uint16_t* bl, int64_t Tpad, float* part, void* dst, bool trans, int accumulate,
                            hipStream_t s) {
   if (C == 0 || r == 0) return hipSuccess;
@@ -173,28 +187,27 @@ hipError_t launch_lr_wgrad(Dt out, const void* chunks, int64_t T, int64_t C, int
   const int64_t per = Tch ? cdiv(Tch, split_count(tiles, Tch, cdiv(r, 32) * 32)) : 1, splits = Tch ? cdiv(Tch, per) : 1;
   const int fj = (int)cdiv(r, 32);
   const char* ch = (const char*)chunks;
+  const bool h16 = in == Dt::F16;
   if (Tch == 0) {
     // no tokens: the sums are empty (one split of zeros, cleared by a kernel)
     hipError_t e = launch_fill_zero(Dt::F32, part, (int64_t)fj * 32 * Cpad, s);
     if (e != hipSuccess) return e;
   } else if (fj == 1) {
-    launch_partial<1>(ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
+    launch_partial<1>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
   } else if (fj == 2) {
-    launch_partial<2>(ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
+    launch_partial<2>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
   } else if (fj == 3) {
-    launch_partial<3>(ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
+    launch_partial<3>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
   } else {
-    launch_partial<4>(ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
+    launch_partial<4>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
   }
-  const unsigned rb = (unsigned)cdiv(r * C, 256);
   const int sp = Tch ? (int)splits : 1;
-  if (out == Dt::BF16) {
-    if (trans) lr_wgrad_reduce_kernel<uint16_t, true><<<rb, 256, 0, s>>>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, (uint16_t*)dst);
-    else lr_wgrad_reduce_kernel<uint16_t, false><<<rb, 256, 0, s>>>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, (uint16_t*)dst);
-  } else {
-    if (trans) lr_wgrad_reduce_kernel<float, true><<<rb, 256, 0, s>>>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, (float*)dst);
-    else lr_wgrad_reduce_kernel<float, false><<<rb, 256, 0, s>>>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, (float*)dst);
-  }
+  if (out == Dt::BF16)
+    launch_reduce<uint16_t>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
+  else if (out == Dt::F16)
+    launch_reduce<_Float16>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
+  else
+    launch_reduce<float>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
   return hipGetLastError();
 }
 

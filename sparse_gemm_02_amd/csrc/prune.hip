@@ -18,6 +18,7 @@ constexpr int kThreads = 256;
 
 template <typename E> struct Vec4;                       // one group of four raw values
 template <> struct Vec4<uint16_t> { typedef u32x2 T; };  // 8 bytes
+template <> struct Vec4<_Float16> { typedef u32x2 T; };
 template <> struct Vec4<uint32_t> { typedef u32x4 T; };  // 16 bytes
 
 __device__ __forceinline__ void unpack(u32x2 v, uint16_t e[4]) {
@@ -25,10 +26,22 @@ __device__ __forceinline__ void unpack(u32x2 v, uint16_t e[4]) {
   e[2] = (uint16_t)(v[1] & 0xFFFF); e[3] = (uint16_t)(v[1] >> 16);
 }
 __device__ __forceinline__ void unpack(u32x4 v, uint32_t e[4]) { e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3]; }
+__device__ __forceinline__ void unpack(u32x2 v, _Float16 e[4]) {
+  uint16_t b[4];
+  unpack(v, b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = __builtin_bit_cast(_Float16, b[i]);
+}
 __device__ __forceinline__ u32x2 pack(const uint16_t e[4]) {
   u32x2 v; v[0] = e[0] | ((uint32_t)e[1] << 16); v[1] = e[2] | ((uint32_t)e[3] << 16); return v;
 }
 __device__ __forceinline__ u32x4 pack(const uint32_t e[4]) { u32x4 v; v[0] = e[0]; v[1] = e[1]; v[2] = e[2]; v[3] = e[3]; return v; }
+__device__ __forceinline__ u32x2 pack(const _Float16 e[4]) {
+  uint16_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(uint16_t, e[i]);
+  return pack(b);
+}
 
 // ------------------------------------------------------------------ prune24
 // One group of four per thread and iteration; groups never straddle rows
@@ -205,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restr
   }
 }
 
-// Wide-access variant for bf16 with K % 16 == 0 and N % 16 == 0.  Block tile:
-// 128 rows n x 128 columns k.  Phase 1: eight lanes per row read one 128-byte
+// Wide-access variant for 16-bit values (bf16; fp16 with H) with K % 16 == 0
+// and N % 16 == 0.  Block tile: 128 rows n x 128 columns k.  Phase 1: eight lanes per row read one 128-byte
 // line of compressed values and the matching metadata words, decompress four
 // groups each with selects and write 32 bytes of the dense row to LDS.  Phase
 // 2: thread (column pair cp, quarter q) reads rows 32q .. 32q+31 of columns
@@ -223,7 +236,7 @@ constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit 
 // loads (gradient GT, fp32 moments m and v at the same element index), writes
 // the new values and moments back in place and double-prunes the new values:
 // the optimizer's pass over the weight and the double prune share one read.
-template <bool UPD, typename GT>
+template <bool UPD, typename GT, bool H = false>
 __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* vals, const uint32_t* __restrict__ meta,
                                                                     int64_t N, int64_t K,
                                                                     uint16_t* __restrict__ out_vals,
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
       w4 = *reinterpret_cast<const u32x4*>(vals + e);
       nibs = meta[row * in_wpr + (kc >> 5)] >> (16 * (c & 1));
       if constexpr (UPD) {
-        w4 = adamw8_bf16(w4, grads + e, m + e, v + e, hp);
+        w4 = adamw8_16<H>(w4, grads + e, m + e, v + e, hp);
         *reinterpret_cast<u32x4*>(vals + e) = w4;
       }
     }
@@ -290,7 +303,10 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
       uint16_t e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = (uint16_t)(col[4 * g + j] >> (16 * h));
-      const uint32_t keep = top2_of_4(mag_key(e[0]), mag_key(e[1]), mag_key(e[2]), mag_key(e[3]));
+      uint32_t k4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k4[j] = H ? mag_key(__builtin_bit_cast(_Float16, e[j])) : mag_key(e[j]);
+      const uint32_t keep = top2_of_4(k4[0], k4[1], k4[2], k4[3]);
       const uint32_t nib = pair_nibble(keep);
       word |= nib << (4 * g);
       const uint32_t i0 = nib & 3u, i1 = nib >> 2;
@@ -328,6 +344,8 @@ hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint
   const int grid = grid_for(groups, kThreads * U);
   if (dt == Dt::BF16)
     prune24_kernel<uint16_t, U><<<grid, kThreads, 0, s>>>((const uint16_t*)W, groups, (uint32_t*)mask, (uint16_t*)W_s);
+  else if (dt == Dt::F16)
+    prune24_kernel<_Float16, U><<<grid, kThreads, 0, s>>>((const _Float16*)W, groups, (uint32_t*)mask, (_Float16*)W_s);
   else
     prune24_kernel<uint32_t, U><<<grid, kThreads, 0, s>>>((const uint32_t*)W, groups, (uint32_t*)mask, (uint32_t*)W_s);
   return hipGetLastError();
@@ -340,6 +358,8 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
   const int grid = grid_for(slots, kThreads);
   if (dt == Dt::BF16)
     compress24_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)W, mask, rows, cols, (uint16_t*)values, meta, invalid);
+  else if (dt == Dt::F16)
+    compress24_kernel<_Float16><<<grid, kThreads, 0, s>>>((const _Float16*)W, mask, rows, cols, (_Float16*)values, meta, invalid);
   else
     compress24_kernel<uint32_t><<<grid, kThreads, 0, s>>>((const uint32_t*)W, mask, rows, cols, (uint32_t*)values, meta, invalid);
   return hipGetLastError();
@@ -348,16 +368,23 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
   if (N == 0 || K == 0) return hipSuccess;
-  if (dt == Dt::BF16 && K % 16 == 0 && N % 16 == 0) {
+  if (dt != Dt::F32 && K % 16 == 0 && N % 16 == 0) {
     dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
-    double_prune_wide_kernel<false, uint16_t><<<g, kThreads, 0, s>>>(
-        const_cast<uint16_t*>((const uint16_t*)values_s), meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT,
-        nullptr, nullptr, nullptr, AdamWStep{});
+    uint16_t* vin = const_cast<uint16_t*>((const uint16_t*)values_s);
+    if (dt == Dt::BF16)
+      double_prune_wide_kernel<false, uint16_t, false><<<g, kThreads, 0, s>>>(
+          vin, meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT, nullptr, nullptr, nullptr, AdamWStep{});
+    else
+      double_prune_wide_kernel<false, uint16_t, true><<<g, kThreads, 0, s>>>(
+          vin, meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT, nullptr, nullptr, nullptr, AdamWStep{});
     return hipGetLastError();
   }
   dim3 grid((unsigned)cdiv(K, DP_TK), (unsigned)cdiv(N, DP_TN));
   if (dt == Dt::BF16)
     double_prune_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,
+                                                            meta_dpT, mask_dpT);
+  else if (dt == Dt::F16)
+    double_prune_kernel<_Float16><<<grid, kThreads, 0, s>>>((const _Float16*)values_s, meta_s, N, K, (_Float16*)values_dpT,
                                                             meta_dpT, mask_dpT);
   else
     double_prune_kernel<uint32_t><<<grid, kThreads, 0, s>>>((const uint32_t*)values_s, meta_s, N, K, (uint32_t*)values_dpT,

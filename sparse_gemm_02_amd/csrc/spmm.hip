@@ -65,7 +65,7 @@ namespace {
 // PK: the sparse operand comes as tile chunks (see pack_sparse_kernel): each
 // stage loads one contiguous 18 KB chunk (values then metadata) instead of 256
 // separate 64-byte row pieces and a strided metadata read.
-template <class G, bool ADAPTER, typename O, bool PK>
+template <class G, bool ADAPTER, typename O, bool PK, bool H = false>
 __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
     int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   }
 
   struct Frags {
-    bf16x8 a[G::FM];
+    typename Fmt16<H>::v8 a[G::FM];
     int ix[G::FM];
-    bf16x16 b[G::FT];
+    typename Fmt16<H>::v16 b[G::FT];
   };
   auto read_frags = [&](Frags& f, int s, int ks) {
     const char* base = lds + (s % G::NST) * SLOT;
@@ -173,13 +173,13 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
                            : meta_lds + ((s >> 1) & 1) * G::META_SLOT + ((s & 1) * 2 + ks) * 4;
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm) {
-      f.a[fm] = *reinterpret_cast<const bf16x8*>(base + a_off[ks][fm]);
+      f.a[fm] = *reinterpret_cast<const typename Fmt16<H>::v8*>(base + a_off[ks][fm]);
       f.ix[fm] = (int)*reinterpret_cast<const uint16_t*>(mbase + m_off[fm]);
     }
 #pragma unroll
     for (int ft = 0; ft < G::FT; ++ft) {
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(base + b_off[ks][ft][0]);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(base + b_off[ks][ft][1]);
+      const typename Fmt16<H>::v8 lo = *reinterpret_cast<const typename Fmt16<H>::v8*>(base + b_off[ks][ft][0]);
+      const typename Fmt16<H>::v8 hi = *reinterpret_cast<const typename Fmt16<H>::v8*>(base + b_off[ks][ft][1]);
       f.b[ft] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
   };
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   auto mma_col = [&](const Frags& f, int ft) {
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm)
-      acc[fm][ft] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm], 0, 0);
+      acc[fm][ft] = Fmt16<H>::smfmac32x32x32(f.a[fm], f.b[ft], acc[fm][ft], f.ix[fm]);
   };
   auto mma = [&](const Frags& f) {
 #pragma unroll
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     for (int ft = 1; ft < G::FT; ++ft) mma_col(f1, ft);
   }
   wait_vmcnt<0>();
-  if constexpr (ADAPTER) adapter_mma<G>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
+  if constexpr (ADAPTER) adapter_mma<G, H>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
   store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
 }
 
@@ -266,11 +266,11 @@ __global__ __launch_bounds__(256) void pack_sparse_kernel(const uint16_t* __rest
   }
 }
 
-template <bool ADAPTER, typename O, bool PK>
+template <bool ADAPTER, typename O, bool PK, bool H>
 hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
                       const LowrankWs* w, O* Y, hipStream_t s) {
   typedef GeoBig G;
-  auto kern = spmm_smfmac_kernel<G, ADAPTER, O, PK>;
+  auto kern = spmm_smfmac_kernel<G, ADAPTER, O, PK, H>;
   constexpr int lds_bytes = PK ? G::PLDS_BYTES : G::LDS_BYTES;
   // once per process (thread-safe static initialisation)
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
@@ -282,17 +282,24 @@ hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, 
   return hipGetLastError();
 }
 
+template <bool PK, bool H, typename O>
+hipError_t dispatch_ad(const uint16_t* B, int64_t T, int64_t Kred, const uint16_t* vals, const uint32_t* meta,
+                       int64_t M, const LowrankWs* ws, O* Y, hipStream_t s) {
+  return ws ? launch_big<true, O, PK, H>(B, (int)T, (int)Kred, vals, meta, (int)M, ws, Y, s)
+            : launch_big<false, O, PK, H>(B, (int)T, (int)Kred, vals, meta, (int)M, nullptr, Y, s);
+}
+
+// in: BF16 or F16 (raw 16-bit operands); out: the input format or F32
 template <bool PK>
-hipError_t dispatch_big(Dt out, const void* B, int64_t T, int64_t Kred, const void* values, const uint32_t* meta,
-                        int64_t M, const LowrankWs* ws, void* Y, hipStream_t s) {
+hipError_t dispatch_big(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
+                        const uint32_t* meta, int64_t M, const LowrankWs* ws, void* Y, hipStream_t s) {
   const uint16_t* Bb = (const uint16_t*)B;
   const uint16_t* vb = (const uint16_t*)values;
-  const bool ad = ws != nullptr;
-  if (out == Dt::BF16)
-    return ad ? launch_big<true, uint16_t, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (uint16_t*)Y, s)
-              : launch_big<false, uint16_t, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (uint16_t*)Y, s);
-  return ad ? launch_big<true, float, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, ws, (float*)Y, s)
-            : launch_big<false, float, PK>(Bb, (int)T, (int)Kred, vb, meta, (int)M, nullptr, (float*)Y, s);
+  if (in == Dt::F16)
+    return out == Dt::F16 ? dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (_Float16*)Y, s)
+                          : dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, s);
+  return out == Dt::BF16 ? dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (uint16_t*)Y, s)
+                         : dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, s);
 }
 
 }  // namespace
@@ -301,12 +308,12 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
                        const uint32_t* meta, int64_t M, const LowrankWs* ws, int64_t r, const void* R, void* Y,
                        hipStream_t s) {
   // block resources stay below 2 GiB: 256 rows x Kred x 2 bytes
-  const bool fast = in == Dt::BF16 && Kred % 16 == 0 && M % 4 == 0 && Kred <= (1 << 21);
+  const bool fast = in != Dt::F32 && Kred % 16 == 0 && M % 4 == 0 && Kred <= (1 << 21);
   const bool ad = ws != nullptr && r > 0;
   if (!fast || (ad && !ws->mfma))
     return launch_spmm_generic(in, out, B, T, Kred, values, meta, M, ad ? ws->part : nullptr, ad ? ws->splits : 1,
                                ad ? r : 0, R, Y, s);
-  return dispatch_big<false>(out, B, T, Kred, values, meta, M, ad ? ws : nullptr, Y, s);
+  return dispatch_big<false>(in, out, B, T, Kred, values, meta, M, ad ? ws : nullptr, Y, s);
 }
 
 int64_t packed_sparse_bytes(int64_t M, int64_t Kred) {
@@ -322,9 +329,9 @@ hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_spmm_packed(Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
+hipError_t launch_spmm_packed(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
                               const LowrankWs* ws, void* Y, hipStream_t s) {
-  return dispatch_big<true>(out, B, T, Kred, packed, nullptr, M, ws, Y, s);
+  return dispatch_big<true>(in, out, B, T, Kred, packed, nullptr, M, ws, Y, s);
 }
 
 }  // namespace slope

@@ -50,24 +50,32 @@ struct WGeo {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Two adjacent outputs as one store (4-byte aligned for bf16, 8-byte for fp32).
-__device__ __forceinline__ void store_pair(uint16_t* p, float a, float b) {
-  *reinterpret_cast<uint32_t*>(p) = f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+// 16-bit output patterns back to fp32 (bf16 for uint16_t outputs, fp16 for _Float16).
+template <typename O> __device__ __forceinline__ float out16_to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float out16_to_f32<uint16_t>(uint32_t b) { return bf16_bits_to_f32((uint16_t)b); }
+template <> __device__ __forceinline__ float out16_to_f32<_Float16>(uint32_t b) { return f16_bits_to_f32((uint16_t)b); }
+
+// Two adjacent outputs as one store (4-byte aligned for 16-bit outputs, 8-byte for fp32).
+template <typename O>
+__device__ __forceinline__ void store_pair(O* p, float a, float b) {
+  if constexpr (sizeof(O) == 2) {
+    *reinterpret_cast<uint32_t*>(p) = out16_bits<O>(a) | ((uint32_t)out16_bits<O>(b) << 16);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  }
 }
-__device__ __forceinline__ void store_pair(float* p, float a, float b) {
-  *reinterpret_cast<float2*>(p) = make_float2(a, b);
-}
-// Four adjacent outputs (8-byte aligned for bf16, 16-byte for fp32), optionally accumulated.
-__device__ __forceinline__ void store_quad(uint16_t* p, const float (&x)[4], int accumulate) {
+// Four adjacent outputs (8-byte aligned for 16-bit outputs, 16-byte for fp32), optionally accumulated.
+template <typename O>
+__device__ __forceinline__ void store_quad(O* p, const float (&x)[4], int accumulate) {
   float y[4] = {x[0], x[1], x[2], x[3]};
   if (accumulate) {
     const u32x2 o = *reinterpret_cast<const u32x2*>(p);
-    y[0] += bf16_bits_to_f32(o[0] & 0xFFFF); y[1] += bf16_bits_to_f32(o[0] >> 16);
-    y[2] += bf16_bits_to_f32(o[1] & 0xFFFF); y[3] += bf16_bits_to_f32(o[1] >> 16);
+    y[0] += out16_to_f32<O>(o[0] & 0xFFFF); y[1] += out16_to_f32<O>(o[0] >> 16);
+    y[2] += out16_to_f32<O>(o[1] & 0xFFFF); y[3] += out16_to_f32<O>(o[1] >> 16);
   }
   u32x2 w;
-  w[0] = f32_to_bf16_bits(y[0]) | ((uint32_t)f32_to_bf16_bits(y[1]) << 16);
-  w[1] = f32_to_bf16_bits(y[2]) | ((uint32_t)f32_to_bf16_bits(y[3]) << 16);
+  w[0] = out16_bits<O>(y[0]) | ((uint32_t)out16_bits<O>(y[1]) << 16);
+  w[1] = out16_bits<O>(y[2]) | ((uint32_t)out16_bits<O>(y[3]) << 16);
   *reinterpret_cast<u32x2*>(p) = w;
 }
 __device__ __forceinline__ void store_quad(float* p, const float (&x)[4], int accumulate) {
@@ -81,7 +89,8 @@ __device__ __forceinline__ void store_quad(float* p, const float (&x)[4], int ac
 // are 512 bytes; row r keeps its 16-byte granule q at q ^ ((r & 3) << 2), which
 // puts the four rows a 32-lane pass of the transposing load touches in four
 // different 64-byte bank groups.
-__device__ __forceinline__ bf16x8 frag_tr(const char* tile, int tb, int c0, int lane) {
+template <bool H>
+__device__ __forceinline__ typename Fmt16<H>::v8 frag_tr(const char* tile, int tb, int c0, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int col = c0 + 16 * (g & 1) + 4 * (j & 3);      // element column of this lane's 4 values
   const int t = tb + 8 * (g >> 1) + (j >> 2);
@@ -92,7 +101,7 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int tb, int c0, int 
   s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(typename Fmt16<H>::v8, v);
 }
 
 // Epilogue of both weight-gradient kernels: lane l of accumulator [a][b] holds
@@ -143,7 +152,7 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], c
 // is refilled as soon as every wave holds its fragments, so NST-1 stages stay
 // in flight).  Columns past
 // K or N and tokens past T read as 0.
-template <class G, typename O>
+template <class G, typename O, bool H>
 __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_t* __restrict__ dY,
                                                                  const uint16_t* __restrict__ X, int T, int N, int K,
                                                                  const uint32_t* __restrict__ meta,
@@ -193,15 +202,15 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
   };
 
   struct Frags {
-    bf16x8 x[G::FK];
-    bf16x8 d[G::FN];
+    typename Fmt16<H>::v8 x[G::FK];
+    typename Fmt16<H>::v8 d[G::FN];
   };
   auto read_frags = [&](Frags& f, int s, int sub) {
     const char* base = lds + (s % G::NST) * G::STAGE_BYTES;
 #pragma unroll
-    for (int a = 0; a < G::FK; ++a) f.x[a] = frag_tr(base, 16 * sub, wk * G::WK + a * 32, lane);
+    for (int a = 0; a < G::FK; ++a) f.x[a] = frag_tr<H>(base, 16 * sub, wk * G::WK + a * 32, lane);
 #pragma unroll
-    for (int b = 0; b < G::FN; ++b) f.d[b] = frag_tr(base + G::X_BYTES, 16 * sub, wn * G::WN + b * 32, lane);
+    for (int b = 0; b < G::FN; ++b) f.d[b] = frag_tr<H>(base + G::X_BYTES, 16 * sub, wn * G::WN + b * 32, lane);
   };
 
   f32x16 acc[G::FK][G::FN];
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
     for (int b = 0; b < G::FN; ++b)
 #pragma unroll
       for (int a = 0; a < G::FK; ++a)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], f.d[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = Fmt16<H>::mfma32x32x16(f.x[a], f.d[b], acc[a][b]);
   };
 
 #pragma unroll
@@ -315,7 +324,7 @@ struct DGeo {
   static_assert(NST >= 2 && PD >= 1, "pipeline depth");
 };
 
-template <class G, typename O>
+template <class G, typename O, bool H>
 __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint16_t* __restrict__ dp,
                                                                    const uint16_t* __restrict__ xp, int T, int N,
                                                                    int K, const uint32_t* __restrict__ meta,
@@ -358,22 +367,22 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
   }
 
   struct DFrags {
-    bf16x8 d[2][G::FN];
+    typename Fmt16<H>::v8 d[2][G::FN];
   };
   auto load_d = [&](DFrags& f, int s) {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(ds + (int64_t)s * kChunkElems, s < stages ? G::CHUNK_BYTES : 0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int b = 0; b < G::FN; ++b) f.d[ks][b] = __builtin_bit_cast(bf16x8, load16(rd, d_off[ks][b]));
+      for (int b = 0; b < G::FN; ++b) f.d[ks][b] = __builtin_bit_cast(typename Fmt16<H>::v8, load16(rd, d_off[ks][b]));
   };
   struct XFrags {
-    bf16x8 x[G::FK];
+    typename Fmt16<H>::v8 x[G::FK];
   };
   auto read_x = [&](XFrags& f, int s, int ks) {
     const char* base = lds + (s % G::NST) * G::CHUNK_BYTES;
 #pragma unroll
-    for (int a = 0; a < G::FK; ++a) f.x[a] = *reinterpret_cast<const bf16x8*>(base + x_off[ks][a]);
+    for (int a = 0; a < G::FK; ++a) f.x[a] = *reinterpret_cast<const typename Fmt16<H>::v8*>(base + x_off[ks][a]);
   };
 
   f32x16 acc[G::FK][G::FN];
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
     for (int b = 0; b < G::FN; ++b)
 #pragma unroll
       for (int a = 0; a < G::FK; ++a)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[a], d.d[ks][b], acc[a][b], 0, 0, 0);
+        acc[a][b] = Fmt16<H>::mfma32x32x16(f.x[a], d.d[ks][b], acc[a][b]);
   };
 
   DFrags ring[G::RING];
@@ -442,11 +451,11 @@ hipError_t launch_pack(const uint16_t* src, int64_t T, int64_t C, uint16_t* dst,
   return hipGetLastError();
 }
 
-template <typename O>
+template <typename O, bool H>
 hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int64_t N, int64_t K,
                          const uint32_t* meta, O* dWv, O* dWd, int accumulate, hipStream_t s) {
   typedef DGeoBig G;
-  auto kern = wgrad_direct_kernel<G, O>;
+  auto kern = wgrad_direct_kernel<G, O, H>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const int64_t nb = chunks_of(K) * chunks_of(N);
@@ -455,6 +464,19 @@ hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int6
 }
 
 typedef WGeo<256, 256, 4, 2, 4> WGeoBig;
+
+template <typename O, bool H>
+hipError_t launch_token_major(const void* dY, const void* X, int64_t T, int64_t N, int64_t K, const uint32_t* meta,
+                              O* dWv, O* dWd, int accumulate, hipStream_t s) {
+  typedef WGeoBig G;
+  const int64_t nb = cdiv(K, G::BK) * cdiv(N, G::BN);
+  auto kern = wgrad_mfma_kernel<G, O, H>;
+  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
+                                                    meta, dWv, dWd, accumulate);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -469,20 +491,26 @@ hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed,
   return launch_pack((const uint16_t*)M, T, C, (uint16_t*)packed, s);
 }
 
-hipError_t launch_masked_wgrad_packed(Dt out, const void* dY_packed, const void* X_packed, int64_t T, int64_t N,
-                                      int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
+hipError_t launch_masked_wgrad_packed(Dt in, Dt out, const void* dY_packed, const void* X_packed, int64_t T,
+                                      int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
                                       int accumulate, hipStream_t s) {
   const uint16_t* dp = (const uint16_t*)dY_packed;
   const uint16_t* xp = (const uint16_t*)X_packed;
   if (out == Dt::BF16)
-    return launch_packed(dp, xp, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense, accumulate, s);
-  return launch_packed(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
+    return launch_packed<uint16_t, false>(dp, xp, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense,
+                                          accumulate, s);
+  if (out == Dt::F16)
+    return launch_packed<_Float16, true>(dp, xp, T, N, K, meta_s, (_Float16*)dW_values, (_Float16*)dW_dense,
+                                         accumulate, s);
+  if (in == Dt::F16)
+    return launch_packed<float, true>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
+  return launch_packed<float, false>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
 }
 
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
                                void* workspace, hipStream_t s) {
-  const bool fast = in == Dt::BF16 && K % 8 == 0 && N % 8 == 0;
+  const bool fast = in != Dt::F32 && K % 8 == 0 && N % 8 == 0;
   if (!fast) return launch_wgrad_generic(in, out, dY, X, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
   if (workspace != nullptr) {
     // packed path: transpose both operands into token chunks, then one GEMM
@@ -492,24 +520,19 @@ hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int
     if (e != hipSuccess) return e;
     e = launch_pack_tokens(dY, T, N, dp, s);
     if (e != hipSuccess) return e;
-    return launch_masked_wgrad_packed(out, dp, xp, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
+    return launch_masked_wgrad_packed(in, out, dp, xp, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
   }
-  typedef WGeoBig G;
-  const int64_t nb = cdiv(K, G::BK) * cdiv(N, G::BN);
-  if (out == Dt::BF16) {
-    auto kern = wgrad_mfma_kernel<G, uint16_t>;
-    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
-                                                      meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense, accumulate);
-  } else {
-    auto kern = wgrad_mfma_kernel<G, float>;
-    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>((const uint16_t*)dY, (const uint16_t*)X, (int)T, (int)N, (int)K,
-                                                      meta_s, (float*)dW_values, (float*)dW_dense, accumulate);
-  }
-  return hipGetLastError();
+  if (out == Dt::BF16)
+    return launch_token_major<uint16_t, false>(dY, X, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense,
+                                               accumulate, s);
+  if (out == Dt::F16)
+    return launch_token_major<_Float16, true>(dY, X, T, N, K, meta_s, (_Float16*)dW_values, (_Float16*)dW_dense,
+                                              accumulate, s);
+  if (in == Dt::F16)
+    return launch_token_major<float, true>(dY, X, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate,
+                                           s);
+  return launch_token_major<float, false>(dY, X, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate,
+                                          s);
 }
 
 }  // namespace slope

@@ -13,14 +13,15 @@ Layer state, per SLoPe (explainer 2.A and 2.B; discussion page, "Memory
 Footprint Reduction During Pretraining and Inference" and "Choice of
 Optimizer"):
 
-    values  [N, K/2] bf16   kept weights of W_s (an nn.Parameter; its .grad is
+    values  [N, K/2]        kept weights of W_s (an nn.Parameter; its .grad is
                             the weight gradient in the same slot order)
     meta    [N, K/32] int32 positions of the kept weights (static mask)
     values_dpT, meta_dpT    the double-pruned transposed weight W_dp^T
     packed_s, packed_dpT    tile-chunk copies of both for the GEMM kernels
     L [K, r], R [r, N]      the adapter (nn.Parameters), when rank > 0
 
-Shapes: bf16 weights with K and N multiples of 16 (the packed operand format).
+Formats: bf16 or fp16 weights and activations (one format per layer), with K
+and N multiples of 16 (the packed operand format).
 """
 from __future__ import annotations
 
@@ -82,7 +83,7 @@ class _SparseLinearFn(torch.autograd.Function):
             slope_pack_tokens(dY, dYp)
             if need_w:
                 dW = torch.empty_like(layer.values)
-                slope_masked_wgrad_packed(dYp, Xp, T, N, K, layer.meta, dW)
+                slope_masked_wgrad_packed(dYp, Xp, T, N, K, layer.meta, dW, in_dtype=X.dtype)
             if need_a:
                 dL, dR = torch.empty_like(L), torch.empty_like(R)
                 wsg = _bytes(slope_lowrank_grads_workspace_bytes(T, K, r, N), X.device)
@@ -93,40 +94,40 @@ class _SparseLinearFn(torch.autograd.Function):
 
 
 class SparseLinear(torch.nn.Module):
-    """2:4 sparse linear layer y = x . W_s^T (+ (x . L) . R), built from a dense
-    bf16 weight [out_features, in_features] on the GPU: magnitude 2:4 pruning
-    along the input dimension (the mask is fixed from then on), compression,
-    the double-pruned transposed copy and the packed operands."""
+    """2:4 sparse linear layer y = x . W_s^T (+ (x . L) . R), built from a
+    dense bf16 or fp16 weight [out_features, in_features] on the GPU: magnitude
+    2:4 pruning along the input dimension (the mask is fixed from then on),
+    compression, the double-pruned transposed copy and the packed operands."""
 
     def __init__(self, weight: torch.Tensor, L: torch.Tensor | None = None, R: torch.Tensor | None = None):
         super().__init__()
-        if weight.dtype != torch.bfloat16 or not weight.is_cuda or weight.dim() != 2:
-            raise ValueError("weight must be a 2-D bfloat16 GPU tensor [out_features, in_features]")
+        if weight.dtype not in (torch.bfloat16, torch.float16) or not weight.is_cuda or weight.dim() != 2:
+            raise ValueError("weight must be a 2-D bfloat16 or float16 GPU tensor [out_features, in_features]")
         N, K = weight.shape
         if K % 16 or N % 16:
             raise ValueError("in_features and out_features must be multiples of 16")
         if (L is None) != (R is None):
             raise ValueError("give both adapter factors L [K, r] and R [r, N], or neither")
-        dev = weight.device
+        dev, dt = weight.device, weight.dtype
         self.in_features, self.out_features = K, N
         weight = weight.contiguous()
         mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
         slope_prune24(weight, mask)
-        values = torch.empty((N, K // 2), dtype=torch.bfloat16, device=dev)
+        values = torch.empty((N, K // 2), dtype=dt, device=dev)
         meta = torch.empty((N, (K // 4 + 7) // 8), dtype=torch.int32, device=dev)
         slope_compress24(weight, mask, values, meta)
         del mask
         self.values = torch.nn.Parameter(values)
         self.register_buffer("meta", meta)
-        self.register_buffer("values_dpT", torch.empty((K, N // 2), dtype=torch.bfloat16, device=dev))
+        self.register_buffer("values_dpT", torch.empty((K, N // 2), dtype=dt, device=dev))
         self.register_buffer("meta_dpT", torch.empty((K, (N // 4 + 7) // 8), dtype=torch.int32, device=dev))
         self.register_buffer("packed_s", _bytes(slope_packed_sparse_bytes(N, K), dev))
         self.register_buffer("packed_dpT", _bytes(slope_packed_sparse_bytes(K, N), dev))
         if L is not None:
             if L.shape[0] != K or R.shape[1] != N or L.shape[1] != R.shape[0]:
                 raise ValueError("adapter shapes must be L [K, r] and R [r, N]")
-            self.L = torch.nn.Parameter(L.detach().to(torch.bfloat16).contiguous())
-            self.R = torch.nn.Parameter(R.detach().to(torch.bfloat16).contiguous())
+            self.L = torch.nn.Parameter(L.detach().to(dt).contiguous())
+            self.R = torch.nn.Parameter(R.detach().to(dt).contiguous())
             self.rank = L.shape[1]
         else:
             self.L = self.R = None
@@ -149,8 +150,8 @@ class SparseLinear(torch.nn.Module):
         slope_pack_sparse(self.values_dpT, self.meta_dpT, K, N, self.packed_dpT)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        if x.shape[-1] != self.in_features or x.dtype != torch.bfloat16:
-            raise ValueError("input must be bfloat16 with in_features columns")
+        if x.shape[-1] != self.in_features or x.dtype != self.values.dtype:
+            raise ValueError("input must have in_features columns and the layer's format")
         lead = x.shape[:-1]
         y = _SparseLinearFn.apply(x.reshape(-1, self.in_features).contiguous(), self.values, self.L, self.R, self)
         return y.reshape(*lead, self.out_features)

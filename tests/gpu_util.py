@@ -16,12 +16,14 @@ def say(*a):
 
 
 def dev(bits: np.ndarray) -> torch.Tensor:
-    """Raw host bits -> device tensor (uint16 -> bfloat16, uint32 -> float32, uint8 stays)."""
+    """Raw host bits -> device tensor (uint16 -> bfloat16, uint32 -> float32, float16 and uint8 stay)."""
     bits = np.ascontiguousarray(bits)
     if bits.dtype == np.uint16:
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
     if bits.dtype == np.uint32:
         return torch.from_numpy(bits.view(np.float32)).to(DEV)
+    if bits.dtype == np.float16:
+        return torch.from_numpy(bits).to(DEV)
     if bits.dtype == np.uint8:
         return torch.from_numpy(bits).to(DEV)
     raise TypeError(bits.dtype)
@@ -32,12 +34,14 @@ def dev_meta(meta: np.ndarray) -> torch.Tensor:
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """Device tensor -> raw host bits (bf16 -> uint16, f32 -> uint32, int32 -> uint32)."""
+    """Device tensor -> raw host bits (bf16 -> uint16, f32 -> uint32, int32 -> uint32; fp16 stays float16)."""
     t = t.detach().to("cpu").contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy().view(np.uint32)
+    if t.dtype == torch.float16:
+        return t.numpy()
     if t.dtype == torch.int32:
         return t.numpy().view(np.uint32)
     if t.dtype == torch.uint8:
@@ -67,11 +71,11 @@ def normwise(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def torch_dtype(dt: str):
-    return torch.bfloat16 if dt == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
 
 
 # tolerances: bf16 outputs with fp32 accumulation, and the fp32 path
-TOL = {"bf16": 1e-2, "f32": 1e-5}
+TOL = {"bf16": 1e-2, "f16": 1e-2, "f32": 1e-5}
 
 
 class Compressed:
@@ -90,16 +94,15 @@ def workspace(T, K, r, N):
 
 
 def spacing(x, fmt):
-    """Distance between neighbouring representable values at |x| (bf16 or fp32)."""
-    mant = 8 if fmt == "bf16" else 24
-    tiny = -133 if fmt == "bf16" else -149
+    """Distance between neighbouring representable values at |x| (bf16, f16 or fp32)."""
+    mant, tiny = {"bf16": (8, -133), "f16": (11, -24), "f32": (24, -149)}[fmt]
     _, e = np.frexp(np.abs(np.asarray(x, np.float64)))
     return np.ldexp(1.0, np.maximum(e - mant, tiny))
 
 
 def check_adamw_update(p0, g, m0, v0, step, hp, p_gpu, m_gpu, v_gpu):
     """Stored values and moments against the oracle, within the derived bound."""
-    fmt = "bf16" if p0.dtype == np.uint16 else "f32"
+    fmt = {np.dtype(np.uint16): "bf16", np.dtype(np.float16): "f16"}.get(np.asarray(p0).dtype, "f32")
     p_ref, m_ref, v_ref = oracle.adamw_compressed(p0, g, m0, v0, step, **hp)
     pe, me, ve = oracle.adamw_update(oracle.widen(p0), oracle.widen(g), m0, v0, step, **hp)
     gw = oracle.widen(g)
@@ -114,7 +117,7 @@ def check_adamw_update(p0, g, m0, v0, step, hp, p_gpu, m_gpu, v_gpu):
     bound = spacing(np.maximum(np.abs(got), np.abs(want)), fmt) + err
     bad = np.abs(got - want) > bound
     assert not bad.any(), (np.flatnonzero(bad)[:5], got[bad][:5], want[bad][:5], pe[bad][:5])
-    if fmt == "bf16":       # the fp32 error is far below a bf16 spacing: nearly every value rounds alike
+    if fmt != "f32":        # the fp32 error is far below a 16-bit spacing: nearly every value rounds alike
         assert (p_gpu == p_ref).mean() >= 0.99
     assert (np.abs(m_gpu.astype(np.float64) - m_ref) <= spacing(m_ref, "f32") + 2.0 ** -20 * m_terms).all()
     assert (np.abs(v_gpu.astype(np.float64) - v_ref) <= spacing(v_ref, "f32") + 2.0 ** -20 * v_terms).all()

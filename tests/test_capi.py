@@ -107,9 +107,9 @@ def test_argument_errors(lib):
     assert lib.slope_pack_tokens(bf, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
     assert lib.slope_pack_tokens(bf, FAKE, 32, 256, FAKE, 1024, None) == -4
     assert lib.slope_pack_tokens(bf, None, 32, 256, FAKE, 1 << 30, None) == -1
-    assert lib.slope_masked_wgrad_packed(bf, FAKE, FAKE, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
-    assert lib.slope_masked_wgrad_packed(bf, FAKE, None, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
-    assert lib.slope_masked_wgrad_packed(7, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, FAKE, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, None, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(7, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
     # sparse tile chunks: bf16 only, cols % 16, enough room; packed products' limits
     assert lib.slope_pack_sparse(f32, FAKE, FAKE, 256, 256, FAKE, 1 << 30, None) == -6
     assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 264, FAKE, 1 << 30, None) == -2
@@ -128,13 +128,13 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
                                         None) == -6
     # adapter weight gradients
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, None, None, FAKE,
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, None, None, FAKE,
                                           1 << 30, FAKE, FAKE, 0, None) == -2
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
                                           16, FAKE, FAKE, 0, None) == -4
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, None, None,
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, None, None,
                                           FAKE, 1 << 30, FAKE, FAKE, 0, None) == -6
-    assert lib.slope_lowrank_grads_packed(bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
                                           1 << 30, FAKE, FAKE, 0, None) == -1
     # few-token forward: T <= 64, bf16, a workspace of the queried size
     assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
@@ -144,6 +144,16 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
+    # fp16: outputs in fp16 or fp32, never bf16; fp32 inputs never give 16-bit outputs
+    h = 2
+    assert lib.slope_spmm_fwd(h, bf, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_spmm_fwd(f32, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_spmm_fwd(bf, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_masked_wgrad_packed(h, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
+    assert lib.slope_masked_wgrad_packed(f32, f32, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
+    assert lib.slope_spmm_fwd_packed(h, h, FAKE, 64, 264, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_prune24(3, FAKE, 4, 4, FAKE, None, None) == -1             # no dtype 3
+    assert lib.slope_pack_tokens(h, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
 
 
 def test_adamw_argument_errors(lib):

@@ -102,6 +102,37 @@ def test_layer_forward_backward_step(T, N, K, r):
         assert abs(acc["canonical_ratio"] - 7.25 / 12) < 1e-12
 
 
+def test_layer_f16_step():
+    """The same cycle in fp16: forward, backward, optimizer step against the oracle."""
+    T, N, K, r = 96, 272, 528, 8
+    d = layer_inputs(K, N, T, r, "f16", seed=8)
+    layer = SparseLinear(dev(d["W"]), dev(d["L"]), dev(d["R"]))
+    assert layer.values.dtype == torch.float16
+    x = dev(d["X"]).clone().requires_grad_(True)
+    y = layer(x)
+    y.backward(dev(d["dY"]))
+    mask_ref, _ = oracle.prune24(d["W"])
+    vs_ref, ms_ref, _ = oracle.compress24(d["W"], mask_ref)
+    vdp_ref, mdp_ref, _ = oracle.double_prune(vs_ref, ms_ref, N, K)
+    tol = TOL["f16"]
+    assert normwise(host_f64(y), oracle.spmm_fwd(d["X"], vs_ref, ms_ref, K, d["L"], d["R"])) <= tol
+    term, dL_ref, dR_ref = oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])
+    assert normwise(host_f64(x.grad), oracle.spmm_bwd_dx(d["dY"], vdp_ref, mdp_ref, N) + term) <= tol
+    assert normwise(host_f64(layer.values.grad), oracle.masked_wgrad(d["dY"], d["X"], ms_ref, K)[0]) <= tol
+    assert normwise(host_f64(layer.L.grad), dL_ref) <= tol and normwise(host_f64(layer.R.grad), dR_ref) <= tol
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-6, weight_decay=0.1)
+    opt = SparseAdamW([layer], lr=hp["lr"], eps=hp["eps"], weight_decay=hp["weight_decay"])
+    g = host(layer.values.grad)
+    opt.step()
+    torch.cuda.synchronize()
+    z = np.zeros(g.shape, np.float32)
+    st = opt.state[layer.values]
+    check_adamw_update(vs_ref, g, z, z, 1, hp, host(layer.values), st["exp_avg"].cpu().numpy(),
+                       st["exp_avg_sq"].cpu().numpy())
+    vdp1, mdp1, _ = oracle.double_prune(host(layer.values), ms_ref, N, K)
+    assert np.array_equal(host(layer.values_dpT), vdp1) and np.array_equal(host(layer.meta_dpT), mdp1)
+
+
 def test_two_layer_mlp_gradients_flow():
     """dX of the second layer is the first layer's output gradient (autograd chains the kernels)."""
     T, D, H = 128, 256, 512
