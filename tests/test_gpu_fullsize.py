@@ -28,7 +28,8 @@ import oracle
 import sparse_gemm_02_amd as S
 from workloads import WORKLOADS, layer_inputs, optimizer_inputs
 
-from gpu_util import TOL, Compressed, check_adamw_update as _check_update, dev, host, host_f64, normwise, say, workspace
+from gpu_util import (TOL, Compressed, check_adamw_update as _check_update, dev, host, host_f64, normwise, say,
+                      torch_dtype, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +45,16 @@ def _gpu():
     yield
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+def _same_bits(a, b):
+    """Bit-for-bit equality (fp16 arrays compared as their 16-bit patterns)."""
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if b.dtype == np.float16:
+        b = b.view(np.uint16)
+    return a.dtype == b.dtype and np.array_equal(a, b)
 
 
 def _group_cols(rng, K, n):
@@ -67,7 +78,7 @@ def _run_path(d, T, N, K, r, tdt):
     S.slope_double_prune(c.values, c.meta, N, K, dp.values, dp.meta)
     Y = torch.empty((T, N), dtype=tdt, device="cuda")
     dX = torch.empty((T, K), dtype=tdt, device="cuda")
-    if tdt == torch.bfloat16:   # the benchmark's form: tile-chunk weights
+    if tdt != torch.float32:   # the benchmark's form: tile-chunk weights
         ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
         pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
         S.slope_pack_sparse(c.values, c.meta, N, K, ps)
@@ -79,7 +90,7 @@ def _run_path(d, T, N, K, r, tdt):
         S.slope_spmm_fwd(X, c.values, c.meta, N, Y, L=L, R=R, workspace=workspace(T, K, r, N))
         S.slope_spmm_bwd_dx(dY, dp.values, dp.meta, K, dX)
     dW = torch.empty((N, K // 2), dtype=tdt, device="cuda")
-    if tdt == torch.bfloat16:   # the benchmark's form: packed operands, then the GEMM
+    if tdt != torch.float32:   # the benchmark's form: packed operands, then the GEMM
         Xp = torch.empty(S.slope_packed_tokens_bytes(T, K), dtype=torch.uint8, device="cuda")
         dYp = torch.empty(S.slope_packed_tokens_bytes(T, N), dtype=torch.uint8, device="cuda")
         S.slope_pack_tokens(X, Xp)
@@ -92,15 +103,28 @@ def _run_path(d, T, N, K, r, tdt):
     return out
 
 
+F16_CASES = [("opt_66b", 0), ("gpt2_small", 2)]
+
+
 @pytest.mark.parametrize("wl,idx", CASES, ids=[f"{w}-{WORKLOADS[w].linears[i].name}" for w, i in CASES])
 def test_full_path_sampled(wl, idx):
+    _full_path_sampled(wl, idx, WORKLOADS[wl].dtype)
+
+
+@pytest.mark.parametrize("wl,idx", F16_CASES, ids=[f"{w}-{WORKLOADS[w].linears[i].name}-f16" for w, i in F16_CASES])
+def test_full_path_sampled_f16(wl, idx):
+    """The same full-size checks on the fp16 instantiation of the path."""
+    _full_path_sampled(wl, idx, "f16")
+
+
+def _full_path_sampled(wl, idx, dtype):
     w = WORKLOADS[wl]
     lin = w.linears[idx]
     T, N, K, r = w.T, lin.N, lin.K, w.r
-    say(f"[fullsize] {wl} {lin.name}: T={T} K={K} N={N} r={r} dtype={w.dtype}")
-    d = layer_inputs(K, N, T, r, w.dtype, seed=0, index=idx)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    tol = TOL[w.dtype]
+    say(f"[fullsize] {wl} {lin.name}: T={T} K={K} N={N} r={r} dtype={dtype}")
+    d = layer_inputs(K, N, T, r, dtype, seed=0, index=idx)
+    tdt = torch_dtype(dtype)
+    tol = TOL[dtype]
     o = _run_path(d, T, N, K, r, tdt)
     rng = np.random.default_rng(1000 + idx)
 
@@ -110,7 +134,7 @@ def test_full_path_sampled(wl, idx):
     mask_ref, _ = oracle.prune24(d["W"][rows])
     assert (host(o["mask"][rows]) == mask_ref).all()
     v_ref, m_ref, _ = oracle.compress24(d["W"][rows], mask_ref)
-    assert (host(o["vs"][rows]) == v_ref).all()
+    assert _same_bits(host(o["vs"][rows]), v_ref)
     assert (host(o["ms"][rows]) == m_ref).all()
 
     # --- double pruning on sampled column groups (all N rows of W_s for 4 columns)
@@ -120,7 +144,7 @@ def test_full_path_sampled(wl, idx):
         mc, _ = oracle.prune24(Wc)                 # W_s restricted to these columns
         vc, mcw, _ = oracle.compress24(Wc, mc)
         vdp_ref, mdp_ref, _ = oracle.double_prune(vc, mcw, N, 4)
-        assert (host(o["vdp"][c0:c0 + 4]) == vdp_ref).all(), c0
+        assert _same_bits(host(o["vdp"][c0:c0 + 4]), vdp_ref), c0
         assert (host(o["mdp"][c0:c0 + 4]) == mdp_ref).all(), c0
 
     # --- forward with adapter on a sampled token x feature block
@@ -279,7 +303,7 @@ def test_weight_update_sampled(wl, idx):
         _check_update(vc, opt["G"][:, sl], opt["M"][:, sl], opt["V"][:, sl], step, UPDATE_HP, new_vc,
                       M[:, sl].cpu().numpy(), V[:, sl].cpu().numpy())
         vdp_ref, mdp_ref, _ = oracle.double_prune(new_vc, mcw, N, 4)
-        assert (host(dp.values[c0:c0 + 4]) == vdp_ref).all(), c0
+        assert _same_bits(host(dp.values[c0:c0 + 4]), vdp_ref), c0
         assert (host(dp.meta[c0:c0 + 4]) == mdp_ref).all(), c0
     del c, dp, G, M, V
     torch.cuda.empty_cache()
