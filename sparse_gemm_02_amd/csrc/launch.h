@@ -9,6 +9,16 @@ namespace slope {
 
 enum class Dt { F32 = 0, BF16 = 1, F16 = 2 };
 
+// Compute units of the current device (256 on MI355X; that figure if the
+// query fails, in which case the following launch reports the error).
+inline int64_t device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
 hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* W_s,
                           hipStream_t s);
 hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols, void* values,

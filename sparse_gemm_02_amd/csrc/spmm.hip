@@ -65,17 +65,24 @@ namespace {
 // PK: the sparse operand comes as tile chunks (see pack_sparse_kernel): each
 // stage loads one contiguous 18 KB chunk (values then metadata) instead of 256
 // separate 64-byte row pieces and a strided metadata read.
+//
+// A launch covers the row tiles tm0 .. tm0 + tiles_m - 1 (BM rows each) and
+// every column tile; the host splits a product into a launch of full-width
+// tiles and one of narrower tiles for the rows that would otherwise leave the
+// last round of blocks half empty.  Each output accumulates over k in the
+// same order whatever the tile width, so the split does not change results.
 template <class G, bool ADAPTER, typename O, bool PK, bool H = false>
 __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
     int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
-    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y) {
+    const uint16_t* __restrict__ xll, int rpad, int tm0, int tiles_m, O* __restrict__ Y) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % G::WGM, wt = wave / G::WGM;
-  const int tiles_m = (M + G::BM - 1) / G::BM, tiles_t = (T + G::BT - 1) / G::BT;
+  const int tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
+  tm += tm0;
   static_assert(PK || G::NST == 3, "metadata ring holds four stages");
   constexpr int SLOT = PK ? G::PSTAGE_BYTES : G::STAGE_BYTES;
   const int64_t m0 = (int64_t)tm * G::BM, t0 = (int64_t)tt * G::BT;
@@ -231,6 +238,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
 }
 
 typedef Geo<256, 256, 3, 2, 4> GeoBig;
+// the narrower tile for the rows of a product's last, partly filled round
+typedef Geo<256, 128, 3, 2, 4> GeoHalf;
+static_assert(GeoHalf::BM == GeoBig::BM && GeoHalf::CHUNK_BYTES == GeoBig::CHUNK_BYTES, "same row tiles and chunks");
 
 // Tile chunks of a compressed bf16 matrix [M, Kred] (values [M, Kred/2],
 // metadata [M, ceil(Kred/32)]): chunk (tm, s) covers rows 256tm .. 256tm+255
@@ -266,20 +276,31 @@ __global__ __launch_bounds__(256) void pack_sparse_kernel(const uint16_t* __rest
   }
 }
 
-template <bool ADAPTER, typename O, bool PK, bool H>
-hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
-                      const LowrankWs* w, O* Y, hipStream_t s) {
-  typedef GeoBig G;
+// Row tiles [tm0, tm0 + tiles_m) of the product in tiles of geometry G.
+template <class G, bool ADAPTER, typename O, bool PK, bool H>
+hipError_t launch_rows(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
+                       const LowrankWs* w, int tm0, int tiles_m, O* Y, hipStream_t s) {
   auto kern = spmm_smfmac_kernel<G, ADAPTER, O, PK, H>;
   constexpr int lds_bytes = PK ? G::PLDS_BYTES : G::LDS_BYTES;
   // once per process (thread-safe static initialisation)
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (attr != hipSuccess) return attr;
-  const int64_t nb = cdiv(M, G::BM) * cdiv(T, G::BT);
+  const int64_t nb = (int64_t)tiles_m * cdiv(T, G::BT);
+  if (nb == 0) return hipSuccess;
   kern<<<(unsigned)nb, G::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, w ? w->rt : nullptr,
                                                    w ? w->xlh : nullptr, w ? w->xll : nullptr,
-                                                   w ? (int)w->rpad : 0, Y);
+                                                   w ? (int)w->rpad : 0, tm0, tiles_m, Y);
   return hipGetLastError();
+}
+
+template <bool ADAPTER, typename O, bool PK, bool H>
+hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
+                      const LowrankWs* w, O* Y, hipStream_t s) {
+  const int tiles_m = (int)cdiv(M, GeoBig::BM);
+  const int rows = (int)full_width_rows(tiles_m, cdiv(T, GeoBig::BT), cdiv(T, GeoHalf::BT), device_compute_units());
+  hipError_t e = launch_rows<GeoBig, ADAPTER, O, PK, H>(B, T, Kred, vals, meta, M, w, 0, rows, Y, s);
+  if (e != hipSuccess || rows == tiles_m) return e;
+  return launch_rows<GeoHalf, ADAPTER, O, PK, H>(B, T, Kred, vals, meta, M, w, rows, tiles_m - rows, Y, s);
 }
 
 template <bool PK, bool H, typename O>

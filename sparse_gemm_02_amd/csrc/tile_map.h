@@ -22,4 +22,27 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_r,
   tc = in_group / gsize;
 }
 
+// Host side: how many row tiles of a sparse product to run in full-width
+// tiles when the remaining rows take half-width tiles (twice the column tiles,
+// each costing about 0.65 of a full tile, measured on the OPT-66B shapes), so that
+// a launch whose full-width grid would end in a partly filled round of
+// blocks finishes sooner.  Minimises the estimated time in rounds of `cus`
+// blocks over all-half-width and the last 4 * cus rows (more half-width rows
+// than that only pay when every row does, as for a single column tile); ties
+// keep more full-width rows.
+inline int64_t full_width_rows(int64_t tiles_r, int64_t cols_full, int64_t cols_half, int64_t cus) {
+  auto rounds = [cus](int64_t blocks) { return (blocks + cus - 1) / cus; };
+  auto cost = [&](int64_t rows) { return 100 * rounds(rows * cols_full) + 65 * rounds((tiles_r - rows) * cols_half); };
+  int64_t best_rows = tiles_r, best_cost = cost(tiles_r);
+  const int64_t lowest = tiles_r > 4 * cus ? tiles_r - 4 * cus : 0;
+  for (int64_t rows = tiles_r - 1; rows >= lowest; --rows) {
+    if (cost(rows) < best_cost) {
+      best_cost = cost(rows);
+      best_rows = rows;
+    }
+  }
+  if (cost(0) < best_cost) best_rows = 0;
+  return best_rows;
+}
+
 }  // namespace slope

@@ -290,6 +290,46 @@ def test_spmm_packed_matches_unpacked(T, N, K, adapter, out_dt):
         assert normwise(host_f64(dXp), oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N)) <= TOL["bf16"]
 
 
+# Token counts near 8192 with 256-row output tiles: on a 256-CU device the
+# sparse products run (T, M) = (8142, 2000) in full-width tiles only (one full
+# round), (8142, 2224) as eight rows of full-width tiles plus one row of
+# half-width tiles, and M = 96 in half-width tiles only; M is N for the
+# forward and K for dX.  Rows, tokens and the reduction (96 = 1.5 stages) are
+# ragged.
+SPLIT_SHAPES = [(8142, 2000, 96), (8142, 96, 2000), (8142, 2224, 96), (8142, 96, 2224)]
+
+
+@pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
+@pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
+def test_spmm_tile_split(T, N, K, ints):
+    """Forward with the adapter and dX with the adapter's dX term, packed and
+    unpacked, whichever mix of tile widths the launch takes: within tolerance
+    of the oracle, and bit-exact in fp32 for integer inputs (every sum exact)."""
+    r = 8
+    say(f"spmm tile split T={T} N={N} K={K} ints={ints}")
+    d = _layer(T, N, K, r, "bf16", seed=29 * T + N + K, ints=ints)
+    od = torch.float32 if ints else torch.bfloat16
+    L, R = dev(d["L"]), dev(d["R"])
+    ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
+    pd = torch.empty(S.slope_packed_sparse_bytes(K, N), dtype=torch.uint8, device="cuda")
+    S.slope_pack_sparse(dev(d["vdp"]), dev_meta(d["mdp"]), K, N, pd)
+    Yp, Yu, dXp = empty((T, N), od), empty((T, N), od), empty((T, K), od)
+    S.slope_spmm_fwd_packed(dev(d["X"]), ps, N, Yp, L=L, R=R, workspace=workspace(T, K, r, N))
+    S.slope_spmm_fwd(dev(d["X"]), dev(d["vs"]), dev_meta(d["ms"]), N, Yu, L=L, R=R, workspace=workspace(T, K, r, N))
+    S.slope_spmm_bwd_dx_packed(dev(d["dY"]), pd, K, dXp, L=L, R=R, workspace=workspace(T, N, r, K))
+    torch.cuda.synchronize()
+    ref_y = oracle.spmm_fwd(d["X"], d["vs"], d["ms"], K, d["L"], d["R"])
+    ref_dx = oracle.spmm_bwd_dx(d["dY"], d["vdp"], d["mdp"], N) + oracle.lowrank_bwd(d["X"], d["dY"], d["L"], d["R"])[0]
+    assert np.array_equal(host(Yp), host(Yu))
+    if ints:
+        assert np.array_equal(host_f64(Yp), ref_y)
+        assert np.array_equal(host_f64(dXp), ref_dx)
+    else:
+        assert normwise(host_f64(Yp), ref_y) <= TOL["bf16"]
+        assert normwise(host_f64(dXp), ref_dx) <= TOL["bf16"]
+
+
 DECODE_SHAPES = [(1, 256, 256), (5, 520, 272), (16, 768, 1024), (33, 260, 528), (64, 1040, 1296), (0, 64, 64),
                  (3, 64, 4096)]
 
@@ -487,8 +527,10 @@ def test_masked_wgrad(T, N, K, out_dt, packed):
     assert normwise(host_f64(acc), v_ref + host_f64(base)) <= TOL["bf16"]
 
 
+# (70, 8136, 2000) and (70, 8136, 2224): 256 and 288 output tiles, a whole
+# round of blocks and a partly filled second one, ragged in k and n.
 @pytest.mark.parametrize("T,N,K", [(300, 520, 272), (257, 264, 520), (1, 64, 128), (2048, 512, 768), (32, 8, 1032),
-                                   (64, 256, 1032), (97, 264, 776)])
+                                   (64, 256, 1032), (97, 264, 776), (70, 8136, 2000), (70, 8136, 2224)])
 def test_masked_wgrad_packed_matches_direct(T, N, K):
     """Both kernels feed the same operands to the same MFMA positions in the
     same token order, so with and without the workspace results are bitwise equal."""
