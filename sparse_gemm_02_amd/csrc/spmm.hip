@@ -66,22 +66,24 @@ namespace {
 // stage loads one contiguous 18 KB chunk (values then metadata) instead of 256
 // separate 64-byte row pieces and a strided metadata read.
 //
-// A launch covers the row tiles tm0 .. tm0 + tiles_m - 1 (BM rows each) and
-// every column tile; the host splits a product into a launch of full-width
-// tiles and one of narrower tiles for the rows that would otherwise leave the
-// last round of blocks half empty.  Each output accumulates over k in the
-// same order whatever the tile width, so the split does not change results.
-template <class G, bool ADAPTER, typename O, bool PK, bool H = false>
-__global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
-    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
-    int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
-    const uint16_t* __restrict__ xll, int rpad, int tm0, int tiles_m, O* __restrict__ Y) {
+// Block `bid` of `nblocks` computes one tile of the row tiles tm0 .. tm0 +
+// tiles_m - 1 (BM rows each), any column tile.  A product whose full-width
+// tiles would end in a partly filled round of blocks gives its last row tiles
+// narrower tiles in the same launch (spmm_split_kernel).  Each output
+// accumulates over k in the same order whatever the tile width, so the split
+// does not change results.
+template <class G, bool ADAPTER, typename O, bool PK, bool H>
+__device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals,
+                                          const uint32_t* __restrict__ meta, int M, int T, int Kred,
+                                          const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
+                                          const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, int bid,
+                                          int nblocks, int tm0, int tiles_m) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % G::WGM, wt = wave / G::WGM;
   const int tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_t, 8, tm, tt);
+  tile_of_block(bid, nblocks, tiles_m, tiles_t, 8, tm, tt);
   tm += tm0;
   static_assert(PK || G::NST == 3, "metadata ring holds four stages");
   constexpr int SLOT = PK ? G::PSTAGE_BYTES : G::STAGE_BYTES;
@@ -237,6 +239,35 @@ __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
   store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
 }
 
+// Every row tile in tiles of geometry G.
+template <class G, bool ADAPTER, typename O, bool PK, bool H = false>
+__global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
+    int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
+    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y) {
+  spmm_tile<G, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, gridDim.x, 0,
+                                  (M + G::BM - 1) / G::BM);
+}
+
+// Row tiles 0 .. rows_full - 1 in tiles of geometry GF (the first blocks),
+// the rest in the narrower tiles of GN (the last blocks, which the dispatcher
+// hands to compute units as they come free).
+template <class GF, class GN, bool ADAPTER, typename O, bool PK, bool H = false>
+__global__ __launch_bounds__(GF::THREADS, 1) void spmm_split_kernel(
+    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
+    int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
+    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, int rows_full) {
+  static_assert(GF::THREADS == GN::THREADS && GF::BM == GN::BM, "same block and row tiles");
+  const int tiles_m = (M + GF::BM - 1) / GF::BM;
+  const int nfull = rows_full * ((T + GF::BT - 1) / GF::BT);
+  if ((int)blockIdx.x < nfull)
+    spmm_tile<GF, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, nfull, 0,
+                                     rows_full);
+  else
+    spmm_tile<GN, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x - nfull,
+                                     gridDim.x - nfull, rows_full, tiles_m - rows_full);
+}
+
 typedef Geo<256, 256, 3, 2, 4> GeoBig;
 // the narrower tile for the rows of a product's last, partly filled round
 typedef Geo<256, 128, 3, 2, 4> GeoHalf;
@@ -276,31 +307,36 @@ __global__ __launch_bounds__(256) void pack_sparse_kernel(const uint16_t* __rest
   }
 }
 
-// Row tiles [tm0, tm0 + tiles_m) of the product in tiles of geometry G.
-template <class G, bool ADAPTER, typename O, bool PK, bool H>
-hipError_t launch_rows(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
-                       const LowrankWs* w, int tm0, int tiles_m, O* Y, hipStream_t s) {
-  auto kern = spmm_smfmac_kernel<G, ADAPTER, O, PK, H>;
-  constexpr int lds_bytes = PK ? G::PLDS_BYTES : G::LDS_BYTES;
-  // once per process (thread-safe static initialisation)
-  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (attr != hipSuccess) return attr;
-  const int64_t nb = (int64_t)tiles_m * cdiv(T, G::BT);
-  if (nb == 0) return hipSuccess;
-  kern<<<(unsigned)nb, G::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, w ? w->rt : nullptr,
-                                                   w ? w->xlh : nullptr, w ? w->xll : nullptr,
-                                                   w ? (int)w->rpad : 0, tm0, tiles_m, Y);
-  return hipGetLastError();
-}
-
+// Whole product: full-width tiles, or full-width rows plus half-width rows
+// in one launch when the full-width grid would end in a partly filled round.
 template <bool ADAPTER, typename O, bool PK, bool H>
 hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
                       const LowrankWs* w, O* Y, hipStream_t s) {
-  const int tiles_m = (int)cdiv(M, GeoBig::BM);
-  const int rows = (int)full_width_rows(tiles_m, cdiv(T, GeoBig::BT), cdiv(T, GeoHalf::BT), device_compute_units());
-  hipError_t e = launch_rows<GeoBig, ADAPTER, O, PK, H>(B, T, Kred, vals, meta, M, w, 0, rows, Y, s);
-  if (e != hipSuccess || rows == tiles_m) return e;
-  return launch_rows<GeoHalf, ADAPTER, O, PK, H>(B, T, Kred, vals, meta, M, w, rows, tiles_m - rows, Y, s);
+  const int64_t tiles_m = cdiv(M, GeoBig::BM), cols = cdiv(T, GeoBig::BT), cols_half = cdiv(T, GeoHalf::BT);
+  const int64_t rows = full_width_rows(tiles_m, cols, cols_half, device_compute_units());
+  constexpr int lds_bytes = PK ? GeoBig::PLDS_BYTES : GeoBig::LDS_BYTES;
+  static_assert((PK ? GeoHalf::PLDS_BYTES : GeoHalf::LDS_BYTES) <= lds_bytes, "the narrow tile fits the wide one's LDS");
+  const uint16_t* rt = w ? w->rt : nullptr;
+  const uint16_t* xlh = w ? w->xlh : nullptr;
+  const uint16_t* xll = w ? w->xll : nullptr;
+  const int rpad = w ? (int)w->rpad : 0;
+  if (rows == tiles_m) {
+    auto kern = spmm_smfmac_kernel<GeoBig, ADAPTER, O, PK, H>;
+    // once per process (thread-safe static initialisation)
+    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (attr != hipSuccess) return attr;
+    if (tiles_m * cols == 0) return hipSuccess;
+    kern<<<(unsigned)(tiles_m * cols), GeoBig::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, rt, xlh, xll,
+                                                                        rpad, Y);
+  } else {
+    auto kern = spmm_split_kernel<GeoBig, GeoHalf, ADAPTER, O, PK, H>;
+    static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (attr != hipSuccess) return attr;
+    const int64_t nb = rows * cols + (tiles_m - rows) * cols_half;
+    kern<<<(unsigned)nb, GeoBig::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y,
+                                                          (int)rows);
+  }
+  return hipGetLastError();
 }
 
 template <bool PK, bool H, typename O>
