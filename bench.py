@@ -4,17 +4,18 @@ One step is one pass of the whole hot path over the four linears of an OPT-66B
 transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 36864->9216; T = 8192 tokens, adapter rank 72, bf16 with fp32 accumulation):
 
-    prune24 -> compress24 -> double_prune -> pack_sparse (W_s and W_dp^T
-    into tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx (+ the
-    adapter's dX term) -> pack_tokens (X and dY into token chunks)
-    -> masked_wgrad -> lowrank_grads (dL, dR)
+    prune24 -> compress24 -> double_prune (straight into W_dp^T's tile
+    chunks) -> pack_sparse (W_s into tile chunks) -> spmm_fwd (+ fused
+    adapter) -> spmm_bwd_dx (+ the adapter's dX term) -> pack_tokens (X and
+    dY into token chunks) -> masked_wgrad -> lowrank_grads (dL, dR)
 
 The three products run on the packed operands (the *_packed entry points);
 the packing passes are part of the step.  A `decode` object adds the
 few-token forward (slope_spmm_fwd_decode) at the workload's inference token
 counts, as HBM bytes per second, and a `weight_update` object times the optimizer
-step (AdamW on the compressed values fused with the double prune, and on the
-adapter factors), also as HBM bytes per second.
+step (AdamW on the compressed values fused with the double prune, writing both
+GEMM operands' tile chunks, and AdamW on the adapter factors), also as HBM
+bytes per second.
 
 prune24 and compress24 run once per layer in training (the forward mask is
 static); they are kept inside the timed step so the step covers every kernel of
@@ -83,8 +84,6 @@ class Linear:
         self.mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
         self.vs = torch.empty((N, K // 2), dtype=bf, device=dev)
         self.ms = torch.empty((N, (K // 4 + 7) // 8), dtype=torch.int32, device=dev)
-        self.vdp = torch.empty((K, N // 2), dtype=bf, device=dev)
-        self.mdp = torch.empty((K, (N // 4 + 7) // 8), dtype=torch.int32, device=dev)
         self.Y = torch.empty((T, N), dtype=bf, device=dev)
         self.dX = torch.empty((T, K), dtype=bf, device=dev)
         self.dW = torch.empty((N, K // 2), dtype=bf, device=dev)
@@ -122,7 +121,10 @@ OPS = ("prune24", "compress24", "double_prune", "pack_sparse", "spmm_fwd", "spmm
 
 def pack_sparse(S, li):
     S.slope_pack_sparse(li.vs, li.ms, li.N, li.K, li.ps)
-    S.slope_pack_sparse(li.vdp, li.mdp, li.K, li.N, li.pd)
+
+
+def double_prune(S, li):
+    S.slope_double_prune_packed(li.vs, li.ms, li.N, li.K, li.pd)
 
 
 def pack(S, li):
@@ -150,7 +152,7 @@ def step(lins, S, ev=None):
         calls = (
             ("prune24", lambda: S.slope_prune24(li.W, li.mask)),
             ("compress24", lambda: S.slope_compress24(li.W, li.mask, li.vs, li.ms)),
-            ("double_prune", lambda: S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)),
+            ("double_prune", lambda: double_prune(S, li)),
             ("pack_sparse", lambda: pack_sparse(S, li)),
             ("spmm_fwd", lambda: S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
             ("spmm_bwd_dx", lambda: bwd_dx(S, li)),
@@ -257,7 +259,7 @@ def profile_mode(args, wl, T):
     for li in lins:  # prerequisites of every op
         S.slope_prune24(li.W, li.mask)
         S.slope_compress24(li.W, li.mask, li.vs, li.ms)
-        S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+        double_prune(S, li)
         pack_sparse(S, li)
         pack(S, li)
         S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
@@ -275,7 +277,7 @@ def profile_mode(args, wl, T):
             elif op == "compress24":
                 S.slope_compress24(li.W, li.mask, li.vs, li.ms)
             elif op == "double_prune":
-                S.slope_double_prune(li.vs, li.ms, li.N, li.K, li.vdp, li.mdp)
+                double_prune(S, li)
             elif op == "pack_sparse":
                 pack_sparse(S, li)
             elif op == "spmm_fwd":
@@ -289,8 +291,8 @@ def profile_mode(args, wl, T):
             elif op == "masked_wgrad":
                 wgrad(S, li)
             elif op == "adamw_double_prune":
-                S.slope_adamw_double_prune(li.vs, li.ms, li.dW, li.opt_m, li.opt_v, li.N, li.K, li.vdp, li.mdp,
-                                           1, lr=1e-4)
+                S.slope_adamw_double_prune_packed(li.vs, li.ms, li.dW, li.opt_m, li.opt_v, li.N, li.K, li.ps,
+                                                  li.pd, 1, lr=1e-4)
     torch.cuda.synchronize()
     print(f"[profile] {op} x {args.repeat} on {[l.name for l in lins]} T={T}", flush=True)
 
@@ -331,11 +333,12 @@ def decode_pass(lins, wl, S, torch, reps=20):
 def update_pass(lins, S, torch, reps=10):
     """The weight update of a training step, timed apart from the GEMM step:
     AdamW on the compressed values fused with the double prune of the updated
-    weight (slope_adamw_double_prune) on every linear, plus AdamW on the
+    weight, both GEMM operands written as tile chunks
+    (slope_adamw_double_prune_packed) on every linear, plus AdamW on the
     adapter factors L and R (slope_adamw), with fp32 moments.  HBM bound:
-    algorithmic bytes are 12.25 B per weight (values, gradient and metadata
-    read, values and moments read and written, the double-pruned copy written)
-    and 22 B per adapter element."""
+    algorithmic bytes are 13.25 B per weight (values, gradient and metadata
+    read; values and moments read and written; W_s's packed values and
+    W_dp^T's tile chunks written) and 22 B per adapter element."""
     hp = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
     state, nbytes = [], 0
     for li in lins:
@@ -345,13 +348,13 @@ def update_pass(lins, S, torch, reps=10):
         aL = [torch.zeros(li.L.numel(), device="cuda") for _ in range(2)]
         aR = [torch.zeros(li.R.numel(), device="cuda") for _ in range(2)]
         state.append((li, m, v, aL, aR))
-        nbytes += 12.25 * li.N * li.K + 22 * (li.L.numel() + li.R.numel())
+        nbytes += 13.25 * li.N * li.K + 22 * (li.L.numel() + li.R.numel())
     k = [0]
 
     def run():
         k[0] += 1
         for li, m, v, aL, aR in state:
-            S.slope_adamw_double_prune(li.vs, li.ms, li.dW, m, v, li.N, li.K, li.vdp, li.mdp, k[0], **hp)
+            S.slope_adamw_double_prune_packed(li.vs, li.ms, li.dW, m, v, li.N, li.K, li.ps, li.pd, k[0], **hp)
             S.slope_adamw(li.L, li.dL, aL[0], aL[1], k[0], **hp)
             S.slope_adamw(li.R, li.dR, aR[0], aR[1], k[0], **hp)
     for _ in range(2):
@@ -368,8 +371,8 @@ def update_pass(lins, S, torch, reps=10):
     del state
     return {"ms_per_layer": round(ms, 4), "bytes": int(nbytes), "gbs": round(gbs, 1),
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "what": "AdamW on the compressed values fused with the double prune (four linears) "
-                    "+ AdamW on the adapter factors; fp32 moments"}
+            "what": "AdamW on the compressed values fused with the double prune, writing both operands' "
+                    "tile chunks (four linears) + AdamW on the adapter factors; fp32 moments"}
 
 
 def measured_traffic(op):
@@ -454,7 +457,7 @@ def main():
     # algorithmic HBM bytes: per weight for the pruning ops, per activation
     # element (read + written once) for the packing pass
     hbm = {"prune24": lambda l: 3.0 * l.N * l.K, "compress24": lambda l: 4.125 * l.N * l.K,
-           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_sparse": lambda l: 2 * 2 * 1.125 * l.N * l.K,
+           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_sparse": lambda l: 2 * 1.125 * l.N * l.K,
            "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
     for op, f in hbm.items():
         by = sum(f(l) for l in lins)

@@ -339,6 +339,36 @@ slope_status slope_adamw_double_prune(slope_dtype dt, slope_dtype grad_dt, void*
                                       const slope_adamw_params* hp, void* values_dpT, uint32_t* meta_dpT,
                                       uint8_t* mask_dpT_or_null, void* stream);
 
+/* slope_double_prune (explainer 2.A, the double-pruned backward weight) with
+ * W_dpT written straight to its tile-chunk form: packed_dpT afterwards holds
+ * exactly what slope_pack_sparse (rows K, cols N) makes of slope_double_prune's
+ * values_dpT and meta_dpT, bitwise, without those canonical rows.  values_s
+ * [N, K/2], meta_s [N, ceil(K/32)] dt (BF16 or F16); packed_dpT: caller-owned
+ * device memory of at least slope_packed_sparse_bytes(K, N) bytes, overwritten
+ * (padding included).  Errors: SLOPE_ERR_UNSUPPORTED for F32 or N > 2^21,
+ * SLOPE_ERR_SHAPE unless N % 16 == 0 and K % 16 == 0, SLOPE_ERR_WORKSPACE if
+ * packed_dpT_bytes is short. */
+slope_status slope_double_prune_packed(slope_dtype dt, const void* values_s, const uint32_t* meta_s, int64_t N,
+                                       int64_t K, void* packed_dpT, int64_t packed_dpT_bytes, void* stream);
+
+/* The fused weight update of slope_adamw_double_prune for a layer whose GEMM
+ * operands are kept in tile-chunk form (explainer 2.A: the backward weight is
+ * pruned again from the updated weight; discussion page, "Memory Footprint":
+ * optimizer state only for the kept values).  values_s, m, v are updated in
+ * place as there; packed_s must hold slope_pack_sparse(values_s, meta_s, N, K)
+ * of the values before the update, and afterwards holds that of the updated
+ * values (only its value granules are rewritten: the mask is static);
+ * packed_dpT receives slope_double_prune_packed of the updated W_s.  Results
+ * equal slope_adamw_double_prune followed by slope_pack_sparse of both
+ * operands, bitwise.  dt BF16 or F16; grad_dt BF16, F16 or F32.  Errors: those
+ * of slope_adamw_double_prune and slope_double_prune_packed, SLOPE_ERR_UNSUPPORTED
+ * for K > 2^21, SLOPE_ERR_WORKSPACE if either packed size is short. */
+slope_status slope_adamw_double_prune_packed(slope_dtype dt, slope_dtype grad_dt, void* values_s,
+                                             const uint32_t* meta_s, const void* dW_values, float* m, float* v,
+                                             int64_t N, int64_t K, const slope_adamw_params* hp, void* packed_s,
+                                             int64_t packed_s_bytes, void* packed_dpT, int64_t packed_dpT_bytes,
+                                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

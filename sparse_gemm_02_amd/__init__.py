@@ -32,7 +32,7 @@ __all__ = [
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
     "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_lowrank_grads_workspace_bytes",
     "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
-    "EXPORTED_SYMBOLS",
+    "slope_double_prune_packed", "slope_adamw_double_prune_packed", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +84,9 @@ _SIGS = {
     "slope_adamw": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _P_HP, _vp]),
     "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
                                         _vp]),
+    "slope_double_prune_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "slope_adamw_double_prune_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _i64,
+                                               _vp, _i64, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -336,6 +339,28 @@ def slope_adamw(params, grads, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     hp = _hp(step, lr, beta1, beta2, eps, weight_decay)
     _check("slope_adamw", library().slope_adamw(_dt(params), _dt(grads), _nn(params), _nn(grads), _f32(m), _f32(v),
                                                 n, ctypes.byref(hp), _s(stream)))
+
+
+def slope_double_prune_packed(values_s, meta_s, N, K, packed_dpT, stream=None) -> None:
+    """The double prune of W_s written straight to W_dp^T's tile-chunk form."""
+    nb = packed_dpT.numel() * packed_dpT.element_size()
+    _check("slope_double_prune_packed", library().slope_double_prune_packed(
+        _dt(values_s), _nn(values_s), _nn(meta_s), N, K, _nn(packed_dpT), nb, _s(stream)))
+
+
+def slope_adamw_double_prune_packed(values_s, meta_s, dW_values, m, v, N, K, packed_s, packed_dpT, step, lr,
+                                    beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, stream=None) -> None:
+    """AdamW on the compressed values of W_s (in place, and inside its tile
+    chunks packed_s), then the double prune of the updated W_s into the tile
+    chunks packed_dpT."""
+    n = values_s.numel()
+    if dW_values.numel() != n or m.numel() != n or v.numel() != n:
+        raise ValueError("values_s, dW_values, m and v must have the same number of elements")
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay)
+    _check("slope_adamw_double_prune_packed", library().slope_adamw_double_prune_packed(
+        _dt(values_s), _dt(dW_values), _nn(values_s), _nn(meta_s), _nn(dW_values), _f32(m), _f32(v), N, K,
+        ctypes.byref(hp), _nn(packed_s), packed_s.numel() * packed_s.element_size(), _nn(packed_dpT),
+        packed_dpT.numel() * packed_dpT.element_size(), _s(stream)))
 
 
 def slope_adamw_double_prune(values_s, meta_s, dW_values, m, v, N, K, values_dpT, meta_dpT, step, lr, beta1=0.9,

@@ -520,4 +520,42 @@ slope_status slope_adamw_double_prune(slope_dtype dt, slope_dtype grad_dt, void*
                                                    values_dpT, meta_dpT, mask_dpT_or_null, (hipStream_t)stream));
 }
 
+slope_status slope_double_prune_packed(slope_dtype dt, const void* values_s, const uint32_t* meta_s, int64_t N,
+                                       int64_t K, void* packed_dpT, int64_t packed_dpT_bytes, void* stream) {
+  if (!dt_ok(dt) || N < 0 || K < 0 || packed_dpT_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values_s, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(packed_dpT, true));
+  if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // 16-bit values only
+  if (N % 16 || K % 16) return SLOPE_ERR_SHAPE;
+  if (!in_range(K) || N > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_dpT_bytes < slope::packed_sparse_bytes(K, N)) return SLOPE_ERR_WORKSPACE;
+  return from_hip(slope::launch_double_prune_packed((Dt)dt, values_s, meta_s, N, K, packed_dpT, (hipStream_t)stream));
+}
+
+slope_status slope_adamw_double_prune_packed(slope_dtype dt, slope_dtype grad_dt, void* values_s,
+                                             const uint32_t* meta_s, const void* dW_values, float* m, float* v,
+                                             int64_t N, int64_t K, const slope_adamw_params* hp, void* packed_s,
+                                             int64_t packed_s_bytes, void* packed_dpT, int64_t packed_dpT_bytes,
+                                             void* stream) {
+  if (!dt_ok(dt) || !dt_ok(grad_dt) || N < 0 || K < 0 || packed_s_bytes < 0 || packed_dpT_bytes < 0)
+    return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values_s, true));
+  SLOPE_TRY(ptr(meta_s, true));
+  SLOPE_TRY(ptr(dW_values, true));
+  SLOPE_TRY(ptr(m, true));
+  SLOPE_TRY(ptr(v, true));
+  SLOPE_TRY(ptr(packed_s, true));
+  SLOPE_TRY(ptr(packed_dpT, true));
+  slope::AdamWStep c;
+  SLOPE_TRY(adamw_step(hp, &c));
+  if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // 16-bit values only
+  if (N % 16 || K % 16) return SLOPE_ERR_SHAPE;
+  if (K > kPackedMaxCols || N > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_s_bytes < slope::packed_sparse_bytes(N, K) || packed_dpT_bytes < slope::packed_sparse_bytes(K, N))
+    return SLOPE_ERR_WORKSPACE;
+  return from_hip(slope::launch_adamw_double_prune_packed((Dt)dt, (Dt)grad_dt, values_s, meta_s, dW_values, m, v, N,
+                                                          K, c, packed_s, packed_dpT, (hipStream_t)stream));
+}
+
 }  // extern "C"

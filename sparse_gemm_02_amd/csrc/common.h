@@ -118,4 +118,16 @@ template <> struct Fmt16<true> {
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tile-chunk form of a compressed 16-bit 2:4 matrix [rows, cols], the sparse
+// products' operand format: chunk (t, s) holds rows 256t .. 256t+255 and dense
+// columns 64s .. 64s+63 at byte offset (t * ceil(cols/64) + s) * kPackChunkBytes;
+// first each row's 32 values (64 bytes at row*64, 16-byte granule c at
+// c ^ ((row/4) % 4)), then each row's two metadata words (8 bytes at
+// kPackValueBytes + row*8); rows past `rows` and columns past `cols` are 0.
+constexpr int kPackRows = 256, kPackCols = 64;
+constexpr int kPackValueBytes = kPackRows * 64, kPackChunkBytes = kPackValueBytes + kPackRows * 8;
+__host__ __device__ constexpr int64_t pack_chunk_offset(int64_t row, int64_t col, int64_t cols) {
+  return ((row / kPackRows) * cdiv(cols, kPackCols) + col / kPackCols) * kPackChunkBytes;
+}
+
 }  // namespace slope

@@ -39,6 +39,14 @@ hipError_t launch_adamw(Dt param, Dt grad, void* params, const void* grads, floa
 hipError_t launch_adamw_double_prune(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s, const void* grads,
                                      float* m, float* v, int64_t N, int64_t K, const AdamWStep& c,
                                      void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s);
+// The same two steps with W_dp^T written as tile chunks, and the updated
+// values also rewritten inside W_s's tile chunks (16-bit, K % 16 == 0,
+// N % 16 == 0; checked by the caller).
+hipError_t launch_double_prune_packed(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
+                                      void* packed_dpT, hipStream_t s);
+hipError_t launch_adamw_double_prune_packed(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s,
+                                            const void* grads, float* m, float* v, int64_t N, int64_t K,
+                                            const AdamWStep& c, void* packed_s, void* packed_dpT, hipStream_t s);
 
 // Adapter workspace (caller-owned device memory), carved into:
 //   part [splits][T][r] fp32   partial sums of X . L over k-splits

@@ -236,12 +236,21 @@ constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit 
 // loads (gradient GT, fp32 moments m and v at the same element index), writes
 // the new values and moments back in place and double-prunes the new values:
 // the optimizer's pass over the weight and the double prune share one read.
-template <bool UPD, typename GT, bool H = false>
+//
+// With PK the double-pruned W_dp^T goes straight to its tile-chunk form
+// (pk_dpT) instead of values / metadata rows: each thread's 16 values of a row
+// are two granules of one chunk row and its metadata word one of the row's
+// two.  The grid then covers whole 256-row chunks, rows past K written as 0.
+// UPD with PK also rewrites the updated values inside W_s's tile chunks
+// (pk_s, which holds W_s packed: the mask is static, so only values change).
+template <bool UPD, typename GT, bool H = false, bool PK = false>
 __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* vals, const uint32_t* __restrict__ meta,
                                                                     int64_t N, int64_t K,
                                                                     uint16_t* __restrict__ out_vals,
                                                                     uint32_t* __restrict__ out_meta,
                                                                     uint8_t* __restrict__ out_mask,
+                                                                    char* __restrict__ pk_dpT,
+                                                                    char* __restrict__ pk_s,
                                                                     const GT* __restrict__ grads,
                                                                     float* __restrict__ m, float* __restrict__ v,
                                                                     AdamWStep hp) {
@@ -265,6 +274,10 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
       if constexpr (UPD) {
         w4 = adamw8_16<H>(w4, grads + e, m + e, v + e, hp);
         *reinterpret_cast<u32x4*>(vals + e) = w4;
+        if constexpr (PK) {                           // the same granule of W_s's chunk row
+          const int rs = (int)(row % kPackRows), gs = (int)((kc % kPackCols) / 16);
+          *reinterpret_cast<u32x4*>(pk_s + pack_chunk_offset(row, kc, K) + rs * 64 + ((gs ^ ((rs >> 2) & 3)) << 4)) = w4;
+        }
       }
     }
     uint32_t d[8];                                    // 16 dense bf16, two per word
@@ -296,7 +309,8 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t krow = k0 + 2 * cp + h;
-    if (krow >= K || ngroups == 0) continue;
+    const bool live = krow < K && ngroups > 0;
+    if (!PK && !live) continue;
     uint32_t word = 0, ov[8], mw[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -316,14 +330,29 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
       mw[g] = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
     }
     if (ngroups < 8) word &= 0xFFFFu;
-    out_meta[krow * out_wpr + (g0 >> 3)] = word;
-    uint32_t* ovp = reinterpret_cast<uint32_t*>(out_vals + krow * (N / 2) + 2 * g0);
-    *reinterpret_cast<u32x4*>(ovp) = u32x4{ov[0], ov[1], ov[2], ov[3]};
-    if (ngroups == 8) *reinterpret_cast<u32x4*>(ovp + 4) = u32x4{ov[4], ov[5], ov[6], ov[7]};
-    if (out_mask) {
-      uint32_t* mp = reinterpret_cast<uint32_t*>(out_mask + krow * N + 4 * g0);
-      *reinterpret_cast<u32x4*>(mp) = u32x4{mw[0], mw[1], mw[2], mw[3]};
-      if (ngroups == 8) *reinterpret_cast<u32x4*>(mp + 4) = u32x4{mw[4], mw[5], mw[6], mw[7]};
+    if constexpr (PK) {
+      // chunk row krow % 256 of the chunk holding dense columns 4 g0 ..; groups
+      // g0 .. g0+7 are its granules 2w, 2w+1 and metadata word w (w = (g0 / 8) % 2)
+      if (g0 * 4 >= cdiv(N, kPackCols) * kPackCols) continue;        // past the last chunk column
+      const bool hi = live && ngroups == 8;
+      const int r = (int)(krow % kPackRows), w = (int)((g0 >> 3) & 1), sw = (r >> 2) & 3;
+      char* const row_base = pk_dpT + pack_chunk_offset(krow, g0 * 4, N) + r * 64;
+      *reinterpret_cast<u32x4*>(row_base + (((2 * w) ^ sw) << 4)) =
+          live ? u32x4{ov[0], ov[1], ov[2], ov[3]} : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(row_base + (((2 * w + 1) ^ sw) << 4)) =
+          hi ? u32x4{ov[4], ov[5], ov[6], ov[7]} : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint32_t*>(pk_dpT + pack_chunk_offset(krow, g0 * 4, N) + kPackValueBytes + r * 8 + w * 4) =
+          live ? word : 0u;
+    } else {
+      out_meta[krow * out_wpr + (g0 >> 3)] = word;
+      uint32_t* ovp = reinterpret_cast<uint32_t*>(out_vals + krow * (N / 2) + 2 * g0);
+      *reinterpret_cast<u32x4*>(ovp) = u32x4{ov[0], ov[1], ov[2], ov[3]};
+      if (ngroups == 8) *reinterpret_cast<u32x4*>(ovp + 4) = u32x4{ov[4], ov[5], ov[6], ov[7]};
+      if (out_mask) {
+        uint32_t* mp = reinterpret_cast<uint32_t*>(out_mask + krow * N + 4 * g0);
+        *reinterpret_cast<u32x4*>(mp) = u32x4{mw[0], mw[1], mw[2], mw[3]};
+        if (ngroups == 8) *reinterpret_cast<u32x4*>(mp + 4) = u32x4{mw[4], mw[5], mw[6], mw[7]};
+      }
     }
   }
 }
@@ -365,20 +394,56 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
   return hipGetLastError();
 }
 
+namespace {
+
+// The wide double prune over a [N, K] W_s (16-bit, K % 16 == 0, N % 16 == 0):
+// canonical W_dp^T rows, or (PK) W_dp^T tile chunks over whole 256-row chunks.
+template <bool UPD, typename GT, bool H, bool PK>
+hipError_t dp_wide(uint16_t* vals, const uint32_t* meta, int64_t N, int64_t K, uint16_t* out_vals,
+                   uint32_t* out_meta, uint8_t* out_mask, char* pk_dpT, char* pk_s, const void* grads, float* m,
+                   float* v, const AdamWStep& c, hipStream_t s) {
+  const int64_t ktiles = PK ? cdiv(K, kPackRows) * (kPackRows / DW_T) : cdiv(K, DW_T);
+  dim3 g((unsigned)ktiles, (unsigned)cdiv(N, DW_T));
+  double_prune_wide_kernel<UPD, GT, H, PK><<<g, kThreads, 0, s>>>(vals, meta, N, K, out_vals, out_meta, out_mask,
+                                                                 pk_dpT, pk_s, (const GT*)grads, m, v, c);
+  return hipGetLastError();
+}
+
+template <bool UPD, bool H, bool PK>
+hipError_t dp_wide_grad(Dt grad, uint16_t* vals, const uint32_t* meta, int64_t N, int64_t K, uint16_t* out_vals,
+                        uint32_t* out_meta, uint8_t* out_mask, char* pk_dpT, char* pk_s, const void* grads,
+                        float* m, float* v, const AdamWStep& c, hipStream_t s) {
+  if (!UPD || grad == Dt::BF16)
+    return dp_wide<UPD, uint16_t, H, PK>(vals, meta, N, K, out_vals, out_meta, out_mask, pk_dpT, pk_s, grads, m, v,
+                                         c, s);
+  if (grad == Dt::F16)
+    return dp_wide<UPD, _Float16, H, PK>(vals, meta, N, K, out_vals, out_meta, out_mask, pk_dpT, pk_s, grads, m, v,
+                                         c, s);
+  return dp_wide<UPD, float, H, PK>(vals, meta, N, K, out_vals, out_meta, out_mask, pk_dpT, pk_s, grads, m, v, c,
+                                    s);
+}
+
+template <bool UPD, bool PK>
+hipError_t dp_wide_dt(Dt dt, Dt grad, void* vals, const uint32_t* meta, int64_t N, int64_t K, void* out_vals,
+                      uint32_t* out_meta, uint8_t* out_mask, void* pk_dpT, void* pk_s, const void* grads, float* m,
+                      float* v, const AdamWStep& c, hipStream_t s) {
+  if (dt == Dt::F16)
+    return dp_wide_grad<UPD, true, PK>(grad, (uint16_t*)vals, meta, N, K, (uint16_t*)out_vals, out_meta, out_mask,
+                                       (char*)pk_dpT, (char*)pk_s, grads, m, v, c, s);
+  return dp_wide_grad<UPD, false, PK>(grad, (uint16_t*)vals, meta, N, K, (uint16_t*)out_vals, out_meta, out_mask,
+                                      (char*)pk_dpT, (char*)pk_s, grads, m, v, c, s);
+}
+
+bool wide_ok(Dt dt, int64_t N, int64_t K) { return dt != Dt::F32 && K % 16 == 0 && N % 16 == 0; }
+
+}  // namespace
+
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
   if (N == 0 || K == 0) return hipSuccess;
-  if (dt != Dt::F32 && K % 16 == 0 && N % 16 == 0) {
-    dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
-    uint16_t* vin = const_cast<uint16_t*>((const uint16_t*)values_s);
-    if (dt == Dt::BF16)
-      double_prune_wide_kernel<false, uint16_t, false><<<g, kThreads, 0, s>>>(
-          vin, meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT, nullptr, nullptr, nullptr, AdamWStep{});
-    else
-      double_prune_wide_kernel<false, uint16_t, true><<<g, kThreads, 0, s>>>(
-          vin, meta_s, N, K, (uint16_t*)values_dpT, meta_dpT, mask_dpT, nullptr, nullptr, nullptr, AdamWStep{});
-    return hipGetLastError();
-  }
+  if (wide_ok(dt, N, K))
+    return dp_wide_dt<false, false>(dt, dt, const_cast<void*>(values_s), meta_s, N, K, values_dpT, meta_dpT,
+                                    mask_dpT, nullptr, nullptr, nullptr, nullptr, nullptr, AdamWStep{}, s);
   dim3 grid((unsigned)cdiv(K, DP_TK), (unsigned)cdiv(N, DP_TN));
   if (dt == Dt::BF16)
     double_prune_kernel<uint16_t><<<grid, kThreads, 0, s>>>((const uint16_t*)values_s, meta_s, N, K, (uint16_t*)values_dpT,
@@ -392,26 +457,32 @@ hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta
   return hipGetLastError();
 }
 
+hipError_t launch_double_prune_packed(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
+                                      void* packed_dpT, hipStream_t s) {
+  if (N == 0 || K == 0) return hipSuccess;
+  return dp_wide_dt<false, true>(dt, dt, const_cast<void*>(values_s), meta_s, N, K, nullptr, nullptr, nullptr,
+                                 packed_dpT, nullptr, nullptr, nullptr, nullptr, AdamWStep{}, s);
+}
+
 hipError_t launch_adamw_double_prune(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s, const void* grads,
                                      float* m, float* v, int64_t N, int64_t K, const AdamWStep& c,
                                      void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {
   if (N == 0 || K == 0) return hipSuccess;
-  if (dt == Dt::BF16 && K % 16 == 0 && N % 16 == 0) {
-    dim3 g((unsigned)cdiv(K, DW_T), (unsigned)cdiv(N, DW_T));
-    if (grad == Dt::BF16)
-      double_prune_wide_kernel<true, uint16_t><<<g, kThreads, 0, s>>>((uint16_t*)values_s, meta_s, N, K,
-                                                                      (uint16_t*)values_dpT, meta_dpT, mask_dpT,
-                                                                      (const uint16_t*)grads, m, v, c);
-    else
-      double_prune_wide_kernel<true, float><<<g, kThreads, 0, s>>>((uint16_t*)values_s, meta_s, N, K,
-                                                                   (uint16_t*)values_dpT, meta_dpT, mask_dpT,
-                                                                   (const float*)grads, m, v, c);
-    return hipGetLastError();
-  }
+  if (wide_ok(dt, N, K))
+    return dp_wide_dt<true, false>(dt, grad, values_s, meta_s, N, K, values_dpT, meta_dpT, mask_dpT, nullptr,
+                                   nullptr, grads, m, v, c, s);
   // other shapes and fp32 weights: the elementwise update, then the double prune
   hipError_t e = launch_adamw(dt, grad, values_s, grads, m, v, N * (K / 2), c, s);
   if (e != hipSuccess) return e;
   return launch_double_prune(dt, values_s, meta_s, N, K, values_dpT, meta_dpT, mask_dpT, s);
+}
+
+hipError_t launch_adamw_double_prune_packed(Dt dt, Dt grad, void* values_s, const uint32_t* meta_s,
+                                            const void* grads, float* m, float* v, int64_t N, int64_t K,
+                                            const AdamWStep& c, void* packed_s, void* packed_dpT, hipStream_t s) {
+  if (N == 0 || K == 0) return hipSuccess;
+  return dp_wide_dt<true, true>(dt, grad, values_s, meta_s, N, K, nullptr, nullptr, nullptr, packed_dpT, packed_s,
+                                grads, m, v, c, s);
 }
 
 }  // namespace slope

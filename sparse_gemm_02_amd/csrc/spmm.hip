@@ -269,6 +269,9 @@ __global__ __launch_bounds__(GF::THREADS, 1) void spmm_split_kernel(
 }
 
 typedef Geo<256, 256, 3, 2, 4> GeoBig;
+static_assert(GeoBig::BM == kPackRows && GeoBig::KS == kPackCols && GeoBig::A_BYTES == kPackValueBytes &&
+                  GeoBig::CHUNK_BYTES == kPackChunkBytes,
+              "tile chunks are the stage slices of the wide tile");
 // the narrower tile for the rows of a product's last, partly filled round
 typedef Geo<256, 128, 3, 2, 4> GeoHalf;
 static_assert(GeoHalf::BM == GeoBig::BM && GeoHalf::CHUNK_BYTES == GeoBig::CHUNK_BYTES, "same row tiles and chunks");

@@ -22,14 +22,13 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_r,
   tc = in_group / gsize;
 }
 
-// Host side: how many row tiles of a sparse product to run in full-width
-// tiles when the remaining rows take half-width tiles (twice the column tiles,
-// each costing about 0.65 of a full tile, measured on the OPT-66B shapes), so that
-// a launch whose full-width grid would end in a partly filled round of
-// blocks finishes sooner.  Minimises the estimated time in rounds of `cus`
-// blocks over all-half-width and the last 4 * cus rows (more half-width rows
-// than that only pay when every row does, as for a single column tile); ties
-// keep more full-width rows.
+// Host side: how many row tiles of a product to run in full tiles when the
+// remaining rows take half tiles (cols_half blocks per row, each costing
+// about 0.65 of a full tile, measured on the OPT-66B shapes), so that a
+// launch whose full-tile grid would end in a partly filled round of blocks
+// finishes sooner.  Minimises the estimated time in rounds of `cus` blocks
+// over all-half and the last 4 * cus rows (more half rows than that only pay
+// when every row does, as for a single column tile); ties keep more full rows.
 inline int64_t full_width_rows(int64_t tiles_r, int64_t cols_full, int64_t cols_half, int64_t cus) {
   auto rounds = [cus](int64_t blocks) { return (blocks + cus - 1) / cus; };
   auto cost = [&](int64_t rows) { return 100 * rounds(rows * cols_full) + 65 * rounds((tiles_r - rows) * cols_half); };

@@ -6,8 +6,8 @@ Orchestration only: every arithmetic step runs in libslope.so through the
 binding in this package (the forward product with the fused adapter term, the
 double-pruned dX product with the adapter's dX term, the weight gradient at the
 static mask, the adapter gradients, the optimizer step fused with the double
-prune, and the operand packing).  torch provides device memory, streams and
-the autograd graph.
+prune and the rewrite of both GEMM operands, and the operand packing).  torch
+provides device memory, streams and the autograd graph.
 
 Layer state, per SLoPe (explainer 2.A and 2.B; discussion page, "Memory
 Footprint Reduction During Pretraining and Inference" and "Choice of
@@ -16,8 +16,9 @@ Optimizer"):
     values  [N, K/2]        kept weights of W_s (an nn.Parameter; its .grad is
                             the weight gradient in the same slot order)
     meta    [N, K/32] int32 positions of the kept weights (static mask)
-    values_dpT, meta_dpT    the double-pruned transposed weight W_dp^T
-    packed_s, packed_dpT    tile-chunk copies of both for the GEMM kernels
+    packed_s                W_s in tile-chunk form, the forward's operand
+    packed_dpT              the double-pruned transposed weight W_dp^T, kept
+                            only in tile-chunk form (the dX product's operand)
     L [K, r], R [r, N]      the adapter (nn.Parameters), when rank > 0
 
 Formats: bf16 or fp16 weights and activations (one format per layer), with K
@@ -27,7 +28,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (slope_adamw, slope_adamw_double_prune, slope_compress24, slope_double_prune,
+from . import (slope_adamw, slope_adamw_double_prune_packed, slope_compress24, slope_double_prune_packed,
                slope_lowrank_grads_packed, slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes,
                slope_masked_wgrad_packed, slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes,
                slope_packed_tokens_bytes, slope_prune24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed)
@@ -119,8 +120,6 @@ class SparseLinear(torch.nn.Module):
         del mask
         self.values = torch.nn.Parameter(values)
         self.register_buffer("meta", meta)
-        self.register_buffer("values_dpT", torch.empty((K, N // 2), dtype=dt, device=dev))
-        self.register_buffer("meta_dpT", torch.empty((K, (N // 4 + 7) // 8), dtype=torch.int32, device=dev))
         self.register_buffer("packed_s", _bytes(slope_packed_sparse_bytes(N, K), dev))
         self.register_buffer("packed_dpT", _bytes(slope_packed_sparse_bytes(K, N), dev))
         if L is not None:
@@ -136,18 +135,12 @@ class SparseLinear(torch.nn.Module):
 
     @torch.no_grad()
     def refresh(self) -> None:
-        """Re-derive W_dp^T and the packed operands from the current values
-        (needed after changing `values` by other means than SparseAdamW)."""
-        slope_double_prune(self.values, self.meta, self.out_features, self.in_features, self.values_dpT,
-                           self.meta_dpT)
-        self.repack()
-
-    @torch.no_grad()
-    def repack(self) -> None:
-        """Rewrite the tile-chunk operands from values / values_dpT."""
+        """Re-derive both GEMM operands from the current values: W_s's tile
+        chunks and the double-pruned W_dp^T's (needed after changing `values`
+        by other means than SparseAdamW)."""
         N, K = self.out_features, self.in_features
         slope_pack_sparse(self.values, self.meta, N, K, self.packed_s)
-        slope_pack_sparse(self.values_dpT, self.meta_dpT, K, N, self.packed_dpT)
+        slope_double_prune_packed(self.values, self.meta, N, K, self.packed_dpT)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.shape[-1] != self.in_features or x.dtype != self.values.dtype:
@@ -161,10 +154,11 @@ class SparseAdamW(torch.optim.Optimizer):
     """AdamW for SparseLinear layers (and any other bf16 / fp32 parameters).
 
     The compressed values of each layer are updated by the fused kernel that
-    also re-derives the double-pruned transposed weight, after which the
-    layer's packed operands are rewritten; other parameters (the adapter
-    factors) take the elementwise kernel.  Moments are fp32, two per stored
-    value: the optimizer state of a 2:4 weight is half that of a dense one."""
+    also rewrites them inside W_s's tile chunks and re-derives the
+    double-pruned transposed weight's tile chunks, so both GEMM operands are
+    current after one pass; other parameters (the adapter factors) take the
+    elementwise kernel.  Moments are fp32, two per stored value: the
+    optimizer state of a 2:4 weight is half that of a dense one."""
 
     def __init__(self, modules, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, extra_params=()):
         modules = list(modules)
@@ -202,9 +196,9 @@ class SparseAdamW(torch.optim.Optimizer):
                 g = p.grad.contiguous()
                 layer = self._layer_of.get(p)
                 if layer is not None:
-                    slope_adamw_double_prune(p, layer.meta, g, st["exp_avg"], st["exp_avg_sq"], layer.out_features,
-                                             layer.in_features, layer.values_dpT, layer.meta_dpT, st["step"], **hp)
-                    layer.repack()
+                    slope_adamw_double_prune_packed(p, layer.meta, g, st["exp_avg"], st["exp_avg_sq"],
+                                                    layer.out_features, layer.in_features, layer.packed_s,
+                                                    layer.packed_dpT, st["step"], **hp)
                 else:
                     slope_adamw(p, g, st["exp_avg"], st["exp_avg_sq"], st["step"], **hp)
         return loss
@@ -213,10 +207,12 @@ class SparseAdamW(torch.optim.Optimizer):
 def training_state_bytes(layer: SparseLinear, optimizer: SparseAdamW | None = None) -> dict:
     """Bytes the layer's training state occupies on the GPU, next to a dense
     bf16 layer of the same shape trained with AdamW (weight, gradient, two fp32
-    moments).  `canonical` counts what the pages' accounting counts (the
-    compressed weight and its double-pruned copy, the gradient at the kept
-    weights, two moments per kept weight; no separate binary mask is kept:
-    the metadata is the mask); `packed` adds the tile-chunk operand copies."""
+    moments).  `canonical` counts what the pages' accounting counts: the
+    compressed weight, its double-pruned copy (held only as tile chunks, 1.125
+    bytes per weight up to the chunks' padding), the gradient at the kept
+    weights and two moments per kept weight; no separate binary mask is kept
+    (the metadata is the mask).  `with_packed_operands` adds W_s's tile-chunk
+    copy, the forward's operand."""
     def nb(t):
         return 0 if t is None else t.numel() * t.element_size()
     N, K = layer.out_features, layer.in_features
@@ -226,8 +222,8 @@ def training_state_bytes(layer: SparseLinear, optimizer: SparseAdamW | None = No
         moments = nb(optimizer.state[vals]["exp_avg"]) + nb(optimizer.state[vals]["exp_avg_sq"])
     else:
         moments = 2 * 4 * vals.numel()
-    canonical = nb(vals) + nb(layer.meta) + nb(layer.values_dpT) + nb(layer.meta_dpT) + grad + moments
+    canonical = nb(vals) + nb(layer.meta) + nb(layer.packed_dpT) + grad + moments
     dense = N * K * (2 + 2 + 4 + 4)
-    packed = canonical + nb(layer.packed_s) + nb(layer.packed_dpT)
+    packed = canonical + nb(layer.packed_s)
     return {"canonical": canonical, "with_packed_operands": packed, "dense_adamw": dense,
             "canonical_ratio": canonical / dense, "with_packed_ratio": packed / dense}

@@ -121,3 +121,25 @@ def check_adamw_update(p0, g, m0, v0, step, hp, p_gpu, m_gpu, v_gpu):
         assert (p_gpu == p_ref).mean() >= 0.99
     assert (np.abs(m_gpu.astype(np.float64) - m_ref) <= spacing(m_ref, "f32") + 2.0 ** -20 * m_terms).all()
     assert (np.abs(v_gpu.astype(np.float64) - v_ref) <= spacing(v_ref, "f32") + 2.0 ** -20 * v_terms).all()
+
+
+def pack_sparse_reference(vals_bits, meta_words, rows, cols):
+    """The tile-chunk layout as include/slope.h states it, built with numpy."""
+    S_ = -(-cols // 64)
+    tiles = -(-rows // 256)
+    wpr = meta_words.shape[1]
+    out = np.zeros((tiles, S_, 18432), dtype=np.uint8)
+    vb = np.zeros((tiles * 256, S_ * 32), dtype=np.uint16)
+    vb[:rows, :cols // 2] = vals_bits
+    mw = np.zeros((tiles * 256, 2 * S_), dtype=np.uint32)
+    mw[:rows, :wpr] = meta_words
+    for t in range(tiles):
+        for s_ in range(S_):
+            blk = vb[256 * t:256 * t + 256, 32 * s_:32 * s_ + 32].reshape(256, 4, 8)   # [row][granule][value]
+            a = np.zeros((256, 4, 8), dtype=np.uint16)
+            for r in range(256):
+                for c in range(4):
+                    a[r, c ^ ((r >> 2) & 3)] = blk[r, c]
+            out[t, s_, :16384] = a.reshape(-1).view(np.uint8)
+            out[t, s_, 16384:] = np.ascontiguousarray(mw[256 * t:256 * t + 256, 2 * s_:2 * s_ + 2]).view(np.uint8).reshape(-1)
+    return out.reshape(-1)

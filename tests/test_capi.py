@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -186,6 +186,40 @@ def test_adamw_argument_errors(lib):
                                         FAKE + 1, None) == -3
     assert lib.slope_adamw_double_prune(bf, bf, FAKE, FAKE, FAKE, FAKE, FAKE, 64, (1 << 22) + 4, ctypes.byref(ok),
                                         FAKE, FAKE, None, None) == -6
+
+
+def test_packed_double_prune_argument_errors(lib):
+    """The entry points that write tile chunks straight from the double prune:
+    16-bit only, both dimensions multiples of 16, packed buffers at least the
+    size slope_packed_sparse_bytes reports."""
+    bf, f16, f32 = 1, 2, 0
+    ok = S.AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    need_dp = S.slope_packed_sparse_bytes(256, 512)        # W_dp^T: rows K = 256, cols N = 512
+    need_s = S.slope_packed_sparse_bytes(512, 256)         # W_s: rows N = 512, cols K = 256
+    dp = lib.slope_double_prune_packed
+    assert dp(f32, FAKE, FAKE, 512, 256, FAKE, need_dp, None) == -6
+    assert dp(7, FAKE, FAKE, 512, 256, FAKE, need_dp, None) == -1
+    assert dp(bf, FAKE, FAKE, -16, 256, FAKE, need_dp, None) == -1
+    assert dp(bf, None, FAKE, 512, 256, FAKE, need_dp, None) == -1
+    assert dp(bf, FAKE, FAKE, 512, 256, FAKE + 8, need_dp, None) == -3
+    assert dp(bf, FAKE, FAKE, 520, 256, FAKE, 1 << 30, None) == -2      # N % 16
+    assert dp(f16, FAKE, FAKE, 512, 264, FAKE, 1 << 30, None) == -2     # K % 16
+    assert dp(bf, FAKE, FAKE, 512, 256, FAKE, need_dp - 1, None) == -4
+    assert dp(bf, FAKE, FAKE, (1 << 21) + 16, 256, FAKE, 1 << 40, None) == -6
+    up = lib.slope_adamw_double_prune_packed
+    args = lambda dt=bf, g=bf, N=512, K=256, hp=ok, ps=FAKE, nps=need_s, pd=FAKE, npd=need_dp: (
+        dt, g, FAKE, FAKE, FAKE, FAKE, FAKE, N, K, ctypes.byref(hp) if hp is not None else None, ps, nps, pd, npd, None)
+    assert up(*args(dt=f32)) == -6
+    assert up(*args(g=9)) == -1
+    assert up(*args(hp=None)) == -1
+    assert up(*args(hp=S.AdamWParams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0))) == -1
+    assert up(*args(ps=None)) == -1
+    assert up(*args(pd=FAKE + 4)) == -3
+    assert up(*args(N=520, nps=1 << 30, npd=1 << 30)) == -2
+    assert up(*args(K=264, nps=1 << 30, npd=1 << 30)) == -2
+    assert up(*args(nps=need_s - 1)) == -4
+    assert up(*args(npd=need_dp - 1)) == -4
+    assert up(*args(K=(1 << 21) + 16, nps=1 << 40, npd=1 << 40)) == -6
 
 
 def test_binding_refuses_host_tensors(lib):

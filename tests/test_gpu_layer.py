@@ -2,11 +2,13 @@
 against the oracle: one forward / backward / optimizer step / forward cycle.
 
 The layer only orchestrates C-ABI calls, so this checks that it feeds each
-call the right operands: construction state bit-exact (mask, compression,
-double prune), products and gradients within the bf16 tolerance, the update
-within the optimizer bound of the values the backward produced, the new W_dp^T
-bit-exact against the oracle's double prune of the stored values, and the next
-forward against the oracle on the updated weights.
+call the right operands: construction state bit-exact (mask, compression, the
+tile chunks of W_s and of its double prune), products and gradients within the
+bf16 tolerance, the update within the optimizer bound of the values the
+backward produced, both operands' tile chunks bit-exact against the oracle's
+values and double prune of the stored values, and the next forward against
+the oracle on the updated weights.  The tile-chunk layout comes from a numpy
+restatement of include/slope.h.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,18 @@ import oracle
 from sparse_gemm_02_amd.layer import SparseAdamW, SparseLinear, training_state_bytes
 from workloads import layer_inputs
 
-from gpu_util import TOL, check_adamw_update, dev, host, host_f64, normwise, say
+from gpu_util import TOL, check_adamw_update, dev, host, host_f64, normwise, pack_sparse_reference, say
+
+
+def _chunks_match(layer, vals, meta, vdp, mdp):
+    """The layer's packed W_s and W_dp^T equal the tile chunks of the given
+    compressed values (raw bits) and metadata."""
+    N, K = layer.out_features, layer.in_features
+    bits = lambda a: np.asarray(a).view(np.uint16)
+    want_s = pack_sparse_reference(bits(vals), meta, N, K)
+    want_dp = pack_sparse_reference(bits(vdp), mdp, K, N)
+    return (np.array_equal(layer.packed_s.cpu().numpy()[:want_s.size], want_s)
+            and np.array_equal(layer.packed_dpT.cpu().numpy()[:want_dp.size], want_dp))
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +58,7 @@ def test_layer_forward_backward_step(T, N, K, r):
     vs_ref, ms_ref, _ = oracle.compress24(d["W"], mask_ref)
     vdp_ref, mdp_ref, _ = oracle.double_prune(vs_ref, ms_ref, N, K)
     assert np.array_equal(host(layer.values), vs_ref) and np.array_equal(host(layer.meta), ms_ref)
-    assert np.array_equal(host(layer.values_dpT), vdp_ref) and np.array_equal(host(layer.meta_dpT), mdp_ref)
+    assert _chunks_match(layer, vs_ref, ms_ref, vdp_ref, mdp_ref)
 
     La, Ra = (d["L"], d["R"]) if r else (None, None)
     tol = TOL["bf16"]
@@ -78,7 +91,7 @@ def test_layer_forward_backward_step(T, N, K, r):
                            opt.state[p]["exp_avg_sq"].cpu().numpy())
     assert np.array_equal(host(layer.meta), ms_ref)
     vdp1, mdp1, _ = oracle.double_prune(new_vs, ms_ref, N, K)
-    assert np.array_equal(host(layer.values_dpT), vdp1) and np.array_equal(host(layer.meta_dpT), mdp1)
+    assert _chunks_match(layer, new_vs, ms_ref, vdp1, mdp1)
 
     # the next forward and dX run on the updated, repacked weights
     x2 = X.clone().requires_grad_(True)
@@ -93,13 +106,16 @@ def test_layer_forward_backward_step(T, N, K, r):
     assert normwise(host_f64(x2.grad), dx2) <= tol
 
     # training state against a dense bf16 layer with AdamW: 7.25 of 12 bytes per weight
-    # (values of W_s and W_dp^T, gradient, two fp32 moments, plus metadata words rounded up per row)
+    # (values of W_s and W_dp^T, gradient, two fp32 moments, plus metadata words rounded up per row;
+    # W_dp^T is held as tile chunks of 256 rows x 64 columns, 18432 bytes each)
     acc = training_state_bytes(layer, opt)
     words = lambda cols: -(-(cols // 4) // 8)
-    assert acc["canonical"] == 7 * N * K + 4 * N * words(K) + 4 * K * words(N)
-    assert acc["dense_adamw"] == 12 * N * K
-    if K % 32 == 0 and N % 32 == 0:
+    chunks = lambda rows, cols: -(-rows // 256) * -(-cols // 64) * 18432
+    assert acc["canonical"] == 6 * N * K + 4 * N * words(K) + chunks(K, N)
+    if K % 256 == 0 and N % 64 == 0:
+        assert acc["canonical"] == 7 * N * K + 4 * N * words(K) + 4 * K * words(N)
         assert abs(acc["canonical_ratio"] - 7.25 / 12) < 1e-12
+    assert acc["dense_adamw"] == 12 * N * K
 
 
 def test_layer_f16_step():
@@ -130,7 +146,7 @@ def test_layer_f16_step():
     check_adamw_update(vs_ref, g, z, z, 1, hp, host(layer.values), st["exp_avg"].cpu().numpy(),
                        st["exp_avg_sq"].cpu().numpy())
     vdp1, mdp1, _ = oracle.double_prune(host(layer.values), ms_ref, N, K)
-    assert np.array_equal(host(layer.values_dpT), vdp1) and np.array_equal(host(layer.meta_dpT), mdp1)
+    assert _chunks_match(layer, host(layer.values), ms_ref, vdp1, mdp1)
 
 
 def test_two_layer_mlp_gradients_flow():

@@ -15,7 +15,8 @@ import oracle
 import sparse_gemm_02_amd as S
 from workloads import f32_to_bf16_bits, layer_inputs
 
-from gpu_util import TOL, Compressed, dev, dev_meta, empty, host, host_f64, normwise, say, torch_dtype, workspace
+from gpu_util import (TOL, Compressed, dev, dev_meta, empty, host, host_f64, normwise, pack_sparse_reference, say,
+                      torch_dtype, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -218,28 +219,6 @@ def test_spmm_bwd_dx(T, N, K, out_dt):
 
 # ------------------------------------------------------------------ packed sparse operands (tile chunks)
 
-def _pack_sparse_reference(vals_bits, meta_words, rows, cols):
-    """The tile-chunk layout as include/slope.h states it, built with numpy."""
-    S_ = -(-cols // 64)
-    tiles = -(-rows // 256)
-    wpr = meta_words.shape[1]
-    out = np.zeros((tiles, S_, 18432), dtype=np.uint8)
-    vb = np.zeros((tiles * 256, S_ * 32), dtype=np.uint16)
-    vb[:rows, :cols // 2] = vals_bits
-    mw = np.zeros((tiles * 256, 2 * S_), dtype=np.uint32)
-    mw[:rows, :wpr] = meta_words
-    for t in range(tiles):
-        for s_ in range(S_):
-            blk = vb[256 * t:256 * t + 256, 32 * s_:32 * s_ + 32].reshape(256, 4, 8)   # [row][granule][value]
-            a = np.zeros((256, 4, 8), dtype=np.uint16)
-            for r in range(256):
-                for c in range(4):
-                    a[r, c ^ ((r >> 2) & 3)] = blk[r, c]
-            out[t, s_, :16384] = a.reshape(-1).view(np.uint8)
-            out[t, s_, 16384:] = np.ascontiguousarray(mw[256 * t:256 * t + 256, 2 * s_:2 * s_ + 2]).view(np.uint8).reshape(-1)
-    return out.reshape(-1)
-
-
 @pytest.mark.parametrize("rows,cols", [(256, 64), (300, 272), (4, 16), (520, 1040)])
 def test_pack_sparse_layout(rows, cols):
     say(f"pack_sparse rows={rows} cols={cols}")
@@ -250,7 +229,7 @@ def test_pack_sparse_layout(rows, cols):
     packed.fill_(0xCD)
     S.slope_pack_sparse(dev(vs), dev_meta(ms), rows, cols, packed)
     torch.cuda.synchronize()
-    assert np.array_equal(packed.cpu().numpy(), _pack_sparse_reference(vs, ms, rows, cols))
+    assert np.array_equal(packed.cpu().numpy(), pack_sparse_reference(vs, ms, rows, cols))
 
 
 PACKED_SHAPES = [(64, 256, 256), (300, 528, 272), (512, 768, 1024), (1, 64, 128), (257, 272, 528), (0, 64, 64),
