@@ -60,13 +60,17 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
         lv[2 * e] = F::to_f32((uint16_t)(w[e] & 0xFFFFu));
         lv[2 * e + 1] = F::to_f32((uint16_t)(w[e] >> 16));
       }
-    } else {
+    } else {                                       // clamped columns, then masked (no branch per load)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) lv[c] = c0 + c < r ? F::to_f32(L[(int64_t)k * r + c0 + c]) : 0.f;
+      for (int c = 0; c < 8; ++c) {
+        const float x = F::to_f32(L[(int64_t)k * r + (c0 + c < r ? c0 + c : r - 1)]);
+        lv[c] = c0 + c < r ? x : 0.f;
+      }
     }
 #pragma unroll
     for (int i = 0; i < kXlMaxT; ++i) {
-      const float x = i < T ? F::to_f32(X[(int64_t)i * K + k]) : 0.f;
+      const float xv = F::to_f32(X[(int64_t)(i < T ? i : T - 1) * K + k]);
+      const float x = i < T ? xv : 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(x, lv[c], acc[i][c]);
     }

@@ -108,11 +108,44 @@ __device__ __forceinline__ typename Fmt16<H>::v8 frag_tr(const char* tile, int t
 // column n = n0 + wn*WN + b*32 + l%32 and rows k = k0 + wk*WK + a*32 + 8q + 4(l/32)
 // + i (i < 4) in elements 4q+i, i.e. one whole 2:4 group of k; keep the two
 // positions meta_s names and write them in slot order (plus the masked dense copy).
+//
+// The metadata word of a lane's rows is the same for the four q of a 32-row
+// block (k >> 5 does not depend on q or lane / 32), so the FN x FK words are
+// loaded first, all in flight, from clamped addresses (a word past N or K is
+// never used); with accumulate so are the previous values pairs.  Loads under
+// the bounds branches would each be followed by a wait.
 template <class G, typename O>
 __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], const uint32_t* __restrict__ meta,
                                             int K, int N, int64_t k0, int64_t n0, int wk, int wn, int lane,
                                             O* __restrict__ dWv, O* __restrict__ dWd, int accumulate) {
   const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
+  uint32_t words[G::FN][G::FK];
+#pragma unroll
+  for (int b = 0; b < G::FN; ++b) {
+    const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
+    const int64_t nc = n < N ? n : N - 1;
+#pragma unroll
+    for (int a = 0; a < G::FK; ++a) {
+      const int64_t w = (k0 + wk * G::WK + a * 32) >> 5;
+      words[b][a] = meta[nc * wpr + (w < wpr ? w : wpr - 1)];
+    }
+  }
+  float prev[G::FN][G::FK][4][2];
+  if (accumulate) {
+#pragma unroll
+    for (int b = 0; b < G::FN; ++b) {
+      const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
+#pragma unroll
+      for (int a = 0; a < G::FK; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
+          const O* vp = (n < N && k < K) ? dWv + n * (K / 2) + 2 * (k >> 2) : dWv;
+          prev[b][a][q][0] = load_out(vp);
+          prev[b][a][q][1] = load_out(vp + 1);
+        }
+    }
+  }
 #pragma unroll
   for (int b = 0; b < G::FN; ++b) {
     const int64_t n = n0 + wn * G::WN + b * 32 + (lane & 31);
@@ -124,7 +157,7 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], c
         const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
         if (k >= K) continue;
         const int64_t g = k >> 2;
-        const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
+        const uint32_t nib = (words[b][a] >> (4 * (g & 7))) & 0xFu;
         const uint32_t i0 = nib & 3u, i1 = nib >> 2;
         const float r0 = acc[a][b][4 * q], r1 = acc[a][b][4 * q + 1];
         const float r2 = acc[a][b][4 * q + 2], r3 = acc[a][b][4 * q + 3];
@@ -132,7 +165,7 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], c
         float v0 = i0 == 0 ? r0 : (i0 == 1 ? r1 : r2);
         float v1 = i1 == 3 ? r3 : (i1 == 2 ? r2 : r1);
         O* vp = dWv + n * (K / 2) + 2 * g;
-        if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
+        if (accumulate) { v0 += prev[b][a][q][0]; v1 += prev[b][a][q][1]; }
         store_pair(vp, v0, v1);
         if (dWd) {
           O* dp = dWd + n * K + k;
