@@ -4,10 +4,11 @@ One step is one pass of the whole hot path over the four linears of an OPT-66B
 transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 36864->9216; T = 8192 tokens, adapter rank 72, bf16 with fp32 accumulation):
 
-    prune24 -> compress24 -> double_prune (straight into W_dp^T's tile
-    chunks) -> pack_sparse (W_s into tile chunks) -> spmm_fwd (+ fused
-    adapter) -> spmm_bwd_dx (+ the adapter's dX term) -> pack_tokens (X and
-    dY into token chunks) -> masked_wgrad -> lowrank_grads (dL, dR)
+    prune_compress24 (magnitude 2:4 prune and compression of W, with W_s
+    written as tile chunks, one pass) -> double_prune (straight into W_dp^T's
+    tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx (+ the
+    adapter's dX term) -> pack_tokens (X and dY into token chunks)
+    -> masked_wgrad -> lowrank_grads (dL, dR)
 
 The three products run on the packed operands (the *_packed entry points);
 the packing passes are part of the step.  A `decode` object adds the
@@ -17,9 +18,11 @@ step (AdamW on the compressed values fused with the double prune, writing both
 GEMM operands' tile chunks, and AdamW on the adapter factors), also as HBM
 bytes per second.
 
-prune24 and compress24 run once per layer in training (the forward mask is
-static); they are kept inside the timed step so the step covers every kernel of
-the path.  Inputs are synthetic (seeded Gaussian, see workloads/) and resident in
+The prune and compression run once per layer in training (the forward mask is
+static); they are kept inside the timed step so the step covers every row of
+the path.  The standalone prune24, compress24 and pack_sparse entry points
+compute the same results in three passes (bitwise; tested) and can be timed
+with --profile-op.  Inputs are synthetic (seeded Gaussian, see workloads/) and resident in
 HBM before the timed region starts.
 
 Prints one JSON line.  `value` is dense-equivalent TFLOP/s of the step's GEMMs
@@ -55,7 +58,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
-    ap.add_argument("--profile-op", choices=OPS + ("adamw_double_prune", "copy"), default=None,
+    ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "adamw_double_prune", "copy"),
+                    default=None,
                     help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
     ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
     ap.add_argument("--repeat", type=int, default=10)
@@ -115,12 +119,16 @@ class Linear:
                 "masked_wgrad": T * N * K, "lowrank_grads": 2 * T * r * (K + N)}
 
 
-OPS = ("prune24", "compress24", "double_prune", "pack_sparse", "spmm_fwd", "spmm_bwd_dx", "pack_tokens",
-       "masked_wgrad", "lowrank_grads")
+OPS = ("prune_compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "pack_tokens", "masked_wgrad",
+       "lowrank_grads")
 
 
 def pack_sparse(S, li):
     S.slope_pack_sparse(li.vs, li.ms, li.N, li.K, li.ps)
+
+
+def prune_compress(S, li):
+    S.slope_prune_compress24(li.W, li.vs, li.ms, packed=li.ps)
 
 
 def double_prune(S, li):
@@ -150,10 +158,8 @@ def step(lins, S, ev=None):
     """One pass of the hot path over every linear; optional per-op events."""
     for li in lins:
         calls = (
-            ("prune24", lambda: S.slope_prune24(li.W, li.mask)),
-            ("compress24", lambda: S.slope_compress24(li.W, li.mask, li.vs, li.ms)),
+            ("prune_compress24", lambda: prune_compress(S, li)),
             ("double_prune", lambda: double_prune(S, li)),
-            ("pack_sparse", lambda: pack_sparse(S, li)),
             ("spmm_fwd", lambda: S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
             ("spmm_bwd_dx", lambda: bwd_dx(S, li)),
             ("pack_tokens", lambda: pack(S, li)),
@@ -258,9 +264,8 @@ def profile_mode(args, wl, T):
     lins = [Linear(l.name, l.K, l.N, T, wl.r, seed=0, index=i) for i, l in sel]
     for li in lins:  # prerequisites of every op
         S.slope_prune24(li.W, li.mask)
-        S.slope_compress24(li.W, li.mask, li.vs, li.ms)
+        prune_compress(S, li)
         double_prune(S, li)
-        pack_sparse(S, li)
         pack(S, li)
         S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
         bwd_dx(S, li)
@@ -272,7 +277,9 @@ def profile_mode(args, wl, T):
     op = args.profile_op
     for _ in range(args.repeat):
         for li in lins:
-            if op == "prune24":
+            if op == "prune_compress24":
+                prune_compress(S, li)
+            elif op == "prune24":
                 S.slope_prune24(li.W, li.mask)
             elif op == "compress24":
                 S.slope_compress24(li.W, li.mask, li.vs, li.ms)
@@ -456,8 +463,8 @@ def main():
                        frac_dense_peak_useful=uf / t / 1e12 / PEAK_BF16_DENSE_TFLOPS)
     # algorithmic HBM bytes: per weight for the pruning ops, per activation
     # element (read + written once) for the packing pass
-    hbm = {"prune24": lambda l: 3.0 * l.N * l.K, "compress24": lambda l: 4.125 * l.N * l.K,
-           "double_prune": lambda l: 2.25 * l.N * l.K, "pack_sparse": lambda l: 2 * 1.125 * l.N * l.K,
+    # (prune_compress24: W read, values + metadata + W_s's tile chunks written)
+    hbm = {"prune_compress24": lambda l: 4.25 * l.N * l.K, "double_prune": lambda l: 2.25 * l.N * l.K,
            "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
     for op, f in hbm.items():
         by = sum(f(l) for l in lins)

@@ -110,6 +110,25 @@ slope_status slope_wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_
 slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask,
                            void* W_s_or_null, void* stream);
 
+/* slope_prune24 followed by slope_compress24 of its mask, in one pass over W
+ * (explainer 2.A: the forward weight pruned 2:4 along its rows, once, at
+ * initialisation; discussion page, "Memory Footprint": two 16-bit non-zeros
+ * plus their indices per four weights), optionally also writing W_s's
+ * tile-chunk form for the *_packed products.
+ *   W         [rows, cols] dt, input
+ *   mask      [rows, cols] uint8 output as slope_prune24 writes it, or NULL
+ *   values    [rows, cols/2] dt output, meta [rows, ceil(cols/32)] uint32 output
+ *   packed    NULL, or caller-owned device memory of at least
+ *             slope_packed_sparse_bytes(rows, cols) bytes (16-bit dt,
+ *             cols % 16 == 0), overwritten with slope_pack_sparse's result
+ * Results equal the separate calls, bit for bit.  Errors: SLOPE_ERR_SHAPE if
+ * cols % 4 != 0 (cols % 16 != 0 with packed); SLOPE_ERR_UNSUPPORTED for a
+ * packed float32 matrix or cols > 2^21 with packed; SLOPE_ERR_WORKSPACE if
+ * packed_bytes is short. */
+slope_status slope_prune_compress24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask_or_null,
+                                    void* values, uint32_t* meta, void* packed_or_null, int64_t packed_bytes,
+                                    void* stream);
+
 /* Compressed form of W under a mask (discussion page, "Memory Footprint":
  * two 16-bit non-zeros plus their indices per four weights).
  *   W, mask   [rows, cols] inputs (mask byte != 0 = kept)

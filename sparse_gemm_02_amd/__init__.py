@@ -32,7 +32,7 @@ __all__ = [
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
     "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_lowrank_grads_workspace_bytes",
     "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
-    "slope_double_prune_packed", "slope_adamw_double_prune_packed", "EXPORTED_SYMBOLS",
+    "slope_double_prune_packed", "slope_adamw_double_prune_packed", "slope_prune_compress24", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,7 @@ _SIGS = {
     "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
                                         _vp]),
     "slope_double_prune_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "slope_prune_compress24": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
     "slope_adamw_double_prune_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _i64,
                                                _vp, _i64, _vp]),
 }
@@ -339,6 +340,15 @@ def slope_adamw(params, grads, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
     hp = _hp(step, lr, beta1, beta2, eps, weight_decay)
     _check("slope_adamw", library().slope_adamw(_dt(params), _dt(grads), _nn(params), _nn(grads), _f32(m), _f32(v),
                                                 n, ctypes.byref(hp), _s(stream)))
+
+
+def slope_prune_compress24(W, values, meta, mask=None, packed=None, stream=None) -> None:
+    """Magnitude 2:4 prune and compression of W [rows, cols] in one pass, with
+    the mask and W_s's tile-chunk form as optional outputs."""
+    rows, cols = W.shape
+    nb = packed.numel() * packed.element_size() if packed is not None else 0
+    _check("slope_prune_compress24", library().slope_prune_compress24(
+        _dt(W), _nn(W), rows, cols, _p(mask), _nn(values), _nn(meta), _p(packed), nb, _s(stream)))
 
 
 def slope_double_prune_packed(values_s, meta_s, N, K, packed_dpT, stream=None) -> None:

@@ -112,6 +112,27 @@ slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t 
   return from_hip(slope::launch_prune24((Dt)dt, W, rows, cols, mask, W_s_or_null, (hipStream_t)stream));
 }
 
+slope_status slope_prune_compress24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask_or_null,
+                                    void* values, uint32_t* meta, void* packed_or_null, int64_t packed_bytes,
+                                    void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0 || packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(W, true));
+  SLOPE_TRY(ptr(mask_or_null, false));
+  SLOPE_TRY(ptr(values, true));
+  SLOPE_TRY(ptr(meta, true));
+  SLOPE_TRY(ptr(packed_or_null, false));
+  if (cols % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || !in_range(cols)) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_or_null) {
+    if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // tile chunks hold 16-bit values
+    if (cols % 16) return SLOPE_ERR_SHAPE;
+    if (cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+    if (packed_bytes < slope::packed_sparse_bytes(rows, cols)) return SLOPE_ERR_WORKSPACE;
+  }
+  return from_hip(slope::launch_prune_compress24((Dt)dt, W, rows, cols, mask_or_null, values, meta, packed_or_null,
+                                                 (hipStream_t)stream));
+}
+
 slope_status slope_compress24(slope_dtype dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols,
                               void* values, uint32_t* meta, int32_t* invalid_groups_or_null, void* stream) {
   if (!dt_ok(dt) || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;

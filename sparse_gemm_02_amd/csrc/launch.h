@@ -25,6 +25,10 @@ hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t 
                              uint32_t* meta, int32_t* invalid, hipStream_t s);
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s);
+// prune24 and compress24 in one pass (mask optional); with packed (16-bit,
+// cols % 16 == 0) also W_s's tile chunks.
+hipError_t launch_prune_compress24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* values,
+                                   uint32_t* meta, void* packed, hipStream_t s);
 
 // Per-update constants of AdamW, derived on the host in double precision and
 // rounded once to fp32:

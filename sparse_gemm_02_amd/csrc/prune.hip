@@ -80,6 +80,99 @@ __global__ __launch_bounds__(kThreads) void prune24_kernel(const E* __restrict__
   }
 }
 
+// ------------------------------------------------------------------ prune24 + compress24 in one pass
+// Lane f of the grid -> (row, pair p) over rows_pad x pairs_pad: groups 2p and
+// 2p+1 of the row (columns 8p .. 8p+7), read as one 8- or 16-byte load, so a
+// wave reads one contiguous run of the row and writes its 4 kept values, 8
+// mask bytes (if asked for) contiguously; the four lanes of a metadata word
+// (groups 8w .. 8w+7) OR their nibbles together with shuffles and the first
+// writes it.  With PK (16-bit, cols % 16 == 0) the 8 bytes of values also go
+// to W_s's tile chunk (lanes 2c, 2c+1 of a chunk row fill granule c) and the
+// word to the chunk's metadata; rows_pad and pairs_pad cover whole chunks and
+// lanes past the matrix write the chunks' zero padding.  The selection is
+// prune24's, and with a mask of exactly two per group compress24 keeps those
+// two: results equal the two passes (and pack_sparse), bit for bit.
+template <typename E, bool PK>
+__global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __restrict__ W, int64_t rows,
+                                                                   int64_t cols, int64_t rows_pad,
+                                                                   int64_t pairs_pad, uint32_t* __restrict__ mask4,
+                                                                   E* __restrict__ values, uint32_t* __restrict__ meta,
+                                                                   char* __restrict__ packed) {
+  typedef typename Vec4<E>::T V;
+  const int64_t gpr = cols / 4, wpr = cdiv(gpr, 8);
+  const int64_t total = rows_pad * pairs_pad;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform loop bound: every lane of a wave takes part in the shuffles
+  for (int64_t base = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); base < total; base += stride) {
+    const int64_t f = base + lane;
+    const int64_t row = f < total ? f / pairs_pad : rows_pad;
+    const int64_t p = f < total ? f - row * pairs_pad : 0;
+    const int64_t g0 = 2 * p;                      // first group of the pair
+    const bool in_row = row < rows;
+    const int ng = in_row ? (g0 + 2 <= gpr ? 2 : (g0 < gpr ? 1 : 0)) : 0;   // groups of the pair in the matrix
+    uint32_t nibs = 0, mb[2] = {0u, 0u};
+    E kept[4] = {(E)0, (E)0, (E)0, (E)0};
+    if (ng > 0) {
+      V v[2];
+      const V* src = reinterpret_cast<const V*>(W) + row * gpr + g0;
+      v[0] = __builtin_nontemporal_load(src);
+      v[1] = __builtin_nontemporal_load(src + (ng > 1 ? 1 : 0));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        E e[4];
+        unpack(v[j], e);
+        const uint32_t keep = top2_of_4(mag_key(e[0]), mag_key(e[1]), mag_key(e[2]), mag_key(e[3]));
+        const uint32_t nib = pair_nibble(keep);
+        const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+        if (j < ng) {
+          nibs |= nib << (4 * j);
+          mb[j] = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
+          kept[2 * j] = i0 == 0 ? e[0] : (i0 == 1 ? e[1] : e[2]);
+          kept[2 * j + 1] = i1 == 3 ? e[3] : (i1 == 2 ? e[2] : e[1]);
+        }
+      }
+      E* vp = values + row * (cols / 2) + 2 * g0;
+      uint32_t* mp = mask4 ? mask4 + row * gpr + g0 : nullptr;
+      constexpr uintptr_t kAlign = 4 * sizeof(E);             // the four kept values in one store
+      if (ng == 2 && (reinterpret_cast<uintptr_t>(vp) & (kAlign - 1)) == 0) {
+        if constexpr (sizeof(E) == 2)
+          *reinterpret_cast<u32x2*>(vp) =
+              u32x2{(uint32_t)__builtin_bit_cast(uint16_t, kept[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, kept[1]) << 16),
+                    (uint32_t)__builtin_bit_cast(uint16_t, kept[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, kept[3]) << 16)};
+        else
+          *reinterpret_cast<u32x4*>(vp) = u32x4{(uint32_t)kept[0], (uint32_t)kept[1], (uint32_t)kept[2], (uint32_t)kept[3]};
+      } else {
+        for (int j = 0; j < 2 * ng; ++j) vp[j] = kept[j];
+      }
+      if (mp) {
+        if (ng == 2 && (reinterpret_cast<uintptr_t>(mp) & 7) == 0)
+          *reinterpret_cast<u32x2*>(mp) = u32x2{mb[0], mb[1]};
+        else
+          for (int j = 0; j < ng; ++j) mp[j] = mb[j];
+      }
+    }
+    // the metadata word of groups 8w .. 8w+7 (w = p / 4) from its four lanes
+    uint32_t word = nibs << (8 * (p & 3));
+    word |= __shfl_xor(word, 1, 4);
+    word |= __shfl_xor(word, 2, 4);
+    if ((p & 3) == 0 && in_row && g0 < gpr) meta[row * wpr + (p >> 2)] = word;
+    if constexpr (PK) {
+      static_assert(sizeof(E) == 2, "tile chunks hold 16-bit values");
+      if (f < total && 8 * p < cdiv(cols, kPackCols) * kPackCols) {
+        const int r = (int)(row % kPackRows), c = (int)((p >> 1) & 3), sw = (r >> 2) & 3;
+        char* const chunk = packed + pack_chunk_offset(row, 8 * p, cols);
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, kept[0]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, kept[1]) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, kept[2]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, kept[3]) << 16);
+        *reinterpret_cast<u32x2*>(chunk + r * 64 + ((c ^ sw) << 4) + (p & 1) * 8) = u32x2{lo, hi};
+        if ((p & 3) == 0) *reinterpret_cast<uint32_t*>(chunk + kPackValueBytes + r * 8 + ((p >> 2) & 1) * 4) = word;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ compress24
 // Thread slot f -> (row, word, j): eight consecutive lanes build one metadata
 // word (groups 8*word .. 8*word+7 of a row) and OR their nibbles together.
@@ -437,6 +530,37 @@ hipError_t dp_wide_dt(Dt dt, Dt grad, void* vals, const uint32_t* meta, int64_t 
 bool wide_ok(Dt dt, int64_t N, int64_t K) { return dt != Dt::F32 && K % 16 == 0 && N % 16 == 0; }
 
 }  // namespace
+
+hipError_t launch_prune_compress24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* values,
+                                   uint32_t* meta, void* packed, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  // group pairs per row, four per metadata word; with packed output whole
+  // 256-row chunks and eight pairs per chunk column
+  const int64_t rows_pad = packed ? cdiv(rows, kPackRows) * kPackRows : rows;
+  const int64_t words_pad = packed ? 4 * 2 * cdiv(cols, kPackCols) : 4 * cdiv(cols / 4, 8);
+  const int grid = grid_for(rows_pad * words_pad, kThreads);
+  uint32_t* m4 = (uint32_t*)mask;
+  char* pk = (char*)packed;
+  if (dt == Dt::F32) {
+    prune_compress24_kernel<uint32_t, false><<<grid, kThreads, 0, s>>>((const uint32_t*)W, rows, cols, rows_pad,
+                                                                       words_pad, m4, (uint32_t*)values, meta, nullptr);
+  } else if (dt == Dt::F16) {
+    if (packed)
+      prune_compress24_kernel<_Float16, true><<<grid, kThreads, 0, s>>>((const _Float16*)W, rows, cols, rows_pad,
+                                                                        words_pad, m4, (_Float16*)values, meta, pk);
+    else
+      prune_compress24_kernel<_Float16, false><<<grid, kThreads, 0, s>>>((const _Float16*)W, rows, cols, rows_pad,
+                                                                         words_pad, m4, (_Float16*)values, meta, nullptr);
+  } else {
+    if (packed)
+      prune_compress24_kernel<uint16_t, true><<<grid, kThreads, 0, s>>>((const uint16_t*)W, rows, cols, rows_pad,
+                                                                        words_pad, m4, (uint16_t*)values, meta, pk);
+    else
+      prune_compress24_kernel<uint16_t, false><<<grid, kThreads, 0, s>>>((const uint16_t*)W, rows, cols, rows_pad,
+                                                                         words_pad, m4, (uint16_t*)values, meta, nullptr);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,
                                void* values_dpT, uint32_t* meta_dpT, uint8_t* mask_dpT, hipStream_t s) {

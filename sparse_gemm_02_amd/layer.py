@@ -28,10 +28,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (slope_adamw, slope_adamw_double_prune_packed, slope_compress24, slope_double_prune_packed,
-               slope_lowrank_grads_packed, slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes,
-               slope_masked_wgrad_packed, slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes,
-               slope_packed_tokens_bytes, slope_prune24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed)
+from . import (slope_adamw, slope_adamw_double_prune_packed, slope_double_prune_packed, slope_lowrank_grads_packed,
+               slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes, slope_masked_wgrad_packed,
+               slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes, slope_packed_tokens_bytes,
+               slope_prune_compress24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed)
 
 __all__ = ["SparseLinear", "SparseAdamW", "training_state_bytes"]
 
@@ -112,15 +112,15 @@ class SparseLinear(torch.nn.Module):
         dev, dt = weight.device, weight.dtype
         self.in_features, self.out_features = K, N
         weight = weight.contiguous()
-        mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
-        slope_prune24(weight, mask)
+        # one pass: magnitude 2:4 mask, compressed values and metadata, and
+        # W_s's tile chunks (no dense mask is materialised)
         values = torch.empty((N, K // 2), dtype=dt, device=dev)
         meta = torch.empty((N, (K // 4 + 7) // 8), dtype=torch.int32, device=dev)
-        slope_compress24(weight, mask, values, meta)
-        del mask
+        packed_s = _bytes(slope_packed_sparse_bytes(N, K), dev)
+        slope_prune_compress24(weight, values, meta, packed=packed_s)
         self.values = torch.nn.Parameter(values)
         self.register_buffer("meta", meta)
-        self.register_buffer("packed_s", _bytes(slope_packed_sparse_bytes(N, K), dev))
+        self.register_buffer("packed_s", packed_s)
         self.register_buffer("packed_dpT", _bytes(slope_packed_sparse_bytes(K, N), dev))
         if L is not None:
             if L.shape[0] != K or R.shape[1] != N or L.shape[1] != R.shape[0]:
@@ -131,7 +131,7 @@ class SparseLinear(torch.nn.Module):
         else:
             self.L = self.R = None
             self.rank = 0
-        self.refresh()
+        slope_double_prune_packed(self.values, self.meta, N, K, self.packed_dpT)
 
     @torch.no_grad()
     def refresh(self) -> None:

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -220,6 +220,25 @@ def test_packed_double_prune_argument_errors(lib):
     assert up(*args(nps=need_s - 1)) == -4
     assert up(*args(npd=need_dp - 1)) == -4
     assert up(*args(K=(1 << 21) + 16, nps=1 << 40, npd=1 << 40)) == -6
+
+
+def test_prune_compress24_argument_errors(lib):
+    """The one-pass prune and compression: the optional tile chunks need a
+    16-bit matrix, cols % 16 == 0 and enough bytes."""
+    bf, f32 = 1, 0
+    f = lib.slope_prune_compress24
+    need = S.slope_packed_sparse_bytes(64, 256)
+    assert f(7, FAKE, 64, 256, None, FAKE, FAKE, None, 0, None) == -1
+    assert f(bf, FAKE, -1, 256, None, FAKE, FAKE, None, 0, None) == -1
+    assert f(bf, None, 64, 256, None, FAKE, FAKE, None, 0, None) == -1
+    assert f(bf, FAKE, 64, 256, None, None, FAKE, None, 0, None) == -1
+    assert f(bf, FAKE, 64, 256, FAKE + 2, FAKE, FAKE, None, 0, None) == -3
+    assert f(bf, FAKE, 64, 254, None, FAKE, FAKE, None, 0, None) == -2
+    assert f(f32, FAKE, 64, 256, None, FAKE, FAKE, FAKE, 1 << 30, None) == -6
+    assert f(bf, FAKE, 64, 260, None, FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    assert f(bf, FAKE, 64, 256, None, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert f(bf, FAKE, 64, (1 << 21) + 16, None, FAKE, FAKE, FAKE, 1 << 40, None) == -6
+    assert f(bf, FAKE, 64, 256, None, FAKE, FAKE, FAKE + 8, need, None) == -3
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -96,6 +96,42 @@ def test_compress24_bit_exact(dt, rows, cols):
     assert int(inv.item()) == inv_ref == 0
 
 
+# ragged last metadata words (cols 68, 36, 4, 272), a partial last chunk
+# column (272, 80) and whole chunks
+FUSED_PRUNE_SHAPES = PRUNE_SHAPES + [(300, 272), (520, 1040), (2, 80)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("rows,cols", FUSED_PRUNE_SHAPES)
+def test_prune_compress24_fused(dt, rows, cols):
+    """One pass equals prune24 + compress24 (+ pack_sparse) of the oracle, bit
+    for bit, with and without the optional mask and tile-chunk outputs."""
+    say(f"prune_compress24 {dt} {rows}x{cols}")
+    if dt == "f16":
+        W = layer_inputs(cols, rows, 1, 1, "f16", seed=rows + cols, which=("W",))["W"]
+    else:
+        W = _special_matrix(rows, cols, dt, 3 * rows + cols)
+    bits = lambda a: np.asarray(a).view(np.uint16) if np.asarray(a).dtype == np.float16 else np.asarray(a)
+    mask_ref, _ = oracle.prune24(W)
+    vals_ref, meta_ref, _ = oracle.compress24(W, mask_ref)
+    c = Compressed(rows, cols, torch_dtype(dt))
+    mask = torch.full((rows, cols), 7, dtype=torch.uint8, device="cuda")
+    pk = None
+    if dt != "f32" and cols % 16 == 0:
+        pk = torch.full((S.slope_packed_sparse_bytes(rows, cols),), 0x5A, dtype=torch.uint8, device="cuda")
+    S.slope_prune_compress24(dev(W), c.values, c.meta, mask=mask, packed=pk)
+    torch.cuda.synchronize()
+    assert (host(mask) == mask_ref).all()
+    assert (bits(host(c.values)) == bits(vals_ref)).all()
+    assert (host(c.meta) == meta_ref).all()
+    if pk is not None:
+        assert np.array_equal(pk.cpu().numpy(), pack_sparse_reference(bits(vals_ref), meta_ref, rows, cols))
+    c2 = Compressed(rows, cols, torch_dtype(dt))
+    S.slope_prune_compress24(dev(W), c2.values, c2.meta)
+    torch.cuda.synchronize()
+    assert (bits(host(c2.values)) == bits(vals_ref)).all() and (host(c2.meta) == meta_ref).all()
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_compress24_user_masks(dt):
     say(f"compress24 user masks {dt}")
