@@ -352,32 +352,68 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
   const int64_t n0 = (int64_t)blockIdx.y * DW_T, k0 = (int64_t)blockIdx.x * DW_T;
   const int64_t in_wpr = cdiv(K / 4, 8), out_wpr = cdiv(N / 4, 8);
 
-  // phase 1: row r, dense columns 16c .. 16c+15 (compressed groups 4c .. 4c+3)
+  // phase 1: row r, dense columns 16c .. 16c+15 (compressed groups 4c .. 4c+3).
+  // The loads of the thread's four rows (and with UPD their gradients and
+  // moments) go out first, from clamped addresses: a row or column past the
+  // matrix reads a valid element, is zeroed and never stored.  Loads under
+  // bounds branches would each be waited for before the next was issued.
   const int c = tid & 7;
+  const int64_t kc = k0 + 16 * c;
+  const bool col_ok = kc < K;                         // K % 16 == 0: the 16 columns are all in or all out
+  const int64_t kcc = col_ok ? kc : K - 16;
+  u32x4 w4[4];
+  uint32_t nibs[4];
+  int64_t el[4];
+  bool ok[4];
+  float gf[UPD ? 4 : 1][8], mf[UPD ? 4 : 1][8], vf[UPD ? 4 : 1][8];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int64_t row = n0 + it * 32 + (tid >> 3);
+    const int64_t rowc = row < N ? row : N - 1;
+    ok[it] = row < N && col_ok;
+    el[it] = rowc * (K / 2) + kcc / 2;                // the thread's eight compressed values
+    w4[it] = *reinterpret_cast<const u32x4*>(vals + el[it]);
+    nibs[it] = meta[rowc * in_wpr + (kcc >> 5)] >> (16 * (c & 1));
+    if constexpr (UPD) {
+      load8_f32(grads + el[it], gf[it]);
+      load8_f32(m + el[it], mf[it]);
+      load8_f32(v + el[it], vf[it]);
+    }
+  }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = it * 32 + (tid >> 3);
-    const int64_t row = n0 + r, kc = k0 + 16 * c;
-    u32x4 w4 = {0u, 0u, 0u, 0u};
-    uint32_t nibs = 0;
-    if (row < N && kc < K) {                          // K % 16 == 0: the 16 columns are all in or all out
-      const int64_t e = row * (K / 2) + kc / 2;       // the thread's eight compressed values
-      w4 = *reinterpret_cast<const u32x4*>(vals + e);
-      nibs = meta[row * in_wpr + (kc >> 5)] >> (16 * (c & 1));
-      if constexpr (UPD) {
-        w4 = adamw8_16<H>(w4, grads + e, m + e, v + e, hp);
-        *reinterpret_cast<u32x4*>(vals + e) = w4;
+    if constexpr (UPD) {
+      typedef Fmt16<H> F;
+      u32x4 nw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = adamw_apply(F::to_f32((uint16_t)(w4[it][i] & 0xFFFFu)), gf[it][2 * i], mf[it][2 * i],
+                                     vf[it][2 * i], hp);
+        const float hi = adamw_apply(F::to_f32((uint16_t)(w4[it][i] >> 16)), gf[it][2 * i + 1], mf[it][2 * i + 1],
+                                     vf[it][2 * i + 1], hp);
+        nw[i] = (uint32_t)F::from_f32(lo) | ((uint32_t)F::from_f32(hi) << 16);
+      }
+      w4[it] = nw;
+      if (ok[it]) {
+        const int64_t e = el[it];
+        *reinterpret_cast<u32x4*>(vals + e) = nw;
+        store8_f32(m + e, mf[it]);
+        store8_f32(v + e, vf[it]);
         if constexpr (PK) {                           // the same granule of W_s's chunk row
+          const int64_t row = n0 + r;
           const int rs = (int)(row % kPackRows), gs = (int)((kc % kPackCols) / 16);
-          *reinterpret_cast<u32x4*>(pk_s + pack_chunk_offset(row, kc, K) + rs * 64 + ((gs ^ ((rs >> 2) & 3)) << 4)) = w4;
+          *reinterpret_cast<u32x4*>(pk_s + pack_chunk_offset(row, kc, K) + rs * 64 + ((gs ^ ((rs >> 2) & 3)) << 4)) = nw;
         }
       }
     }
-    uint32_t d[8];                                    // 16 dense bf16, two per word
+    const u32x4 wv = ok[it] ? w4[it] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t nb = ok[it] ? nibs[it] : 0u;
+    uint32_t d[8];                                    // 16 dense 16-bit values, two per word
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t nib = (nibs >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
-      const uint32_t w = w4[g], v0 = w & 0xFFFFu, v1 = w >> 16;
+      const uint32_t nib = (nb >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
+      const uint32_t w = wv[g], v0 = w & 0xFFFFu, v1 = w >> 16;
       uint32_t e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = i1 == (uint32_t)j ? v1 : (i0 == (uint32_t)j ? v0 : 0u);
