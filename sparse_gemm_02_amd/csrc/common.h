@@ -80,6 +80,10 @@ __device__ __forceinline__ float load_out(const float* p) { return *p; }
 template <typename O> __device__ __forceinline__ uint16_t out16_bits(float v);
 template <> __device__ __forceinline__ uint16_t out16_bits<uint16_t>(float v) { return f32_to_bf16_bits(v); }
 template <> __device__ __forceinline__ uint16_t out16_bits<_Float16>(float v) { return f32_to_f16_bits(v); }
+// ... and 16-bit output patterns back to fp32.
+template <typename O> __device__ __forceinline__ float out16_to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float out16_to_f32<uint16_t>(uint32_t b) { return bf16_bits_to_f32((uint16_t)b); }
+template <> __device__ __forceinline__ float out16_to_f32<_Float16>(uint32_t b) { return f16_bits_to_f32((uint16_t)b); }
 
 // The two 16-bit input formats of the matrix kernels, selected by H (fp16)
 // or not (bf16): operand vectors, conversions of raw 16-bit patterns, and the

@@ -110,21 +110,34 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FM][G::FT], O*
 }
 
 // Load the transposed tile from Out[t][m] (the inverse of store_tile; rows or
-// columns outside [T, M] read as 0).
+// columns outside [T, M] read as 0).  Four consecutive m per load (M % 4 ==
+// 0: all in or all out), every load from a clamped valid address and then
+// masked, so they are all in flight together.
 template <class G, typename O>
 __device__ __forceinline__ void load_tile(f32x16 (&acc)[G::FM][G::FT], const O* __restrict__ Y, int64_t m0,
                                           int64_t t0, int M, int T, int wm, int wt, int lane) {
 #pragma unroll
   for (int ft = 0; ft < G::FT; ++ft) {
     const int64_t t = t0 + wt * G::WT + ft * 32 + (lane & 31);
+    const int64_t tc = t < T ? t : T - 1;
 #pragma unroll
     for (int fm = 0; fm < G::FM; ++fm) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t m = m0 + wm * G::WM + fm * 32 + 8 * q + 4 * (lane >> 5);
         const bool ok = t < T && m < M;
+        const O* p = Y + tc * M + (m < M ? m : M - 4);
+        float x[4];
+        if constexpr (sizeof(O) == 2) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+          x[0] = out16_to_f32<O>(w[0] & 0xFFFFu); x[1] = out16_to_f32<O>(w[0] >> 16);
+          x[2] = out16_to_f32<O>(w[1] & 0xFFFFu); x[3] = out16_to_f32<O>(w[1] >> 16);
+        } else {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+          x[0] = w[0]; x[1] = w[1]; x[2] = w[2]; x[3] = w[3];
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[fm][ft][4 * q + i] = ok ? load_out(Y + t * M + m + i) : 0.f;
+        for (int i = 0; i < 4; ++i) acc[fm][ft][4 * q + i] = ok ? x[i] : 0.f;
       }
     }
   }

@@ -50,11 +50,6 @@ struct WGeo {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16-bit output patterns back to fp32 (bf16 for uint16_t outputs, fp16 for _Float16).
-template <typename O> __device__ __forceinline__ float out16_to_f32(uint32_t bits);
-template <> __device__ __forceinline__ float out16_to_f32<uint16_t>(uint32_t b) { return bf16_bits_to_f32((uint16_t)b); }
-template <> __device__ __forceinline__ float out16_to_f32<_Float16>(uint32_t b) { return f16_bits_to_f32((uint16_t)b); }
-
 // Two adjacent outputs as one store (4-byte aligned for 16-bit outputs, 8-byte for fp32).
 template <typename O>
 __device__ __forceinline__ void store_pair(O* p, float a, float b) {
@@ -303,14 +298,22 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint16_t* __rest
   const int64_t nchunks = chunks_c * Tch;
   for (int64_t q = blockIdx.x; q < nchunks; q += gridDim.x) {
     const int64_t cb = q % chunks_c, ts = q / chunks_c;
-    // 32 token rows x 512 bytes, 16 bytes per load
+    // 32 token rows x 512 bytes, 16 bytes per load; all four loads in flight
+    // at once (clamped addresses, entries past T or C then zeroed: loads under
+    // a bounds branch would each be waited for)
+    u32x4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int piece = tid + 256 * j, t = piece >> 5, g = piece & 31;
       const int64_t tg = ts * kChunkTokens + t, cg = cb * kChunkRows + 8 * g;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (tg < T && cg < C) v = *reinterpret_cast<const u32x4*>(src + tg * C + cg);   // C % 8 == 0
-      *reinterpret_cast<u32x4*>(&tile[t * kPitch + 8 * g]) = v;
+      const int64_t tc = tg < T ? tg : T - 1, cc = cg < C ? cg : C - 8;   // C % 8 == 0
+      v[j] = *reinterpret_cast<const u32x4*>(src + tc * C + cc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + 256 * j, t = piece >> 5, g = piece & 31;
+      const int64_t tg = ts * kChunkTokens + t, cg = cb * kChunkRows + 8 * g;
+      *reinterpret_cast<u32x4*>(&tile[t * kPitch + 8 * g]) = (tg < T && cg < C) ? v[j] : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
     // thread r writes chunk row r: 8 tokens per granule
