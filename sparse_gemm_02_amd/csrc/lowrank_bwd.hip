@@ -76,28 +76,41 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
 #pragma unroll
     for (int fj = 0; fj < FJ; ++fj) acc[fm][fj] = f32x16{};
 
-  for (int64_t s = s0; s < s1; ++s) {
+  // chunk s's loads are issued while chunk s-1 is multiplied: the A
+  // fragments and B's slice go to registers one chunk ahead (the buffer
+  // resources return 0 past the split's chunks and past Tpad)
+  typedef typename Fmt16<H>::v8 v8;
+  v8 an[2][2];
+  u32x4 bn[FJ];
+  auto load_chunk = [&](int64_t s) {
     const uint32_t c = (uint32_t)(s - s0) * kChunkBytes;
-    typename Fmt16<H>::v8 a[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) a[ks][fm] = __builtin_bit_cast(typename Fmt16<H>::v8, load16(ra, c + a_off[fm][ks]));
-    char* buf = bs[s & 1];
+      for (int fm = 0; fm < 2; ++fm) an[ks][fm] = __builtin_bit_cast(v8, load16(ra, c + a_off[fm][ks]));
     const uint32_t tb = (uint32_t)(s * kChunkTokens) * 2;
 #pragma unroll
-    for (int i = 0; i < FJ; ++i) {
-      const u32x4 v = load16(st_lo[i] ? rl : rh, st_src[i] + tb);
-      *reinterpret_cast<u32x4*>(buf + st_dst[i]) = v;
-    }
+    for (int i = 0; i < FJ; ++i) bn[i] = load16(st_lo[i] ? rl : rh, st_src[i] + tb);
+  };
+  if (s0 < s1) load_chunk(s0);
+  for (int64_t s = s0; s < s1; ++s) {
+    v8 a[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm) a[ks][fm] = an[ks][fm];
+    char* buf = bs[s & 1];
+#pragma unroll
+    for (int i = 0; i < FJ; ++i) *reinterpret_cast<u32x4*>(buf + st_dst[i]) = bn[i];
+    load_chunk(s + 1);                                 // past s1 these read 0 and are not used
     __syncthreads();                                   // slice s staged; slice s-2's buffer no longer read
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      typename Fmt16<H>::v8 h[FJ], l[FJ];
+      v8 h[FJ], l[FJ];
 #pragma unroll
       for (int fj = 0; fj < FJ; ++fj) {
-        h[fj] = *reinterpret_cast<const typename Fmt16<H>::v8*>(buf + b_off[ks][fj]);
-        l[fj] = *reinterpret_cast<const typename Fmt16<H>::v8*>(buf + BROWS * 64 + b_off[ks][fj]);
+        h[fj] = *reinterpret_cast<const v8*>(buf + b_off[ks][fj]);
+        l[fj] = *reinterpret_cast<const v8*>(buf + BROWS * 64 + b_off[ks][fj]);
       }
 #pragma unroll
       for (int fj = 0; fj < FJ; ++fj)
