@@ -266,9 +266,10 @@ slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, c
                                         void* dL, void* dR, int accumulate, void* stream);
 
 /* Bytes of device workspace slope_spmm_fwd_decode needs for T <= 64 tokens:
- * fp32 split partial sums, plus the adapter's workspace
- * (slope_lowrank_workspace_bytes) when r > 0.  Host-only;
- * SLOPE_ERR_UNSUPPORTED if T > 64 or r > 128. */
+ * fp32 split partial sums, plus, when r > 0, X . L in fp32 as
+ * [slices][T][rpad] (rpad = r rounded up to 16; one slice above four tokens,
+ * ceil(K / 2048) up to 64 at or below).  Host-only; SLOPE_ERR_UNSUPPORTED if
+ * T > 64 or r > 128. */
 slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);
 
 /* Few-token forward (T <= 64; the inference case of the discussion page's

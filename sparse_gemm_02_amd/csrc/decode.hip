@@ -9,11 +9,11 @@
 // from memory into registers (v_smfmac_f32_32x32x32_bf16, measured lane
 // layouts as in spmm.hip); a block's four waves cover one tile over one
 // k-range and write fp32 partial sums.  A second kernel adds the partial sums
-// in split order (deterministic), adds the adapter term and rounds once.  For
-// up to four tokens the adapter's X . L is computed in fp32 by an extra row of
-// blocks of the same launch, straight from L's own [K, r] layout; for more it
-// comes from the down-projection of lowrank.hip.  The up-projection reads R in
-// its own layout (no transposed copy of R).
+// in split order (deterministic), adds the adapter term and rounds once.  The
+// adapter's X . L is computed in fp32 by an extra row of blocks of the same
+// launch, straight from L's own [K, r] layout, while the other blocks stream
+// the weight; the up-projection reads R in its own layout (no transposed copy
+// of R).
 #include "common.h"
 #include "dma.h"
 #include "gemm_tile.h"
@@ -26,57 +26,93 @@ namespace {
 typedef Geo<256, 256, 3, 2, 4> Chunk;            // the tile-chunk geometry written by pack_sparse
 constexpr int kDecodeMaxT = 64;
 constexpr int kUnroll = 4;                       // stages whose loads are issued together
-constexpr int kXlMaxT = 4;                       // tokens whose X . L the partial kernel computes
-constexpr int kXlRows = 2048;                    // rows of L per k-slice of that X . L, at most
+constexpr int kXlTok = 4;                        // tokens per X . L block
+constexpr int kXlRows = 2048;                    // rows of L per k-slice of X . L (up to four tokens), at most
+static_assert(kXlRows / 256 <= 8, "up to four tokens a thread has at most 8 rows of a slice");
 constexpr int kXlMaxSlices = 64;
 
+// k-slices of the X . L blocks: up to four tokens the partial kernel is short,
+// so K is cut into slices of at most kXlRows rows (the reduce adds them in
+// order); with more tokens the weight streams long enough to hide one block
+// walking all of K, and one slice keeps the reduce's staging cheap.
+int xl_slices(int64_t T, int64_t K) {
+  if (T > kXlTok) return 1;
+  const int64_t n = cdiv(K, kXlRows);
+  return (int)(n < 1 ? 1 : (n > kXlMaxSlices ? kXlMaxSlices : n));
+}
+
 // xl[t][8cg .. 8cg+7] = sum over k in [k0, k1) of X[t][k] L[k][8cg ..] for
-// t < T <= 4 (columns past r are 0), fp32 with one fma per product.  Thread i
+// t < T <= 4 (columns past r are 0; X and xl start at the block's first
+// token), fp32 with one fma per product.  Thread i
 // takes rows k0 + i, k0 + i + 256, ...; the 256 per-thread sums are then added
 // by a fixed butterfly within each wave and the four wave sums in wave order,
 // so the result does not depend on timing.
-template <bool H>
+template <bool H, int kXlBatch>
 __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const uint16_t* __restrict__ L, int T,
                                            int K, int r, int rpad, int cg, int k0, int k1, float* __restrict__ xl) {
-  __shared__ float wsum[4][kXlMaxT * 8];
+  __shared__ float wsum[4][kXlTok * 8];
   typedef Fmt16<H> F;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c0 = 8 * cg;
   // with r % 8 == 0 a group starting below r lies inside the row: one 16-byte
   // load (L is 16-byte aligned); groups starting at or past r (the padding
   // up to rpad) read nothing and write zeros
   const bool vec = r % 8 == 0;
-  float acc[kXlMaxT][8];
+  float acc[kXlTok][8];
 #pragma unroll
-  for (int i = 0; i < kXlMaxT; ++i)
+  for (int i = 0; i < kXlTok; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
-#pragma unroll 4
-  for (int k = c0 < r ? k0 + (int)threadIdx.x : k1; k < k1; k += 256) {
-    float lv[8];
-    if (vec) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(L + (int64_t)k * r + c0);
+  // rows in batches of kXlBatch: every load of a batch (clamped to a valid
+  // row, masked afterwards) is issued before the first product, since with
+  // the weight streaming beside it each round trip to memory is long
+  if (vec) {
+    for (int kb = c0 < r ? k0 + (int)threadIdx.x : k1; kb < k1; kb += 256 * kXlBatch) {
+      u32x4 lw[kXlBatch];
+      uint16_t xr[kXlBatch][kXlTok];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lv[2 * e] = F::to_f32((uint16_t)(w[e] & 0xFFFFu));
-        lv[2 * e + 1] = F::to_f32((uint16_t)(w[e] >> 16));
+      for (int j = 0; j < kXlBatch; ++j) {
+        const int k = kb + 256 * j, kc = k < k1 ? k : k1 - 1;
+        lw[j] = *reinterpret_cast<const u32x4*>(L + (int64_t)kc * r + c0);
+#pragma unroll
+        for (int i = 0; i < kXlTok; ++i) xr[j][i] = X[(int64_t)(i < T ? i : T - 1) * K + kc];
       }
-    } else {                                       // clamped columns, then masked (no branch per load)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int j = 0; j < kXlBatch; ++j) {
+        const bool live = kb + 256 * j < k1;
+        float lv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lv[2 * e] = F::to_f32((uint16_t)(lw[j][e] & 0xFFFFu));
+          lv[2 * e + 1] = F::to_f32((uint16_t)(lw[j][e] >> 16));
+        }
+#pragma unroll
+        for (int i = 0; i < kXlTok; ++i) {
+          const float x = (live && i < T) ? F::to_f32(xr[j][i]) : 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(x, lv[c], acc[i][c]);
+        }
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int k = c0 < r ? k0 + (int)threadIdx.x : k1; k < k1; k += 256) {
+      float lv[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {                // clamped columns, then masked (no branch per load)
         const float x = F::to_f32(L[(int64_t)k * r + (c0 + c < r ? c0 + c : r - 1)]);
         lv[c] = c0 + c < r ? x : 0.f;
       }
-    }
 #pragma unroll
-    for (int i = 0; i < kXlMaxT; ++i) {
-      const float xv = F::to_f32(X[(int64_t)(i < T ? i : T - 1) * K + k]);
-      const float x = i < T ? xv : 0.f;
+      for (int i = 0; i < kXlTok; ++i) {
+        const float xv = F::to_f32(X[(int64_t)(i < T ? i : T - 1) * K + k]);
+        const float x = i < T ? xv : 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(x, lv[c], acc[i][c]);
+        for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(x, lv[c], acc[i][c]);
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < kXlMaxT; ++i)
+  for (int i = 0; i < kXlTok; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v = acc[i][c];
@@ -86,12 +122,12 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
     }
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < kXlMaxT; ++i)
+    for (int i = 0; i < kXlTok; ++i)
 #pragma unroll
       for (int c = 0; c < 8; ++c) wsum[wave][i * 8 + c] = acc[i][c];
   }
   __syncthreads();
-  if (threadIdx.x < kXlMaxT * 8) {
+  if (threadIdx.x < kXlTok * 8) {
     const int i = threadIdx.x / 8, c = threadIdx.x % 8;
     if (i < T && c0 + c < rpad)
       xl[i * rpad + c0 + c] = ((wsum[0][threadIdx.x] + wsum[1][threadIdx.x]) + wsum[2][threadIdx.x]) + wsum[3][threadIdx.x];
@@ -100,12 +136,15 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
 
 // part[split][t][n] (n < Npad) = sum over this split's k of X[t][k] W_s[n][k].
 // Block = 4 waves = one 256-row tile; wave w rows 64w .. 64w+63 (two 32-row
-// A operands), FT = 1 or 2 token tiles of 32.  With XL (T <= 4) the grid has
-// one more row of blocks, first: its block x < (rpad / 8) * slices writes
-// X . L's columns 8g .. 8g+7 (g = x % (rpad / 8)) over k-slice s = x / (rpad
-// / 8) of K to xl [s][T][rpad] (xl_columns) while the other rows stream the
-// weight.
-template <int FT, bool H, bool XL = false>
+// A operands), FT = 1 or 2 token tiles of 32.  With XL (the adapter on) the
+// grid has XR = ceil(XB / tiles) more rows of blocks, first, for the XB = G *
+// TG * slices X . L blocks (G = rpad / 8 column groups, TG = ceil(T / 4) token
+// groups): X . L block x (its index in those rows) writes the columns 8g ..
+// 8g+7 (g = x % G) for tokens 4tg .. 4tg+3 (tg = (x / G) % TG) over k-slice
+// s = x / (G * TG) of K to xl [s][T][rpad] (xl_columns, rows XB at a time)
+// while the other rows stream the weight.  The grid keeps the tiles' width: rows padded with idle
+// blocks to fit the X . L blocks measured up to twice as slow at T = 64.
+template <int FT, bool H, int XB = 0>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ X,
                                                              const char* __restrict__ packed, int T, int K,
                                                              int stages, int kc, int64_t Npad,
@@ -114,19 +153,23 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
                                                              int slices, float* __restrict__ xl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
+  int xrows = 0;
+  constexpr bool XL = XB > 0;
   if constexpr (XL) {
-    if (blockIdx.y == 0) {
-      const int groups = rpad / 8, x = blockIdx.x;
-      if (x < groups * slices) {
-        const int g = x % groups, sl = x / groups, rows = (K + slices - 1) / slices;
-        const int k0 = sl * rows, k1 = k0 + rows < K ? k0 + rows : K;
-        xl_columns<H>(X, L, T, K, r, rpad, g, k0, k1, xl + (int64_t)sl * T * rpad);
+    const int groups = rpad / 8, tgroups = (T + kXlTok - 1) / kXlTok, xb = groups * tgroups * slices;
+    xrows = (xb + (int)gridDim.x - 1) / (int)gridDim.x;
+    if ((int)blockIdx.y < xrows) {
+      const int x = blockIdx.y * gridDim.x + blockIdx.x;
+      if (x < xb) {
+        const int g = x % groups, tg = (x / groups) % tgroups, sl = x / (groups * tgroups);
+        const int rows = (K + slices - 1) / slices, k0 = sl * rows, k1 = k0 + rows < K ? k0 + rows : K;
+        const int t0 = tg * kXlTok, tn = T - t0 < kXlTok ? T - t0 : kXlTok;
+        xl_columns<H, XB>(X + (int64_t)t0 * K, L, tn, K, r, rpad, g, k0, k1, xl + ((int64_t)sl * T + t0) * rpad);
       }
       return;
     }
-    if ((int64_t)tile * 256 >= Npad) return;      // the grid is as wide as the X . L row needs
   }
-  const int split = XL ? blockIdx.y - 1 : blockIdx.y;
+  const int split = blockIdx.y - xrows;
   const int s0 = split * kc, s1 = (s0 + kc < stages) ? s0 + kc : stages;
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(packed + ((int64_t)tile * stages + s0) * Chunk::CHUNK_BYTES, (int64_t)(s1 - s0) * Chunk::CHUNK_BYTES);
@@ -219,9 +262,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
 }
 
 // Y[t][n] = sum over the splits (in order) of part + sum_j xl[t][j] R[j][n],
-// rounded once, with xl either the sum in slice order of fp32 [xl_slices][T]
-// [rpad] (xlf, from the partial kernel) or xlh + xll (X . L as a 16-bit hi/lo pair, prepared by the adapter's
-// down-projection; their fp32 sum is exact).  A block covers 64 consecutive n
+// rounded once, with xl the sum in slice order of fp32 [xl_slices][T][rpad]
+// (xlf, from the partial kernel).  A block covers 64 consecutive n
 // (one per lane) and TB tokens; its four waves split the work into quarters
 // (wave w: the w-th quarter of the splits, in order, and the w-th quarter of
 // the rank rows), each wave issuing its loads of partial sums (Q at a time)
@@ -236,10 +278,8 @@ constexpr int kReduceMaxRank = 128;
 template <typename O, int TB, int Q, bool H>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part, int splits, int T,
                                                             int64_t N, int64_t Npad, const uint16_t* __restrict__ R,
-                                                            const float* __restrict__ xlf, int xl_slices,
-                                                            const uint16_t* __restrict__ xlh,
-                                                            const uint16_t* __restrict__ xll, int r, int rpad,
-                                                            O* __restrict__ Y) {
+                                                            const float* __restrict__ xlf, int xl_slices, int r,
+                                                            int rpad, O* __restrict__ Y) {
   constexpr int RQ = kReduceMaxRank / 4;           // rank rows per wave, at most
   __shared__ float xl[TB][kReduceMaxRank];
   __shared__ float sum[4][TB][64];
@@ -262,20 +302,16 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
       const int i = e / rpad, j = e % rpad;
       const int t = tb + i < T ? tb + i : T - 1;
       float v = 0.f;
-      if (xlf) {                                   // eight slices' loads in flight, added in slice order
-        for (int sl0 = 0; sl0 < xl_slices; sl0 += 8) {
-          float t8[8];
+      for (int sl0 = 0; sl0 < xl_slices; sl0 += 8) {   // eight slices' loads in flight, added in slice order
+        float t8[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int sl = sl0 + q < xl_slices ? sl0 + q : xl_slices - 1;
-            t8[q] = xlf[((int64_t)sl * T + t) * rpad + j];
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (sl0 + q < xl_slices) v += t8[q];
+        for (int q = 0; q < 8; ++q) {
+          const int sl = sl0 + q < xl_slices ? sl0 + q : xl_slices - 1;
+          t8[q] = xlf[((int64_t)sl * T + t) * rpad + j];
         }
-      } else {
-        v = Fmt16<H>::to_f32(xlh[t * rpad + j]) + Fmt16<H>::to_f32(xll[t * rpad + j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (sl0 + q < xl_slices) v += t8[q];
       }
       xl[i][j] = tb + i < T ? v : 0.f;
     }
@@ -321,18 +357,16 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
 
 template <typename O, bool H>
 void launch_decode_reduce(const float* part, int splits, int64_t T, int64_t N, int64_t Npad, const uint16_t* R,
-                          const float* xf, int xs, const uint16_t* xh, const uint16_t* xo, int r, int rpad, O* Y,
-                          hipStream_t s) {
+                          const float* xf, int xs, int r, int rpad, O* Y, hipStream_t s) {
   if (T == 1) {
     dim3 g((unsigned)cdiv(N, 64), 1);
-    decode_reduce_kernel<O, 1, 8, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, xh, xo, r, rpad, Y);
+    decode_reduce_kernel<O, 1, 8, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, r, rpad, Y);
   } else if (T <= 4) {
     dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 4));
-    decode_reduce_kernel<O, 4, 8, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, xh, xo, r, rpad, Y);
+    decode_reduce_kernel<O, 4, 8, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, r, rpad, Y);
   } else {
     dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 16));
-    decode_reduce_kernel<O, 16, 4, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, xh, xo, r, rpad,
-                                                        Y);
+    decode_reduce_kernel<O, 16, 4, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, r, rpad, Y);
   }
 }
 
@@ -362,9 +396,14 @@ DecodePlan decode_plan(int64_t T, int64_t K, int64_t N) {
 
 }  // namespace
 
+// fp32 X . L slices [xl_slices][T][rpad] (rpad = r rounded up to 16)
+int64_t xl_bytes(int64_t T, int64_t K, int64_t r) {
+  return r > 0 ? cdiv((int64_t)xl_slices(T, K) * T * cdiv(r, 16) * 16 * 4, 256) * 256 : 0;
+}
+
 int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N) {
   if (T == 0 || N == 0) return 0;
-  return decode_plan(T, K, N).part_bytes + (r > 0 ? lowrank_workspace_bytes(T, K, r, N) : 0);
+  return decode_plan(T, K, N).part_bytes + xl_bytes(T, K, r);
 }
 
 namespace {
@@ -373,11 +412,20 @@ void decode_partial_launch(int64_t T, dim3 grid, const void* X, const void* pack
                            float* part, const void* L, int64_t r, int64_t rpad, int xs, float* xl, hipStream_t s) {
   const uint16_t* Xb = (const uint16_t*)X;
   const char* pk = (const char*)packed;
-  if (xl) {                                        // T <= 4 with the adapter: one more row of blocks for X . L
-    const unsigned xb = (unsigned)(rpad / 8 * xs);
-    dim3 g(grid.x > xb ? grid.x : xb, grid.y + 1);
-    decode_partial_kernel<1, H, true><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part,
-                                                        (const uint16_t*)L, (int)r, (int)rpad, xs, xl);
+  const uint16_t* Lb = (const uint16_t*)L;
+  if (xl) {                                        // the adapter on: leading rows of blocks for X . L
+    const int64_t xb = rpad / 8 * cdiv(T, kXlTok) * xs;
+    dim3 g(grid.x, grid.y + (unsigned)cdiv(xb, grid.x));
+    // up to four tokens a thread has at most eight rows of a slice: batches of 8
+    if (T <= kXlTok)
+      decode_partial_kernel<1, H, 8><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
+                                                       (int)r, (int)rpad, xs, xl);
+    else if (T <= 32)
+      decode_partial_kernel<1, H, 16><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
+                                                        (int)r, (int)rpad, xs, xl);
+    else
+      decode_partial_kernel<2, H, 16><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
+                                                        (int)r, (int)rpad, xs, xl);
   } else if (T <= 32) {
     decode_partial_kernel<1, H><<<grid, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, nullptr,
                                                      0, 0, 0, nullptr);
@@ -394,45 +442,25 @@ hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K
   const DecodePlan p = decode_plan(T, K, N);
   float* part = (float*)workspace;
   const bool ad = r > 0 && L != nullptr && R != nullptr;
-  // up to four tokens: X . L in fp32 by the partial kernel, in k-slices of
-  // at most kXlRows rows, [slices][T][rpad] after the partial sums (inside the
-  // adapter's share of the workspace, which holds 2 * 256 * rpad * 2 bytes of
-  // hi/lo pair alone: room for 64 slices of 4 tokens); more tokens: the
-  // adapter's down-projection into its hi/lo pair
-  const bool fused = ad && T <= kXlMaxT;
-  LowrankWs w;
-  float* xl = nullptr;
-  int64_t rpad = 0;
-  int xs = 0;
-  if (fused) {
-    xl = (float*)((char*)workspace + p.part_bytes);
-    rpad = cdiv(r, 16) * 16;
-    xs = (int)cdiv(K, kXlRows);
-    if (xs > kXlMaxSlices) xs = kXlMaxSlices;
-    if (xs < 1) xs = 1;
-  } else if (ad) {
-    w = lowrank_layout(in, (char*)workspace + p.part_bytes, T, K, r, N);
-    const hipError_t e = launch_lowrank_down(in, X, L, T, K, r, w, s);
-    if (e != hipSuccess) return e;
-    rpad = w.rpad;
-  }
+  // the adapter's X . L: fp32 slices [xs][T][rpad] after the partial sums
+  float* xl = ad ? (float*)((char*)workspace + p.part_bytes) : nullptr;
+  const int64_t rpad = ad ? cdiv(r, 16) * 16 : 0;
+  const int xs = ad ? xl_slices(T, K) : 0;
   dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
   if (in == Dt::F16)
     decode_partial_launch<true>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s);
   else
     decode_partial_launch<false>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s);
   const uint16_t* Ra = ad ? (const uint16_t*)R : nullptr;
-  const uint16_t* xh = ad && !fused ? w.xlh : nullptr;
-  const uint16_t* xo = ad && !fused ? w.xll : nullptr;
   const int rp = (int)rpad;
   if (out == Dt::BF16)
-    launch_decode_reduce<uint16_t, false>(part, p.splits, T, N, p.Npad, Ra, xl, xs, xh, xo, (int)r, rp, (uint16_t*)Y, s);
+    launch_decode_reduce<uint16_t, false>(part, p.splits, T, N, p.Npad, Ra, xl, xs, (int)r, rp, (uint16_t*)Y, s);
   else if (out == Dt::F16)
-    launch_decode_reduce<_Float16, true>(part, p.splits, T, N, p.Npad, Ra, xl, xs, xh, xo, (int)r, rp, (_Float16*)Y, s);
+    launch_decode_reduce<_Float16, true>(part, p.splits, T, N, p.Npad, Ra, xl, xs, (int)r, rp, (_Float16*)Y, s);
   else if (in == Dt::F16)
-    launch_decode_reduce<float, true>(part, p.splits, T, N, p.Npad, Ra, xl, xs, xh, xo, (int)r, rp, (float*)Y, s);
+    launch_decode_reduce<float, true>(part, p.splits, T, N, p.Npad, Ra, xl, xs, (int)r, rp, (float*)Y, s);
   else
-    launch_decode_reduce<float, false>(part, p.splits, T, N, p.Npad, Ra, xl, xs, xh, xo, (int)r, rp, (float*)Y, s);
+    launch_decode_reduce<float, false>(part, p.splits, T, N, p.Npad, Ra, xl, xs, (int)r, rp, (float*)Y, s);
   return hipGetLastError();
 }
 

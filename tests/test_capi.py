@@ -57,10 +57,13 @@ def test_size_queries(lib):
     assert S.slope_packed_tokens_bytes(8192, 9216) == 36 * 256 * 16384
     assert S.slope_packed_sparse_bytes(9216, 27648) == 36 * 432 * 18432
     assert S.slope_packed_sparse_bytes(300, 272) == 2 * 5 * 18432
-    # decode: fp32 partials (splits x T x padded N) plus the adapter's workspace
+    # decode: fp32 partials (splits x T x padded N) plus X . L in fp32 [slices][T][rpad]
     b0 = S.slope_decode_workspace_bytes(1, 9216, 0, 27648)
     assert b0 > 0 and b0 % 256 == 0 and b0 % (27648 * 4) == 0
-    assert S.slope_decode_workspace_bytes(1, 9216, 72, 27648) == b0 + S.slope_lowrank_workspace_bytes(1, 9216, 72, 27648)
+    xl = lambda slices, T, r: -(-slices * T * (-(-r // 16) * 16) * 4 // 256) * 256
+    assert S.slope_decode_workspace_bytes(1, 9216, 72, 27648) == b0 + xl(5, 1, 72)        # ceil(9216 / 2048) slices
+    assert S.slope_decode_workspace_bytes(4, 36864, 128, 256) == S.slope_decode_workspace_bytes(4, 36864, 0, 256) + xl(18, 4, 128)
+    assert S.slope_decode_workspace_bytes(64, 9216, 72, 256) == S.slope_decode_workspace_bytes(64, 9216, 0, 256) + xl(1, 64, 72)
     assert S.slope_decode_workspace_bytes(0, 9216, 0, 27648) == 0
     g = S.slope_lowrank_grads_workspace_bytes(8192, 9216, 72, 27648)
     assert g > S.slope_lowrank_workspace_bytes(8192, 9216, 72, 27648) + S.slope_lowrank_workspace_bytes(8192, 27648, 72, 9216)
