@@ -381,9 +381,14 @@ DecodePlan decode_plan(int64_t T, int64_t K, int64_t N) {
   p.tiles = cdiv(N, 256);
   p.Npad = p.tiles * 256;
   // about 2048 blocks, with at most 0.02 K / T splits so that the partial sums
-  // (splits x T x N x 8 bytes written and read) stay small next to the weight
+  // (splits x T x N x 8 bytes written and read) stay small next to the weight.
+  // With many tokens a block spends long on each stage and the weight stream is
+  // no longer the limit: then keep at least about 1024 blocks (latency hiding on
+  // a few blocks per CU) as long as each still runs 16 stages or more.
   int64_t want = cdiv(2048, p.tiles < 1 ? 1 : p.tiles);
-  const int64_t cap = (int64_t)(0.02 * (double)K / (double)(T < 1 ? 1 : T));
+  int64_t cap = (int64_t)(0.02 * (double)K / (double)(T < 1 ? 1 : T));
+  const int64_t busy = std::min<int64_t>(cdiv(1024, p.tiles < 1 ? 1 : p.tiles), p.stages / 16);
+  if (cap < busy) cap = busy;
   if (want > cap) want = cap;
   if (want > p.stages) want = p.stages;
   if (want < 1) want = 1;
