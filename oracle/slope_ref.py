@@ -49,7 +49,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "widen", "prune24", "compress24", "decompress24", "mask_from_meta",
+    "widen", "prune24", "prune_nm", "compress24", "decompress24", "mask_from_meta",
     "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add", "lowrank_bwd",
     "round_bf16", "round_f16", "round_f32", "adamw_update", "adamw_compressed", "adamw_double_prune",
     "storage_accounting", "LEGAL_NIBBLES",
@@ -114,6 +114,38 @@ def prune24(A: np.ndarray):
             if i != j:
                 above += _ranks_above(mag, nan, i, j)
         keep[..., j] = above < 2
+    mask = keep.reshape(rows, cols).astype(np.uint8)
+    A_s = np.where(mask != 0, A, np.zeros((), dtype=A.dtype)).astype(A.dtype)
+    return mask, A_s
+
+
+def prune_nm(A: np.ndarray, n: int, m: int):
+    """Magnitude N:M pruning along the rows of A: in every group of m
+    consecutive columns the n highest-ranked elements are kept (same ranking as
+    prune24: magnitude, NaN above every number, ties to the lower index).
+
+    The explainer's Technical Summary 1 (Problem Statement) introduces N:M
+    structured sparsity in general; its "N zeros out of M" is read, as for 2:4,
+    as n kept (non-zero) positions out of every m.  prune24 is the case n = 2,
+    m = 4.  Element j is kept iff fewer than n elements of its group rank above it.
+
+    Returns (mask uint8 [rows, cols], A_s: bits of A at kept positions, +0 elsewhere).
+    """
+    A = np.asarray(A)
+    rows, cols = A.shape
+    if m < 1 or not 1 <= n <= m:
+        raise ValueError("need 1 <= n <= m")
+    if cols % m:
+        raise ValueError("the pruned dimension must be a multiple of m")
+    v = widen(A).reshape(rows, cols // m, m)
+    mag, nan = np.abs(v), np.isnan(v)
+    keep = np.zeros(v.shape, dtype=bool)
+    for j in range(m):
+        above = np.zeros(v.shape[:-1], dtype=np.int64)
+        for i in range(m):
+            if i != j:
+                above += _ranks_above(mag, nan, i, j)
+        keep[..., j] = above < n
     mask = keep.reshape(rows, cols).astype(np.uint8)
     A_s = np.where(mask != 0, A, np.zeros((), dtype=A.dtype)).astype(A.dtype)
     return mask, A_s
