@@ -16,7 +16,8 @@ few-token forward (slope_spmm_fwd_decode) at the workload's inference token
 counts, as HBM bytes per second, and a `weight_update` object times the optimizer
 step (AdamW on the compressed values fused with the double prune, writing both
 GEMM operands' tile chunks, and AdamW on the adapter factors), also as HBM
-bytes per second.
+bytes per second, and a `prune_nm` object times the general N:M prune
+(slope_prune_nm at 2:8, 1:4 and 2:16) of the layer's dense weights.
 
 The prune and compression run once per layer in training (the forward mask is
 static); they are kept inside the timed step so the step covers every row of
@@ -58,7 +59,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
-    ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "adamw_double_prune", "copy"),
+    ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "adamw_double_prune", "prune_nm",
+                                              "copy"),
                     default=None,
                     help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
     ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
@@ -270,6 +272,8 @@ def profile_mode(args, wl, T):
         S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
         bwd_dx(S, li)
         wgrad(S, li)
+        if args.profile_op == "prune_nm":
+            li.Wnm = torch.empty_like(li.W)
         if args.profile_op == "adamw_double_prune":
             li.opt_m = torch.zeros(li.vs.numel(), device="cuda")
             li.opt_v = torch.zeros(li.vs.numel(), device="cuda")
@@ -281,6 +285,8 @@ def profile_mode(args, wl, T):
                 prune_compress(S, li)
             elif op == "prune24":
                 S.slope_prune24(li.W, li.mask)
+            elif op == "prune_nm":
+                S.slope_prune_nm(li.W, 2, 8, li.mask, li.Wnm)
             elif op == "compress24":
                 S.slope_compress24(li.W, li.mask, li.vs, li.ms)
             elif op == "double_prune":
@@ -334,6 +340,34 @@ def decode_pass(lins, wl, S, torch, reps=20):
         out[f"T={T}"] = {"us_per_layer": round(ms * 1e3, 1), "bytes": int(nbytes), "gbs": round(gbs, 1),
                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         del calls
+    return out
+
+
+def prune_nm_pass(lins, S, torch, patterns=((2, 8), (1, 4), (2, 16)), reps=5):
+    """General N:M magnitude pruning (slope_prune_nm, mask and W_s written) of
+    the layer's dense weights, timed apart from the step (it runs once, at
+    initialisation, in place of the 2:4 prune).  HBM bound: 5 B per weight
+    (the weight read, one mask byte and W_s written)."""
+    big = max(lins, key=lambda li: li.W.numel())
+    mask = torch.empty(big.W.numel(), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(big.W.numel(), dtype=big.W.dtype, device="cuda")
+    nbytes = sum(5 * li.W.numel() for li in lins)
+    out = {}
+    for n, m in patterns:
+        calls = [(li, mask[:li.W.numel()].view(li.W.shape), ws[:li.W.numel()].view(li.W.shape)) for li in lins]
+        run = lambda: [S.slope_prune_nm(li.W, n, m, mk, w) for li, mk, w in calls]
+        run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"{n}:{m}"] = {"ms_per_layer": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del mask, ws
     return out
 
 
@@ -498,6 +532,7 @@ def main():
     if wl.decode_T:
         out["decode"] = decode_pass(lins, wl, S, torch)
     out["weight_update"] = update_pass(lins, S, torch)
+    out["prune_nm"] = prune_nm_pass(lins, S, torch)
     # free the layer before the CPU leg
     del lins
     torch.cuda.empty_cache()

@@ -110,6 +110,23 @@ slope_status slope_wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_
 slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask,
                            void* W_s_or_null, void* stream);
 
+/* Magnitude N:M pruning of W [rows, cols] along its rows: in every group of m
+ * consecutive columns the n highest-ranked elements are kept, ranked as in
+ * slope_prune24 (n = 2, m = 4 gives slope_prune24's result).  The explainer's
+ * Technical Summary 1 (Problem Statement) names N:M structured sparsity in
+ * general; its "N zeros out of M" is read as n kept positions out of m.
+ * With n <= 2 and m a multiple of four every aligned group of four keeps at
+ * most two positions (1:4, 1:8, 2:8, 2:16, 2:32), so slope_compress24 of W_s
+ * under this mask feeds the 2:4 products and the double prune unchanged.
+ *   W         [rows, cols] dt, input
+ *   n, m      m in {4, 8, 16, 32}, 1 <= n <= m
+ *   mask      [rows, cols] uint8 output, 1 at kept positions, 0 elsewhere
+ *   W_s       [rows, cols] dt output (kept values, +0 elsewhere) or NULL
+ * Errors: SLOPE_ERR_UNSUPPORTED for another m; SLOPE_ERR_INVALID_ARG for n
+ * outside [1, m]; SLOPE_ERR_SHAPE if cols % m != 0. */
+slope_status slope_prune_nm(slope_dtype dt, const void* W, int64_t rows, int64_t cols, int n, int m, uint8_t* mask,
+                           void* W_s_or_null, void* stream);
+
 /* slope_prune24 followed by slope_compress24 of its mask, in one pass over W
  * (explainer 2.A: the forward weight pruned 2:4 along its rows, once, at
  * initialisation; discussion page, "Memory Footprint": two 16-bit non-zeros

@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "SlopeError", "library", "library_path", "STATUS",
     "slope_version", "slope_compressed_sizes", "slope_lowrank_workspace_bytes",
-    "slope_prune24", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
+    "slope_prune24", "slope_prune_nm", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
@@ -86,6 +86,7 @@ _SIGS = {
                                         _vp]),
     "slope_double_prune_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_prune_compress24": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "slope_prune_nm": (_i32, [_i32, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]),
     "slope_adamw_double_prune_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _i64,
                                                _vp, _i64, _vp]),
 }
@@ -182,6 +183,12 @@ def slope_lowrank_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
 def slope_prune24(W, mask, W_s=None, stream=None) -> None:
     rows, cols = W.shape
     _check("slope_prune24", library().slope_prune24(_dt(W), _nn(W), rows, cols, _nn(mask), _p(W_s), _s(stream)))
+
+
+def slope_prune_nm(W, n, m, mask, W_s=None, stream=None) -> None:
+    rows, cols = W.shape
+    _check("slope_prune_nm", library().slope_prune_nm(_dt(W), _nn(W), rows, cols, n, m, _nn(mask), _p(W_s),
+                                                      _s(stream)))
 
 
 def slope_compress24(W, mask, values, meta, invalid=None, stream=None) -> None:

@@ -112,6 +112,19 @@ slope_status slope_prune24(slope_dtype dt, const void* W, int64_t rows, int64_t 
   return from_hip(slope::launch_prune24((Dt)dt, W, rows, cols, mask, W_s_or_null, (hipStream_t)stream));
 }
 
+slope_status slope_prune_nm(slope_dtype dt, const void* W, int64_t rows, int64_t cols, int n, int m, uint8_t* mask,
+                           void* W_s_or_null, void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  if (m != 4 && m != 8 && m != 16 && m != 32) return SLOPE_ERR_UNSUPPORTED;
+  if (n < 1 || n > m) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(W, true));
+  SLOPE_TRY(ptr(mask, true));
+  SLOPE_TRY(ptr(W_s_or_null, false));
+  if (cols % m) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || !in_range(cols)) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_prune_nm((Dt)dt, W, rows, cols, n, m, mask, W_s_or_null, (hipStream_t)stream));
+}
+
 slope_status slope_prune_compress24(slope_dtype dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask_or_null,
                                     void* values, uint32_t* meta, void* packed_or_null, int64_t packed_bytes,
                                     void* stream) {

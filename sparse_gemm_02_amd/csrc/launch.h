@@ -21,6 +21,8 @@ inline int64_t device_compute_units() {
 
 hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint8_t* mask, void* W_s,
                           hipStream_t s);
+hipError_t launch_prune_nm(Dt dt, const void* W, int64_t rows, int64_t cols, int n, int m, uint8_t* mask, void* W_s,
+                           hipStream_t s);
 hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols, void* values,
                              uint32_t* meta, int32_t* invalid, hipStream_t s);
 hipError_t launch_double_prune(Dt dt, const void* values_s, const uint32_t* meta_s, int64_t N, int64_t K,

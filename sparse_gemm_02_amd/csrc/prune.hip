@@ -80,6 +80,98 @@ __global__ __launch_bounds__(kThreads) void prune24_kernel(const E* __restrict__
   }
 }
 
+// ------------------------------------------------------------------ prune N:M
+// General N:M (the explainer's Technical Summary 1 names N:M sparsity in
+// general): per group of M consecutive elements the n highest-ranked are kept,
+// ranked as in prune24 (magnitude key, equal keys to the lower position).  One
+// group per thread: position j is kept when fewer than n positions outrank it.
+// The group's M * sizeof(E) bytes move as 16-byte words (8 bytes for four
+// 16-bit values); the mask bytes and W_s go out the same way.
+template <typename E> __device__ __forceinline__ uint32_t elem_key(const uint32_t* w, int i) {
+  if constexpr (sizeof(E) == 4) {
+    return mag_key(w[i]);
+  } else {
+    const uint16_t b = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+    if constexpr (__is_same(E, _Float16)) return mag_key(__builtin_bit_cast(_Float16, b));
+    else return mag_key(b);
+  }
+}
+
+template <int WORDS> __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
+  if constexpr (WORDS % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < WORDS / 4; ++q) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + q);
+      w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+    }
+  } else if constexpr (WORDS == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    static_assert(WORDS == 1, "group sizes of 4, 8, 16 or 32 elements");
+    w[0] = __builtin_nontemporal_load(p);
+  }
+}
+
+template <int WORDS> __device__ __forceinline__ void store_words(uint32_t* p, const uint32_t* w) {
+  if constexpr (WORDS % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < WORDS / 4; ++q) {
+      u32x4 v; v[0] = w[4 * q]; v[1] = w[4 * q + 1]; v[2] = w[4 * q + 2]; v[3] = w[4 * q + 3];
+      reinterpret_cast<u32x4*>(p)[q] = v;
+    }
+  } else if constexpr (WORDS == 2) {
+    u32x2 v; v[0] = w[0]; v[1] = w[1];
+    *reinterpret_cast<u32x2*>(p) = v;
+  } else {
+    p[0] = w[0];
+  }
+}
+
+template <typename E, int M>
+__global__ __launch_bounds__(kThreads) void prune_nm_kernel(const uint32_t* __restrict__ W, int64_t groups, int n,
+                                                           uint32_t* __restrict__ mask, uint32_t* __restrict__ W_s) {
+  constexpr int WORDS = M * (int)sizeof(E) / 4;   // 32-bit words of one group
+  constexpr int PER = 4 / (int)sizeof(E);          // elements per word
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += stride) {
+    uint32_t w[WORDS];
+    load_words<WORDS>(W + g * WORDS, w);
+    uint32_t k[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) k[i] = elem_key<E>(w, i);
+    uint32_t keep = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      int above = 0;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        if (i < j) above += k[i] >= k[j];
+        else if (i > j) above += k[i] > k[j];
+      }
+      keep |= (uint32_t)(above < n) << j;
+    }
+    uint32_t mb[M / 4];                             // mask bytes 0/1, four positions per word
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q) {
+      const uint32_t b = keep >> (4 * q);
+      mb[q] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+    }
+    store_words<M / 4>(mask + g * (M / 4), mb);
+    if (W_s) {
+#pragma unroll
+      for (int q = 0; q < WORDS; ++q) {
+        uint32_t clear = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if (!((keep >> (q * PER + e)) & 1u)) clear |= (PER == 1 ? 0xFFFFFFFFu : 0xFFFFu << (16 * e));
+        w[q] &= ~clear;
+      }
+      store_words<WORDS>(W_s + g * WORDS, w);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ prune24 + compress24 in one pass
 // Lane f of the grid -> (row, pair p) over rows_pad x pairs_pad: groups 2p and
 // 2p+1 of the row (columns 8p .. 8p+7), read as one 8- or 16-byte load, so a
@@ -507,6 +599,31 @@ hipError_t launch_prune24(Dt dt, const void* W, int64_t rows, int64_t cols, uint
   else
     prune24_kernel<uint32_t, U><<<grid, kThreads, 0, s>>>((const uint32_t*)W, groups, (uint32_t*)mask, (uint32_t*)W_s);
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t prune_nm_dispatch(const void* W, int64_t groups, int n, int m, uint8_t* mask, void* W_s, hipStream_t s) {
+  const int grid = grid_for(groups, kThreads);
+  const uint32_t* w = (const uint32_t*)W;
+  uint32_t* mk = (uint32_t*)mask;
+  uint32_t* ws = (uint32_t*)W_s;
+  switch (m) {
+    case 4: prune_nm_kernel<E, 4><<<grid, kThreads, 0, s>>>(w, groups, n, mk, ws); break;
+    case 8: prune_nm_kernel<E, 8><<<grid, kThreads, 0, s>>>(w, groups, n, mk, ws); break;
+    case 16: prune_nm_kernel<E, 16><<<grid, kThreads, 0, s>>>(w, groups, n, mk, ws); break;
+    case 32: prune_nm_kernel<E, 32><<<grid, kThreads, 0, s>>>(w, groups, n, mk, ws); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_nm(Dt dt, const void* W, int64_t rows, int64_t cols, int n, int m, uint8_t* mask, void* W_s,
+                           hipStream_t s) {
+  const int64_t groups = rows * (cols / m);
+  if (groups == 0) return hipSuccess;
+  if (dt == Dt::BF16) return prune_nm_dispatch<uint16_t>(W, groups, n, m, mask, W_s, s);
+  if (dt == Dt::F16) return prune_nm_dispatch<_Float16>(W, groups, n, m, mask, W_s, s);
+  return prune_nm_dispatch<uint32_t>(W, groups, n, m, mask, W_s, s);
 }
 
 hipError_t launch_compress24(Dt dt, const void* W, const uint8_t* mask, int64_t rows, int64_t cols, void* values,

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -242,6 +242,24 @@ def test_prune_compress24_argument_errors(lib):
     assert f(bf, FAKE, 64, 256, None, FAKE, FAKE, FAKE, need - 1, None) == -4
     assert f(bf, FAKE, 64, (1 << 21) + 16, None, FAKE, FAKE, FAKE, 1 << 40, None) == -6
     assert f(bf, FAKE, 64, 256, None, FAKE, FAKE, FAKE + 8, need, None) == -3
+
+
+def test_prune_nm_argument_errors(lib):
+    """General N:M prune: m in {4, 8, 16, 32}, 1 <= n <= m, cols a multiple of m."""
+    bf = 1
+    f = lib.slope_prune_nm
+    assert f(7, FAKE, 64, 256, 2, 8, FAKE, None, None) == -1
+    assert f(bf, FAKE, -1, 256, 2, 8, FAKE, None, None) == -1
+    assert f(bf, None, 64, 256, 2, 8, FAKE, None, None) == -1
+    assert f(bf, FAKE, 64, 256, 2, 8, None, None, None) == -1
+    assert f(bf, FAKE, 64, 256, 2, 6, FAKE, None, None) == -6
+    assert f(bf, FAKE, 64, 256, 2, 64, FAKE, None, None) == -6
+    assert f(bf, FAKE, 64, 256, 0, 8, FAKE, None, None) == -1
+    assert f(bf, FAKE, 64, 256, 9, 8, FAKE, None, None) == -1
+    assert f(bf, FAKE, 64, 260, 2, 8, FAKE, None, None) == -2
+    assert f(bf, FAKE, 64, 256, 2, 8, FAKE + 2, None, None) == -3
+    assert f(bf, FAKE, 64, 256, 2, 8, FAKE, FAKE + 8, None) == -3
+    assert f(bf, FAKE, 0, 256, 2, 8, FAKE, None, None) == 0          # empty: nothing launched
 
 
 def test_binding_refuses_host_tensors(lib):
