@@ -72,6 +72,74 @@ namespace {
 // narrower tiles in the same launch (spmm_split_kernel).  Each output
 // accumulates over k in the same order whatever the tile width, so the split
 // does not change results.
+// The adapter term of a tile, (X . L) . R added to its accumulators, with the
+// operands staged through LDS: once the main loop is done the operand ring is
+// idle, so the tile's rows of R^T and of X . L (hi and lo parts) come in by
+// buffer-to-LDS loads, SL rank slices of 16 columns at a time: one round trip
+// per chunk (one in all up to rank 96) instead of one per 16-deep rank step.
+// A slice holds 32 bytes per row, the BM rows of R^T then the BT rows of the
+// hi and the lo part; a lane reads its 16-byte half of a row, so eight
+// consecutive lanes touch distinct banks.  The MFMAs are adapter_mma's, in the
+// same order, so the results are identical.
+template <class G, bool H, int LDS_AVAIL>
+__device__ __forceinline__ void adapter_mma_lds(f32x16 (&acc)[G::FM][G::FT], char* lds,
+                                                const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
+                                                const uint16_t* __restrict__ xll, int rpad, int64_t m0, int64_t t0,
+                                                int wm, int wt, int wave, int lane) {
+  typedef Fmt16<H> F;
+  typedef typename F::v8 v8;
+  constexpr int ROWS = G::BM + 2 * G::BT;
+  constexpr int SLICE_BYTES = ROWS * 32, BLOCKS = ROWS / 32;   // 1 KB loads per slice
+  constexpr int SL_FIT = LDS_AVAIL / SLICE_BYTES;
+  constexpr int SL = SL_FIT < 8 ? SL_FIT : 8;
+  static_assert(SL >= 1 && G::BM % 32 == 0 && G::BT % 32 == 0, "adapter slices fit the LDS ring");
+  // the padded R^T [Mpad][rpad] and X . L [Tpad][rpad] hold every row of the tile
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rt + m0 * rpad, (int64_t)G::BM * rpad * 2);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(xlh + t0 * rpad, (int64_t)G::BT * rpad * 2);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(xll + t0 * rpad, (int64_t)G::BT * rpad * 2);
+  const uint32_t pitch = (uint32_t)rpad * 2;
+  const uint32_t lrow = (uint32_t)(lane >> 1), lhalf = (uint32_t)(lane & 1) * 16;
+  const int slices = rpad / 16;
+  for (int q0 = 0; q0 < slices; q0 += SL) {
+    const int nq = slices - q0 < SL ? slices - q0 : SL;
+    barrier();                                       // no wave reads the ring (or the last chunk) any more
+    compiler_fence();
+    for (int b = wave; b < nq * BLOCKS; b += G::WAVES) {
+      const int q = b / BLOCKS, rb = b % BLOCKS;     // wave-uniform
+      const uint32_t col = (uint32_t)(q0 + q) * 32 + lhalf;
+      char* dst = lds + b * 1024;
+      if (rb * 32 < G::BM)
+        dma16(rr, dst, (rb * 32 + lrow) * pitch + col);
+      else if (rb * 32 < G::BM + G::BT)
+        dma16(rh, dst, (rb * 32 - G::BM + lrow) * pitch + col);
+      else
+        dma16(rl, dst, (rb * 32 - G::BM - G::BT + lrow) * pitch + col);
+    }
+    compiler_fence();
+    wait_vmcnt<0>();                                 // this wave's slices landed
+    barrier();                                       // everyone's
+    compiler_fence();
+    for (int q = 0; q < nq; ++q) {
+      const char* base = lds + q * SLICE_BYTES + 16 * (lane >> 5);
+      v8 ra[G::FM];
+#pragma unroll
+      for (int fm = 0; fm < G::FM; ++fm)
+        ra[fm] = *reinterpret_cast<const v8*>(base + (wm * G::WM + fm * 32 + (lane & 31)) * 32);
+#pragma unroll
+      for (int ft = 0; ft < G::FT; ++ft) {
+        const int tr = wt * G::WT + ft * 32 + (lane & 31);
+        const v8 xh = *reinterpret_cast<const v8*>(base + (G::BM + tr) * 32);
+        const v8 xo = *reinterpret_cast<const v8*>(base + (G::BM + G::BT + tr) * 32);
+#pragma unroll
+        for (int fm = 0; fm < G::FM; ++fm) {
+          acc[fm][ft] = F::mfma32x32x16(ra[fm], xh, acc[fm][ft]);
+          acc[fm][ft] = F::mfma32x32x16(ra[fm], xo, acc[fm][ft]);
+        }
+      }
+    }
+  }
+}
+
 template <class G, bool ADAPTER, typename O, bool PK, bool H>
 __device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals,
                                           const uint32_t* __restrict__ meta, int M, int T, int Kred,
@@ -235,7 +303,8 @@ __device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const
     for (int ft = 1; ft < G::FT; ++ft) mma_col(f1, ft);
   }
   wait_vmcnt<0>();
-  if constexpr (ADAPTER) adapter_mma<G, H>(acc, rt, xlh, xll, rpad, m0, t0, wm, wt, lane);
+  if constexpr (ADAPTER)
+    adapter_mma_lds<G, H, PK ? G::PLDS_BYTES : G::LDS_BYTES>(acc, lds, rt, xlh, xll, rpad, m0, t0, wm, wt, wave, lane);
   store_tile<G, O>(acc, Y, m0, t0, M, T, wm, wt, lane);
 }
 
