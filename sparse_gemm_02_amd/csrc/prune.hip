@@ -416,6 +416,46 @@ __global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restr
 // conflicts.
 constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit words
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+// The rule of top2_of_4 for two columns at once: w[j] holds row j of a group
+// of four for one column in its low half and for the next column in its high
+// half.  Magnitude keys are at most 15 bits, so with packed 16-bit arithmetic
+// the sign of k_j - k_i - 1 says whether i (< j) outranks j, ranks are sums of
+// those signs and a position is kept when its rank is below two.  Per half:
+// a / b = the values at the lower / higher kept position, nib = i0 | i1 << 2.
+template <bool H>
+__device__ __forceinline__ void top2_of_4_x2(const uint32_t w[4], uint32_t& a, uint32_t& b, uint32_t& nib,
+                                             uint32_t keep[4]) {
+  const uint16_t nan_key = H ? 0x7C01 : 0x7F81;     // every NaN ranks as this key (ties among NaNs)
+  i16x2 k[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+    k[j] = __builtin_bit_cast(i16x2, __builtin_elementwise_min(m, (u16x2){nan_key, nan_key}));
+  }
+  // o_ij = -1 where i outranks j (k_i >= k_j for i < j), else 0
+  auto outranks = [&](int i, int j) { return (i16x2)((k[j] - k[i] - (i16x2){1, 1}) >> (i16x2){15, 15}); };
+  const i16x2 o01 = outranks(0, 1), o02 = outranks(0, 2), o03 = outranks(0, 3);
+  const i16x2 o12 = outranks(1, 2), o13 = outranks(1, 3), o23 = outranks(2, 3);
+  // rank - 2 of each position
+  const i16x2 r0 = (i16x2){1, 1} + o01 + o02 + o03;
+  const i16x2 r1 = o12 + o13 - o01;
+  const i16x2 r2 = o23 - o02 - o12 - (i16x2){1, 1};
+  const i16x2 r3 = (i16x2){-2, -2} - o03 - o13 - o23;
+  keep[0] = __builtin_bit_cast(uint32_t, (i16x2)(r0 >> (i16x2){15, 15}));
+  keep[1] = __builtin_bit_cast(uint32_t, (i16x2)(r1 >> (i16x2){15, 15}));
+  keep[2] = __builtin_bit_cast(uint32_t, (i16x2)(r2 >> (i16x2){15, 15}));
+  keep[3] = __builtin_bit_cast(uint32_t, (i16x2)(r3 >> (i16x2){15, 15}));
+  auto sel = [](uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); };
+  a = sel(keep[0], w[0], sel(keep[1], w[1], w[2]));
+  b = sel(keep[3], w[3], sel(keep[2], w[2], w[1]));
+  const uint32_t i0 = sel(keep[0], 0u, sel(keep[1], 0x00010001u, 0x00020002u));
+  const uint32_t i1 = sel(keep[3], 0x00030003u, sel(keep[2], 0x00020002u, 0x00010001u));
+  nib = i0 | (i1 << 2);
+}
+
 //
 // With UPD the kernel first applies one AdamW step to the compressed values it
 // loads (gradient GT, fp32 moments m and v at the same element index), writes
@@ -472,6 +512,20 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
       load8_f32(v + el[it], vf[it]);
     }
   }
+  // byte selectors (v_perm_b32 of a group's word with itself) giving the two
+  // dense words of a group from its nibble: position p holds the high value
+  // if p == i1, else the low value if p == i0, else 0 (the rule of the
+  // selects this replaces, for every nibble)
+  __shared__ uint32_t expand_sel[32];
+  if (tid < 16) {
+    const int i0 = tid & 3, i1 = tid >> 2;
+    uint32_t h[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) h[p] = i1 == p ? 0x0302u : (i0 == p ? 0x0100u : 0x0C0Cu);
+    expand_sel[2 * tid] = h[0] | (h[1] << 16);
+    expand_sel[2 * tid + 1] = h[2] | (h[3] << 16);
+  }
+  __syncthreads();
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = it * 32 + (tid >> 3);
@@ -504,13 +558,10 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
     uint32_t d[8];                                    // 16 dense 16-bit values, two per word
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t nib = (nb >> (4 * g)) & 0xFu, i0 = nib & 3u, i1 = nib >> 2;
-      const uint32_t w = wv[g], v0 = w & 0xFFFFu, v1 = w >> 16;
-      uint32_t e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) e[j] = i1 == (uint32_t)j ? v1 : (i0 == (uint32_t)j ? v0 : 0u);
-      d[2 * g] = e[0] | (e[1] << 16);
-      d[2 * g + 1] = e[2] | (e[3] << 16);
+      const uint32_t nib = (nb >> (4 * g)) & 0xFu;
+      const u32x2 sel = *reinterpret_cast<const u32x2*>(&expand_sel[2 * nib]);
+      d[2 * g] = __builtin_amdgcn_perm(wv[g], wv[g], sel[0]);
+      d[2 * g + 1] = __builtin_amdgcn_perm(wv[g], wv[g], sel[1]);
     }
     const int swz = 16 * ((r >> 5) & 3);
     uint32_t* dst = tile + r * DW_PITCH;
@@ -527,29 +578,31 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
   const int64_t g0 = (n0 >> 2) + 8 * q;               // first output group (n / 4)
   const int64_t left = N / 4 - g0;
   const int ngroups = left <= 0 ? 0 : (left < 8 ? (int)left : 8);   // 0, 4 or 8 (N % 16 == 0)
+  // both columns' groups at once (column 2cp in the low halves, 2cp+1 in the high)
+  uint32_t words[2] = {0u, 0u}, ovs[2][8], mws[2][8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t a, b, nib, keep[4];
+    top2_of_4_x2<H>(&col[4 * g], a, b, nib, keep);
+    words[0] |= (nib & 0xFu) << (4 * g);
+    words[1] |= ((nib >> 16) & 0xFu) << (4 * g);
+    ovs[0][g] = (a & 0xFFFFu) | (b << 16);
+    ovs[1][g] = (a >> 16) | (b & 0xFFFF0000u);
+    if constexpr (!PK) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mws[h][g] = ((keep[0] >> (16 * h)) & 1u) | (((keep[1] >> (16 * h)) & 1u) << 8) |
+                    (((keep[2] >> (16 * h)) & 1u) << 16) | (((keep[3] >> (16 * h)) & 1u) << 24);
+    }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int64_t krow = k0 + 2 * cp + h;
     const bool live = krow < K && ngroups > 0;
     if (!PK && !live) continue;
-    uint32_t word = 0, ov[8], mw[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      uint16_t e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) e[j] = (uint16_t)(col[4 * g + j] >> (16 * h));
-      uint32_t k4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) k4[j] = H ? mag_key(__builtin_bit_cast(_Float16, e[j])) : mag_key(e[j]);
-      const uint32_t keep = top2_of_4(k4[0], k4[1], k4[2], k4[3]);
-      const uint32_t nib = pair_nibble(keep);
-      word |= nib << (4 * g);
-      const uint32_t i0 = nib & 3u, i1 = nib >> 2;
-      const uint32_t a = i0 == 0 ? e[0] : (i0 == 1 ? e[1] : e[2]);
-      const uint32_t b = i1 == 3 ? e[3] : (i1 == 2 ? e[2] : e[1]);
-      ov[g] = a | (b << 16);
-      mw[g] = (keep & 1u) | ((keep & 2u) << 7) | ((keep & 4u) << 14) | ((keep & 8u) << 21);
-    }
+    uint32_t word = words[h];
+    const uint32_t* ov = ovs[h];
+    const uint32_t* mw = mws[h];
     if (ngroups < 8) word &= 0xFFFFu;
     if constexpr (PK) {
       // chunk row krow % 256 of the chunk holding dense columns 4 g0 ..; groups
