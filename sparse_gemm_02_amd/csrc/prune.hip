@@ -43,6 +43,45 @@ __device__ __forceinline__ u32x2 pack(const _Float16 e[4]) {
   return pack(b);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+// The rule of top2_of_4 for two groups at once: w[j] holds element j of one
+// group of four in its low half and of another group in its high half.  Magnitude keys are at most 15 bits, so with packed 16-bit arithmetic
+// the sign of k_j - k_i - 1 says whether i (< j) outranks j, ranks are sums of
+// those signs and a position is kept when its rank is below two.  Per half:
+// a / b = the values at the lower / higher kept position, nib = i0 | i1 << 2.
+template <bool H>
+__device__ __forceinline__ void top2_of_4_x2(const uint32_t w[4], uint32_t& a, uint32_t& b, uint32_t& nib,
+                                             uint32_t keep[4]) {
+  const uint16_t nan_key = H ? 0x7C01 : 0x7F81;     // every NaN ranks as this key (ties among NaNs)
+  i16x2 k[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+    k[j] = __builtin_bit_cast(i16x2, __builtin_elementwise_min(m, (u16x2){nan_key, nan_key}));
+  }
+  // o_ij = -1 where i outranks j (k_i >= k_j for i < j), else 0
+  auto outranks = [&](int i, int j) { return (i16x2)((k[j] - k[i] - (i16x2){1, 1}) >> (i16x2){15, 15}); };
+  const i16x2 o01 = outranks(0, 1), o02 = outranks(0, 2), o03 = outranks(0, 3);
+  const i16x2 o12 = outranks(1, 2), o13 = outranks(1, 3), o23 = outranks(2, 3);
+  // rank - 2 of each position
+  const i16x2 r0 = (i16x2){1, 1} + o01 + o02 + o03;
+  const i16x2 r1 = o12 + o13 - o01;
+  const i16x2 r2 = o23 - o02 - o12 - (i16x2){1, 1};
+  const i16x2 r3 = (i16x2){-2, -2} - o03 - o13 - o23;
+  keep[0] = __builtin_bit_cast(uint32_t, (i16x2)(r0 >> (i16x2){15, 15}));
+  keep[1] = __builtin_bit_cast(uint32_t, (i16x2)(r1 >> (i16x2){15, 15}));
+  keep[2] = __builtin_bit_cast(uint32_t, (i16x2)(r2 >> (i16x2){15, 15}));
+  keep[3] = __builtin_bit_cast(uint32_t, (i16x2)(r3 >> (i16x2){15, 15}));
+  auto sel = [](uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); };
+  a = sel(keep[0], w[0], sel(keep[1], w[1], w[2]));
+  b = sel(keep[3], w[3], sel(keep[2], w[2], w[1]));
+  const uint32_t i0 = sel(keep[0], 0u, sel(keep[1], 0x00010001u, 0x00020002u));
+  const uint32_t i1 = sel(keep[3], 0x00030003u, sel(keep[2], 0x00020002u, 0x00010001u));
+  nib = i0 | (i1 << 2);
+}
+
 // ------------------------------------------------------------------ prune24
 // One group of four per thread and iteration; groups never straddle rows
 // because cols % 4 == 0, so the matrix is a flat array of groups.
@@ -195,21 +234,48 @@ __global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __r
   const int64_t total = rows_pad * pairs_pad;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int lane = threadIdx.x & 63;
+  // the lane's (row, pair) advances by a fixed step each iteration (one
+  // division before the loop instead of a 64-bit division per iteration);
+  // past the end the row is at least rows_pad, so nothing is stored
+  const int64_t base0 = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63);
+  const int drow = (int)(stride / pairs_pad), dpair = (int)(stride - (int64_t)drow * pairs_pad);
+  const int npairs = (int)pairs_pad;
+  int row = (int)((base0 + lane) / pairs_pad), p = (int)(base0 + lane - (int64_t)row * pairs_pad);
   // wave-uniform loop bound: every lane of a wave takes part in the shuffles
-  for (int64_t base = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); base < total; base += stride) {
+  for (int64_t base = base0; base < total; base += stride,
+               row += drow + (p + dpair >= npairs ? 1 : 0), p += dpair - (p + dpair >= npairs ? npairs : 0)) {
     const int64_t f = base + lane;
-    const int64_t row = f < total ? f / pairs_pad : rows_pad;
-    const int64_t p = f < total ? f - row * pairs_pad : 0;
-    const int64_t g0 = 2 * p;                      // first group of the pair
+    const int64_t g0 = 2 * (int64_t)p;             // first group of the pair
     const bool in_row = row < rows;
     const int ng = in_row ? (g0 + 2 <= gpr ? 2 : (g0 < gpr ? 1 : 0)) : 0;   // groups of the pair in the matrix
     uint32_t nibs = 0, mb[2] = {0u, 0u};
     E kept[4] = {(E)0, (E)0, (E)0, (E)0};
     if (ng > 0) {
       V v[2];
-      const V* src = reinterpret_cast<const V*>(W) + row * gpr + g0;
+      const V* src = reinterpret_cast<const V*>(W) + (int64_t)row * gpr + g0;
       v[0] = __builtin_nontemporal_load(src);
       v[1] = __builtin_nontemporal_load(src + (ng > 1 ? 1 : 0));
+      if constexpr (sizeof(E) == 2) {
+        // both groups ranked at once: element j of group 0 in the low half, of group 1 in the high
+        uint32_t w[4], a, b, nib, keep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = __builtin_amdgcn_perm(v[1][j >> 1], v[0][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+        top2_of_4_x2<__is_same(E, _Float16)>(w, a, b, nib, keep);
+        nibs = (nib & 0xFu) | (ng > 1 ? ((nib >> 12) & 0xF0u) : 0u);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (j < ng)
+            mb[j] = ((keep[0] >> (16 * j)) & 1u) | (((keep[1] >> (16 * j)) & 1u) << 8) |
+                    (((keep[2] >> (16 * j)) & 1u) << 16) | (((keep[3] >> (16 * j)) & 1u) << 24);
+        }
+        kept[0] = __builtin_bit_cast(E, (uint16_t)(a & 0xFFFFu));
+        kept[1] = __builtin_bit_cast(E, (uint16_t)(b & 0xFFFFu));
+        if (ng > 1) {
+          kept[2] = __builtin_bit_cast(E, (uint16_t)(a >> 16));
+          kept[3] = __builtin_bit_cast(E, (uint16_t)(b >> 16));
+        }
+      } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         E e[4];
@@ -224,8 +290,9 @@ __global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __r
           kept[2 * j + 1] = i1 == 3 ? e[3] : (i1 == 2 ? e[2] : e[1]);
         }
       }
-      E* vp = values + row * (cols / 2) + 2 * g0;
-      uint32_t* mp = mask4 ? mask4 + row * gpr + g0 : nullptr;
+      }
+      E* vp = values + (int64_t)row * (cols / 2) + 2 * g0;
+      uint32_t* mp = mask4 ? mask4 + (int64_t)row * gpr + g0 : nullptr;
       constexpr uintptr_t kAlign = 4 * sizeof(E);             // the four kept values in one store
       if (ng == 2 && (reinterpret_cast<uintptr_t>(vp) & (kAlign - 1)) == 0) {
         if constexpr (sizeof(E) == 2)
@@ -416,45 +483,7 @@ __global__ __launch_bounds__(kThreads) void double_prune_kernel(const E* __restr
 // conflicts.
 constexpr int DW_T = 128, DW_PITCH = 68;  // tile edge; LDS row pitch in 32-bit words
 
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
 
-// The rule of top2_of_4 for two columns at once: w[j] holds row j of a group
-// of four for one column in its low half and for the next column in its high
-// half.  Magnitude keys are at most 15 bits, so with packed 16-bit arithmetic
-// the sign of k_j - k_i - 1 says whether i (< j) outranks j, ranks are sums of
-// those signs and a position is kept when its rank is below two.  Per half:
-// a / b = the values at the lower / higher kept position, nib = i0 | i1 << 2.
-template <bool H>
-__device__ __forceinline__ void top2_of_4_x2(const uint32_t w[4], uint32_t& a, uint32_t& b, uint32_t& nib,
-                                             uint32_t keep[4]) {
-  const uint16_t nan_key = H ? 0x7C01 : 0x7F81;     // every NaN ranks as this key (ties among NaNs)
-  i16x2 k[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
-    k[j] = __builtin_bit_cast(i16x2, __builtin_elementwise_min(m, (u16x2){nan_key, nan_key}));
-  }
-  // o_ij = -1 where i outranks j (k_i >= k_j for i < j), else 0
-  auto outranks = [&](int i, int j) { return (i16x2)((k[j] - k[i] - (i16x2){1, 1}) >> (i16x2){15, 15}); };
-  const i16x2 o01 = outranks(0, 1), o02 = outranks(0, 2), o03 = outranks(0, 3);
-  const i16x2 o12 = outranks(1, 2), o13 = outranks(1, 3), o23 = outranks(2, 3);
-  // rank - 2 of each position
-  const i16x2 r0 = (i16x2){1, 1} + o01 + o02 + o03;
-  const i16x2 r1 = o12 + o13 - o01;
-  const i16x2 r2 = o23 - o02 - o12 - (i16x2){1, 1};
-  const i16x2 r3 = (i16x2){-2, -2} - o03 - o13 - o23;
-  keep[0] = __builtin_bit_cast(uint32_t, (i16x2)(r0 >> (i16x2){15, 15}));
-  keep[1] = __builtin_bit_cast(uint32_t, (i16x2)(r1 >> (i16x2){15, 15}));
-  keep[2] = __builtin_bit_cast(uint32_t, (i16x2)(r2 >> (i16x2){15, 15}));
-  keep[3] = __builtin_bit_cast(uint32_t, (i16x2)(r3 >> (i16x2){15, 15}));
-  auto sel = [](uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); };
-  a = sel(keep[0], w[0], sel(keep[1], w[1], w[2]));
-  b = sel(keep[3], w[3], sel(keep[2], w[2], w[1]));
-  const uint32_t i0 = sel(keep[0], 0u, sel(keep[1], 0x00010001u, 0x00020002u));
-  const uint32_t i1 = sel(keep[3], 0x00030003u, sel(keep[2], 0x00020002u, 0x00010001u));
-  nib = i0 | (i1 << 2);
-}
 
 //
 // With UPD the kernel first applies one AdamW step to the compressed values it
