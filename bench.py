@@ -46,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_DENSE_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_BF16_SPARSE_TFLOPS = 5000.0  # MI355X 2:4-sparse bf16 MFMA, dense-equivalent (published)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E (published)
 METRIC = "2:4 sparse-GEMM TFLOP/s fwd+bwd(dX,dW) +LoRA, % MFMA peak, OPT-66B layer"
 
@@ -495,6 +496,12 @@ def main():
         t = ops[op]["ms_per_step"] * 1e-3
         ops[op].update(useful_tflops=uf / t / 1e12, dense_equiv_tflops=df / t / 1e12,
                        frac_dense_peak_useful=uf / t / 1e12 / PEAK_BF16_DENSE_TFLOPS)
+        if op in ("spmm_fwd", "spmm_bwd_dx"):
+            # the sparse products against the dense bf16 MFMA peak (dense-equivalent
+            # flops, what a dense GEMM of the same shape would need) and against the
+            # 2:4-sparse MFMA peak
+            ops[op].update(frac_dense_peak_dense_equiv=df / t / 1e12 / PEAK_BF16_DENSE_TFLOPS,
+                           frac_sparse_peak=df / t / 1e12 / PEAK_BF16_SPARSE_TFLOPS)
     # algorithmic HBM bytes: per weight for the pruning ops, per activation
     # element (read + written once) for the packing pass
     # (prune_compress24: W read, values + metadata + W_s's tile chunks written)
