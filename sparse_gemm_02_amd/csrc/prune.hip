@@ -510,7 +510,14 @@ __global__ __launch_bounds__(kThreads) void double_prune_wide_kernel(uint16_t* v
                                                                     AdamWStep hp) {
   __shared__ __attribute__((aligned(16))) uint32_t tile[DW_T * DW_PITCH];
   const int tid = threadIdx.x;
-  const int64_t n0 = (int64_t)blockIdx.y * DW_T, k0 = (int64_t)blockIdx.x * DW_T;
+  // Workgroups are dealt to the eight XCDs in turn; give each XCD a contiguous
+  // range of tiles, k fastest, so that the eight tiles sharing a 128-byte line
+  // of metadata (1024 columns of a row) run on one XCD and read it once into
+  // its L2 instead of once per XCD.
+  const int64_t nb = (int64_t)gridDim.x * gridDim.y, bid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t per = nb / 8, rem = nb % 8, xcd = bid % 8, slot = bid / 8;
+  const int64_t lin = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int64_t n0 = (lin / gridDim.x) * DW_T, k0 = (lin % gridDim.x) * DW_T;
   const int64_t in_wpr = cdiv(K / 4, 8), out_wpr = cdiv(N / 4, 8);
 
   // phase 1: row r, dense columns 16c .. 16c+15 (compressed groups 4c .. 4c+3).
