@@ -314,14 +314,16 @@ def test_spmm_packed_matches_unpacked(T, N, K, adapter, out_dt):
 SPLIT_SHAPES = [(8142, 2000, 96), (8142, 96, 2000), (8142, 2224, 96), (8142, 96, 2224)]
 
 
+@pytest.mark.parametrize("r", [8, 100, 128])
 @pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
 @pytest.mark.parametrize("T,N,K", SPLIT_SHAPES)
-def test_spmm_tile_split(T, N, K, ints):
+def test_spmm_tile_split(T, N, K, ints, r):
     """Forward with the adapter and dX with the adapter's dX term, packed and
     unpacked, whichever mix of tile widths the launch takes: within tolerance
-    of the oracle, and bit-exact in fp32 for integer inputs (every sum exact)."""
-    r = 8
-    say(f"spmm tile split T={T} N={N} K={K} ints={ints}")
+    of the oracle, and bit-exact in fp32 for integer inputs (every sum exact).
+    Ranks above 96 take the epilogue's rank slices through LDS in two chunks
+    on the 256-token tiles (six slices fit) and, at 128, on the 128-token tiles."""
+    say(f"spmm tile split T={T} N={N} K={K} ints={ints} r={r}")
     d = _layer(T, N, K, r, "bf16", seed=29 * T + N + K, ints=ints)
     od = torch.float32 if ints else torch.bfloat16
     L, R = dev(d["L"]), dev(d["R"])
