@@ -308,3 +308,39 @@ def test_weight_update_sampled(wl, idx):
     del c, dp, G, M, V
     torch.cuda.empty_cache()
 
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_prune_compress24_full_size(idx):
+    """The one-pass prune at OPT-66B QKV / FC2 weight size (many grid-stride
+    iterations per lane, with the (row, pair) step carrying across rows):
+    mask, values, metadata and W_s's tile chunks equal the separate prune24,
+    compress24 and pack_sparse calls bit for bit, and sampled rows equal the
+    oracle."""
+    lin = WORKLOADS["opt_66b"].linears[idx]
+    K, N = lin.K, lin.N
+    say(f"[prune_compress24 full] {lin.name}: {N}x{K}")
+    Wh = layer_inputs(K, N, 1, 1, "bf16", seed=41 + idx, which=("W",), threads=16)["W"]
+    W = dev(Wh)
+    mask = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    c = Compressed(N, K, torch.bfloat16)
+    pk = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
+    S.slope_prune_compress24(W, c.values, c.meta, mask=mask, packed=pk)
+    mask2 = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    c2 = Compressed(N, K, torch.bfloat16)
+    pk2 = torch.empty_like(pk)
+    S.slope_prune24(W, mask2)
+    S.slope_compress24(W, mask2, c2.values, c2.meta)
+    S.slope_pack_sparse(c2.values, c2.meta, N, K, pk2)
+    torch.cuda.synchronize()
+    assert torch.equal(mask, mask2)
+    assert torch.equal(c.values.view(torch.int16), c2.values.view(torch.int16))
+    assert torch.equal(c.meta, c2.meta)
+    assert torch.equal(pk, pk2)
+    rows = np.sort(np.random.default_rng(42).choice(N, size=32, replace=False))
+    m_ref, _ = oracle.prune24(Wh[rows])
+    v_ref, meta_ref, _ = oracle.compress24(Wh[rows], m_ref)
+    idx_t = torch.from_numpy(rows).cuda()
+    assert (host(mask.index_select(0, idx_t)) == m_ref).all()
+    assert (host(c.values.index_select(0, idx_t)) == v_ref).all()
+    assert (host(c.meta.index_select(0, idx_t)) == meta_ref).all()
