@@ -31,7 +31,14 @@ Prints one JSON line.  `value` is dense-equivalent TFLOP/s of the step's GEMMs
 backward); `useful_tflops` counts only products with a kept weight (T*N*K per
 sparse GEMM) plus the adapter's.  `roofline` reports the
 kernel with the largest share of the step against the dense bf16 MFMA peak
-(2.5 PFLOP/s) using useful flops.  `cpu_baseline` times the CPU oracle on a
+(2.5 PFLOP/s) using useful flops.  `layer_roofline_frac` is the step's ideal
+time (forward and dX at the 2:4-sparse MFMA peak, the weight gradient's dense
+flops at the dense peak) over the measured step; `sparse_products_target`
+gives the forward and dX products as fractions of the 2:4-sparse peak.
+`configs` runs the GPT-2-small, BERT-Large and OPT-13B layers (and OPT-13B's
+few-token forward at T = 16) through the same step, each against its own
+ideal; `dense_context` times the same twelve GEMMs as dense bf16 products
+through torch (context only).  `cpu_baseline` times the CPU oracle on a
 bounded slice of the same layer on this host.
 """
 from __future__ import annotations
@@ -48,6 +55,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_DENSE_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_BF16_SPARSE_TFLOPS = 5000.0  # MI355X 2:4-sparse bf16 MFMA, dense-equivalent (published)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E (published)
+# the layer roofline basis: the sparse products' dense-equivalent flops at the
+# 2:4-sparse bf16 MFMA rate, the weight gradient's computed dense flops at the
+# dense rate (256 CUs x 2.4 GHz x 4096 / 8192 flop per clock and CU)
+IDEAL_SPARSE_TFLOPS, IDEAL_DENSE_TFLOPS = 5033.0, 2516.6
 METRIC = "2:4 sparse-GEMM TFLOP/s fwd+bwd(dX,dW) +LoRA, % MFMA peak, OPT-66B layer"
 
 
@@ -59,6 +70,8 @@ def parse():
     ap.add_argument("--workload", default="opt_66b")
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens) of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the context legs (other configs, dense GEMMs, decode, update, N:M prune)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "adamw_double_prune", "prune_nm",
                                               "copy"),
@@ -434,6 +447,84 @@ def measured_traffic(op):
             "source": "profiles/traffic.json (rocprofv3 FETCH_SIZE x2.0, WRITE_SIZE x1.0 by copy calibration)"}
 
 
+def ideal_step_ms(wl, T):
+    """Ideal time of one layer step on the layer roofline basis: forward and dX
+    at the 2:4-sparse MFMA rate (dense-equivalent 2*T*N*K each), the weight
+    gradient at the dense rate (2*T*N*K computed); adapter and pruning excluded."""
+    f = sum(2 * T * l.N * l.K for l in wl.linears)
+    return (2 * f / (IDEAL_SPARSE_TFLOPS * 1e12) + f / (IDEAL_DENSE_TFLOPS * 1e12)) * 1e3
+
+
+def time_steps(lins, S, torch, steps, warmup):
+    """ms per whole step (no per-op events), after `warmup` untimed steps."""
+    for _ in range(warmup):
+        step(lins, S)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(lins, S)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def configs_pass(args, S, torch, WORKLOADS, steps=5, warmup=2):
+    """The other training configurations (GPT-2-small, BERT-Large, OPT-13B) through
+    the same step, each against its own layer roofline, and OPT-13B's few-token
+    forward at T = 16 (HBM bound) against its compressed-weight bytes."""
+    out = {}
+    for name in ("gpt2_small", "bert_large", "opt_13b"):
+        wl = WORKLOADS[name]
+        lins = [Linear(l.name, l.K, l.N, wl.T, wl.r, seed=0, index=i) for i, l in enumerate(wl.linears)]
+        ms = time_steps(lins, S, torch, steps, warmup)
+        flops = sum(sum(l.flops().values()) for l in lins)
+        ideal = ideal_step_ms(wl, wl.T)
+        out[name] = {"tokens": wl.T, "adapter_rank": wl.r, "ms_per_step": round(ms, 4),
+                     "dense_equiv_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "ideal_step_ms": round(ideal, 4), "layer_roofline_frac": round(ideal / ms, 4)}
+        if wl.decode_T:
+            for T, v in decode_pass(lins, wl, S, torch).items():
+                ideal_us = v["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
+                out[f"{name}_decode_{T}"] = dict(v, ideal_us=round(ideal_us, 1))
+        del lins
+        torch.cuda.empty_cache()
+        print(f"[bench] config {name} done", file=sys.stderr, flush=True)
+    return out
+
+
+def dense_context(lins, torch, reps=5):
+    """Context only: the same twelve GEMMs as dense bf16 products through
+    torch (hipBLASLt): Y = X W^T, dX = dY W, dW = dY^T X on the dense weights,
+    fp32 accumulation, timed with events.  The analogue of the pages' sparse vs
+    dense timing; not a target."""
+    out, tot = {}, {"fwd": 0.0, "dx": 0.0, "dw": 0.0}
+    for li in lins:
+        Y = torch.empty((li.T, li.N), dtype=torch.bfloat16, device="cuda")
+        dX = torch.empty((li.T, li.K), dtype=torch.bfloat16, device="cuda")
+        dW = torch.empty((li.N, li.K), dtype=torch.bfloat16, device="cuda")
+        calls = {"fwd": lambda: torch.mm(li.X, li.W.t(), out=Y), "dx": lambda: torch.mm(li.dY, li.W, out=dX),
+                 "dw": lambda: torch.mm(li.dY.t(), li.X, out=dW)}
+        for k, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            tot[k] += a.elapsed_time(b) / reps
+        del Y, dX, dW
+    flops = sum(2 * li.T * li.N * li.K for li in lins)
+    for k, v in tot.items():
+        out[k] = {"ms_per_step": round(v, 4), "tflops": round(flops / (v * 1e-3) / 1e12, 2)}
+    out["total_ms"] = round(sum(tot.values()), 4)
+    out["what"] = "torch.mm bf16 (hipBLASLt) on the dense weights, the same 12 GEMMs; context, not a target"
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,20 +549,8 @@ def main():
     print(f"[bench] inputs ready in {time.perf_counter() - t_in:.1f}s: {args.workload} T={T} r={wl.r}",
           file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        step(lins, S)
-    torch.cuda.synchronize()
-
     # timed region: whole steps, no per-op events
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step(lins, S)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_step = time_steps(lins, S, torch, args.steps, args.warmup)
 
     # the same steps again with an event pair around every call (per-op durations)
     ev = Events(torch)
@@ -533,16 +612,28 @@ def main():
            "value_kind": "dense-equivalent TFLOP/s (2*T*N*K per GEMM)",
            "useful_tflops": round(useful, 2),
            "frac_dense_peak_useful": round(useful / PEAK_BF16_DENSE_TFLOPS, 4),
-           "ideal_step_ms": round(useful_flops / (PEAK_BF16_DENSE_TFLOPS * 1e12) * 1e3, 3),
+           "ideal_step_ms": round(ideal_step_ms(wl, T), 3),
+           "layer_roofline_frac": round(ideal_step_ms(wl, T) / ms_step, 4),
+           "ideal_basis": "fwd and dX dense-equivalent flops at the 2:4-sparse MFMA peak (5.03 PFLOP/s), dW's computed "
+                          "dense flops at the dense peak (2.52 PFLOP/s); adapter and pruning excluded",
+           "sparse_products_target": {
+               "what": "sparse fwd and dX, dense-equivalent TFLOP/s over the 2:4-sparse bf16 MFMA peak (5.0 PFLOP/s); "
+                       "target >= 0.5",
+               "spmm_fwd": round(ops["spmm_fwd"]["frac_sparse_peak"], 4),
+               "spmm_bwd_dx": round(ops["spmm_bwd_dx"]["frac_sparse_peak"], 4)},
            "ops": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
            "roofline": roofline}
-    if wl.decode_T:
-        out["decode"] = decode_pass(lins, wl, S, torch)
-    out["weight_update"] = update_pass(lins, S, torch)
-    out["prune_nm"] = prune_nm_pass(lins, S, torch)
-    # free the layer before the CPU leg
+    if not args.no_extras:
+        if wl.decode_T:
+            out["decode"] = decode_pass(lins, wl, S, torch)
+        out["weight_update"] = update_pass(lins, S, torch)
+        out["prune_nm"] = prune_nm_pass(lins, S, torch)
+        out["dense_context"] = dense_context(lins, torch)
+    # free the layer before the other configs and the CPU leg
     del lins
     torch.cuda.empty_cache()
+    if not args.no_extras and not args.tokens and args.workload == "opt_66b":
+        out["configs"] = configs_pass(args, S, torch, WORKLOADS)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -48,7 +48,18 @@
  * before anything is enqueued; on an error nothing is written and no kernel is
  * launched.  SLOPE_ERR_HIP reports a failed launch (hipGetLastError).  Calls
  * that overlap on one stream are ordered; the library keeps no state between
- * calls and is safe to call from several host threads.
+ * calls and is safe to call from several host threads.  Every buffer whose
+ * layout depends on the sizes of a call (workspaces, tile and token chunks)
+ * comes with its byte count, checked against the matching size query.
+ *
+ * Adapter arguments (L_or_null, R_or_null, r): both factors with r > 0 turn
+ * the adapter on; both NULL (any r >= 0) turn it off.  Exactly one factor, or
+ * factors with r == 0, is SLOPE_ERR_INVALID_ARG.
+ *
+ * Data checks.  Mask content is validated only where a mask comes from the
+ * caller (slope_compress24): groups keeping more than two positions are
+ * counted into a caller-owned device counter, read after the stream is
+ * synchronised.  No device-side status is kept inside the library.
  */
 #ifndef SLOPE_H_
 #define SLOPE_H_
@@ -67,7 +78,7 @@ typedef enum {
   SLOPE_ERR_INVALID_ARG = -1, /* null pointer, unknown dtype, negative size */
   SLOPE_ERR_SHAPE = -2,       /* a 2:4 dimension not a multiple of 4 (8 where stated) */
   SLOPE_ERR_ALIGN = -3,       /* a pointer not 16-byte aligned */
-  SLOPE_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+  SLOPE_ERR_WORKSPACE = -4,   /* workspace or operand buffer missing, or fewer bytes than its size query */
   SLOPE_ERR_HIP = -5,         /* the HIP runtime reported an error */
   SLOPE_ERR_UNSUPPORTED = -6  /* dtype combination or size beyond the limits */
 } slope_status;
@@ -235,14 +246,15 @@ slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_
                                void* packed, int64_t packed_bytes, void* stream);
 
 /* slope_spmm_fwd with W_s given in tile-chunk form (slope_pack_sparse of
- * values_s, meta_s; rows N, cols K): same result, bitwise.  16-bit inputs only;
- * K % 16 == 0, K <= 2^21, N % 4 == 0, adapter rank r <= 128.  Errors as
+ * values_s, meta_s; rows N, cols K): same result, bitwise.  packed_s_bytes:
+ * bytes of packed_s, at least slope_packed_sparse_bytes(N, K).  16-bit inputs
+ * only; K % 16 == 0, K <= 2^21, N % 4 == 0, adapter rank r <= 128.  Errors as
  * slope_spmm_fwd, plus SLOPE_ERR_UNSUPPORTED / SLOPE_ERR_SHAPE for the limits
- * above. */
+ * above and SLOPE_ERR_WORKSPACE for a short packed_s. */
 slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
-                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
-                                   int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* Y,
-                                   void* stream);
+                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                                   const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
+                                   void* Y, void* stream);
 
 /* slope_spmm_bwd_dx with W_dpT given in tile-chunk form (slope_pack_sparse of
  * values_dpT, meta_dpT; rows K, cols N): same result, bitwise.  With L [K, r]
@@ -250,12 +262,14 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
  * (the derivative of explainer 2.B's term):
  *   dX [T, K] = dY . W_dp (+ (dY . R^T) . L^T)
  * using workspace_or_null of slope_lowrank_workspace_bytes(T, N, r, K) bytes
- * (note the order: the reduction runs over N, the output over K).  16-bit
- * inputs only; N % 16 == 0, N <= 2^21, K % 4 == 0, r <= 128. */
+ * (note the order: the reduction runs over N, the output over K).
+ * packed_dpT_bytes: bytes of packed_dpT, at least slope_packed_sparse_bytes(K,
+ * N).  16-bit inputs only; N % 16 == 0, N <= 2^21, K % 4 == 0, r <= 128.
+ * Errors as slope_spmm_fwd_packed. */
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
-                                      const void* packed_dpT, int64_t K, const void* L_or_null,
-                                      const void* R_or_null, int64_t r, void* workspace_or_null,
-                                      int64_t workspace_bytes, void* dX, void* stream);
+                                      const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
+                                      const void* L_or_null, const void* R_or_null, int64_t r,
+                                      void* workspace_or_null, int64_t workspace_bytes, void* dX, void* stream);
 
 /* Bytes of device workspace slope_lowrank_grads_packed needs.  Host-only;
  * SLOPE_ERR_UNSUPPORTED if r > 128. */
@@ -265,21 +279,25 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
  *   dL [K, r] = X^T . (dY . R^T),   dR [r, N] = (X . L)^T . dY
  * X [T, K], dY [T, N], L, R in_dt (BF16 or F16) row-major; X_packed, dY_packed: the same
  * matrices in token-chunk form (slope_pack_tokens), as the weight gradient
- * uses them.  fwd_workspace_or_null / bwd_workspace_or_null: the adapter
+ * uses them, with their byte counts (at least slope_packed_tokens_bytes(T, K)
+ * and (T, N)).  fwd_workspace_or_null / bwd_workspace_or_null: the adapter
  * workspaces that slope_spmm_fwd_packed (X, L, R) and slope_spmm_bwd_dx_packed
  * (dY, L, R) filled for these same operands, untouched since (they hold
- * X . L and dY . R^T, which are then not recomputed); NULL to compute them
- * here (workspaces filled for the same in_dt).  dL, dR in out_dt (in_dt or
- * F32), overwritten, or added to when
- * accumulate != 0.  workspace: slope_lowrank_grads_workspace_bytes(T, K, r,
- * N) bytes, scratch.  Sums over tokens run in a fixed order.  Errors:
- * SLOPE_ERR_SHAPE unless K % 8 == 0 and N % 8 == 0; SLOPE_ERR_UNSUPPORTED
- * for r > 128; SLOPE_ERR_WORKSPACE. */
+ * X . L and dY . R^T, which are then not recomputed), with their byte counts
+ * (at least slope_lowrank_workspace_bytes(T, K, r, N) and (T, N, r, K)); NULL
+ * to compute them here.  A handed-over workspace must have been filled for the
+ * same sizes and in_dt: only its size can be checked.  dL, dR in out_dt (in_dt
+ * or F32), overwritten, or added to when accumulate != 0.  workspace:
+ * slope_lowrank_grads_workspace_bytes(T, K, r, N) bytes, scratch.  Sums over
+ * tokens run in a fixed order.  Errors: SLOPE_ERR_SHAPE unless K % 8 == 0 and
+ * N % 8 == 0; SLOPE_ERR_UNSUPPORTED for r > 128; SLOPE_ERR_WORKSPACE for any
+ * short buffer. */
 slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* dY,
-                                        const void* X_packed,
-                                        const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
+                                        const void* X_packed, int64_t X_packed_bytes, const void* dY_packed,
+                                        int64_t dY_packed_bytes, int64_t T, int64_t K, int64_t r, int64_t N,
                                         const void* L, const void* R, const void* fwd_workspace_or_null,
-                                        const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
+                                        int64_t fwd_workspace_bytes, const void* bwd_workspace_or_null,
+                                        int64_t bwd_workspace_bytes, void* workspace, int64_t workspace_bytes,
                                         void* dL, void* dR, int accumulate, void* stream);
 
 /* Bytes of device workspace slope_spmm_fwd_decode needs for T <= 64 tokens:
@@ -292,16 +310,18 @@ slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64
 /* Few-token forward (T <= 64; the inference case of the discussion page's
  * "SLoPe inference computation": weight kept sparse, adapter unmerged):
  *   Y [T, N] = X [T, K] . W_s^T (+ (X . L) . R)
- * with W_s in tile-chunk form (slope_pack_sparse, rows N, cols K).  The
- * compressed weight is streamed once, split along K over enough waves to
- * keep HBM busy; partial sums are added in a fixed order (deterministic).
- * workspace: caller-owned device memory of slope_decode_workspace_bytes(T,
- * K, r, N) bytes (16-byte aligned; scratch, overwritten).  16-bit inputs
- * only; K % 16 == 0, N % 4 == 0, r <= 128.  Errors: SLOPE_ERR_UNSUPPORTED for
- * T > 64 or the dtype/size limits, SLOPE_ERR_SHAPE, SLOPE_ERR_WORKSPACE. */
+ * with W_s in tile-chunk form (slope_pack_sparse, rows N, cols K; packed_s_bytes
+ * at least slope_packed_sparse_bytes(N, K)).  The compressed weight is
+ * streamed once, split along K over enough waves to keep HBM busy; partial
+ * sums are added in a fixed order (deterministic).  workspace: caller-owned
+ * device memory of slope_decode_workspace_bytes(T, K, r, N) bytes (16-byte
+ * aligned; scratch, overwritten).  16-bit inputs only; K % 16 == 0,
+ * N % 4 == 0, r <= 128.  Errors: SLOPE_ERR_UNSUPPORTED for T > 64 or the
+ * dtype/size limits, SLOPE_ERR_SHAPE, SLOPE_ERR_WORKSPACE. */
 slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
-                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
-                                   int64_t r, void* workspace, int64_t workspace_bytes, void* Y, void* stream);
+                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                                   const void* R_or_null, int64_t r, void* workspace, int64_t workspace_bytes, void* Y,
+                                   void* stream);
 
 /* Bytes of a 16-bit matrix M [T, C] rewritten as token chunks (see
  * slope_pack_tokens).  Host-only. */
@@ -322,12 +342,13 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
 
 /* slope_masked_wgrad on operands already packed by slope_pack_tokens:
  * dY_packed from dY [T, N], X_packed from X [T, K], both in_dt (BF16 or
- * F16; the chunks do not record it).  Same outputs, bitwise, as
+ * F16; the chunks do not record it), with their byte counts (at least
+ * slope_packed_tokens_bytes(T, N) and (T, K)).  Same outputs, bitwise, as
  * slope_masked_wgrad.  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or
- * K % 8 != 0. */
+ * K % 8 != 0; SLOPE_ERR_WORKSPACE if a packed operand is short. */
 slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
-                                       const void* X_packed, int64_t T,
-                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                       int64_t dY_packed_bytes, const void* X_packed, int64_t X_packed_bytes,
+                                       int64_t T, int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
                                        void* dW_dense_or_null, int accumulate, void* stream);
 
 /* Low-rank adapter term on its own (explainer 2.B: W_dense = W_sparse + L R):

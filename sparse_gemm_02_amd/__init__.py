@@ -70,16 +70,19 @@ _SIGS = {
     "slope_packed_tokens_bytes": (_i32, [_i64, _i64, _P_I64]),
     "slope_packed_sparse_bytes": (_i32, [_i64, _i64, _P_I64]),
     "slope_decode_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
-    "slope_spmm_fwd_decode": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "slope_spmm_fwd_decode": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                     _vp]),
     "slope_pack_sparse": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
-    "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp]),
-    "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
-                                        _vp]),
+    "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                     _vp]),
+    "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
+                                        _vp, _vp]),
     "slope_lowrank_grads_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
-    "slope_lowrank_grads_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
-                                          _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
+    "slope_lowrank_grads_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                          _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
-    "slope_masked_wgrad_packed": (_i32, [_i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
+    "slope_masked_wgrad_packed": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
+                                         _vp]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "slope_adamw": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _P_HP, _vp]),
     "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
@@ -158,6 +161,23 @@ def _nn(t):
     return p if p is not None else 256  # never dereferenced: the size is zero
 
 
+def _adapter(L, R):
+    """(L pointer, R pointer, r) of the adapter arguments.  Factors with no
+    elements (K, N or r zero) make the adapter term zero and go as two NULLs; a
+    single factor goes through as given, for the library to reject."""
+    if L is None and R is None:
+        return None, None, 0
+    r = int(L.shape[1]) if L is not None else int(R.shape[0])
+    if L is not None and R is not None and (L.numel() == 0 or R.numel() == 0):
+        return None, None, r
+    return _p(L), _p(R), r
+
+
+def _nb(t):
+    """Bytes of a buffer tensor (0 for None)."""
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def _s(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -205,10 +225,10 @@ def slope_double_prune(values_s, meta_s, N, K, values_dpT, meta_dpT, mask_dpT=No
 
 def slope_spmm_fwd(X, values_s, meta_s, N, Y, L=None, R=None, workspace=None, stream=None) -> None:
     T, K = X.shape
-    r = int(L.shape[1]) if L is not None else 0
+    pl, pr, r = _adapter(L, R)
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_spmm_fwd", library().slope_spmm_fwd(_dt(X), _dt(Y), _nn(X), T, K, _nn(values_s), _nn(meta_s), N,
-                                                      _p(L), _p(R), r, _p(workspace), wb, _nn(Y), _s(stream)))
+                                                      pl, pr, r, _p(workspace), wb, _nn(Y), _s(stream)))
 
 
 def slope_spmm_bwd_dx(dY, values_dpT, meta_dpT, K, dX, stream=None) -> None:
@@ -248,11 +268,11 @@ def slope_pack_sparse(values, meta, rows, cols, packed, stream=None) -> None:
 
 def slope_spmm_fwd_packed(X, packed_s, N, Y, L=None, R=None, workspace=None, stream=None) -> None:
     T, K = X.shape
-    r = int(L.shape[1]) if L is not None else 0
+    pl, pr, r = _adapter(L, R)
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("slope_spmm_fwd_packed", library().slope_spmm_fwd_packed(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), N,
-                                                                    _p(L), _p(R), r, _p(workspace), wb, _nn(Y),
-                                                                    _s(stream)))
+    _check("slope_spmm_fwd_packed", library().slope_spmm_fwd_packed(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s),
+                                                                    _nb(packed_s), N, pl, pr, r, _p(workspace),
+                                                                    wb, _nn(Y), _s(stream)))
 
 
 def slope_decode_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
@@ -263,20 +283,21 @@ def slope_decode_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
 
 def slope_spmm_fwd_decode(X, packed_s, N, Y, workspace, L=None, R=None, stream=None) -> None:
     T, K = X.shape
-    r = int(L.shape[1]) if L is not None else 0
+    pl, pr, r = _adapter(L, R)
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("slope_spmm_fwd_decode", library().slope_spmm_fwd_decode(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), N,
-                                                                    _p(L), _p(R), r, _p(workspace), wb, _nn(Y),
-                                                                    _s(stream)))
+    _check("slope_spmm_fwd_decode", library().slope_spmm_fwd_decode(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s),
+                                                                    _nb(packed_s), N, pl, pr, r, _p(workspace),
+                                                                    wb, _nn(Y), _s(stream)))
 
 
 def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, L=None, R=None, workspace=None, stream=None) -> None:
     T, N = dY.shape
-    r = int(L.shape[1]) if L is not None else 0
+    pl, pr, r = _adapter(L, R)
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_spmm_bwd_dx_packed", library().slope_spmm_bwd_dx_packed(_dt(dY), _dt(dX), _nn(dY), T, N,
-                                                                          _nn(packed_dpT), K, _p(L), _p(R), r,
-                                                                          _p(workspace), wb, _nn(dX), _s(stream)))
+                                                                          _nn(packed_dpT), _nb(packed_dpT), K, pl,
+                                                                          pr, r, _p(workspace), wb, _nn(dX),
+                                                                          _s(stream)))
 
 
 def slope_lowrank_grads_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
@@ -293,8 +314,9 @@ def slope_lowrank_grads_packed(X, dY, X_packed, dY_packed, L, R, workspace, dL, 
     r = int(L.shape[1])
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("slope_lowrank_grads_packed", library().slope_lowrank_grads_packed(
-        _dt(X), _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nn(dY_packed), T, K, r, N, _nn(L), _nn(R), _p(fwd_workspace),
-        _p(bwd_workspace), _p(workspace), wb, _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
+        _dt(X), _dt(dL), _nn(X), _nn(dY), _nn(X_packed), _nb(X_packed), _nn(dY_packed), _nb(dY_packed), T, K, r, N,
+        _nn(L), _nn(R), _p(fwd_workspace), _nb(fwd_workspace), _p(bwd_workspace), _nb(bwd_workspace), _p(workspace),
+        wb, _nn(dL), _nn(dR), int(bool(accumulate)), _s(stream)))
 
 
 def slope_packed_tokens_bytes(T: int, C: int) -> int:
@@ -316,8 +338,8 @@ def slope_masked_wgrad_packed(dY_packed, X_packed, T, N, K, meta_s, dW_values, d
     if in_dtype is None:
         in_dtype = dW_values.dtype if dW_values.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
     _check("slope_masked_wgrad_packed", library().slope_masked_wgrad_packed(
-        _dt(in_dtype), _dt(dW_values), _nn(dY_packed), _nn(X_packed), T, N, K, _nn(meta_s), _nn(dW_values), _p(dW_dense),
-        int(bool(accumulate)), _s(stream)))
+        _dt(in_dtype), _dt(dW_values), _nn(dY_packed), _nb(dY_packed), _nn(X_packed), _nb(X_packed), T, N, K,
+        _nn(meta_s), _nn(dW_values), _p(dW_dense), int(bool(accumulate)), _s(stream)))
 
 
 def slope_lowrank_add(X, L, R, workspace, Y, stream=None) -> None:

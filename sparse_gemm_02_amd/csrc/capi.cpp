@@ -67,11 +67,26 @@ slope_status adamw_step(const slope_adamw_params* hp, slope::AdamWStep* c) {
 
 constexpr int64_t kAdamwMaxElems = int64_t(1) << 40;
 
+// Adapter arguments: both factors with r > 0 (adapter on), or neither with any
+// r >= 0 (adapter off).  One factor without the other, or factors with r == 0,
+// is a caller error rather than a silent adapter-free product.
+slope_status adapter_args(const void* L, const void* R, int64_t r, bool* on) {
+  const bool have_l = L != nullptr, have_r = R != nullptr;
+  if (have_l != have_r) return SLOPE_ERR_INVALID_ARG;
+  if (have_l && r == 0) return SLOPE_ERR_INVALID_ARG;
+  *on = have_l && r > 0;
+  if (*on) {
+    SLOPE_TRY(ptr(L, true));
+    SLOPE_TRY(ptr(R, true));
+  }
+  return SLOPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int slope_version(void) { return 100; }
+int slope_version(void) { return 200; }
 
 const char* slope_status_string(int status) {
   switch (status) {
@@ -79,7 +94,7 @@ const char* slope_status_string(int status) {
     case SLOPE_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown dtype or negative size)";
     case SLOPE_ERR_SHAPE: return "a 2:4 dimension is not a multiple of 4";
     case SLOPE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case SLOPE_ERR_WORKSPACE: return "adapter workspace missing or too small";
+    case SLOPE_ERR_WORKSPACE: return "workspace or operand buffer missing or too small";
     case SLOPE_ERR_HIP: return "HIP runtime error";
     case SLOPE_ERR_UNSUPPORTED: return "unsupported dtype combination or size";
     default: return "unknown status";
@@ -184,11 +199,8 @@ slope_status slope_spmm_fwd(slope_dtype in_dt, slope_dtype out_dt, const void* X
   SLOPE_TRY(ptr(values_s, true));
   SLOPE_TRY(ptr(meta_s, true));
   SLOPE_TRY(ptr(Y, true));
-  const bool adapter = L_or_null && R_or_null && r > 0;
-  if (adapter) {
-    SLOPE_TRY(ptr(L_or_null, true));
-    SLOPE_TRY(ptr(R_or_null, true));
-  }
+  bool adapter = false;
+  SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N) || !in_range(r)) return SLOPE_ERR_UNSUPPORTED;
   if (adapter) {
@@ -275,22 +287,20 @@ slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_
 }
 
 slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
-                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
-                                   int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* Y,
-                                   void* stream) {
+                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                                   const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
+                                   void* Y, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_s_bytes < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(packed_s, true));
   SLOPE_TRY(ptr(Y, true));
-  const bool adapter = L_or_null && R_or_null && r > 0;
-  if (adapter) {
-    SLOPE_TRY(ptr(L_or_null, true));
-    SLOPE_TRY(ptr(R_or_null, true));
-  }
+  bool adapter = false;
+  SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_s_bytes < slope::packed_sparse_bytes(N, K)) return SLOPE_ERR_WORKSPACE;
   if (adapter) {
     const int64_t need = workspace_need(T, K, r, N);
     if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
@@ -316,22 +326,21 @@ slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64
 }
 
 slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
-                                   const void* packed_s, int64_t N, const void* L_or_null, const void* R_or_null,
-                                   int64_t r, void* workspace, int64_t workspace_bytes, void* Y, void* stream) {
+                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                                   const void* R_or_null, int64_t r, void* workspace, int64_t workspace_bytes, void* Y,
+                                   void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_s_bytes < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(packed_s, true));
   SLOPE_TRY(ptr(Y, true));
   SLOPE_TRY(ptr(workspace, false));
-  const bool adapter = L_or_null && R_or_null && r > 0;
-  if (adapter) {
-    SLOPE_TRY(ptr(L_or_null, true));
-    SLOPE_TRY(ptr(R_or_null, true));
-  }
+  bool adapter = false;
+  SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
   if (T > kDecodeMaxTokens || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_s_bytes < slope::packed_sparse_bytes(N, K)) return SLOPE_ERR_WORKSPACE;
   const int64_t need = slope::decode_workspace_bytes(T, K, adapter ? r : 0, N);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
   if (T == 0 || N == 0) return SLOPE_OK;
@@ -340,22 +349,20 @@ slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const 
 }
 
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
-                                      const void* packed_dpT, int64_t K, const void* L_or_null,
-                                      const void* R_or_null, int64_t r, void* workspace_or_null,
-                                      int64_t workspace_bytes, void* dX, void* stream) {
+                                      const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
+                                      const void* L_or_null, const void* R_or_null, int64_t r,
+                                      void* workspace_or_null, int64_t workspace_bytes, void* dX, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_dpT_bytes < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY, true));
   SLOPE_TRY(ptr(packed_dpT, true));
   SLOPE_TRY(ptr(dX, true));
-  const bool adapter = L_or_null && R_or_null && r > 0;
-  if (adapter) {
-    SLOPE_TRY(ptr(L_or_null, true));
-    SLOPE_TRY(ptr(R_or_null, true));
-  }
+  bool adapter = false;
+  SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (N % 16 || K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || N > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_dpT_bytes < slope::packed_sparse_bytes(K, N)) return SLOPE_ERR_WORKSPACE;
   if (adapter) {
     // the forward's adapter workspace with the roles of K and N exchanged
     const int64_t need = workspace_need(T, N, r, K);
@@ -401,13 +408,16 @@ slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r
 }
 
 slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* dY,
-                                        const void* X_packed,
-                                        const void* dY_packed, int64_t T, int64_t K, int64_t r, int64_t N,
+                                        const void* X_packed, int64_t X_packed_bytes, const void* dY_packed,
+                                        int64_t dY_packed_bytes, int64_t T, int64_t K, int64_t r, int64_t N,
                                         const void* L, const void* R, const void* fwd_workspace_or_null,
-                                        const void* bwd_workspace_or_null, void* workspace, int64_t workspace_bytes,
+                                        int64_t fwd_workspace_bytes, const void* bwd_workspace_or_null,
+                                        int64_t bwd_workspace_bytes, void* workspace, int64_t workspace_bytes,
                                         void* dL, void* dR, int accumulate, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || workspace_bytes < 0 || X_packed_bytes < 0 || dY_packed_bytes < 0 ||
+      fwd_workspace_bytes < 0 || bwd_workspace_bytes < 0)
+    return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(dY, true));
   SLOPE_TRY(ptr(X_packed, true));
@@ -424,6 +434,13 @@ slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, c
   if (!in_range(T) || !in_range(K) || !in_range(N) || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   const GradsWs g = grads_ws(T, K, r, N);
   if (g.total > 0 && (!workspace || workspace_bytes < g.total)) return SLOPE_ERR_WORKSPACE;
+  // the token chunks and the handed-over adapter workspaces must be laid out
+  // for these very sizes: each at least the size its own query reports
+  if (r > 0 &&
+      (X_packed_bytes < slope::packed_tokens_bytes(T, K) || dY_packed_bytes < slope::packed_tokens_bytes(T, N)))
+    return SLOPE_ERR_WORKSPACE;
+  if (fwd_workspace_or_null && fwd_workspace_bytes < g.fwd) return SLOPE_ERR_WORKSPACE;
+  if (bwd_workspace_or_null && bwd_workspace_bytes < g.bwd) return SLOPE_ERR_WORKSPACE;
   if (r == 0 || K == 0 || N == 0) return SLOPE_OK;
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {   // empty sums: dL = dR = 0 (or unchanged when accumulating)
@@ -482,10 +499,11 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
 }
 
 slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
-                                       const void* X_packed, int64_t T, int64_t N, int64_t K, const uint32_t* meta_s,
-                                       void* dW_values, void* dW_dense_or_null, int accumulate, void* stream) {
+                                       int64_t dY_packed_bytes, const void* X_packed, int64_t X_packed_bytes,
+                                       int64_t T, int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
+                                       void* dW_dense_or_null, int accumulate, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || dY_packed_bytes < 0 || X_packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY_packed, true));
   SLOPE_TRY(ptr(X_packed, true));
   SLOPE_TRY(ptr(meta_s, true));
@@ -494,6 +512,8 @@ slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, co
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 8 || N % 8) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  if (dY_packed_bytes < slope::packed_tokens_bytes(T, N) || X_packed_bytes < slope::packed_tokens_bytes(T, K))
+    return SLOPE_ERR_WORKSPACE;
   if (N == 0 || K == 0) return SLOPE_OK;
   return from_hip(slope::launch_masked_wgrad_packed((Dt)in_dt, (Dt)out_dt, dY_packed, X_packed, T, N, K, meta_s,
                                                     dW_values, dW_dense_or_null, accumulate, (hipStream_t)stream));

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert S.slope_version() == 100
+    assert S.slope_version() == 200
     for code in S.STATUS:
         assert lib.slope_status_string(code)
     assert lib.slope_status_string(12345) == b"unknown status"
@@ -77,6 +77,7 @@ def test_size_queries(lib):
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails its checks first
+BIG = 1 << 40   # a byte count that passes every size check
 
 
 def test_argument_errors(lib):
@@ -110,41 +111,41 @@ def test_argument_errors(lib):
     assert lib.slope_pack_tokens(bf, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
     assert lib.slope_pack_tokens(bf, FAKE, 32, 256, FAKE, 1024, None) == -4
     assert lib.slope_pack_tokens(bf, None, 32, 256, FAKE, 1 << 30, None) == -1
-    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, FAKE, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
-    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, None, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
-    assert lib.slope_masked_wgrad_packed(7, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, FAKE, BIG, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, None, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(7, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
     # sparse tile chunks: bf16 only, cols % 16, enough room; packed products' limits
     assert lib.slope_pack_sparse(f32, FAKE, FAKE, 256, 256, FAKE, 1 << 30, None) == -6
     assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 264, FAKE, 1 << 30, None) == -2
     assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 256, FAKE, 1024, None) == -4
     assert lib.slope_pack_sparse(bf, FAKE, None, 256, 256, FAKE, 1 << 30, None) == -1
-    assert lib.slope_spmm_fwd_packed(f32, f32, FAKE, 64, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -6
-    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 264, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
-    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 66, None, None, 0, None, 0, FAKE, None) == -2
-    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
+    assert lib.slope_spmm_fwd_packed(f32, f32, FAKE, 64, 256, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 264, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, BIG, 66, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, BIG, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
                                      None) == -6
-    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, 64, None, None, 0, None, 0, FAKE, None) == -1
+    assert lib.slope_spmm_fwd_packed(bf, bf, FAKE, 64, 256, FAKE, BIG, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 72, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 64, None, BIG, 64, None, None, 0, None, 0, FAKE, None) == -1
     # the adapter's dX term needs the (N, K)-exchanged adapter workspace
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
-    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, BIG, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, 64, 256, FAKE, BIG, 64, FAKE, FAKE, 129, FAKE, 1 << 30, FAKE,
                                         None) == -6
     # adapter weight gradients
-    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 260, 8, 256, FAKE, FAKE, None, None, FAKE,
-                                          1 << 30, FAKE, FAKE, 0, None) == -2
-    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
-                                          16, FAKE, FAKE, 0, None) == -4
-    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, FAKE, 64, 256, 200, 256, FAKE, FAKE, None, None,
-                                          FAKE, 1 << 30, FAKE, FAKE, 0, None) == -6
-    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, None, FAKE, 64, 256, 8, 256, FAKE, FAKE, None, None, FAKE,
-                                          1 << 30, FAKE, FAKE, 0, None) == -1
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, BIG, FAKE, BIG, 
+                                          64, 260, 8, 256, FAKE, FAKE, None, 0, None, 0, FAKE, 1 << 30, FAKE, FAKE, 0, None) == -2
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, BIG, FAKE, BIG, 
+                                          64, 256, 8, 256, FAKE, FAKE, None, 0, None, 0, FAKE, 16, FAKE, FAKE, 0, None) == -4
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, BIG, FAKE, BIG, 
+                                          64, 256, 200, 256, FAKE, FAKE, None, 0, None, 0, FAKE, 1 << 30, FAKE, FAKE, 0, None) == -6
+    assert lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, None, BIG, FAKE, BIG, 
+                                          64, 256, 8, 256, FAKE, FAKE, None, 0, None, 0, FAKE, 1 << 30, FAKE, FAKE, 0, None) == -1
     # few-token forward: T <= 64, bf16, a workspace of the queried size
-    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
-    assert lib.slope_spmm_fwd_decode(f32, f32, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
-    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 264, FAKE, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -2
-    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, FAKE, 16, FAKE, None) == -4
-    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -4
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 65, 256, FAKE, BIG, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_decode(f32, f32, FAKE, 8, 256, FAKE, BIG, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -6
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 264, FAKE, BIG, 64, None, None, 0, FAKE, 1 << 30, FAKE, None) == -2
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, BIG, 64, None, None, 0, FAKE, 16, FAKE, None) == -4
+    assert lib.slope_spmm_fwd_decode(bf, bf, FAKE, 8, 256, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, FAKE, 64, 256, 8, 64, None, 0, FAKE, None) == -4
     assert lib.slope_lowrank_add(bf, bf, FAKE, FAKE, None, 64, 256, 8, 64, FAKE, 1 << 30, FAKE, None) == -1
     # fp16: outputs in fp16 or fp32, never bf16; fp32 inputs never give 16-bit outputs
@@ -152,11 +153,72 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd(h, bf, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
     assert lib.slope_spmm_fwd(f32, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
     assert lib.slope_spmm_fwd(bf, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
-    assert lib.slope_masked_wgrad_packed(h, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
-    assert lib.slope_masked_wgrad_packed(f32, f32, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
-    assert lib.slope_spmm_fwd_packed(h, h, FAKE, 64, 264, FAKE, 64, None, None, 0, None, 0, FAKE, None) == -2
+    assert lib.slope_masked_wgrad_packed(h, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
+    assert lib.slope_masked_wgrad_packed(f32, f32, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
+    assert lib.slope_spmm_fwd_packed(h, h, FAKE, 64, 264, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -2
     assert lib.slope_prune24(3, FAKE, 4, 4, FAKE, None, None) == -1             # no dtype 3
     assert lib.slope_pack_tokens(h, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
+
+
+def test_buffer_byte_counts(lib):
+    """Every buffer laid out for a call's sizes comes with its byte count, and a
+    count below the size query's answer is SLOPE_ERR_WORKSPACE before any launch."""
+    bf = 1
+    T, K, N, r = 64, 256, 512, 8
+    ps, pdT = S.slope_packed_sparse_bytes(N, K), S.slope_packed_sparse_bytes(K, N)
+    xp, dyp = S.slope_packed_tokens_bytes(T, K), S.slope_packed_tokens_bytes(T, N)
+    wf, wb = S.slope_lowrank_workspace_bytes(T, K, r, N), S.slope_lowrank_workspace_bytes(T, N, r, K)
+    wg = S.slope_lowrank_grads_workspace_bytes(T, K, r, N)
+    wd = S.slope_decode_workspace_bytes(16, K, 0, N)
+    fwd = lambda nb: lib.slope_spmm_fwd_packed(bf, bf, FAKE, T, K, FAKE, nb, N, None, None, 0, None, 0, FAKE, None)
+    assert fwd(ps - 1) == -4 and fwd(-1) == -1
+    dx = lambda nb: lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, T, N, FAKE, nb, K, None, None, 0, None, 0, FAKE, None)
+    assert dx(pdT - 1) == -4 and dx(-1) == -1
+    dec = lambda nb: lib.slope_spmm_fwd_decode(bf, bf, FAKE, 16, K, FAKE, nb, N, None, None, 0, FAKE, wd, FAKE, None)
+    assert dec(ps - 1) == -4
+    wg_ = lambda a, b: lib.slope_masked_wgrad_packed(bf, bf, FAKE, a, FAKE, b, T, N, K, FAKE, FAKE, None, 0, None)
+    assert wg_(dyp - 1, xp) == -4 and wg_(dyp, xp - 1) == -4 and wg_(-1, xp) == -1
+
+    def grads(xb=xp, yb=dyp, fw=None, fb=0, bw=None, bb=0, wsb=wg):
+        return lib.slope_lowrank_grads_packed(bf, bf, FAKE, FAKE, FAKE, xb, FAKE, yb, T, K, r, N, FAKE, FAKE, fw, fb,
+                                              bw, bb, FAKE, wsb, FAKE, FAKE, 0, None)
+    assert grads(xb=xp - 1) == -4
+    assert grads(yb=dyp - 1) == -4
+    assert grads(fw=FAKE, fb=wf - 1) == -4          # a handed-over forward workspace for other sizes
+    assert grads(bw=FAKE, bb=wb - 1) == -4          # ... or the dX product's
+    assert grads(fw=FAKE, fb=-1) == -1
+    assert grads(wsb=wg - 1) == -4
+
+
+def test_adapter_arguments_go_together(lib):
+    """L and R with r > 0 turn the adapter on, neither turns it off; one factor
+    alone, or factors with r == 0, is an argument error rather than a silent
+    adapter-free product."""
+    bf = 1
+    T, K, N = 64, 256, 512
+    big = 1 << 30
+    f = lambda L, R, r: lib.slope_spmm_fwd(bf, bf, FAKE, T, K, FAKE, FAKE, N, L, R, r, FAKE, big, FAKE, None)
+    fp = lambda L, R, r: lib.slope_spmm_fwd_packed(bf, bf, FAKE, T, K, FAKE, BIG, N, L, R, r, FAKE, big, FAKE, None)
+    dx = lambda L, R, r: lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, T, N, FAKE, BIG, K, L, R, r, FAKE, big, FAKE,
+                                                      None)
+    dec = lambda L, R, r: lib.slope_spmm_fwd_decode(bf, bf, FAKE, 16, K, FAKE, BIG, N, L, R, r, FAKE, big, FAKE, None)
+    for call in (f, fp, dx, dec):
+        assert call(FAKE, None, 8) == -1
+        assert call(None, FAKE, 8) == -1
+        assert call(FAKE, FAKE, 0) == -1
+        assert call(FAKE + 4, FAKE, 8) == -3
+    # both NULL is the adapter-free product whatever r says: shapes are checked next
+    assert lib.slope_spmm_fwd(bf, bf, FAKE, T, 6, FAKE, FAKE, N, None, None, 8, None, 0, FAKE, None) == -2
+
+
+def test_mask_check_is_a_caller_counter():
+    """The device-side mask check is a caller-owned counter argument of
+    slope_compress24 (groups keeping more than two positions), not library state:
+    the header exports no device-status query and -4 means a short buffer."""
+    txt = open(HEADER).read()
+    assert "int32_t* invalid_groups_or_null" in txt
+    assert "slope_last_device_error" not in re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    assert S.STATUS[-4] == "SLOPE_ERR_WORKSPACE"
 
 
 def test_adamw_argument_errors(lib):

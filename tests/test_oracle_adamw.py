@@ -76,6 +76,69 @@ def test_round_f16_is_nearest_ties_to_even():
     assert (np.abs(x[zero_cross]) <= 2.0 ** -25).all()
 
 
+def _f32_neighbours(f):
+    """The fp32 values one representable step below and above each finite f."""
+    f = np.asarray(f, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))
+
+
+def test_round_f32_is_nearest_ties_to_even():
+    # Brute force: no fp32 value adjacent to the result is nearer to the float64 input, and
+    # exact midpoints go to the pattern with an even last bit.  The inputs span normal
+    # binades, the subnormal range (quantum 2^-149), values near the overflow threshold,
+    # and exact midpoints built from neighbouring fp32 pairs (exact in float64).
+    rng = np.random.default_rng(19)
+    a = (rng.normal(size=4000) * 2.0 ** rng.integers(-120, 120, size=4000)).astype(np.float32)
+    a = a[np.isfinite(a) & (a != 0)]
+    lo, hi = _f32_neighbours(a)
+    mid = (a.astype(np.float64) + hi.astype(np.float64)) / 2           # exact halfway points
+    sub = (rng.integers(-2 ** 23, 2 ** 23, size=3000) * 2 + 1) * 2.0 ** -150  # halfway between subnormals
+    x = np.concatenate([
+        rng.normal(size=20000),
+        rng.normal(size=4000) * 2.0 ** rng.integers(-160, -126, size=4000),   # fp32 subnormal range
+        rng.normal(size=4000) * 2.0 ** rng.integers(100, 127, size=4000),
+        rng.uniform(-1, 1, size=4000) * 2.0 ** -149 * 3,                      # a few quanta around zero
+        mid, sub,
+    ])
+    r = oracle.round_f32(x)
+    assert r.dtype == np.float32 and np.isfinite(r).all()
+    got = r.astype(np.float64)
+    err = np.abs(x - got)
+    down, up = _f32_neighbours(r)
+    for nb in (down, up):
+        alt = nb.astype(np.float64)
+        ok = np.isfinite(alt)
+        d = np.abs(x - alt)
+        assert (err[ok] <= d[ok]).all()                           # no neighbour is nearer
+        tie = ok & (err == d) & (err > 0)
+        assert ((r[tie].view(np.uint32) & 1) == 0).all()          # ties go to the even pattern
+    # the constructed midpoints are ties, and a truncating rounding would fail them
+    nm = len(mid)
+    at_mid = r[20000 + 4000 * 3: 20000 + 4000 * 3 + nm]
+    assert ((at_mid == a) | (at_mid == hi)).all()
+    assert (at_mid.view(np.uint32) & 1 == 0).all()
+    assert (at_mid != np.where(np.abs(a) < np.abs(hi), a, hi)).any()   # not always toward zero
+    # a value just past a midpoint goes up, just short of it goes down
+    above = oracle.round_f32(np.nextafter(mid, np.inf * np.sign(mid)))
+    assert np.array_equal(above, np.where(np.abs(hi) > np.abs(a), hi, a))
+
+
+def test_round_f32_exact_values_and_specials():
+    rng = np.random.default_rng(20)
+    pats = np.concatenate([rng.integers(0, 2 ** 32, size=50000, dtype=np.uint64).astype(np.uint32),
+                           np.arange(0, 4096, dtype=np.uint32)])                 # subnormals and zero
+    vals = pats.view(np.float32)
+    fin = np.isfinite(vals)
+    assert np.array_equal(oracle.round_f32(vals[fin].astype(np.float64)).view(np.uint32), pats[fin])
+    big = (2 - 2 ** -24) * 2.0 ** 127                                 # midpoint above the largest finite fp32
+    assert oracle.round_f32(np.array([big]))[0] == np.inf
+    assert oracle.round_f32(np.array([np.nextafter(big, 0)]))[0] == np.float32(3.4028234663852886e38)
+    assert oracle.round_f32(np.array([2.0 ** -150]))[0] == 0.0        # halfway to the smallest subnormal: even (0)
+    assert oracle.round_f32(np.array([3 * 2.0 ** -150]))[0] == np.float32(2.0 ** -148)   # 1.5 quanta -> 2
+    assert np.isnan(oracle.round_f32(np.array([np.nan]))).all()
+
+
 def test_round_bf16_exact_values_and_specials():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = oracle.widen(bits)
