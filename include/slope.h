@@ -323,6 +323,29 @@ slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const 
                                    const void* R_or_null, int64_t r, void* workspace, int64_t workspace_bytes, void* Y,
                                    void* stream);
 
+/* Size of the static device scratch of slope_spmm_fwd_decode_noalloc: 32 MiB
+ * on each GPU the library runs on, held until the process ends. */
+#define SLOPE_DECODE_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+/* slope_spmm_fwd_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments except the workspace, same results bit for bit.
+ * Its split partial sums and X . L go to a static device array of
+ * SLOPE_DECODE_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace;
+ * the call allocates nothing (no hipMalloc or allocating library routine).
+ * It accepts sizes whose slope_decode_workspace_bytes(T, K, r, N) fits that
+ * array (at bf16 or fp16: every OPT-66B linear up to T = 16, every OPT-13B
+ * linear up to T = 64) and returns SLOPE_ERR_UNSUPPORTED beyond it.  Every
+ * call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents: calls that overlap on one GPU (several streams or host threads
+ * at once) race and must be serialised by the caller; consecutive calls on one
+ * stream are ordered and safe.  Errors: those of slope_spmm_fwd_decode, with
+ * SLOPE_ERR_UNSUPPORTED for a scratch need above the array's size. */
+slope_status slope_spmm_fwd_decode_noalloc(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T,
+                                           int64_t K, const void* packed_s, int64_t packed_s_bytes, int64_t N,
+                                           const void* L_or_null, const void* R_or_null, int64_t r, void* Y,
+                                           void* stream);
+
 /* Bytes of a 16-bit matrix M [T, C] rewritten as token chunks (see
  * slope_pack_tokens).  Host-only. */
 slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);

@@ -30,7 +30,8 @@ __all__ = [
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
-    "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_lowrank_grads_workspace_bytes",
+    "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_spmm_fwd_decode_noalloc",
+    "DECODE_NOALLOC_SCRATCH_BYTES", "slope_lowrank_grads_workspace_bytes",
     "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
     "slope_double_prune_packed", "slope_adamw_double_prune_packed", "slope_prune_compress24", "EXPORTED_SYMBOLS",
 ]
@@ -72,6 +73,8 @@ _SIGS = {
     "slope_decode_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
     "slope_spmm_fwd_decode": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                      _vp]),
+    "slope_spmm_fwd_decode_noalloc": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp,
+                                             _vp]),
     "slope_pack_sparse": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_spmm_fwd_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                      _vp]),
@@ -288,6 +291,17 @@ def slope_spmm_fwd_decode(X, packed_s, N, Y, workspace, L=None, R=None, stream=N
     _check("slope_spmm_fwd_decode", library().slope_spmm_fwd_decode(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s),
                                                                     _nb(packed_s), N, pl, pr, r, _p(workspace),
                                                                     wb, _nn(Y), _s(stream)))
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20   # SLOPE_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def slope_spmm_fwd_decode_noalloc(X, packed_s, N, Y, L=None, R=None, stream=None) -> None:
+    """slope_spmm_fwd_decode without a workspace: the library's static scratch."""
+    T, K = X.shape
+    pl, pr, r = _adapter(L, R)
+    _check("slope_spmm_fwd_decode_noalloc", library().slope_spmm_fwd_decode_noalloc(
+        _dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), _nb(packed_s), N, pl, pr, r, _nn(Y), _s(stream)))
 
 
 def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, L=None, R=None, workspace=None, stream=None) -> None:

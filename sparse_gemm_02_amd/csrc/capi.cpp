@@ -348,6 +348,32 @@ slope_status slope_spmm_fwd_decode(slope_dtype in_dt, slope_dtype out_dt, const 
                                             workspace, Y, (hipStream_t)stream));
 }
 
+slope_status slope_spmm_fwd_decode_noalloc(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T,
+                                           int64_t K, const void* packed_s, int64_t packed_s_bytes, int64_t N,
+                                           const void* L_or_null, const void* R_or_null, int64_t r, void* Y,
+                                           void* stream) {
+  SLOPE_TRY(check_io(in_dt, out_dt));
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_s_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(X, true));
+  SLOPE_TRY(ptr(packed_s, true));
+  SLOPE_TRY(ptr(Y, true));
+  bool adapter = false;
+  SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
+  if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
+  if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
+  if (T > kDecodeMaxTokens || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_s_bytes < slope::packed_sparse_bytes(N, K)) return SLOPE_ERR_WORKSPACE;
+  // the call's scratch must fit the library's static array
+  if (slope::decode_workspace_bytes(T, K, adapter ? r : 0, N) > slope::kDecodeScratchBytes)
+    return SLOPE_ERR_UNSUPPORTED;
+  if (T == 0 || N == 0) return SLOPE_OK;
+  void* scratch = nullptr;
+  hipError_t e = slope::decode_scratch_address(&scratch);
+  if (e != hipSuccess) return SLOPE_ERR_HIP;
+  return from_hip(slope::launch_spmm_decode((Dt)in_dt, (Dt)out_dt, X, T, K, packed_s, N, L_or_null, R_or_null,
+                                            adapter ? r : 0, scratch, Y, (hipStream_t)stream));
+}
+
 slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
                                       const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
                                       const void* L_or_null, const void* R_or_null, int64_t r,

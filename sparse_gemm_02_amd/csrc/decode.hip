@@ -14,12 +14,50 @@
 // launch, straight from L's own [K, r] layout, while the other blocks stream
 // the weight; the up-projection reads R in its own layout (no transposed copy
 // of R).
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "dma.h"
 #include "gemm_tile.h"
 #include "launch.h"
 
 namespace slope {
+
+// Scratch of the allocation-free few-token forward: the split partial sums
+// and X . L slices of one call, in a static device array (each GPU the library
+// runs on holds its own copy until the process ends).  Every byte a call reads
+// from it is written earlier by the same call, so nothing needs clearing; two
+// calls that overlap on one GPU share it and race.  In host code the name is a
+// host-side stand-in: only the address hipGetSymbolAddress returns for the
+// current device may be handed to kernels.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {                                        // first call on this device: look the address up once
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 namespace {
 

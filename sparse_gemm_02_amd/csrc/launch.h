@@ -116,6 +116,11 @@ hipError_t launch_spmm_packed(Dt in, Dt out, const void* B, int64_t T, int64_t K
 // sums reduced in order, plus the adapter term when r > 0 (L [K, r],
 // R [r, N]); workspace of decode_workspace_bytes(T, K, r, N) bytes.
 int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N);
+// The few-token forward's own scratch (a static device array, one per GPU):
+// its size, and its device address on the current device (looked up once per
+// device, then cached).
+constexpr int64_t kDecodeScratchBytes = int64_t(32) << 20;
+hipError_t decode_scratch_address(void** ptr);
 hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K, const void* packed, int64_t N,
                               const void* L, const void* R, int64_t r, void* workspace, void* Y, hipStream_t s);
 
