@@ -53,6 +53,7 @@ __all__ = [
     "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_add", "lowrank_bwd",
     "round_bf16", "round_f16", "round_f32", "adamw_update", "adamw_compressed", "adamw_double_prune",
     "storage_accounting", "LEGAL_NIBBLES",
+    "E4M3_MAX", "decode_e4m3", "round_e4m3", "e4m3_scale", "quantize_e4m3", "spmm_e4m3",
 ]
 
 # The six ways to keep 2 of 4 positions, as nibbles i0 | i1 << 2 with i0 < i1.
@@ -437,3 +438,78 @@ def storage_accounting(value_bits=16, index_bits=3, mask_bits=8, moment_bits=32)
                     + 2 * 2 * moment_bits)   # two optimizer moments at the non-zeros
     dense_train = 4 * value_bits + 4 * value_bits + 2 * 4 * moment_bits
     return inference, sparse_train / dense_train
+
+
+# --------------------------------------------------------------------------- 8-bit (e4m3) variant
+
+# The explainer's Technical Summary 1 (Problem Statement) names N:M sparsity
+# in general and the discussion page ("Memory Footprint Reduction During
+# Pretraining and Inference") counts 16-bit values; neither gives an 8-bit
+# format or a scaling rule.  The 8-bit variant here is this build's reading:
+# the OCP FP8 E4M3 format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits, subnormals, no infinities, the all-ones codes 0x7F / 0xFF are NaN,
+# largest finite value 448), one scale per tensor chosen from its largest
+# magnitude, products accumulated in float32 and the two scales divided out
+# at the end.
+
+E4M3_MAX = 448.0
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """Exact float64 values of E4M3 codes (uint8), from the format definition:
+    exponent field e and mantissa field m give (1 + m/8) * 2^(e - 7) for
+    e >= 1 and (m/8) * 2^-6 for e == 0; codes 0x7F and 0xFF are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def round_e4m3(x) -> np.ndarray:
+    """E4M3 codes (uint8) nearest to float64 values, ties to the even code
+    (even mantissa), saturating: magnitudes beyond 448 give +-448 (this build's
+    reading; a conversion to the largest finite value, since the format has no
+    infinity).  NaN gives 0x7F; the sign of zero is kept.
+
+    Written as a nearest-value search over the 127 finite non-negative codes."""
+    x = np.asarray(x, dtype=np.float64)
+    table = decode_e4m3(np.arange(0x7F, dtype=np.uint8))          # 0x00 .. 0x7E, increasing
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = np.abs(a - table[lo]), np.abs(table[hi] - a)
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = pick.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def e4m3_scale(bits) -> np.float32:
+    """Per-tensor scale of the 8-bit variant: 448 / amax as one float32
+    division (round to nearest), amax the largest magnitude of the stored
+    16-bit values (exact); 1 when amax is 0 or not finite."""
+    a = np.abs(widen(bits))
+    amax = float(np.max(a)) if a.size else 0.0
+    if not (amax > 0.0) or not np.isfinite(amax):
+        return np.float32(1.0)
+    return np.float32(np.float32(E4M3_MAX) / np.float32(amax))
+
+
+def quantize_e4m3(bits, scale) -> np.ndarray:
+    """E4M3 codes of stored 16-bit values times a float32 scale: the product is
+    rounded to float32 once (the kernel's precision, which decides the code),
+    then to E4M3 with round_e4m3."""
+    prod = widen(bits).astype(np.float32) * np.float32(scale)
+    return round_e4m3(prod.astype(np.float64))
+
+
+def spmm_e4m3(Xq, x_scale, values_q, meta_q, K, w_scale) -> np.ndarray:
+    """The 2:4 product on E4M3 operands: Y = (Xq . W_q^T) / (x_scale * w_scale)
+    with W_q the decompressed E4M3 weight (values_q [N, K/2] codes, meta_q the
+    same 2:4 metadata as the 16-bit weight).  Exact float64 products and sums,
+    returned unrounded; it serves the forward (X, W_s) and dX (dY, W_dp^T)."""
+    Xd = decode_e4m3(Xq)
+    Wd = decode_e4m3(decompress24(np.asarray(values_q, dtype=np.uint8), meta_q, K))   # code 0 (+0) elsewhere
+    return (Xd @ Wd.T) / (float(x_scale) * float(w_scale))
