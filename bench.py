@@ -123,6 +123,8 @@ class Linear:
         # weight-gradient operands as transposed token chunks
         self.Xp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, K)), dtype=torch.uint8, device=dev)
         self.dYp = torch.empty(max(16, S.slope_packed_tokens_bytes(T, N)), dtype=torch.uint8, device=dev)
+        # the weight gradient's token-split partial sums (empty when its tiles fill the device)
+        self.wsp = torch.empty(max(16, S.slope_wgrad_split_workspace_bytes(T, N, K)), dtype=torch.uint8, device=dev)
 
     def flops(self):
         T, N, K, r = self.T, self.N, self.K, self.r
@@ -157,7 +159,7 @@ def pack(S, li):
 
 
 def wgrad(S, li):
-    S.slope_masked_wgrad_packed(li.dYp, li.Xp, li.T, li.N, li.K, li.ms, li.dW)
+    S.slope_masked_wgrad_packed(li.dYp, li.Xp, li.T, li.N, li.K, li.ms, li.dW, split_workspace=li.wsp)
 
 
 def bwd_dx(S, li):

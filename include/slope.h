@@ -363,16 +363,31 @@ slope_status slope_packed_tokens_bytes(int64_t T, int64_t C, int64_t* bytes);
 slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t C, void* packed,
                                int64_t packed_bytes, void* stream);
 
+/* Bytes of the token-split workspace slope_masked_wgrad_packed can use for T
+ * tokens, N outputs and K inputs on the current device: fp32 partial sums of
+ * the kept gradient values, one [N, K/2] plane per token range.  0 when the
+ * output tiles alone keep the device busy (no split is made).  Host-only. */
+slope_status slope_wgrad_split_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes);
+
 /* slope_masked_wgrad on operands already packed by slope_pack_tokens:
  * dY_packed from dY [T, N], X_packed from X [T, K], both in_dt (BF16 or
  * F16; the chunks do not record it), with their byte counts (at least
  * slope_packed_tokens_bytes(T, N) and (T, K)).  Same outputs, bitwise, as
- * slope_masked_wgrad.  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or
- * K % 8 != 0; SLOPE_ERR_WORKSPACE if a packed operand is short. */
+ * slope_masked_wgrad when split_workspace_or_null is NULL.
+ * split_workspace_or_null: NULL, or caller-owned device memory of at least
+ * slope_wgrad_split_workspace_bytes(T, N, K) bytes (scratch, overwritten):
+ * when the output tiles alone would leave more than half of the compute units
+ * idle, the token reduction is then split into ranges whose fp32 partial sums
+ * are added in a fixed order by a second kernel (deterministic; the sums are
+ * grouped differently, so results may differ from the unsplit form in the
+ * last bits).  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or K % 8 != 0;
+ * SLOPE_ERR_WORKSPACE if a packed operand or the given split workspace is
+ * short. */
 slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
                                        int64_t dY_packed_bytes, const void* X_packed, int64_t X_packed_bytes,
                                        int64_t T, int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
-                                       void* dW_dense_or_null, int accumulate, void* stream);
+                                       void* dW_dense_or_null, int accumulate, void* split_workspace_or_null,
+                                       int64_t split_workspace_bytes, void* stream);
 
 /* Low-rank adapter term on its own (explainer 2.B: W_dense = W_sparse + L R):
  *   Y [T, N] += (X [T, K] . L [K, r]) . R [r, N]

@@ -28,7 +28,7 @@ __all__ = [
     "slope_version", "slope_compressed_sizes", "slope_lowrank_workspace_bytes",
     "slope_prune24", "slope_prune_nm", "slope_compress24", "slope_double_prune", "slope_spmm_fwd",
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
-    "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed",
+    "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed", "slope_wgrad_split_workspace_bytes",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
     "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_spmm_fwd_decode_noalloc",
     "DECODE_NOALLOC_SCRATCH_BYTES", "slope_lowrank_grads_workspace_bytes",
@@ -85,7 +85,8 @@ _SIGS = {
                                           _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32, _vp]),
     "slope_pack_tokens": (_i32, [_i32, _vp, _i64, _i64, _vp, _i64, _vp]),
     "slope_masked_wgrad_packed": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
-                                         _vp]),
+                                         _vp, _i64, _vp]),
+    "slope_wgrad_split_workspace_bytes": (_i32, [_i64, _i64, _i64, _P_I64]),
     "slope_lowrank_add": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "slope_adamw": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, _P_HP, _vp]),
     "slope_adamw_double_prune": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _vp, _vp,
@@ -345,15 +346,23 @@ def slope_pack_tokens(M, packed, stream=None) -> None:
     _check("slope_pack_tokens", library().slope_pack_tokens(_dt(M), _nn(M), T, C, _nn(packed), nb, _s(stream)))
 
 
+def slope_wgrad_split_workspace_bytes(T: int, N: int, K: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_wgrad_split_workspace_bytes", library().slope_wgrad_split_workspace_bytes(T, N, K, ctypes.byref(b)))
+    return b.value
+
+
 def slope_masked_wgrad_packed(dY_packed, X_packed, T, N, K, meta_s, dW_values, dW_dense=None, accumulate=False,
-                              stream=None, in_dtype=None) -> None:
+                              stream=None, in_dtype=None, split_workspace=None) -> None:
     """in_dtype: torch dtype the packed operands hold (the chunks do not record
-    it); defaults to dW_values' dtype when that is 16-bit, else bfloat16."""
+    it); defaults to dW_values' dtype when that is 16-bit, else bfloat16.
+    split_workspace: optional buffer of slope_wgrad_split_workspace_bytes()."""
     if in_dtype is None:
         in_dtype = dW_values.dtype if dW_values.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
     _check("slope_masked_wgrad_packed", library().slope_masked_wgrad_packed(
         _dt(in_dtype), _dt(dW_values), _nn(dY_packed), _nb(dY_packed), _nn(X_packed), _nb(X_packed), T, N, K,
-        _nn(meta_s), _nn(dW_values), _p(dW_dense), int(bool(accumulate)), _s(stream)))
+        _nn(meta_s), _nn(dW_values), _p(dW_dense), int(bool(accumulate)), _p(split_workspace), _nb(split_workspace),
+        _s(stream)))
 
 
 def slope_lowrank_add(X, L, R, workspace, Y, stream=None) -> None:

@@ -524,12 +524,22 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
   return from_hip(slope::launch_pack_tokens(M, T, C, packed, (hipStream_t)stream));
 }
 
+slope_status slope_wgrad_split_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes || T < 0 || K < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
+  if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::wgrad_split_bytes(T, N, K);
+  return SLOPE_OK;
+}
+
 slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
                                        int64_t dY_packed_bytes, const void* X_packed, int64_t X_packed_bytes,
                                        int64_t T, int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values,
-                                       void* dW_dense_or_null, int accumulate, void* stream) {
+                                       void* dW_dense_or_null, int accumulate, void* split_workspace_or_null,
+                                       int64_t split_workspace_bytes, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || dY_packed_bytes < 0 || X_packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || dY_packed_bytes < 0 || X_packed_bytes < 0 || split_workspace_bytes < 0)
+    return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(split_workspace_or_null, false));
   SLOPE_TRY(ptr(dY_packed, true));
   SLOPE_TRY(ptr(X_packed, true));
   SLOPE_TRY(ptr(meta_s, true));
@@ -540,9 +550,14 @@ slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, co
   if (!in_range(T) || !in_range(K) || !in_range(N)) return SLOPE_ERR_UNSUPPORTED;
   if (dY_packed_bytes < slope::packed_tokens_bytes(T, N) || X_packed_bytes < slope::packed_tokens_bytes(T, K))
     return SLOPE_ERR_WORKSPACE;
+  // the token split runs only when a split workspace is given and the shape needs one
+  const int64_t split_need = split_workspace_or_null ? slope::wgrad_split_bytes(T, N, K) : 0;
+  if (split_need > 0 && split_workspace_bytes < split_need) return SLOPE_ERR_WORKSPACE;
   if (N == 0 || K == 0) return SLOPE_OK;
   return from_hip(slope::launch_masked_wgrad_packed((Dt)in_dt, (Dt)out_dt, dY_packed, X_packed, T, N, K, meta_s,
-                                                    dW_values, dW_dense_or_null, accumulate, (hipStream_t)stream));
+                                                    dW_values, dW_dense_or_null, accumulate,
+                                                    split_need > 0 ? split_workspace_or_null : nullptr,
+                                                    (hipStream_t)stream));
 }
 
 slope_status slope_lowrank_add(slope_dtype in_dt, slope_dtype out_dt, const void* X, const void* L, const void* R,

@@ -130,11 +130,14 @@ hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K
 int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K);
 // Token chunks of a bf16 matrix [T, C] (C % 8 == 0): bytes, and the packing pass.
 int64_t packed_tokens_bytes(int64_t T, int64_t C);
+// fp32 partial sums of the weight gradient's token split on the current
+// device (0 when the tile grid fills the device without it).
+int64_t wgrad_split_bytes(int64_t T, int64_t N, int64_t K);
 hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s);
 // The weight-gradient GEMM on packed bf16 operands (N % 8 == 0, K % 8 == 0).
 hipError_t launch_masked_wgrad_packed(Dt in, Dt out, const void* dY_packed, const void* X_packed, int64_t T,
                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
-                                      int accumulate, hipStream_t s);
+                                      int accumulate, void* split_part, hipStream_t s);
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
                                const uint32_t* meta_s, void* dW_values, void* dW_dense, int accumulate,
                                void* workspace, hipStream_t s);

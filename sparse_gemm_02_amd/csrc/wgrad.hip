@@ -18,6 +18,8 @@
 // i receives value i%4 of the rows supplied by lanes i/4, i/4+4, i/4+8, i/4+12.
 // With lane j pointing at row (t + j/4), columns (c + 4*(j%4)) .. +3, lane i
 // receives column c + i of rows t .. t+3.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "tile_map.h"
@@ -360,21 +362,32 @@ struct DGeo {
   static_assert(NST >= 2 && PD >= 1, "pipeline depth");
 };
 
-template <class G, typename O, bool H>
+//
+// Token split (SPLIT, part != NULL): the grid holds `splits` copies of the tile grid;
+// copy j sums token chunks [j * kc, min((j + 1) * kc, Tch)) only and writes its
+// kept values in fp32 to part + j * N * (K / 2) (W_s's slot order, no dense
+// copy, no accumulation); wgrad_split_reduce_kernel then adds the copies in
+// order.  Used when the tile grid alone would leave most compute units idle.
+template <class G, typename O, bool H, bool SPLIT = false>
 __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint16_t* __restrict__ dp,
                                                                    const uint16_t* __restrict__ xp, int T, int N,
                                                                    int K, const uint32_t* __restrict__ meta,
                                                                    O* __restrict__ dWv, O* __restrict__ dWd,
-                                                                   int accumulate) {
+                                                                   int accumulate, float* __restrict__ part, int kc) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wk = wave % G::WGK, wn = wave / G::WGK;
   const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
+  const int ntiles = tiles_k * tiles_n;
+  const int split = SPLIT ? (int)blockIdx.x / ntiles : 0;
   int tk, tn;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_k, tiles_n, 8, tk, tn);
+  tile_of_block(SPLIT ? (int)blockIdx.x % ntiles : (int)blockIdx.x, SPLIT ? ntiles : (int)gridDim.x, tiles_k,
+                tiles_n, 8, tk, tn);
   const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
   const int64_t Tch = (T + kChunkTokens - 1) / kChunkTokens;
-  const int stages = (int)Tch;
+  // this block's token chunks [s_first, stages)
+  const int s_first = SPLIT ? split * kc : 0;
+  const int stages = SPLIT ? (s_first + kc < (int)Tch ? s_first + kc : (int)Tch) : (int)Tch;
   const uint16_t* const xs = xp + (int64_t)tk * Tch * kChunkElems;
   const uint16_t* const ds = dp + (int64_t)tn * Tch * kChunkElems;
   const uint32_t src0 = (uint32_t)(wave * G::DMA * 1024);
@@ -436,21 +449,22 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
 
   DFrags ring[G::RING];
 #pragma unroll
-  for (int p = 0; p < G::NST; ++p) issue_x(p);
+  for (int p = 0; p < G::NST; ++p) issue_x(s_first + p);
 #pragma unroll
-  for (int p = 0; p < G::PD; ++p) load_d(ring[p], p);
+  for (int p = 0; p < G::PD; ++p) load_d(ring[p], s_first + p);
   compiler_fence();                                              // the loads above are counted by the wait
-  wait_vmcnt<G::DMA * (G::NST - 1) + G::DLOADS * G::PD>();     // X's stage 0 landed (this wave's part)
+  wait_vmcnt<G::DMA * (G::NST - 1) + G::DLOADS * G::PD>();     // X's first stage landed (this wave's part)
   barrier();
   compiler_fence();                                              // the first LDS reads stay after the barrier
   XFrags x0, x1;
-  read_x(x0, 0, 0);
+  read_x(x0, s_first, 0);
   // whole groups of RING stages, at least one (the ring index stays static, no
   // early exit leaves the compiler's wait counting pessimistic, and no branch
   // around the loop lets the prologue's loads sink past its wait); stages past
   // the last token chunk read zeros and add nothing
-  const int stages_pad = stages <= G::RING ? G::RING : (stages + G::RING - 1) / G::RING * G::RING;
-  int s0 = 0;
+  const int span = stages - s_first;
+  const int stages_pad = s_first + (span <= G::RING ? G::RING : (span + G::RING - 1) / G::RING * G::RING);
+  int s0 = s_first;
   do {
 #pragma unroll
     for (int u = 0; u < G::RING; ++u) {
@@ -471,7 +485,52 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
     s0 += G::RING;
   } while (s0 < stages_pad);
   wait_vmcnt<0>();
-  wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+  if constexpr (SPLIT)
+    wgrad_store<G, float>(acc, meta, K, N, k0, n0, wk, wn, lane, part + (int64_t)split * N * (K / 2), nullptr, 0);
+  else
+    wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+}
+
+// dW from the token split's fp32 partials: one thread per 2:4 group (n, g)
+// adds the splits' two kept values in split order (then the previous values
+// with accumulate), rounds once and writes the pair in slot order, and the
+// masked dense copy from the group's metadata nibble.
+template <typename O>
+__global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(const float* __restrict__ part, int splits,
+                                                                 int64_t N, int64_t K,
+                                                                 const uint32_t* __restrict__ meta,
+                                                                 O* __restrict__ dWv, O* __restrict__ dWd,
+                                                                 int accumulate) {
+  const int64_t groups = N * (K / 4), plane = N * (K / 2), wpr = (K / 4 + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < groups; i += (int64_t)gridDim.x * 256) {
+    const int64_t n = i / (K / 4), g = i % (K / 4);
+    const float* p = part + 2 * i;
+    float v0 = 0.f, v1 = 0.f;
+    int sp = 0;
+    for (; sp + 4 <= splits; sp += 4) {            // four splits' loads in flight, added in order
+      float2 x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const float2*>(p + (int64_t)(sp + q) * plane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v0 += x[q].x; v1 += x[q].y; }
+    }
+    for (; sp < splits; ++sp) {
+      const float2 x = *reinterpret_cast<const float2*>(p + (int64_t)sp * plane);
+      v0 += x.x;
+      v1 += x.y;
+    }
+    O* vp = dWv + 2 * i;
+    // the dense copy from the new sums (store_quad adds its own previous values)
+    if (dWd) {
+      const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
+      const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+      const float x[4] = {i0 == 0 ? v0 : 0.f, i0 == 1 ? v0 : (i1 == 1 ? v1 : 0.f),
+                          i0 == 2 ? v0 : (i1 == 2 ? v1 : 0.f), i1 == 3 ? v1 : 0.f};
+      store_quad(dWd + n * K + 4 * g, x, accumulate);
+    }
+    if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
+    store_pair(vp, v0, v1);
+  }
 }
 
 typedef DGeo<4, 3> DGeoBig;
@@ -487,15 +546,50 @@ hipError_t launch_pack(const uint16_t* src, int64_t T, int64_t C, uint16_t* dst,
   return hipGetLastError();
 }
 
+// Token split of the weight-gradient GEMM: when the tile grid fills fewer
+// than half the compute units, run `splits` token ranges of kc chunks each
+// (at least kMinSplitChunks chunks, 256 tokens, per range) so that about one
+// round of blocks runs; 1 = no split.
+constexpr int64_t kMinSplitChunks = 8;
+struct WgradSplit {
+  int64_t splits, kc;
+};
+WgradSplit wgrad_split_plan(int64_t T, int64_t N, int64_t K, int64_t cus) {
+  const int64_t nb = chunks_of(K) * chunks_of(N), tch = token_chunks(T);
+  WgradSplit p{1, tch};
+  if (nb == 0 || tch < 2 * kMinSplitChunks || 2 * nb > cus) return p;
+  int64_t want = cus / nb;
+  const int64_t most = tch / kMinSplitChunks;
+  if (want > most) want = most;
+  if (want < 2) return p;
+  p.kc = cdiv(tch, want);
+  p.splits = cdiv(tch, p.kc);
+  return p;
+}
+
 template <typename O, bool H>
 hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int64_t N, int64_t K,
-                         const uint32_t* meta, O* dWv, O* dWd, int accumulate, hipStream_t s) {
+                         const uint32_t* meta, O* dWv, O* dWd, int accumulate, float* part, hipStream_t s) {
   typedef DGeoBig G;
-  auto kern = wgrad_direct_kernel<G, O, H>;
+  auto kern = wgrad_direct_kernel<G, O, H, false>;
+  auto kern_split = wgrad_direct_kernel<G, O, H, true>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const int64_t nb = chunks_of(K) * chunks_of(N);
-  kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv, dWd, accumulate);
+  const WgradSplit sp = part ? wgrad_split_plan(T, N, K, device_compute_units()) : WgradSplit{1, token_chunks(T)};
+  if (sp.splits < 2) {
+    kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv, dWd, accumulate,
+                                                        nullptr, 0);
+    return hipGetLastError();
+  }
+  static hipError_t attr_split =
+      hipFuncSetAttribute((const void*)kern_split, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+  if (attr_split != hipSuccess) return attr_split;
+  kern_split<<<(unsigned)(nb * sp.splits), G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv,
+                                                                          dWd, accumulate, part, (int)sp.kc);
+  const int64_t groups = N * (K / 4);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(groups, 256), 4096);
+  wgrad_split_reduce_kernel<O><<<grid, 256, 0, s>>>(part, (int)sp.splits, N, K, meta, dWv, dWd, accumulate);
   return hipGetLastError();
 }
 
@@ -523,24 +617,32 @@ int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K) {
 
 int64_t packed_tokens_bytes(int64_t T, int64_t C) { return chunks_of(C) * token_chunks(T) * kChunkElems * 2; }
 
+int64_t wgrad_split_bytes(int64_t T, int64_t N, int64_t K) {
+  const WgradSplit sp = wgrad_split_plan(T, N, K, device_compute_units());
+  return sp.splits < 2 ? 0 : cdiv(sp.splits * N * (K / 2) * 4, 256) * 256;
+}
+
 hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s) {
   return launch_pack((const uint16_t*)M, T, C, (uint16_t*)packed, s);
 }
 
 hipError_t launch_masked_wgrad_packed(Dt in, Dt out, const void* dY_packed, const void* X_packed, int64_t T,
                                       int64_t N, int64_t K, const uint32_t* meta_s, void* dW_values, void* dW_dense,
-                                      int accumulate, hipStream_t s) {
+                                      int accumulate, void* split_part, hipStream_t s) {
   const uint16_t* dp = (const uint16_t*)dY_packed;
   const uint16_t* xp = (const uint16_t*)X_packed;
+  float* part = (float*)split_part;
   if (out == Dt::BF16)
     return launch_packed<uint16_t, false>(dp, xp, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense,
-                                          accumulate, s);
+                                          accumulate, part, s);
   if (out == Dt::F16)
     return launch_packed<_Float16, true>(dp, xp, T, N, K, meta_s, (_Float16*)dW_values, (_Float16*)dW_dense,
-                                         accumulate, s);
+                                         accumulate, part, s);
   if (in == Dt::F16)
-    return launch_packed<float, true>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
-  return launch_packed<float, false>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, s);
+    return launch_packed<float, true>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, part,
+                                      s);
+  return launch_packed<float, false>(dp, xp, T, N, K, meta_s, (float*)dW_values, (float*)dW_dense, accumulate, part,
+                                     s);
 }
 
 hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
@@ -556,7 +658,7 @@ hipError_t launch_masked_wgrad(Dt in, Dt out, const void* dY, const void* X, int
     if (e != hipSuccess) return e;
     e = launch_pack_tokens(dY, T, N, dp, s);
     if (e != hipSuccess) return e;
-    return launch_masked_wgrad_packed(in, out, dp, xp, T, N, K, meta_s, dW_values, dW_dense, accumulate, s);
+    return launch_masked_wgrad_packed(in, out, dp, xp, T, N, K, meta_s, dW_values, dW_dense, accumulate, nullptr, s);
   }
   if (out == Dt::BF16)
     return launch_token_major<uint16_t, false>(dY, X, T, N, K, meta_s, (uint16_t*)dW_values, (uint16_t*)dW_dense,

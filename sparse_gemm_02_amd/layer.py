@@ -31,7 +31,8 @@ import torch
 from . import (slope_adamw, slope_adamw_double_prune_packed, slope_double_prune_packed, slope_lowrank_grads_packed,
                slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes, slope_masked_wgrad_packed,
                slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes, slope_packed_tokens_bytes,
-               slope_prune_compress24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed)
+               slope_prune_compress24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed,
+               slope_wgrad_split_workspace_bytes)
 
 __all__ = ["SparseLinear", "SparseAdamW", "training_state_bytes"]
 
@@ -84,7 +85,8 @@ class _SparseLinearFn(torch.autograd.Function):
             slope_pack_tokens(dY, dYp)
             if need_w:
                 dW = torch.empty_like(layer.values)
-                slope_masked_wgrad_packed(dYp, Xp, T, N, K, layer.meta, dW, in_dtype=X.dtype)
+                wsp = _bytes(slope_wgrad_split_workspace_bytes(T, N, K), X.device)
+                slope_masked_wgrad_packed(dYp, Xp, T, N, K, layer.meta, dW, in_dtype=X.dtype, split_workspace=wsp)
             if need_a:
                 dL, dR = torch.empty_like(L), torch.empty_like(R)
                 wsg = _bytes(slope_lowrank_grads_workspace_bytes(T, K, r, N), X.device)

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -99,8 +99,10 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, None, 0, FAKE, None) == -4
     assert lib.slope_spmm_fwd(bf, bf, FAKE, 64, 256, FAKE, FAKE, 64, FAKE, FAKE, 8, FAKE, 16, FAKE, None) == -4
     assert lib.slope_spmm_bwd_dx(bf, bf, FAKE, 4, 6, FAKE, FAKE, 8, FAKE, None) == -2
-    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 4, 8, 6, FAKE, FAKE, None, 0, None, 0, None) == -2
-    assert lib.slope_masked_wgrad(bf, bf, FAKE, None, 4, 8, 8, FAKE, FAKE, None, 0, None, 0, None) == -1
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 4, 8, 6, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -2
+    assert lib.slope_masked_wgrad(bf, bf, FAKE, None, 4, 8, 8, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -1
     # a workspace that is given must be large enough and aligned
     assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, FAKE, 16, None) == -4
     assert lib.slope_masked_wgrad(bf, bf, FAKE, FAKE, 64, 256, 256, FAKE, FAKE, None, 0, FAKE + 8, 1 << 30,
@@ -111,9 +113,12 @@ def test_argument_errors(lib):
     assert lib.slope_pack_tokens(bf, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
     assert lib.slope_pack_tokens(bf, FAKE, 32, 256, FAKE, 1024, None) == -4
     assert lib.slope_pack_tokens(bf, None, 32, 256, FAKE, 1 << 30, None) == -1
-    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, FAKE, BIG, 64, 260, 256, FAKE, FAKE, None, 0, None) == -2
-    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, None, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
-    assert lib.slope_masked_wgrad_packed(7, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, FAKE, BIG, 64, 260, 256, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -2
+    assert lib.slope_masked_wgrad_packed(bf, bf, FAKE, BIG, None, BIG, 64, 256, 256, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -1
+    assert lib.slope_masked_wgrad_packed(7, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -1
     # sparse tile chunks: bf16 only, cols % 16, enough room; packed products' limits
     assert lib.slope_pack_sparse(f32, FAKE, FAKE, 256, 256, FAKE, 1 << 30, None) == -6
     assert lib.slope_pack_sparse(bf, FAKE, FAKE, 256, 264, FAKE, 1 << 30, None) == -2
@@ -153,8 +158,10 @@ def test_argument_errors(lib):
     assert lib.slope_spmm_fwd(h, bf, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
     assert lib.slope_spmm_fwd(f32, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
     assert lib.slope_spmm_fwd(bf, h, FAKE, 4, 8, FAKE, FAKE, 4, None, None, 0, None, 0, FAKE, None) == -6
-    assert lib.slope_masked_wgrad_packed(h, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
-    assert lib.slope_masked_wgrad_packed(f32, f32, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0, None) == -6
+    assert lib.slope_masked_wgrad_packed(h, bf, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -6
+    assert lib.slope_masked_wgrad_packed(f32, f32, FAKE, BIG, FAKE, BIG, 64, 256, 256, FAKE, FAKE, None, 0,
+                                         None, 0, None) == -6
     assert lib.slope_spmm_fwd_packed(h, h, FAKE, 64, 264, FAKE, BIG, 64, None, None, 0, None, 0, FAKE, None) == -2
     assert lib.slope_prune24(3, FAKE, 4, 4, FAKE, None, None) == -1             # no dtype 3
     assert lib.slope_pack_tokens(h, FAKE, 32, 260, FAKE, 1 << 30, None) == -2
@@ -176,7 +183,7 @@ def test_buffer_byte_counts(lib):
     assert dx(pdT - 1) == -4 and dx(-1) == -1
     dec = lambda nb: lib.slope_spmm_fwd_decode(bf, bf, FAKE, 16, K, FAKE, nb, N, None, None, 0, FAKE, wd, FAKE, None)
     assert dec(ps - 1) == -4
-    wg_ = lambda a, b: lib.slope_masked_wgrad_packed(bf, bf, FAKE, a, FAKE, b, T, N, K, FAKE, FAKE, None, 0, None)
+    wg_ = lambda a, b: lib.slope_masked_wgrad_packed(bf, bf, FAKE, a, FAKE, b, T, N, K, FAKE, FAKE, None, 0, None, 0, None)
     assert wg_(dyp - 1, xp) == -4 and wg_(dyp, xp - 1) == -4 and wg_(-1, xp) == -1
 
     def grads(xb=xp, yb=dyp, fw=None, fb=0, bw=None, bb=0, wsb=wg):
@@ -188,6 +195,25 @@ def test_buffer_byte_counts(lib):
     assert grads(bw=FAKE, bb=wb - 1) == -4          # ... or the dX product's
     assert grads(fw=FAKE, fb=-1) == -1
     assert grads(wsb=wg - 1) == -4
+
+
+def test_wgrad_split_workspace(lib):
+    """The weight gradient's token split: its partial-sum workspace is sized by a
+    host query (0 when the output tiles fill the device on their own), and a
+    split workspace that is given must hold that many bytes."""
+    bf = 1
+    # GPT-2-small QKV: 3 x 9 output tiles of 256 x 256 leave most compute units idle
+    need = S.slope_wgrad_split_workspace_bytes(8192, 2304, 768)
+    assert need > 0 and need % (2304 * 384 * 4) == 0 and need // (2304 * 384 * 4) >= 2
+    assert S.slope_wgrad_split_workspace_bytes(8192, 27648, 9216) == 0      # OPT-66B QKV: no split
+    assert S.slope_wgrad_split_workspace_bytes(256, 2304, 768) == 0         # too few tokens to split
+    T, N, K = 8192, 2304, 768
+    xp, dyp = S.slope_packed_tokens_bytes(T, K), S.slope_packed_tokens_bytes(T, N)
+    f = lambda ws, nb: lib.slope_masked_wgrad_packed(bf, bf, FAKE, dyp, FAKE, xp, T, N, K, FAKE, FAKE, None, 0, ws,
+                                                     nb, None)
+    assert f(FAKE, need - 1) == -4
+    assert f(FAKE + 8, need) == -3
+    assert f(FAKE, -1) == -1
 
 
 def test_adapter_arguments_go_together(lib):
