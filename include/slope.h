@@ -465,6 +465,60 @@ slope_status slope_adamw_double_prune_packed(slope_dtype dt, slope_dtype grad_dt
                                              int64_t packed_s_bytes, void* packed_dpT, int64_t packed_dpT_bytes,
                                              void* stream);
 
+/* ---------------------------------------------------------------- 8-bit variant
+ * The explainer's Technical Summary 1 (Problem Statement) names N:M sparsity
+ * in general and the discussion page ("Memory Footprint Reduction During
+ * Pretraining and Inference") counts 16-bit values; the pages give no 8-bit
+ * format or scaling rule.  This variant reads them as: OCP FP8 E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F
+ * and 0xFF are NaN; largest finite 448), one float32 scale per tensor,
+ * scale = 448 / amax (amax = largest magnitude of the stored 16-bit values;
+ * one fp32 division; 1 when amax is 0 or not finite), code = E4M3 value
+ * nearest to fp32(x * scale), ties to the even code, magnitudes beyond 448
+ * saturated to +-448.  Products accumulate in float32; the scales are
+ * divided out at the end.  The 2:4 pattern and metadata are the 16-bit
+ * weight's. */
+
+/* Per-tensor scale and E4M3 codes of a 16-bit tensor M (n values, BF16 or
+ * F16): *scale (device float, 4-byte aligned) <- 448 / amax, q [n] uint8 <- codes
+ * (both overwritten; the scale word is scratch while the call runs).
+ * Deterministic.  Errors: SLOPE_ERR_UNSUPPORTED for F32 or n > 2^40. */
+slope_status slope_quantize_e4m3(slope_dtype dt, const void* M, int64_t n, float* scale, uint8_t* q, void* stream);
+
+/* Bytes of the E4M3 tile-chunk form of a compressed [rows, cols] matrix (see
+ * slope_pack_sparse_e4m3).  Host-only; SLOPE_ERR_SHAPE if cols % 16 != 0,
+ * SLOPE_ERR_UNSUPPORTED if cols > 2^21. */
+slope_status slope_packed_sparse_e4m3_bytes(int64_t rows, int64_t cols, int64_t* bytes);
+
+/* E4M3 tile chunks of a compressed 16-bit 2:4 matrix (values [rows, cols/2],
+ * meta [rows, ceil(cols/32)] as slope_compress24 / slope_double_prune write
+ * them), quantized with the matrix's own scale: *scale (device float) <- 448 /
+ * amax over the values; chunk (t, s) holds rows 256t .. 256t+255 and dense
+ * columns 128s .. 128s+127, 20480 bytes at offset (t * ceil(cols/128) + s) *
+ * 20480: first each row's 64 codes (64 bytes at row*64; 16-byte granule c at
+ * c ^ ((row / 4) % 4)), then each row's four metadata words 4s .. 4s+3 (16
+ * bytes at 16384 + row*16); rows past `rows` and columns past `cols` are 0.
+ * packed: caller-owned, at least slope_packed_sparse_e4m3_bytes(rows, cols)
+ * bytes, overwritten.  Errors: SLOPE_ERR_UNSUPPORTED for F32 or cols > 2^21,
+ * SLOPE_ERR_SHAPE if cols % 16 != 0, SLOPE_ERR_WORKSPACE if packed is short. */
+slope_status slope_pack_sparse_e4m3(slope_dtype dt, const void* values, const uint32_t* meta, int64_t rows,
+                                    int64_t cols, float* scale, void* packed, int64_t packed_bytes, void* stream);
+
+/* The 2:4 sparse product on E4M3 operands (explainer 2.A: the forward with
+ * W_s, and dX with W_dp, in the 8-bit reading above):
+ *   Y [T, N] = (Xq [T, K] . W_q^T) / (x_scale * w_scale)
+ * Xq: E4M3 codes [T, K] (slope_quantize_e4m3 of X, or of dY for dX);
+ * packed_w: slope_pack_sparse_e4m3 of W_s (rows N, cols K), or of W_dp^T
+ * (rows K, cols N) for dX, with packed_w_bytes at least
+ * slope_packed_sparse_e4m3_bytes(N, K); x_scale, w_scale: the device floats
+ * those calls wrote.  out_dt BF16 or F32.  Y is overwritten.  No adapter
+ * term (slope_lowrank_add adds it).  Errors: SLOPE_ERR_SHAPE unless
+ * K % 16 == 0 and N % 4 == 0; SLOPE_ERR_UNSUPPORTED for F16 outputs or
+ * K > 2^21; SLOPE_ERR_WORKSPACE if packed_w is short. */
+slope_status slope_spmm_e4m3_packed(slope_dtype out_dt, const uint8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                                    const void* packed_w, int64_t packed_w_bytes, const float* w_scale, int64_t N,
+                                    void* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,7 @@ __all__ = [
     "DECODE_NOALLOC_SCRATCH_BYTES", "slope_lowrank_grads_workspace_bytes",
     "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
     "slope_double_prune_packed", "slope_adamw_double_prune_packed", "slope_prune_compress24", "EXPORTED_SYMBOLS",
+    "slope_quantize_e4m3", "slope_packed_sparse_e4m3_bytes", "slope_pack_sparse_e4m3", "slope_spmm_e4m3_packed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +97,10 @@ _SIGS = {
     "slope_prune_nm": (_i32, [_i32, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]),
     "slope_adamw_double_prune_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _P_HP, _vp, _i64,
                                                _vp, _i64, _vp]),
+    "slope_quantize_e4m3": (_i32, [_i32, _vp, _i64, _vp, _vp, _vp]),
+    "slope_packed_sparse_e4m3_bytes": (_i32, [_i64, _i64, _P_I64]),
+    "slope_pack_sparse_e4m3": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp]),
+    "slope_spmm_e4m3_packed": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -436,3 +441,41 @@ def slope_adamw_double_prune(values_s, meta_s, dW_values, m, v, N, K, values_dpT
         _dt(values_s), _dt(dW_values), _nn(values_s), _nn(meta_s), _nn(dW_values), _f32(m), _f32(v), N, K,
         ctypes.byref(hp), _nn(values_dpT), _nn(meta_dpT), _p(mask_dpT), _s(stream)))
 
+
+
+# ------------------------------------------------------------------ 8-bit (E4M3) variant
+# Codes travel as torch.uint8 tensors; scales as one-element torch.float32 tensors.
+
+def slope_quantize_e4m3(M, scale, q, stream=None) -> None:
+    """scale[0] <- 448 / amax(|M|); q <- E4M3 codes of M * scale (same shape as M)."""
+    if q.dtype != torch.uint8 or q.numel() != M.numel():
+        raise ValueError("q must be a uint8 tensor with as many elements as M")
+    if scale.dtype != torch.float32:
+        raise TypeError("scale must be float32")
+    _check("slope_quantize_e4m3", library().slope_quantize_e4m3(_dt(M), _nn(M), M.numel(), _nn(scale), _nn(q),
+                                                                _s(stream)))
+
+
+def slope_packed_sparse_e4m3_bytes(rows: int, cols: int) -> int:
+    b = ctypes.c_int64()
+    _check("slope_packed_sparse_e4m3_bytes", library().slope_packed_sparse_e4m3_bytes(rows, cols, ctypes.byref(b)))
+    return b.value
+
+
+def slope_pack_sparse_e4m3(values, meta, rows, cols, scale, packed, stream=None) -> None:
+    """E4M3 tile chunks of a compressed 16-bit matrix, with its scale in scale[0]."""
+    if scale.dtype != torch.float32:
+        raise TypeError("scale must be float32")
+    _check("slope_pack_sparse_e4m3", library().slope_pack_sparse_e4m3(_dt(values), _nn(values), _nn(meta), rows, cols,
+                                                                      _nn(scale), _nn(packed), _nb(packed),
+                                                                      _s(stream)))
+
+
+def slope_spmm_e4m3_packed(Xq, x_scale, packed_w, w_scale, N, Y, stream=None) -> None:
+    """Y [T, N] = (Xq . W_q^T) / (x_scale * w_scale) on E4M3 operands."""
+    if Xq.dtype != torch.uint8:
+        raise TypeError("Xq must hold uint8 E4M3 codes")
+    T, K = Xq.shape
+    _check("slope_spmm_e4m3_packed", library().slope_spmm_e4m3_packed(_dt(Y), _nn(Xq), _nn(x_scale), T, K,
+                                                                      _nn(packed_w), _nb(packed_w), _nn(w_scale), N,
+                                                                      _nn(Y), _s(stream)))

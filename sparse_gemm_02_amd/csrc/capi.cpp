@@ -653,4 +653,57 @@ slope_status slope_adamw_double_prune_packed(slope_dtype dt, slope_dtype grad_dt
                                                           K, c, packed_s, packed_dpT, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------- 8-bit (E4M3) variant
+
+slope_status slope_quantize_e4m3(slope_dtype dt, const void* M, int64_t n, float* scale, uint8_t* q, void* stream) {
+  if ((dt != SLOPE_BF16 && dt != SLOPE_F16) || n < 0) return dt == SLOPE_F32 ? SLOPE_ERR_UNSUPPORTED : SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(M, true));
+  SLOPE_TRY(ptr(q, true));
+  if (!scale) return SLOPE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scale) & 3u) return SLOPE_ERR_ALIGN;
+  if (n > kAdamwMaxElems) return SLOPE_ERR_UNSUPPORTED;
+  return from_hip(slope::launch_quantize_e4m3((Dt)dt, M, n, scale, q, (hipStream_t)stream));
+}
+
+slope_status slope_packed_sparse_e4m3_bytes(int64_t rows, int64_t cols, int64_t* bytes) {
+  if (!bytes || rows < 0 || cols < 0) return SLOPE_ERR_INVALID_ARG;
+  if (cols % 16) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  *bytes = slope::packed_sparse_e4m3_bytes(rows, cols);
+  return SLOPE_OK;
+}
+
+slope_status slope_pack_sparse_e4m3(slope_dtype dt, const void* values, const uint32_t* meta, int64_t rows,
+                                    int64_t cols, float* scale, void* packed, int64_t packed_bytes, void* stream) {
+  if (!dt_ok(dt) || rows < 0 || cols < 0 || packed_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(values, true));
+  SLOPE_TRY(ptr(meta, true));
+  SLOPE_TRY(ptr(packed, true));
+  if (!scale) return SLOPE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scale) & 3u) return SLOPE_ERR_ALIGN;
+  if (dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;   // codes come from 16-bit values
+  if (cols % 16) return SLOPE_ERR_SHAPE;
+  if (!in_range(rows) || cols > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_bytes < slope::packed_sparse_e4m3_bytes(rows, cols)) return SLOPE_ERR_WORKSPACE;
+  return from_hip(slope::launch_pack_sparse_e4m3((Dt)dt, values, meta, rows, cols, scale, packed, (hipStream_t)stream));
+}
+
+slope_status slope_spmm_e4m3_packed(slope_dtype out_dt, const uint8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                                    const void* packed_w, int64_t packed_w_bytes, const float* w_scale, int64_t N,
+                                    void* Y, void* stream) {
+  if (!dt_ok(out_dt) || T < 0 || K < 0 || N < 0 || packed_w_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  SLOPE_TRY(ptr(Xq, true));
+  SLOPE_TRY(ptr(packed_w, true));
+  SLOPE_TRY(ptr(Y, true));
+  if (!x_scale || !w_scale) return SLOPE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) || (reinterpret_cast<uintptr_t>(w_scale) & 3u)) return SLOPE_ERR_ALIGN;
+  if (out_dt == SLOPE_F16) return SLOPE_ERR_UNSUPPORTED;   // bf16 or fp32 outputs
+  if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
+  if (!in_range(T) || !in_range(N) || K > kPackedMaxCols) return SLOPE_ERR_UNSUPPORTED;
+  if (packed_w_bytes < slope::packed_sparse_e4m3_bytes(N, K)) return SLOPE_ERR_WORKSPACE;
+  if (T == 0 || N == 0) return SLOPE_OK;
+  return from_hip(slope::launch_spmm_e4m3((Dt)out_dt, Xq, x_scale, T, K, packed_w, w_scale, N, Y,
+                                          (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -149,4 +149,15 @@ hipError_t launch_lowrank_up_add(Dt in, Dt out, const LowrankWs& w, const void* 
 // Y[t][m] = 0 (empty reductions).
 hipError_t launch_fill_zero(Dt out, void* Y, int64_t count, hipStream_t s);
 
+// 8-bit (E4M3) variant: per-tensor scale 448 / amax and codes of a 16-bit
+// tensor (scale: one device float, also used as the amax word while the
+// kernels run); E4M3 tile chunks of a compressed 16-bit matrix with its scale;
+// the 2:4 product on them, Y [T, M] = (Xq . W_q^T) / (x_scale * w_scale).
+int64_t packed_sparse_e4m3_bytes(int64_t rows, int64_t cols);
+hipError_t launch_quantize_e4m3(Dt dt, const void* M, int64_t n, float* scale, uint8_t* q, hipStream_t s);
+hipError_t launch_pack_sparse_e4m3(Dt dt, const void* values, const uint32_t* meta, int64_t M, int64_t Kred,
+                                   float* scale, void* packed, hipStream_t s);
+hipError_t launch_spmm_e4m3(Dt out, const uint8_t* Xq, const float* x_scale, int64_t T, int64_t Kred,
+                            const void* packed, const float* w_scale, int64_t M, void* Y, hipStream_t s);
+
 }  // namespace slope
