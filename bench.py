@@ -38,7 +38,8 @@ gives the forward and dX products as fractions of the 2:4-sparse peak.
 `configs` runs the GPT-2-small, BERT-Large and OPT-13B layers (and OPT-13B's
 few-token forward at T = 16) through the same step, each against its own
 ideal; `dense_context` times the same twelve GEMMs as dense bf16 products
-through torch (context only).  `cpu_baseline` times the CPU oracle on a
+through torch (context only); `fp8` times the forward and dX products of the
+8-bit (E4M3) variant on the same layer (quantizing and packing apart).  `cpu_baseline` times the CPU oracle on a
 bounded slice of the same layer on this host.
 """
 from __future__ import annotations
@@ -432,6 +433,77 @@ def update_pass(lins, S, torch, reps=10):
                     "tile chunks (four linears) + AdamW on the adapter factors; fp32 moments"}
 
 
+PEAK_FP8_SPARSE_TFLOPS = 10000.0   # MI355X 2:4-sparse fp8 MFMA, dense-equivalent (twice the 5.0 PFLOP/s dense fp8)
+
+
+def fp8_pass(lins, S, torch, reps=10):
+    """The 8-bit (E4M3) variant of the sparse products on the same layer: X and
+    dY quantized per tensor (slope_quantize_e4m3), W_s and the double-pruned
+    W_dp^T turned into E4M3 tile chunks (slope_pack_sparse_e4m3), then the
+    forward and dX products (slope_spmm_e4m3_packed, bf16 outputs).  The
+    products are reported as dense-equivalent TFLOP/s against the 2:4-sparse
+    fp8 peak; quantizing and packing are timed apart (HBM bound)."""
+    st = []
+    for li in lins:
+        vdp = torch.empty((li.K, li.N // 2), dtype=torch.bfloat16, device="cuda")
+        mdp = torch.empty((li.K, (li.N // 4 + 7) // 8), dtype=torch.int32, device="cuda")
+        S.slope_double_prune(li.vs, li.ms, li.N, li.K, vdp, mdp)
+        o = dict(li=li, vdp=vdp, mdp=mdp,
+                 xq=torch.empty((li.T, li.K), dtype=torch.uint8, device="cuda"),
+                 dyq=torch.empty((li.T, li.N), dtype=torch.uint8, device="cuda"),
+                 pw=torch.empty(S.slope_packed_sparse_e4m3_bytes(li.N, li.K), dtype=torch.uint8, device="cuda"),
+                 pdp=torch.empty(S.slope_packed_sparse_e4m3_bytes(li.K, li.N), dtype=torch.uint8, device="cuda"),
+                 sc=torch.empty(4, dtype=torch.float32, device="cuda"))
+        st.append(o)
+
+    def prep():
+        for o in st:
+            li, sc = o["li"], o["sc"]
+            S.slope_quantize_e4m3(li.X, sc[0:1], o["xq"])
+            S.slope_quantize_e4m3(li.dY, sc[1:2], o["dyq"])
+            S.slope_pack_sparse_e4m3(li.vs, li.ms, li.N, li.K, sc[2:3], o["pw"])
+            S.slope_pack_sparse_e4m3(o["vdp"], o["mdp"], li.K, li.N, sc[3:4], o["pdp"])
+
+    def fwd():
+        for o in st:
+            li, sc = o["li"], o["sc"]
+            S.slope_spmm_e4m3_packed(o["xq"], sc[0:1], o["pw"], sc[2:3], li.N, li.Y)
+
+    def dx():
+        for o in st:
+            li, sc = o["li"], o["sc"]
+            S.slope_spmm_e4m3_packed(o["dyq"], sc[1:2], o["pdp"], sc[3:4], li.K, li.dX)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_prep, t_fwd, t_dx = timed(prep), timed(fwd), timed(dx)
+    flops = sum(2 * li.T * li.N * li.K for li in lins)
+    # algorithmic bytes: each activation read twice (amax, then codes) and its
+    # codes written (5 B per element); each compressed weight's values read
+    # twice, its metadata read and its chunks written (2.75 B per dense weight)
+    prep_bytes = sum(5 * li.T * (li.K + li.N) + 2 * 2.75 * li.N * li.K for li in lins)
+    out = {"what": "E4M3 (OCP fp8) operands, per-tensor amax scales, bf16 outputs; the 2:4 pattern of the bf16 layer",
+           "quantize_and_pack": {"ms_per_step": round(t_prep, 4),
+                                 "gbs": round(prep_bytes / (t_prep * 1e-3) / 1e9, 1)}}
+    for k, t in (("spmm_fwd", t_fwd), ("spmm_bwd_dx", t_dx)):
+        de = flops / (t * 1e-3) / 1e12
+        out[k] = {"ms_per_step": round(t, 4), "dense_equiv_tflops": round(de, 2),
+                  "frac_fp8_sparse_peak": round(de / PEAK_FP8_SPARSE_TFLOPS, 4),
+                  "speedup_vs_bf16": None}
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(op):
     """HBM bytes per launch (fetched + written) of `op`'s kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has
@@ -631,6 +703,9 @@ def main():
         out["weight_update"] = update_pass(lins, S, torch)
         out["prune_nm"] = prune_nm_pass(lins, S, torch)
         out["dense_context"] = dense_context(lins, torch)
+        out["fp8"] = fp8_pass(lins, S, torch)
+        for k in ("spmm_fwd", "spmm_bwd_dx"):
+            out["fp8"][k]["speedup_vs_bf16"] = round(ops[k]["ms_per_step"] / out["fp8"][k]["ms_per_step"], 3)
     # free the layer before the other configs and the CPU leg
     del lins
     torch.cuda.empty_cache()

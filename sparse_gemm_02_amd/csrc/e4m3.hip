@@ -74,22 +74,32 @@ __global__ void amax_clear_kernel(uint32_t* amax) { *amax = 0u; }
 
 // amax <- max(amax, |x|) over n 16-bit values, as fp32 bits (an integer maximum
 // of non-negative fp32 patterns: order independent, so deterministic).  Eight
-// values per thread from one 16-byte load, a wave maximum by shuffles, one
-// atomic per wave.
+// values per thread from each 16-byte load, four loads in flight, a block
+// maximum by shuffles and LDS, one atomic per block (a few hundred blocks: the
+// atomics on the one word are serialised at the cache).
 template <typename In>
 __global__ __launch_bounds__(256) void amax_kernel(const In* __restrict__ src, int64_t n, uint32_t* amax) {
+  __shared__ uint32_t wmax[4];
   uint32_t m = 0u;
-  const int64_t n8 = n / 8;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * i);
+  const int64_t n8 = n / 8, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < n8; i0 += 4 * stride) {
+    u32x4 w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const In lo = __builtin_bit_cast(In, (uint16_t)(w[e] & 0xFFFFu));
-      const In hi = __builtin_bit_cast(In, (uint16_t)(w[e] >> 16));
-      const uint32_t a = __float_as_uint(in_to_f32<In>(lo)) & 0x7FFFFFFFu;
-      const uint32_t c = __float_as_uint(in_to_f32<In>(hi)) & 0x7FFFFFFFu;
-      m = a > m ? a : m;
-      m = c > m ? c : m;
+    for (int u = 0; u < 4; ++u) {                  // clamped addresses, masked below
+      const int64_t i = i0 + u * stride;
+      w[u] = *reinterpret_cast<const u32x4*>(src + 8 * (i < n8 ? i : i0));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const In lo = __builtin_bit_cast(In, (uint16_t)(w[u][e] & 0xFFFFu));
+        const In hi = __builtin_bit_cast(In, (uint16_t)(w[u][e] >> 16));
+        const uint32_t a = __float_as_uint(in_to_f32<In>(lo)) & 0x7FFFFFFFu;
+        const uint32_t c = __float_as_uint(in_to_f32<In>(hi)) & 0x7FFFFFFFu;
+        m = a > m ? a : m;                         // a clamped load repeats an element: harmless for a maximum
+        m = c > m ? c : m;
+      }
     }
   }
   for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
@@ -101,7 +111,14 @@ __global__ __launch_bounds__(256) void amax_kernel(const In* __restrict__ src, i
     const uint32_t x = (uint32_t)__shfl_xor((int)m, o);
     m = x > m ? x : m;
   }
-  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(amax, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) b = wmax[w] > b ? wmax[w] : b;
+    if (b != 0u) atomicMax(amax, b);
+  }
 }
 
 // scale word: from the amax bits it holds to the scale (after every reader of amax)
@@ -373,7 +390,10 @@ template <typename In>
 hipError_t amax_into(const void* src, int64_t n, float* word, hipStream_t s) {
   uint32_t* w = reinterpret_cast<uint32_t*>(word);
   amax_clear_kernel<<<1, 1, 0, s>>>(w);
-  if (n > 0) amax_kernel<In><<<grid_for(n, 256 * 8 * 4), 256, 0, s>>>((const In*)src, n, w);
+  if (n > 0) {
+    const int64_t blocks = cdiv(n, 256 * 8 * 4);
+    amax_kernel<In><<<(unsigned)(blocks < 512 ? blocks : 512), 256, 0, s>>>((const In*)src, n, w);
+  }
   return hipGetLastError();
 }
 

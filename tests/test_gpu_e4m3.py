@@ -90,8 +90,8 @@ def test_quantize_every_rounding_boundary(dt):
 
 
 def test_quantize_saturates_and_keeps_nan():
-    # a tiny amax makes the scale huge for nothing, but magnitudes beyond 448 cannot
-    # arise from the scale; NaN and a second scale check through a NaN-free tensor
+    # a NaN makes amax not finite: the scale is 1, NaN keeps code 0x7F, the other
+    # values (all E4M3 values) convert exactly, signed zeros included
     x = f32_to_bf16_bits(np.array([1.0, -1.0, 0.5, np.nan, 3.0, -2.0, 0.0, -0.0] * 2, np.float32)).reshape(1, -1)
     q, s = _quantize(x)
     assert _same_scale(s, oracle.e4m3_scale(x))                     # amax not finite: scale 1
