@@ -182,7 +182,19 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
 // s = x / (G * TG) of K to xl [s][T][rpad] (xl_columns, rows XB at a time)
 // while the other rows stream the weight.  The grid keeps the tiles' width: rows padded with idle
 // blocks to fit the X . L blocks measured up to twice as slow at T = 64.
-template <int FT, bool H, int XB = 0>
+//
+// XS (more than four tokens): X's rows for each group of kUnroll stages go to
+// LDS once per block, 128 bytes per token and stage (granule c at
+// c ^ ((t ^ (t >> 3)) & 7), the sparse GEMM's B swizzle), in two buffers: the
+// next group's rows are loaded into registers while the current group
+// multiplies, and written behind one barrier per group.  The four waves then
+// read their B fragments from LDS instead of each streaming all of X from the
+// cache (at 64 tokens X's bytes per stage are 3.5x the weight's).
+constexpr int kXsRow = 128;                        // bytes of X per token and stage
+template <int FT>
+constexpr int xs_lds_bytes() { return 2 * kUnroll * FT * 32 * kXsRow; }
+
+template <int FT, bool H, int XB = 0, bool XS = false>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ X,
                                                              const char* __restrict__ packed, int T, int K,
                                                              int stages, int kc, int64_t Npad,
@@ -237,6 +249,91 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) acc[fm][ft] = f32x16{};
 
+  if constexpr (XS) {
+    extern __shared__ __attribute__((aligned(16))) char xs_lds[];
+    typedef typename Fmt16<H>::v8 v8;
+    constexpr int TOK = FT * 32, BUF = kUnroll * TOK * kXsRow;
+    constexpr int GPT = TOK * kUnroll * 8 / 256;   // 16-byte granules of X per thread and group
+    static_assert(GPT >= 1 && (GPT == 8 || GPT == 4), "fill mapping");
+    // fill: granule q = threadIdx.x * GPT + j is row q / 8 = u * TOK + t, granule q % 8
+    auto fill_load = [&](u32x4 (&xr)[GPT], int sb) {
+#pragma unroll
+      for (int j = 0; j < GPT; ++j) {
+        const int q = (int)threadIdx.x * GPT + j, row = q >> 3, g = q & 7;
+        const int u = row / TOK, t = row % TOK, st = sb + u;
+        const bool ok = t < T && st < s1 && st * 64 + 8 * g < K;
+        xr[j] = load16(rx, ok ? (uint32_t)(t * K + st * 64 + 8 * g) * 2 : kOutOfRange);
+      }
+    };
+    auto fill_store = [&](const u32x4 (&xr)[GPT], char* buf) {
+#pragma unroll
+      for (int j = 0; j < GPT; ++j) {
+        const int q = (int)threadIdx.x * GPT + j, row = q >> 3, g = q & 7;
+        const int t = row % TOK;
+        *reinterpret_cast<u32x4*>(buf + row * kXsRow + ((g ^ ((t ^ (t >> 3)) & 7)) << 4)) = xr[j];
+      }
+    };
+    // per-lane B fragment offsets within a stage's rows: token ft*32 + lane%32,
+    // granules 4ks + lane/32 and 4ks + 2 + lane/32
+    int bo[FT][2][2];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const int t = ft * 32 + (lane & 31), sw = (t ^ (t >> 3)) & 7;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bo[ft][ks][0] = t * kXsRow + (((4 * ks + (lane >> 5)) ^ sw) << 4);
+        bo[ft][ks][1] = t * kXsRow + (((4 * ks + 2 + (lane >> 5)) ^ sw) << 4);
+      }
+    }
+    {
+      u32x4 xr[GPT];
+      fill_load(xr, s0);
+      fill_store(xr, xs_lds);
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int sb = s0; sb < s1; sb += kUnroll) {
+      v8 a[kUnroll][2][2];
+      int ix[kUnroll][2][2];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int s = sb + u;
+        const bool live = s < s1;
+        const uint32_t c = (uint32_t)(s - s0) * Chunk::CHUNK_BYTES;
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            a[u][fm][ks] = __builtin_bit_cast(v8, load16(ra, live ? c + a_off[fm][ks] : kOutOfRange));
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(ra, live ? c + m_off[fm] + ks * 4 : kOutOfRange, 0, 0);
+            ix[u][fm][ks] = (int)(w >> ix_shift);
+          }
+        }
+      }
+      const bool more = sb + kUnroll < s1;         // block-uniform
+      u32x4 xr[GPT];
+      if (more) fill_load(xr, sb + kUnroll);
+      const char* buf = xs_lds + cur * BUF;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) {
+            const char* rowp = buf + u * TOK * kXsRow;
+            const v8 lo = *reinterpret_cast<const v8*>(rowp + bo[ft][ks][0]);
+            const v8 hi = *reinterpret_cast<const v8*>(rowp + bo[ft][ks][1]);
+            const typename Fmt16<H>::v16 b =
+                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+            for (int fm = 0; fm < 2; ++fm)
+              acc[fm][ft] = Fmt16<H>::smfmac32x32x32(a[u][fm][ks], b, acc[fm][ft], ix[u][fm][ks]);
+          }
+      if (more) fill_store(xr, xs_lds + (cur ^ 1) * BUF);
+      __syncthreads();                             // next buffer written; this one read by every wave
+      cur ^= 1;
+    }
+  } else
   for (int sb = s0; sb < s1; sb += kUnroll) {
     typedef typename Fmt16<H>::v8 v8;
     v8 a[kUnroll][2][2];
@@ -450,9 +547,18 @@ int64_t decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N) {
 }
 
 namespace {
+// X staged through LDS above four tokens (XS); dynamic LDS of that variant
+template <int FT, bool H, int XB>
+hipError_t decode_xs_attr() {
+  static hipError_t e = hipFuncSetAttribute((const void*)decode_partial_kernel<FT, H, XB, true>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, xs_lds_bytes<FT>());
+  return e;
+}
+
 template <bool H>
-void decode_partial_launch(int64_t T, dim3 grid, const void* X, const void* packed, int64_t K, const DecodePlan& p,
-                           float* part, const void* L, int64_t r, int64_t rpad, int xs, float* xl, hipStream_t s) {
+hipError_t decode_partial_launch(int64_t T, dim3 grid, const void* X, const void* packed, int64_t K,
+                                 const DecodePlan& p, float* part, const void* L, int64_t r, int64_t rpad, int xs,
+                                 float* xl, hipStream_t s) {
   const uint16_t* Xb = (const uint16_t*)X;
   const char* pk = (const char*)packed;
   const uint16_t* Lb = (const uint16_t*)L;
@@ -460,22 +566,35 @@ void decode_partial_launch(int64_t T, dim3 grid, const void* X, const void* pack
     const int64_t xb = rpad / 8 * cdiv(T, kXlTok) * xs;
     dim3 g(grid.x, grid.y + (unsigned)cdiv(xb, grid.x));
     // up to four tokens a thread has at most eight rows of a slice: batches of 8
-    if (T <= kXlTok)
+    if (T <= kXlTok) {
       decode_partial_kernel<1, H, 8><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
                                                        (int)r, (int)rpad, xs, xl);
-    else if (T <= 32)
-      decode_partial_kernel<1, H, 16><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
-                                                        (int)r, (int)rpad, xs, xl);
-    else
-      decode_partial_kernel<2, H, 16><<<g, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb,
-                                                        (int)r, (int)rpad, xs, xl);
-  } else if (T <= 32) {
+    } else if (T <= 32) {
+      hipError_t e = decode_xs_attr<1, H, 16>();
+      if (e != hipSuccess) return e;
+      decode_partial_kernel<1, H, 16, true><<<g, 256, xs_lds_bytes<1>(), s>>>(
+          Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb, (int)r, (int)rpad, xs, xl);
+    } else {
+      hipError_t e = decode_xs_attr<2, H, 16>();
+      if (e != hipSuccess) return e;
+      decode_partial_kernel<2, H, 16, true><<<g, 256, xs_lds_bytes<2>(), s>>>(
+          Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, Lb, (int)r, (int)rpad, xs, xl);
+    }
+  } else if (T <= kXlTok) {
     decode_partial_kernel<1, H><<<grid, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, nullptr,
                                                      0, 0, 0, nullptr);
+  } else if (T <= 32) {
+    hipError_t e = decode_xs_attr<1, H, 0>();
+    if (e != hipSuccess) return e;
+    decode_partial_kernel<1, H, 0, true><<<grid, 256, xs_lds_bytes<1>(), s>>>(
+        Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, nullptr, 0, 0, 0, nullptr);
   } else {
-    decode_partial_kernel<2, H><<<grid, 256, 0, s>>>(Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, nullptr,
-                                                     0, 0, 0, nullptr);
+    hipError_t e = decode_xs_attr<2, H, 0>();
+    if (e != hipSuccess) return e;
+    decode_partial_kernel<2, H, 0, true><<<grid, 256, xs_lds_bytes<2>(), s>>>(
+        Xb, pk, (int)T, (int)K, p.stages, p.kc, p.Npad, part, nullptr, 0, 0, 0, nullptr);
   }
+  return hipSuccess;
 }
 }  // namespace
 
@@ -490,10 +609,9 @@ hipError_t launch_spmm_decode(Dt in, Dt out, const void* X, int64_t T, int64_t K
   const int64_t rpad = ad ? cdiv(r, 16) * 16 : 0;
   const int xs = ad ? xl_slices(T, K) : 0;
   dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
-  if (in == Dt::F16)
-    decode_partial_launch<true>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s);
-  else
-    decode_partial_launch<false>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s);
+  const hipError_t pe = in == Dt::F16 ? decode_partial_launch<true>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s)
+                                       : decode_partial_launch<false>(T, grid, X, packed, K, p, part, L, r, rpad, xs, xl, s);
+  if (pe != hipSuccess) return pe;
   const uint16_t* Ra = ad ? (const uint16_t*)R : nullptr;
   const int rp = (int)rpad;
   if (out == Dt::BF16)
