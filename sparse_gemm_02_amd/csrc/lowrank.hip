@@ -23,7 +23,6 @@ namespace {
 
 constexpr int kDownWaveRows = 64;                  // tokens per down-projection wave
 constexpr int kDownRows = 4 * kDownWaveRows;       // tokens per down-projection block
-constexpr int kDownK = 32;       // k per MFMA step
 constexpr int kRankMax = 128;    // largest rank of the MFMA down-projection
 
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -34,10 +33,14 @@ struct Sizes {
   int64_t kc, rpad, Tpad, Kpad, Npad, part, xl, lt, rt;
 };
 
+// k splits of the down-projection: one block (256 tokens, one k range) per
+// compute unit and round, so that whole rounds of blocks run (256 / token
+// blocks splits), doubled as long as every block keeps 32 or more stages of
+// 64 k; at most one split per 64 k.
 int choose_splits(int64_t T, int64_t K) {
   const int64_t tblocks = cdiv(T, kDownRows) < 1 ? 1 : cdiv(T, kDownRows);
-  int64_t want = cdiv(1024, tblocks);            // enough blocks to fill 256 CUs
-  if (want > (tblocks == 1 ? 64 : 16)) want = tblocks == 1 ? 64 : 16;   // one token block: split K further
+  int64_t want = 256 / tblocks < 1 ? 1 : 256 / tblocks;
+  while (want * 2 * 64 * 32 <= K && want * 2 * tblocks <= 1024) want *= 2;
   const int64_t ksteps = cdiv(K, 64);
   if (want > ksteps) want = ksteps;
   if (want < 1) want = 1;
@@ -123,64 +126,126 @@ __global__ __launch_bounds__(256) void transpose_hilo_kernel(const uint16_t* __r
   xlt[i] = in ? xl[t * rpad + j] : (uint16_t)0;
 }
 
-// part[s][t][j] = sum over k in split s of X[t][k] lt[j][k].  A wave owns 64
-// tokens (four 16-row MFMA A operands) and every rank column (NJ blocks of
-// 16), so each 16-byte piece of lt it loads serves four operands; operands
-// come straight from global memory and the next 32-wide k step's loads are
-// issued before the current step's MFMAs.  Dense 16x16x32 MFMA: A lane l = row
-// l%16, k = 8*(l/16)+e; B lane l = column l%16, same k; D lane l = column l%16,
-// rows 4*(l/16)+v.
+// part[s][t][j] = sum over k in split s of X[t][k] lt[j][k], with both operands staged
+// in LDS: each stage of 64 k brings the block's 256 token rows of X (128 bytes
+// each, whole cache lines) and the same 64 k of the RP rows of L^T into a ring
+// of three slots by buffer-to-LDS loads (rows and k past the block's range
+// read 0), so X streams at line granularity and L^T is fetched once per block
+// instead of once per wave.  16-byte granule c of a 128-byte LDS row r sits at
+// c ^ ((r ^ (r >> 3)) & 7) (fragment reads of 16 rows hit distinct banks).  A
+// wave owns 64 tokens (four 16-row MFMA A operands) and every rank column (NJ
+// blocks of 16), 32 k per 16x16x32 MFMA step in order.  Dense 16x16x32 MFMA:
+// A lane l = row l%16, k = 8*(l/16)+e; B lane l = column l%16, same k; D lane
+// l = column l%16, rows 4*(l/16)+v.
+template <int NJ>
+struct DownLds {
+  static constexpr int RP = NJ * 16;                          // rank rows of L^T per stage
+  static constexpr int X_DMA = 256 * 128 / 1024 / 4;           // 1 KB loads per wave and stage: 8
+  static constexpr int LT_DMA = (RP / 8 + 3) / 4;             // 8 rank rows per load, spread over 4 waves
+  static constexpr int X_BYTES = 256 * 128, LT_BYTES = LT_DMA * 4 * 1024;
+  static constexpr int SLOT = X_BYTES + LT_BYTES, NST = 3, LDS_BYTES = NST * SLOT;
+  static constexpr int DMA_PER_STAGE = X_DMA + LT_DMA;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
 template <int NJ, bool H>
-__global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ X,
-                                                           const uint16_t* __restrict__ lt, int T, int K, int r,
-                                                           int rpad, int Kpad, int kc, float* __restrict__ part) {
+__global__ __launch_bounds__(256, 1) void lowrank_down_lds_kernel(const uint16_t* __restrict__ X,
+                                                                  const uint16_t* __restrict__ lt, int T, int K,
+                                                                  int rpad, int Kpad, int kc, int r,
+                                                                  float* __restrict__ part) {
+  typedef DownLds<NJ> D;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int G = kDownWaveRows / 16;                         // 16-token operands per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int s = blockIdx.y;
-  const int64_t tw = (int64_t)blockIdx.x * kDownRows + wave * kDownWaveRows;   // first token of this wave
-  const int kb = s * kc, ke = (kb + kc < K) ? kb + kc : K;
-  // tokens past T read as 0 through the resource bound; k past the split is masked
-  const int64_t rows_left = (int64_t)T - tw;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (rows_left > 0 ? tw : 0) * K, rows_left > 0 ? rows_left * K * 2 : 0);
+  const int split = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kDownRows;
+  const int kb = split * kc, ke = (kb + kc < K) ? kb + kc : K;
+  const int stages = (ke - kb + 63) / 64;
+  const int64_t rows_t = (T - t0) < kDownRows ? (T - t0) : kDownRows;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + t0 * K, rows_t * K * 2);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(lt, (int64_t)rpad * Kpad * 2);
-  const int kl = 8 * (lane >> 4);
-  uint32_t xa[G];
+  // DMA lanes: 8 rows x 8 granules per 1 KB load; lane i -> row i / 8, stored granule i % 8
+  uint32_t x_src[D::X_DMA], l_src[D::LT_DMA];
+  int x_k[D::X_DMA], l_k[D::LT_DMA];
+  bool l_ok[D::LT_DMA];
 #pragma unroll
-  for (int g = 0; g < G; ++g) xa[g] = (uint32_t)((g * 16 + (lane & 15)) * K) * 2;
+  for (int j = 0; j < D::X_DMA; ++j) {
+    const int row = (wave * D::X_DMA + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    x_src[j] = (uint32_t)(row * K + kb + c * 8) * 2;
+    x_k[j] = kb + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < D::LT_DMA; ++j) {
+    const int row = (wave * D::LT_DMA + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    l_src[j] = (uint32_t)(row * Kpad + kb + c * 8) * 2;
+    l_k[j] = kb + c * 8;
+    l_ok[j] = row < rpad;
+  }
+  auto issue = [&](int st) {
+    char* base = lds + (st % D::NST) * D::SLOT;
+#pragma unroll
+    for (int j = 0; j < D::X_DMA; ++j) {
+      const bool ok = st < stages && x_k[j] + st * 64 < ke;
+      dma16(rx, base + (wave * D::X_DMA + j) * 1024, ok ? x_src[j] + st * 128 : kOutOfRange);
+    }
+#pragma unroll
+    for (int j = 0; j < D::LT_DMA; ++j) {
+      const bool ok = l_ok[j] && st < stages && l_k[j] + st * 64 < ke;
+      dma16(rl, base + D::X_BYTES + (wave * D::LT_DMA + j) * 1024, ok ? l_src[j] + st * 128 : kOutOfRange);
+    }
+  };
+  // fragment offsets: A row = token wave*64 + 16g + lane%16, B row = rank 16jb + lane%16;
+  // k step ks takes logical granule 4ks + lane/16 of the stage's 128-byte row
+  int a_off[2][G], b_off[2][NJ];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int row = wave * kDownWaveRows + g * 16 + (lane & 15);
+      a_off[ks][g] = row * 128 + (((4 * ks + (lane >> 4)) ^ ((row ^ (row >> 3)) & 7)) << 4);
+    }
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+      const int row = jb * 16 + (lane & 15);
+      b_off[ks][jb] = D::X_BYTES + row * 128 + (((4 * ks + (lane >> 4)) ^ ((row ^ (row >> 3)) & 7)) << 4);
+    }
+  }
   f32x4 acc[G][NJ];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[g][j] = f32x4{};
-  struct Ops {
-    u32x4 a[G], b[NJ];
-  };
-  auto load = [&](Ops& o, int k0) {
-    const int k = k0 + kl;
-    const bool ok = k0 < ke && k + 8 <= ke;
+  typedef typename Fmt16<H>::v8 v8;
+
 #pragma unroll
-    for (int g = 0; g < G; ++g) o.a[g] = load16(rx, ok ? xa[g] + k * 2 : kOutOfRange);
+  for (int p = 0; p < D::NST; ++p) issue(p);
+  wait_vmcnt<D::DMA_PER_STAGE * (D::NST - 1)>();
+  barrier();
+  compiler_fence();
+  for (int st = 0; st < stages; ++st) {
+    const char* base = lds + (st % D::NST) * D::SLOT;
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb)
-      o.b[jb] = load16(rl, ok ? (uint32_t)((jb * 16 + (lane & 15)) * Kpad + k) * 2 : kOutOfRange);
-  };
-  auto mma = [&](const Ops& o) {
+    for (int ks = 0; ks < 2; ++ks) {
+      v8 a[G], b[NJ];
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) {
-      typedef typename Fmt16<H>::v8 v8;
-      const v8 bb = __builtin_bit_cast(v8, o.b[jb]);
+      for (int g = 0; g < G; ++g) a[g] = *reinterpret_cast<const v8*>(base + a_off[ks][g]);
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g][jb] = Fmt16<H>::mfma16x16x32(__builtin_bit_cast(v8, o.a[g]), bb, acc[g][jb]);
+      for (int jb = 0; jb < NJ; ++jb) b[jb] = *reinterpret_cast<const v8*>(base + b_off[ks][jb]);
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g][jb] = Fmt16<H>::mfma16x16x32(a[g], b[jb], acc[g][jb]);
     }
-  };
-  Ops p0, p1;
-  load(p0, kb);
-  for (int k0 = kb; k0 < ke; k0 += 2 * kDownK) {
-    load(p1, k0 + kDownK);
-    mma(p0);
-    load(p0, k0 + 2 * kDownK);
-    mma(p1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();                                  // this wave's reads of stage st are in registers
+    wait_vmcnt<D::DMA_PER_STAGE * (D::NST - 2)>();   // this wave's share of stage st+1 landed
+    barrier();                                        // everyone's; stage st fully read
+    compiler_fence();
+    issue(st + D::NST);                               // refill st's slot (past the range: zeros)
   }
+  wait_vmcnt<0>();
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
     const int j = jb * 16 + (lane & 15);
@@ -189,37 +254,45 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t t = tw + 16 * g + 4 * (lane >> 4) + v;
-        if (t < T) part[((int64_t)s * T + t) * r + j] = acc[g][jb][v];
+        const int64_t t = t0 + wave * kDownWaveRows + 16 * g + 4 * (lane >> 4) + v;
+        if (t < T) part[((int64_t)split * T + t) * r + j] = acc[g][jb][v];
       }
   }
 }
 
+template <int NJ, bool H>
+hipError_t down_nj_fmt(dim3 grid, const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r,
+                       const LowrankWs& w, hipStream_t s) {
+  typedef DownLds<NJ> D;
+  auto kern = lowrank_down_lds_kernel<NJ, H>;
+  static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, D::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  kern<<<grid, 256, D::LDS_BYTES, s>>>(X, lt, (int)T, (int)K, (int)w.rpad, (int)w.Kpad, (int)w.kc, (int)r, w.part);
+  return hipSuccess;
+}
+
 template <int NJ>
-void down_nj(dim3 grid, const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
-             hipStream_t s) {
-  if (w.h16)
-    lowrank_down_kernel<NJ, true><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad,
-                                                       (int)w.kc, w.part);
-  else
-    lowrank_down_kernel<NJ, false><<<grid, 256, 0, s>>>(X, lt, (int)T, (int)K, (int)r, (int)w.rpad, (int)w.Kpad,
-                                                        (int)w.kc, w.part);
+hipError_t down_nj(dim3 grid, const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r,
+                   const LowrankWs& w, hipStream_t s) {
+  return w.h16 ? down_nj_fmt<NJ, true>(grid, X, lt, T, K, r, w, s) : down_nj_fmt<NJ, false>(grid, X, lt, T, K, r, w, s);
 }
 
 hipError_t launch_down(const uint16_t* X, const uint16_t* lt, int64_t T, int64_t K, int64_t r, const LowrankWs& w,
                        hipStream_t s) {
   const dim3 grid((unsigned)cdiv(T, kDownRows), (unsigned)w.splits);
+  hipError_t e = hipSuccess;
   switch (w.rpad / 16) {
-    case 1: down_nj<1>(grid, X, lt, T, K, r, w, s); break;
-    case 2: down_nj<2>(grid, X, lt, T, K, r, w, s); break;
-    case 3: down_nj<3>(grid, X, lt, T, K, r, w, s); break;
-    case 4: down_nj<4>(grid, X, lt, T, K, r, w, s); break;
-    case 5: down_nj<5>(grid, X, lt, T, K, r, w, s); break;
-    case 6: down_nj<6>(grid, X, lt, T, K, r, w, s); break;
-    case 7: down_nj<7>(grid, X, lt, T, K, r, w, s); break;
-    case 8: down_nj<8>(grid, X, lt, T, K, r, w, s); break;
+    case 1: e = down_nj<1>(grid, X, lt, T, K, r, w, s); break;
+    case 2: e = down_nj<2>(grid, X, lt, T, K, r, w, s); break;
+    case 3: e = down_nj<3>(grid, X, lt, T, K, r, w, s); break;
+    case 4: e = down_nj<4>(grid, X, lt, T, K, r, w, s); break;
+    case 5: e = down_nj<5>(grid, X, lt, T, K, r, w, s); break;
+    case 6: e = down_nj<6>(grid, X, lt, T, K, r, w, s); break;
+    case 7: e = down_nj<7>(grid, X, lt, T, K, r, w, s); break;
+    case 8: e = down_nj<8>(grid, X, lt, T, K, r, w, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
