@@ -6,12 +6,15 @@ transformer layer (QKV 9216->27648, O 9216->9216, FC1 9216->36864, FC2
 
     prune_compress24 (magnitude 2:4 prune and compression of W, with W_s
     written as tile chunks, one pass) -> double_prune (straight into W_dp^T's
-    tile chunks) -> spmm_fwd (+ fused adapter) -> spmm_bwd_dx (+ the
-    adapter's dX term) -> pack_tokens (X and dY into token chunks)
-    -> masked_wgrad -> lowrank_grads (dL, dR)
+    tile chunks) -> spmm_fwd (+ fused adapter; also writes X's token
+    chunks) -> spmm_bwd_dx (+ the adapter's dX term; also writes dY's token
+    chunks) -> masked_wgrad -> lowrank_grads (dL, dR)
 
 The three products run on the packed operands (the *_packed entry points);
-the packing passes are part of the step.  A `decode` object adds the
+the sparse operands' packing is part of the step, and the dense operands'
+token chunks come out of the two sparse products (the *_packed_tokens entry
+points), which stream those operands anyway; the separate packing pass
+(slope_pack_tokens, bitwise the same chunks) can be timed with --profile-op.  A `decode` object adds the
 few-token forward (slope_spmm_fwd_decode) at the workload's inference token
 counts, as HBM bytes per second, and a `weight_update` object times the optimizer
 step (AdamW on the compressed values fused with the double prune, writing both
@@ -74,8 +77,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the context legs (other configs, dense GEMMs, decode, update, N:M prune)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
-    ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "adamw_double_prune", "prune_nm",
-                                              "copy"),
+    ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "pack_tokens",
+                                              "adamw_double_prune", "prune_nm", "copy"),
                     default=None,
                     help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
     ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
@@ -138,8 +141,9 @@ class Linear:
                 "masked_wgrad": T * N * K, "lowrank_grads": 2 * T * r * (K + N)}
 
 
-OPS = ("prune_compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "pack_tokens", "masked_wgrad",
-       "lowrank_grads")
+# the step's calls; the two sparse products also write X's and dY's token
+# chunks (the weight gradient's operands), so no separate packing pass runs
+OPS = ("prune_compress24", "double_prune", "spmm_fwd", "spmm_bwd_dx", "masked_wgrad", "lowrank_grads")
 
 
 def pack_sparse(S, li):
@@ -167,6 +171,14 @@ def bwd_dx(S, li):
     S.slope_spmm_bwd_dx_packed(li.dY, li.pd, li.K, li.dX, L=li.L, R=li.R, workspace=li.ws_bwd)
 
 
+def fwd_tokens(S, li):
+    S.slope_spmm_fwd_packed_tokens(li.X, li.ps, li.N, li.Y, li.Xp, L=li.L, R=li.R, workspace=li.ws)
+
+
+def bwd_dx_tokens(S, li):
+    S.slope_spmm_bwd_dx_packed_tokens(li.dY, li.pd, li.K, li.dX, li.dYp, L=li.L, R=li.R, workspace=li.ws_bwd)
+
+
 def lowrank_grads(S, li):
     # X . L and dY . R^T come from the forward's and the dX product's workspaces
     S.slope_lowrank_grads_packed(li.X, li.dY, li.Xp, li.dYp, li.L, li.R, li.ws_grads, li.dL, li.dR,
@@ -179,9 +191,8 @@ def step(lins, S, ev=None):
         calls = (
             ("prune_compress24", lambda: prune_compress(S, li)),
             ("double_prune", lambda: double_prune(S, li)),
-            ("spmm_fwd", lambda: S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)),
-            ("spmm_bwd_dx", lambda: bwd_dx(S, li)),
-            ("pack_tokens", lambda: pack(S, li)),
+            ("spmm_fwd", lambda: fwd_tokens(S, li)),
+            ("spmm_bwd_dx", lambda: bwd_dx_tokens(S, li)),
             ("masked_wgrad", lambda: wgrad(S, li)),
             ("lowrank_grads", lambda: lowrank_grads(S, li)),
         )
@@ -311,9 +322,9 @@ def profile_mode(args, wl, T):
             elif op == "pack_sparse":
                 pack_sparse(S, li)
             elif op == "spmm_fwd":
-                S.slope_spmm_fwd_packed(li.X, li.ps, li.N, li.Y, L=li.L, R=li.R, workspace=li.ws)
+                fwd_tokens(S, li)
             elif op == "spmm_bwd_dx":
-                bwd_dx(S, li)
+                bwd_dx_tokens(S, li)
             elif op == "lowrank_grads":
                 lowrank_grads(S, li)
             elif op == "pack_tokens":
@@ -655,11 +666,9 @@ def main():
             # 2:4-sparse MFMA peak
             ops[op].update(frac_dense_peak_dense_equiv=df / t / 1e12 / PEAK_BF16_DENSE_TFLOPS,
                            frac_sparse_peak=df / t / 1e12 / PEAK_BF16_SPARSE_TFLOPS)
-    # algorithmic HBM bytes: per weight for the pruning ops, per activation
-    # element (read + written once) for the packing pass
+    # algorithmic HBM bytes per weight for the pruning ops
     # (prune_compress24: W read, values + metadata + W_s's tile chunks written)
-    hbm = {"prune_compress24": lambda l: 4.25 * l.N * l.K, "double_prune": lambda l: 2.25 * l.N * l.K,
-           "pack_tokens": lambda l: 4.0 * l.T * (l.N + l.K)}
+    hbm = {"prune_compress24": lambda l: 4.25 * l.N * l.K, "double_prune": lambda l: 2.25 * l.N * l.K}
     for op, f in hbm.items():
         by = sum(f(l) for l in lins)
         ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9

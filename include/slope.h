@@ -271,6 +271,31 @@ slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, con
                                       const void* L_or_null, const void* R_or_null, int64_t r,
                                       void* workspace_or_null, int64_t workspace_bytes, void* dX, void* stream);
 
+/* The two packed products that also write their dense operand as token
+ * chunks (the layout of slope_pack_tokens, bitwise the same bytes), so that
+ * the weight gradient's operands need no separate packing pass: the product
+ * streams X (or dY) through its tiles anyway, and each stage of 64 columns of
+ * each 256-token tile is written out once, by one of the blocks that read it.
+ * The weight gradient dW = dY^T . X at the kept weights (explainer, Technical
+ * Summary 2.A; discussion page, "Memory Footprint Reduction During
+ * Pretraining and Inference") reads these chunks.  Arguments as
+ * slope_spmm_fwd_packed / slope_spmm_bwd_dx_packed, plus X_packed (dY_packed):
+ * caller-owned device memory of at least slope_packed_tokens_bytes(T, K)
+ * (slope_packed_tokens_bytes(T, N)) bytes, 16-byte aligned, overwritten.
+ * Results Y (dX) are bitwise those of the plain calls.  Errors: those of the
+ * plain calls, SLOPE_ERR_INVALID_ARG for a NULL chunk buffer and
+ * SLOPE_ERR_WORKSPACE for a short one. */
+slope_status slope_spmm_fwd_packed_tokens(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                          const void* packed_s, int64_t packed_s_bytes, int64_t N,
+                                          const void* L_or_null, const void* R_or_null, int64_t r,
+                                          void* workspace_or_null, int64_t workspace_bytes, void* Y, void* X_packed,
+                                          int64_t X_packed_bytes, void* stream);
+slope_status slope_spmm_bwd_dx_packed_tokens(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T,
+                                             int64_t N, const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
+                                             const void* L_or_null, const void* R_or_null, int64_t r,
+                                             void* workspace_or_null, int64_t workspace_bytes, void* dX,
+                                             void* dY_packed, int64_t dY_packed_bytes, void* stream);
+
 /* Bytes of device workspace slope_lowrank_grads_packed needs.  Host-only;
  * SLOPE_ERR_UNSUPPORTED if r > 128. */
 slope_status slope_lowrank_grads_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes);

@@ -30,6 +30,7 @@ __all__ = [
     "slope_spmm_bwd_dx", "slope_masked_wgrad", "slope_lowrank_add", "slope_wgrad_workspace_bytes",
     "slope_packed_tokens_bytes", "slope_pack_tokens", "slope_masked_wgrad_packed", "slope_wgrad_split_workspace_bytes",
     "slope_packed_sparse_bytes", "slope_pack_sparse", "slope_spmm_fwd_packed", "slope_spmm_bwd_dx_packed",
+    "slope_spmm_fwd_packed_tokens", "slope_spmm_bwd_dx_packed_tokens",
     "slope_decode_workspace_bytes", "slope_spmm_fwd_decode", "slope_spmm_fwd_decode_noalloc",
     "DECODE_NOALLOC_SCRATCH_BYTES", "slope_lowrank_grads_workspace_bytes",
     "slope_lowrank_grads_packed", "slope_adamw", "slope_adamw_double_prune", "AdamWParams",
@@ -81,6 +82,10 @@ _SIGS = {
                                      _vp]),
     "slope_spmm_bwd_dx_packed": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
                                         _vp, _vp]),
+    "slope_spmm_fwd_packed_tokens": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp,
+                                            _i64, _vp, _vp, _i64, _vp]),
+    "slope_spmm_bwd_dx_packed_tokens": (_i32, [_i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp,
+                                               _i64, _vp, _vp, _i64, _vp]),
     "slope_lowrank_grads_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _P_I64]),
     "slope_lowrank_grads_packed": (_i32, [_i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                           _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32, _vp]),
@@ -284,6 +289,16 @@ def slope_spmm_fwd_packed(X, packed_s, N, Y, L=None, R=None, workspace=None, str
                                                                     wb, _nn(Y), _s(stream)))
 
 
+def slope_spmm_fwd_packed_tokens(X, packed_s, N, Y, X_packed, L=None, R=None, workspace=None, stream=None) -> None:
+    T, K = X.shape
+    pl, pr, r = _adapter(L, R)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_spmm_fwd_packed_tokens",
+           library().slope_spmm_fwd_packed_tokens(_dt(X), _dt(Y), _nn(X), T, K, _nn(packed_s), _nb(packed_s), N, pl,
+                                                  pr, r, _p(workspace), wb, _nn(Y), _nn(X_packed), _nb(X_packed),
+                                                  _s(stream)))
+
+
 def slope_decode_workspace_bytes(T: int, K: int, r: int, N: int) -> int:
     b = ctypes.c_int64()
     _check("slope_decode_workspace_bytes", library().slope_decode_workspace_bytes(T, K, r, N, ctypes.byref(b)))
@@ -318,6 +333,17 @@ def slope_spmm_bwd_dx_packed(dY, packed_dpT, K, dX, L=None, R=None, workspace=No
                                                                           _nn(packed_dpT), _nb(packed_dpT), K, pl,
                                                                           pr, r, _p(workspace), wb, _nn(dX),
                                                                           _s(stream)))
+
+
+def slope_spmm_bwd_dx_packed_tokens(dY, packed_dpT, K, dX, dY_packed, L=None, R=None, workspace=None,
+                                    stream=None) -> None:
+    T, N = dY.shape
+    pl, pr, r = _adapter(L, R)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("slope_spmm_bwd_dx_packed_tokens",
+           library().slope_spmm_bwd_dx_packed_tokens(_dt(dY), _dt(dX), _nn(dY), T, N, _nn(packed_dpT),
+                                                     _nb(packed_dpT), K, pl, pr, r, _p(workspace), wb, _nn(dX),
+                                                     _nn(dY_packed), _nb(dY_packed), _s(stream)))
 
 
 def slope_lowrank_grads_workspace_bytes(T: int, K: int, r: int, N: int) -> int:

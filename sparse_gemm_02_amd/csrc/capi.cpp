@@ -286,28 +286,35 @@ slope_status slope_pack_sparse(slope_dtype dt, const void* values, const uint32_
   return from_hip(slope::launch_pack_sparse(values, meta, rows, cols, packed, (hipStream_t)stream));
 }
 
-slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
-                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
-                                   const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
-                                   void* Y, void* stream) {
+namespace {
+// The packed products, with an optional output of the dense operand's token
+// chunks (tok == nullptr: none).
+slope_status fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                        const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                        const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* Y,
+                        void* tok, int64_t tok_bytes, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_s_bytes < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_s_bytes < 0 || workspace_bytes < 0 || tok_bytes < 0)
+    return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(X, true));
   SLOPE_TRY(ptr(packed_s, true));
   SLOPE_TRY(ptr(Y, true));
+  SLOPE_TRY(ptr(tok, false));
   bool adapter = false;
   SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (K % 16 || N % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(N) || K > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   if (packed_s_bytes < slope::packed_sparse_bytes(N, K)) return SLOPE_ERR_WORKSPACE;
+  if (tok && tok_bytes < slope::packed_tokens_bytes(T, K)) return SLOPE_ERR_WORKSPACE;
   if (adapter) {
     const int64_t need = workspace_need(T, K, r, N);
     if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
     if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
   }
-  if (T == 0 || N == 0) return SLOPE_OK;
   hipStream_t s = (hipStream_t)stream;
+  // no output rows: the token chunks (if asked for) come from the packing pass
+  if (T == 0 || N == 0) return tok && T > 0 && K > 0 ? from_hip(slope::launch_pack_tokens(X, T, K, tok, s)) : SLOPE_OK;
   slope::LowrankWs w;
   if (adapter) {
     w = slope::lowrank_layout((Dt)in_dt, workspace_or_null, T, K, r, N);
@@ -315,8 +322,9 @@ slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const 
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
   return from_hip(slope::launch_spmm_packed((Dt)in_dt, (Dt)out_dt, X, T, K, packed_s, N, adapter ? &w : nullptr, Y,
-                                            s));
+                                            tok, s));
 }
+}  // namespace
 
 slope_status slope_decode_workspace_bytes(int64_t T, int64_t K, int64_t r, int64_t N, int64_t* bytes) {
   if (!bytes || T < 0 || K < 0 || r < 0 || N < 0) return SLOPE_ERR_INVALID_ARG;
@@ -374,29 +382,33 @@ slope_status slope_spmm_fwd_decode_noalloc(slope_dtype in_dt, slope_dtype out_dt
                                             adapter ? r : 0, scratch, Y, (hipStream_t)stream));
 }
 
-slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
-                                      const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
-                                      const void* L_or_null, const void* R_or_null, int64_t r,
-                                      void* workspace_or_null, int64_t workspace_bytes, void* dX, void* stream) {
+namespace {
+slope_status dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                       const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K, const void* L_or_null,
+                       const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes, void* dX,
+                       void* tok, int64_t tok_bytes, void* stream) {
   SLOPE_TRY(check_io(in_dt, out_dt));
-  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_dpT_bytes < 0 || workspace_bytes < 0) return SLOPE_ERR_INVALID_ARG;
+  if (T < 0 || K < 0 || N < 0 || r < 0 || packed_dpT_bytes < 0 || workspace_bytes < 0 || tok_bytes < 0)
+    return SLOPE_ERR_INVALID_ARG;
   SLOPE_TRY(ptr(dY, true));
   SLOPE_TRY(ptr(packed_dpT, true));
   SLOPE_TRY(ptr(dX, true));
+  SLOPE_TRY(ptr(tok, false));
   bool adapter = false;
   SLOPE_TRY(adapter_args(L_or_null, R_or_null, r, &adapter));
   if (in_dt == SLOPE_F32) return SLOPE_ERR_UNSUPPORTED;
   if (N % 16 || K % 4) return SLOPE_ERR_SHAPE;
   if (!in_range(T) || !in_range(K) || N > kPackedMaxCols || r > kPackedMaxRank) return SLOPE_ERR_UNSUPPORTED;
   if (packed_dpT_bytes < slope::packed_sparse_bytes(K, N)) return SLOPE_ERR_WORKSPACE;
+  if (tok && tok_bytes < slope::packed_tokens_bytes(T, N)) return SLOPE_ERR_WORKSPACE;
   if (adapter) {
     // the forward's adapter workspace with the roles of K and N exchanged
     const int64_t need = workspace_need(T, N, r, K);
     if (need > 0 && (!workspace_or_null || workspace_bytes < need)) return SLOPE_ERR_WORKSPACE;
     if (workspace_or_null && !aligned16(workspace_or_null)) return SLOPE_ERR_ALIGN;
   }
-  if (T == 0 || K == 0) return SLOPE_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (T == 0 || K == 0) return tok && T > 0 && N > 0 ? from_hip(slope::launch_pack_tokens(dY, T, N, tok, s)) : SLOPE_OK;
   slope::LowrankWs w;
   if (adapter) {
     w = slope::lowrank_layout((Dt)in_dt, workspace_or_null, T, N, r, K);
@@ -404,7 +416,44 @@ slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, con
     if (e != hipSuccess) return SLOPE_ERR_HIP;
   }
   return from_hip(slope::launch_spmm_packed((Dt)in_dt, (Dt)out_dt, dY, T, N, packed_dpT, K, adapter ? &w : nullptr,
-                                            dX, s));
+                                            dX, tok, s));
+}
+}  // namespace
+
+slope_status slope_spmm_fwd_packed(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                   const void* packed_s, int64_t packed_s_bytes, int64_t N, const void* L_or_null,
+                                   const void* R_or_null, int64_t r, void* workspace_or_null, int64_t workspace_bytes,
+                                   void* Y, void* stream) {
+  return fwd_packed(in_dt, out_dt, X, T, K, packed_s, packed_s_bytes, N, L_or_null, R_or_null, r, workspace_or_null,
+                    workspace_bytes, Y, nullptr, 0, stream);
+}
+
+slope_status slope_spmm_fwd_packed_tokens(slope_dtype in_dt, slope_dtype out_dt, const void* X, int64_t T, int64_t K,
+                                          const void* packed_s, int64_t packed_s_bytes, int64_t N,
+                                          const void* L_or_null, const void* R_or_null, int64_t r,
+                                          void* workspace_or_null, int64_t workspace_bytes, void* Y, void* X_packed,
+                                          int64_t X_packed_bytes, void* stream) {
+  SLOPE_TRY(ptr(X_packed, true));
+  return fwd_packed(in_dt, out_dt, X, T, K, packed_s, packed_s_bytes, N, L_or_null, R_or_null, r, workspace_or_null,
+                    workspace_bytes, Y, X_packed, X_packed_bytes, stream);
+}
+
+slope_status slope_spmm_bwd_dx_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T, int64_t N,
+                                      const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
+                                      const void* L_or_null, const void* R_or_null, int64_t r,
+                                      void* workspace_or_null, int64_t workspace_bytes, void* dX, void* stream) {
+  return dx_packed(in_dt, out_dt, dY, T, N, packed_dpT, packed_dpT_bytes, K, L_or_null, R_or_null, r,
+                   workspace_or_null, workspace_bytes, dX, nullptr, 0, stream);
+}
+
+slope_status slope_spmm_bwd_dx_packed_tokens(slope_dtype in_dt, slope_dtype out_dt, const void* dY, int64_t T,
+                                             int64_t N, const void* packed_dpT, int64_t packed_dpT_bytes, int64_t K,
+                                             const void* L_or_null, const void* R_or_null, int64_t r,
+                                             void* workspace_or_null, int64_t workspace_bytes, void* dX,
+                                             void* dY_packed, int64_t dY_packed_bytes, void* stream) {
+  SLOPE_TRY(ptr(dY_packed, true));
+  return dx_packed(in_dt, out_dt, dY, T, N, packed_dpT, packed_dpT_bytes, K, L_or_null, R_or_null, r,
+                   workspace_or_null, workspace_bytes, dX, dY_packed, dY_packed_bytes, stream);
 }
 
 namespace {

@@ -105,12 +105,14 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
 
 // Tile chunks of a compressed bf16 operand [M, Kred] (Kred % 16 == 0,
 // Kred <= 2^21): size in bytes and the packing pass; launch_spmm_packed is
-// launch_spmm on that form (bf16 B; ws with ws->mfma, or nullptr).
+// launch_spmm on that form (bf16 B; ws with ws->mfma, or nullptr); with tok
+// not null it also writes B's token chunks (pack_tokens' layout,
+// packed_tokens_bytes(T, Kred) bytes) from the operand stages it loads.
 int64_t packed_sparse_bytes(int64_t M, int64_t Kred);
 hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t M, int64_t Kred, void* packed,
                               hipStream_t s);
 hipError_t launch_spmm_packed(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
-                              const LowrankWs* ws, void* Y, hipStream_t s);
+                              const LowrankWs* ws, void* Y, void* tok, hipStream_t s);
 
 // Forward for T <= 64 tokens on tile-chunk weights (bf16): split-k partial
 // sums reduced in order, plus the adapter term when r > 0 (L [K, r],

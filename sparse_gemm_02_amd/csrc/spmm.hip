@@ -140,18 +140,75 @@ __device__ __forceinline__ void adapter_mma_lds(f32x16 (&acc)[G::FM][G::FT], cha
   }
 }
 
-template <class G, bool ADAPTER, typename O, bool PK, bool H>
+// Token chunks of the dense operand (the layout pack_tokens_kernel writes:
+// chunk (c, g) holds columns 256c .. 256c+255 as rows x tokens 32g .. 32g+31,
+// 64-byte rows of four 16-byte granules of 8 tokens, granule j stored at
+// j ^ ((row >> 2) & 3)), written from a stage's B slice in LDS: the stage's 64
+// k are rows 64 (s % 4) .. of chunk column s / 4.  Wave w takes the tile's
+// token group w, lane l the chunk row of k = l.  The gfx950 transposing LDS
+// load does the transpose: in each group of 16 lanes, lane j names four
+// consecutive k of token row t + j/4, and lane i receives k = c + i of tokens
+// t .. t+3 (measured; see the weight-gradient kernels), so two loads give a
+// lane the 8 tokens of one granule of its row.  The writer of the last stage
+// also writes the rows of the last chunk column that no stage covers as zeros.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <class G>
+__device__ __forceinline__ void store_token_chunks(const char* __restrict__ bslot, uint16_t* __restrict__ chunks,
+                                                   int s, int stages, int64_t t0, int64_t Tch, int lane_in,
+                                                   int wave_in) {
+  // Everything below is computed here, in the rare branch that calls this,
+  // rather than hoisted into the main loop's registers: the lane index passes
+  // through an empty asm statement the compiler cannot see through.
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(wave_in);
+  if (wave >= G::BT / 32) return;
+  const int64_t gt = t0 / 32 + wave;
+  if (gt >= Tch) return;
+  const int r = 64 * (s & 3) + lane;
+  uint16_t* row = chunks + ((int64_t)(s >> 2) * Tch + gt) * 8192 + r * 32;
+  // the address this lane supplies: token 32w + 8j + 4h + rl, k 16 (l/16) + 4 (l%4);
+  // B row t keeps granule c at c ^ ((t ^ (t >> 3)) & 7) = c ^ (4h + rl) ^ ((4w + j) & 7)
+  const int rl = (lane & 15) >> 2;
+  const int gsel = (2 * (lane >> 4) + ((lane >> 1) & 1)) ^ rl;
+  const char* base = bslot + (32 * wave + rl) * 128 + 8 * (lane & 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = (4 * wave + j) & 7;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * j * 128 + ((gsel ^ q) << 4)));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(base + (8 * j + 4) * 128 + ((gsel ^ q ^ 4) << 4)));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    *reinterpret_cast<u32x4*>(row + 8 * (j ^ ((r >> 2) & 3))) = u32x4{ua[0], ua[1], ub[0], ub[1]};
+  }
+  if (s == stages - 1) {
+    for (int rz = 64 * ((s & 3) + 1) + lane; rz < 256; rz += 64) {
+      uint16_t* zr = row + (rz - r) * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(zr + 8 * j) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <class G, bool ADAPTER, typename O, bool PK, bool H, bool TOK>
 __device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals,
                                           const uint32_t* __restrict__ meta, int M, int T, int Kred,
                                           const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
                                           const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, int bid,
-                                          int nblocks, int tm0, int tiles_m) {
+                                          int nblocks, int tm0, int tiles_m, uint16_t* __restrict__ tok,
+                                          int64_t Tch, int pack_rows) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % G::WGM, wt = wave / G::WGM;
   const int tiles_t = (T + G::BT - 1) / G::BT;
   int tm, tt;
   tile_of_block(bid, nblocks, tiles_m, tiles_t, 8, tm, tt);
+  // token chunks: row tiles 0 .. pack_rows - 1 of this geometry share the
+  // stages of each token tile, stage s going to row tile (s + tt) % pack_rows
+  // (TOK: a separate instantiation, so that the plain product keeps its registers)
+  int next_store = 0x7fffffff;
+  if (TOK && tm < pack_rows) next_store = ((tm - tt) % pack_rows + pack_rows) % pack_rows;
   tm += tm0;
   static_assert(PK || G::NST == 3, "metadata ring holds four stages");
   constexpr int SLOT = PK ? G::PSTAGE_BYTES : G::STAGE_BYTES;
@@ -289,6 +346,12 @@ __device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const
     mma(f0);
     // keep the first k-step's MFMAs ahead of the waits: they run meanwhile
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TOK) {
+      if (s == next_store) {                          // block-uniform; before the slot is refilled
+        store_token_chunks<G>(lds + (s % G::NST) * SLOT + G::A_BYTES, tok, s, stages, t0, Tch, lane, wave);
+        next_store += pack_rows;
+      }
+    }
     wait_lgkmcnt0();                                  // this wave's reads of stage s are in registers
     wait_vmcnt<G::DMA_PER_STAGE * (G::NST - 2)>();   // this wave's loads of stage s+1 landed
     barrier();                                        // everyone's have; stage s fully read
@@ -309,32 +372,35 @@ __device__ __forceinline__ void spmm_tile(const uint16_t* __restrict__ Bm, const
 }
 
 // Every row tile in tiles of geometry G.
-template <class G, bool ADAPTER, typename O, bool PK, bool H = false>
+template <class G, bool ADAPTER, typename O, bool PK, bool H = false, bool TOK = false>
 __global__ __launch_bounds__(G::THREADS, 1) void spmm_smfmac_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
     int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
-    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y) {
-  spmm_tile<G, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, gridDim.x, 0,
-                                  (M + G::BM - 1) / G::BM);
+    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, uint16_t* __restrict__ tok, int64_t Tch) {
+  const int tiles_m = (M + G::BM - 1) / G::BM;
+  spmm_tile<G, ADAPTER, O, PK, H, TOK>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, gridDim.x, 0,
+                                  tiles_m, tok, Tch, tiles_m);
 }
 
 // Row tiles 0 .. rows_full - 1 in tiles of geometry GF (the first blocks),
 // the rest in the narrower tiles of GN (the last blocks, which the dispatcher
 // hands to compute units as they come free).
-template <class GF, class GN, bool ADAPTER, typename O, bool PK, bool H = false>
+template <class GF, class GN, bool ADAPTER, typename O, bool PK, bool H = false, bool TOK = false>
 __global__ __launch_bounds__(GF::THREADS, 1) void spmm_split_kernel(
     const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ vals, const uint32_t* __restrict__ meta, int M,
     int T, int Kred, const uint16_t* __restrict__ rt, const uint16_t* __restrict__ xlh,
-    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, int rows_full) {
+    const uint16_t* __restrict__ xll, int rpad, O* __restrict__ Y, int rows_full, uint16_t* __restrict__ tok,
+    int64_t Tch) {
   static_assert(GF::THREADS == GN::THREADS && GF::BM == GN::BM, "same block and row tiles");
   const int tiles_m = (M + GF::BM - 1) / GF::BM;
   const int nfull = rows_full * ((T + GF::BT - 1) / GF::BT);
   if ((int)blockIdx.x < nfull)
-    spmm_tile<GF, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, nfull, 0,
-                                     rows_full);
-  else
-    spmm_tile<GN, ADAPTER, O, PK, H>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x - nfull,
-                                     gridDim.x - nfull, rows_full, tiles_m - rows_full);
+    spmm_tile<GF, ADAPTER, O, PK, H, TOK>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x, nfull, 0,
+                                     rows_full, tok, Tch, rows_full);
+  else   // the narrow tiles store token chunks only when no row runs full width
+    spmm_tile<GN, ADAPTER, O, PK, H, TOK>(Bm, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y, blockIdx.x - nfull,
+                                     gridDim.x - nfull, rows_full, tiles_m - rows_full, tok, Tch,
+                                     rows_full > 0 ? 0 : tiles_m);
 }
 
 typedef Geo<256, 256, 3, 2, 4> GeoBig;
@@ -381,10 +447,11 @@ __global__ __launch_bounds__(256) void pack_sparse_kernel(const uint16_t* __rest
 
 // Whole product: full-width tiles, or full-width rows plus half-width rows
 // in one launch when the full-width grid would end in a partly filled round.
-template <bool ADAPTER, typename O, bool PK, bool H>
+template <bool ADAPTER, typename O, bool PK, bool H, bool TOK>
 hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, const uint32_t* meta, int M,
-                      const LowrankWs* w, O* Y, hipStream_t s) {
+                      const LowrankWs* w, O* Y, uint16_t* tok, hipStream_t s) {
   const int64_t tiles_m = cdiv(M, GeoBig::BM), cols = cdiv(T, GeoBig::BT), cols_half = cdiv(T, GeoHalf::BT);
+  const int64_t Tch = cdiv(T, 32);
   const int64_t rows = full_width_rows(tiles_m, cols, cols_half, device_compute_units());
   constexpr int lds_bytes = PK ? GeoBig::PLDS_BYTES : GeoBig::LDS_BYTES;
   static_assert((PK ? GeoHalf::PLDS_BYTES : GeoHalf::LDS_BYTES) <= lds_bytes, "the narrow tile fits the wide one's LDS");
@@ -393,42 +460,48 @@ hipError_t launch_big(const uint16_t* B, int T, int Kred, const uint16_t* vals, 
   const uint16_t* xll = w ? w->xll : nullptr;
   const int rpad = w ? (int)w->rpad : 0;
   if (rows == tiles_m) {
-    auto kern = spmm_smfmac_kernel<GeoBig, ADAPTER, O, PK, H>;
+    auto kern = spmm_smfmac_kernel<GeoBig, ADAPTER, O, PK, H, TOK>;
     // once per process (thread-safe static initialisation)
     static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (attr != hipSuccess) return attr;
     if (tiles_m * cols == 0) return hipSuccess;
     kern<<<(unsigned)(tiles_m * cols), GeoBig::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, rt, xlh, xll,
-                                                                        rpad, Y);
+                                                                        rpad, Y, tok, Tch);
   } else {
-    auto kern = spmm_split_kernel<GeoBig, GeoHalf, ADAPTER, O, PK, H>;
+    auto kern = spmm_split_kernel<GeoBig, GeoHalf, ADAPTER, O, PK, H, TOK>;
     static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (attr != hipSuccess) return attr;
     const int64_t nb = rows * cols + (tiles_m - rows) * cols_half;
     kern<<<(unsigned)nb, GeoBig::THREADS, lds_bytes, s>>>(B, vals, meta, M, T, Kred, rt, xlh, xll, rpad, Y,
-                                                          (int)rows);
+                                                          (int)rows, tok, Tch);
   }
   return hipGetLastError();
 }
 
 template <bool PK, bool H, typename O>
 hipError_t dispatch_ad(const uint16_t* B, int64_t T, int64_t Kred, const uint16_t* vals, const uint32_t* meta,
-                       int64_t M, const LowrankWs* ws, O* Y, hipStream_t s) {
-  return ws ? launch_big<true, O, PK, H>(B, (int)T, (int)Kred, vals, meta, (int)M, ws, Y, s)
-            : launch_big<false, O, PK, H>(B, (int)T, (int)Kred, vals, meta, (int)M, nullptr, Y, s);
+                       int64_t M, const LowrankWs* ws, O* Y, uint16_t* tok, hipStream_t s) {
+  if constexpr (PK) {   // token chunks: packed operands only
+    if (tok)
+      return ws ? launch_big<true, O, PK, H, true>(B, (int)T, (int)Kred, vals, meta, (int)M, ws, Y, tok, s)
+                : launch_big<false, O, PK, H, true>(B, (int)T, (int)Kred, vals, meta, (int)M, nullptr, Y, tok, s);
+  }
+  return ws ? launch_big<true, O, PK, H, false>(B, (int)T, (int)Kred, vals, meta, (int)M, ws, Y, nullptr, s)
+            : launch_big<false, O, PK, H, false>(B, (int)T, (int)Kred, vals, meta, (int)M, nullptr, Y, nullptr, s);
 }
 
 // in: BF16 or F16 (raw 16-bit operands); out: the input format or F32
 template <bool PK>
 hipError_t dispatch_big(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* values,
-                        const uint32_t* meta, int64_t M, const LowrankWs* ws, void* Y, hipStream_t s) {
+                        const uint32_t* meta, int64_t M, const LowrankWs* ws, void* Y, uint16_t* tok,
+                        hipStream_t s) {
   const uint16_t* Bb = (const uint16_t*)B;
   const uint16_t* vb = (const uint16_t*)values;
   if (in == Dt::F16)
-    return out == Dt::F16 ? dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (_Float16*)Y, s)
-                          : dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, s);
-  return out == Dt::BF16 ? dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (uint16_t*)Y, s)
-                         : dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, s);
+    return out == Dt::F16 ? dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (_Float16*)Y, tok, s)
+                          : dispatch_ad<PK, true>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, tok, s);
+  return out == Dt::BF16 ? dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (uint16_t*)Y, tok, s)
+                         : dispatch_ad<PK, false>(Bb, T, Kred, vb, meta, M, ws, (float*)Y, tok, s);
 }
 
 }  // namespace
@@ -442,7 +515,7 @@ hipError_t launch_spmm(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, co
   if (!fast || (ad && !ws->mfma))
     return launch_spmm_generic(in, out, B, T, Kred, values, meta, M, ad ? ws->part : nullptr, ad ? ws->splits : 1,
                                ad ? r : 0, R, Y, s);
-  return dispatch_big<false>(in, out, B, T, Kred, values, meta, M, ad ? ws : nullptr, Y, s);
+  return dispatch_big<false>(in, out, B, T, Kred, values, meta, M, ad ? ws : nullptr, Y, nullptr, s);
 }
 
 int64_t packed_sparse_bytes(int64_t M, int64_t Kred) {
@@ -459,8 +532,8 @@ hipError_t launch_pack_sparse(const void* values, const uint32_t* meta, int64_t 
 }
 
 hipError_t launch_spmm_packed(Dt in, Dt out, const void* B, int64_t T, int64_t Kred, const void* packed, int64_t M,
-                              const LowrankWs* ws, void* Y, hipStream_t s) {
-  return dispatch_big<true>(in, out, B, T, Kred, packed, nullptr, M, ws, Y, s);
+                              const LowrankWs* ws, void* Y, void* tok, hipStream_t s) {
+  return dispatch_big<true>(in, out, B, T, Kred, packed, nullptr, M, ws, Y, (uint16_t*)tok, s);
 }
 
 }  // namespace slope

@@ -31,8 +31,8 @@ import torch
 from . import (slope_adamw, slope_adamw_double_prune_packed, slope_double_prune_packed, slope_lowrank_grads_packed,
                slope_lowrank_grads_workspace_bytes, slope_lowrank_workspace_bytes, slope_masked_wgrad_packed,
                slope_pack_sparse, slope_pack_tokens, slope_packed_sparse_bytes, slope_packed_tokens_bytes,
-               slope_prune_compress24, slope_spmm_bwd_dx_packed, slope_spmm_fwd_packed,
-               slope_wgrad_split_workspace_bytes)
+               slope_prune_compress24, slope_spmm_bwd_dx_packed, slope_spmm_bwd_dx_packed_tokens,
+               slope_spmm_fwd_packed, slope_wgrad_split_workspace_bytes)
 
 __all__ = ["SparseLinear", "SparseAdamW", "training_state_bytes"]
 
@@ -71,18 +71,25 @@ class _SparseLinearFn(torch.autograd.Function):
         need_a = r > 0 and (ctx.needs_input_grad[2] or ctx.needs_input_grad[3])
         dX = dW = dL = dR = None
         ws_bwd = None
+        # the weight gradients read X and dY as token chunks: the dX product
+        # writes dY's while it streams dY; X's come from the packing pass (a
+        # forward that wrote them would hold a second copy of X until here)
+        dYp = _bytes(slope_packed_tokens_bytes(T, N), dY.device) if need_w or need_a else None
         if need_x:
             dX = torch.empty((T, K), dtype=dY.dtype, device=dY.device)
             if r > 0:
                 ws_bwd = _bytes(slope_lowrank_workspace_bytes(T, N, r, K), dY.device)
-                slope_spmm_bwd_dx_packed(dY, layer.packed_dpT, K, dX, L=L, R=R, workspace=ws_bwd)
+            if dYp is not None:
+                slope_spmm_bwd_dx_packed_tokens(dY, layer.packed_dpT, K, dX, dYp, L=L if r > 0 else None,
+                                                R=R if r > 0 else None, workspace=ws_bwd)
             else:
-                slope_spmm_bwd_dx_packed(dY, layer.packed_dpT, K, dX)
+                slope_spmm_bwd_dx_packed(dY, layer.packed_dpT, K, dX, L=L if r > 0 else None,
+                                         R=R if r > 0 else None, workspace=ws_bwd)
+        elif dYp is not None:
+            slope_pack_tokens(dY, dYp)
         if need_w or need_a:
             Xp = _bytes(slope_packed_tokens_bytes(T, K), X.device)
-            dYp = _bytes(slope_packed_tokens_bytes(T, N), X.device)
             slope_pack_tokens(X, Xp)
-            slope_pack_tokens(dY, dYp)
             if need_w:
                 dW = torch.empty_like(layer.values)
                 wsp = _bytes(slope_wgrad_split_workspace_bytes(T, N, K), X.device)

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 35
+    assert len(names) == 37
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(S.EXPORTED_SYMBOLS)
@@ -181,6 +181,15 @@ def test_buffer_byte_counts(lib):
     assert fwd(ps - 1) == -4 and fwd(-1) == -1
     dx = lambda nb: lib.slope_spmm_bwd_dx_packed(bf, bf, FAKE, T, N, FAKE, nb, K, None, None, 0, None, 0, FAKE, None)
     assert dx(pdT - 1) == -4 and dx(-1) == -1
+    # the products that also write their dense operand's token chunks
+    fwt = lambda tb, tp=FAKE: lib.slope_spmm_fwd_packed_tokens(bf, bf, FAKE, T, K, FAKE, ps, N, None, None, 0, None, 0,
+                                                               FAKE, tp, tb, None)
+    assert fwt(xp - 1) == -4 and fwt(-1) == -1 and fwt(xp, None) == -1 and fwt(xp, FAKE + 8) == -3
+    dxt = lambda tb, tp=FAKE: lib.slope_spmm_bwd_dx_packed_tokens(bf, bf, FAKE, T, N, FAKE, pdT, K, None, None, 0,
+                                                                  None, 0, FAKE, tp, tb, None)
+    assert dxt(dyp - 1) == -4 and dxt(-1) == -1 and dxt(dyp, None) == -1 and dxt(dyp, FAKE + 8) == -3
+    assert lib.slope_spmm_fwd_packed_tokens(bf, bf, FAKE, T, K, FAKE, ps - 1, N, None, None, 0, None, 0, FAKE, FAKE,
+                                            xp, None) == -4
     dec = lambda nb: lib.slope_spmm_fwd_decode(bf, bf, FAKE, 16, K, FAKE, nb, N, None, None, 0, FAKE, wd, FAKE, None)
     assert dec(ps - 1) == -4
     wg_ = lambda a, b: lib.slope_masked_wgrad_packed(bf, bf, FAKE, a, FAKE, b, T, N, K, FAKE, FAKE, None, 0, None, 0, None)

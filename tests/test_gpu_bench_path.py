@@ -3,14 +3,16 @@
 buffers reused the way bench.py reuses them:
 
     slope_prune_compress24 (W_s's tile chunks written) -> slope_double_prune_packed
-    -> slope_spmm_fwd_packed (+ adapter, workspace ws)
-    -> slope_spmm_bwd_dx_packed (+ the adapter's dX term, workspace ws_bwd)
-    -> slope_pack_tokens (X, dY) -> slope_masked_wgrad_packed
+    -> slope_spmm_fwd_packed_tokens (+ adapter, workspace ws; X's token chunks)
+    -> slope_spmm_bwd_dx_packed_tokens (+ the adapter's dX term, workspace
+       ws_bwd; dY's token chunks) -> slope_masked_wgrad_packed
     -> slope_lowrank_grads_packed (X . L and dY . R^T taken from ws and ws_bwd)
 
 and the training step's weight update, slope_adamw_double_prune_packed.
 
 Checks (the oracle computes only sampled outputs at this size):
+* the token chunks the two products write equal slope_pack_tokens' chunks
+  byte for byte;
 * the packed double prune equals slope_double_prune followed by
   slope_pack_sparse byte for byte, and sampled column groups of that canonical
   W_dp^T equal the oracle's double prune bit for bit;
@@ -93,12 +95,20 @@ def test_bench_step_opt66b(idx):
     # the benchmark's step, in its order and with its buffer reuse
     S.slope_prune_compress24(W, c.values, c.meta, packed=ps)
     S.slope_double_prune_packed(c.values, c.meta, N, K, pd)
-    S.slope_spmm_fwd_packed(X, ps, N, Y, L=L, R=R, workspace=ws)
-    S.slope_spmm_bwd_dx_packed(dY, pd, K, dX, L=L, R=R, workspace=ws_bwd)
-    S.slope_pack_tokens(X, Xp)
-    S.slope_pack_tokens(dY, dYp)
+    S.slope_spmm_fwd_packed_tokens(X, ps, N, Y, Xp, L=L, R=R, workspace=ws)
+    S.slope_spmm_bwd_dx_packed_tokens(dY, pd, K, dX, dYp, L=L, R=R, workspace=ws_bwd)
     S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, c.meta, dW)
     S.slope_lowrank_grads_packed(X, dY, Xp, dYp, L, R, ws_g, dL, dR, fwd_workspace=ws, bwd_workspace=ws_bwd)
+
+    # the token chunks against the packing pass
+    chunks_ref = _u8(max(Xp.numel(), dYp.numel()))
+    S.slope_pack_tokens(dY, chunks_ref[:dYp.numel()])
+    torch.cuda.synchronize()
+    assert torch.equal(dYp, chunks_ref[:dYp.numel()])
+    S.slope_pack_tokens(X, chunks_ref[:Xp.numel()])
+    torch.cuda.synchronize()
+    assert torch.equal(Xp, chunks_ref[:Xp.numel()])
+    del chunks_ref
 
     # the packed double prune against the canonical one, then packed
     dp = Compressed(K, N, bf)
