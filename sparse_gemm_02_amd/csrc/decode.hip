@@ -183,16 +183,19 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
 // while the other rows stream the weight.  The grid keeps the tiles' width: rows padded with idle
 // blocks to fit the X . L blocks measured up to twice as slow at T = 64.
 //
-// XS (more than four tokens): X's rows for each group of kUnroll stages go to
-// LDS once per block, 128 bytes per token and stage (granule c at
+// XS (more than four tokens): X's rows for each group of kUnrollXs stages go
+// to LDS once per block, 128 bytes per token and stage (granule c at
 // c ^ ((t ^ (t >> 3)) & 7), the sparse GEMM's B swizzle), in two buffers: the
 // next group's rows are loaded into registers while the current group
 // multiplies, and written behind one barrier per group.  The four waves then
 // read their B fragments from LDS instead of each streaming all of X from the
-// cache (at 64 tokens X's bytes per stage are 3.5x the weight's).
+// cache (at 64 tokens X's bytes per stage are 3.5x the weight's).  Groups of
+// two stages (not four) halve the LDS a block holds, so more blocks share a
+// compute unit (T = 64 layer 460 -> 441 us, the same at T = 16).
 constexpr int kXsRow = 128;                        // bytes of X per token and stage
+constexpr int kUnrollXs = 2;                       // stages per X group
 template <int FT>
-constexpr int xs_lds_bytes() { return 2 * kUnroll * FT * 32 * kXsRow; }
+constexpr int xs_lds_bytes() { return 2 * kUnrollXs * FT * 32 * kXsRow; }
 
 template <int FT, bool H, int XB = 0, bool XS = false>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ X,
@@ -252,9 +255,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
   if constexpr (XS) {
     extern __shared__ __attribute__((aligned(16))) char xs_lds[];
     typedef typename Fmt16<H>::v8 v8;
-    constexpr int TOK = FT * 32, BUF = kUnroll * TOK * kXsRow;
-    constexpr int GPT = TOK * kUnroll * 8 / 256;   // 16-byte granules of X per thread and group
-    static_assert(GPT >= 1 && (GPT == 8 || GPT == 4), "fill mapping");
+    constexpr int TOK = FT * 32, BUF = kUnrollXs * TOK * kXsRow;
+    constexpr int GPT = TOK * kUnrollXs * 8 / 256;   // 16-byte granules of X per thread and group
+    static_assert(GPT == 8 || GPT == 4 || GPT == 2, "fill mapping");
     // fill: granule q = threadIdx.x * GPT + j is row q / 8 = u * TOK + t, granule q % 8
     auto fill_load = [&](u32x4 (&xr)[GPT], int sb) {
 #pragma unroll
@@ -292,11 +295,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
     }
     __syncthreads();
     int cur = 0;
-    for (int sb = s0; sb < s1; sb += kUnroll) {
-      v8 a[kUnroll][2][2];
-      int ix[kUnroll][2][2];
+    for (int sb = s0; sb < s1; sb += kUnrollXs) {
+      v8 a[kUnrollXs][2][2];
+      int ix[kUnrollXs][2][2];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollXs; ++u) {
         const int s = sb + u;
         const bool live = s < s1;
         const uint32_t c = (uint32_t)(s - s0) * Chunk::CHUNK_BYTES;
@@ -310,12 +313,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
           }
         }
       }
-      const bool more = sb + kUnroll < s1;         // block-uniform
+      const bool more = sb + kUnrollXs < s1;         // block-uniform
       u32x4 xr[GPT];
-      if (more) fill_load(xr, sb + kUnroll);
+      if (more) fill_load(xr, sb + kUnrollXs);
       const char* buf = xs_lds + cur * BUF;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnrollXs; ++u)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
