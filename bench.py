@@ -78,7 +78,7 @@ def parse():
                     help="skip the context legs (other configs, dense GEMMs, decode, update, N:M prune)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--profile-op", choices=OPS + ("prune24", "compress24", "pack_sparse", "pack_tokens",
-                                              "adamw_double_prune", "prune_nm", "copy"),
+                                              "adamw_double_prune", "prune_nm", "decode", "copy"),
                     default=None,
                     help="profiling mode: run only this op (after its inputs are prepared) --repeat times")
     ap.add_argument("--linear", default=None, help="profiling mode: only this linear of the layer (e.g. fc1)")
@@ -307,6 +307,9 @@ def profile_mode(args, wl, T):
             li.opt_v = torch.zeros(li.vs.numel(), device="cuda")
     torch.cuda.synchronize()
     op = args.profile_op
+    if op == "decode":   # the few-token forward at the workload's inference token counts
+        print(f"[profile] decode {decode_pass(lins, wl, S, torch, reps=args.repeat)}", flush=True)
+        return
     for _ in range(args.repeat):
         for li in lins:
             if op == "prune_compress24":
