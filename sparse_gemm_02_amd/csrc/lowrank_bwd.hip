@@ -8,7 +8,8 @@
 // with A the large operand (dY or X) in token-chunk form (pack_tokens: one
 // 64-byte row of 32 tokens per column c) and B the small one (X . L or
 // dY . R^T) as a transposed 16-bit hi/lo pair [rpad32][Tpad] (the operands'
-// format: bf16, or fp16 with H).  Each block takes
+// format: bf16, or fp16 with H; rows from the rank up are zero, and the kernel
+// reads the rank rounded up to 16 of them).  Each block takes
 // one 256-column chunk column over a range of token chunks (B's slice staged
 // in LDS once per chunk for the block's four waves); the fp32 partial
 // sums are added in range order by a second kernel, which also writes the
@@ -23,18 +24,22 @@ namespace {
 
 constexpr int kChunkRows = 256, kChunkTokens = 32, kChunkBytes = kChunkRows * kChunkTokens * 2;
 
-// part[split][j][c] (c < Cpad) = sum over the split's token chunks of A[t][c] B[t][j].
-// Wave w: chunk rows 64w .. 64w+63 (two 32-row MFMA tiles) x FJ 32-wide rank
-// tiles; 32x32x16 MFMA over 16 tokens, hi and lo parts of B.  A comes straight
-// from memory; the block stages each chunk's slice of B (FJ*32 rows x 32
-// tokens, hi and lo) in LDS once, in a double buffer, with 16-byte granule g
-// of row j at g ^ ((j/4) % 4) so that fragment reads are free of conflicts.
-template <int FJ, bool H>
+// part[split][j][c] (c < Cpad, j < 16 NJ) = sum over the split's token chunks of
+// A[t][c] B[t][j].  Wave w: chunk rows 64w .. 64w+63 (four 16-row MFMA tiles) x
+// NJ 16-wide rank tiles (a rank of 72 pads to 80, not 96); one 16x16x32 MFMA
+// covers a whole 32-token chunk, for the hi and the lo part of B.  Dense
+// 16x16x32 MFMA: A lane l = row l%16, k = 8*(l/16)+e; B lane l = column l%16,
+// same k; D lane l = column l%16, rows 4*(l/16)+v.  A comes straight from
+// memory; the block stages each chunk's slice of B (16 NJ rows x 32 tokens, hi
+// and lo) in LDS once, in a double buffer, with 16-byte granule g of row j at
+// g ^ ((j/4) % 4) so that fragment reads are free of bank conflicts.
+template <int NJ, bool H>
 __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __restrict__ chunks, int64_t Tch,
                                                                int per_split, const uint16_t* __restrict__ bh,
                                                                const uint16_t* __restrict__ bl, int64_t Tpad,
                                                                int64_t Cpad, float* __restrict__ part) {
-  constexpr int BROWS = FJ * 32, SLICE = 2 * BROWS * 64;        // bytes of one chunk's B slice (hi and lo)
+  constexpr int BROWS = NJ * 16, SLICE = 2 * BROWS * 64;        // bytes of one chunk's B slice (hi and lo)
+  constexpr int PIECES = SLICE / 16, PPT = (PIECES + 255) / 256;  // 16-byte staging pieces, per thread
   __shared__ __attribute__((aligned(16))) char bs[2][SLICE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x, split = blockIdx.y;
@@ -44,95 +49,81 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
                                               s1 > s0 ? (s1 - s0) * kChunkBytes : 0);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(bh, (int64_t)BROWS * Tpad * 2);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(bl, (int64_t)BROWS * Tpad * 2);
-  uint32_t a_off[2][2];
+  // A fragments: row tile rt, chunk row 64w + 16rt + l%16, granule l/16 (8 tokens)
+  uint32_t a_off[4];
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm) {
-    const int r = wave * 64 + fm * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_off[fm][ks] = r * 64 + (((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3)) << 4);
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = wave * 64 + rt * 16 + (lane & 15);
+    a_off[rt] = r * 64 + (((lane >> 4) ^ ((r >> 2) & 3)) << 4);
   }
-  // staging: thread piece i < FJ: slice row q = piece / 4 (hi rows, then lo rows), granule g = piece % 4
-  uint32_t st_src[FJ], st_dst[FJ];
-  bool st_lo[FJ];
+  // staging: piece = slice row q (hi rows, then lo rows) x granule g; pieces past the slice load nothing
+  uint32_t st_src[PPT], st_dst[PPT];
+  bool st_lo[PPT], st_on[PPT];
 #pragma unroll
-  for (int i = 0; i < FJ; ++i) {
-    const int piece = tid + 256 * i, q = piece >> 2, g = piece & 3, j = q % BROWS;
+  for (int i = 0; i < PPT; ++i) {
+    const int piece = tid + 256 * i, q = (piece >> 2) % (2 * BROWS), g = piece & 3, j = q % BROWS;
+    st_on[i] = piece < PIECES;
     st_lo[i] = q >= BROWS;
     st_src[i] = (uint32_t)(j * Tpad + g * 8) * 2;
     st_dst[i] = q * 64 + ((g ^ ((j >> 2) & 3)) << 4);
   }
-  // fragment reads: row j = 32 fj + lane%32 (hi at row j, lo at row BROWS + j), granule 2 ks + lane/32
-  uint32_t b_off[2][FJ];
+  // B fragments: rank tile jb, row j = 16jb + l%16, granule l/16
+  uint32_t b_off[NJ];
 #pragma unroll
-  for (int fj = 0; fj < FJ; ++fj) {
-    const int j = fj * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) b_off[ks][fj] = j * 64 + (((2 * ks + (lane >> 5)) ^ ((j >> 2) & 3)) << 4);
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int j = jb * 16 + (lane & 15);
+    b_off[jb] = j * 64 + (((lane >> 4) ^ ((j >> 2) & 3)) << 4);
   }
 
-  f32x16 acc[2][FJ];
+  f32x4 acc[4][NJ];
 #pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int fj = 0; fj < FJ; ++fj) acc[fm][fj] = f32x16{};
+    for (int jb = 0; jb < NJ; ++jb) acc[rt][jb] = f32x4{};
 
   // chunk s's loads are issued while chunk s-1 is multiplied: the A
   // fragments and B's slice go to registers one chunk ahead (the buffer
   // resources return 0 past the split's chunks and past Tpad)
   typedef typename Fmt16<H>::v8 v8;
-  v8 an[2][2];
-  u32x4 bn[FJ];
+  v8 an[4];
+  u32x4 bn[PPT];
   auto load_chunk = [&](int64_t s) {
     const uint32_t c = (uint32_t)(s - s0) * kChunkBytes;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm) an[ks][fm] = __builtin_bit_cast(v8, load16(ra, c + a_off[fm][ks]));
+    for (int rt = 0; rt < 4; ++rt) an[rt] = __builtin_bit_cast(v8, load16(ra, c + a_off[rt]));
     const uint32_t tb = (uint32_t)(s * kChunkTokens) * 2;
 #pragma unroll
-    for (int i = 0; i < FJ; ++i) bn[i] = load16(st_lo[i] ? rl : rh, st_src[i] + tb);
+    for (int i = 0; i < PPT; ++i) bn[i] = load16(st_lo[i] ? rl : rh, st_on[i] ? st_src[i] + tb : kOutOfRange);
   };
   if (s0 < s1) load_chunk(s0);
   for (int64_t s = s0; s < s1; ++s) {
-    v8 a[2][2];
+    v8 a[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm) a[ks][fm] = an[ks][fm];
+    for (int rt = 0; rt < 4; ++rt) a[rt] = an[rt];
     char* buf = bs[s & 1];
 #pragma unroll
-    for (int i = 0; i < FJ; ++i) *reinterpret_cast<u32x4*>(buf + st_dst[i]) = bn[i];
+    for (int i = 0; i < PPT; ++i)
+      if (st_on[i]) *reinterpret_cast<u32x4*>(buf + st_dst[i]) = bn[i];
     load_chunk(s + 1);                                 // past s1 these read 0 and are not used
     __syncthreads();                                   // slice s staged; slice s-2's buffer no longer read
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8 h[FJ], l[FJ];
+    for (int jb = 0; jb < NJ; ++jb) {
+      const v8 h = *reinterpret_cast<const v8*>(buf + b_off[jb]);
+      const v8 l = *reinterpret_cast<const v8*>(buf + BROWS * 64 + b_off[jb]);
 #pragma unroll
-      for (int fj = 0; fj < FJ; ++fj) {
-        h[fj] = *reinterpret_cast<const v8*>(buf + b_off[ks][fj]);
-        l[fj] = *reinterpret_cast<const v8*>(buf + BROWS * 64 + b_off[ks][fj]);
+      for (int rt = 0; rt < 4; ++rt) {
+        acc[rt][jb] = Fmt16<H>::mfma16x16x32(a[rt], h, acc[rt][jb]);
+        acc[rt][jb] = Fmt16<H>::mfma16x16x32(a[rt], l, acc[rt][jb]);
       }
-#pragma unroll
-      for (int fj = 0; fj < FJ; ++fj)
-#pragma unroll
-        for (int fm = 0; fm < 2; ++fm) {
-          acc[fm][fj] = Fmt16<H>::mfma32x32x16(a[ks][fm], h[fj], acc[fm][fj]);
-          acc[fm][fj] = Fmt16<H>::mfma32x32x16(a[ks][fm], l[fj], acc[fm][fj]);
-        }
     }
   }
-  // D: lane holds rank column fj*32 + lane%32, chunk rows 8*(v/4) + 4*(lane/32) + v%4
+  // D: lane holds rank column 16jb + lane%16, chunk rows 16rt + 4(lane/16) + v
 #pragma unroll
-  for (int fj = 0; fj < FJ; ++fj) {
-    const int j = fj * 32 + (lane & 31);
-    float* dst = part + ((int64_t)split * FJ * 32 + j) * Cpad + (int64_t)tile * 256 + wave * 64;
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int j = jb * 16 + (lane & 15);
+    float* dst = part + ((int64_t)split * BROWS + j) * Cpad + (int64_t)tile * 256 + wave * 64 + 4 * (lane >> 4);
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {acc[fm][fj][4 * q], acc[fm][fj][4 * q + 1], acc[fm][fj][4 * q + 2], acc[fm][fj][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(dst + fm * 32 + 8 * q + 4 * (lane >> 5)) = v;
-      }
+    for (int rt = 0; rt < 4; ++rt) *reinterpret_cast<f32x4*>(dst + rt * 16) = acc[rt][jb];
   }
 }
 
@@ -140,14 +131,14 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
 // as out[j][c] (TRANS false: dR [r, N]) or out[c][j] (TRANS true: dL [K, r]).
 template <typename O, bool TRANS>
 __global__ __launch_bounds__(256) void lr_wgrad_reduce_kernel(const float* __restrict__ part, int splits, int r,
-                                                              int rows32, int64_t C, int64_t Cpad, int accumulate,
+                                                              int rows, int64_t C, int64_t Cpad, int accumulate,
                                                               O* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)r * C) return;
   const int64_t j = i / C, c = i % C;
   float v = 0.f;
 #pragma unroll 4
-  for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * rows32 + j) * Cpad + c];
+  for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * rows + j) * Cpad + c];
   O* p = TRANS ? out + c * r + j : out + j * C + c;
   if (accumulate) v += load_out(p);
   store_out(p, v);
@@ -164,14 +155,14 @@ int64_t split_count(int64_t tiles, int64_t Tch, int64_t brows) {
   return want < 1 ? 1 : want;
 }
 
-template <int FJ>
+template <int NJ>
 void launch_partial(bool h16, const char* chunks, int64_t tiles, int64_t Tch, int per, int64_t splits,
                     const uint16_t* bh, const uint16_t* bl, int64_t Tpad, int64_t Cpad, float* part, hipStream_t s) {
   const dim3 grid((unsigned)tiles, (unsigned)splits);
   if (h16)
-    lr_wgrad_partial_kernel<FJ, true><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+    lr_wgrad_partial_kernel<NJ, true><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
   else
-    lr_wgrad_partial_kernel<FJ, false><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+    lr_wgrad_partial_kernel<NJ, false><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
 }
 
 template <typename O>
@@ -186,10 +177,13 @@ void launch_reduce(const float* part, int sp, int r, int rows, int64_t C, int64_
 
 }  // namespace
 
+// rows of B and of the partial sums: the rank rounded up to 16
+int64_t lr_rows(int64_t r) { return cdiv(r, 16) * 16; }
+
 int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r) {
   const int64_t tiles = cdiv(C, kChunkRows), Tch = cdiv(T, kChunkTokens);
-  const int64_t per = cdiv(Tch, split_count(tiles, Tch, cdiv(r, 32) * 32)), splits = Tch ? cdiv(Tch, per) : 1;
-  return cdiv(splits * cdiv(r, 32) * 32 * tiles * kChunkRows * 4, 256) * 256;
+  const int64_t per = cdiv(Tch, split_count(tiles, Tch, lr_rows(r))), splits = Tch ? cdiv(Tch, per) : 1;
+  return cdiv(splits * lr_rows(r) * tiles * kChunkRows * 4, 256) * 256;
 }
 
 hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
@@ -197,30 +191,34 @@ hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t
                            hipStream_t s) {
   if (C == 0 || r == 0) return hipSuccess;
   const int64_t tiles = cdiv(C, kChunkRows), Tch = cdiv(T, kChunkTokens), Cpad = tiles * kChunkRows;
-  const int64_t per = Tch ? cdiv(Tch, split_count(tiles, Tch, cdiv(r, 32) * 32)) : 1, splits = Tch ? cdiv(Tch, per) : 1;
-  const int fj = (int)cdiv(r, 32);
+  const int64_t rows = lr_rows(r);
+  const int64_t per = Tch ? cdiv(Tch, split_count(tiles, Tch, rows)) : 1, splits = Tch ? cdiv(Tch, per) : 1;
   const char* ch = (const char*)chunks;
   const bool h16 = in == Dt::F16;
   if (Tch == 0) {
     // no tokens: the sums are empty (one split of zeros, cleared by a kernel)
-    hipError_t e = launch_fill_zero(Dt::F32, part, (int64_t)fj * 32 * Cpad, s);
+    hipError_t e = launch_fill_zero(Dt::F32, part, rows * Cpad, s);
     if (e != hipSuccess) return e;
-  } else if (fj == 1) {
-    launch_partial<1>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
-  } else if (fj == 2) {
-    launch_partial<2>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
-  } else if (fj == 3) {
-    launch_partial<3>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
   } else {
-    launch_partial<4>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s);
+    switch (rows / 16) {
+      case 1: launch_partial<1>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 2: launch_partial<2>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 3: launch_partial<3>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 4: launch_partial<4>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 5: launch_partial<5>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 6: launch_partial<6>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 7: launch_partial<7>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      case 8: launch_partial<8>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
+      default: return hipErrorInvalidValue;     // rank above 128: refused by the caller
+    }
   }
   const int sp = Tch ? (int)splits : 1;
   if (out == Dt::BF16)
-    launch_reduce<uint16_t>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<uint16_t>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
   else if (out == Dt::F16)
-    launch_reduce<_Float16>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<_Float16>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
   else
-    launch_reduce<float>(part, sp, (int)r, fj * 32, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<float>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
   return hipGetLastError();
 }
 
