@@ -212,17 +212,22 @@ __global__ __launch_bounds__(kThreads) void prune_nm_kernel(const uint32_t* __re
 }
 
 // ------------------------------------------------------------------ prune24 + compress24 in one pass
-// Lane f of the grid -> (row, pair p) over rows_pad x pairs_pad: groups 2p and
-// 2p+1 of the row (columns 8p .. 8p+7), read as one 8- or 16-byte load, so a
-// wave reads one contiguous run of the row and writes its 4 kept values, 8
-// mask bytes (if asked for) contiguously; the four lanes of a metadata word
-// (groups 8w .. 8w+7) OR their nibbles together with shuffles and the first
-// writes it.  With PK (16-bit, cols % 16 == 0) the 8 bytes of values also go
-// to W_s's tile chunk (lanes 2c, 2c+1 of a chunk row fill granule c) and the
-// word to the chunk's metadata; rows_pad and pairs_pad cover whole chunks and
-// lanes past the matrix write the chunks' zero padding.  The selection is
-// prune24's, and with a mask of exactly two per group compress24 keeps those
-// two: results equal the two passes (and pack_sparse), bit for bit.
+// Each lane takes one (row, pair p) of rows_pad x pairs_pad: groups 2p and
+// 2p+1 of the row (columns 8p .. 8p+7), read as one 8- or 16-byte load, and
+// writes its 4 kept values and 8 mask bytes (if asked for); the four lanes of
+// a metadata word (groups 8w .. 8w+7) OR their nibbles together with shuffles
+// and the first writes it.  Without PK the lanes of a wave take 64
+// consecutive pairs of one row (one contiguous run in and out).  With PK
+// (16-bit, cols % 16 == 0) the 8 bytes of values also go to W_s's tile chunk
+// (lanes 2c, 2c+1 of a chunk row fill granule c) and the word to the chunk's
+// metadata; rows_pad and pairs_pad cover whole chunks and lanes past the
+// matrix write the chunks' zero padding.  There a block takes 16 rows x 16
+// pairs (128 columns: two chunk columns), so that its chunk writes are whole
+// 128-byte lines (16 rows x 64 bytes of values, 16 rows x 8 bytes of metadata
+// per chunk) and so are its value rows (64 values of each row), instead of one
+// 64-byte row piece of eight chunks per wave.  The selection is prune24's,
+// and with a mask of exactly two per group compress24 keeps those two:
+// results equal the two passes (and pack_sparse), bit for bit.
 template <typename E, bool PK>
 __global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __restrict__ W, int64_t rows,
                                                                    int64_t cols, int64_t rows_pad,
@@ -231,20 +236,29 @@ __global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __r
                                                                    char* __restrict__ packed) {
   typedef typename Vec4<E>::T V;
   const int64_t gpr = cols / 4, wpr = cdiv(gpr, 8);
-  const int64_t total = rows_pad * pairs_pad;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int lane = threadIdx.x & 63;
-  // the lane's (row, pair) advances by a fixed step each iteration (one
-  // division before the loop instead of a 64-bit division per iteration);
-  // past the end the row is at least rows_pad, so nothing is stored
-  const int64_t base0 = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63);
-  const int drow = (int)(stride / pairs_pad), dpair = (int)(stride - (int64_t)drow * pairs_pad);
+  // PK: tasks of 16 rows x 16 pairs, one per block and iteration (pairs_pad is
+  // a multiple of 8: a last task may reach a chunk column past the matrix,
+  // whose lanes store nothing); else the lane's (row, pair) advances by a
+  // fixed step each iteration (one division before the loop instead of a
+  // 64-bit division per iteration); past the end the row is at least
+  // rows_pad, so nothing is stored
+  const int64_t total = PK ? (rows_pad / 16) * cdiv(pairs_pad, 16) : rows_pad * pairs_pad;
+  const int64_t stride = PK ? (int64_t)gridDim.x : (int64_t)gridDim.x * kThreads;
+  const int64_t base0 = PK ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63);
+  const int cbs = (int)cdiv(pairs_pad, 16);
+  const int drow = PK ? 0 : (int)(stride / pairs_pad), dpair = PK ? 0 : (int)(stride - (int64_t)drow * pairs_pad);
   const int npairs = (int)pairs_pad;
-  int row = (int)((base0 + lane) / pairs_pad), p = (int)(base0 + lane - (int64_t)row * pairs_pad);
+  int row = PK ? 0 : (int)((base0 + lane) / pairs_pad), p = PK ? 0 : (int)(base0 + lane - (int64_t)row * pairs_pad);
   // wave-uniform loop bound: every lane of a wave takes part in the shuffles
   for (int64_t base = base0; base < total; base += stride,
                row += drow + (p + dpair >= npairs ? 1 : 0), p += dpair - (p + dpair >= npairs ? npairs : 0)) {
-    const int64_t f = base + lane;
+    if constexpr (PK) {
+      const int task = (int)base, rb = task / cbs, cb = task - rb * cbs;
+      row = rb * 16 + (int)(threadIdx.x >> 4);
+      p = cb * 16 + (int)(threadIdx.x & 15);
+    }
+    const bool slot = PK ? p < npairs : base + lane < total;   // inside rows_pad x pairs_pad
     const int64_t g0 = 2 * (int64_t)p;             // first group of the pair
     const bool in_row = row < rows;
     const int ng = in_row ? (g0 + 2 <= gpr ? 2 : (g0 < gpr ? 1 : 0)) : 0;   // groups of the pair in the matrix
@@ -318,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void prune_compress24_kernel(const E* __r
     if ((p & 3) == 0 && in_row && g0 < gpr) meta[row * wpr + (p >> 2)] = word;
     if constexpr (PK) {
       static_assert(sizeof(E) == 2, "tile chunks hold 16-bit values");
-      if (f < total && 8 * p < cdiv(cols, kPackCols) * kPackCols) {
+      if (slot && 8 * p < cdiv(cols, kPackCols) * kPackCols) {
         const int r = (int)(row % kPackRows), c = (int)((p >> 1) & 3), sw = (r >> 2) & 3;
         char* const chunk = packed + pack_chunk_offset(row, 8 * p, cols);
         const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, kept[0]) |
@@ -780,7 +794,8 @@ hipError_t launch_prune_compress24(Dt dt, const void* W, int64_t rows, int64_t c
   // 256-row chunks and eight pairs per chunk column
   const int64_t rows_pad = packed ? cdiv(rows, kPackRows) * kPackRows : rows;
   const int64_t words_pad = packed ? 4 * 2 * cdiv(cols, kPackCols) : 4 * cdiv(cols / 4, 8);
-  const int grid = grid_for(rows_pad * words_pad, kThreads);
+  // with chunks, one block per task of 16 rows x 16 pairs
+  const int grid = packed ? grid_for((rows_pad / 16) * cdiv(words_pad, 16), 1) : grid_for(rows_pad * words_pad, kThreads);
   uint32_t* m4 = (uint32_t*)mask;
   char* pk = (char*)packed;
   if (dt == Dt::F32) {
