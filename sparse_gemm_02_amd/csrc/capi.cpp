@@ -542,8 +542,7 @@ slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, c
   hipError_t e = hipSuccess;
   if (!have_f) e = slope::launch_lowrank_down((Dt)in_dt, X, L, T, K, r, wf, s);                      // X . L
   if (e == hipSuccess && !have_b) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
-  if (e == hipSuccess) e = slope::launch_transpose_hilo(wf, r32, xh, xl, s);
-  if (e == hipSuccess) e = slope::launch_transpose_hilo(wb, r32, gh, gl, s);
+  if (e == hipSuccess) e = slope::launch_transpose_hilo2(wf, wb, r32, xh, xl, gh, gl, s);
   if (e == hipSuccess)
     e = slope::launch_lr_wgrad((Dt)in_dt, (Dt)out_dt, dY_packed, T, N, r, xh, xl, wf.Tpad, pr, dR, false, accumulate,
                                s);

@@ -85,8 +85,10 @@ hipError_t launch_lowrank_down(Dt in, const void* X, const void* L, int64_t T, i
 // forward's roles with (X, L, R, K, N) -> (dY, R^T, L^T, N, K).
 hipError_t launch_lowrank_prepare_bwd(const void* dY, const void* L, const void* R, int64_t T, int64_t N, int64_t r,
                                       int64_t K, const LowrankWs& w, hipStream_t s);
-// The hi/lo pair of w transposed to [rpad32][Tpad] (rows past rpad zero).
-hipError_t launch_transpose_hilo(const LowrankWs& w, int64_t rpad32, uint16_t* xht, uint16_t* xlt, hipStream_t s);
+// The hi/lo pairs of w1 and w2, each transposed to [rpad32][Tpad] (rows past
+// rpad zero), in one launch.
+hipError_t launch_transpose_hilo2(const LowrankWs& w1, const LowrankWs& w2, int64_t rpad32, uint16_t* xht1,
+                                  uint16_t* xlt1, uint16_t* xht2, uint16_t* xlt2, hipStream_t s);
 
 // Adapter weight gradients from token chunks: out = A^T . B over the tokens with
 // A the chunks of a [T, C] matrix and B given as a transposed hi/lo pair

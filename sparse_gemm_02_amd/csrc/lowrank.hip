@@ -68,9 +68,9 @@ Sizes sizes(int64_t T, int64_t K, int64_t r, int64_t N) {
 // lt[j][k] = L[k][j] for j < r, k < K; 0 in the padding.  Thread (k-group of
 // eight, j) with j fastest: the reads of a wave cover consecutive j of eight
 // rows of L, the write is one 16-byte piece of a row of lt (Kpad % 8 == 0).
-__global__ __launch_bounds__(256) void transpose_l_kernel(const uint16_t* __restrict__ L, int64_t K, int64_t r,
-                                                          int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void transpose_l_body(int64_t bid, const uint16_t* __restrict__ L, int64_t K, int64_t r,
+                                                 int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt) {
+  const int64_t i = bid * 256 + threadIdx.x;
   if (i >= rpad * (Kpad / 8)) return;
   const int64_t j = i % rpad, k0 = (i / rpad) * 8;
   uint16_t v[8];
@@ -85,9 +85,9 @@ __global__ __launch_bounds__(256) void transpose_l_kernel(const uint16_t* __rest
 // rt[n][j] = R[j][n] for j < r, n < N; 0 in the padding.  Thread (n, j-group
 // of eight) with n fastest: reads cover consecutive n of eight rows of R, the
 // write is one 16-byte piece of a row of rt (rpad % 8 == 0).
-__global__ __launch_bounds__(256) void transpose_r_kernel(const uint16_t* __restrict__ R, int64_t r, int64_t N,
-                                                          int64_t rpad, int64_t Npad, uint16_t* __restrict__ rt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void transpose_r_body(int64_t bid, const uint16_t* __restrict__ R, int64_t r, int64_t N,
+                                                 int64_t rpad, int64_t Npad, uint16_t* __restrict__ rt) {
+  const int64_t i = bid * 256 + threadIdx.x;
   if (i >= Npad * (rpad / 8)) return;
   const int64_t n = i % Npad, j0 = (i / Npad) * 8;
   uint16_t v[8];
@@ -99,26 +99,69 @@ __global__ __launch_bounds__(256) void transpose_r_kernel(const uint16_t* __rest
   *reinterpret_cast<u32x4*>(rt + n * rpad + j0) = w;
 }
 
+__global__ __launch_bounds__(256) void transpose_l_kernel(const uint16_t* __restrict__ L, int64_t K, int64_t r,
+                                                          int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt) {
+  transpose_l_body(blockIdx.x, L, K, r, rpad, Kpad, lt);
+}
+
+// Both transposes of the forward's adapter operands in one launch: blocks
+// below nl transpose L, the others R.
+__global__ __launch_bounds__(256) void transpose_lr_kernel(const uint16_t* __restrict__ L, int64_t K, int64_t r,
+                                                           int64_t rpad, int64_t Kpad, uint16_t* __restrict__ lt,
+                                                           unsigned nl, const uint16_t* __restrict__ R, int64_t N,
+                                                           int64_t Npad, uint16_t* __restrict__ rt) {
+  if (blockIdx.x < nl)
+    transpose_l_body(blockIdx.x, L, K, r, rpad, Kpad, lt);
+  else
+    transpose_r_body(blockIdx.x - nl, R, r, N, rpad, Npad, rt);
+}
+
 // dst[i][j] = src[i][j] for i < rows, j < cols (src row-major, cols wide); 0 in
 // the padding up to [rows_pad, cols_pad].  The adapter backward uses it for the
 // operands that need no transposition there: R [r, N] as the down-projection's
 // [rpad, Kpad] operand and L [K, r] as the epilogue's [Npad, rpad] operand.
-__global__ __launch_bounds__(256) void pad_copy_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
-                                                       int64_t rows_pad, int64_t cols_pad,
-                                                       uint16_t* __restrict__ dst) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void pad_copy_body(int64_t bid, const uint16_t* __restrict__ src, int64_t rows,
+                                              int64_t cols, int64_t rows_pad, int64_t cols_pad,
+                                              uint16_t* __restrict__ dst) {
+  const int64_t i = bid * 256 + threadIdx.x;
   if (i >= rows_pad * cols_pad) return;
   const int64_t a = i / cols_pad, b = i % cols_pad;
   dst[i] = (a < rows && b < cols) ? src[a * cols + b] : (uint16_t)0;
 }
 
+// Both padded copies of the dX product's adapter operands in one launch:
+// blocks below n1 copy R as [rpad, Kpad], the others L as [Npad, rpad].
+__global__ __launch_bounds__(256) void pad_copy2_kernel(const uint16_t* __restrict__ src1, int64_t rows1,
+                                                        int64_t cols1, int64_t rows_pad1, int64_t cols_pad1,
+                                                        uint16_t* __restrict__ dst1, unsigned n1,
+                                                        const uint16_t* __restrict__ src2, int64_t rows2,
+                                                        int64_t cols2, int64_t rows_pad2, int64_t cols_pad2,
+                                                        uint16_t* __restrict__ dst2) {
+  if (blockIdx.x < n1)
+    pad_copy_body(blockIdx.x, src1, rows1, cols1, rows_pad1, cols_pad1, dst1);
+  else
+    pad_copy_body(blockIdx.x - n1, src2, rows2, cols2, rows_pad2, cols_pad2, dst2);
+}
+
 // xt[j][t] = x[t][j] for the hi and lo parts (x [Tpad][rpad] -> xt [rpad32][Tpad],
 // rows j >= rpad zero).  Thread (j, t) with t fastest: coalesced writes.
-__global__ __launch_bounds__(256) void transpose_hilo_kernel(const uint16_t* __restrict__ xh,
-                                                             const uint16_t* __restrict__ xl, int64_t Tpad,
-                                                             int64_t rpad, int64_t rpad32, uint16_t* __restrict__ xht,
-                                                             uint16_t* __restrict__ xlt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Two such transposes (X . L and dY . R^T for the adapter's gradients) in one
+// launch: blocks below n1 take the first.
+__global__ __launch_bounds__(256) void transpose_hilo2_kernel(const uint16_t* __restrict__ xh1,
+                                                              const uint16_t* __restrict__ xl1, int64_t Tpad1,
+                                                              int64_t rpad1, uint16_t* __restrict__ xht1,
+                                                              uint16_t* __restrict__ xlt1, unsigned n1,
+                                                              const uint16_t* __restrict__ xh2,
+                                                              const uint16_t* __restrict__ xl2, int64_t Tpad2,
+                                                              int64_t rpad2, uint16_t* __restrict__ xht2,
+                                                              uint16_t* __restrict__ xlt2, int64_t rpad32) {
+  const bool first = blockIdx.x < n1;
+  const int64_t i = (int64_t)(first ? blockIdx.x : blockIdx.x - n1) * 256 + threadIdx.x;
+  const int64_t Tpad = first ? Tpad1 : Tpad2, rpad = first ? rpad1 : rpad2;
+  const uint16_t* xh = first ? xh1 : xh2;
+  const uint16_t* xl = first ? xl1 : xl2;
+  uint16_t* xht = first ? xht1 : xht2;
+  uint16_t* xlt = first ? xlt1 : xlt2;
   if (i >= rpad32 * Tpad) return;
   const int64_t j = i / Tpad, t = i % Tpad;
   const bool in = j < rpad;
@@ -380,8 +423,9 @@ hipError_t launch_lowrank_prepare(Dt in, const void* X, const void* L, const voi
                                   int64_t r, int64_t N, const LowrankWs& w, hipStream_t s) {
   if (!w.mfma) return launch_lowrank_down_generic(in, X, L, T, K, r, w.splits, w.kc, w.part, s);
   // 16-bit inputs: transposed L and R, the split down-projection, the hi/lo reduction
-  transpose_l_kernel<<<blocks_for(w.rpad * w.Kpad / 8), 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt);
-  transpose_r_kernel<<<blocks_for(w.Npad * w.rpad / 8), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Npad, w.rt);
+  const unsigned nl = blocks_for(w.rpad * w.Kpad / 8), nr = blocks_for(w.Npad * w.rpad / 8);
+  transpose_lr_kernel<<<nl + nr, 256, 0, s>>>((const uint16_t*)L, K, r, w.rpad, w.Kpad, w.lt, nl, (const uint16_t*)R, N,
+                                             w.Npad, w.rt);
   const hipError_t ed = launch_down((const uint16_t*)X, w.lt, T, K, r, w, s);
   if (ed != hipSuccess) return ed;
   reduce_split(w, T, r, s);
@@ -402,16 +446,20 @@ hipError_t launch_lowrank_prepare_bwd(const void* dY, const void* L, const void*
                                       int64_t K, const LowrankWs& w, hipStream_t s) {
   if (!w.mfma) return hipErrorInvalidValue;
   // down-projection operand: R as [rpad][Kpad] (its own layout, padded); epilogue operand: L as [Npad][rpad]
-  pad_copy_kernel<<<blocks_for(w.rpad * w.Kpad), 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Kpad, w.lt);
-  pad_copy_kernel<<<blocks_for(w.Npad * w.rpad), 256, 0, s>>>((const uint16_t*)L, K, r, w.Npad, w.rpad, w.rt);
+  const unsigned n1 = blocks_for(w.rpad * w.Kpad), n2 = blocks_for(w.Npad * w.rpad);
+  pad_copy2_kernel<<<n1 + n2, 256, 0, s>>>((const uint16_t*)R, r, N, w.rpad, w.Kpad, w.lt, n1, (const uint16_t*)L, K, r,
+                                          w.Npad, w.rpad, w.rt);
   const hipError_t ed = launch_down((const uint16_t*)dY, w.lt, T, N, r, w, s);
   if (ed != hipSuccess) return ed;
   reduce_split(w, T, r, s);
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_hilo(const LowrankWs& w, int64_t rpad32, uint16_t* xht, uint16_t* xlt, hipStream_t s) {
-  transpose_hilo_kernel<<<blocks_for(rpad32 * w.Tpad), 256, 0, s>>>(w.xlh, w.xll, w.Tpad, w.rpad, rpad32, xht, xlt);
+hipError_t launch_transpose_hilo2(const LowrankWs& w1, const LowrankWs& w2, int64_t rpad32, uint16_t* xht1,
+                                  uint16_t* xlt1, uint16_t* xht2, uint16_t* xlt2, hipStream_t s) {
+  const unsigned n1 = blocks_for(rpad32 * w1.Tpad), n2 = blocks_for(rpad32 * w2.Tpad);
+  transpose_hilo2_kernel<<<n1 + n2, 256, 0, s>>>(w1.xlh, w1.xll, w1.Tpad, w1.rpad, xht1, xlt1, n1, w2.xlh, w2.xll,
+                                                w2.Tpad, w2.rpad, xht2, xlt2, rpad32);
   return hipGetLastError();
 }
 
