@@ -677,7 +677,9 @@ def main():
         ops[op]["gbs"] = by / (ops[op]["ms_per_step"] * 1e-3) / 1e9
         ops[op]["frac_hbm_peak"] = ops[op]["gbs"] / PEAK_HBM_GBS
 
-    # dominant kernel: the weight-gradient GEMM (one kernel per call; the two
+    # dominant kernel: the weight-gradient GEMM (its call is the GEMM kernel plus,
+    # where the tiles end in a partly filled round of blocks, a small kernel
+    # adding that round's token ranges: a few microseconds of the call; the two
     # sparse products also launch the adapter's small kernels, so their call
     # time is not one kernel's)
     dom = "masked_wgrad"
@@ -687,6 +689,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_DENSE_TFLOPS, 4),
                 "traffic": measured_traffic(dom),
                 "flops_counted": "useful (T*N*K per launch: products with a kept weight / kept output)",
+                "kernels": "wgrad_direct_kernel (+ wgrad_tail_reduce_kernel for the last round's token ranges)",
                 "avg_launch_ms": {l.name: round(t, 4) for l, t in launches}}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -4,15 +4,10 @@
 
 namespace slope {
 
-// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
-// with a private L2.  Renumber so that the workgroups resident on one XCD at
-// the same time get consecutive logical ids, then walk the logical ids in
-// groups of `group` row tiles so that those workgroups share operand tiles.
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_r, int tiles_c, int group,
-                                              int& tr, int& tc) {
-  constexpr int kXcds = 8;
-  int logical = bid;
-  if (nblocks % kXcds == 0) logical = (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+// Logical tile id -> (row tile, column tile): groups of `group` row tiles, all
+// column tiles of a group before the next, row tiles fastest within a group,
+// so that consecutive logical ids share operand tiles.
+__device__ __forceinline__ void logical_tile(int logical, int tiles_r, int tiles_c, int group, int& tr, int& tc) {
   const int per_group = group * tiles_c;
   const int g = logical / per_group;
   const int first = g * group;
@@ -20,6 +15,17 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_r,
   const int in_group = logical - g * per_group;
   tr = first + in_group % gsize;
   tc = in_group / gsize;
+}
+
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with a private L2.  Renumber so that the workgroups resident on one XCD at
+// the same time get consecutive logical ids, then map those to tiles.
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_r, int tiles_c, int group,
+                                              int& tr, int& tc) {
+  constexpr int kXcds = 8;
+  int logical = bid;
+  if (nblocks % kXcds == 0) logical = (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+  logical_tile(logical, tiles_r, tiles_c, group, tr, tc);
 }
 
 // Host side: how many row tiles of a product to run in full tiles when the

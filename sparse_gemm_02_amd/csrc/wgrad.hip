@@ -111,10 +111,14 @@ __device__ __forceinline__ typename Fmt16<H>::v8 frag_tr(const char* tile, int t
 // loaded first, all in flight, from clamped addresses (a word past N or K is
 // never used); with accumulate so are the previous values pairs.  Loads under
 // the bounds branches would each be followed by a wait.
+//
+// dWv's rows are ldv elements apart (K/2 for the whole matrix; a tile's own
+// compact buffer passes 128 and a base shifted by its first row and group).
 template <class G, typename O>
 __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], const uint32_t* __restrict__ meta,
                                             int K, int N, int64_t k0, int64_t n0, int wk, int wn, int lane,
-                                            O* __restrict__ dWv, O* __restrict__ dWd, int accumulate) {
+                                            O* __restrict__ dWv, O* __restrict__ dWd, int accumulate,
+                                            int64_t ldv) {
   const int64_t wpr = ((int64_t)K / 4 + 7) / 8;
   uint32_t words[G::FN][G::FK];
 #pragma unroll
@@ -137,7 +141,7 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], c
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t k = k0 + wk * G::WK + a * 32 + 8 * q + 4 * (lane >> 5);
-          const O* vp = (n < N && k < K) ? dWv + n * (K / 2) + 2 * (k >> 2) : dWv;
+          const O* vp = (n < N && k < K) ? dWv + n * ldv + 2 * (k >> 2) : dWv + n0 * ldv + 2 * (k0 >> 2);
           prev[b][a][q][0] = load_out(vp);
           prev[b][a][q][1] = load_out(vp + 1);
         }
@@ -161,7 +165,7 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[G::FK][G::FN], c
         // i0 < i1: i0 in {0,1,2}, i1 in {1,2,3}; selects without indexing registers
         float v0 = i0 == 0 ? r0 : (i0 == 1 ? r1 : r2);
         float v1 = i1 == 3 ? r3 : (i1 == 2 ? r2 : r1);
-        O* vp = dWv + n * (K / 2) + 2 * g;
+        O* vp = dWv + n * ldv + 2 * g;
         if (accumulate) { v0 += prev[b][a][q][0]; v1 += prev[b][a][q][1]; }
         store_pair(vp, v0, v1);
         if (dWd) {
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_mfma_kernel(const uint16_
   }
   wait_vmcnt<0>();
 
-  wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+  wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate, K / 2);
 }
 
 // ---------------------------------------------------------------- packed path
@@ -363,31 +367,51 @@ struct DGeo {
 };
 
 //
-// Token split (SPLIT, part != NULL): the grid holds `splits` copies of the tile grid;
-// copy j sums token chunks [j * kc, min((j + 1) * kc, Tch)) only and writes its
-// kept values in fp32 to part + j * N * (K / 2) (W_s's slot order, no dense
-// copy, no accumulation); wgrad_split_reduce_kernel then adds the copies in
-// order.  Used when the tile grid alone would leave most compute units idle.
-template <class G, typename O, bool H, bool SPLIT = false>
+// Token split (MODE kSplit, part != NULL): the grid holds `splits` copies of
+// the tile grid; copy j sums token chunks [j * kc, min((j + 1) * kc, Tch)) only
+// and writes its kept values in fp32 to part + j * N * (K / 2) (W_s's slot
+// order, no dense copy, no accumulation); wgrad_split_reduce_kernel then adds
+// the copies in order.  Used when the tile grid alone would leave most compute
+// units idle.
+//
+// Tail split (MODE kTail): the first nb_main blocks (whole rounds of the
+// device) run logical tiles 0 .. nb_main-1 as the plain kernel does; the
+// remaining ntail tiles, which would run alone in a last, partly filled
+// round, are cut into token ranges of kc chunks: block nb_main + j sums range
+// j / ntail of tail tile j % ntail and writes its kept values in fp32 to that
+// tile's own 256 x 128 buffer in part (range-major); wgrad_tail_reduce_kernel
+// adds the ranges in order.
+constexpr int kPlain = 0, kSplit = 1, kTail = 2;
+constexpr int kTileValues = 256 * 128;     // kept values of one 256 x 256 output tile
+
+template <class G, typename O, bool H, int MODE = kPlain>
 __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint16_t* __restrict__ dp,
                                                                    const uint16_t* __restrict__ xp, int T, int N,
                                                                    int K, const uint32_t* __restrict__ meta,
                                                                    O* __restrict__ dWv, O* __restrict__ dWd,
-                                                                   int accumulate, float* __restrict__ part, int kc) {
+                                                                   int accumulate, float* __restrict__ part, int kc,
+                                                                   int nb_main, int ntail) {
+  static_assert(G::BK == 256 && G::BN == 256, "tail buffers hold 256 x 256 tiles");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wk = wave % G::WGK, wn = wave / G::WGK;
   const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
   const int ntiles = tiles_k * tiles_n;
-  const int split = SPLIT ? (int)blockIdx.x / ntiles : 0;
+  const bool tail = MODE == kTail && (int)blockIdx.x >= nb_main;          // block-uniform
+  const int tj = tail ? (int)blockIdx.x - nb_main : 0;
+  const int split = MODE == kSplit ? (int)blockIdx.x / ntiles : (tail ? tj / ntail : 0);
   int tk, tn;
-  tile_of_block(SPLIT ? (int)blockIdx.x % ntiles : (int)blockIdx.x, SPLIT ? ntiles : (int)gridDim.x, tiles_k,
-                tiles_n, 8, tk, tn);
+  if (tail)
+    logical_tile(nb_main + tj % ntail, tiles_k, tiles_n, 8, tk, tn);
+  else
+    tile_of_block(MODE == kSplit ? (int)blockIdx.x % ntiles : (int)blockIdx.x,
+                  MODE == kSplit ? ntiles : (MODE == kTail ? nb_main : (int)gridDim.x), tiles_k, tiles_n, 8, tk, tn);
   const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
   const int64_t Tch = (T + kChunkTokens - 1) / kChunkTokens;
   // this block's token chunks [s_first, stages)
-  const int s_first = SPLIT ? split * kc : 0;
-  const int stages = SPLIT ? (s_first + kc < (int)Tch ? s_first + kc : (int)Tch) : (int)Tch;
+  const bool ranged = MODE == kSplit || tail;
+  const int s_first = ranged ? split * kc : 0;
+  const int stages = ranged ? (s_first + kc < (int)Tch ? s_first + kc : (int)Tch) : (int)Tch;
   const uint16_t* const xs = xp + (int64_t)tk * Tch * kChunkElems;
   const uint16_t* const ds = dp + (int64_t)tn * Tch * kChunkElems;
   const uint32_t src0 = (uint32_t)(wave * G::DMA * 1024);
@@ -485,10 +509,18 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
     s0 += G::RING;
   } while (s0 < stages_pad);
   wait_vmcnt<0>();
-  if constexpr (SPLIT)
-    wgrad_store<G, float>(acc, meta, K, N, k0, n0, wk, wn, lane, part + (int64_t)split * N * (K / 2), nullptr, 0);
-  else
-    wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate);
+  if constexpr (MODE == kSplit) {
+    wgrad_store<G, float>(acc, meta, K, N, k0, n0, wk, wn, lane, part + (int64_t)split * N * (K / 2), nullptr, 0,
+                          K / 2);
+  } else {
+    if (tail) {
+      // the tile's own buffer, rows 128 values apart, shifted by its first row and group
+      float* tb = part + (int64_t)(split * ntail + tj % ntail) * kTileValues - n0 * 128 - 2 * (k0 >> 2);
+      wgrad_store<G, float>(acc, meta, K, N, k0, n0, wk, wn, lane, tb, nullptr, 0, 128);
+    } else {
+      wgrad_store<G, O>(acc, meta, K, N, k0, n0, wk, wn, lane, dWv, dWd, accumulate, K / 2);
+    }
+  }
 }
 
 // dW from the token split's fp32 partials: one thread per 2:4 group (n, g)
@@ -533,6 +565,50 @@ __global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(const float* __
   }
 }
 
+// dW of the tail tiles from their token ranges' fp32 partials (part: range-major
+// [ranges][ntail][256 n][128 values]): block (tile i, rows 4b .. 4b+3), thread
+// (row, group) adds the ranges' two kept values in range order, then as
+// wgrad_split_reduce_kernel (dense copy, accumulate, one rounding).
+template <typename O>
+__global__ __launch_bounds__(256) void wgrad_tail_reduce_kernel(const float* __restrict__ part, int ranges, int ntail,
+                                                                int nb_main, int tiles_k, int tiles_n, int64_t N,
+                                                                int64_t K, const uint32_t* __restrict__ meta,
+                                                                O* __restrict__ dWv, O* __restrict__ dWd,
+                                                                int accumulate) {
+  const int i = (int)blockIdx.x / 64, rb = (int)blockIdx.x % 64;
+  int tk, tn;
+  logical_tile(nb_main + i, tiles_k, tiles_n, 8, tk, tn);
+  const int nl = rb * 4 + (int)(threadIdx.x >> 6), gl = (int)(threadIdx.x & 63);
+  const int64_t n = (int64_t)tn * 256 + nl, g = (int64_t)tk * 64 + gl;
+  if (n >= N || 4 * g >= K) return;
+  const int64_t plane = (int64_t)ntail * kTileValues, wpr = (K / 4 + 7) / 8;
+  const float* p = part + (int64_t)i * kTileValues + nl * 128 + 2 * gl;
+  float v0 = 0.f, v1 = 0.f;
+  int sp = 0;
+  for (; sp + 4 <= ranges; sp += 4) {              // four ranges' loads in flight, added in order
+    float2 x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const float2*>(p + (int64_t)(sp + q) * plane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v0 += x[q].x; v1 += x[q].y; }
+  }
+  for (; sp < ranges; ++sp) {
+    const float2 x = *reinterpret_cast<const float2*>(p + (int64_t)sp * plane);
+    v0 += x.x;
+    v1 += x.y;
+  }
+  O* vp = dWv + n * (K / 2) + 2 * g;
+  if (dWd) {
+    const uint32_t nib = (meta[n * wpr + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
+    const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+    const float x[4] = {i0 == 0 ? v0 : 0.f, i0 == 1 ? v0 : (i1 == 1 ? v1 : 0.f),
+                        i0 == 2 ? v0 : (i1 == 2 ? v1 : 0.f), i1 == 3 ? v1 : 0.f};
+    store_quad(dWd + n * K + 4 * g, x, accumulate);
+  }
+  if (accumulate) { v0 += load_out(vp); v1 += load_out(vp + 1); }
+  store_pair(vp, v0, v1);
+}
+
 typedef DGeo<4, 3> DGeoBig;
 
 int64_t chunks_of(int64_t C) { return (C + kChunkRows - 1) / kChunkRows; }
@@ -567,26 +643,65 @@ WgradSplit wgrad_split_plan(int64_t T, int64_t N, int64_t K, int64_t cus) {
   return p;
 }
 
+// Tail split of the weight-gradient GEMM: when the tiles fill more than one
+// round of blocks and the last round is at most three quarters full, that
+// round's tiles run in `ranges` token ranges of kc chunks (at least
+// kMinSplitChunks each, about one round of blocks in all); ntail = 0: no tail split.
+struct WgradTail {
+  int64_t nb_main, ntail, ranges, kc;
+};
+WgradTail wgrad_tail_plan(int64_t T, int64_t N, int64_t K, int64_t cus) {
+  const int64_t nb = chunks_of(K) * chunks_of(N), tch = token_chunks(T);
+  WgradTail p{nb, 0, 1, tch};
+  if (cus < 1 || nb <= cus) return p;
+  const int64_t tail = nb % cus;
+  if (tail == 0 || 4 * tail > 3 * cus) return p;
+  int64_t want = cus / tail;
+  const int64_t most = tch / kMinSplitChunks;
+  if (want > most) want = most;
+  if (want < 2) return p;
+  p.kc = cdiv(tch, want);
+  p.ranges = cdiv(tch, p.kc);
+  if (p.ranges < 2) return p;
+  p.nb_main = nb - tail;
+  p.ntail = tail;
+  return p;
+}
+
 template <typename O, bool H>
 hipError_t launch_packed(const uint16_t* dp, const uint16_t* xp, int64_t T, int64_t N, int64_t K,
                          const uint32_t* meta, O* dWv, O* dWd, int accumulate, float* part, hipStream_t s) {
   typedef DGeoBig G;
-  auto kern = wgrad_direct_kernel<G, O, H, false>;
-  auto kern_split = wgrad_direct_kernel<G, O, H, true>;
+  auto kern = wgrad_direct_kernel<G, O, H, kPlain>;
+  auto kern_split = wgrad_direct_kernel<G, O, H, kSplit>;
+  auto kern_tail = wgrad_direct_kernel<G, O, H, kTail>;
   static hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  const int64_t nb = chunks_of(K) * chunks_of(N);
-  const WgradSplit sp = part ? wgrad_split_plan(T, N, K, device_compute_units()) : WgradSplit{1, token_chunks(T)};
+  const int64_t nb = chunks_of(K) * chunks_of(N), cus = device_compute_units();
+  const WgradSplit sp = part ? wgrad_split_plan(T, N, K, cus) : WgradSplit{1, token_chunks(T)};
+  const WgradTail tp = part ? wgrad_tail_plan(T, N, K, cus) : WgradTail{nb, 0, 1, token_chunks(T)};
+  if (tp.ntail > 0) {
+    static hipError_t attr_tail =
+        hipFuncSetAttribute((const void*)kern_tail, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
+    if (attr_tail != hipSuccess) return attr_tail;
+    kern_tail<<<(unsigned)(tp.nb_main + tp.ntail * tp.ranges), G::THREADS, G::LDS_BYTES, s>>>(
+        dp, xp, (int)T, (int)N, (int)K, meta, dWv, dWd, accumulate, part, (int)tp.kc, (int)tp.nb_main,
+        (int)tp.ntail);
+    wgrad_tail_reduce_kernel<O><<<(unsigned)(tp.ntail * 64), 256, 0, s>>>(
+        part, (int)tp.ranges, (int)tp.ntail, (int)tp.nb_main, (int)chunks_of(K), (int)chunks_of(N), N, K, meta, dWv,
+        dWd, accumulate);
+    return hipGetLastError();
+  }
   if (sp.splits < 2) {
     kern<<<(unsigned)nb, G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv, dWd, accumulate,
-                                                        nullptr, 0);
+                                                        nullptr, 0, 0, 0);
     return hipGetLastError();
   }
   static hipError_t attr_split =
       hipFuncSetAttribute((const void*)kern_split, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS_BYTES);
   if (attr_split != hipSuccess) return attr_split;
   kern_split<<<(unsigned)(nb * sp.splits), G::THREADS, G::LDS_BYTES, s>>>(dp, xp, (int)T, (int)N, (int)K, meta, dWv,
-                                                                          dWd, accumulate, part, (int)sp.kc);
+                                                                          dWd, accumulate, part, (int)sp.kc, 0, 0);
   const int64_t groups = N * (K / 4);
   const unsigned grid = (unsigned)std::min<int64_t>(cdiv(groups, 256), 4096);
   wgrad_split_reduce_kernel<O><<<grid, 256, 0, s>>>(part, (int)sp.splits, N, K, meta, dWv, dWd, accumulate);
@@ -618,8 +733,11 @@ int64_t wgrad_workspace_bytes(int64_t T, int64_t N, int64_t K) {
 int64_t packed_tokens_bytes(int64_t T, int64_t C) { return chunks_of(C) * token_chunks(T) * kChunkElems * 2; }
 
 int64_t wgrad_split_bytes(int64_t T, int64_t N, int64_t K) {
-  const WgradSplit sp = wgrad_split_plan(T, N, K, device_compute_units());
-  return sp.splits < 2 ? 0 : cdiv(sp.splits * N * (K / 2) * 4, 256) * 256;
+  const int64_t cus = device_compute_units();
+  const WgradSplit sp = wgrad_split_plan(T, N, K, cus);
+  if (sp.splits >= 2) return cdiv(sp.splits * N * (K / 2) * 4, 256) * 256;
+  const WgradTail tp = wgrad_tail_plan(T, N, K, cus);
+  return tp.ntail > 0 ? cdiv(tp.ranges * tp.ntail * kTileValues * 4, 256) * 256 : 0;
 }
 
 hipError_t launch_pack_tokens(const void* M, int64_t T, int64_t C, void* packed, hipStream_t s) {

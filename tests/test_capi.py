@@ -214,7 +214,12 @@ def test_wgrad_split_workspace(lib):
     # GPT-2-small QKV: 3 x 9 output tiles of 256 x 256 leave most compute units idle
     need = S.slope_wgrad_split_workspace_bytes(8192, 2304, 768)
     assert need > 0 and need % (2304 * 384 * 4) == 0 and need // (2304 * 384 * 4) >= 2
-    assert S.slope_wgrad_split_workspace_bytes(8192, 27648, 9216) == 0      # OPT-66B QKV: no split
+    # OPT-66B QKV: 36 x 108 = 3888 tiles, a last round of 48 tiles (256 compute
+    # units) cut into 5 token ranges of 52 chunks: one 256 x 128 fp32 buffer per tile and range
+    assert S.slope_wgrad_split_workspace_bytes(8192, 27648, 9216) == 5 * 48 * 256 * 128 * 4
+    assert S.slope_wgrad_split_workspace_bytes(8192, 9216, 9216) == 16 * 16 * 256 * 128 * 4     # O: 1296 tiles
+    assert S.slope_wgrad_split_workspace_bytes(8192, 4096, 4096) == 0       # 256 tiles: whole rounds
+    assert S.slope_wgrad_split_workspace_bytes(8192, 4096 + 2560, 4096) == 0   # last round 160 of 256: kept
     assert S.slope_wgrad_split_workspace_bytes(256, 2304, 768) == 0         # too few tokens to split
     T, N, K = 8192, 2304, 768
     xp, dyp = S.slope_packed_tokens_bytes(T, K), S.slope_packed_tokens_bytes(T, N)

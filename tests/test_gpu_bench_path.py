@@ -5,7 +5,8 @@ buffers reused the way bench.py reuses them:
     slope_prune_compress24 (W_s's tile chunks written) -> slope_double_prune_packed
     -> slope_spmm_fwd_packed_tokens (+ adapter, workspace ws; X's token chunks)
     -> slope_spmm_bwd_dx_packed_tokens (+ the adapter's dX term, workspace
-       ws_bwd; dY's token chunks) -> slope_masked_wgrad_packed
+       ws_bwd; dY's token chunks) -> slope_masked_wgrad_packed (split workspace:
+       the last round's tiles in token ranges)
     -> slope_lowrank_grads_packed (X . L and dY . R^T taken from ws and ws_bwd)
 
 and the training step's weight update, slope_adamw_double_prune_packed.
@@ -97,7 +98,8 @@ def test_bench_step_opt66b(idx):
     S.slope_double_prune_packed(c.values, c.meta, N, K, pd)
     S.slope_spmm_fwd_packed_tokens(X, ps, N, Y, Xp, L=L, R=R, workspace=ws)
     S.slope_spmm_bwd_dx_packed_tokens(dY, pd, K, dX, dYp, L=L, R=R, workspace=ws_bwd)
-    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, c.meta, dW)
+    wsp = _u8(S.slope_wgrad_split_workspace_bytes(T, N, K))    # the last round's tiles in token ranges
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, c.meta, dW, split_workspace=wsp)
     S.slope_lowrank_grads_packed(X, dY, Xp, dYp, L, R, ws_g, dL, dR, fwd_workspace=ws, bwd_workspace=ws_bwd)
 
     # the token chunks against the packing pass
@@ -144,6 +146,14 @@ def test_bench_step_opt66b(idx):
     # dW on sampled rows x a 64-column window, over all tokens
     nw = _rows(rng, N, 8)
     kw0 = int(rng.integers(0, K // 64)) * 64
+    Wsub = np.ascontiguousarray(d["W"][nw][:, kw0:kw0 + 64])
+    _, msub, _ = oracle.compress24(Wsub, oracle.prune24(Wsub)[0])
+    dwv_ref, _ = oracle.masked_wgrad(np.ascontiguousarray(d["dY"][:, nw]), np.ascontiguousarray(d["X"][:, kw0:kw0 + 64]),
+                                     msub, 64)
+    assert normwise(host_f64(dW[nw][:, kw0 // 2:kw0 // 2 + 32]), dwv_ref) <= tol
+    # ... and in the bottom-right output tile, always one of the last round's (token-range) tiles
+    nw = np.sort(rng.choice(np.arange(N - 256, N), size=8, replace=False))
+    kw0 = K - 64
     Wsub = np.ascontiguousarray(d["W"][nw][:, kw0:kw0 + 64])
     _, msub, _ = oracle.compress24(Wsub, oracle.prune24(Wsub)[0])
     dwv_ref, _ = oracle.masked_wgrad(np.ascontiguousarray(d["dY"][:, nw]), np.ascontiguousarray(d["X"][:, kw0:kw0 + 64]),

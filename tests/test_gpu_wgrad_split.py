@@ -146,3 +146,73 @@ def test_wgrad_split_not_needed_is_unchanged():
     S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, b)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# Tail split: 17 x 16 = 272 output tiles on 256 compute units leave a last round
+# of 16 tiles; with a split workspace those run in 4 token ranges (T = 1024: 32
+# chunks, at least 8 per range), their fp32 sums added in range order.  The
+# tail tiles are the last logical ids: k tiles 8..15 x n tiles 15..16 (rows
+# 3840 .. 4351, columns 2048 .. 4095).
+TAIL = (1024, 4352, 4096)
+
+
+def _tail_rows(rng, N):
+    rows = np.concatenate([rng.choice(np.arange(3840, N), size=24, replace=False),
+                           rng.choice(np.arange(0, 3840), size=8, replace=False)])
+    return np.sort(rows)
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_wgrad_tail_split_matches_oracle(out_dt):
+    T, N, K = TAIL
+    need = S.slope_wgrad_split_workspace_bytes(T, N, K)
+    say(f"[wgrad tail split] T={T} N={N} K={K} out={out_dt} workspace={need}")
+    assert need == 4 * 16 * 256 * 128 * 4
+    d = _inputs(T, N, K, "bf16", seed=91, ints=False)
+    X, dY = dev(d["X"]), dev(d["dY"])
+    Xp, dYp, ws = _chunks(X), _chunks(dY), _split_ws(T, N, K)
+    ms = dev_meta(d["ms"])
+    tdt = torch_dtype(out_dt)
+    dWv, dWd = empty((N, K // 2), tdt), empty((N, K), tdt)
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, dWv, dWd, split_workspace=ws, in_dtype=torch.bfloat16)
+    dWu = empty((N, K // 2), tdt)
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, dWu, in_dtype=torch.bfloat16)
+    base = torch.randn((N, K // 2), device="cuda").to(tdt)
+    acc = base.clone()
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, acc, accumulate=True, split_workspace=ws,
+                                in_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = _tail_rows(np.random.default_rng(92), N)
+    v_ref, d_ref = oracle.masked_wgrad(np.ascontiguousarray(d["dY"][:, rows]), d["X"], d["ms"][rows], K)
+    got_v, got_d = host_f64(dWv)[rows], host_f64(dWd)[rows]
+    assert normwise(got_v, v_ref) <= TOL["bf16"]
+    assert normwise(got_d, d_ref) <= TOL["bf16"]
+    assert (got_d[d["mask"][rows] == 0] == 0).all()
+    assert normwise(host_f64(acc)[rows], v_ref + host_f64(base)[rows]) <= TOL["bf16"]
+    # the whole matrix against the unsplit form: tiles of whole rounds bitwise, the tail's within the rounding
+    a, b = host_f64(dWv), host_f64(dWu)
+    assert np.array_equal(a[:3840], b[:3840]) and np.array_equal(a[:, :1024], b[:, :1024])
+    assert normwise(a, b) <= (TOL["bf16"] if out_dt == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_wgrad_tail_split_integer_exact(dt):
+    """Integer inputs: every partial sum is exact in fp32, so the tail split's
+    fp32 output equals the unsplit one and the oracle bit for bit."""
+    T, N, K = TAIL
+    say(f"[wgrad tail split integer] T={T} N={N} K={K} {dt}")
+    d = _inputs(T, N, K, dt, seed=93, ints=True)
+    tdt = torch_dtype(dt)
+    X, dY = dev(d["X"]), dev(d["dY"])
+    Xp, dYp, ws = _chunks(X), _chunks(dY), _split_ws(T, N, K)
+    ms = dev_meta(d["ms"])
+    a, b = empty((N, K // 2), torch.float32), empty((N, K // 2), torch.float32)
+    ad = empty((N, K), torch.float32)
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, a, ad, split_workspace=ws, in_dtype=tdt)
+    S.slope_masked_wgrad_packed(dYp, Xp, T, N, K, ms, b, in_dtype=tdt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rows = _tail_rows(np.random.default_rng(94), N)
+    v_ref, d_ref = oracle.masked_wgrad(np.ascontiguousarray(d["dY"][:, rows]), d["X"], d["ms"][rows], K)
+    assert np.array_equal(host_f64(a)[rows], v_ref)
+    assert np.array_equal(host_f64(ad)[rows], d_ref)
