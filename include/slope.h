@@ -390,8 +390,11 @@ slope_status slope_pack_tokens(slope_dtype dt, const void* M, int64_t T, int64_t
 
 /* Bytes of the token-split workspace slope_masked_wgrad_packed can use for T
  * tokens, N outputs and K inputs on the current device: fp32 partial sums of
- * the kept gradient values, one [N, K/2] plane per token range.  0 when the
- * output tiles alone keep the device busy (no split is made).  Host-only. */
+ * the kept gradient values, either one [N, K/2] plane per token range (when
+ * the 256 x 256 output tiles fill at most half the compute units), or one
+ * 256 x 128 buffer per token range and tile of a last, partly filled round
+ * of tiles (when they fill more than one round and the last is at most three
+ * quarters full).  0 when neither applies (no split is made).  Host-only. */
 slope_status slope_wgrad_split_workspace_bytes(int64_t T, int64_t N, int64_t K, int64_t* bytes);
 
 /* slope_masked_wgrad on operands already packed by slope_pack_tokens:
@@ -402,10 +405,11 @@ slope_status slope_wgrad_split_workspace_bytes(int64_t T, int64_t N, int64_t K, 
  * split_workspace_or_null: NULL, or caller-owned device memory of at least
  * slope_wgrad_split_workspace_bytes(T, N, K) bytes (scratch, overwritten):
  * when the output tiles alone would leave more than half of the compute units
- * idle, the token reduction is then split into ranges whose fp32 partial sums
- * are added in a fixed order by a second kernel (deterministic; the sums are
- * grouped differently, so results may differ from the unsplit form in the
- * last bits).  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or K % 8 != 0;
+ * idle, or end in a partly filled last round, the token reduction of all
+ * tiles, or of that round's tiles, is then split into ranges whose fp32
+ * partial sums are added in a fixed order by a second kernel (deterministic;
+ * the sums are grouped differently, so those outputs may differ from the
+ * unsplit form in the last bits; the other tiles' are bitwise the same).  Errors: SLOPE_ERR_SHAPE if N % 8 != 0 or K % 8 != 0;
  * SLOPE_ERR_WORKSPACE if a packed operand or the given split workspace is
  * short. */
 slope_status slope_masked_wgrad_packed(slope_dtype in_dt, slope_dtype out_dt, const void* dY_packed,
