@@ -105,6 +105,38 @@ def test_products_write_token_chunks(T, K, N, adapter):
         assert np.array_equal(dYp[:yb].cpu().numpy().view(np.uint16), _layout(d["dY"], T, N))
 
 
+@pytest.mark.parametrize("adapter", [False, True])
+def test_products_write_token_chunks_f16(adapter):
+    """The fp16 instantiations: the same bytes as the packing pass, the same outputs as the plain calls."""
+    T, K, N = 777, 528, 336
+    r = 16 if adapter else 0
+    say(f"[token chunks f16] T={T} K={K} N={N} r={r}")
+    d = layer_inputs(K, N, T, max(r, 1), "f16", seed=5, which=("W", "X", "dY", "L", "R"))
+    W, X, dY = dev(d["W"]), dev(d["X"]), dev(d["dY"])
+    L, R = (dev(d["L"]), dev(d["R"])) if adapter else (None, None)
+    h = torch.float16
+    c = Compressed(N, K, h)
+    ps, pd = _u8(S.slope_packed_sparse_bytes(N, K)), _u8(S.slope_packed_sparse_bytes(K, N))
+    S.slope_prune_compress24(W, c.values, c.meta, packed=ps)
+    S.slope_double_prune_packed(c.values, c.meta, N, K, pd)
+    ws = _u8(S.slope_lowrank_workspace_bytes(T, K, r, N)) if adapter else None
+    wsb = _u8(S.slope_lowrank_workspace_bytes(T, N, r, K)) if adapter else None
+    xb, yb = S.slope_packed_tokens_bytes(T, K), S.slope_packed_tokens_bytes(T, N)
+    Xp, Xq, dYp, dYq = _u8(xb, 0xAB), _u8(xb, 0xCD), _u8(yb, 0xAB), _u8(yb, 0xCD)
+    Y, Y_ref = (torch.empty((T, N), dtype=h, device="cuda") for _ in range(2))
+    dX, dX_ref = (torch.empty((T, K), dtype=h, device="cuda") for _ in range(2))
+    S.slope_spmm_fwd_packed_tokens(X, ps, N, Y, Xp, L=L, R=R, workspace=ws)
+    S.slope_spmm_fwd_packed(X, ps, N, Y_ref, L=L, R=R, workspace=ws)
+    S.slope_spmm_bwd_dx_packed_tokens(dY, pd, K, dX, dYp, L=L, R=R, workspace=wsb)
+    S.slope_spmm_bwd_dx_packed(dY, pd, K, dX_ref, L=L, R=R, workspace=wsb)
+    S.slope_pack_tokens(X, Xq)
+    S.slope_pack_tokens(dY, dYq)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y_ref.view(torch.int16))
+    assert torch.equal(dX.view(torch.int16), dX_ref.view(torch.int16))
+    assert torch.equal(Xp[:xb], Xq[:xb]) and torch.equal(dYp[:yb], dYq[:yb])
+
+
 def test_chunks_feed_the_weight_gradient():
     """The chunks the products write serve the weight gradient as the packing
     pass's do: dW from them equals dW from slope_pack_tokens bit for bit, and
