@@ -288,34 +288,42 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
         bo[ft][ks][1] = t * kXsRow + (((4 * ks + 2 + (lane >> 5)) ^ sw) << 4);
       }
     }
-    {
-      u32x4 xr[GPT];
-      fill_load(xr, s0);
-      fill_store(xr, xs_lds);
-    }
-    __syncthreads();
-    int cur = 0;
-    for (int sb = s0; sb < s1; sb += kUnrollXs) {
-      v8 a[kUnrollXs][2][2];
-      int ix[kUnrollXs][2][2];
+    // the weight of a group of stages, loaded one group ahead of its use into
+    // the other of two register sets (the loop is unrolled by two, so no set
+    // is copied while its loads are in flight).  Each lane loads its own 16-bit
+    // half of a metadata word, so the index goes to the MFMA as loaded (a shift
+    // after the load makes the wave wait for it there).
+    uint32_t m16[2];
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) m16[fm] = m_off[fm] + 2 * (lane >> 5);
+    auto load_a = [&](v8 (&a)[kUnrollXs][2][2], int (&ix)[kUnrollXs][2][2], int sb) {
 #pragma unroll
       for (int u = 0; u < kUnrollXs; ++u) {
         const int s = sb + u;
-        const bool live = s < s1;
+        const uint32_t dead = s < s1 ? 0u : kOutOfRange;
         const uint32_t c = (uint32_t)(s - s0) * Chunk::CHUNK_BYTES;
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            a[u][fm][ks] = __builtin_bit_cast(v8, load16(ra, live ? c + a_off[fm][ks] : kOutOfRange));
-            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(ra, live ? c + m_off[fm] + ks * 4 : kOutOfRange, 0, 0);
-            ix[u][fm][ks] = (int)(w >> ix_shift);
+            a[u][fm][ks] = __builtin_bit_cast(v8, load16(ra, (c + a_off[fm][ks]) | dead));
+            ix[u][fm][ks] = (int)__builtin_amdgcn_raw_buffer_load_b16(ra, (c + m16[fm] + ks * 4) | dead, 0, 0);
           }
         }
       }
+    };
+    int cur = 0, sb = s0;
+    // one group: start the next group's X and weight loads (X first, so that
+    // waiting for it before the barrier leaves the weight in flight), multiply
+    // this group, then write the next group's X to the other buffer
+    auto step = [&](v8 (&a)[kUnrollXs][2][2], int (&ix)[kUnrollXs][2][2], v8 (&an)[kUnrollXs][2][2],
+                    int (&ixn)[kUnrollXs][2][2]) -> bool {
       const bool more = sb + kUnrollXs < s1;         // block-uniform
       u32x4 xr[GPT];
-      if (more) fill_load(xr, sb + kUnrollXs);
+      if (more) {
+        fill_load(xr, sb + kUnrollXs);
+        load_a(an, ixn, sb + kUnrollXs);
+      }
       const char* buf = xs_lds + cur * BUF;
 #pragma unroll
       for (int u = 0; u < kUnrollXs; ++u)
@@ -332,9 +340,23 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
             for (int fm = 0; fm < 2; ++fm)
               acc[fm][ft] = Fmt16<H>::smfmac32x32x32(a[u][fm][ks], b, acc[fm][ft], ix[u][fm][ks]);
           }
-      if (more) fill_store(xr, xs_lds + (cur ^ 1) * BUF);
+      if (!more) return false;
+      fill_store(xr, xs_lds + (cur ^ 1) * BUF);
       __syncthreads();                             // next buffer written; this one read by every wave
       cur ^= 1;
+      sb += kUnrollXs;
+      return true;
+    };
+    v8 a0[kUnrollXs][2][2], a1[kUnrollXs][2][2];
+    int ix0[kUnrollXs][2][2], ix1[kUnrollXs][2][2];
+    load_a(a0, ix0, s0);
+    {
+      u32x4 xr[GPT];
+      fill_load(xr, s0);
+      fill_store(xr, xs_lds);
+    }
+    __syncthreads();
+    while (step(a0, ix0, a1, ix1) && step(a1, ix1, a0, ix0)) {
     }
   } else
   for (int sb = s0; sb < s1; sb += kUnroll) {
@@ -401,7 +423,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
 
 // Y[t][n] = sum over the splits (in order) of part + sum_j xl[t][j] R[j][n],
 // rounded once, with xl the sum in slice order of fp32 [xl_slices][T][rpad]
-// (xlf, from the partial kernel).  A block covers 64 consecutive n
+// (xlf, from the partial kernel).  Up to four tokens (more take the wide
+// reduce below).  A block covers 64 consecutive n
 // (one per lane) and TB tokens; its four waves split the work into quarters
 // (wave w: the w-th quarter of the splits, in order, and the w-th quarter of
 // the rank rows), each wave issuing its loads of partial sums (Q at a time)
@@ -436,22 +459,38 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
       const float x = Fmt16<H>::to_f32(R[(int64_t)(j < r ? j : r - 1) * N + nc]);
       rv[q] = (col && q < rq && j < r) ? x : 0.f;
     }
-    for (int e = threadIdx.x; e < TB * rpad; e += 256) {
-      const int i = e / rpad, j = e % rpad;
-      const int t = tb + i < T ? tb + i : T - 1;
-      float v = 0.f;
-      for (int sl0 = 0; sl0 < xl_slices; sl0 += 8) {   // eight slices' loads in flight, added in slice order
-        float t8[8];
+    // element e = threadIdx.x + 256 k of the TB x rpad values: every element's
+    // loads of SB slices in flight together, the slices added in slice order
+    constexpr int EPT = (TB * kReduceMaxRank + 255) / 256;
+    constexpr int SB = EPT >= 8 ? 1 : 8 / EPT;
+    float v[EPT];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+    for (int k = 0; k < EPT; ++k) v[k] = 0.f;
+    for (int sl0 = 0; sl0 < xl_slices; sl0 += SB) {
+      float t8[SB][EPT];
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+          const int e = threadIdx.x + 256 * k, ec = e < TB * rpad ? e : 0;
+          const int i = ec / rpad, j = ec % rpad;
+          const int t = tb + i < T ? tb + i : T - 1;
           const int sl = sl0 + q < xl_slices ? sl0 + q : xl_slices - 1;
-          t8[q] = xlf[((int64_t)sl * T + t) * rpad + j];
+          t8[q][k] = xlf[((int64_t)sl * T + t) * rpad + j];
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (sl0 + q < xl_slices) v += t8[q];
+      for (int q = 0; q < SB; ++q)
+#pragma unroll
+        for (int k = 0; k < EPT; ++k)
+          if (sl0 + q < xl_slices) v[k] += t8[q][k];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = threadIdx.x + 256 * k;
+      if (e < TB * rpad) {
+        const int i = e / rpad, j = e % rpad;
+        xl[i][j] = tb + i < T ? v[k] : 0.f;
       }
-      xl[i][j] = tb + i < T ? v : 0.f;
     }
   }
   float y[TB];
@@ -493,6 +532,136 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   }
 }
 
+// Above four tokens: Y for 64 consecutive n (one per lane) and a span of
+// TBLK = 4 TW tokens per block, wave w taking tokens TW w .. TW w + TW - 1 of
+// the span.  Each wave adds every split of its own tokens, in split order,
+// so no sums cross waves; its partial sums are loaded Q splits at a time
+// (Q TW = 32 values a lane) with the next batch in flight while one is added.
+// With the adapter the block's xl rows (a single slice above four tokens)
+// and R's rows for its 64 columns (as fp32, rows r .. rpad zero) are staged
+// in LDS by 16- and 8-byte loads issued with the first partial sums, and the
+// rank term is added after the splits, in rank order.  Every load is from a
+// clamped, valid address (values past the ends are not used), so that none
+// is a branch.  LDS: (TBLK + 64) rpad floats with the adapter, none without.
+template <typename O, int TW, bool H>
+__global__ __launch_bounds__(256) void decode_reduce_wide_kernel(const float* __restrict__ part, int splits, int T,
+                                                                 int64_t N, int64_t Npad, const uint16_t* __restrict__ R,
+                                                                 const float* __restrict__ xlf, int r, int rpad,
+                                                                 O* __restrict__ Y) {
+  constexpr int Q = 32 / TW, TBLK = 4 * TW;
+  constexpr int XPT = TBLK * kReduceMaxRank / 4 / 256;   // 16-byte granules of xl per thread, at most
+  constexpr int RPT = kReduceMaxRank * 16 / 256;          // 8-byte granules of R per thread, at most
+  extern __shared__ __attribute__((aligned(16))) float wide_lds[];
+  float* xs = wide_lds;                            // [TBLK][rpad]
+  float* rs = wide_lds + TBLK * rpad;              // [rpad][64]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 64, n = n0 + lane;   // < Npad: N in 256s covers the grid's 64s
+  const int tblk = blockIdx.y * TBLK, tw = tblk + wave * TW;
+  auto load_parts = [&](int c0, float (&v)[Q][TW]) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const int c = c0 + q < splits ? c0 + q : splits - 1;
+        const int t = tw + i < T ? tw + i : T - 1;
+        v[q][i] = part[((int64_t)c * T + t) * Npad + n];
+      }
+  };
+  float va[Q][TW], vb[Q][TW];
+  load_parts(0, va);
+  if (Q < splits) load_parts(Q, vb);             // block-uniform
+  if (R) {
+    u32x4 xg[XPT];
+    u32x2 rg[RPT];
+    const int xn = TBLK * rpad / 4, rn = rpad * 16;
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int g = (int)threadIdx.x + 256 * k, e = (g < xn ? g : 0) * 4;
+      const int i = e / rpad, j = e % rpad, t = tblk + i < T ? tblk + i : T - 1;
+      xg[k] = *reinterpret_cast<const u32x4*>(xlf + (int64_t)t * rpad + j);
+    }
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int g = (int)threadIdx.x + 256 * k, gc = g < rn ? g : 0;
+      const int j = gc >> 4, c = (gc & 15) * 4;
+      const int64_t col = n0 + c < N ? n0 + c : 0;   // N % 4 == 0: a granule is inside or past N
+      rg[k] = *reinterpret_cast<const u32x2*>(R + (int64_t)(j < r ? j : 0) * N + col);
+    }
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int g = (int)threadIdx.x + 256 * k, e = g * 4;
+      if (g < xn) {
+        const int i = e / rpad;
+        *reinterpret_cast<u32x4*>(xs + e) = tblk + i < T ? xg[k] : u32x4{};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int g = (int)threadIdx.x + 256 * k;
+      if (g < rn) {
+        const int j = g >> 4, c = (g & 15) * 4;
+        const bool ok = j < r && n0 + c < N;
+        f32x4 f;
+        f[0] = Fmt16<H>::to_f32((uint16_t)(rg[k][0] & 0xffffu));
+        f[1] = Fmt16<H>::to_f32((uint16_t)(rg[k][0] >> 16));
+        f[2] = Fmt16<H>::to_f32((uint16_t)(rg[k][1] & 0xffffu));
+        f[3] = Fmt16<H>::to_f32((uint16_t)(rg[k][1] >> 16));
+        *reinterpret_cast<f32x4*>(rs + j * 64 + c) = ok ? f : f32x4{};
+      }
+    }
+  }
+  float y[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i) y[i] = 0.f;
+  // the splits in order: add one batch while the next is in flight
+  auto add = [&](int c0, float (&v)[Q][TW]) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (c0 + q < splits)
+#pragma unroll
+        for (int i = 0; i < TW; ++i) y[i] += v[q][i];
+  };
+  for (int c0 = 0;;) {
+    add(c0, va);
+    if (c0 + 2 * Q < splits) load_parts(c0 + 2 * Q, va);
+    c0 += Q;
+    if (c0 >= splits) break;
+    add(c0, vb);
+    if (c0 + 2 * Q < splits) load_parts(c0 + 2 * Q, vb);
+    c0 += Q;
+    if (c0 >= splits) break;
+  }
+  if (R) {
+    __syncthreads();                               // xl and R staged
+    const float* xw = xs + wave * TW * rpad;
+    for (int j = 0; j < rpad; j += 4) {
+      const f32x4 rv = {rs[j * 64 + lane], rs[(j + 1) * 64 + lane], rs[(j + 2) * 64 + lane], rs[(j + 3) * 64 + lane]};
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xw + i * rpad + j);
+        y[i] += xv[0] * rv[0];
+        y[i] += xv[1] * rv[1];
+        y[i] += xv[2] * rv[2];
+        y[i] += xv[3] * rv[3];
+      }
+    }
+  }
+  if (n < N) {
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+      if (tw + i < T) store_out(Y + (int64_t)(tw + i) * N + n, y[i]);
+  }
+}
+
+// dynamic LDS of the wide reduce: up to (4 TW + 64) x 128 floats
+template <typename O, int TW, bool H>
+void decode_wide_attr() {
+  static const hipError_t e = hipFuncSetAttribute((const void*)decode_reduce_wide_kernel<O, TW, H>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (4 * TW + 64) * kReduceMaxRank * (int)sizeof(float));
+  (void)e;                                         // a failure shows as the launch's error
+}
+
 template <typename O, bool H>
 void launch_decode_reduce(const float* part, int splits, int64_t T, int64_t N, int64_t Npad, const uint16_t* R,
                           const float* xf, int xs, int r, int rpad, O* Y, hipStream_t s) {
@@ -503,8 +672,22 @@ void launch_decode_reduce(const float* part, int splits, int64_t T, int64_t N, i
     dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 4));
     decode_reduce_kernel<O, 4, 8, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, r, rpad, Y);
   } else {
-    dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 16));
-    decode_reduce_kernel<O, 16, 4, H><<<g, 256, 0, s>>>(part, splits, (int)T, N, Npad, R, xf, xs, r, rpad, Y);
+    // token span per block: 16 up to 16 tokens, else 32, halved to 16 while
+    // the grid has fewer than 512 blocks.  (A 64-token span needs 232 VGPRs,
+    // two waves a SIMD: the OPT-66B layer at 64 tokens took 385 us with it
+    // against 380 us with spans of 32 at most.)
+    const int64_t nb = cdiv(N, 64);
+    int span = T <= 16 ? 16 : 32;
+    if (span > 16 && nb * cdiv(T, span) < 512) span = 16;
+    const size_t lds = R ? (size_t)(span + 64) * rpad * sizeof(float) : 0;
+    dim3 g((unsigned)nb, (unsigned)cdiv(T, span));
+    // above four tokens X . L has one slice (xl_slices), read as [T][rpad]
+    if (span == 32) decode_wide_attr<O, 8, H>();
+    else decode_wide_attr<O, 4, H>();
+    if (span == 32)
+      decode_reduce_wide_kernel<O, 8, H><<<g, 256, lds, s>>>(part, splits, (int)T, N, Npad, R, xf, r, rpad, Y);
+    else
+      decode_reduce_wide_kernel<O, 4, H><<<g, 256, lds, s>>>(part, splits, (int)T, N, Npad, R, xf, r, rpad, Y);
   }
 }
 
@@ -522,12 +705,19 @@ DecodePlan decode_plan(int64_t T, int64_t K, int64_t N) {
   // (splits x T x N x 8 bytes written and read) stay small next to the weight.
   // With many tokens a block spends long on each stage and the weight stream is
   // no longer the limit: then keep at least about 1024 blocks (latency hiding on
-  // a few blocks per CU) as long as each still runs 16 stages or more.
-  int64_t want = cdiv(2048, p.tiles < 1 ? 1 : p.tiles);
+  // a few blocks per CU) as long as each still runs 16 stages or more.  Above
+  // four tokens (X staged in LDS, two blocks per CU by registers, each with the
+  // next group's weight in flight) fewer blocks pay, measured on the OPT-66B
+  // linears: above 32 tokens about 512 (the floor, not 1024; 441 -> 406 us a
+  // layer at 64 tokens), and up to 32 tokens with 64 tiles or more one round
+  // of 512 blocks (QKV and FC1 at 16 tokens 10% faster; 36 tiles keep the cap).
+  const int64_t tiles = p.tiles < 1 ? 1 : p.tiles;
+  int64_t want = cdiv(2048, tiles);
   int64_t cap = (int64_t)(0.02 * (double)K / (double)(T < 1 ? 1 : T));
-  const int64_t busy = std::min<int64_t>(cdiv(1024, p.tiles < 1 ? 1 : p.tiles), p.stages / 16);
+  const int64_t busy = std::min<int64_t>(cdiv(T > 32 ? 512 : 1024, tiles), p.stages / 16);
   if (cap < busy) cap = busy;
   if (want > cap) want = cap;
+  if (T > kXlTok && T <= 32 && tiles >= 64) want = 512 / tiles;
   if (want > p.stages) want = p.stages;
   if (want < 1) want = 1;
   p.kc = (int)cdiv(p.stages, want);

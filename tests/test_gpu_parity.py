@@ -379,9 +379,11 @@ def test_spmm_fwd_decode(T, N, K, adapter, out_dt):
 
 
 @pytest.mark.parametrize("T,N,K,r", [(1, 256, 9216, 72), (4, 520, 1040, 128), (2, 64, 131072, 33), (1, 64, 16, 1),
-                                     (3, 272, 4112, 17)])
+                                     (3, 272, 4112, 17), (40, 520, 1040, 128), (17, 264, 4112, 33),
+                                     (64, 136, 2064, 100)])
 def test_spmm_fwd_decode_adapter_ranks(T, N, K, r):
-    """Few tokens with the adapter: ranks up to 128, long reductions, ragged sizes."""
+    """Few tokens with the adapter: ranks up to 128, long reductions, ragged
+    sizes; above four tokens token spans that end inside a wave's tokens."""
     say(f"spmm_fwd_decode adapter T={T} N={N} K={K} r={r}")
     d = _layer(T, N, K, r, "bf16", seed=5 * T + N + K + r)
     ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
@@ -394,7 +396,7 @@ def test_spmm_fwd_decode_adapter_ranks(T, N, K, r):
     assert normwise(host_f64(Y), ref) <= 2e-5 * max(1.0, np.sqrt(K / 256))
 
 
-@pytest.mark.parametrize("T", [3, 7])
+@pytest.mark.parametrize("T", [3, 7, 40])
 def test_spmm_fwd_decode_integer_exact(T):
     """Integer inputs: every partial sum is exact, so fp32 output equals the oracle."""
     N, K, r = 520, 1040, 4

@@ -61,7 +61,7 @@ class Case:
 
 
 def test_noalloc_decode_matches_workspace_form():
-    # OPT-66B QKV at 16 tokens (15.2 MiB of scratch), then a small ragged layer
+    # OPT-66B QKV at 16 tokens (6.8 MiB of scratch), then a small ragged layer
     big = Case(16, 9216, 27648, 72, seed=3)
     small = Case(3, 528, 272, 8, seed=4)
     assert S.slope_decode_workspace_bytes(16, 9216, 72, 27648) <= S.DECODE_NOALLOC_SCRATCH_BYTES
@@ -91,7 +91,7 @@ def test_noalloc_decode_without_adapter_and_fp32_output():
 
 
 def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
-    # OPT-66B FC1 at 64 tokens needs 72 MiB of scratch: refused, nothing written
+    # OPT-66B FC1 at 64 tokens needs 36 MiB of scratch: refused, nothing written
     T, K, N, r = 64, 9216, 36864, 72
     assert S.slope_decode_workspace_bytes(T, K, r, N) > S.DECODE_NOALLOC_SCRATCH_BYTES
     X = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
