@@ -396,11 +396,12 @@ def test_spmm_fwd_decode_adapter_ranks(T, N, K, r):
     assert normwise(host_f64(Y), ref) <= 2e-5 * max(1.0, np.sqrt(K / 256))
 
 
-@pytest.mark.parametrize("T", [3, 7, 40])
-def test_spmm_fwd_decode_integer_exact(T):
-    """Integer inputs: every partial sum is exact, so fp32 output equals the oracle."""
-    N, K, r = 520, 1040, 4
-    say(f"decode integer probe T={T}")
+@pytest.mark.parametrize("T,K", [(3, 1040), (7, 1040), (40, 1040), (40, 8224)])
+def test_spmm_fwd_decode_integer_exact(T, K):
+    """Integer inputs: every partial sum is exact, so fp32 output equals the
+    oracle (K = 8224: a longer reduction, X . L over all of it)."""
+    N, r = 520, 4
+    say(f"decode integer probe T={T} K={K}")
     d = _layer(T, N, K, r, "bf16", seed=23, ints=True)
     ps = torch.empty(S.slope_packed_sparse_bytes(N, K), dtype=torch.uint8, device="cuda")
     S.slope_pack_sparse(dev(d["vs"]), dev_meta(d["ms"]), N, K, ps)
