@@ -543,12 +543,11 @@ slope_status slope_lowrank_grads_packed(slope_dtype in_dt, slope_dtype out_dt, c
   if (!have_f) e = slope::launch_lowrank_down((Dt)in_dt, X, L, T, K, r, wf, s);                      // X . L
   if (e == hipSuccess && !have_b) e = slope::launch_lowrank_prepare_bwd(dY, L, R, T, N, r, K, wb, s);  // dY . R^T
   if (e == hipSuccess) e = slope::launch_transpose_hilo2(wf, wb, r32, xh, xl, gh, gl, s);
-  if (e == hipSuccess)
-    e = slope::launch_lr_wgrad((Dt)in_dt, (Dt)out_dt, dY_packed, T, N, r, xh, xl, wf.Tpad, pr, dR, false, accumulate,
-                               s);
-  if (e == hipSuccess)
-    e = slope::launch_lr_wgrad((Dt)in_dt, (Dt)out_dt, X_packed, T, K, r, gh, gl, wb.Tpad, pl, dL, true, accumulate,
-                               s);
+  if (e == hipSuccess) {
+    const slope::LrGrad grad_r{dY_packed, N, xh, xl, wf.Tpad, pr, dR, false};   // dR = (X . L)^T . dY
+    const slope::LrGrad grad_l{X_packed, K, gh, gl, wb.Tpad, pl, dL, true};     // dL = X^T . (dY . R^T)
+    e = slope::launch_lr_wgrad_pair((Dt)in_dt, (Dt)out_dt, grad_r, grad_l, T, r, accumulate, s);
+  }
   return from_hip(e);
 }
 

@@ -94,10 +94,21 @@ hipError_t launch_transpose_hilo2(const LowrankWs& w1, const LowrankWs& w2, int6
 // A the chunks of a [T, C] matrix and B given as a transposed hi/lo pair
 // [32*ceil(r/32)][Tpad]; written as out[j][c] (dR) or, trans, out[c][j] (dL).
 // part: lr_wgrad_part_bytes(T, C, r) of fp32 scratch.
+struct LrGrad {
+  const void* chunks;
+  int64_t C;
+  const uint16_t* bh;
+  const uint16_t* bl;
+  int64_t Tpad;
+  float* part;
+  void* dst;
+  bool trans;
+};
 int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r);
-hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
-                           const uint16_t* bl, int64_t Tpad, float* part, void* dst, bool trans, int accumulate,
-                           hipStream_t s);
+// Both gradients of one adapter (the same T and r) in one partial-sum launch
+// and one reduce; T > 0, r in 1 .. 128, both C > 0.
+hipError_t launch_lr_wgrad_pair(Dt in, Dt out, const LrGrad& g0, const LrGrad& g1, int64_t T, int64_t r,
+                                int accumulate, hipStream_t s);
 
 // Y[t][m] = B[t, :] . Adense[m, :]  (+ (X . L)[t, :] . R[:, m] when ws != nullptr)
 // with Adense the decompressed 2:4 operand [M, Kred] and B row-major [T, Kred].

@@ -13,7 +13,8 @@
 // one 256-column chunk column over a range of token chunks (B's slice staged
 // in LDS once per chunk for the block's four waves); the fp32 partial
 // sums are added in range order by a second kernel, which also writes the
-// output in its own layout (dR row-major [r, N], dL row-major [K, r]).
+// output in its own layout (dR row-major [r, N], dL row-major [K, r]).  One
+// launch of each kernel computes both gradients of a layer.
 #include "common.h"
 #include "dma.h"
 #include "launch.h"
@@ -33,16 +34,38 @@ constexpr int kChunkRows = 256, kChunkTokens = 32, kChunkBytes = kChunkRows * kC
 // memory; the block stages each chunk's slice of B (16 NJ rows x 32 tokens, hi
 // and lo) in LDS once, in a double buffer, with 16-byte granule g of row j at
 // g ^ ((j/4) % 4) so that fragment reads are free of bank conflicts.
+// One product of the pair a launch computes: A's token chunks, B's hi/lo
+// pair, the partial sums, and the grid of tiles x splits that covers it.
+struct LrTask {
+  const char* chunks;
+  const uint16_t* bh;
+  const uint16_t* bl;
+  float* part;
+  int64_t Tch, Tpad, Cpad;
+  int per_split, tiles, splits;
+};
+
+// Blocks 0 .. t0.tiles * t0.splits - 1 compute t0 (tile fastest), the rest t1:
+// both adapter products of a layer in one launch, so that the one with few
+// column tiles (216 blocks for a 9216-wide operand) shares the device with the
+// other instead of running alone.
 template <int NJ, bool H>
-__global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __restrict__ chunks, int64_t Tch,
-                                                               int per_split, const uint16_t* __restrict__ bh,
-                                                               const uint16_t* __restrict__ bl, int64_t Tpad,
-                                                               int64_t Cpad, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const LrTask t0, const LrTask t1) {
   constexpr int BROWS = NJ * 16, SLICE = 2 * BROWS * 64;        // bytes of one chunk's B slice (hi and lo)
   constexpr int PIECES = SLICE / 16, PPT = (PIECES + 255) / 256;  // 16-byte staging pieces, per thread
   __shared__ __attribute__((aligned(16))) char bs[2][SLICE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int n0 = t0.tiles * t0.splits;
+  const bool second = (int)blockIdx.x >= n0;                      // block-uniform
+  const LrTask& t = second ? t1 : t0;
+  const int b = second ? (int)blockIdx.x - n0 : (int)blockIdx.x;
+  const int tile = b % t.tiles, split = b / t.tiles;
+  const char* __restrict__ chunks = t.chunks;
+  const uint16_t* __restrict__ bh = t.bh;
+  const uint16_t* __restrict__ bl = t.bl;
+  float* __restrict__ part = t.part;
+  const int64_t Tch = t.Tch, Tpad = t.Tpad, Cpad = t.Cpad;
+  const int per_split = t.per_split;
   const int64_t s0 = (int64_t)split * per_split;
   const int64_t s1 = (s0 + per_split < Tch) ? s0 + per_split : Tch;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(chunks + ((int64_t)tile * Tch + s0) * kChunkBytes,
@@ -127,19 +150,31 @@ __global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const char* __res
   }
 }
 
+// One output of the pair: its partial sums and where the sums go.
+struct LrOut {
+  const float* part;
+  void* out;
+  int64_t C, Cpad;
+  int splits;
+  bool trans;
+};
+
 // out = sum over splits (in order) of part[s][j][c], for j < r, c < C, written
-// as out[j][c] (TRANS false: dR [r, N]) or out[c][j] (TRANS true: dL [K, r]).
-template <typename O, bool TRANS>
-__global__ __launch_bounds__(256) void lr_wgrad_reduce_kernel(const float* __restrict__ part, int splits, int r,
-                                                              int rows, int64_t C, int64_t Cpad, int accumulate,
-                                                              O* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)r * C) return;
-  const int64_t j = i / C, c = i % C;
+// as out[j][c] (trans false: dR [r, N]) or out[c][j] (trans true: dL [K, r]);
+// elements 0 .. r C0 - 1 are o0's, the rest o1's.
+template <typename O>
+__global__ __launch_bounds__(256) void lr_wgrad_reduce_kernel(const LrOut o0, const LrOut o1, int r, int rows,
+                                                              int accumulate) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool second = i >= (int64_t)r * o0.C;
+  if (second) i -= (int64_t)r * o0.C;
+  const LrOut& o = second ? o1 : o0;
+  if (i >= (int64_t)r * o.C) return;
+  const int64_t j = i / o.C, c = i % o.C;
   float v = 0.f;
 #pragma unroll 4
-  for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * rows + j) * Cpad + c];
-  O* p = TRANS ? out + c * r + j : out + j * C + c;
+  for (int sp = 0; sp < o.splits; ++sp) v += o.part[((int64_t)sp * rows + j) * o.Cpad + c];
+  O* p = o.trans ? (O*)o.out + c * r + j : (O*)o.out + j * o.C + c;
   if (accumulate) v += load_out(p);
   store_out(p, v);
 }
@@ -156,23 +191,18 @@ int64_t split_count(int64_t tiles, int64_t Tch, int64_t brows) {
 }
 
 template <int NJ>
-void launch_partial(bool h16, const char* chunks, int64_t tiles, int64_t Tch, int per, int64_t splits,
-                    const uint16_t* bh, const uint16_t* bl, int64_t Tpad, int64_t Cpad, float* part, hipStream_t s) {
-  const dim3 grid((unsigned)tiles, (unsigned)splits);
+void launch_partial(bool h16, const LrTask& t0, const LrTask& t1, hipStream_t s) {
+  const unsigned grid = (unsigned)(t0.tiles * t0.splits + t1.tiles * t1.splits);
   if (h16)
-    lr_wgrad_partial_kernel<NJ, true><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+    lr_wgrad_partial_kernel<NJ, true><<<grid, 256, 0, s>>>(t0, t1);
   else
-    lr_wgrad_partial_kernel<NJ, false><<<grid, 256, 0, s>>>(chunks, Tch, per, bh, bl, Tpad, Cpad, part);
+    lr_wgrad_partial_kernel<NJ, false><<<grid, 256, 0, s>>>(t0, t1);
 }
 
 template <typename O>
-void launch_reduce(const float* part, int sp, int r, int rows, int64_t C, int64_t Cpad, int accumulate, bool trans,
-                   void* dst, hipStream_t s) {
-  const unsigned rb = (unsigned)cdiv((int64_t)r * C, 256);
-  if (trans)
-    lr_wgrad_reduce_kernel<O, true><<<rb, 256, 0, s>>>(part, sp, r, rows, C, Cpad, accumulate, (O*)dst);
-  else
-    lr_wgrad_reduce_kernel<O, false><<<rb, 256, 0, s>>>(part, sp, r, rows, C, Cpad, accumulate, (O*)dst);
+void launch_reduce(const LrOut& o0, const LrOut& o1, int r, int rows, int accumulate, hipStream_t s) {
+  const unsigned rb = (unsigned)cdiv((int64_t)r * (o0.C + o1.C), 256);
+  lr_wgrad_reduce_kernel<O><<<rb, 256, 0, s>>>(o0, o1, r, rows, accumulate);
 }
 
 }  // namespace
@@ -186,39 +216,38 @@ int64_t lr_wgrad_part_bytes(int64_t T, int64_t C, int64_t r) {
   return cdiv(splits * lr_rows(r) * tiles * kChunkRows * 4, 256) * 256;
 }
 
-hipError_t launch_lr_wgrad(Dt in, Dt out, const void* chunks, int64_t T, int64_t C, int64_t r, const uint16_t* bh,
-                           const uint16_t* bl, int64_t Tpad, float* part, void* dst, bool trans, int accumulate,
-                           hipStream_t s) {
-  if (C == 0 || r == 0) return hipSuccess;
-  const int64_t tiles = cdiv(C, kChunkRows), Tch = cdiv(T, kChunkTokens), Cpad = tiles * kChunkRows;
-  const int64_t rows = lr_rows(r);
-  const int64_t per = Tch ? cdiv(Tch, split_count(tiles, Tch, rows)) : 1, splits = Tch ? cdiv(Tch, per) : 1;
-  const char* ch = (const char*)chunks;
+hipError_t launch_lr_wgrad_pair(Dt in, Dt out, const LrGrad& g0, const LrGrad& g1, int64_t T, int64_t r,
+                                int accumulate, hipStream_t s) {
+  if (r == 0 || g0.C == 0 || g1.C == 0) return hipErrorInvalidValue;   // the caller returns before
+  const int64_t Tch = cdiv(T, kChunkTokens), rows = lr_rows(r);
+  if (Tch == 0) return hipErrorInvalidValue;                            // no tokens: the caller clears dL, dR
+  auto task = [&](const LrGrad& g) {
+    const int64_t tiles = cdiv(g.C, kChunkRows);
+    const int64_t per = cdiv(Tch, split_count(tiles, Tch, rows)), splits = cdiv(Tch, per);
+    return LrTask{(const char*)g.chunks, g.bh, g.bl, g.part, Tch, g.Tpad, tiles * kChunkRows, (int)per, (int)tiles,
+                  (int)splits};
+  };
+  const LrTask t0 = task(g0), t1 = task(g1);
   const bool h16 = in == Dt::F16;
-  if (Tch == 0) {
-    // no tokens: the sums are empty (one split of zeros, cleared by a kernel)
-    hipError_t e = launch_fill_zero(Dt::F32, part, rows * Cpad, s);
-    if (e != hipSuccess) return e;
-  } else {
-    switch (rows / 16) {
-      case 1: launch_partial<1>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 2: launch_partial<2>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 3: launch_partial<3>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 4: launch_partial<4>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 5: launch_partial<5>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 6: launch_partial<6>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 7: launch_partial<7>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      case 8: launch_partial<8>(h16, ch, tiles, Tch, (int)per, splits, bh, bl, Tpad, Cpad, part, s); break;
-      default: return hipErrorInvalidValue;     // rank above 128: refused by the caller
-    }
+  switch (rows / 16) {
+    case 1: launch_partial<1>(h16, t0, t1, s); break;
+    case 2: launch_partial<2>(h16, t0, t1, s); break;
+    case 3: launch_partial<3>(h16, t0, t1, s); break;
+    case 4: launch_partial<4>(h16, t0, t1, s); break;
+    case 5: launch_partial<5>(h16, t0, t1, s); break;
+    case 6: launch_partial<6>(h16, t0, t1, s); break;
+    case 7: launch_partial<7>(h16, t0, t1, s); break;
+    case 8: launch_partial<8>(h16, t0, t1, s); break;
+    default: return hipErrorInvalidValue;     // rank above 128: refused by the caller
   }
-  const int sp = Tch ? (int)splits : 1;
+  const LrOut o0{g0.part, g0.dst, g0.C, t0.Cpad, t0.splits, g0.trans};
+  const LrOut o1{g1.part, g1.dst, g1.C, t1.Cpad, t1.splits, g1.trans};
   if (out == Dt::BF16)
-    launch_reduce<uint16_t>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<uint16_t>(o0, o1, (int)r, (int)rows, accumulate, s);
   else if (out == Dt::F16)
-    launch_reduce<_Float16>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<_Float16>(o0, o1, (int)r, (int)rows, accumulate, s);
   else
-    launch_reduce<float>(part, sp, (int)r, (int)rows, C, Cpad, accumulate, trans, dst, s);
+    launch_reduce<float>(o0, o1, (int)r, (int)rows, accumulate, s);
   return hipGetLastError();
 }
 
