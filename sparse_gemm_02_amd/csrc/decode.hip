@@ -191,7 +191,9 @@ __device__ __forceinline__ void xl_columns(const uint16_t* __restrict__ X, const
 // read their B fragments from LDS instead of each streaming all of X from the
 // cache (at 64 tokens X's bytes per stage are 3.5x the weight's).  Groups of
 // two stages (not four) halve the LDS a block holds, so more blocks share a
-// compute unit (T = 64 layer 460 -> 441 us, the same at T = 16).
+// compute unit (T = 64 layer 460 -> 441 us, the same at T = 16).  Each wave
+// also loads the next group's weight into a second register set while the
+// current group multiplies, so two groups of weight are in flight per wave.
 constexpr int kXsRow = 128;                        // bytes of X per token and stage
 constexpr int kUnrollXs = 2;                       // stages per X group
 template <int FT>
