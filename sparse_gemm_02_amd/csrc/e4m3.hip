@@ -169,56 +169,56 @@ __global__ __launch_bounds__(256) void quantize_kernel(const In* __restrict__ sr
 constexpr int kChunk8Rows = 256, kChunk8Cols = 128;
 constexpr int kChunk8ValueBytes = kChunk8Rows * 64, kChunk8Bytes = kChunk8ValueBytes + kChunk8Rows * 16;
 
+// Eight lanes per row: lane k of a row's group reads its 16-byte piece
+// (compressed values 8k .. 8k+7 of the chunk's 64) and the group's first four
+// lanes its metadata words, so each group reads one contiguous 128-byte line
+// of values per row; 32 rows per pass, all eight passes' loads issued first.
+// Lane k writes its eight codes (half of granule k / 2) and, k < 4, metadata
+// word k.
 template <typename In>
 __global__ __launch_bounds__(256) void pack_e4m3_kernel(const In* __restrict__ vals, const uint32_t* __restrict__ meta,
                                                         int64_t M, int64_t Kred, int64_t stages, int64_t nchunks,
                                                         const uint32_t* __restrict__ amax, char* __restrict__ out) {
   const float sc = e4m3_scale_from_amax(*amax);
-  const int r = threadIdx.x;                         // one row of the chunk per thread
+  const int k = threadIdx.x & 7, rsub = threadIdx.x >> 3;
   const int64_t wpr = (Kred / 4 + 7) / 8, half = Kred / 2;
   for (int64_t q = blockIdx.x; q < nchunks; q += gridDim.x) {
     const int64_t tm = q / stages, s = q % stages;
-    const int64_t row = tm * kChunk8Rows + r;
-    const bool live = row < M;
-    const int64_t rc = live ? row : 0;
     char* chunk = out + q * kChunk8Bytes;
-    // 64 compressed values from eight 16-byte loads (clamped, then masked: each
-    // granule of 8 values lies entirely inside or outside the row, Kred % 16 == 0)
+    const int64_t c0 = s * 64 + 8 * k;                // this lane's first compressed value of the row
+    const int64_t word = 4 * s + (k & 3);             // this lane's metadata word (lanes 4..7 repeat 0..3)
+    // every load from a clamped, valid address, masked afterwards (Kred % 16 == 0:
+    // a piece of 8 values lies entirely inside or outside the row)
     u32x4 v[8];
+    uint32_t mw[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t c0 = s * 64 + 8 * j;
-      v[j] = *reinterpret_cast<const u32x4*>(vals + rc * half + (c0 < half ? c0 : 0));
+    for (int p = 0; p < 8; ++p) {
+      const int64_t row = tm * kChunk8Rows + 32 * p + rsub;
+      const int64_t rc = row < M ? row : 0;
+      v[p] = *reinterpret_cast<const u32x4*>(vals + rc * half + (c0 < half ? c0 : 0));
+      mw[p] = meta[rc * wpr + (word < wpr ? word : 0)];
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {                    // granule g: values 16g .. 16g+15
-      u32x4 o;
+    for (int p = 0; p < 8; ++p) {
+      const int r = 32 * p + rsub;
+      const bool live = tm * kChunk8Rows + r < M;
+      const bool ok = live && c0 < half;
+      u32x2 o;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = 2 * g + h;
-        const bool ok = live && s * 64 + 8 * j < half;
+      for (int e = 0; e < 2; ++e) {
+        uint32_t w = 0u;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          uint32_t word = 0u;
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const uint32_t pair = v[j][2 * e + p];
-            const float a = in_to_f32<In>(__builtin_bit_cast(In, (uint16_t)(pair & 0xFFFFu))) * sc;
-            const float c = in_to_f32<In>(__builtin_bit_cast(In, (uint16_t)(pair >> 16))) * sc;
-            word |= (f32_to_e4m3(a) | (f32_to_e4m3(c) << 8)) << (16 * p);
-          }
-          o[2 * h + e] = ok ? word : 0u;
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t pair = v[p][2 * e + h];
+          const float a = in_to_f32<In>(__builtin_bit_cast(In, (uint16_t)(pair & 0xFFFFu))) * sc;
+          const float c = in_to_f32<In>(__builtin_bit_cast(In, (uint16_t)(pair >> 16))) * sc;
+          w |= (f32_to_e4m3(a) | (f32_to_e4m3(c) << 8)) << (16 * h);
         }
+        o[e] = ok ? w : 0u;
       }
-      *reinterpret_cast<u32x4*>(chunk + r * 64 + ((g ^ ((r >> 2) & 3)) << 4)) = o;
+      *reinterpret_cast<u32x2*>(chunk + r * 64 + (((k >> 1) ^ ((r >> 2) & 3)) << 4) + 8 * (k & 1)) = o;
+      if (k < 4) *reinterpret_cast<uint32_t*>(chunk + kChunk8ValueBytes + r * 16 + 4 * k) = (live && word < wpr) ? mw[p] : 0u;
     }
-    u32x4 m;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int64_t word = 4 * s + w;
-      m[w] = (live && word < wpr) ? meta[rc * wpr + word] : 0u;
-    }
-    *reinterpret_cast<u32x4*>(chunk + kChunk8ValueBytes + r * 16) = m;
   }
 }
 
