@@ -711,15 +711,16 @@ DecodePlan decode_plan(int64_t T, int64_t K, int64_t N) {
   // four tokens (X staged in LDS, two blocks per CU by registers, each with the
   // next group's weight in flight) fewer blocks pay, measured on the OPT-66B
   // linears: above 32 tokens about 512 (the floor, not 1024; 441 -> 406 us a
-  // layer at 64 tokens), and up to 32 tokens with 64 tiles or more one round
-  // of 512 blocks (QKV and FC1 at 16 tokens 10% faster; 36 tiles keep the cap).
+  // layer at 64 tokens), and up to 32 tokens with 48 tiles or more one round
+  // of 512 blocks (QKV and FC1 at 16 tokens 10% faster, OPT-13B's 60-tile QKV
+  // 3%; 36 tiles keep the cap).
   const int64_t tiles = p.tiles < 1 ? 1 : p.tiles;
   int64_t want = cdiv(2048, tiles);
   int64_t cap = (int64_t)(0.02 * (double)K / (double)(T < 1 ? 1 : T));
   const int64_t busy = std::min<int64_t>(cdiv(T > 32 ? 512 : 1024, tiles), p.stages / 16);
   if (cap < busy) cap = busy;
   if (want > cap) want = cap;
-  if (T > kXlTok && T <= 32 && tiles >= 64) want = 512 / tiles;
+  if (T > kXlTok && T <= 32 && tiles >= 48) want = 512 / tiles;
   if (want > p.stages) want = p.stages;
   if (want < 1) want = 1;
   p.kc = (int)cdiv(p.stages, want);
