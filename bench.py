@@ -38,9 +38,11 @@ kernel with the largest share of the step against the dense bf16 MFMA peak
 time (forward and dX at the 2:4-sparse MFMA peak, the weight gradient's dense
 flops at the dense peak) over the measured step; `sparse_products_target`
 gives the forward and dX products as fractions of the 2:4-sparse peak.
-`configs` runs the GPT-2-small, BERT-Large and OPT-13B layers (and OPT-13B's
-few-token forward at T = 16) through the same step, each against its own
-ideal; `dense_context` times the same twelve GEMMs as dense bf16 products
+`graph` replays the same step from a HIP graph (context; `value` stays the
+eager step). `configs` runs the GPT-2-small, BERT-Large and OPT-13B layers (and
+OPT-13B's few-token forward at T = 16) through the same step, each against its
+own ideal, eager and replayed from a graph (the small layers are bound by
+launches); `dense_context` times the same twelve GEMMs as dense bf16 products
 through torch (context only); `fp8` times the forward and dX products of the
 8-bit (E4M3) variant on the same layer (quantizing and packing apart).  `cpu_baseline` times the CPU oracle on a
 bounded slice of the same layer on this host.
@@ -557,6 +559,36 @@ def time_steps(lins, S, torch, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def time_steps_graph(lins, S, torch, steps, warmup):
+    """ms per whole step replayed from a HIP graph (torch.cuda.CUDAGraph over
+    the same library calls): eager warm-up steps first (every kernel attribute
+    set, every plan made outside the capture), one step captured, `warmup`
+    replays untimed, `steps` replays timed.  The library records no memset and
+    allocates nothing, so a step captures as it runs."""
+    for _ in range(max(1, warmup)):
+        step(lins, S)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(lins, S)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(lins, S)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / steps
+
+
 def configs_pass(args, S, torch, WORKLOADS, steps=5, warmup=2):
     """The other training configurations (GPT-2-small, BERT-Large, OPT-13B) through
     the same step, each against its own layer roofline, and OPT-13B's few-token
@@ -566,11 +598,13 @@ def configs_pass(args, S, torch, WORKLOADS, steps=5, warmup=2):
         wl = WORKLOADS[name]
         lins = [Linear(l.name, l.K, l.N, wl.T, wl.r, seed=0, index=i) for i, l in enumerate(wl.linears)]
         ms = time_steps(lins, S, torch, steps, warmup)
+        ms_g = time_steps_graph(lins, S, torch, steps, warmup)
         flops = sum(sum(l.flops().values()) for l in lins)
         ideal = ideal_step_ms(wl, wl.T)
         out[name] = {"tokens": wl.T, "adapter_rank": wl.r, "ms_per_step": round(ms, 4),
                      "dense_equiv_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-                     "ideal_step_ms": round(ideal, 4), "layer_roofline_frac": round(ideal / ms, 4)}
+                     "ideal_step_ms": round(ideal, 4), "layer_roofline_frac": round(ideal / ms, 4),
+                     "ms_per_step_graph": round(ms_g, 4), "layer_roofline_frac_graph": round(ideal / ms_g, 4)}
         if wl.decode_T:
             for T, v in decode_pass(lins, wl, S, torch).items():
                 ideal_us = v["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
@@ -713,6 +747,10 @@ def main():
            "ops": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
            "roofline": roofline}
     if not args.no_extras:
+        ms_graph = time_steps_graph(lins, S, torch, args.steps, args.warmup)
+        out["graph"] = {"ms_per_step": round(ms_graph, 4),
+                        "what": "the same step replayed from a HIP graph (torch.cuda.CUDAGraph over the library's "
+                                "calls); context: value is the eager step"}
         if wl.decode_T:
             out["decode"] = decode_pass(lins, wl, S, torch)
         out["weight_update"] = update_pass(lins, S, torch)
