@@ -48,9 +48,11 @@ struct LrTask {
 // Blocks 0 .. t0.tiles * t0.splits - 1 compute t0 (tile fastest), the rest t1:
 // both adapter products of a layer in one launch, so that the one with few
 // column tiles (216 blocks for a 9216-wide operand) shares the device with the
-// other instead of running alone.
+// other instead of running alone.  Up to rank 80 the register budget of three
+// blocks per compute unit holds the accumulators without spilling (four
+// linears of OPT-66B at rank 72: 0.81 -> 0.79 ms with two blocks per unit).
 template <int NJ, bool H>
-__global__ __launch_bounds__(256) void lr_wgrad_partial_kernel(const LrTask t0, const LrTask t1) {
+__global__ __launch_bounds__(256, NJ <= 5 ? 3 : 2) void lr_wgrad_partial_kernel(const LrTask t0, const LrTask t1) {
   constexpr int BROWS = NJ * 16, SLICE = 2 * BROWS * 64;        // bytes of one chunk's B slice (hi and lo)
   constexpr int PIECES = SLICE / 16, PPT = (PIECES + 255) / 256;  // 16-byte staging pieces, per thread
   __shared__ __attribute__((aligned(16))) char bs[2][SLICE];
