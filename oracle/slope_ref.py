@@ -445,7 +445,7 @@ def storage_accounting(value_bits=16, index_bits=3, mask_bits=8, moment_bits=32)
 # The explainer's Technical Summary 1 (Problem Statement) names N:M sparsity
 # in general and the discussion page ("Memory Footprint Reduction During
 # Pretraining and Inference") counts 16-bit values; neither gives an 8-bit
-# format or a scaling rule.  The 8-bit variant here is this build's reading:
+# format or a scaling rule.  The 8-bit variant here is a reading taken for them:
 # the OCP FP8 E4M3 format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 # bits, subnormals, no infinities, the all-ones codes 0x7F / 0xFF are NaN,
 # largest finite value 448), one scale per tensor chosen from its largest
@@ -470,8 +470,8 @@ def decode_e4m3(codes) -> np.ndarray:
 
 def round_e4m3(x) -> np.ndarray:
     """E4M3 codes (uint8) nearest to float64 values, ties to the even code
-    (even mantissa), saturating: magnitudes beyond 448 give +-448 (this build's
-    reading; a conversion to the largest finite value, since the format has no
+    (even mantissa), saturating: magnitudes beyond 448 give +-448 (a reading
+    taken here; a conversion to the largest finite value, since the format has no
     infinity).  NaN gives 0x7F; the sign of zero is kept.
 
     Written as a nearest-value search over the 127 finite non-negative codes."""
