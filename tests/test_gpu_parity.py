@@ -415,7 +415,7 @@ def test_spmm_fwd_decode_integer_exact(T, K):
 # ------------------------------------------------------------------ adapter backward
 
 ADAPTER_BWD_SHAPES = [(64, 256, 256, 8), (300, 528, 272, 40), (37, 64, 136, 72), (512, 768, 1024, 128),
-                      (1, 64, 64, 1), (130, 272, 520, 33)]
+                      (1, 64, 64, 1), (130, 272, 520, 33), (96, 256, 512, 24), (200, 512, 256, 96)]
 
 
 def _chunks(M):
