@@ -282,15 +282,23 @@ def profile_mode(args, wl, T):
 
     import sparse_gemm_02_amd as S
     if args.profile_op == "copy":
+        # a plain device copy of known size: the counters' calibration, and the
+        # box's own copy rate (n bytes read, n written) as context for HBM fractions
         n = args.copy_mib * (1 << 20)
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         a.fill_(1)
+        b.copy_(a)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(args.repeat):
             b.copy_(a)
+        e1.record()
         torch.cuda.synchronize()
-        print(f"[profile] copy {n} bytes x {args.repeat}", flush=True)
+        ms = e0.elapsed_time(e1) / args.repeat
+        print(json.dumps({"profile": "copy", "bytes": n, "repeat": args.repeat, "ms": round(ms, 4),
+                          "tbs": round(2 * n / (ms * 1e-3) / 1e12, 3)}), flush=True)
         return
     sel = [(i, l) for i, l in enumerate(wl.linears) if args.linear in (None, l.name)]
     lins = [Linear(l.name, l.K, l.N, T, wl.r, seed=0, index=i) for i, l in sel]
