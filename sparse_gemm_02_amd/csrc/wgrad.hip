@@ -34,6 +34,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Rows of k tiles per group of the XCD-aware tile order (tile_map.h), as in
+// the sparse products: eight with few k tiles; with many (FC2 of OPT-66B: 144
+// k tiles, its X too large to stay in the infinity cache while dY does)
+// narrower groups, six when each XCD's share of the order is a whole number of
+// six-row groups, else four (FC2: 4.53 -> 4.40 ms; QKV and FC1, 36 k tiles,
+// are 1-4% slower with four or six).  `nblocks` is the number of blocks the
+// order covers, the same at every use for one launch.
+__device__ __forceinline__ int wgrad_group(int nblocks, int tiles_k, int tiles_n) {
+  if (tiles_k < 72) return 8;
+  const int per_xcd = nblocks % 8 == 0 ? nblocks / 8 : 0;
+  return per_xcd > 0 && per_xcd % (6 * tiles_n) == 0 ? 6 : 4;
+}
+
 template <int BK_, int BN_, int NST_, int WGK_, int WGN_>
 struct WGeo {
   static constexpr int BK = BK_, BN = BN_;         // tile rows (k) x columns (n) of dW^T
@@ -401,11 +414,13 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
   const int tj = tail ? (int)blockIdx.x - nb_main : 0;
   const int split = MODE == kSplit ? (int)blockIdx.x / ntiles : (tail ? tj / ntail : 0);
   int tk, tn;
+  const int order_blocks = MODE == kSplit ? ntiles : (MODE == kTail ? nb_main : (int)gridDim.x);
+  const int group = wgrad_group(order_blocks, tiles_k, tiles_n);
   if (tail)
-    logical_tile(nb_main + tj % ntail, tiles_k, tiles_n, 8, tk, tn);
+    logical_tile(nb_main + tj % ntail, tiles_k, tiles_n, group, tk, tn);
   else
-    tile_of_block(MODE == kSplit ? (int)blockIdx.x % ntiles : (int)blockIdx.x,
-                  MODE == kSplit ? ntiles : (MODE == kTail ? nb_main : (int)gridDim.x), tiles_k, tiles_n, 8, tk, tn);
+    tile_of_block(MODE == kSplit ? (int)blockIdx.x % ntiles : (int)blockIdx.x, order_blocks, tiles_k, tiles_n, group,
+                  tk, tn);
   const int64_t k0 = (int64_t)tk * G::BK, n0 = (int64_t)tn * G::BN;
   const int64_t Tch = (T + kChunkTokens - 1) / kChunkTokens;
   // this block's token chunks [s_first, stages)
@@ -577,7 +592,7 @@ __global__ __launch_bounds__(256) void wgrad_tail_reduce_kernel(const float* __r
                                                                 int accumulate) {
   const int i = (int)blockIdx.x / 64, rb = (int)blockIdx.x % 64;
   int tk, tn;
-  logical_tile(nb_main + i, tiles_k, tiles_n, 8, tk, tn);
+  logical_tile(nb_main + i, tiles_k, tiles_n, wgrad_group(nb_main, tiles_k, tiles_n), tk, tn);
   const int nl = rb * 4 + (int)(threadIdx.x >> 6), gl = (int)(threadIdx.x & 63);
   const int64_t n = (int64_t)tn * 256 + nl, g = (int64_t)tk * 64 + gl;
   if (n >= N || 4 * g >= K) return;
