@@ -361,10 +361,19 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint16_t* __rest
 // staging both operands in LDS this halves the LDS fill traffic and cuts the
 // LDS fragment reads by a third.  Operands meet the MFMAs in the same
 // positions and order as in the token-major kernel, so results are identical.
-template <int NST_, int PD_>
+//
+// PP (ping-pong): the waves form two groups, 0-3 and 4-7, one wave of each on
+// every SIMD, running half a stage apart with two barriers per stage.  While
+// one group issues a stage's MFMAs, the other issues its loads, reads the next
+// stage's X fragments from LDS and waits, so each SIMD's matrix pipe always has
+// one wave with MFMAs ready instead of both waves draining it at the same
+// barrier.  Every load is issued in the same per-wave order as without PP (one
+// stage's X, then the dY set PD stages ahead), so one wait count serves both.
+template <int NST_, int PD_, bool PP_ = false>
 struct DGeo {
   static constexpr int BK = 256, BN = 256, WGK = 2, WGN = 4, WAVES = 8, THREADS = 512;
   static constexpr int WK = BK / WGK, WN = BN / WGN, FK = WK / 32, FN = WN / 32;
+  static constexpr bool PP = PP_;
   static constexpr int NST = NST_, PD = PD_, RING = PD_ + 1;
   static constexpr int CHUNK_BYTES = kChunkElems * 2;
   static constexpr int LDS_BYTES = NST * CHUNK_BYTES;
@@ -375,8 +384,12 @@ struct DGeo {
   static constexpr int W1 = (DMA + DLOADS) * (NST - 2) + DLOADS;
   static constexpr int W0 = DMA * (NST - 2) + DLOADS * PD;
   static constexpr int XWAIT = W1 < W0 ? W1 : W0;
+  // PP prologue: X's first stage landed while group 1 still holds back the
+  // last prologue phase (it issues that in its first phase in the loop)
+  static constexpr int PWAIT = DMA * (NST - 2) + DLOADS * (PD - 1);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(NST >= 2 && PD >= 1, "pipeline depth");
+  static_assert(!PP || (NST >= 3 && PD >= 2 && PD <= NST - 1 && XWAIT == W0), "ping-pong wait counts");
 };
 
 //
@@ -406,7 +419,9 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
                                                                    int nb_main, int ntail) {
   static_assert(G::BK == 256 && G::BN == 256, "tail buffers hold 256 x 256 tiles");
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: the LDS addresses of the
+  // buffer-to-LDS loads are then computed without vector temporaries
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave % G::WGK, wn = wave / G::WGK;
   const int tiles_k = (K + G::BK - 1) / G::BK, tiles_n = (N + G::BN - 1) / G::BN;
   const int ntiles = tiles_k * tiles_n;
@@ -487,6 +502,97 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
   };
 
   DFrags ring[G::RING];
+  // whole groups of RING stages, at least one (the ring index stays static, no
+  // early exit leaves the compiler's wait counting pessimistic, and no branch
+  // around the loop lets the prologue's loads sink past its wait); stages past
+  // the last token chunk read zeros and add nothing
+  const int span = stages - s_first;
+  const int stages_pad = s_first + (span <= G::RING ? G::RING : (span + G::RING - 1) / G::RING * G::RING);
+  if constexpr (G::PP) {
+    // Ping-pong.  Phases between barriers: group 0 runs M(s) (the 16 MFMAs of
+    // stage s) then L(s) (the loads of X stage s+NST and dY stage s+PD, X's
+    // fragments of stage s+1 into registers); group 1 runs L(s-1) then M(s).
+    // Before the barrier that ends M(s) of group 0 and L(s-1) of group 1,
+    // every wave has waited for its part of X stage s+1, so that barrier makes
+    // the stage visible to both groups' next reads; X stage s is read by group
+    // 0 before the previous barrier and by group 1 before this one, so the
+    // loads into its slot (stage s+NST) are issued after it.
+    const bool g1 = wave >= 4;                                   // wave-uniform
+    // a barrier that no instruction is scheduled across, MFMAs included
+    auto phase_barrier = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The prologue issues as the phases L(s_first - NST) .. L(s_first - 1)
+    // would (each stage's X, then the dY set of the stage PD later, where
+    // that is one of this block's), so that every dY set has the same loads
+    // after it on entry to the loop as in the loop, and the compiler's waits
+    // for them are as loose in the first stages as in the rest; group 1
+    // leaves the last of these phases to its first phase in the loop.  Each
+    // group has a code path of its own from the prologue on, so that neither
+    // inherits the other's pending loads at the loop head.
+    XFrags x0, x1;
+    auto prologue = [&](int phases) {
+#pragma unroll
+      for (int p = 0; p < G::NST; ++p) {
+        if (p < phases) {
+          issue_x(s_first + p);
+          if (p >= G::NST - G::PD) load_d(ring[p - (G::NST - G::PD)], s_first + p - (G::NST - G::PD));
+        }
+      }
+      compiler_fence();
+      wait_vmcnt<G::PWAIT>();                                    // X's first stage landed (this wave's part)
+      phase_barrier();
+      compiler_fence();
+    };
+    int s0 = s_first;
+    if (!g1) {
+      prologue(G::NST);
+      read_x(x0, s_first, 0);
+      read_x(x1, s_first, 1);
+      do {
+#pragma unroll
+        for (int u = 0; u < G::RING; ++u) {
+          const int s = s0 + u;
+          mma(x0, ring[u], 0);
+          mma(x1, ring[u], 1);
+          wait_vmcnt<G::XWAIT>();                                // X's stage s+1 landed (this wave's part)
+          phase_barrier();
+          compiler_fence();
+          issue_x(s + G::NST);
+          load_d(ring[(u + G::PD) % G::RING], s + G::PD);
+          read_x(x0, s + 1, 0);
+          read_x(x1, s + 1, 1);
+          wait_lgkmcnt0();                                       // stage s+1's fragments in registers
+          phase_barrier();
+          compiler_fence();
+        }
+        s0 += G::RING;
+      } while (s0 < stages_pad);
+    } else {
+      prologue(G::NST - 1);
+      do {
+#pragma unroll
+        for (int u = 0; u < G::RING; ++u) {
+          const int s = s0 + u;
+          issue_x(s - 1 + G::NST);
+          load_d(ring[(u + G::PD - 1) % G::RING], s - 1 + G::PD);
+          read_x(x0, s, 0);
+          read_x(x1, s, 1);
+          wait_lgkmcnt0();                                       // stage s's fragments in registers
+          wait_vmcnt<G::XWAIT>();                                // X's stage s+1 landed (this wave's part)
+          phase_barrier();
+          compiler_fence();
+          mma(x0, ring[u], 0);
+          mma(x1, ring[u], 1);
+          phase_barrier();
+          compiler_fence();
+        }
+        s0 += G::RING;
+      } while (s0 < stages_pad);
+    }
+  } else {
 #pragma unroll
   for (int p = 0; p < G::NST; ++p) issue_x(s_first + p);
 #pragma unroll
@@ -497,12 +603,6 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
   compiler_fence();                                              // the first LDS reads stay after the barrier
   XFrags x0, x1;
   read_x(x0, s_first, 0);
-  // whole groups of RING stages, at least one (the ring index stays static, no
-  // early exit leaves the compiler's wait counting pessimistic, and no branch
-  // around the loop lets the prologue's loads sink past its wait); stages past
-  // the last token chunk read zeros and add nothing
-  const int span = stages - s_first;
-  const int stages_pad = s_first + (span <= G::RING ? G::RING : (span + G::RING - 1) / G::RING * G::RING);
   int s0 = s_first;
   do {
 #pragma unroll
@@ -523,6 +623,7 @@ __global__ __launch_bounds__(G::THREADS, 1) void wgrad_direct_kernel(const uint1
     }
     s0 += G::RING;
   } while (s0 < stages_pad);
+  }
   wait_vmcnt<0>();
   if constexpr (MODE == kSplit) {
     wgrad_store<G, float>(acc, meta, K, N, k0, n0, wk, wn, lane, part + (int64_t)split * N * (K / 2), nullptr, 0,
@@ -624,7 +725,7 @@ __global__ __launch_bounds__(256) void wgrad_tail_reduce_kernel(const float* __r
   store_pair(vp, v0, v1);
 }
 
-typedef DGeo<4, 3> DGeoBig;
+typedef DGeo<8, 3, true> DGeoBig;
 
 int64_t chunks_of(int64_t C) { return (C + kChunkRows - 1) / kChunkRows; }
 int64_t token_chunks(int64_t T) { return (T + kChunkTokens - 1) / kChunkTokens; }
