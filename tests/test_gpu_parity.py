@@ -517,7 +517,7 @@ def test_adapter_backward_integer_exact():
 
 
 WGRAD_SHAPES = [(64, 256, 256), (300, 520, 272), (512, 768, 1024), (37, 100, 68), (1, 64, 128), (130, 36, 4),
-                (0, 64, 64), (257, 264, 520)]
+                (0, 64, 64), (257, 264, 520), (288, 256, 512), (416, 776, 264)]
 
 
 def wgrad_ws(T, N, K):
@@ -548,9 +548,13 @@ def test_masked_wgrad(T, N, K, out_dt, packed):
 
 
 # (70, 8136, 2000) and (70, 8136, 2224): 256 and 288 output tiles, a whole
-# round of blocks and a partly filled second one, ragged in k and n.
+# round of blocks and a partly filled second one, ragged in k and n.  The
+# token-chunk counts 3, 5, 9 and 13 sit on either side of the packed kernel's
+# four-stage register ring and eight-stage X ring (its loop runs whole groups
+# of four stages, the extra ones reading zeros).
 @pytest.mark.parametrize("T,N,K", [(300, 520, 272), (257, 264, 520), (1, 64, 128), (2048, 512, 768), (32, 8, 1032),
-                                   (64, 256, 1032), (97, 264, 776), (70, 8136, 2000), (70, 8136, 2224)])
+                                   (64, 256, 1032), (97, 264, 776), (70, 8136, 2000), (70, 8136, 2224),
+                                   (96, 264, 520), (160, 520, 272), (288, 256, 512), (416, 776, 264)])
 def test_masked_wgrad_packed_matches_direct(T, N, K):
     """Both kernels feed the same operands to the same MFMA positions in the
     same token order, so with and without the workspace results are bitwise equal."""
